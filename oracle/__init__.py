@@ -1,0 +1,165 @@
+"""CPU oracle for in-place partial RoPE (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the HIP path.
+
+The arithmetic lives in ``rope_oracle.c`` (plain C, built with gcc and no
+floating-point contraction); this module only marshals numpy arrays into it.
+The operation follows two pages:
+
+* "CANN ops-transformer 算子详解：inplace_partial_rotary_mul 原地部分旋转位置编码"
+  -- section 计算公式 (the interleave formula), section 约束说明 (slice and
+  broadcast rules), the mixed-precision paragraph of the tiling/kernel section
+  (fp32 compute, round-to-nearest-even write-back), section 自动微分说明
+  (backward = gradient of x only).
+* "ANE实战RoPE位置编码在MIL中的纯ANE实现" -- section 先搞懂RoPE (the
+  rotate_half pairing (i, i+h/2)) and the backward section (inverse rotation).
+
+Storage convention: fp32 data is a ``numpy.float32`` array; fp16 and bf16
+data are ``numpy.uint16`` arrays holding the raw 16-bit patterns.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
+against closed forms, brute force and library conversions.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rope_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "librope_oracle.so")
+
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+MODES = {"rotate_half": 0, "interleave": 1}
+DIRECTIONS = {"fwd": 0, "bwd": 1}
+
+GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99",
+           "-fPIC", "-shared", _SRC, "-o", _LIB_PATH, "-lm"]
+
+
+def build() -> str:
+    """Compile the oracle library with gcc; returns its path."""
+    subprocess.run(GCC_CMD, check=True)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        L = ctypes.CDLL(_LIB_PATH)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        L.rope_oracle_rows.restype = ctypes.c_int
+        L.rope_oracle_rows.argtypes = [
+            ctypes.c_void_p, i64p, ctypes.c_int,
+            ctypes.c_void_p, i64p, i64p,
+            ctypes.c_void_p, i64p, i64p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+            i64p, ctypes.c_int64,
+        ]
+        for name in ("oracle_f16_to_f32_n", "oracle_bf16_to_f32_n"):
+            f = getattr(L, name)
+            f.restype = None
+            f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        for name in ("oracle_f32_to_f16_n", "oracle_f32_to_bf16_n"):
+            f = getattr(L, name)
+            f.restype = None
+            f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        _lib = L
+    return _lib
+
+
+def _i64(seq) -> ctypes.Array:
+    arr = (ctypes.c_int64 * len(seq))(*[int(v) for v in seq])
+    return arr
+
+
+def _check_storage(a: np.ndarray, dtype: str) -> None:
+    want = np.float32 if dtype == "f32" else np.uint16
+    if a.dtype != want:
+        raise TypeError(f"{dtype} data must be stored as {np.dtype(want).name}, got {a.dtype}")
+    if not a.flags.c_contiguous:
+        raise ValueError("oracle buffers must be C-contiguous")
+
+
+def _table_strides(t: np.ndarray) -> list[int]:
+    item = t.itemsize
+    return [s // item for s in t.strides]
+
+
+def rope_rows(x: np.ndarray, x_shape, dtype: str, r1: np.ndarray, r2: np.ndarray,
+              mode: str, partial_slice, direction: str, rows=None, table_dtype: str | None = None) -> None:
+    """Rotate the slice of rows of ``x`` in place (see ``rope_oracle.c``).
+
+    ``x`` holds either the whole (B,S,N,D) tensor (``rows=None``) or, in row
+    order, the rows whose flat indices ``(b*S+s)*N+n`` are listed in ``rows``.
+    ``r1``/``r2`` are 4-D numpy arrays (any strides, including the zero
+    strides of ``np.broadcast_to``) whose size-1 dimensions broadcast.
+    ``table_dtype`` defaults to ``dtype``. ``partial_slice=None`` means
+    [0, 0), the empty slice.
+    """
+    _check_storage(x, dtype)
+    table_dtype = dtype if table_dtype is None else table_dtype
+    want = np.float32 if table_dtype == "f32" else np.uint16
+    for t in (r1, r2):
+        if t.dtype != want or t.ndim != 4:
+            raise TypeError("tables must be 4-D arrays in the table storage type")
+    start, end = (0, 0) if partial_slice is None else (int(partial_slice[0]), int(partial_slice[1]))
+    B, S, N, D = (int(v) for v in x_shape)
+    if rows is None:
+        if x.size != B * S * N * D:
+            raise ValueError("x does not hold the full tensor")
+        rows_p = None
+        nrows = B * S * N
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        if x.size != rows.size * D:
+            raise ValueError("x must hold len(rows) rows of D elements")
+        rows_p = rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+        nrows = rows.size
+    rc = lib().rope_oracle_rows(
+        x.ctypes.data, _i64(x_shape), DTYPES[dtype],
+        r1.ctypes.data, _i64(r1.shape), _i64(_table_strides(r1)),
+        r2.ctypes.data, _i64(r2.shape), _i64(_table_strides(r2)),
+        DTYPES[table_dtype], MODES[mode], start, end, DIRECTIONS[direction],
+        rows_p, nrows)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+
+
+# Converters (oracle-private; exposed so that tests can pin them).
+
+def f16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float32)
+    lib().oracle_f16_to_f32_n(bits.ctypes.data, out.ctypes.data, bits.size)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(bits.shape, np.float32)
+    lib().oracle_bf16_to_f32_n(bits.ctypes.data, out.ctypes.data, bits.size)
+    return out
+
+
+def f32_to_f16_bits(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_f32_to_f16_n(v.ctypes.data, out.ctypes.data, v.size)
+    return out
+
+
+def f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint16)
+    lib().oracle_f32_to_bf16_n(v.ctypes.data, out.ctypes.data, v.size)
+    return out
