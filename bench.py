@@ -1,0 +1,262 @@
+"""Throughput of in-place partial RoPE on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload c4|c3|c4_f32|...]
+
+One step = one backward and one forward launch over the whole workload (the
+full hot path: argument checks, index mapping, loads, fp32 rotation,
+round-to-nearest-even stores), in place, inputs resident in HBM. The default
+workload is the long-context backward shard: dx (16,8192,32,128) bf16, slice
+[32,96), interleave, per-batch position tables (16,8192,1,64) with base 5e5.
+
+Prints one JSON line: whole-job algorithmic GB/s (slice read + slice written +
+cos/sin read once, per launch) and Gelem/s, the roofline of the dominant
+kernel (average launch duration from HIP events on the launch stream), HBM
+traffic from the committed rocprofv3 counter summary when it matches the
+current kernel source, and the CPU oracle timed on a bounded sample.
+
+`--profile-target` runs only launches of the chosen kernel plus a copy of
+known size (for rocprofv3 counter passes), and prints nothing else.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of MI355X peak) + Gelem/s, partial-RoPE fwd/bwd in place"
+PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD public spec
+KERNEL_SRC = os.path.join(ROOT, "transformer_positional_encoding_amd", "csrc", "rope_kernels.hip")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(workload: str, direction: str):
+    """Per-launch HBM bytes (read, write) measured by rocprofv3 for this
+    kernel source, from profiles/hbm_traffic.md; None if absent or stale."""
+    if not os.path.exists(TRAFFIC_MD):
+        return None
+    text = open(TRAFFIC_MD, encoding="utf-8").read()
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    data = json.loads(m.group(1))
+    if data.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    entry = data.get("launches", {}).get(f"{workload}:{direction}")
+    return entry
+
+
+def launch_fn(direction):
+    import transformer_positional_encoding_amd as rp
+    return rp.rope_partial_fwd_inplace if direction == "fwd" else rp.rope_partial_bwd_inplace
+
+
+def time_launches(fn, args, n: int, stream) -> float:
+    """Average duration (s) of n back-to-back launches on `stream`, from HIP
+    events recorded on that same stream."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(n):
+        fn(*args)
+    end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / 1e3 / n
+
+
+def cpu_baseline(w, x_cpu, r1, r2, direction: str, budget_s: float) -> dict:
+    """The CPU oracle, single-threaded as written, on the first rows of the
+    same workload: calibrated on a small slice, then run for ~budget_s."""
+    import numpy as np
+
+    import oracle
+    import workloads as W
+
+    B, S, N, D = (int(v) for v in x_cpu.shape)
+    flat = W.to_numpy_storage(x_cpu).reshape(-1, D)
+    t1, t2 = W.to_numpy_storage(r1), W.to_numpy_storage(r2)
+    per_row = 2 * w.L * W.ESIZE[w.dtype]
+
+    def run(nrows):
+        rows = np.arange(nrows, dtype=np.int64)
+        buf = np.ascontiguousarray(flat[:nrows])
+        t0 = time.perf_counter()
+        oracle.rope_rows(buf, x_cpu.shape, w.dtype, t1, t2, w.mode, w.partial_slice, direction, rows=rows)
+        return time.perf_counter() - t0
+
+    n_cal = min(flat.shape[0], 20000)
+    dt = run(n_cal)
+    rate = n_cal / max(dt, 1e-9)
+    nrows = int(min(flat.shape[0], max(n_cal, rate * budget_s)))
+    dt = run(nrows)
+    groups = -(-nrows // N)
+    table_bytes = 2 * groups * w.L * W.ESIZE[w.tdtype]
+    gbps = (nrows * per_row + table_bytes) / dt / 1e9
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {nrows} of {B * S * N} rows of the workload, one {direction} pass, "
+                      f"{dt:.1f} s single-threaded C oracle; bytes counted as on the GPU"}
+
+
+def bench_workload(name: str, steps: int, warmup: int, reps: int, stream, want_cpu: bool, cpu_s: float):
+    import torch
+
+    import workloads as W
+    w = W.WORKLOADS[name]
+    x_cpu = W.make_x(w)
+    r1, r2 = W.make_tables(w)
+    x = x_cpu.to("cuda")
+    r1d, r2d = r1.to("cuda"), r2.to("cuda")
+    torch.cuda.synchronize()
+    # a step runs both directions, the workload's own direction first
+    dirs = list(w.directions) + [d for d in ("fwd", "bwd") if d not in w.directions]
+    calls = [(launch_fn(d), (x, r1d, r2d, w.mode, w.partial_slice)) for d in dirs]
+
+    for _ in range(warmup):
+        for fn, args in calls:
+            fn(*args)
+    torch.cuda.synchronize()
+    # whole steps (every direction once per step)
+    t_start = time.perf_counter()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(steps):
+        for fn, args in calls:
+            fn(*args)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_s = ev0.elapsed_time(ev1) / 1e3 / steps
+    # per-kernel average launch durations
+    per_launch = {}
+    for d, (fn, args) in zip(dirs, calls):
+        per_launch[d] = time_launches(fn, args, reps, stream)
+    bytes_launch = w.algorithmic_bytes()
+    elems_launch = w.rotated_elements()
+    out = {
+        "workload": name, "note": w.note, "x_shape": list(w.x_shapes[0]), "dtype": w.dtype,
+        "slice": list(w.partial_slice), "mode": w.mode, "table_shape": list(w.table_shape),
+        "directions": dirs, "step_s": step_s, "wall_s": wall,
+        "bytes_per_launch": bytes_launch, "elements_per_launch": elems_launch,
+        "kernels": {d: {"avg_launch_us": round(t * 1e6, 3),
+                        "GBps": round(bytes_launch / t / 1e9, 1),
+                        "Gelem_per_s": round(elems_launch / t / 1e9, 1),
+                        "frac_of_peak": round(bytes_launch / t / 1e9 / PEAK_GBPS, 4)}
+                    for d, t in per_launch.items()},
+    }
+    if want_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, x_cpu, r1, r2, dirs[0], cpu_s)
+    del x, x_cpu
+    return out
+
+
+def profile_target(name: str, reps: int) -> None:
+    """Launches for rocprofv3 counter passes: the workload's kernels, then a
+    plain device copy of known size for calibrating the byte counters."""
+    import torch
+
+    import workloads as W
+    w = W.WORKLOADS[name]
+    x = W.make_x(w).to("cuda")
+    r1, r2 = (t.to("cuda") for t in W.make_tables(w))
+    for d in w.directions:
+        for _ in range(reps):
+            launch_fn(d)(x, r1, r2, w.mode, w.partial_slice)
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")  # 256 MiB
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_target": name, "reps": reps, "copy_bytes": src.numel()}), flush=True)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--also", default="c3,c4_f32",
+                    help="other workloads measured in the same run (reported under 'other_workloads')")
+    ap.add_argument("--reps", type=int, default=50, help="launches per per-kernel timing")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-target", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the operation shards over B, S or heads with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    import transformer_positional_encoding_amd as rp
+    rp.library()  # fail loudly if the HIP library is missing
+
+    if args.profile_target:
+        profile_target(args.workload, args.reps)
+        return 0
+
+    stream = torch.cuda.current_stream()
+    main_res = bench_workload(args.workload, args.steps, args.warmup, args.reps, stream,
+                              not args.no_cpu_baseline, args.cpu_seconds)
+    others = []
+    for name in [n for n in args.also.split(",") if n and n != args.workload]:
+        r = bench_workload(name, max(5, args.steps // 5), 2, max(10, args.reps // 2), stream, False, 0)
+        others.append({k: r[k] for k in ("workload", "note", "dtype", "directions", "bytes_per_launch",
+                                         "elements_per_launch", "kernels")})
+
+    import workloads as W
+    w = W.WORKLOADS[args.workload]
+    n_launch = len(main_res["directions"])
+    step_bytes = main_res["bytes_per_launch"] * n_launch
+    step_elems = main_res["elements_per_launch"] * n_launch
+    value = step_bytes / main_res["step_s"] / 1e9
+    dom = main_res["directions"][0]
+    k = main_res["kernels"][dom]
+    traffic = committed_traffic(args.workload, dom)
+    roofline = {
+        "bound": "hbm", "achieved": k["GBps"], "peak": PEAK_GBPS, "unit": "GB/s",
+        "frac": k["frac_of_peak"],
+        "traffic": None if traffic is None else traffic["hbm_bytes_per_launch"],
+        "kernel": f"rope_vec_kernel ({w.dtype}, {w.mode}, {dom})",
+        "bytes_per_launch": main_res["bytes_per_launch"], "avg_launch_us": k["avg_launch_us"],
+    }
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(main_res["step_s"] * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic (seeded; shapes and tables as the workload states)",
+        "config": {"workload": f"{args.workload}: {w.note}", "x_shape": main_res["x_shape"],
+                   "slice": main_res["slice"], "mode": w.mode, "table_shape": main_res["table_shape"],
+                   "directions_per_step": main_res["directions"], "parallelism": "single GPU"},
+        "gelem_per_s": round(step_elems / main_res["step_s"] / 1e9, 1),
+        "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
+        "roofline": roofline,
+        "kernels": main_res["kernels"],
+        "other_workloads": others,
+    }
+    if "cpu_baseline" in main_res:
+        line["cpu_baseline"] = main_res["cpu_baseline"]
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,122 @@
+/*
+ * rope_partial.h -- C ABI of the MI355X (gfx950) in-place partial rotary
+ * position embedding library, librope_partial.so.
+ *
+ * The operation ("CANN ops-transformer 算子详解：inplace_partial_rotary_mul
+ * 原地部分旋转位置编码", sections 功能与计算公式 and 约束说明; rotate_half
+ * pairing from "ANE实战RoPE位置编码在MIL中的纯ANE实现", section 先搞懂RoPE):
+ *
+ *   x has shape (B,S,N,D), row-major and contiguous (BSND). Only the lanes
+ *   [start,end) of the last dimension are rotated, in place; every other lane
+ *   keeps its bytes. With L = end - start and slice lane j in [0,L):
+ *     interleave  (mode 1): partner p(j) = j xor 1,   sign s(j) = -1 if j even
+ *     rotate_half (mode 0): partner p(j) = j +- L/2,  sign s(j) = -1 if j < L/2
+ *   forward : y_j  = x_j * r1_j + s(j) * x_p(j) * r2_j
+ *   backward: dx_j = g_j * r1_j - s(j) * g_p(j) * r2_p(j)
+ *   (the backward is the transposed Jacobian of the forward -- the gradient
+ *   with respect to x, section 自动微分说明 -- which equals rotating by -θ
+ *   when the tables hold one angle per pair.)
+ *   r1 (cos) and r2 (sin) are read at the broadcast index of (b,s,n,j).
+ *   Arithmetic is fp32: 16-bit data is widened exactly, and each result is
+ *   rounded once to fp32 and once, to nearest-even, to the storage type.
+ *
+ * Memory: every pointer is a device pointer on the current HIP device. The
+ * caller owns all memory; the library allocates nothing and keeps no state
+ * but a per-device cache of the compute-unit count. Calls are asynchronous on
+ * `stream` (a hipStream_t; NULL is the null stream). A call that returns an
+ * error before the launch has not touched device memory.
+ */
+#ifndef ROPE_PARTIAL_H
+#define ROPE_PARTIAL_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rope_status {
+    ROPE_OK = 0,
+    ROPE_ERR_NULLPTR = 1,      /* a required pointer is NULL                   */
+    ROPE_ERR_INVALID = 2,      /* an argument breaks the constraints below     */
+    ROPE_ERR_UNSUPPORTED = 3,  /* a valid combination this build does not run  */
+    ROPE_ERR_RUNTIME = 4       /* the HIP runtime reported an error            */
+} rope_status_t;
+
+typedef enum rope_dtype {
+    ROPE_DTYPE_F32 = 0,
+    ROPE_DTYPE_F16 = 1,
+    ROPE_DTYPE_BF16 = 2
+} rope_dtype_t;
+
+/* rotary modes; interleave keeps the integer the CANN interface gives it */
+#define ROPE_MODE_ROTATE_HALF 0
+#define ROPE_MODE_INTERLEAVE 1
+
+/* largest supported head dimension D (the page's D limit) */
+#define ROPE_D_LIMIT 1024
+
+/*
+ * rope_partial_fwd_inplace -- rotate x[..., start:end) in place (forward).
+ *
+ *   x            device buffer of B*S*N*D elements of `dtype`, contiguous
+ *                BSND; 16-byte alignment enables the vector kernels.
+ *   x_shape      host array {B, S, N, D}; each >= 0, D even, D <= 1024.
+ *   dtype        storage type of x.
+ *   r1, r2       device buffers: cos and sin tables of `table_dtype`.
+ *   r*_shape     host arrays, 4-D; r*_shape[3] == L and, for k < 3,
+ *                r*_shape[k] is 1 (broadcast) or x_shape[k]. This admits the
+ *                layouts the page lists (BSND, B1ND, B11D, 111D, BS1D) and
+ *                any other broadcast of the same rule.
+ *   r*_strides   host arrays, strides in elements, each >= 0;
+ *                r*_strides[3] must be 1. The stride of a size-1 dimension
+ *                is ignored (this is what torch's expand() produces).
+ *   table_dtype  must equal dtype (mixed precision is not built).
+ *   mode         ROPE_MODE_INTERLEAVE or ROPE_MODE_ROTATE_HALF.
+ *   partial_slice host array {start, end} or NULL, which means {0, 0}:
+ *                0 <= start <= end <= D and L = end - start even.
+ *   stream       hipStream_t to launch on, or NULL.
+ *
+ * Checks, in this order: scalar arguments (ROPE_ERR_NULLPTR for a NULL
+ * x_shape, ROPE_ERR_INVALID otherwise); then an empty tensor (B*S*N*D == 0)
+ * or an empty slice (L == 0) returns ROPE_OK at once without reading any
+ * pointer (no-op, as the page specifies for forward and backward); then NULL
+ * data or table pointers (ROPE_ERR_NULLPTR); then table shapes and strides
+ * (ROPE_ERR_INVALID); then dtype support (ROPE_ERR_UNSUPPORTED); finally the
+ * launch (ROPE_ERR_RUNTIME if HIP reports an error).
+ * Overlapping x with r1 or r2 is undefined. Results are deterministic: each
+ * element is computed by one thread from the same inputs on every call.
+ */
+rope_status_t rope_partial_fwd_inplace(
+    void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+/*
+ * rope_partial_bwd_inplace -- the backward of rope_partial_fwd_inplace:
+ * x holds the incoming gradient dy on entry and dx on return (in place).
+ * Arguments, checks and no-op rules are those of the forward; r1 and r2
+ * receive no gradient (the page's autograd returns None for them).
+ */
+rope_status_t rope_partial_bwd_inplace(
+    void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+/* Static text for a status code; never NULL. */
+const char* rope_status_string(rope_status_t status);
+
+/* Text describing the last non-OK status returned on the calling thread
+ * (which check failed, or the HIP error); "" if none. The pointer stays valid
+ * until the next call on that thread. */
+const char* rope_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROPE_PARTIAL_H */

@@ -1,0 +1,165 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+function the header declares, and rejects or no-ops arguments before any
+HIP call, as the header documents (constraints from "CANN ops-transformer
+算子详解：inplace_partial_rotary_mul 原地部分旋转位置编码", section 约束说明; no-op
+rules from section 功能与计算公式)."""
+import ctypes
+import glob
+import os
+import re
+import subprocess
+
+import pytest
+
+import transformer_positional_encoding_amd as rp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULLPTR, INVALID, UNSUPPORTED = rp.ROPE_OK, rp.ROPE_ERR_NULLPTR, rp.ROPE_ERR_INVALID, rp.ROPE_ERR_UNSUPPORTED
+F32, F16, BF16 = 0, 1, 2
+IL, RH = 1, 0
+FAKE = 0x10000  # never dereferenced: every call below returns before the launch
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+                            text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string",
+                 "rope_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = rp.library()
+    out = subprocess.run(["nm", "-D", "--defined-only", rp.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings():
+    for code in range(5):
+        assert rp.rope_status_string(code).startswith("ROPE_")
+    assert "unknown" in rp.rope_status_string(99)
+
+
+SAME = object()  # r2 geometry defaults to r1's
+
+
+def call(direction="fwd", x=FAKE, x_shape=(2, 4, 3, 64), dtype=BF16, r1=FAKE, r1_shape=(1, 4, 1, 32),
+         r1_strides=(128, 32, 32, 1), r2=FAKE, r2_shape=SAME, r2_strides=SAME, table_dtype=None,
+         mode=IL, sl=(0, 32)):
+    return rp.raw_call(direction, x, x_shape, dtype, r1, r1_shape, r1_strides, r2,
+                       r1_shape if r2_shape is SAME else r2_shape,
+                       r1_strides if r2_strides is SAME else r2_strides,
+                       dtype if table_dtype is None else table_dtype, mode, sl, None)
+
+
+# A table dtype different from x's is the last check before the launch, so a
+# call that reaches UNSUPPORTED has passed every geometry check.
+PASSES = dict(table_dtype=F32)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_valid_geometry_reaches_dtype_check(direction):
+    assert call(direction, **PASSES) == UNSUPPORTED
+    assert "dtype" in rp.last_error()
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("kwargs,code,text", [
+    (dict(mode=2), INVALID, "mode"),
+    (dict(mode=-1), INVALID, "mode"),
+    (dict(dtype=7), INVALID, "dtype"),
+    (dict(x_shape=(2, -4, 3, 64)), INVALID, "negative"),
+    (dict(x_shape=(2, 4, 3, 63), sl=(0, 32)), INVALID, "even"),
+    (dict(x_shape=(1, 1, 1, 1026), sl=(0, 32)), INVALID, "1024"),
+    (dict(sl=(-2, 30)), INVALID, ">= 0"),
+    (dict(sl=(10, 8)), INVALID, "start"),
+    (dict(sl=(40, 72)), INVALID, "<= D"),
+    (dict(sl=(0, 31), r1_shape=(1, 4, 1, 31)), INVALID, "even"),
+    (dict(x_shape=None), NULLPTR, "x_shape"),
+])
+def test_scalar_argument_errors(direction, kwargs, code, text):
+    assert call(direction, **kwargs) == code
+    assert text in rp.last_error()
+
+
+@pytest.mark.parametrize("kwargs,code,text", [
+    (dict(x=None), NULLPTR, "x is NULL"),
+    (dict(r1=None), NULLPTR, "r1"),
+    (dict(r2=None), NULLPTR, "r2"),
+    (dict(r1_shape=None), NULLPTR, "r1"),
+    (dict(r2_strides=None, r2_shape=(1, 4, 1, 32)), NULLPTR, "r2"),
+    (dict(r1_shape=(1, 4, 1, 16)), INVALID, "last dimension"),
+    (dict(r1_shape=(1, 3, 1, 32)), INVALID, "dimension S"),
+    (dict(r1_shape=(2, 4, 2, 32)), INVALID, "dimension N"),
+    (dict(r1_strides=(128, 32, 32, 2)), INVALID, "stride 1"),
+    (dict(r1_strides=(128, -32, 32, 1)), INVALID, "negative"),
+    (dict(r2_strides=(2**62, 2**62, 32, 1), r2_shape=(2, 4, 1, 32)), INVALID, "overflow"),
+])
+def test_pointer_and_table_errors(kwargs, code, text):
+    assert call(**kwargs) == code
+    assert text in rp.last_error()
+
+
+@pytest.mark.parametrize("tshape,tstrides", [
+    ((2, 4, 3, 32), (384, 96, 32, 1)),   # BSND
+    ((2, 1, 3, 32), (96, 0, 32, 1)),     # B1ND
+    ((2, 1, 1, 32), (32, 7, 99, 1)),     # B11D: strides of size-1 dims are ignored
+    ((1, 1, 1, 32), (0, 0, 0, 1)),       # 111D
+    ((2, 4, 1, 32), (128, 32, 0, 1)),    # BS1D
+    ((1, 4, 1, 32), (0, 32, 0, 1)),      # expand()-style zero strides
+])
+def test_broadcast_layouts_accepted(tshape, tstrides):
+    assert call(r1_shape=tshape, r1_strides=tstrides, **PASSES) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("kwargs", [
+    dict(sl=(8, 8)),                            # empty slice
+    dict(sl=(64, 64)),
+    dict(sl=None),                              # NULL partial_slice = [0, 0)
+    dict(x_shape=(0, 4, 3, 64)),                # B = 0
+    dict(x_shape=(2, 4, 0, 64)),                # N = 0
+])
+def test_noops_need_no_pointers(direction, kwargs):
+    """No-ops return OK without reading x, the tables or their geometry."""
+    assert call(direction, x=None, r1=None, r2=None, r1_shape=None, r1_strides=None,
+                r2_shape=None, r2_strides=None, table_dtype=F32, **kwargs) == OK
+
+
+def test_noop_still_checks_scalars():
+    assert call(x=None, r1=None, r2=None, sl=(8, 8), mode=5) == INVALID
+    assert call(x=None, r1=None, r2=None, x_shape=(0, 4, 3, 63), sl=(0, 0)) == INVALID
+
+
+def test_binding_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(2, 4, 3, 64)
+    r = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(ValueError):
+        rp.rope_partial_fwd_inplace(x.view(8, 3, 64), r, r, "interleave", (0, 32))
+    with pytest.raises(ValueError):
+        rp.rope_partial_fwd_inplace(x, r, r, "sideways", (0, 32))
+    with pytest.raises(ValueError):
+        rp.rope_partial_fwd_inplace(x, r, r, "interleave", (0, 32))  # CPU tensor
+    # an empty CPU tensor is a no-op that touches nothing
+    rp.rope_partial_fwd_inplace(torch.zeros(0, 4, 3, 64), r, r, "interleave", (0, 32))
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(rp, "_lib", None)
+    monkeypatch.setattr(rp, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        rp.library()

@@ -20,6 +20,8 @@ Sources: "CANN ops-transformer ç®—å­è¯¦è§£ï¼šinplace_partial_rotary_mul åŸåœ°é
 paragraph of the tiling/kernel section) and "ANEå®æˆ˜RoPEä½ç½®ç¼–ç åœ¨MILä¸­çš„çº¯ANE
 å®ç°" (section å…ˆææ‡‚RoPE and the backward section).
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -73,7 +75,7 @@ def _run(x, shape, dtype, r1, r2, mode, sl, direction, rows=None):
 @pytest.mark.parametrize("direction", ["fwd", "bwd"])
 def test_matches_complex_rotation(dtype, mode, shape, sl, direction):
     L = sl[1] - sl[0]
-    x = _x(shape, dtype, seed=hash((dtype, mode, sl)) % 1000)
+    x = _x(shape, dtype, seed=zlib.crc32(repr((dtype, mode, sl)).encode()) % 1000)
     c, s = _rope_tables(shape, L, mode, dtype)
     got = _run(x, shape, dtype, c, s, mode, sl, direction)
     want = rotate_complex_form(widen(x, dtype), expand_tables(widen(c, dtype), shape, L),

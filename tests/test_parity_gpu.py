@@ -1,0 +1,267 @@
+"""HIP path vs the CPU oracle, element by element, on seeded inputs.
+
+Every test calls the C ABI through the binding on an MI355X. Small cases are
+compared on every row; the full-size workloads are compared on sampled rows
+that the oracle computes one by one, while the lanes outside the slice are
+checked bit-for-bit on the device for every row.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_positional_encoding_amd as rp
+import workloads as W
+from gpu_support import announce, compare, run_and_check, oracle_rows, widen
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _workload_inputs(name, k=0):
+    w = W.WORKLOADS[name]
+    x = W.make_x(w, k)
+    r1, r2 = W.make_tables(w)
+    return w, x, r1, r2
+
+
+# ---------------------------------------------------------------- the five configurations
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_c0_fp32_interleave(direction):
+    w, x, r1, r2 = _workload_inputs("c0")
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c0 {direction}")
+    assert info["n"] == 16 * 2 * 32
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_c0_noops(direction):
+    w, x, r1, r2 = _workload_inputs("c0")
+    announce(f"c0 no-op {direction}")
+    xd = x.to(DEV)
+    before = xd.clone()
+    fn = rp.rope_partial_fwd_inplace if direction == "fwd" else rp.rope_partial_bwd_inplace
+    fn(xd, r1.to(DEV), r2.to(DEV), "interleave", (8, 8))          # empty slice
+    fn(xd, r1.to(DEV), r2.to(DEV), "interleave", None)            # None = [0, 0)
+    empty = torch.empty((0, 16, 2, 64), device=DEV)
+    fn(empty, r1.to(DEV), r2.to(DEV), "interleave", (0, 32))      # B = 0
+    torch.cuda.synchronize()
+    assert torch.equal(xd.view(torch.int32), before.view(torch.int32))
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_c1_fp16_mha(direction):
+    w, x, r1, r2 = _workload_inputs("c1")
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c1 {direction}")
+    assert info["exact"] == info["n"], "16-bit results should match the oracle bit for bit"
+
+
+def test_c2_bf16_gqa_q_then_k():
+    """Q then K rotated with the same tables on one stream."""
+    w = W.WORKLOADS["c2"]
+    r1, r2 = W.make_tables(w)
+    q, k = W.make_x(w, 0), W.make_x(w, 1)
+    announce("c2 Q and K, one stream")
+    qd, kd = q.to(DEV), k.to(DEV)
+    r1d, r2d = r1.to(DEV), r2.to(DEV)
+    rp.rope_partial_fwd_inplace(qd, r1d, r2d, "rotate_half", (0, 128))
+    rp.rope_partial_fwd_inplace(kd, r1d, r2d, "rotate_half", (0, 128))
+    torch.cuda.synchronize()
+    for name, src, dev in (("Q", q, qd), ("K", k, kd)):
+        B, S, N, D = src.shape
+        rows = np.arange(B * S * N, dtype=np.int64)
+        x_rows = W.to_numpy_storage(src).reshape(-1, D)
+        want = oracle_rows(x_rows, src.shape, "bf16", r1, r2, "rotate_half", (0, 128), "fwd", None)
+        got = W.to_numpy_storage(dev.cpu()).reshape(-1, D)
+        from gpu_support import expanded_tables
+        c = expanded_tables(r1, src.shape, rows, 128)
+        s = expanded_tables(r2, src.shape, rows, 128)
+        info = compare(got, want.reshape(-1, D), x_rows, c, s, "bf16", "rotate_half", "fwd", (0, 128), name)
+        assert info["exact"] == info["n"]
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_c3_bf16_mla_full_size(direction):
+    w, x, r1, r2 = _workload_inputs("c3")
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c3 {direction}",
+                         sample=6000, seed=3)
+    assert info["exact"] == info["n"]
+
+
+@pytest.mark.parametrize("name", ["c4", "c4_f32"])
+@pytest.mark.parametrize("direction", ["bwd", "fwd"])
+def test_c4_long_context_full_size(name, direction):
+    w, x, r1, r2 = _workload_inputs(name)
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"{name} {direction}",
+                         sample=6000, seed=4)
+    if w.dtype != "f32":
+        assert info["exact"] == info["n"]
+
+
+# ---------------------------------------------------------------- more shapes and layouts
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_single_op_example_random_tables(direction):
+    """(2,32,8,128) fp16, slice [0,64), random BS1D tables: the per-lane reading."""
+    w, x, r1, r2 = _workload_inputs("p1ex")
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"p1ex {direction}")
+    assert info["exact"] == info["n"]
+
+
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _rand(shape, dtype, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=g) * scale).to(DT[dtype])
+
+
+CASES = [
+    # (shape, slice, mode, table shape)     -- what it exercises
+    ((2, 8, 4, 64), (0, 64), "interleave", (1, 8, 1, 64)),        # vector path, full slice
+    ((2, 8, 4, 192), (64, 192), "interleave", (2, 8, 1, 128)),    # slice at the row end
+    ((3, 5, 13, 96), (16, 80), "interleave", (1, 5, 1, 64)),      # ragged head count
+    ((1, 4, 37, 128), (8, 104), "interleave", (1, 4, 1, 96)),     # 12 vectors per row (bf16)
+    ((1, 3, 300, 64), (0, 64), "interleave", (1, 3, 1, 64)),      # many heads per block
+    ((2, 6, 5, 64), (3, 35), "interleave", (1, 6, 1, 32)),        # odd start: scalar path
+    ((2, 6, 5, 40), (2, 14), "interleave", (1, 6, 1, 12)),        # L not a vector multiple
+    ((2, 8, 4, 128), (0, 128), "rotate_half", (1, 8, 1, 128)),    # vector path
+    ((2, 8, 4, 256), (64, 192), "rotate_half", (2, 8, 1, 128)),
+    ((2, 5, 3, 48), (4, 44), "rotate_half", (1, 5, 1, 40)),       # half of 20 lanes: scalar path
+    ((2, 8, 4, 64), (0, 64), "interleave", (2, 8, 4, 64)),        # BSND tables (per head)
+    ((2, 8, 4, 64), (0, 64), "interleave", (2, 1, 4, 64)),        # B1ND
+    ((2, 8, 4, 64), (0, 64), "interleave", (2, 1, 1, 64)),        # B11D
+    ((2, 8, 4, 64), (0, 64), "interleave", (1, 1, 1, 64)),        # 111D
+    ((2, 8, 4, 128), (0, 128), "rotate_half", (2, 8, 4, 128)),    # per-head tables, rotate_half
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}-{c[2]}-{c[3]}" for c in CASES])
+def test_shapes_layouts_dtypes(case, direction, dtype):
+    shape, sl, mode, tshape = case
+    seed = zlib.crc32(repr((shape, sl, mode, tshape)).encode()) % 10000
+    x = _rand(shape, dtype, seed)
+    r1 = _rand(tshape, dtype, seed + 1)
+    r2 = _rand(tshape, dtype, seed + 2)
+    info = run_and_check(x, r1, r2, mode, sl, direction, f"{shape} {sl} {mode} {tshape}")
+    if dtype != "f32":
+        assert info["exact"] == info["n"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_expanded_table_views(dtype):
+    """Tables passed as expand() views (zero strides) and as strided slices
+    of a wider buffer give the oracle's result."""
+    shape, sl = (2, 16, 6, 128), (32, 96)
+    x = _rand(shape, dtype, 21)
+    base1 = _rand((1, 16, 1, 64), dtype, 22)
+    base2 = _rand((1, 16, 1, 64), dtype, 23)
+    e1 = base1.to(DEV).expand(2, 16, 6, 64)
+    e2 = base2.to(DEV).expand(2, 16, 6, 64)
+    run_and_check(x, base1, base2, "interleave", sl, "fwd", "expand() tables", r1_dev=e1, r2_dev=e2)
+    wide1 = _rand((1, 16, 1, 192), dtype, 24)
+    wide2 = _rand((1, 16, 1, 192), dtype, 25)
+    s1, s2 = wide1[..., 64:128], wide2[..., 64:128]
+    run_and_check(x, s1.contiguous(), s2.contiguous(), "interleave", sl, "bwd", "strided tables",
+                  r1_dev=wide1.to(DEV)[..., 64:128], r2_dev=wide2.to(DEV)[..., 64:128])
+
+
+def test_unaligned_x_uses_general_path():
+    """x starting 2 bytes past a 16-byte boundary (a view into a buffer)."""
+    shape, sl = (2, 4, 3, 64), (0, 32)
+    x = _rand(shape, "bf16", 31)
+    r1, r2 = _rand((1, 4, 1, 32), "bf16", 32), _rand((1, 4, 1, 32), "bf16", 33)
+    announce("unaligned x")
+    buf = torch.zeros(x.numel() + 1, dtype=torch.bfloat16, device=DEV)
+    xd = buf[1:].view(shape)
+    xd.copy_(x.to(DEV))
+    assert xd.data_ptr() % 16 != 0
+    rp.rope_partial_fwd_inplace(xd, r1.to(DEV), r2.to(DEV), "interleave", sl)
+    torch.cuda.synchronize()
+    want = oracle_rows(W.to_numpy_storage(x).reshape(-1, 64).copy(), shape, "bf16", r1, r2, "interleave", sl,
+                       "fwd", None)
+    assert W.to_numpy_storage(xd.cpu()).reshape(-1, 64).tobytes() == want.tobytes()
+    assert buf[0].item() == 0
+
+
+# ---------------------------------------------------------------- properties of the launch
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_guard_bands_untouched(dtype):
+    """4 KiB guard bands before and after x stay bit-identical."""
+    shape, sl = (2, 16, 6, 128), (32, 96)
+    x = _rand(shape, dtype, 41)
+    r1, r2 = _rand((1, 16, 1, 64), dtype, 42), _rand((1, 16, 1, 64), dtype, 43)
+    announce(f"guard bands {dtype}")
+    esz = torch.tensor([], dtype=DT[dtype]).element_size()
+    guard = 4096 // esz
+    buf = _rand((guard + x.numel() + guard,), dtype, 44).to(DEV)
+    ref = buf.clone()
+    xd = buf[guard: guard + x.numel()].view(shape)
+    xd.copy_(x.to(DEV))
+    for fn in (rp.rope_partial_fwd_inplace, rp.rope_partial_bwd_inplace):
+        fn(xd, r1.to(DEV), r2.to(DEV), "interleave", sl)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int32)) if dtype == "f32" else (lambda t: t.view(torch.int16))
+    assert torch.equal(bits(buf[:guard]), bits(ref[:guard]))
+    assert torch.equal(bits(buf[guard + x.numel():]), bits(ref[guard + x.numel():]))
+
+
+def test_deterministic_repeats():
+    w, x, r1, r2 = _workload_inputs("c1")
+    announce("determinism c1")
+    outs = []
+    for _ in range(3):
+        xd = x.to(DEV)
+        rp.rope_partial_fwd_inplace(xd, r1.to(DEV), r2.to(DEV), "interleave", (0, 64))
+        rp.rope_partial_bwd_inplace(xd, r1.to(DEV), r2.to(DEV), "interleave", (0, 64))
+        outs.append(xd.view(torch.int16).cpu())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[1], outs[2])
+
+
+def test_runs_on_a_side_stream():
+    w, x, r1, r2 = _workload_inputs("c1")
+    announce("side stream c1")
+    xd, r1d, r2d = x.to(DEV), r1.to(DEV), r2.to(DEV)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        rp.rope_partial_fwd_inplace(xd, r1d, r2d, "interleave", (0, 64))
+    side.synchronize()
+    D = 64
+    want = oracle_rows(W.to_numpy_storage(x).reshape(-1, D).copy(), x.shape, "f16", r1, r2, "interleave",
+                       (0, 64), "fwd", None)
+    assert W.to_numpy_storage(xd.cpu()).reshape(-1, D).tobytes() == want.tobytes()
+
+
+def test_errors_raise_before_touching_memory():
+    x = _rand((2, 4, 3, 64), "bf16", 51).to(DEV)
+    before = x.clone()
+    r = _rand((1, 4, 1, 32), "bf16", 52).to(DEV)
+    with pytest.raises(rp.RopeError) as e:
+        rp.rope_partial_fwd_inplace(x, r, r, "interleave", (0, 30))        # table last dim != L
+    assert e.value.status == rp.ROPE_ERR_INVALID
+    with pytest.raises(rp.RopeError) as e:
+        rp.rope_partial_fwd_inplace(x, r.float(), r.float(), "interleave", (0, 32))
+    assert e.value.status == rp.ROPE_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int16), before.view(torch.int16))
+
+
+def test_golden_cases_on_gpu():
+    from golden_cases import all_cases
+    for case in all_cases():
+        dt = case["dtype"]
+        D = case["x"].size
+        L = case["slice"][1] - case["slice"][0]
+        announce(f"golden {case['name']}")
+        x = torch.tensor(case["x"], dtype=torch.float64).to(DT[dt]).view(1, 1, 1, D).to(DEV)
+        c = torch.tensor(case["cos"], dtype=torch.float64).to(DT[dt]).view(1, 1, 1, L).to(DEV)
+        s = torch.tensor(case["sin"], dtype=torch.float64).to(DT[dt]).view(1, 1, 1, L).to(DEV)
+        fn = rp.rope_partial_fwd_inplace if case["direction"] == "fwd" else rp.rope_partial_bwd_inplace
+        fn(x, c, s, case["mode"], case["slice"])
+        torch.cuda.synchronize()
+        assert x.double().cpu().view(-1).tolist() == case["expect"].tolist(), case["name"]

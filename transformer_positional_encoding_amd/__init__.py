@@ -1,0 +1,163 @@
+"""In-place partial rotary position embedding (RoPE) on MI355X (gfx950).
+
+A thin ctypes binding over ``librope_partial.so``, whose C ABI is declared in
+``include/rope_partial.h``. Every step of the operation runs in the library's
+HIP kernels; this module only marshals torch tensors (device pointers, shapes,
+strides, the current HIP stream) into the C calls and turns status codes into
+exceptions. There is no CPU fallback: without the built library every call
+raises.
+
+The operation follows "CANN ops-transformer 算子详解：inplace_partial_rotary_mul
+原地部分旋转位置编码" (sections 功能与计算公式, 函数原型与参数说明, 约束说明,
+自动微分说明) and, for the rotate_half pairing, "ANE实战RoPE位置编码在MIL中的纯
+ANE实现" (section 先搞懂RoPE).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string",
+    "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
+    "ROPE_ERR_UNSUPPORTED", "ROPE_ERR_RUNTIME", "MODES", "DTYPE_CODES",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "librope_partial.so")
+
+ROPE_OK, ROPE_ERR_NULLPTR, ROPE_ERR_INVALID, ROPE_ERR_UNSUPPORTED, ROPE_ERR_RUNTIME = range(5)
+MODES = {"rotate_half": 0, "interleave": 1}
+DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+
+_I64x4 = ctypes.c_int64 * 4
+_I64x2 = ctypes.c_int64 * 2
+_ENTRY_ARGTYPES = [
+    ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+    ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+    ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+    ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64),
+    ctypes.c_void_p,
+]
+
+
+class RopeError(RuntimeError):
+    """A non-OK status from the library; ``status`` holds the code."""
+
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{rope_status_string(status)}: {detail}" if detail else rope_status_string(status))
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m transformer_positional_encoding_amd.build` "
+                "(or __graft_entry__.build()); there is no fallback path")
+        L = ctypes.CDLL(LIB_PATH)
+        for name in ("rope_partial_fwd_inplace", "rope_partial_bwd_inplace"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = _ENTRY_ARGTYPES
+        L.rope_status_string.restype = ctypes.c_char_p
+        L.rope_status_string.argtypes = [ctypes.c_int]
+        L.rope_last_error.restype = ctypes.c_char_p
+        L.rope_last_error.argtypes = []
+        _lib = L
+    return _lib
+
+
+def rope_status_string(status: int) -> str:
+    return library().rope_status_string(int(status)).decode()
+
+
+def _arr4(v):
+    return None if v is None else _I64x4(*[int(t) for t in v])
+
+
+def raw_call(direction: str, x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides,
+             r2_ptr, r2_shape, r2_strides, table_dtype: int, mode: int, partial_slice,
+             stream=None) -> int:
+    """Call an entry point with plain integers and sequences (None = NULL);
+    returns the status code without raising."""
+    fn = library().rope_partial_fwd_inplace if direction == "fwd" else library().rope_partial_bwd_inplace
+    sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
+    return fn(x_ptr, _arr4(x_shape), int(dtype), r1_ptr, _arr4(r1_shape), _arr4(r1_strides),
+              r2_ptr, _arr4(r2_shape), _arr4(r2_strides), int(table_dtype), int(mode), sl, stream)
+
+
+def last_error() -> str:
+    return library().rope_last_error().decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def _call(direction: str, x, r1, r2, mode, partial_slice, stream) -> None:
+    import torch
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"rotary_mode must be one of {sorted(MODES)}")
+        mode = MODES[mode]
+    for name, t in (("x", x), ("r1", r1), ("r2", r2)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D (B,S,N,D layout), got {t.dim()}-D")
+    if x.numel() and not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (BSND); non-contiguous tensors are not supported")
+    dev = x.device
+    for name, t in (("r1", r1), ("r2", r2)):
+        if t.numel() and x.numel() and t.device != dev:
+            raise ValueError(f"{name} must be on {dev}")
+    if stream is None:
+        handle = torch.cuda.current_stream(dev).cuda_stream if x.is_cuda else None
+    else:
+        handle = getattr(stream, "cuda_stream", stream)
+    with torch.cuda.device(dev) if x.is_cuda else _nullcontext():
+        st = raw_call(direction, x.data_ptr() or None, tuple(x.shape), _dtype_code(x),
+                      r1.data_ptr() or None, tuple(r1.shape), tuple(r1.stride()),
+                      r2.data_ptr() or None, tuple(r2.shape), tuple(r2.stride()),
+                      _dtype_code(r1) if r1.dtype == r2.dtype else -1, mode, partial_slice, handle)
+    if st != ROPE_OK:
+        raise RopeError(st, last_error())
+
+
+class _nullcontext:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
+def rope_partial_fwd_inplace(x, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:
+    """Rotate ``x[..., start:end)`` in place (forward).
+
+    x: contiguous (B,S,N,D) GPU tensor, float32/float16/bfloat16.
+    r1, r2: cos and sin tables, 4-D, last dim ``end-start``, other dims 1 or
+    equal to x's (any strides, e.g. from ``expand``), same dtype as x.
+    rotary_mode: "interleave" (pairs 2i, 2i+1) or "rotate_half" (i, i+L/2).
+    partial_slice: (start, end) or None for the empty slice [0, 0).
+    stream: a torch stream or raw hipStream_t; default torch's current stream.
+    """
+    _call("fwd", x, r1, r2, rotary_mode, partial_slice, stream)
+
+
+def rope_partial_bwd_inplace(dx, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:
+    """Backward of :func:`rope_partial_fwd_inplace`: ``dx`` (the incoming
+    gradient) is replaced in place by the gradient with respect to x."""
+    _call("bwd", dx, r1, r2, rotary_mode, partial_slice, stream)

@@ -1,0 +1,553 @@
+// In-place partial rotary position embedding for MI355X (gfx950, CDNA4).
+//
+// Operation: "CANN ops-transformer 算子详解：inplace_partial_rotary_mul
+// 原地部分旋转位置编码", section 功能与计算公式 (interleave pairs (2i,2i+1),
+// out = x*cos + x_rotate*sin on the lanes [start,end), in place) and section
+// 自动微分说明 (backward = gradient w.r.t. x); rotate_half pairs (i, i+L/2)
+// from "ANE实战RoPE位置编码在MIL中的纯ANE实现", section 先搞懂RoPE.
+// Precision: the mixed-precision paragraph of the first page's tiling/kernel
+// section -- 16-bit data is computed in fp32 and written back with
+// round-to-nearest-even.
+//
+// The page's AICore kernel builds an XOR-1 gather table, multiplies, gathers,
+// negates the even lanes with a bit mask and adds, in separate vector passes.
+// Here a thread instead loads whole rotation pairs with 16-byte loads (a pair
+// of 16-bit lanes is one 32-bit word; a pair of fp32 lanes is 8 bytes), does
+// the swap and sign in registers, computes in fp32 (one fp32 rounding, exact
+// products for 16-bit data) and stores only the slice's 16-byte vectors, so
+// lanes outside [start,end) are never written. The path is HBM-bound
+// (0.375-0.75 flop per byte), so there is no MFMA and no LDS: a block owns
+// all heads of one (b,s) position, and when the tables broadcast over heads
+// each thread loads its cos/sin vectors once and reuses them for every head
+// it handles.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <atomic>
+#include <string>
+
+#include "rope_partial.h"
+#include "rope_plan.hpp"
+
+namespace rope {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kModeRH = ROPE_MODE_ROTATE_HALF;
+constexpr int kModeIL = ROPE_MODE_INTERLEAVE;
+
+// ---------------------------------------------------------------------------
+// fp32 <-> storage conversions. A 32-bit word holds two adjacent 16-bit lanes
+// (lower lane in the low half). Widening is exact; narrowing rounds to nearest
+// even (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32), keeps fp16 subnormals and
+// NaNs, and overflows to infinity.
+// ---------------------------------------------------------------------------
+template <int DT> struct Store;
+
+template <> struct Store<ROPE_DTYPE_BF16> {
+    static constexpr int kLanes = 8;  // per 16-byte vector
+    __device__ static f32x2 widen(uint32_t w)
+    {
+        f32x2 r;
+        r.x = __uint_as_float(w << 16);
+        r.y = __uint_as_float(w & 0xffff0000u);
+        return r;
+    }
+    __device__ static uint32_t narrow(f32x2 v)
+    {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    }
+    __device__ static float load1(const void* p, int64_t i)
+    {
+        return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
+    }
+    __device__ static void store1(void* p, int64_t i, float v)
+    {
+        static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+    }
+};
+
+template <> struct Store<ROPE_DTYPE_F16> {
+    static constexpr int kLanes = 8;
+    __device__ static f32x2 widen(uint32_t w)
+    {
+        return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
+    }
+    __device__ static uint32_t narrow(f32x2 v)
+    {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    }
+    __device__ static float load1(const void* p, int64_t i)
+    {
+        return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+    }
+    __device__ static void store1(void* p, int64_t i, float v)
+    {
+        static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
+    }
+};
+
+template <> struct Store<ROPE_DTYPE_F32> {
+    static constexpr int kLanes = 4;
+    __device__ static float load1(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
+    __device__ static void store1(void* p, int64_t i, float v) { static_cast<float*>(p)[i] = v; }
+};
+
+// A 16-byte vector of lanes as fp32 values.
+template <int DT>
+struct Lanes {
+    float v[Store<DT>::kLanes];
+    __device__ void unpack(const uint4& q)
+    {
+        if constexpr (DT == ROPE_DTYPE_F32) {
+            v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+            v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+        } else {
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                f32x2 f = Store<DT>::widen(w[k]);
+                v[2 * k] = f.x;
+                v[2 * k + 1] = f.y;
+            }
+        }
+    }
+    __device__ uint4 pack() const
+    {
+        if constexpr (DT == ROPE_DTYPE_F32) {
+            return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
+                              __float_as_uint(v[2]), __float_as_uint(v[3]));
+        } else {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                f32x2 f;
+                f.x = v[2 * k];
+                f.y = v[2 * k + 1];
+                w[k] = Store<DT>::narrow(f);
+            }
+            return make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// The rotation of one pair (a, b) = (x_j, x_p(j)) where j is the lane whose
+// partner term is negated in the forward (even lane / first half):
+//   forward : a' = a*c_a - b*s_a        b' = b*c_b + a*s_b
+//   backward: a' = a*c_a + b*s_b        b' = b*c_b - a*s_a   (transpose)
+// Both products of a 16-bit pair are exact in fp32, so the single fp32
+// rounding of the sum (fused or not) is the only rounding before the store.
+// ---------------------------------------------------------------------------
+template <int DIR>
+__device__ __forceinline__ void rotate_pair(float& a, float& b, float ca, float sa, float cb, float sb)
+{
+    float na, nb;
+    if constexpr (DIR == kFwd) {
+        na = a * ca - b * sa;
+        nb = b * cb + a * sb;
+    } else {
+        na = a * ca + b * sb;
+        nb = b * cb - a * sa;
+    }
+    a = na;
+    b = nb;
+}
+
+// ---------------------------------------------------------------------------
+// Vector kernel. Work unit = one 16-byte vector of the slice (interleave:
+// whole pairs inside it) or, for rotate_half, vector k of the first half plus
+// vector k of the second half (lanes i and i+L/2 in matching positions).
+//
+// Tile = one (b,s) position and a chunk of HL*U heads. Thread t of a block
+// takes work vector v = t % nvec and head lane hl = t / nvec, and handles
+// heads n = chunk*HL*U + hl + k*HL for k < U, issuing all U loads before any
+// arithmetic. Blocks stride over tiles (a persistent grid sized to the CUs).
+// ---------------------------------------------------------------------------
+struct VecArgs {
+    uint4* x;               // x as 16-byte vectors
+    const uint4* r1;        // cos table as 16-byte vectors
+    const uint4* r2;        // sin table
+    int64_t row_vecs;       // vectors per row of x (D*esize/16)
+    int64_t start_vec;      // first slice vector within a row
+    int64_t half_vecs;      // rotate_half: vectors per half of the slice
+    int64_t t1b, t1s, t1n;  // cos strides in vectors (0 = broadcast)
+    int64_t t2b, t2s, t2n;  // sin strides in vectors
+    uint32_t S, N;
+    uint32_t nvec;          // work units per row
+    uint32_t HL;            // head lanes per block
+    uint32_t nchunk;        // head chunks per (b,s)
+    uint32_t tiles;         // B*S*nchunk
+};
+
+template <int DT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES>
+__global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
+{
+    constexpr int K = Store<DT>::kLanes;
+    const uint32_t t = threadIdx.x;
+    const uint32_t v = t % a.nvec;
+    const uint32_t hl = t / a.nvec;
+    if (hl >= a.HL) return;  // no barriers below, so idle threads may leave
+
+    for (uint32_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+        const uint32_t g = tile / a.nchunk;          // (b,s) position
+        const uint32_t chunk = tile - g * a.nchunk;
+        const uint32_t b = g / a.S;
+        const uint32_t s = g - b * a.S;
+        const uint32_t n0 = chunk * a.HL * U + hl;
+        const int64_t c_base = (int64_t)b * a.t1b + (int64_t)s * a.t1s + v;
+        const int64_t s_base = (int64_t)b * a.t2b + (int64_t)s * a.t2s + v;
+        const int64_t row0 = (int64_t)g * a.N;
+
+        uint4 xa[U], xb[U];
+        uint4 ca[U], sa[U], cb[U], sb[U];
+        bool live[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t n = n0 + (uint32_t)k * a.HL;
+            live[k] = n < a.N;
+            if (live[k]) {
+                const int64_t off = (row0 + n) * a.row_vecs + a.start_vec + v;
+                xa[k] = a.x[off];
+                if constexpr (MODE == kModeRH) xb[k] = a.x[off + a.half_vecs];
+                if constexpr (!HEADS_SHARE_TABLES) {
+                    ca[k] = a.r1[c_base + (int64_t)n * a.t1n];
+                    sa[k] = a.r2[s_base + (int64_t)n * a.t2n];
+                    if constexpr (MODE == kModeRH) {
+                        cb[k] = a.r1[c_base + (int64_t)n * a.t1n + a.half_vecs];
+                        sb[k] = a.r2[s_base + (int64_t)n * a.t2n + a.half_vecs];
+                    }
+                }
+            }
+        }
+        if constexpr (HEADS_SHARE_TABLES) {
+            ca[0] = a.r1[c_base];
+            sa[0] = a.r2[s_base];
+            if constexpr (MODE == kModeRH) {
+                cb[0] = a.r1[c_base + a.half_vecs];
+                sb[0] = a.r2[s_base + a.half_vecs];
+            }
+        }
+
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (!live[k]) continue;
+            const int kt = HEADS_SHARE_TABLES ? 0 : k;
+            const uint32_t n = n0 + (uint32_t)k * a.HL;
+            const int64_t off = (row0 + n) * a.row_vecs + a.start_vec + v;
+            Lanes<DT> X, C, S;
+            X.unpack(xa[k]);
+            C.unpack(ca[kt]);
+            S.unpack(sa[kt]);
+            if constexpr (MODE == kModeIL) {
+#pragma unroll
+                for (int i = 0; i < K; i += 2)
+                    rotate_pair<DIR>(X.v[i], X.v[i + 1], C.v[i], S.v[i], C.v[i + 1], S.v[i + 1]);
+                a.x[off] = X.pack();
+            } else {
+                Lanes<DT> X2, C2, S2;
+                X2.unpack(xb[k]);
+                C2.unpack(cb[kt]);
+                S2.unpack(sb[kt]);
+#pragma unroll
+                for (int i = 0; i < K; ++i)
+                    rotate_pair<DIR>(X.v[i], X2.v[i], C.v[i], S.v[i], C2.v[i], S2.v[i]);
+                a.x[off] = X.pack();
+                a.x[off + a.half_vecs] = X2.pack();
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scalar kernel: any alignment, any start parity, any slice length. One
+// thread per rotation pair; 64-bit indexing throughout.
+// ---------------------------------------------------------------------------
+struct ScalarArgs {
+    void* x;
+    const void* r1;
+    const void* r2;
+    int64_t S, N, D, start, L;
+    int64_t pairs;          // pairs per row = L/2
+    int64_t items;          // rows * pairs
+    int64_t t1b, t1s, t1n;  // cos strides in elements (0 = broadcast)
+    int64_t t2b, t2s, t2n;
+};
+
+template <int DT, int DIR, int MODE>
+__global__ void __launch_bounds__(256) rope_scalar_kernel(ScalarArgs a)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.items; i += stride) {
+        const int64_t row = i / a.pairs;
+        const int64_t q = i - row * a.pairs;
+        const int64_t j = MODE == kModeIL ? 2 * q : q;              // negated-partner lane
+        const int64_t pj = MODE == kModeIL ? 2 * q + 1 : q + a.L / 2;
+        const int64_t n = row % a.N;
+        const int64_t bs = row / a.N;
+        const int64_t s = bs % a.S;
+        const int64_t b = bs / a.S;
+        const int64_t xo = row * a.D + a.start;
+        const int64_t co = b * a.t1b + s * a.t1s + n * a.t1n;
+        const int64_t so = b * a.t2b + s * a.t2s + n * a.t2n;
+        float xa = Store<DT>::load1(a.x, xo + j);
+        float xb = Store<DT>::load1(a.x, xo + pj);
+        const float ca = Store<DT>::load1(a.r1, co + j), cb = Store<DT>::load1(a.r1, co + pj);
+        const float sa = Store<DT>::load1(a.r2, so + j), sb = Store<DT>::load1(a.r2, so + pj);
+        rotate_pair<DIR>(xa, xb, ca, sa, cb, sb);
+        Store<DT>::store1(a.x, xo + j, xa);
+        Store<DT>::store1(a.x, xo + pj, xb);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+thread_local std::string g_last_error;
+
+rope_status_t set_error(rope_status_t st, const std::string& msg)
+{
+    g_last_error = msg;
+    return st;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int cu_count(int dev)
+{
+    if (dev < 0 || dev >= kMaxDevices) return 256;
+    int v = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Launch shape of the vector kernel.
+struct VecConfig {
+    int U = 1;          // heads per thread per tile
+    uint32_t HL = 1;    // head lanes per block
+    uint32_t grid = 0;  // blocks; 0 = persistent default
+};
+
+// Can the 16-byte vector kernel run this plan? Fills the geometry of `a`.
+bool vec_geometry(const Plan& p, VecArgs* a)
+{
+    const int64_t es = p.esize;
+    if (!aligned16(p.x) || !aligned16(p.r1) || !aligned16(p.r2)) return false;
+    if ((p.D * es) % 16 || (p.start * es) % 16) return false;
+    const int64_t unit_bytes = p.mode == kModeIL ? p.L * es : (p.L / 2) * es;
+    if (unit_bytes % 16) return false;
+    for (int k = 0; k < 3; ++k)
+        if ((p.t1[k] * es) % 16 || (p.t2[k] * es) % 16) return false;
+    if (p.S >= (1ll << 31) || p.N >= (1ll << 31) || p.B * p.S >= (1ll << 31)) return false;
+    a->x = static_cast<uint4*>(p.x);
+    a->r1 = static_cast<const uint4*>(p.r1);
+    a->r2 = static_cast<const uint4*>(p.r2);
+    a->row_vecs = p.D * es / 16;
+    a->start_vec = p.start * es / 16;
+    a->half_vecs = p.mode == kModeRH ? (p.L / 2) * es / 16 : 0;
+    a->t1b = p.t1[0] * es / 16; a->t1s = p.t1[1] * es / 16; a->t1n = p.t1[2] * es / 16;
+    a->t2b = p.t2[0] * es / 16; a->t2s = p.t2[1] * es / 16; a->t2n = p.t2[2] * es / 16;
+    a->S = (uint32_t)p.S;
+    a->N = (uint32_t)p.N;
+    a->nvec = (uint32_t)(unit_bytes / 16);
+    return a->nvec >= 1 && a->nvec <= 256;
+}
+
+// Default launch shape: up to 256 threads per block, enough heads per thread
+// that one tile covers all heads of a (b,s) position when N is large.
+VecConfig default_vec_config(const VecArgs& a)
+{
+    VecConfig c;
+    const uint32_t hl_max = 256u / a.nvec;
+    int U = 1;
+    while (U < 8 && (uint64_t)hl_max * U < a.N) U *= 2;
+    c.U = U;
+    c.HL = (uint32_t)std::min<uint64_t>(hl_max, (a.N + U - 1) / U);
+    return c;
+}
+
+template <int DT, int DIR, int MODE, int U>
+hipError_t launch_vec_u(const VecArgs& a, bool share, dim3 grid, dim3 block, hipStream_t stream)
+{
+    void* args[] = {const_cast<VecArgs*>(&a)};
+    const void* fn = share ? reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, true>)
+                           : reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, false>);
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+template <int DT, int DIR, int MODE>
+hipError_t launch_vec_t(const VecArgs& a, int U, bool share, dim3 grid, dim3 block, hipStream_t stream)
+{
+    switch (U) {
+    case 1: return launch_vec_u<DT, DIR, MODE, 1>(a, share, grid, block, stream);
+    case 2: return launch_vec_u<DT, DIR, MODE, 2>(a, share, grid, block, stream);
+    case 4: return launch_vec_u<DT, DIR, MODE, 4>(a, share, grid, block, stream);
+    default: return launch_vec_u<DT, DIR, MODE, 8>(a, share, grid, block, stream);
+    }
+}
+
+template <int DT>
+hipError_t launch_vec_dt(const Plan& p, const VecArgs& a, int U, bool share, dim3 grid, dim3 block,
+                         hipStream_t stream)
+{
+    if (p.dir == kFwd)
+        return p.mode == kModeIL ? launch_vec_t<DT, kFwd, kModeIL>(a, U, share, grid, block, stream)
+                                 : launch_vec_t<DT, kFwd, kModeRH>(a, U, share, grid, block, stream);
+    return p.mode == kModeIL ? launch_vec_t<DT, kBwd, kModeIL>(a, U, share, grid, block, stream)
+                             : launch_vec_t<DT, kBwd, kModeRH>(a, U, share, grid, block, stream);
+}
+
+// Complete `a` for a launch shape: head chunks and tile count. False if the
+// tile index could come near 32-bit wrap-around (the grid-stride loop adds
+// gridDim.x to it), in which case the scalar kernel runs instead.
+bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
+{
+    if (cfg.U < 1 || cfg.U > 8 || cfg.HL < 1 || (uint64_t)cfg.HL * a->nvec > 256) return false;
+    a->HL = cfg.HL;
+    const uint64_t heads_per_tile = (uint64_t)cfg.HL * cfg.U;
+    const uint64_t nchunk = (a->N + heads_per_tile - 1) / heads_per_tile;
+    const uint64_t tiles = (uint64_t)p.B * p.S * nchunk;
+    if (tiles >= (1ull << 31) || nchunk * heads_per_tile >= (1ull << 31)) return false;
+    a->nchunk = (uint32_t)nchunk;
+    a->tiles = (uint32_t)tiles;
+    return true;
+}
+
+// Launch the vector kernel; `a` is complete (vec_geometry + finish_vec_args).
+hipError_t launch_vec(const Plan& p, const VecArgs& a, const VecConfig& cfg, int cus, hipStream_t stream)
+{
+    const uint32_t threads = a.nvec * a.HL;
+    // Persistent grid: as many blocks as the CUs hold at once (2048 threads
+    // per CU), never more than there are tiles.
+    uint64_t grid = cfg.grid ? cfg.grid : (uint64_t)cus * (2048u / ((threads + 63) / 64 * 64));
+    grid = std::max<uint64_t>(1, std::min<uint64_t>(grid, a.tiles));
+    const bool share = p.t1[2] == 0 && p.t2[2] == 0;
+    const dim3 g((uint32_t)grid), b(threads);
+    switch (p.dtype) {
+    case ROPE_DTYPE_F32: return launch_vec_dt<ROPE_DTYPE_F32>(p, a, cfg.U, share, g, b, stream);
+    case ROPE_DTYPE_F16: return launch_vec_dt<ROPE_DTYPE_F16>(p, a, cfg.U, share, g, b, stream);
+    default: return launch_vec_dt<ROPE_DTYPE_BF16>(p, a, cfg.U, share, g, b, stream);
+    }
+}
+
+template <int DT, int DIR, int MODE>
+hipError_t launch_scalar_t(const ScalarArgs& a, dim3 grid, dim3 block, hipStream_t stream)
+{
+    void* args[] = {const_cast<ScalarArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&rope_scalar_kernel<DT, DIR, MODE>), grid, block,
+                           args, 0, stream);
+}
+
+template <int DT>
+hipError_t launch_scalar_dt(const Plan& p, const ScalarArgs& a, dim3 grid, dim3 block, hipStream_t stream)
+{
+    if (p.dir == kFwd)
+        return p.mode == kModeIL ? launch_scalar_t<DT, kFwd, kModeIL>(a, grid, block, stream)
+                                 : launch_scalar_t<DT, kFwd, kModeRH>(a, grid, block, stream);
+    return p.mode == kModeIL ? launch_scalar_t<DT, kBwd, kModeIL>(a, grid, block, stream)
+                             : launch_scalar_t<DT, kBwd, kModeRH>(a, grid, block, stream);
+}
+
+hipError_t launch_scalar(const Plan& p, int cus, hipStream_t stream)
+{
+    ScalarArgs a;
+    a.x = p.x; a.r1 = p.r1; a.r2 = p.r2;
+    a.S = p.S; a.N = p.N; a.D = p.D; a.start = p.start; a.L = p.L;
+    a.pairs = p.L / 2;
+    a.items = p.B * p.S * p.N * a.pairs;
+    a.t1b = p.t1[0]; a.t1s = p.t1[1]; a.t1n = p.t1[2];
+    a.t2b = p.t2[0]; a.t2s = p.t2[1]; a.t2n = p.t2[2];
+    const uint32_t threads = 256;
+    uint64_t grid = (uint64_t)cus * 8;
+    grid = std::max<uint64_t>(1, std::min<uint64_t>(grid, (a.items + threads - 1) / threads));
+    const dim3 g((uint32_t)grid), b(threads);
+    switch (p.dtype) {
+    case ROPE_DTYPE_F32: return launch_scalar_dt<ROPE_DTYPE_F32>(p, a, g, b, stream);
+    case ROPE_DTYPE_F16: return launch_scalar_dt<ROPE_DTYPE_F16>(p, a, g, b, stream);
+    default: return launch_scalar_dt<ROPE_DTYPE_BF16>(p, a, g, b, stream);
+    }
+}
+
+rope_status_t run(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                  const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                  const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                  rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                  void* stream, Direction dir)
+{
+    Plan p;
+    std::string why;
+    rope_status_t st = make_plan(x, x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides,
+                                 table_dtype, mode, partial_slice, dir, &p, &why);
+    if (st != ROPE_OK) return set_error(st, why);
+    if (p.noop) return ROPE_OK;
+
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("hipGetDevice: ") + hipGetErrorString(err));
+    const int cus = cu_count(dev);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    VecArgs a{};
+    VecConfig cfg;
+    if (vec_geometry(p, &a) && finish_vec_args(p, cfg = default_vec_config(a), &a))
+        err = launch_vec(p, a, cfg, cus, s);
+    else
+        err = launch_scalar(p, cus, s);
+    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
+    return ROPE_OK;
+}
+
+}  // namespace
+}  // namespace rope
+
+extern "C" {
+
+rope_status_t rope_partial_fwd_inplace(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                       const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                                       const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                                       rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                       void* stream)
+{
+    return rope::run(x, x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides, table_dtype, mode,
+                     partial_slice, stream, rope::kFwd);
+}
+
+rope_status_t rope_partial_bwd_inplace(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                       const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                                       const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                                       rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                       void* stream)
+{
+    return rope::run(x, x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides, table_dtype, mode,
+                     partial_slice, stream, rope::kBwd);
+}
+
+const char* rope_status_string(rope_status_t status)
+{
+    switch (status) {
+    case ROPE_OK: return "ROPE_OK: success";
+    case ROPE_ERR_NULLPTR: return "ROPE_ERR_NULLPTR: a required pointer is NULL";
+    case ROPE_ERR_INVALID: return "ROPE_ERR_INVALID: an argument violates the operation's constraints";
+    case ROPE_ERR_UNSUPPORTED: return "ROPE_ERR_UNSUPPORTED: valid arguments this library does not support";
+    case ROPE_ERR_RUNTIME: return "ROPE_ERR_RUNTIME: the HIP runtime reported an error";
+    default: return "unknown rope_status_t";
+    }
+}
+
+const char* rope_last_error(void)
+{
+    return rope::g_last_error.c_str();
+}
+
+}  // extern "C"
