@@ -63,18 +63,39 @@ def launch_fn(direction):
     return rp.rope_partial_fwd_inplace if direction == "fwd" else rp.rope_partial_bwd_inplace
 
 
-def time_launches(fn, args, n: int, stream) -> float:
-    """Average duration (s) of n back-to-back launches on `stream`, from HIP
-    events recorded on that same stream."""
+def time_launches(calls, n: int, stream) -> float:
+    """Average duration (s) of n back-to-back launches on `stream`, taking
+    the (fn, args) pairs of `calls` in turn, from HIP events recorded on that
+    same stream."""
     import torch
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
-    for _ in range(n):
+    for i in range(n):
+        fn, args = calls[i % len(calls)]
         fn(*args)
     end.record(stream)
     end.synchronize()
     return start.elapsed_time(end) / 1e3 / n
+
+
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache
+
+
+def slice_line_bytes(w, k: int = 0) -> int:
+    """Bytes of the 128-byte lines that one launch's slice touches in x."""
+    import workloads as W
+    B, S, N, D = w.x_shapes[k]
+    es = W.ESIZE[w.dtype]
+    lo = (w.partial_slice[0] * es) // 128 * 128
+    hi = -(-(w.partial_slice[1] * es) // 128) * 128
+    return B * S * N * (hi - lo)
+
+
+def rotating_copies(w) -> int:
+    """How many copies of x the timed launches rotate over so that each
+    launch reads lines the 256 MB MALL no longer holds (>= 3x its size)."""
+    return max(1, min(8, -(-(3 * MALL_BYTES) // slice_line_bytes(w))))
 
 
 def cpu_baseline(w, x_cpu, r1, r2, direction: str, budget_s: float) -> dict:
@@ -117,70 +138,85 @@ def bench_workload(name: str, steps: int, warmup: int, reps: int, stream, want_c
     w = W.WORKLOADS[name]
     x_cpu = W.make_x(w)
     r1, r2 = W.make_tables(w)
-    x = x_cpu.to("cuda")
+    ncopy = rotating_copies(w)
+    xs = [x_cpu.to("cuda")]
+    xs += [xs[0].clone() for _ in range(ncopy - 1)]
     r1d, r2d = r1.to("cuda"), r2.to("cuda")
     torch.cuda.synchronize()
     # a step runs both directions, the workload's own direction first
     dirs = list(w.directions) + [d for d in ("fwd", "bwd") if d not in w.directions]
-    calls = [(launch_fn(d), (x, r1d, r2d, w.mode, w.partial_slice)) for d in dirs]
+    step_calls = [(launch_fn(d), (None, r1d, r2d, w.mode, w.partial_slice)) for d in dirs]
 
-    for _ in range(warmup):
-        for fn, args in calls:
-            fn(*args)
+    def launches(i0, n):
+        # launch j works on copy j % ncopy: no launch finds its data in a cache
+        for j in range(i0, i0 + n):
+            fn, args = step_calls[j % len(dirs)]
+            fn(xs[j % ncopy], *args[1:])
+
+    launches(0, warmup * len(dirs))
     torch.cuda.synchronize()
-    # whole steps (every direction once per step)
     t_start = time.perf_counter()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record(stream)
-    for _ in range(steps):
-        for fn, args in calls:
-            fn(*args)
+    launches(0, steps * len(dirs))
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     step_s = ev0.elapsed_time(ev1) / 1e3 / steps
-    # per-kernel average launch durations
-    per_launch = {}
-    for d, (fn, args) in zip(dirs, calls):
-        per_launch[d] = time_launches(fn, args, reps, stream)
+    # per-kernel average launch durations: rotating copies (data from HBM),
+    # and back to back on one buffer (what caches keep of it is reused)
+    per_launch, warm = {}, {}
+    for d in dirs:
+        fn = launch_fn(d)
+        cold = [(fn, (xs[i], r1d, r2d, w.mode, w.partial_slice)) for i in range(ncopy)]
+        time_launches(cold, max(4, reps // 4), stream)  # untimed: settle clocks after the host gap
+        per_launch[d] = time_launches(cold, reps, stream)
+        warm[d] = time_launches(cold[:1], reps, stream)
     bytes_launch = w.algorithmic_bytes()
     elems_launch = w.rotated_elements()
     out = {
         "workload": name, "note": w.note, "x_shape": list(w.x_shapes[0]), "dtype": w.dtype,
         "slice": list(w.partial_slice), "mode": w.mode, "table_shape": list(w.table_shape),
-        "directions": dirs, "step_s": step_s, "wall_s": wall,
+        "directions": dirs, "step_s": step_s, "wall_s": wall, "rotating_copies": ncopy,
         "bytes_per_launch": bytes_launch, "elements_per_launch": elems_launch,
         "kernels": {d: {"avg_launch_us": round(t * 1e6, 3),
                         "GBps": round(bytes_launch / t / 1e9, 1),
                         "Gelem_per_s": round(elems_launch / t / 1e9, 1),
-                        "frac_of_peak": round(bytes_launch / t / 1e9 / PEAK_GBPS, 4)}
+                        "frac_of_peak": round(bytes_launch / t / 1e9 / PEAK_GBPS, 4),
+                        "same_buffer_avg_launch_us": round(warm[d] * 1e6, 3)}
                     for d, t in per_launch.items()},
     }
     if want_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x_cpu, r1, r2, dirs[0], cpu_s)
-    del x, x_cpu
+    del xs, x_cpu
+    torch.cuda.empty_cache()
     return out
 
 
 def profile_target(name: str, reps: int) -> None:
-    """Launches for rocprofv3 counter passes: the workload's kernels, then a
-    plain device copy of known size for calibrating the byte counters."""
+    """Launches for rocprofv3 counter passes: each direction of the workload
+    `reps` times (rotating copies as in the timed run), then a plain device
+    copy of known size for calibrating the byte counters."""
     import torch
 
     import workloads as W
     w = W.WORKLOADS[name]
-    x = W.make_x(w).to("cuda")
+    ncopy = rotating_copies(w)
+    xs = [W.make_x(w).to("cuda")]
+    xs += [xs[0].clone() for _ in range(ncopy - 1)]
     r1, r2 = (t.to("cuda") for t in W.make_tables(w))
-    for d in w.directions:
-        for _ in range(reps):
-            launch_fn(d)(x, r1, r2, w.mode, w.partial_slice)
+    dirs = list(w.directions) + [d for d in ("fwd", "bwd") if d not in w.directions]
+    for d in dirs:
+        for i in range(reps):
+            launch_fn(d)(xs[i % ncopy], r1, r2, w.mode, w.partial_slice)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")  # 256 MiB
     src.fill_(1)
     dst = torch.empty_like(src)
     for _ in range(reps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_target": name, "reps": reps, "copy_bytes": src.numel()}), flush=True)
+    print(json.dumps({"profile_target": name, "reps": reps, "copy_bytes": src.numel(),
+                      "rotating_copies": ncopy}), flush=True)
 
 
 def main() -> int:
@@ -219,8 +255,8 @@ def main() -> int:
     others = []
     for name in [n for n in args.also.split(",") if n and n != args.workload]:
         r = bench_workload(name, max(5, args.steps // 5), 2, max(10, args.reps // 2), stream, False, 0)
-        others.append({k: r[k] for k in ("workload", "note", "dtype", "directions", "bytes_per_launch",
-                                         "elements_per_launch", "kernels")})
+        others.append({k: r[k] for k in ("workload", "note", "dtype", "directions", "rotating_copies",
+                                         "bytes_per_launch", "elements_per_launch", "kernels")})
 
     import workloads as W
     w = W.WORKLOADS[args.workload]
@@ -245,7 +281,8 @@ def main() -> int:
         "dtype": w.dtype, "data": "synthetic (seeded; shapes and tables as the workload states)",
         "config": {"workload": f"{args.workload}: {w.note}", "x_shape": main_res["x_shape"],
                    "slice": main_res["slice"], "mode": w.mode, "table_shape": main_res["table_shape"],
-                   "directions_per_step": main_res["directions"], "parallelism": "single GPU"},
+                   "directions_per_step": main_res["directions"], "parallelism": "single GPU",
+                   "rotating_copies": main_res["rotating_copies"]},
         "gelem_per_s": round(step_elems / main_res["step_s"] / 1e9, 1),
         "pct_of_peak": round(100 * value / PEAK_GBPS, 2),
         "roofline": roofline,

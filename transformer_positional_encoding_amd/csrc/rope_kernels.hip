@@ -36,6 +36,7 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // one 16-byte vector
 
 constexpr int kModeRH = ROPE_MODE_ROTATE_HALF;
 constexpr int kModeIL = ROPE_MODE_INTERLEAVE;
@@ -101,13 +102,13 @@ template <> struct Store<ROPE_DTYPE_F32> {
 template <int DT>
 struct Lanes {
     float v[Store<DT>::kLanes];
-    __device__ void unpack(const uint4& q)
+    __device__ void unpack(const v4u& q)
     {
         if constexpr (DT == ROPE_DTYPE_F32) {
-            v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
-            v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+            v[0] = __uint_as_float(q[0]); v[1] = __uint_as_float(q[1]);
+            v[2] = __uint_as_float(q[2]); v[3] = __uint_as_float(q[3]);
         } else {
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+            const uint32_t w[4] = {q[0], q[1], q[2], q[3]};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 f32x2 f = Store<DT>::widen(w[k]);
@@ -116,11 +117,11 @@ struct Lanes {
             }
         }
     }
-    __device__ uint4 pack() const
+    __device__ v4u pack() const
     {
         if constexpr (DT == ROPE_DTYPE_F32) {
-            return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]),
-                              __float_as_uint(v[2]), __float_as_uint(v[3]));
+            return v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                       __float_as_uint(v[3])};
         } else {
             uint32_t w[4];
 #pragma unroll
@@ -130,7 +131,7 @@ struct Lanes {
                 f.y = v[2 * k + 1];
                 w[k] = Store<DT>::narrow(f);
             }
-            return make_uint4(w[0], w[1], w[2], w[3]);
+            return v4u{w[0], w[1], w[2], w[3]};
         }
     }
 };
@@ -163,15 +164,36 @@ __device__ __forceinline__ void rotate_pair(float& a, float& b, float ca, float 
 // whole pairs inside it) or, for rotate_half, vector k of the first half plus
 // vector k of the second half (lanes i and i+L/2 in matching positions).
 //
-// Tile = one (b,s) position and a chunk of HL*U heads. Thread t of a block
-// takes work vector v = t % nvec and head lane hl = t / nvec, and handles
-// heads n = chunk*HL*U + hl + k*HL for k < U, issuing all U loads before any
-// arithmetic. Blocks stride over tiles (a persistent grid sized to the CUs).
+// Tile = one (b,s) position and a chunk of HL*U heads. A block works on GL
+// tiles at a time; thread t takes work vector v = t % nvec, head lane
+// hl = (t / nvec) % HL and tile lane gl = t / (nvec*HL), and handles heads
+// n = chunk*HL*U + hl + k*HL for k < U. The cos/sin vectors of a thread are
+// loaded once per tile and, when the tables broadcast over heads, reused for
+// all its heads. All loads of a tile are issued before any arithmetic. The
+// grid normally has one block per group of GL tiles; a smaller grid makes
+// the blocks stride over the groups.
 // ---------------------------------------------------------------------------
+// x is streamed (each slice byte is read once and written once); the tables
+// are re-read by every head and stay in the caches. NT selects nontemporal
+// (streaming) loads and stores for x.
+template <bool NT>
+__device__ __forceinline__ v4u load_x(const v4u* p)
+{
+    if constexpr (NT) return __builtin_nontemporal_load(p);
+    else return *p;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store_x(v4u* p, v4u v)
+{
+    if constexpr (NT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
 struct VecArgs {
-    uint4* x;               // x as 16-byte vectors
-    const uint4* r1;        // cos table as 16-byte vectors
-    const uint4* r2;        // sin table
+    v4u* x;                 // x as 16-byte vectors
+    const v4u* r1;          // cos table as 16-byte vectors
+    const v4u* r2;          // sin table
     int64_t row_vecs;       // vectors per row of x (D*esize/16)
     int64_t start_vec;      // first slice vector within a row
     int64_t half_vecs;      // rotate_half: vectors per half of the slice
@@ -179,21 +201,41 @@ struct VecArgs {
     int64_t t2b, t2s, t2n;  // sin strides in vectors
     uint32_t S, N;
     uint32_t nvec;          // work units per row
-    uint32_t HL;            // head lanes per block
+    uint32_t HL;            // head lanes per tile
+    uint32_t GL;            // tiles per block iteration
     uint32_t nchunk;        // head chunks per (b,s)
     uint32_t tiles;         // B*S*nchunk
+    uint32_t btiles;        // ceil(tiles / GL)
+    uint32_t xcd_remap;     // 1: give each XCD a contiguous range of tile groups
 };
 
-template <int DT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES>
+// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
+// XCD i % 8), and each XCD has its own L2. Neighbouring tiles share table
+// rows (the head chunks of one (b,s) position, or one s across batches), so
+// renumber the blocks so that XCD x processes a contiguous range of tile
+// groups: the table rows of a range are then fetched into one L2 only.
+// The map is a bijection of [0, G).
+__device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t bid, uint32_t G)
+{
+    constexpr uint32_t kXcds = 8;
+    const uint32_t q = G / kXcds, r = G % kXcds, x = bid % kXcds;
+    return x * q + min(x, r) + bid / kXcds;
+}
+
+template <int DT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
 __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
 {
     constexpr int K = Store<DT>::kLanes;
     const uint32_t t = threadIdx.x;
     const uint32_t v = t % a.nvec;
-    const uint32_t hl = t / a.nvec;
-    if (hl >= a.HL) return;  // no barriers below, so idle threads may leave
+    const uint32_t hl = (t / a.nvec) % a.HL;
+    const uint32_t gl = t / (a.nvec * a.HL);
+    if (gl >= a.GL) return;  // no barriers below, so idle threads may leave
 
-    for (uint32_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
+    const uint32_t first = a.xcd_remap ? xcd_contiguous_block(blockIdx.x, gridDim.x) : blockIdx.x;
+    for (uint32_t bt = first; bt < a.btiles; bt += gridDim.x) {
+        const uint32_t tile = bt * a.GL + gl;
+        if (tile >= a.tiles) continue;
         const uint32_t g = tile / a.nchunk;          // (b,s) position
         const uint32_t chunk = tile - g * a.nchunk;
         const uint32_t b = g / a.S;
@@ -203,27 +245,13 @@ __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
         const int64_t s_base = (int64_t)b * a.t2b + (int64_t)s * a.t2s + v;
         const int64_t row0 = (int64_t)g * a.N;
 
-        uint4 xa[U], xb[U];
-        uint4 ca[U], sa[U], cb[U], sb[U];
+        // All loads are issued back to back with no branch between them: a
+        // head past N (ragged last chunk) re-reads row N-1 and skips its
+        // store. The tables come first, then the x vectors.
+        v4u xa[U], xb[U];
+        v4u ca[U], sa[U], cb[U], sb[U];
+        int64_t off[U];
         bool live[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const uint32_t n = n0 + (uint32_t)k * a.HL;
-            live[k] = n < a.N;
-            if (live[k]) {
-                const int64_t off = (row0 + n) * a.row_vecs + a.start_vec + v;
-                xa[k] = a.x[off];
-                if constexpr (MODE == kModeRH) xb[k] = a.x[off + a.half_vecs];
-                if constexpr (!HEADS_SHARE_TABLES) {
-                    ca[k] = a.r1[c_base + (int64_t)n * a.t1n];
-                    sa[k] = a.r2[s_base + (int64_t)n * a.t2n];
-                    if constexpr (MODE == kModeRH) {
-                        cb[k] = a.r1[c_base + (int64_t)n * a.t1n + a.half_vecs];
-                        sb[k] = a.r2[s_base + (int64_t)n * a.t2n + a.half_vecs];
-                    }
-                }
-            }
-        }
         if constexpr (HEADS_SHARE_TABLES) {
             ca[0] = a.r1[c_base];
             sa[0] = a.r2[s_base];
@@ -232,13 +260,32 @@ __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
                 sb[0] = a.r2[s_base + a.half_vecs];
             }
         }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t n = n0 + (uint32_t)k * a.HL;
+            live[k] = n < a.N;
+            const uint32_t nl = live[k] ? n : a.N - 1;
+            off[k] = (row0 + nl) * a.row_vecs + a.start_vec + v;
+            if constexpr (!HEADS_SHARE_TABLES) {
+                ca[k] = a.r1[c_base + (int64_t)nl * a.t1n];
+                sa[k] = a.r2[s_base + (int64_t)nl * a.t2n];
+                if constexpr (MODE == kModeRH) {
+                    cb[k] = a.r1[c_base + (int64_t)nl * a.t1n + a.half_vecs];
+                    sb[k] = a.r2[s_base + (int64_t)nl * a.t2n + a.half_vecs];
+                }
+            }
+            xa[k] = load_x<NT>(a.x + off[k]);
+            if constexpr (MODE == kModeRH) xb[k] = load_x<NT>(a.x + off[k] + a.half_vecs);
+        }
+        // Keep every load above in flight together: without this barrier the
+        // machine scheduler starts the arithmetic on the first vectors and
+        // issues the remaining loads only after waiting for them.
+        __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             if (!live[k]) continue;
             const int kt = HEADS_SHARE_TABLES ? 0 : k;
-            const uint32_t n = n0 + (uint32_t)k * a.HL;
-            const int64_t off = (row0 + n) * a.row_vecs + a.start_vec + v;
             Lanes<DT> X, C, S;
             X.unpack(xa[k]);
             C.unpack(ca[kt]);
@@ -247,7 +294,7 @@ __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
 #pragma unroll
                 for (int i = 0; i < K; i += 2)
                     rotate_pair<DIR>(X.v[i], X.v[i + 1], C.v[i], S.v[i], C.v[i + 1], S.v[i + 1]);
-                a.x[off] = X.pack();
+                store_x<NT>(a.x + off[k], X.pack());
             } else {
                 Lanes<DT> X2, C2, S2;
                 X2.unpack(xb[k]);
@@ -256,8 +303,8 @@ __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
 #pragma unroll
                 for (int i = 0; i < K; ++i)
                     rotate_pair<DIR>(X.v[i], X2.v[i], C.v[i], S.v[i], C2.v[i], S2.v[i]);
-                a.x[off] = X.pack();
-                a.x[off + a.half_vecs] = X2.pack();
+                store_x<NT>(a.x + off[k], X.pack());
+                store_x<NT>(a.x + off[k] + a.half_vecs, X2.pack());
             }
         }
     }
@@ -334,9 +381,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Launch shape of the vector kernel.
 struct VecConfig {
-    int U = 1;          // heads per thread per tile
-    uint32_t HL = 1;    // head lanes per block
-    uint32_t grid = 0;  // blocks; 0 = persistent default
+    int U = 1;          // heads per thread per tile (loads in flight per thread)
+    uint32_t HL = 1;    // head lanes per tile
+    uint32_t GL = 1;    // tiles per block iteration
+    uint32_t grid = 0;  // blocks; 0 = one block per tile group
+    bool xcd_remap = true;
+    bool nt = false;    // nontemporal loads/stores of x
 };
 
 // Can the 16-byte vector kernel run this plan? Fills the geometry of `a`.
@@ -350,9 +400,9 @@ bool vec_geometry(const Plan& p, VecArgs* a)
     for (int k = 0; k < 3; ++k)
         if ((p.t1[k] * es) % 16 || (p.t2[k] * es) % 16) return false;
     if (p.S >= (1ll << 31) || p.N >= (1ll << 31) || p.B * p.S >= (1ll << 31)) return false;
-    a->x = static_cast<uint4*>(p.x);
-    a->r1 = static_cast<const uint4*>(p.r1);
-    a->r2 = static_cast<const uint4*>(p.r2);
+    a->x = static_cast<v4u*>(p.x);
+    a->r1 = static_cast<const v4u*>(p.r1);
+    a->r2 = static_cast<const v4u*>(p.r2);
     a->row_vecs = p.D * es / 16;
     a->start_vec = p.start * es / 16;
     a->half_vecs = p.mode == kModeRH ? (p.L / 2) * es / 16 : 0;
@@ -364,81 +414,105 @@ bool vec_geometry(const Plan& p, VecArgs* a)
     return a->nvec >= 1 && a->nvec <= 256;
 }
 
-// Default launch shape: up to 256 threads per block, enough heads per thread
-// that one tile covers all heads of a (b,s) position when N is large.
-VecConfig default_vec_config(const VecArgs& a)
+// Launch shape for U heads per thread and a target block size: head lanes
+// cover the heads of a (b,s) position up to the block size, and the rest of
+// the block takes further tiles.
+VecConfig shape_for(const VecArgs& a, int U, uint32_t threads)
 {
     VecConfig c;
-    const uint32_t hl_max = 256u / a.nvec;
-    int U = 1;
-    while (U < 8 && (uint64_t)hl_max * U < a.N) U *= 2;
     c.U = U;
+    const uint32_t hl_max = std::max<uint32_t>(1, threads / a.nvec);
     c.HL = (uint32_t)std::min<uint64_t>(hl_max, (a.N + U - 1) / U);
+    c.GL = std::max<uint32_t>(1, threads / (a.nvec * c.HL));
     return c;
 }
 
-template <int DT, int DIR, int MODE, int U>
-hipError_t launch_vec_u(const VecArgs& a, bool share, dim3 grid, dim3 block, hipStream_t stream)
+// The launch shape. Measured on MI355X with every launch reading data that
+// no cache holds (the slices of several shapes: 1/3 and 1/2 of the row,
+// whole and half 128-byte lines, bf16 and fp32, tables shared or per batch),
+// sweeping heads per thread (1-8), block size (64-256), nontemporal x and
+// XCD renumbering: one head per thread, 64-thread blocks, nontemporal x and
+// XCD-contiguous blocks was within 3% of the best shape on every one.
+// Streaming x past the caches leaves the L2 to the tables, and small blocks
+// let the dispatcher keep every CU's load queues full.
+VecConfig choose_vec_config(const Plan& p, const VecArgs& a)
 {
-    void* args[] = {const_cast<VecArgs*>(&a)};
-    const void* fn = share ? reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, true>)
-                           : reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, false>);
-    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+    (void)p;
+    VecConfig c = shape_for(a, 1, 64);
+    c.nt = true;
+    c.xcd_remap = true;
+    return c;
 }
 
-template <int DT, int DIR, int MODE>
-hipError_t launch_vec_t(const VecArgs& a, int U, bool share, dim3 grid, dim3 block, hipStream_t stream)
-{
-    switch (U) {
-    case 1: return launch_vec_u<DT, DIR, MODE, 1>(a, share, grid, block, stream);
-    case 2: return launch_vec_u<DT, DIR, MODE, 2>(a, share, grid, block, stream);
-    case 4: return launch_vec_u<DT, DIR, MODE, 4>(a, share, grid, block, stream);
-    default: return launch_vec_u<DT, DIR, MODE, 8>(a, share, grid, block, stream);
-    }
-}
-
-template <int DT>
-hipError_t launch_vec_dt(const Plan& p, const VecArgs& a, int U, bool share, dim3 grid, dim3 block,
-                         hipStream_t stream)
-{
-    if (p.dir == kFwd)
-        return p.mode == kModeIL ? launch_vec_t<DT, kFwd, kModeIL>(a, U, share, grid, block, stream)
-                                 : launch_vec_t<DT, kFwd, kModeRH>(a, U, share, grid, block, stream);
-    return p.mode == kModeIL ? launch_vec_t<DT, kBwd, kModeIL>(a, U, share, grid, block, stream)
-                             : launch_vec_t<DT, kBwd, kModeRH>(a, U, share, grid, block, stream);
-}
-
-// Complete `a` for a launch shape: head chunks and tile count. False if the
+// Complete `a` for a launch shape: head chunks and tile counts. False if a
 // tile index could come near 32-bit wrap-around (the grid-stride loop adds
 // gridDim.x to it), in which case the scalar kernel runs instead.
 bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
 {
-    if (cfg.U < 1 || cfg.U > 8 || cfg.HL < 1 || (uint64_t)cfg.HL * a->nvec > 256) return false;
+    if (cfg.U < 1 || cfg.U > 4 || (cfg.U & (cfg.U - 1)) || cfg.HL < 1 || cfg.GL < 1 ||
+        (uint64_t)cfg.HL * cfg.GL * a->nvec > 256)
+        return false;
     a->HL = cfg.HL;
+    a->GL = cfg.GL;
     const uint64_t heads_per_tile = (uint64_t)cfg.HL * cfg.U;
     const uint64_t nchunk = (a->N + heads_per_tile - 1) / heads_per_tile;
     const uint64_t tiles = (uint64_t)p.B * p.S * nchunk;
     if (tiles >= (1ull << 31) || nchunk * heads_per_tile >= (1ull << 31)) return false;
     a->nchunk = (uint32_t)nchunk;
     a->tiles = (uint32_t)tiles;
+    a->btiles = (uint32_t)((tiles + cfg.GL - 1) / cfg.GL);
+    a->xcd_remap = cfg.xcd_remap ? 1u : 0u;
     return true;
 }
 
-// Launch the vector kernel; `a` is complete (vec_geometry + finish_vec_args).
-hipError_t launch_vec(const Plan& p, const VecArgs& a, const VecConfig& cfg, int cus, hipStream_t stream)
+template <int DT, int DIR, int MODE, int U>
+const void* vec_kernel_u(bool share, bool nt)
 {
-    const uint32_t threads = a.nvec * a.HL;
-    // Persistent grid: as many blocks as the CUs hold at once (2048 threads
-    // per CU), never more than there are tiles.
-    uint64_t grid = cfg.grid ? cfg.grid : (uint64_t)cus * (2048u / ((threads + 63) / 64 * 64));
-    grid = std::max<uint64_t>(1, std::min<uint64_t>(grid, a.tiles));
-    const bool share = p.t1[2] == 0 && p.t2[2] == 0;
-    const dim3 g((uint32_t)grid), b(threads);
-    switch (p.dtype) {
-    case ROPE_DTYPE_F32: return launch_vec_dt<ROPE_DTYPE_F32>(p, a, cfg.U, share, g, b, stream);
-    case ROPE_DTYPE_F16: return launch_vec_dt<ROPE_DTYPE_F16>(p, a, cfg.U, share, g, b, stream);
-    default: return launch_vec_dt<ROPE_DTYPE_BF16>(p, a, cfg.U, share, g, b, stream);
+    if (share)
+        return nt ? reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, true, true>)
+                  : reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, true, false>);
+    return nt ? reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, false, true>)
+              : reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, false, false>);
+}
+
+template <int DT, int DIR, int MODE>
+const void* vec_kernel_m(int U, bool share, bool nt)
+{
+    switch (U) {
+    case 1: return vec_kernel_u<DT, DIR, MODE, 1>(share, nt);
+    case 2: return vec_kernel_u<DT, DIR, MODE, 2>(share, nt);
+    default: return vec_kernel_u<DT, DIR, MODE, 4>(share, nt);
     }
+}
+
+template <int DT>
+const void* vec_kernel_dt(int dir, int mode, int U, bool share, bool nt)
+{
+    if (dir == kFwd)
+        return mode == kModeIL ? vec_kernel_m<DT, kFwd, kModeIL>(U, share, nt)
+                               : vec_kernel_m<DT, kFwd, kModeRH>(U, share, nt);
+    return mode == kModeIL ? vec_kernel_m<DT, kBwd, kModeIL>(U, share, nt)
+                           : vec_kernel_m<DT, kBwd, kModeRH>(U, share, nt);
+}
+
+// Launch the vector kernel; `a` is complete (vec_geometry + finish_vec_args).
+hipError_t launch_vec(const Plan& p, const VecArgs& a, const VecConfig& cfg, hipStream_t stream)
+{
+    const uint32_t threads = a.nvec * a.HL * a.GL;
+    // One block per tile group by default: measured faster on MI355X than a
+    // persistent grid for these streaming shapes (the dispatcher keeps every
+    // CU full and no loop-carried dependence serialises the loads).
+    uint64_t grid = cfg.grid ? cfg.grid : a.btiles;
+    grid = std::max<uint64_t>(1, std::min<uint64_t>(grid, a.btiles));
+    const bool share = p.t1[2] == 0 && p.t2[2] == 0;
+    const void* fn;
+    switch (p.dtype) {
+    case ROPE_DTYPE_F32: fn = vec_kernel_dt<ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt); break;
+    case ROPE_DTYPE_F16: fn = vec_kernel_dt<ROPE_DTYPE_F16>(p.dir, p.mode, cfg.U, share, cfg.nt); break;
+    default: fn = vec_kernel_dt<ROPE_DTYPE_BF16>(p.dir, p.mode, cfg.U, share, cfg.nt); break;
+    }
+    void* args[] = {const_cast<VecArgs*>(&a)};
+    return hipLaunchKernel(fn, dim3((uint32_t)grid), dim3(threads), args, 0, stream);
 }
 
 template <int DT, int DIR, int MODE>
@@ -500,8 +574,8 @@ rope_status_t run(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
 
     VecArgs a{};
     VecConfig cfg;
-    if (vec_geometry(p, &a) && finish_vec_args(p, cfg = default_vec_config(a), &a))
-        err = launch_vec(p, a, cfg, cus, s);
+    if (vec_geometry(p, &a) && finish_vec_args(p, cfg = choose_vec_config(p, a), &a))
+        err = launch_vec(p, a, cfg, s);
     else
         err = launch_scalar(p, cus, s);
     if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
