@@ -222,8 +222,8 @@ def profile_target(name: str, reps: int) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--also", default="c3,c4_f32",
                     help="other workloads measured in the same run (reported under 'other_workloads')")

@@ -1,0 +1,49 @@
+"""Host-side logic of the HIP path that runs without a GPU: the launch-time
+fast division behind the kernels' index math, and the bench's buffer
+rotation and traffic bookkeeping."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "transformer_positional_encoding_amd", "csrc")
+
+
+def test_fast_division_exact(tmp_path):
+    exe = tmp_path / "fastdiv_check"
+    subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC,
+                    os.path.join(ROOT, "tests", "host_checks", "fastdiv_check.cpp"), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "bad 0" in out.stdout
+
+
+def test_bench_rotation_and_line_bytes():
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads as W
+    # c3: one 128-byte line of a 384-byte row per row; c4 bf16: two lines (straddle)
+    assert bench.slice_line_bytes(W.WORKLOADS["c3"]) == 4 * 4096 * 128 * 128
+    assert bench.slice_line_bytes(W.WORKLOADS["c4"]) == 16 * 8192 * 32 * 256
+    assert bench.rotating_copies(W.WORKLOADS["c3"]) == 3
+    assert bench.rotating_copies(W.WORKLOADS["c4"]) == 1
+
+
+def test_bench_refuses_more_than_one_gpu():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True)
+    assert res.returncode == 2 and "one GPU" in res.stderr
+
+
+def test_traffic_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
+    sys.path.insert(0, ROOT)
+    import bench
+    md = tmp_path / "t.md"
+    md.write_text('```json\n{"kernel_source_sha256_16": "%s", "launches": {"c4:bwd": {"hbm_bytes_per_launch": 5}}}\n```\n'
+                  % bench.kernel_source_hash())
+    monkeypatch.setattr(bench, "TRAFFIC_MD", str(md))
+    assert bench.committed_traffic("c4", "bwd")["hbm_bytes_per_launch"] == 5
+    md.write_text('```json\n{"kernel_source_sha256_16": "0000", "launches": {"c4:bwd": {"hbm_bytes_per_launch": 5}}}\n```\n')
+    assert bench.committed_traffic("c4", "bwd") is None

@@ -27,6 +27,7 @@
 #include <atomic>
 #include <string>
 
+#include "rope_fastdiv.hpp"
 #include "rope_partial.h"
 #include "rope_plan.hpp"
 
@@ -165,9 +166,15 @@ __device__ __forceinline__ void rotate_pair(float& a, float& b, float ca, float 
 // vector k of the second half (lanes i and i+L/2 in matching positions).
 //
 // Tile = one (b,s) position and a chunk of HL*U heads. A block works on GL
-// tiles at a time; thread t takes work vector v = t % nvec, head lane
-// hl = (t / nvec) % HL and tile lane gl = t / (nvec*HL), and handles heads
-// n = chunk*HL*U + hl + k*HL for k < U. The cos/sin vectors of a thread are
+// tiles at a time; thread t takes row vector c = lo_vec + t % span, head
+// lane hl = (t / span) % HL and tile lane gl = t / (span*HL), and handles
+// heads n = chunk*HL*U + hl + k*HL for k < U. Normally the threads cover
+// exactly the slice (lo_vec = start_vec, span = nvec). When the slice covers
+// only part of its first or last 128-byte line, the threads of an interleave
+// row cover every vector of those lines instead: each line is then requested
+// whole by one wave instruction, which the L2 serves much faster than two
+// half-line requests (it fetches the whole line either way); vectors outside
+// the slice are loaded and dropped, never stored. The cos/sin vectors of a thread are
 // loaded once per tile and, when the tables broadcast over heads, reused for
 // all its heads. All loads of a tile are issued before any arithmetic. The
 // grid normally has one block per group of GL tiles; a smaller grid makes
@@ -190,23 +197,28 @@ __device__ __forceinline__ void store_x(v4u* p, v4u v)
     else *p = v;
 }
 
+// Offsets are in 16-byte vectors and 32-bit: the host runs this kernel only
+// when x and each table span fewer than 2^32 vectors (64 GiB).
 struct VecArgs {
     v4u* x;                 // x as 16-byte vectors
     const v4u* r1;          // cos table as 16-byte vectors
     const v4u* r2;          // sin table
-    int64_t row_vecs;       // vectors per row of x (D*esize/16)
-    int64_t start_vec;      // first slice vector within a row
-    int64_t half_vecs;      // rotate_half: vectors per half of the slice
-    int64_t t1b, t1s, t1n;  // cos strides in vectors (0 = broadcast)
-    int64_t t2b, t2s, t2n;  // sin strides in vectors
-    uint32_t S, N;
-    uint32_t nvec;          // work units per row
+    uint32_t row_vecs;      // vectors per row of x (D*esize/16)
+    uint32_t start_vec;     // first slice vector within a row
+    uint32_t lo_vec;        // first vector the threads of a row cover
+    uint32_t half_vecs;     // rotate_half: vectors per half of the slice
+    uint32_t t1b, t1s, t1n; // cos strides in vectors (0 = broadcast)
+    uint32_t t2b, t2s, t2n; // sin strides in vectors
+    uint32_t N;
+    uint32_t nvec;          // work units per row (in the slice)
+    uint32_t span;          // vectors per row the threads cover (>= nvec)
     uint32_t HL;            // head lanes per tile
     uint32_t GL;            // tiles per block iteration
     uint32_t nchunk;        // head chunks per (b,s)
     uint32_t tiles;         // B*S*nchunk
     uint32_t btiles;        // ceil(tiles / GL)
     uint32_t xcd_remap;     // 1: give each XCD a contiguous range of tile groups
+    FastDiv span_div, hl_div, nchunk_div, s_div;  // divisions by span, HL, nchunk, S
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
@@ -227,30 +239,34 @@ __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
 {
     constexpr int K = Store<DT>::kLanes;
     const uint32_t t = threadIdx.x;
-    const uint32_t v = t % a.nvec;
-    const uint32_t hl = (t / a.nvec) % a.HL;
-    const uint32_t gl = t / (a.nvec * a.HL);
+    const uint32_t q = fast_div(t, a.span_div);
+    const uint32_t vs = t - q * a.span;
+    const uint32_t gl = fast_div(q, a.hl_div);
+    const uint32_t hl = q - gl * a.HL;
+    const uint32_t c = a.lo_vec + vs;                 // vector within the row
+    const bool in_slice = c >= a.start_vec && c - a.start_vec < a.nvec;
+    const uint32_t v = in_slice ? c - a.start_vec : 0;  // table vector (unused outside)
     if (gl >= a.GL) return;  // no barriers below, so idle threads may leave
 
     const uint32_t first = a.xcd_remap ? xcd_contiguous_block(blockIdx.x, gridDim.x) : blockIdx.x;
     for (uint32_t bt = first; bt < a.btiles; bt += gridDim.x) {
         const uint32_t tile = bt * a.GL + gl;
         if (tile >= a.tiles) continue;
-        const uint32_t g = tile / a.nchunk;          // (b,s) position
+        const uint32_t g = fast_div(tile, a.nchunk_div);  // (b,s) position
         const uint32_t chunk = tile - g * a.nchunk;
-        const uint32_t b = g / a.S;
-        const uint32_t s = g - b * a.S;
-        const uint32_t n0 = chunk * a.HL * U + hl;
-        const int64_t c_base = (int64_t)b * a.t1b + (int64_t)s * a.t1s + v;
-        const int64_t s_base = (int64_t)b * a.t2b + (int64_t)s * a.t2s + v;
-        const int64_t row0 = (int64_t)g * a.N;
+        const uint32_t b = fast_div(g, a.s_div);
+        const uint32_t s = g - b * a.s_div.d;
+        const uint32_t n0 = chunk * (a.HL * U) + hl;
+        const uint32_t c_base = b * a.t1b + s * a.t1s + v;
+        const uint32_t s_base = b * a.t2b + s * a.t2s + v;
+        const uint32_t row0 = g * a.N;
 
         // All loads are issued back to back with no branch between them: a
         // head past N (ragged last chunk) re-reads row N-1 and skips its
         // store. The tables come first, then the x vectors.
         v4u xa[U], xb[U];
         v4u ca[U], sa[U], cb[U], sb[U];
-        int64_t off[U];
+        uint32_t off[U];
         bool live[U];
         if constexpr (HEADS_SHARE_TABLES) {
             ca[0] = a.r1[c_base];
@@ -265,13 +281,13 @@ __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
             const uint32_t n = n0 + (uint32_t)k * a.HL;
             live[k] = n < a.N;
             const uint32_t nl = live[k] ? n : a.N - 1;
-            off[k] = (row0 + nl) * a.row_vecs + a.start_vec + v;
+            off[k] = (row0 + nl) * a.row_vecs + c;
             if constexpr (!HEADS_SHARE_TABLES) {
-                ca[k] = a.r1[c_base + (int64_t)nl * a.t1n];
-                sa[k] = a.r2[s_base + (int64_t)nl * a.t2n];
+                ca[k] = a.r1[c_base + nl * a.t1n];
+                sa[k] = a.r2[s_base + nl * a.t2n];
                 if constexpr (MODE == kModeRH) {
-                    cb[k] = a.r1[c_base + (int64_t)nl * a.t1n + a.half_vecs];
-                    sb[k] = a.r2[s_base + (int64_t)nl * a.t2n + a.half_vecs];
+                    cb[k] = a.r1[c_base + nl * a.t1n + a.half_vecs];
+                    sb[k] = a.r2[s_base + nl * a.t2n + a.half_vecs];
                 }
             }
             xa[k] = load_x<NT>(a.x + off[k]);
@@ -284,7 +300,7 @@ __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
 
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            if (!live[k]) continue;
+            if (!live[k] || !in_slice) continue;
             const int kt = HEADS_SHARE_TABLES ? 0 : k;
             Lanes<DT> X, C, S;
             X.unpack(xa[k]);
@@ -399,19 +415,53 @@ bool vec_geometry(const Plan& p, VecArgs* a)
     if (unit_bytes % 16) return false;
     for (int k = 0; k < 3; ++k)
         if ((p.t1[k] * es) % 16 || (p.t2[k] * es) % 16) return false;
-    if (p.S >= (1ll << 31) || p.N >= (1ll << 31) || p.B * p.S >= (1ll << 31)) return false;
+    // 32-bit vector offsets: x and each table must span fewer than 2^32
+    // vectors; tile indices stay below 2^31 (checked in finish_vec_args).
+    const int64_t kMax = (1ll << 32) - 1;
+    const int64_t x_vecs = p.B * p.S * p.N * (p.D * es / 16);
+    if (x_vecs > kMax || p.N >= (1ll << 31) || p.S >= (1ll << 31) || p.B * p.S >= (1ll << 31)) return false;
+    const int64_t dims[3] = {p.B, p.S, p.N};
+    int64_t t1_span = p.L * es / 16, t2_span = p.L * es / 16;
+    for (int k = 0; k < 3; ++k) {
+        t1_span += (dims[k] - 1) * (p.t1[k] * es / 16);
+        t2_span += (dims[k] - 1) * (p.t2[k] * es / 16);
+    }
+    if (t1_span > kMax || t2_span > kMax) return false;
     a->x = static_cast<v4u*>(p.x);
     a->r1 = static_cast<const v4u*>(p.r1);
     a->r2 = static_cast<const v4u*>(p.r2);
-    a->row_vecs = p.D * es / 16;
-    a->start_vec = p.start * es / 16;
-    a->half_vecs = p.mode == kModeRH ? (p.L / 2) * es / 16 : 0;
-    a->t1b = p.t1[0] * es / 16; a->t1s = p.t1[1] * es / 16; a->t1n = p.t1[2] * es / 16;
-    a->t2b = p.t2[0] * es / 16; a->t2s = p.t2[1] * es / 16; a->t2n = p.t2[2] * es / 16;
-    a->S = (uint32_t)p.S;
+    a->row_vecs = (uint32_t)(p.D * es / 16);
+    a->start_vec = (uint32_t)(p.start * es / 16);
+    a->lo_vec = a->start_vec;
+    a->half_vecs = p.mode == kModeRH ? (uint32_t)((p.L / 2) * es / 16) : 0;
+    a->t1b = (uint32_t)(p.t1[0] * es / 16); a->t1s = (uint32_t)(p.t1[1] * es / 16);
+    a->t1n = (uint32_t)(p.t1[2] * es / 16);
+    a->t2b = (uint32_t)(p.t2[0] * es / 16); a->t2s = (uint32_t)(p.t2[1] * es / 16);
+    a->t2n = (uint32_t)(p.t2[2] * es / 16);
     a->N = (uint32_t)p.N;
+    a->s_div = make_fastdiv((uint32_t)p.S);
     a->nvec = (uint32_t)(unit_bytes / 16);
+    a->span = a->nvec;
     return a->nvec >= 1 && a->nvec <= 256;
+}
+
+// Interleave slices that cover only part of their first or last 128-byte
+// line: let the threads of a row cover the whole lines around the slice
+// (see the vector kernel). Needs rows that start on line boundaries so the
+// lines stay inside the row. Measured on MI355X for bf16 lanes [32,96) of
+// 128 (same HBM bytes either way): 3-4% faster in this kernel, and 15% in a
+// bare read-modify-write of the same bytes.
+void cover_whole_lines(const Plan& p, VecArgs* a)
+{
+    const int64_t es = p.esize;
+    const int64_t lo = (p.start * es) / 128 * 128;
+    const int64_t hi = ((p.start + p.L) * es + 127) / 128 * 128;
+    if (p.mode != kModeIL) return;
+    if (lo == p.start * es && hi == (p.start + p.L) * es) return;   // whole lines already
+    if ((p.D * es) % 128 || (reinterpret_cast<uintptr_t>(p.x) & 127u)) return;
+    if ((hi - lo) / 16 > 256) return;
+    a->lo_vec = (uint32_t)(lo / 16);
+    a->span = (uint32_t)((hi - lo) / 16);
 }
 
 // Launch shape for U heads per thread and a target block size: head lanes
@@ -421,9 +471,9 @@ VecConfig shape_for(const VecArgs& a, int U, uint32_t threads)
 {
     VecConfig c;
     c.U = U;
-    const uint32_t hl_max = std::max<uint32_t>(1, threads / a.nvec);
+    const uint32_t hl_max = std::max<uint32_t>(1, threads / a.span);
     c.HL = (uint32_t)std::min<uint64_t>(hl_max, (a.N + U - 1) / U);
-    c.GL = std::max<uint32_t>(1, threads / (a.nvec * c.HL));
+    c.GL = std::max<uint32_t>(1, threads / (a.span * c.HL));
     return c;
 }
 
@@ -450,7 +500,7 @@ VecConfig choose_vec_config(const Plan& p, const VecArgs& a)
 bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
 {
     if (cfg.U < 1 || cfg.U > 4 || (cfg.U & (cfg.U - 1)) || cfg.HL < 1 || cfg.GL < 1 ||
-        (uint64_t)cfg.HL * cfg.GL * a->nvec > 256)
+        (uint64_t)cfg.HL * cfg.GL * a->span > 256)
         return false;
     a->HL = cfg.HL;
     a->GL = cfg.GL;
@@ -461,6 +511,9 @@ bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
     a->nchunk = (uint32_t)nchunk;
     a->tiles = (uint32_t)tiles;
     a->btiles = (uint32_t)((tiles + cfg.GL - 1) / cfg.GL);
+    a->span_div = make_fastdiv(a->span);
+    a->hl_div = make_fastdiv(a->HL);
+    a->nchunk_div = make_fastdiv(a->nchunk);
     a->xcd_remap = cfg.xcd_remap ? 1u : 0u;
     return true;
 }
@@ -498,7 +551,7 @@ const void* vec_kernel_dt(int dir, int mode, int U, bool share, bool nt)
 // Launch the vector kernel; `a` is complete (vec_geometry + finish_vec_args).
 hipError_t launch_vec(const Plan& p, const VecArgs& a, const VecConfig& cfg, hipStream_t stream)
 {
-    const uint32_t threads = a.nvec * a.HL * a.GL;
+    const uint32_t threads = a.span * a.HL * a.GL;
     // One block per tile group by default: measured faster on MI355X than a
     // persistent grid for these streaming shapes (the dispatcher keeps every
     // CU full and no loop-carried dependence serialises the loads).
@@ -574,7 +627,13 @@ rope_status_t run(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
 
     VecArgs a{};
     VecConfig cfg;
-    if (vec_geometry(p, &a) && finish_vec_args(p, cfg = choose_vec_config(p, a), &a))
+    bool vec = vec_geometry(p, &a);
+    if (vec) {
+        cover_whole_lines(p, &a);
+        cfg = choose_vec_config(p, a);
+        vec = finish_vec_args(p, cfg, &a);
+    }
+    if (vec)
         err = launch_vec(p, a, cfg, s);
     else
         err = launch_scalar(p, cus, s);
