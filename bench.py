@@ -20,6 +20,7 @@ known size (for rocprofv3 counter passes), and prints nothing else.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -193,6 +194,35 @@ def bench_workload(name: str, steps: int, warmup: int, reps: int, stream, want_c
     return out
 
 
+def bench_multi(name: str, reps: int, stream) -> dict:
+    """A workload with several tensors (the GQA Q and K): forward launch time
+    of one _multi call against one single-tensor call per tensor, rotating
+    copies so that no launch finds its data in a cache."""
+    import torch
+
+    import transformer_positional_encoding_amd as rp
+    import workloads as W
+    w = W.WORKLOADS[name]
+    r1, r2 = (t.to("cuda") for t in W.make_tables(w))
+    per_set = sum(slice_line_bytes(dataclasses.replace(w, x_shapes=(shp,))) for shp in w.x_shapes)
+    ncopy = max(1, min(8, -(-(3 * MALL_BYTES) // per_set)))
+    base = [W.make_x(w, k).to("cuda") for k in range(len(w.x_shapes))]
+    sets = [[t.clone() for t in base] for _ in range(ncopy)]
+    one = [(rp.rope_partial_fwd_inplace_multi, (sets[i], r1, r2, w.mode, w.partial_slice)) for i in range(ncopy)]
+    each = [(lambda xs: [rp.rope_partial_fwd_inplace(x, r1, r2, w.mode, w.partial_slice) for x in xs], (sets[i],))
+            for i in range(ncopy)]
+    time_launches(one, max(4, reps // 4), stream)
+    t_one = time_launches(one, reps, stream)
+    time_launches(each, max(4, reps // 4), stream)
+    t_each = time_launches(each, reps, stream)
+    nbytes = w.algorithmic_bytes()
+    return {"workload": name, "note": w.note, "dtype": w.dtype, "directions": ["fwd"], "rotating_copies": ncopy,
+            "bytes_per_call": nbytes, "elements_per_call": w.rotated_elements(),
+            "one_launch_us": round(t_one * 1e6, 3), "one_launch_GBps": round(nbytes / t_one / 1e9, 1),
+            "separate_launches_us": round(t_each * 1e6, 3),
+            "separate_launches_GBps": round(nbytes / t_each / 1e9, 1)}
+
+
 def profile_target(name: str, reps: int) -> None:
     """Launches for rocprofv3 counter passes: each direction of the workload
     `reps` times (rotating copies as in the timed run), then a plain device
@@ -225,7 +255,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
-    ap.add_argument("--also", default="c3,c4_f32",
+    ap.add_argument("--also", default="c3,c4_f32,c2",
                     help="other workloads measured in the same run (reported under 'other_workloads')")
     ap.add_argument("--reps", type=int, default=50, help="launches per per-kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -254,6 +284,10 @@ def main() -> int:
                               not args.no_cpu_baseline, args.cpu_seconds)
     others = []
     for name in [n for n in args.also.split(",") if n and n != args.workload]:
+        import workloads as W
+        if len(W.WORKLOADS[name].x_shapes) > 1:
+            others.append(bench_multi(name, max(10, args.reps // 2), stream))
+            continue
         r = bench_workload(name, max(5, args.steps // 5), 2, max(10, args.reps // 2), stream, False, 0)
         others.append({k: r[k] for k in ("workload", "note", "dtype", "directions", "rotating_copies",
                                          "bytes_per_launch", "elements_per_launch", "kernels")})

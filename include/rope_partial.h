@@ -35,6 +35,9 @@
 extern "C" {
 #endif
 
+/* symbols of the C ABI; everything else in the library is hidden */
+#define ROPE_API __attribute__((visibility("default")))
+
 typedef enum rope_status {
     ROPE_OK = 0,
     ROPE_ERR_NULLPTR = 1,      /* a required pointer is NULL                   */
@@ -87,7 +90,7 @@ typedef enum rope_dtype {
  * Overlapping x with r1 or r2 is undefined. Results are deterministic: each
  * element is computed by one thread from the same inputs on every call.
  */
-rope_status_t rope_partial_fwd_inplace(
+ROPE_API rope_status_t rope_partial_fwd_inplace(
     void* x, const int64_t x_shape[4], rope_dtype_t dtype,
     const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
     const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
@@ -100,20 +103,58 @@ rope_status_t rope_partial_fwd_inplace(
  * Arguments, checks and no-op rules are those of the forward; r1 and r2
  * receive no gradient (the page's autograd returns None for them).
  */
-rope_status_t rope_partial_bwd_inplace(
+ROPE_API rope_status_t rope_partial_bwd_inplace(
     void* x, const int64_t x_shape[4], rope_dtype_t dtype,
     const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
     const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
     rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
     void* stream);
 
+/* largest tensor count of the _multi entry points */
+#define ROPE_MULTI_MAX 4
+
+/*
+ * rope_partial_fwd_inplace_multi / rope_partial_bwd_inplace_multi -- rotate
+ * `count` tensors that share one pair of tables (for example the Q and K of
+ * one attention layer, whose head counts differ under grouped-query
+ * attention) with one call; the result is that of calling the single-tensor
+ * entry point on xs[0], xs[1], ... in order on `stream`. When every tensor
+ * takes the same vector kernel, all of them run in a single kernel launch
+ * (one launch overhead, tables shared in cache). "ANE实战RoPE位置编码在MIL中的
+ * 纯ANE实现", section 第二步, applies the same rotation to Q and to K.
+ *
+ *   count      0..ROPE_MULTI_MAX; 0 is a no-op.
+ *   xs         host array of `count` device pointers.
+ *   x_shapes   host array of `count` shapes {B, S, N, D}.
+ *   Other arguments are those of rope_partial_fwd_inplace and apply to every
+ *   tensor: the tables must broadcast against each tensor's slice.
+ *
+ * Every tensor is checked before anything is launched: on an error no
+ * memory has been touched, and rope_last_error() names the tensor.
+ * count outside [0, ROPE_MULTI_MAX] is ROPE_ERR_INVALID; NULL xs or x_shapes
+ * with count > 0 is ROPE_ERR_NULLPTR. The tensors must not overlap.
+ */
+ROPE_API rope_status_t rope_partial_fwd_inplace_multi(
+    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+ROPE_API rope_status_t rope_partial_bwd_inplace_multi(
+    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
 /* Static text for a status code; never NULL. */
-const char* rope_status_string(rope_status_t status);
+ROPE_API const char* rope_status_string(rope_status_t status);
 
 /* Text describing the last non-OK status returned on the calling thread
  * (which check failed, or the HIP error); "" if none. The pointer stays valid
  * until the next call on that thread. */
-const char* rope_last_error(void);
+ROPE_API const char* rope_last_error(void);
 
 #ifdef __cplusplus
 }

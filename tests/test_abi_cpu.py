@@ -25,7 +25,7 @@ def declared_functions():
     for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
         text = open(h, encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
+        names += re.findall(r"^\s*(?:ROPE_API\s+)?(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(",
                             text, flags=re.M)
     return sorted(set(names))
 
@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string",
-                 "rope_last_error"):
+                 "rope_last_error", "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi"):
         assert want in names
 
 
@@ -163,3 +163,40 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(rp, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         rp.library()
+
+
+def test_autograd_op_rejects_leaf_on_cpu():
+    import torch
+    x = torch.zeros(1, 2, 1, 8, requires_grad=True)
+    r = torch.zeros(1, 2, 1, 8)
+    with pytest.raises(RuntimeError, match="leaf"):
+        rp.inplace_partial_rotary_mul(x, r, r, "interleave", (0, 8))
+
+
+def mcall(direction="fwd", ptrs=(FAKE, FAKE), shapes=((2, 4, 3, 64), (2, 4, 1, 64)), table_dtype=None, **kw):
+    r1_shape = kw.pop("r1_shape", (1, 4, 1, 32))
+    r1_strides = kw.pop("r1_strides", (128, 32, 32, 1))
+    return rp.raw_multi_call(direction, list(ptrs) if ptrs is not None else None,
+                             list(shapes) if shapes is not None else None, kw.pop("dtype", BF16),
+                             kw.pop("r1", FAKE), r1_shape, r1_strides, kw.pop("r2", FAKE), r1_shape, r1_strides,
+                             BF16 if table_dtype is None else table_dtype, kw.pop("mode", IL), kw.pop("sl", (0, 32)),
+                             None, count=kw.pop("count", None))
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_multi_checks_every_tensor_first(direction):
+    # valid geometry for both tensors reaches the dtype check
+    assert mcall(direction, table_dtype=F32) == UNSUPPORTED
+    # the second tensor is named in the error
+    assert mcall(direction, shapes=((2, 4, 3, 64), (2, 5, 1, 64))) == INVALID
+    assert "tensor 1" in rp.last_error()
+    assert mcall(direction, ptrs=(FAKE, None)) == NULLPTR and "tensor 1" in rp.last_error()
+
+
+def test_multi_count_rules():
+    assert mcall(count=0, ptrs=None, shapes=None) == OK
+    assert mcall(count=5, ptrs=[FAKE] * 5, shapes=[(2, 4, 3, 64)] * 5) == INVALID
+    assert mcall(count=-1) == INVALID
+    assert mcall(count=2, ptrs=None) == NULLPTR
+    # every tensor a no-op: nothing launched, no pointer read
+    assert mcall(ptrs=(None, None), sl=(8, 8), r1=None, r2=None) == OK

@@ -18,7 +18,8 @@ import ctypes
 import os
 
 __all__ = [
-    "rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string",
+    "rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string", "inplace_partial_rotary_mul",
+    "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi", "MULTI_MAX",
     "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
     "ROPE_ERR_UNSUPPORTED", "ROPE_ERR_RUNTIME", "MODES", "DTYPE_CODES",
 ]
@@ -29,6 +30,7 @@ LIB_PATH = os.path.join(_PKG, "_lib", "librope_partial.so")
 ROPE_OK, ROPE_ERR_NULLPTR, ROPE_ERR_INVALID, ROPE_ERR_UNSUPPORTED, ROPE_ERR_RUNTIME = range(5)
 MODES = {"rotate_half": 0, "interleave": 1}
 DTYPE_CODES = {"f32": 0, "f16": 1, "bf16": 2}
+MULTI_MAX = 4
 
 _I64x4 = ctypes.c_int64 * 4
 _I64x2 = ctypes.c_int64 * 2
@@ -65,6 +67,10 @@ def library() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = _ENTRY_ARGTYPES
+        for name in ("rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p] + _ENTRY_ARGTYPES[2:]
         L.rope_status_string.restype = ctypes.c_char_p
         L.rope_status_string.argtypes = [ctypes.c_int]
         L.rope_last_error.restype = ctypes.c_char_p
@@ -89,6 +95,23 @@ def raw_call(direction: str, x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_st
     fn = library().rope_partial_fwd_inplace if direction == "fwd" else library().rope_partial_bwd_inplace
     sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
     return fn(x_ptr, _arr4(x_shape), int(dtype), r1_ptr, _arr4(r1_shape), _arr4(r1_strides),
+              r2_ptr, _arr4(r2_shape), _arr4(r2_strides), int(table_dtype), int(mode), sl, stream)
+
+
+def raw_multi_call(direction: str, x_ptrs, x_shapes, dtype: int, r1_ptr, r1_shape, r1_strides,
+                   r2_ptr, r2_shape, r2_strides, table_dtype: int, mode: int, partial_slice,
+                   stream=None, count=None) -> int:
+    """Call a _multi entry point with plain integers and sequences (None =
+    NULL); returns the status code without raising."""
+    L = library()
+    fn = L.rope_partial_fwd_inplace_multi if direction == "fwd" else L.rope_partial_bwd_inplace_multi
+    n = len(x_ptrs) if x_ptrs is not None else 0
+    count = n if count is None else count
+    ptrs = None if x_ptrs is None else (ctypes.c_void_p * max(n, 1))(*x_ptrs)
+    flat = [] if x_shapes is None else [int(v) for sh in x_shapes for v in sh]
+    shapes = None if x_shapes is None else (ctypes.c_int64 * max(len(flat), 4))(*flat)
+    sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
+    return fn(int(count), ptrs, shapes, int(dtype), r1_ptr, _arr4(r1_shape), _arr4(r1_strides),
               r2_ptr, _arr4(r2_shape), _arr4(r2_strides), int(table_dtype), int(mode), sl, stream)
 
 
@@ -136,6 +159,47 @@ def _call(direction: str, x, r1, r2, mode, partial_slice, stream) -> None:
         raise RopeError(st, last_error())
 
 
+def _call_multi(direction: str, xs, r1, r2, mode, partial_slice, stream) -> None:
+    import torch
+    xs = list(xs)
+    if len(xs) > MULTI_MAX:
+        raise ValueError(f"at most {MULTI_MAX} tensors per call")
+    if not xs:
+        return
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"rotary_mode must be one of {sorted(MODES)}")
+        mode = MODES[mode]
+    for name, t in [(f"xs[{i}]", x) for i, x in enumerate(xs)] + [("r1", r1), ("r2", r2)]:
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D (B,S,N,D layout), got {t.dim()}-D")
+    dtypes = {x.dtype for x in xs}
+    if len(dtypes) != 1:
+        raise TypeError("all tensors of one call must share a dtype")
+    devs = {x.device for x in xs if x.numel()}
+    if len(devs) > 1:
+        raise ValueError("all tensors of one call must be on one device")
+    for i, x in enumerate(xs):
+        if x.numel() and not x.is_cuda:
+            raise ValueError(f"xs[{i}] must be a GPU tensor")
+        if not x.is_contiguous():
+            raise ValueError(f"xs[{i}] must be contiguous (BSND)")
+    dev = next(iter(devs)) if devs else None
+    if stream is None:
+        handle = torch.cuda.current_stream(dev).cuda_stream if dev is not None else None
+    else:
+        handle = getattr(stream, "cuda_stream", stream)
+    with torch.cuda.device(dev) if dev is not None else _nullcontext():
+        st = raw_multi_call(direction, [x.data_ptr() or None for x in xs], [tuple(x.shape) for x in xs],
+                            _dtype_code(xs[0]), r1.data_ptr() or None, tuple(r1.shape), tuple(r1.stride()),
+                            r2.data_ptr() or None, tuple(r2.shape), tuple(r2.stride()),
+                            _dtype_code(r1) if r1.dtype == r2.dtype else -1, mode, partial_slice, handle)
+    if st != ROPE_OK:
+        raise RopeError(st, last_error())
+
+
 class _nullcontext:
     def __enter__(self):
         return None
@@ -161,3 +225,76 @@ def rope_partial_bwd_inplace(dx, r1, r2, rotary_mode="interleave", partial_slice
     """Backward of :func:`rope_partial_fwd_inplace`: ``dx`` (the incoming
     gradient) is replaced in place by the gradient with respect to x."""
     _call("bwd", dx, r1, r2, rotary_mode, partial_slice, stream)
+
+
+def rope_partial_fwd_inplace_multi(xs, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:
+    """Forward on up to MULTI_MAX tensors that share r1/r2 (e.g. Q and K), in
+    one kernel launch when they take the same kernel; same result as calling
+    :func:`rope_partial_fwd_inplace` on each in order."""
+    _call_multi("fwd", xs, r1, r2, rotary_mode, partial_slice, stream)
+
+
+def rope_partial_bwd_inplace_multi(dxs, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:
+    """Backward counterpart of :func:`rope_partial_fwd_inplace_multi`."""
+    _call_multi("bwd", dxs, r1, r2, rotary_mode, partial_slice, stream)
+
+
+# ---------------------------------------------------------------------------
+# Autograd op over the C ABI ("CANN ops-transformer 算子详解：
+# inplace_partial_rotary_mul 原地部分旋转位置编码", section 自动微分说明 and the
+# training-mode example of section 调用说明): the forward rotates x in place
+# and marks it dirty; the backward runs the in-place backward entry point on
+# the incoming gradient; r1 and r2 receive no gradient.
+# ---------------------------------------------------------------------------
+
+def _autograd_function():
+    import torch
+
+    class InplacePartialRotaryMulFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, r1, r2, rotary_mode, partial_slice):
+            rope_partial_fwd_inplace(x, r1, r2, rotary_mode, partial_slice)
+            ctx.mark_dirty(x)
+            ctx.save_for_backward(r1, r2)
+            ctx.rotary_mode = rotary_mode
+            ctx.partial_slice = None if partial_slice is None else tuple(int(v) for v in partial_slice)
+            return x
+
+        @staticmethod
+        def backward(ctx, grad):
+            r1, r2 = ctx.saved_tensors
+            # The gradient buffer autograd hands over may be shared or
+            # expanded (stride 0), so the in-place backward runs on a private
+            # contiguous copy of it.
+            dx = grad.contiguous()
+            if dx.data_ptr() == grad.data_ptr():
+                dx = dx.clone()
+            rope_partial_bwd_inplace(dx, r1, r2, ctx.rotary_mode, ctx.partial_slice)
+            return dx, None, None, None, None
+
+    return InplacePartialRotaryMulFn
+
+
+_FN = None
+
+
+def inplace_partial_rotary_mul(x, r1, r2, rotary_mode="interleave", partial_slice=None) -> None:
+    """In-place partial RoPE that records itself for autograd when x needs a
+    gradient, and calls the forward entry point directly otherwise.
+
+    x must not be a leaf tensor that requires grad: in-place changes to such
+    a tensor are illegal in autograd, so rotate a non-leaf copy (y = x * 1.0),
+    as the training example on the page does. r1 and r2 never get gradients.
+    """
+    import torch
+    global _FN
+    if torch.is_grad_enabled() and x.requires_grad:
+        if x.is_leaf:
+            raise RuntimeError("inplace_partial_rotary_mul: x is a leaf tensor that requires grad; "
+                               "rotate a non-leaf copy of it (e.g. y = x * 1.0)")
+        if _FN is None:
+            _FN = _autograd_function()
+        _FN.apply(x, r1, r2, rotary_mode, partial_slice)
+        return None
+    rope_partial_fwd_inplace(x, r1, r2, rotary_mode, partial_slice)
+    return None

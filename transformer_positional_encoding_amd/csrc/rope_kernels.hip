@@ -234,8 +234,10 @@ __device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t bid, uint32_t 
     return x * q + min(x, r) + bid / kXcds;
 }
 
+// The kernel body for one tensor: `bid` is the block's number among the G
+// blocks that work on this tensor.
 template <int DT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
-__global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
+__device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_t G)
 {
     constexpr int K = Store<DT>::kLanes;
     const uint32_t t = threadIdx.x;
@@ -248,8 +250,8 @@ __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
     const uint32_t v = in_slice ? c - a.start_vec : 0;  // table vector (unused outside)
     if (gl >= a.GL) return;  // no barriers below, so idle threads may leave
 
-    const uint32_t first = a.xcd_remap ? xcd_contiguous_block(blockIdx.x, gridDim.x) : blockIdx.x;
-    for (uint32_t bt = first; bt < a.btiles; bt += gridDim.x) {
+    const uint32_t first = a.xcd_remap ? xcd_contiguous_block(bid, G) : bid;
+    for (uint32_t bt = first; bt < a.btiles; bt += G) {
         const uint32_t tile = bt * a.GL + gl;
         if (tile >= a.tiles) continue;
         const uint32_t g = fast_div(tile, a.nchunk_div);  // (b,s) position
@@ -323,6 +325,41 @@ __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
                 store_x<NT>(a.x + off[k] + a.half_vecs, X2.pack());
             }
         }
+    }
+}
+
+template <int DT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
+__global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
+{
+    vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(a, blockIdx.x, gridDim.x);
+}
+
+// Several tensors that share the tables (the Q and K of one layer) in one
+// launch: blocks [first_block[i], first_block[i+1]) work on tensor i. The
+// switch keeps every field access a constant offset into the kernel
+// arguments.
+constexpr int kMultiMax = ROPE_MULTI_MAX;
+
+struct MultiVecArgs {
+    uint32_t count;
+    uint32_t first_block[kMultiMax + 1];
+    VecArgs a[kMultiMax];
+};
+
+template <int DT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
+__global__ void __launch_bounds__(256) rope_vec_multi_kernel(MultiVecArgs m)
+{
+    const uint32_t b = blockIdx.x;
+    uint32_t i = 0;
+#pragma unroll
+    for (int k = 1; k < kMultiMax; ++k)
+        i += (k < (int)m.count && b >= m.first_block[k]) ? 1u : 0u;
+    const uint32_t lo = m.first_block[i], G = m.first_block[i + 1] - lo;
+    switch (i) {
+    case 0: vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[0], b - lo, G); break;
+    case 1: vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[1], b - lo, G); break;
+    case 2: vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[2], b - lo, G); break;
+    default: vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[3], b - lo, G); break;
     }
 }
 
@@ -518,54 +555,68 @@ bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
     return true;
 }
 
+template <int DT, int DIR, int MODE, int U, bool SHARE, bool NT>
+const void* vec_kernel_ptr(bool multi)
+{
+    return multi ? reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, DIR, MODE, U, SHARE, NT>)
+                 : reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, SHARE, NT>);
+}
+
 template <int DT, int DIR, int MODE, int U>
-const void* vec_kernel_u(bool share, bool nt)
+const void* vec_kernel_u(bool share, bool nt, bool multi)
 {
     if (share)
-        return nt ? reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, true, true>)
-                  : reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, true, false>);
-    return nt ? reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, false, true>)
-              : reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, false, false>);
+        return nt ? vec_kernel_ptr<DT, DIR, MODE, U, true, true>(multi)
+                  : vec_kernel_ptr<DT, DIR, MODE, U, true, false>(multi);
+    return nt ? vec_kernel_ptr<DT, DIR, MODE, U, false, true>(multi)
+              : vec_kernel_ptr<DT, DIR, MODE, U, false, false>(multi);
 }
 
 template <int DT, int DIR, int MODE>
-const void* vec_kernel_m(int U, bool share, bool nt)
+const void* vec_kernel_m(int U, bool share, bool nt, bool multi)
 {
     switch (U) {
-    case 1: return vec_kernel_u<DT, DIR, MODE, 1>(share, nt);
-    case 2: return vec_kernel_u<DT, DIR, MODE, 2>(share, nt);
-    default: return vec_kernel_u<DT, DIR, MODE, 4>(share, nt);
+    case 1: return vec_kernel_u<DT, DIR, MODE, 1>(share, nt, multi);
+    case 2: return vec_kernel_u<DT, DIR, MODE, 2>(share, nt, multi);
+    default: return vec_kernel_u<DT, DIR, MODE, 4>(share, nt, multi);
     }
 }
 
 template <int DT>
-const void* vec_kernel_dt(int dir, int mode, int U, bool share, bool nt)
+const void* vec_kernel_dt(int dir, int mode, int U, bool share, bool nt, bool multi)
 {
     if (dir == kFwd)
-        return mode == kModeIL ? vec_kernel_m<DT, kFwd, kModeIL>(U, share, nt)
-                               : vec_kernel_m<DT, kFwd, kModeRH>(U, share, nt);
-    return mode == kModeIL ? vec_kernel_m<DT, kBwd, kModeIL>(U, share, nt)
-                           : vec_kernel_m<DT, kBwd, kModeRH>(U, share, nt);
+        return mode == kModeIL ? vec_kernel_m<DT, kFwd, kModeIL>(U, share, nt, multi)
+                               : vec_kernel_m<DT, kFwd, kModeRH>(U, share, nt, multi);
+    return mode == kModeIL ? vec_kernel_m<DT, kBwd, kModeIL>(U, share, nt, multi)
+                           : vec_kernel_m<DT, kBwd, kModeRH>(U, share, nt, multi);
+}
+
+const void* vec_kernel(const Plan& p, const VecConfig& cfg, bool multi)
+{
+    const bool share = p.t1[2] == 0 && p.t2[2] == 0;
+    switch (p.dtype) {
+    case ROPE_DTYPE_F32: return vec_kernel_dt<ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
+    case ROPE_DTYPE_F16: return vec_kernel_dt<ROPE_DTYPE_F16>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
+    default: return vec_kernel_dt<ROPE_DTYPE_BF16>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
+    }
+}
+
+uint32_t vec_grid(const VecArgs& a, const VecConfig& cfg)
+{
+    // One block per tile group by default: measured faster on MI355X than a
+    // persistent grid for these streaming shapes (the dispatcher keeps every
+    // CU full and no loop-carried dependence serialises the loads).
+    uint64_t grid = cfg.grid ? cfg.grid : a.btiles;
+    return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(grid, a.btiles));
 }
 
 // Launch the vector kernel; `a` is complete (vec_geometry + finish_vec_args).
 hipError_t launch_vec(const Plan& p, const VecArgs& a, const VecConfig& cfg, hipStream_t stream)
 {
     const uint32_t threads = a.span * a.HL * a.GL;
-    // One block per tile group by default: measured faster on MI355X than a
-    // persistent grid for these streaming shapes (the dispatcher keeps every
-    // CU full and no loop-carried dependence serialises the loads).
-    uint64_t grid = cfg.grid ? cfg.grid : a.btiles;
-    grid = std::max<uint64_t>(1, std::min<uint64_t>(grid, a.btiles));
-    const bool share = p.t1[2] == 0 && p.t2[2] == 0;
-    const void* fn;
-    switch (p.dtype) {
-    case ROPE_DTYPE_F32: fn = vec_kernel_dt<ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt); break;
-    case ROPE_DTYPE_F16: fn = vec_kernel_dt<ROPE_DTYPE_F16>(p.dir, p.mode, cfg.U, share, cfg.nt); break;
-    default: fn = vec_kernel_dt<ROPE_DTYPE_BF16>(p.dir, p.mode, cfg.U, share, cfg.nt); break;
-    }
     void* args[] = {const_cast<VecArgs*>(&a)};
-    return hipLaunchKernel(fn, dim3((uint32_t)grid), dim3(threads), args, 0, stream);
+    return hipLaunchKernel(vec_kernel(p, cfg, false), dim3(vec_grid(a, cfg)), dim3(threads), args, 0, stream);
 }
 
 template <int DT, int DIR, int MODE>
@@ -606,37 +657,114 @@ hipError_t launch_scalar(const Plan& p, int cus, hipStream_t stream)
     }
 }
 
+// One tensor's launch, decided on the host.
+struct Launch {
+    Plan p;
+    bool vec = false;
+    VecArgs a{};
+    VecConfig cfg;
+};
+
+void prepare(Launch* L)
+{
+    L->vec = vec_geometry(L->p, &L->a);
+    if (L->vec) {
+        cover_whole_lines(L->p, &L->a);
+        L->cfg = choose_vec_config(L->p, L->a);
+        L->vec = finish_vec_args(L->p, L->cfg, &L->a);
+    }
+}
+
+hipError_t launch_one(const Launch& L, int cus, hipStream_t s)
+{
+    return L.vec ? launch_vec(L.p, L.a, L.cfg, s) : launch_scalar(L.p, cus, s);
+}
+
+rope_status_t device_cus(int* cus)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("hipGetDevice: ") + hipGetErrorString(err));
+    *cus = cu_count(dev);
+    return ROPE_OK;
+}
+
 rope_status_t run(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
                   const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
                   const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
                   rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
                   void* stream, Direction dir)
 {
-    Plan p;
+    Launch L;
     std::string why;
     rope_status_t st = make_plan(x, x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides,
-                                 table_dtype, mode, partial_slice, dir, &p, &why);
+                                 table_dtype, mode, partial_slice, dir, &L.p, &why);
     if (st != ROPE_OK) return set_error(st, why);
-    if (p.noop) return ROPE_OK;
+    if (L.p.noop) return ROPE_OK;
+    int cus = 0;
+    if ((st = device_cus(&cus)) != ROPE_OK) return st;
+    prepare(&L);
+    hipError_t err = launch_one(L, cus, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
+    return ROPE_OK;
+}
 
-    int dev = 0;
-    hipError_t err = hipGetDevice(&dev);
-    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("hipGetDevice: ") + hipGetErrorString(err));
-    const int cus = cu_count(dev);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-
-    VecArgs a{};
-    VecConfig cfg;
-    bool vec = vec_geometry(p, &a);
-    if (vec) {
-        cover_whole_lines(p, &a);
-        cfg = choose_vec_config(p, a);
-        vec = finish_vec_args(p, cfg, &a);
+// Several tensors with shared tables: every tensor is checked before any
+// launch; tensors that all take the same vector kernel and block size go in
+// one launch, otherwise each is launched in turn (same result either way).
+rope_status_t run_multi(int32_t count, void* const xs[], const int64_t (*x_shapes)[4], rope_dtype_t dtype,
+                        const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                        const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                        rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                        void* stream, Direction dir)
+{
+    if (count < 0 || count > kMultiMax)
+        return set_error(ROPE_ERR_INVALID, "count must be in [0, " + std::to_string(kMultiMax) + "]");
+    if (count == 0) return ROPE_OK;
+    if (xs == nullptr || x_shapes == nullptr) return set_error(ROPE_ERR_NULLPTR, "xs or x_shapes is NULL");
+    Launch L[kMultiMax];
+    int live = 0;
+    for (int i = 0; i < count; ++i) {
+        std::string why;
+        rope_status_t st = make_plan(xs[i], x_shapes[i], dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides,
+                                     table_dtype, mode, partial_slice, dir, &L[live].p, &why);
+        if (st != ROPE_OK) return set_error(st, "tensor " + std::to_string(i) + ": " + why);
+        if (!L[live].p.noop) ++live;
     }
-    if (vec)
-        err = launch_vec(p, a, cfg, s);
-    else
-        err = launch_scalar(p, cus, s);
+    if (live == 0) return ROPE_OK;
+    int cus = 0;
+    rope_status_t st = device_cus(&cus);
+    if (st != ROPE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int i = 0; i < live; ++i) prepare(&L[i]);
+
+    bool together = live > 1;
+    const uint32_t threads = L[0].a.span * L[0].a.HL * L[0].a.GL;
+    const void* fn = together && L[0].vec ? vec_kernel(L[0].p, L[0].cfg, true) : nullptr;
+    for (int i = 0; i < live && together; ++i) {
+        together = L[i].vec && L[i].a.span * L[i].a.HL * L[i].a.GL == threads &&
+                   vec_kernel(L[i].p, L[i].cfg, true) == fn && L[i].cfg.grid == 0;
+    }
+    hipError_t err = hipSuccess;
+    if (together) {
+        MultiVecArgs m{};
+        m.count = (uint32_t)live;
+        uint64_t blocks = 0;
+        for (int i = 0; i < live; ++i) {
+            m.a[i] = L[i].a;
+            m.first_block[i] = (uint32_t)blocks;
+            blocks += vec_grid(L[i].a, L[i].cfg);
+        }
+        for (int i = live; i <= kMultiMax; ++i) m.first_block[i] = (uint32_t)blocks;
+        if (blocks >= (1ull << 31)) together = false;
+        if (together) {
+            void* args[] = {&m};
+            err = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(threads), args, 0, s);
+        }
+    }
+    if (!together) {
+        for (int i = 0; i < live && err == hipSuccess; ++i) err = launch_one(L[i], cus, s);
+    }
     if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
     return ROPE_OK;
 }
@@ -664,6 +792,26 @@ rope_status_t rope_partial_bwd_inplace(void* x, const int64_t x_shape[4], rope_d
 {
     return rope::run(x, x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides, table_dtype, mode,
                      partial_slice, stream, rope::kBwd);
+}
+
+rope_status_t rope_partial_fwd_inplace_multi(int32_t count, void* const xs[], const int64_t x_shapes[][4],
+                                             rope_dtype_t dtype, const void* r1, const int64_t r1_shape[4],
+                                             const int64_t r1_strides[4], const void* r2, const int64_t r2_shape[4],
+                                             const int64_t r2_strides[4], rope_dtype_t table_dtype, int64_t mode,
+                                             const int64_t partial_slice[2], void* stream)
+{
+    return rope::run_multi(count, xs, x_shapes, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides,
+                           table_dtype, mode, partial_slice, stream, rope::kFwd);
+}
+
+rope_status_t rope_partial_bwd_inplace_multi(int32_t count, void* const xs[], const int64_t x_shapes[][4],
+                                             rope_dtype_t dtype, const void* r1, const int64_t r1_shape[4],
+                                             const int64_t r1_strides[4], const void* r2, const int64_t r2_shape[4],
+                                             const int64_t r2_strides[4], rope_dtype_t table_dtype, int64_t mode,
+                                             const int64_t partial_slice[2], void* stream)
+{
+    return rope::run_multi(count, xs, x_shapes, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides,
+                           table_dtype, mode, partial_slice, stream, rope::kBwd);
 }
 
 const char* rope_status_string(rope_status_t status)
