@@ -255,7 +255,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
-    ap.add_argument("--also", default="c3,c4_f32,c2",
+    ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32",
                     help="other workloads measured in the same run (reported under 'other_workloads')")
     ap.add_argument("--reps", type=int, default=50, help="launches per per-kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

@@ -17,8 +17,12 @@
  *   with respect to x, section 自动微分说明 -- which equals rotating by -θ
  *   when the tables hold one angle per pair.)
  *   r1 (cos) and r2 (sin) are read at the broadcast index of (b,s,n,j).
- *   Arithmetic is fp32: 16-bit data is widened exactly, and each result is
- *   rounded once to fp32 and once, to nearest-even, to the storage type.
+ *   Arithmetic is fp32 (the page's mixed-precision paragraph: inputs are
+ *   cast to fp32 for the multiply-add and written back with round-to-
+ *   nearest-even). For 16-bit x each product is rounded to fp32, the sum is
+ *   rounded to fp32, and the result is rounded to nearest-even to the
+ *   storage type; with 16-bit tables the products are exact, so that is one
+ *   rounding of the exact sum. For fp32 x the multiply-add may be fused.
  *
  * Memory: every pointer is a device pointer on the current HIP device. The
  * caller owns all memory; the library allocates nothing and keeps no state
@@ -74,7 +78,9 @@ typedef enum rope_dtype {
  *   r*_strides   host arrays, strides in elements, each >= 0;
  *                r*_strides[3] must be 1. The stride of a size-1 dimension
  *                is ignored (this is what torch's expand() produces).
- *   table_dtype  must equal dtype (mixed precision is not built).
+ *   table_dtype  storage type of r1 and r2 (any of the three, independent
+ *                of dtype; the page's mixed case is 16-bit x with fp32
+ *                tables).
  *   mode         ROPE_MODE_INTERLEAVE or ROPE_MODE_ROTATE_HALF.
  *   partial_slice host array {start, end} or NULL, which means {0, 0}:
  *                0 <= start <= end <= D and L = end - start even.
@@ -85,8 +91,9 @@ typedef enum rope_dtype {
  * or an empty slice (L == 0) returns ROPE_OK at once without reading any
  * pointer (no-op, as the page specifies for forward and backward); then NULL
  * data or table pointers (ROPE_ERR_NULLPTR); then table shapes and strides
- * (ROPE_ERR_INVALID); then dtype support (ROPE_ERR_UNSUPPORTED); finally the
- * launch (ROPE_ERR_RUNTIME if HIP reports an error).
+ * (ROPE_ERR_INVALID); finally the launch (ROPE_ERR_RUNTIME if HIP reports
+ * an error). ROPE_ERR_UNSUPPORTED is reserved: no valid combination returns
+ * it at present.
  * Overlapping x with r1 or r2 is undefined. Results are deterministic: each
  * element is computed by one thread from the same inputs on every call.
  */
@@ -109,6 +116,20 @@ ROPE_API rope_status_t rope_partial_bwd_inplace(
     const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
     rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
     void* stream);
+
+/*
+ * rope_partial_check -- run every argument check of the entry points above
+ * (either direction: they are the same) and return the status they would
+ * return, without launching anything or touching device memory. For callers
+ * that validate ahead of time, as the page's graph-mode meta implementation
+ * does at compile time (section 调用说明, graph mode). Pointers are only
+ * compared with NULL.
+ */
+ROPE_API rope_status_t rope_partial_check(
+    const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2]);
 
 /* largest tensor count of the _multi entry points */
 #define ROPE_MULTI_MAX 4

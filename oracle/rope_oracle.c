@@ -27,8 +27,11 @@
  * Precision (P1, section Tiling 与 Kernel 的工程细节, mixed-precision
  * paragraph): 16-bit inputs are widened to fp32, the multiply-add runs in
  * fp32, and the result is written back with round-to-nearest-even. Here that
- * is: both products in fp32 (exact for 16-bit operands), one fp32 add, one RNE
- * narrowing. fp32 inputs are evaluated in fp64 and narrowed once to fp32.
+ * is, for 16-bit x: each product rounded to fp32, the sum rounded to fp32,
+ * one RNE narrowing. With 16-bit tables the products are exact (8x8 or
+ * 11x11 significand bits); with fp32 tables (P1's bf16/fp32 mixed case) their
+ * rounding is part of the definition. fp32 x is evaluated in fp64 and
+ * narrowed to fp32.
  *
  * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no contraction, so every
  * float operation below rounds exactly where it is written).
@@ -247,9 +250,9 @@ int rope_oracle_rows(void* x, const int64_t x_shape[4], int dtype,
                 double t = (double)sign * (double)xs[pj] * (double)sn;
                 y = (float)(a + t);
             } else {
-                float a = xs[j] * c;                 /* exact: 8x8 or 11x11 bits */
-                float t = (float)sign * xs[pj] * sn; /* exact */
-                y = a + t;                           /* the one fp32 rounding */
+                float a = xs[j] * c;                 /* fp32 product */
+                float t = (float)sign * xs[pj] * sn; /* fp32 product */
+                y = a + t;                           /* fp32 sum */
             }
             store_f(x, rowbase + j, dtype, y);       /* RNE to the storage type */
         }

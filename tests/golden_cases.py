@@ -24,12 +24,13 @@ def load(path: str) -> dict:
                 continue
             key, _, rest = line.partition(" ")
             vals = rest.split()
-            if key in ("dtype", "mode", "direction"):
+            if key in ("dtype", "table_dtype", "mode", "direction"):
                 case[key] = vals[0]
             elif key == "slice":
                 case[key] = (int(vals[0]), int(vals[1]))
             else:
                 case[key] = np.array([float(v) for v in vals], np.float64)
+    case.setdefault("table_dtype", case.get("dtype"))
     return case
 
 

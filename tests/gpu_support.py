@@ -93,11 +93,14 @@ def compare(got: np.ndarray, want: np.ndarray, x_in: np.ndarray, c: np.ndarray, 
     return info
 
 
+TDT = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
+
 def oracle_rows(x_rows: np.ndarray, x_shape, dtype: str, r1: torch.Tensor, r2: torch.Tensor, mode: str,
                 sl, direction: str, rows) -> np.ndarray:
     out = np.array(x_rows, copy=True)
     oracle.rope_rows(out, x_shape, dtype, W.to_numpy_storage(r1), W.to_numpy_storage(r2), mode, sl,
-                     direction, rows=rows)
+                     direction, rows=rows, table_dtype=TDT[r1.dtype])
     return out
 
 

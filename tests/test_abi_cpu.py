@@ -56,27 +56,31 @@ def test_status_strings():
 SAME = object()  # r2 geometry defaults to r1's
 
 
-def call(direction="fwd", x=FAKE, x_shape=(2, 4, 3, 64), dtype=BF16, r1=FAKE, r1_shape=(1, 4, 1, 32),
+def call(direction="check", x=FAKE, x_shape=(2, 4, 3, 64), dtype=BF16, r1=FAKE, r1_shape=(1, 4, 1, 32),
          r1_strides=(128, 32, 32, 1), r2=FAKE, r2_shape=SAME, r2_strides=SAME, table_dtype=None,
          mode=IL, sl=(0, 32)):
-    return rp.raw_call(direction, x, x_shape, dtype, r1, r1_shape, r1_strides, r2,
-                       r1_shape if r2_shape is SAME else r2_shape,
-                       r1_strides if r2_strides is SAME else r2_strides,
-                       dtype if table_dtype is None else table_dtype, mode, sl, None)
+    """direction "check" runs rope_partial_check (never launches); "fwd"/"bwd"
+    call the entry points and may only be used with arguments that fail
+    validation or are no-ops, so that nothing is ever launched here."""
+    args = (x, x_shape, dtype, r1, r1_shape, r1_strides, r2,
+            r1_shape if r2_shape is SAME else r2_shape,
+            r1_strides if r2_strides is SAME else r2_strides,
+            dtype if table_dtype is None else table_dtype, mode, sl)
+    if direction == "check":
+        return rp.raw_check(*args)
+    return rp.raw_call(direction, *args, None)
 
 
-# A table dtype different from x's is the last check before the launch, so a
-# call that reaches UNSUPPORTED has passed every geometry check.
-PASSES = dict(table_dtype=F32)
+@pytest.mark.parametrize("dtype", [F32, F16, BF16])
+@pytest.mark.parametrize("table_dtype", [F32, F16, BF16])
+def test_valid_arguments_pass_the_checks(dtype, table_dtype):
+    """Every x/table dtype pair is accepted (the page's mixed case is 16-bit x
+    with fp32 tables)."""
+    assert call(dtype=dtype, table_dtype=table_dtype) == OK
+    assert call(dtype=dtype, table_dtype=table_dtype, mode=RH) == OK
 
 
-@pytest.mark.parametrize("direction", ["fwd", "bwd"])
-def test_valid_geometry_reaches_dtype_check(direction):
-    assert call(direction, **PASSES) == UNSUPPORTED
-    assert "dtype" in rp.last_error()
-
-
-@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("direction", ["check", "fwd", "bwd"])
 @pytest.mark.parametrize("kwargs,code,text", [
     (dict(mode=2), INVALID, "mode"),
     (dict(mode=-1), INVALID, "mode"),
@@ -109,8 +113,9 @@ def test_scalar_argument_errors(direction, kwargs, code, text):
     (dict(r2_strides=(2**62, 2**62, 32, 1), r2_shape=(2, 4, 1, 32)), INVALID, "overflow"),
 ])
 def test_pointer_and_table_errors(kwargs, code, text):
-    assert call(**kwargs) == code
-    assert text in rp.last_error()
+    for direction in ("check", "fwd", "bwd"):
+        assert call(direction, **kwargs) == code
+        assert text in rp.last_error()
 
 
 @pytest.mark.parametrize("tshape,tstrides", [
@@ -122,10 +127,10 @@ def test_pointer_and_table_errors(kwargs, code, text):
     ((1, 4, 1, 32), (0, 32, 0, 1)),      # expand()-style zero strides
 ])
 def test_broadcast_layouts_accepted(tshape, tstrides):
-    assert call(r1_shape=tshape, r1_strides=tstrides, **PASSES) == UNSUPPORTED
+    assert call(r1_shape=tshape, r1_strides=tstrides) == OK
 
 
-@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("direction", ["check", "fwd", "bwd"])
 @pytest.mark.parametrize("kwargs", [
     dict(sl=(8, 8)),                            # empty slice
     dict(sl=(64, 64)),
@@ -185,9 +190,7 @@ def mcall(direction="fwd", ptrs=(FAKE, FAKE), shapes=((2, 4, 3, 64), (2, 4, 1, 6
 
 @pytest.mark.parametrize("direction", ["fwd", "bwd"])
 def test_multi_checks_every_tensor_first(direction):
-    # valid geometry for both tensors reaches the dtype check
-    assert mcall(direction, table_dtype=F32) == UNSUPPORTED
-    # the second tensor is named in the error
+    # the second tensor's error is returned before anything runs, and named
     assert mcall(direction, shapes=((2, 4, 3, 64), (2, 5, 1, 64))) == INVALID
     assert "tensor 1" in rp.last_error()
     assert mcall(direction, ptrs=(FAKE, None)) == NULLPTR and "tensor 1" in rp.last_error()

@@ -16,10 +16,12 @@ def test_golden_case(case):
     assert np.array_equal(widen(x, dt), case["x"]), "fixture value not exact in its type"
     D = x.size
     L = case["slice"][1] - case["slice"][0]
-    c = round_to(case["cos"], dt).reshape(1, 1, 1, L)
-    s = round_to(case["sin"], dt).reshape(1, 1, 1, L)
+    tt = case["table_dtype"]
+    c = round_to(case["cos"], tt).reshape(1, 1, 1, L)
+    s = round_to(case["sin"], tt).reshape(1, 1, 1, L)
+    assert np.array_equal(widen(c, tt).ravel(), case["cos"]), "table value not exact in its type"
     y = x.reshape(1, 1, 1, D).copy()
-    oracle.rope_rows(y, (1, 1, 1, D), dt, c, s, case["mode"], case["slice"], case["direction"])
+    oracle.rope_rows(y, (1, 1, 1, D), dt, c, s, case["mode"], case["slice"], case["direction"], table_dtype=tt)
     assert widen(y, dt).ravel().tolist() == case["expect"].tolist()
 
 

@@ -57,7 +57,8 @@ def _x(shape, dtype, seed, scale=1.0):
 
 def _run(x, shape, dtype, r1, r2, mode, sl, direction, rows=None):
     y = np.array(x, copy=True)
-    oracle.rope_rows(y, shape, dtype, r1, r2, mode, sl, direction, rows=rows)
+    tdt = "f32" if r1.dtype == np.float32 else dtype
+    oracle.rope_rows(y, shape, dtype, r1, r2, mode, sl, direction, rows=rows, table_dtype=tdt)
     return y
 
 
@@ -344,3 +345,54 @@ def test_workload_tables_follow_recipe():
         c, s = _rope_tables(w.x_shapes[0], w.L, w.mode, w.dtype, tshape=w.table_shape)
         assert W.to_numpy_storage(r1).tobytes() == c.tobytes(), name
         assert W.to_numpy_storage(r2).tobytes() == s.tobytes(), name
+
+
+# ---------------------------------------------------------------- mixed precision
+
+def _exact_rotation(xv, cv, sv, sl, mode, direction):
+    """fp64 rotation of widened values (exact products), for error bounds."""
+    L = sl[1] - sl[0]
+    if direction == "fwd":
+        return rotate_vector_form(xv, cv, sv, sl[0], sl[1], mode)
+    return backward_by_autograd(xv, cv, sv, sl[0], sl[1], mode)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("mode", ["interleave", "rotate_half"])
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_mixed_fp32_tables_within_one_ulp_of_exact(dtype, mode, direction):
+    """16-bit x with fp32 tables: the fp32 product and sum roundings stay
+    below one ulp of the 16-bit result, so the oracle is within 1 ulp of the
+    exact rotation rounded to the storage type."""
+    shape, sl = (2, 8, 4, 96), (16, 80)
+    L = sl[1] - sl[0]
+    rng = np.random.default_rng(21)
+    x = round_to(rng.standard_normal(shape), dtype)
+    th = rng.uniform(-np.pi, np.pi, (2, 8, 1, L))
+    c, s = np.cos(th).astype(np.float32), np.sin(th).astype(np.float32)
+    got = _run(x, shape, dtype, c, s, mode, sl, direction)
+    exact = _exact_rotation(widen(x, dtype), expand_tables(c.astype(np.float64), shape, L),
+                            expand_tables(s.astype(np.float64), shape, L), sl, mode, direction)
+    want = round_to(exact, dtype)
+    g = got.view(np.int16).astype(np.int64)
+    w = want.view(np.int16).astype(np.int64)
+    ordered = lambda i: np.where(i < 0, -32768 - i, i)
+    assert np.abs(ordered(g) - ordered(w)).max() <= 1
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_mixed_tables_holding_16_bit_values_match_16_bit_tables(dtype):
+    """fp32 tables whose values are 16-bit numbers give the 16-bit-table
+    result bit for bit (both products are then exact)."""
+    shape, sl = (2, 8, 4, 64), (0, 64)
+    rng = np.random.default_rng(22)
+    x = round_to(rng.standard_normal(shape), dtype)
+    c16 = round_to(rng.standard_normal((2, 8, 1, 64)), dtype)
+    s16 = round_to(rng.standard_normal((2, 8, 1, 64)), dtype)
+    c32, s32 = widen(c16, dtype).astype(np.float32), widen(s16, dtype).astype(np.float32)
+    for mode in ("interleave", "rotate_half"):
+        for direction in ("fwd", "bwd"):
+            a = _run(x, shape, dtype, c16, s16, mode, sl, direction)
+            b = np.array(x, copy=True)
+            oracle.rope_rows(b, shape, dtype, c32, s32, mode, sl, direction, table_dtype="f32")
+            assert a.tobytes() == b.tobytes()

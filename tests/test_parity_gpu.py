@@ -245,8 +245,8 @@ def test_errors_raise_before_touching_memory():
         rp.rope_partial_fwd_inplace(x, r, r, "interleave", (0, 30))        # table last dim != L
     assert e.value.status == rp.ROPE_ERR_INVALID
     with pytest.raises(rp.RopeError) as e:
-        rp.rope_partial_fwd_inplace(x, r.float(), r.float(), "interleave", (0, 32))
-    assert e.value.status == rp.ROPE_ERR_UNSUPPORTED
+        rp.rope_partial_fwd_inplace(x, r, r.float(), "interleave", (0, 32))    # r1 and r2 dtypes differ
+    assert e.value.status == rp.ROPE_ERR_INVALID
     torch.cuda.synchronize()
     assert torch.equal(x.view(torch.int16), before.view(torch.int16))
 
@@ -258,10 +258,49 @@ def test_golden_cases_on_gpu():
         D = case["x"].size
         L = case["slice"][1] - case["slice"][0]
         announce(f"golden {case['name']}")
+        tt = case["table_dtype"]
         x = torch.tensor(case["x"], dtype=torch.float64).to(DT[dt]).view(1, 1, 1, D).to(DEV)
-        c = torch.tensor(case["cos"], dtype=torch.float64).to(DT[dt]).view(1, 1, 1, L).to(DEV)
-        s = torch.tensor(case["sin"], dtype=torch.float64).to(DT[dt]).view(1, 1, 1, L).to(DEV)
+        c = torch.tensor(case["cos"], dtype=torch.float64).to(DT[tt]).view(1, 1, 1, L).to(DEV)
+        s = torch.tensor(case["sin"], dtype=torch.float64).to(DT[tt]).view(1, 1, 1, L).to(DEV)
         fn = rp.rope_partial_fwd_inplace if case["direction"] == "fwd" else rp.rope_partial_bwd_inplace
         fn(x, c, s, case["mode"], case["slice"])
         torch.cuda.synchronize()
         assert x.double().cpu().view(-1).tolist() == case["expect"].tolist(), case["name"]
+
+
+# ---------------------------------------------------------------- table dtypes other than x's
+
+MIXED = [("bf16", "f32"), ("f16", "f32"), ("f32", "bf16"), ("f32", "f16"), ("f16", "bf16"), ("bf16", "f16")]
+MIXED_CASES = [
+    ((2, 8, 4, 128), (32, 96), "interleave", (2, 8, 1, 64)),     # vector path (whole lines for f32 tables)
+    ((2, 8, 4, 128), (0, 128), "rotate_half", (1, 8, 1, 128)),   # vector path, rotate_half
+    ((2, 8, 4, 64), (0, 64), "interleave", (2, 8, 4, 64)),       # per-head tables
+    ((2, 6, 5, 64), (3, 35), "interleave", (1, 6, 1, 32)),       # odd start: scalar path
+]
+
+
+@pytest.mark.parametrize("dtype,tdtype", MIXED, ids=[f"{a}-x-{b}-tables" for a, b in MIXED])
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("case", MIXED_CASES, ids=[f"{c[0]}-{c[1]}-{c[2]}-{c[3]}" for c in MIXED_CASES])
+def test_mixed_table_dtypes(case, direction, dtype, tdtype):
+    shape, sl, mode, tshape = case
+    seed = zlib.crc32(repr((shape, sl, mode, tshape, dtype, tdtype)).encode()) % 10000
+    x = _rand(shape, dtype, seed)
+    r1 = _rand(tshape, tdtype, seed + 1)
+    r2 = _rand(tshape, tdtype, seed + 2)
+    info = run_and_check(x, r1, r2, mode, sl, direction, f"{dtype} x {tdtype} tables {shape} {sl} {mode}")
+    if dtype != "f32":
+        assert info["exact"] == info["n"]
+
+
+@pytest.mark.parametrize("direction", ["bwd", "fwd"])
+def test_c4_bf16_with_fp32_tables_full_size(direction):
+    """The page's mixed case at the long-context shape: bf16 dx, fp32 tables."""
+    from dataclasses import replace
+    w = replace(W.WORKLOADS["c4"], table_dtype="f32")
+    x = W.make_x(w)
+    r1, r2 = W.make_tables(w)
+    assert r1.dtype == torch.float32
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c4 fp32 tables {direction}",
+                         sample=4000, seed=41)
+    assert info["exact"] == info["n"]

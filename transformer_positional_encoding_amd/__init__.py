@@ -19,7 +19,7 @@ import os
 
 __all__ = [
     "rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string", "inplace_partial_rotary_mul",
-    "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi", "MULTI_MAX",
+    "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi", "MULTI_MAX", "rope_partial_check",
     "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
     "ROPE_ERR_UNSUPPORTED", "ROPE_ERR_RUNTIME", "MODES", "DTYPE_CODES",
 ]
@@ -71,6 +71,8 @@ def library() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p] + _ENTRY_ARGTYPES[2:]
+        L.rope_partial_check.restype = ctypes.c_int
+        L.rope_partial_check.argtypes = _ENTRY_ARGTYPES[:-1]
         L.rope_status_string.restype = ctypes.c_char_p
         L.rope_status_string.argtypes = [ctypes.c_int]
         L.rope_last_error.restype = ctypes.c_char_p
@@ -96,6 +98,16 @@ def raw_call(direction: str, x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_st
     sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
     return fn(x_ptr, _arr4(x_shape), int(dtype), r1_ptr, _arr4(r1_shape), _arr4(r1_strides),
               r2_ptr, _arr4(r2_shape), _arr4(r2_strides), int(table_dtype), int(mode), sl, stream)
+
+
+def raw_check(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2_ptr, r2_shape, r2_strides,
+              table_dtype: int, mode: int, partial_slice) -> int:
+    """rope_partial_check with plain integers and sequences (None = NULL):
+    the status the entry points would return, with nothing launched."""
+    sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
+    return library().rope_partial_check(x_ptr, _arr4(x_shape), int(dtype), r1_ptr, _arr4(r1_shape),
+                                        _arr4(r1_strides), r2_ptr, _arr4(r2_shape), _arr4(r2_strides),
+                                        int(table_dtype), int(mode), sl)
 
 
 def raw_multi_call(direction: str, x_ptrs, x_shapes, dtype: int, r1_ptr, r1_shape, r1_strides,
@@ -208,12 +220,27 @@ class _nullcontext:
         return False
 
 
+def rope_partial_check(x, r1, r2, rotary_mode="interleave", partial_slice=None) -> None:
+    """Run the entry points' argument checks on tensors (on any device:
+    nothing is launched or read); raises RopeError on the first failure."""
+    if isinstance(rotary_mode, str):
+        if rotary_mode not in MODES:
+            raise ValueError(f"rotary_mode must be one of {sorted(MODES)}")
+        rotary_mode = MODES[rotary_mode]
+    st = raw_check(x.data_ptr() or None, tuple(x.shape), _dtype_code(x), r1.data_ptr() or None, tuple(r1.shape),
+                   tuple(r1.stride()), r2.data_ptr() or None, tuple(r2.shape), tuple(r2.stride()),
+                   _dtype_code(r1) if r1.dtype == r2.dtype else -1, rotary_mode, partial_slice)
+    if st != ROPE_OK:
+        raise RopeError(st, last_error())
+
+
 def rope_partial_fwd_inplace(x, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:
     """Rotate ``x[..., start:end)`` in place (forward).
 
     x: contiguous (B,S,N,D) GPU tensor, float32/float16/bfloat16.
     r1, r2: cos and sin tables, 4-D, last dim ``end-start``, other dims 1 or
-    equal to x's (any strides, e.g. from ``expand``), same dtype as x.
+    equal to x's (any strides, e.g. from ``expand``); one dtype for both,
+    which may differ from x's (e.g. bf16 x with fp32 tables).
     rotary_mode: "interleave" (pairs 2i, 2i+1) or "rotate_half" (i, i+L/2).
     partial_slice: (start, end) or None for the empty slice [0, 0).
     stream: a torch stream or raw hipStream_t; default torch's current stream.

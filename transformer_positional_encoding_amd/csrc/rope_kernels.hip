@@ -142,12 +142,18 @@ struct Lanes {
 // partner term is negated in the forward (even lane / first half):
 //   forward : a' = a*c_a - b*s_a        b' = b*c_b + a*s_b
 //   backward: a' = a*c_a + b*s_b        b' = b*c_b - a*s_a   (transpose)
-// Both products of a 16-bit pair are exact in fp32, so the single fp32
-// rounding of the sum (fused or not) is the only rounding before the store.
+// 16-bit x (UNFUSED): each product is rounded to fp32 and the sum is rounded
+// once more, as the page's "cast to fp32, multiply-add in fp32" reads. With
+// 16-bit tables both products are exact, so this is also the single
+// rounding of the exact sum; with fp32 tables the product roundings are part
+// of the definition. fp32 x: the compiler may fuse (the result is held to a
+// tolerance, not to bits).
 // ---------------------------------------------------------------------------
 template <int DIR>
-__device__ __forceinline__ void rotate_pair(float& a, float& b, float ca, float sa, float cb, float sb)
+__device__ __forceinline__ void rotate_pair_unfused(float& a, float& b, float ca, float sa, float cb, float sb)
 {
+#pragma clang fp contract(off)
+    // no fused multiply-add in this function: every product and sum rounds
     float na, nb;
     if constexpr (DIR == kFwd) {
         na = a * ca - b * sa;
@@ -159,6 +165,51 @@ __device__ __forceinline__ void rotate_pair(float& a, float& b, float ca, float 
     a = na;
     b = nb;
 }
+
+template <int DIR, bool UNFUSED>
+__device__ __forceinline__ void rotate_pair(float& a, float& b, float ca, float sa, float cb, float sb)
+{
+    if constexpr (UNFUSED) {
+        rotate_pair_unfused<DIR>(a, b, ca, sa, cb, sb);
+    } else {
+        float na, nb;
+        if constexpr (DIR == kFwd) {
+            na = a * ca - b * sa;
+            nb = b * cb + a * sb;
+        } else {
+            na = a * ca + b * sb;
+            nb = b * cb - a * sa;
+        }
+        a = na;
+        b = nb;
+    }
+}
+
+// The cos or sin values for the K lanes of one x vector, from a table of
+// type TT: one 16-byte vector when the table is as wide as x, two when 16-bit
+// x meets an fp32 table (the page's mixed bf16-x / fp32-table case).
+template <int TT, int K>
+struct TableLanes {
+    static constexpr int kVecs = K * (TT == ROPE_DTYPE_F32 ? 4 : 2) / 16;
+    static_assert(kVecs == 1 || kVecs == 2, "table vector shape");
+    float v[K];
+    __device__ void unpack(const v4u* q)
+    {
+        if constexpr (TT == ROPE_DTYPE_F32) {
+#pragma unroll
+            for (int t = 0; t < kVecs; ++t)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) v[4 * t + w] = __uint_as_float(q[t][w]);
+        } else {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                f32x2 f = Store<TT>::widen(q[0][w]);
+                v[2 * w] = f.x;
+                v[2 * w + 1] = f.y;
+            }
+        }
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Vector kernel. Work unit = one 16-byte vector of the slice (interleave:
@@ -206,9 +257,10 @@ struct VecArgs {
     uint32_t row_vecs;      // vectors per row of x (D*esize/16)
     uint32_t start_vec;     // first slice vector within a row
     uint32_t lo_vec;        // first vector the threads of a row cover
-    uint32_t half_vecs;     // rotate_half: vectors per half of the slice
-    uint32_t t1b, t1s, t1n; // cos strides in vectors (0 = broadcast)
-    uint32_t t2b, t2s, t2n; // sin strides in vectors
+    uint32_t half_vecs;     // rotate_half: x vectors per half of the slice
+    uint32_t thalf;         // rotate_half: table vectors per half of the slice
+    uint32_t t1b, t1s, t1n; // cos strides in table vectors (0 = broadcast)
+    uint32_t t2b, t2s, t2n; // sin strides in table vectors
     uint32_t N;
     uint32_t nvec;          // work units per row (in the slice)
     uint32_t span;          // vectors per row the threads cover (>= nvec)
@@ -236,10 +288,12 @@ __device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t bid, uint32_t 
 
 // The kernel body for one tensor: `bid` is the block's number among the G
 // blocks that work on this tensor.
-template <int DT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
+template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
 __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_t G)
 {
     constexpr int K = Store<DT>::kLanes;
+    constexpr int TV = TableLanes<TT, K>::kVecs;      // table vectors per x vector
+    constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
     const uint32_t t = threadIdx.x;
     const uint32_t q = fast_div(t, a.span_div);
     const uint32_t vs = t - q * a.span;
@@ -259,23 +313,26 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
         const uint32_t b = fast_div(g, a.s_div);
         const uint32_t s = g - b * a.s_div.d;
         const uint32_t n0 = chunk * (a.HL * U) + hl;
-        const uint32_t c_base = b * a.t1b + s * a.t1s + v;
-        const uint32_t s_base = b * a.t2b + s * a.t2s + v;
+        const uint32_t c_base = b * a.t1b + s * a.t1s + v * TV;
+        const uint32_t s_base = b * a.t2b + s * a.t2s + v * TV;
         const uint32_t row0 = g * a.N;
 
         // All loads are issued back to back with no branch between them: a
         // head past N (ragged last chunk) re-reads row N-1 and skips its
         // store. The tables come first, then the x vectors.
         v4u xa[U], xb[U];
-        v4u ca[U], sa[U], cb[U], sb[U];
+        v4u ca[U][TV], sa[U][TV], cb[U][TV], sb[U][TV];
         uint32_t off[U];
         bool live[U];
         if constexpr (HEADS_SHARE_TABLES) {
-            ca[0] = a.r1[c_base];
-            sa[0] = a.r2[s_base];
-            if constexpr (MODE == kModeRH) {
-                cb[0] = a.r1[c_base + a.half_vecs];
-                sb[0] = a.r2[s_base + a.half_vecs];
+#pragma unroll
+            for (int t = 0; t < TV; ++t) {
+                ca[0][t] = a.r1[c_base + t];
+                sa[0][t] = a.r2[s_base + t];
+                if constexpr (MODE == kModeRH) {
+                    cb[0][t] = a.r1[c_base + a.thalf + t];
+                    sb[0][t] = a.r2[s_base + a.thalf + t];
+                }
             }
         }
 #pragma unroll
@@ -285,11 +342,14 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
             const uint32_t nl = live[k] ? n : a.N - 1;
             off[k] = (row0 + nl) * a.row_vecs + c;
             if constexpr (!HEADS_SHARE_TABLES) {
-                ca[k] = a.r1[c_base + nl * a.t1n];
-                sa[k] = a.r2[s_base + nl * a.t2n];
-                if constexpr (MODE == kModeRH) {
-                    cb[k] = a.r1[c_base + nl * a.t1n + a.half_vecs];
-                    sb[k] = a.r2[s_base + nl * a.t2n + a.half_vecs];
+#pragma unroll
+                for (int t = 0; t < TV; ++t) {
+                    ca[k][t] = a.r1[c_base + nl * a.t1n + t];
+                    sa[k][t] = a.r2[s_base + nl * a.t2n + t];
+                    if constexpr (MODE == kModeRH) {
+                        cb[k][t] = a.r1[c_base + nl * a.t1n + a.thalf + t];
+                        sb[k][t] = a.r2[s_base + nl * a.t2n + a.thalf + t];
+                    }
                 }
             }
             xa[k] = load_x<NT>(a.x + off[k]);
@@ -304,23 +364,25 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
         for (int k = 0; k < U; ++k) {
             if (!live[k] || !in_slice) continue;
             const int kt = HEADS_SHARE_TABLES ? 0 : k;
-            Lanes<DT> X, C, S;
+            Lanes<DT> X;
+            TableLanes<TT, K> C, S;
             X.unpack(xa[k]);
             C.unpack(ca[kt]);
             S.unpack(sa[kt]);
             if constexpr (MODE == kModeIL) {
 #pragma unroll
                 for (int i = 0; i < K; i += 2)
-                    rotate_pair<DIR>(X.v[i], X.v[i + 1], C.v[i], S.v[i], C.v[i + 1], S.v[i + 1]);
+                    rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C.v[i], S.v[i], C.v[i + 1], S.v[i + 1]);
                 store_x<NT>(a.x + off[k], X.pack());
             } else {
-                Lanes<DT> X2, C2, S2;
+                Lanes<DT> X2;
+                TableLanes<TT, K> C2, S2;
                 X2.unpack(xb[k]);
                 C2.unpack(cb[kt]);
                 S2.unpack(sb[kt]);
 #pragma unroll
                 for (int i = 0; i < K; ++i)
-                    rotate_pair<DIR>(X.v[i], X2.v[i], C.v[i], S.v[i], C2.v[i], S2.v[i]);
+                    rotate_pair<DIR, kUnfused>(X.v[i], X2.v[i], C.v[i], S.v[i], C2.v[i], S2.v[i]);
                 store_x<NT>(a.x + off[k], X.pack());
                 store_x<NT>(a.x + off[k] + a.half_vecs, X2.pack());
             }
@@ -328,10 +390,10 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
     }
 }
 
-template <int DT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
+template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
 __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
 {
-    vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(a, blockIdx.x, gridDim.x);
+    vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(a, blockIdx.x, gridDim.x);
 }
 
 // Several tensors that share the tables (the Q and K of one layer) in one
@@ -346,7 +408,7 @@ struct MultiVecArgs {
     VecArgs a[kMultiMax];
 };
 
-template <int DT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
+template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
 __global__ void __launch_bounds__(256) rope_vec_multi_kernel(MultiVecArgs m)
 {
     const uint32_t b = blockIdx.x;
@@ -356,10 +418,10 @@ __global__ void __launch_bounds__(256) rope_vec_multi_kernel(MultiVecArgs m)
         i += (k < (int)m.count && b >= m.first_block[k]) ? 1u : 0u;
     const uint32_t lo = m.first_block[i], G = m.first_block[i + 1] - lo;
     switch (i) {
-    case 0: vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[0], b - lo, G); break;
-    case 1: vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[1], b - lo, G); break;
-    case 2: vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[2], b - lo, G); break;
-    default: vec_body<DT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[3], b - lo, G); break;
+    case 0: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[0], b - lo, G); break;
+    case 1: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[1], b - lo, G); break;
+    case 2: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[2], b - lo, G); break;
+    default: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[3], b - lo, G); break;
     }
 }
 
@@ -378,7 +440,7 @@ struct ScalarArgs {
     int64_t t2b, t2s, t2n;
 };
 
-template <int DT, int DIR, int MODE>
+template <int DT, int TT, int DIR, int MODE>
 __global__ void __launch_bounds__(256) rope_scalar_kernel(ScalarArgs a)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -396,9 +458,9 @@ __global__ void __launch_bounds__(256) rope_scalar_kernel(ScalarArgs a)
         const int64_t so = b * a.t2b + s * a.t2s + n * a.t2n;
         float xa = Store<DT>::load1(a.x, xo + j);
         float xb = Store<DT>::load1(a.x, xo + pj);
-        const float ca = Store<DT>::load1(a.r1, co + j), cb = Store<DT>::load1(a.r1, co + pj);
-        const float sa = Store<DT>::load1(a.r2, so + j), sb = Store<DT>::load1(a.r2, so + pj);
-        rotate_pair<DIR>(xa, xb, ca, sa, cb, sb);
+        const float ca = Store<TT>::load1(a.r1, co + j), cb = Store<TT>::load1(a.r1, co + pj);
+        const float sa = Store<TT>::load1(a.r2, so + j), sb = Store<TT>::load1(a.r2, so + pj);
+        rotate_pair<DIR, DT != ROPE_DTYPE_F32>(xa, xb, ca, sa, cb, sb);
         Store<DT>::store1(a.x, xo + j, xa);
         Store<DT>::store1(a.x, xo + pj, xb);
     }
@@ -443,25 +505,29 @@ struct VecConfig {
 };
 
 // Can the 16-byte vector kernel run this plan? Fills the geometry of `a`.
+// Table types: the same as x, or fp32 with 16-bit x; other mixes take the
+// scalar kernel.
 bool vec_geometry(const Plan& p, VecArgs* a)
 {
-    const int64_t es = p.esize;
+    const int64_t es = p.esize, ts = p.tesize;
+    if (!(p.tdtype == p.dtype || (p.tdtype == ROPE_DTYPE_F32 && p.dtype != ROPE_DTYPE_F32))) return false;
+    const int64_t tv = ts / es;   // table vectors per x vector: 1 or 2
     if (!aligned16(p.x) || !aligned16(p.r1) || !aligned16(p.r2)) return false;
     if ((p.D * es) % 16 || (p.start * es) % 16) return false;
     const int64_t unit_bytes = p.mode == kModeIL ? p.L * es : (p.L / 2) * es;
     if (unit_bytes % 16) return false;
     for (int k = 0; k < 3; ++k)
-        if ((p.t1[k] * es) % 16 || (p.t2[k] * es) % 16) return false;
+        if ((p.t1[k] * ts) % 16 || (p.t2[k] * ts) % 16) return false;
     // 32-bit vector offsets: x and each table must span fewer than 2^32
     // vectors; tile indices stay below 2^31 (checked in finish_vec_args).
     const int64_t kMax = (1ll << 32) - 1;
     const int64_t x_vecs = p.B * p.S * p.N * (p.D * es / 16);
     if (x_vecs > kMax || p.N >= (1ll << 31) || p.S >= (1ll << 31) || p.B * p.S >= (1ll << 31)) return false;
     const int64_t dims[3] = {p.B, p.S, p.N};
-    int64_t t1_span = p.L * es / 16, t2_span = p.L * es / 16;
+    int64_t t1_span = p.L * ts / 16, t2_span = p.L * ts / 16;
     for (int k = 0; k < 3; ++k) {
-        t1_span += (dims[k] - 1) * (p.t1[k] * es / 16);
-        t2_span += (dims[k] - 1) * (p.t2[k] * es / 16);
+        t1_span += (dims[k] - 1) * (p.t1[k] * ts / 16);
+        t2_span += (dims[k] - 1) * (p.t2[k] * ts / 16);
     }
     if (t1_span > kMax || t2_span > kMax) return false;
     a->x = static_cast<v4u*>(p.x);
@@ -471,10 +537,11 @@ bool vec_geometry(const Plan& p, VecArgs* a)
     a->start_vec = (uint32_t)(p.start * es / 16);
     a->lo_vec = a->start_vec;
     a->half_vecs = p.mode == kModeRH ? (uint32_t)((p.L / 2) * es / 16) : 0;
-    a->t1b = (uint32_t)(p.t1[0] * es / 16); a->t1s = (uint32_t)(p.t1[1] * es / 16);
-    a->t1n = (uint32_t)(p.t1[2] * es / 16);
-    a->t2b = (uint32_t)(p.t2[0] * es / 16); a->t2s = (uint32_t)(p.t2[1] * es / 16);
-    a->t2n = (uint32_t)(p.t2[2] * es / 16);
+    a->thalf = (uint32_t)(a->half_vecs * tv);
+    a->t1b = (uint32_t)(p.t1[0] * ts / 16); a->t1s = (uint32_t)(p.t1[1] * ts / 16);
+    a->t1n = (uint32_t)(p.t1[2] * ts / 16);
+    a->t2b = (uint32_t)(p.t2[0] * ts / 16); a->t2s = (uint32_t)(p.t2[1] * ts / 16);
+    a->t2n = (uint32_t)(p.t2[2] * ts / 16);
     a->N = (uint32_t)p.N;
     a->s_div = make_fastdiv((uint32_t)p.S);
     a->nvec = (uint32_t)(unit_bytes / 16);
@@ -536,7 +603,7 @@ VecConfig choose_vec_config(const Plan& p, const VecArgs& a)
 // gridDim.x to it), in which case the scalar kernel runs instead.
 bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
 {
-    if (cfg.U < 1 || cfg.U > 4 || (cfg.U & (cfg.U - 1)) || cfg.HL < 1 || cfg.GL < 1 ||
+    if (cfg.U < 1 || cfg.U > 2 || cfg.HL < 1 || cfg.GL < 1 ||
         (uint64_t)cfg.HL * cfg.GL * a->span > 256)
         return false;
     a->HL = cfg.HL;
@@ -555,50 +622,54 @@ bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
     return true;
 }
 
-template <int DT, int DIR, int MODE, int U, bool SHARE, bool NT>
+template <int DT, int TT, int DIR, int MODE, int U, bool SHARE, bool NT>
 const void* vec_kernel_ptr(bool multi)
 {
-    return multi ? reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, DIR, MODE, U, SHARE, NT>)
-                 : reinterpret_cast<const void*>(&rope_vec_kernel<DT, DIR, MODE, U, SHARE, NT>);
+    return multi ? reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, TT, DIR, MODE, U, SHARE, NT>)
+                 : reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, U, SHARE, NT>);
 }
 
-template <int DT, int DIR, int MODE, int U>
+template <int DT, int TT, int DIR, int MODE, int U>
 const void* vec_kernel_u(bool share, bool nt, bool multi)
 {
     if (share)
-        return nt ? vec_kernel_ptr<DT, DIR, MODE, U, true, true>(multi)
-                  : vec_kernel_ptr<DT, DIR, MODE, U, true, false>(multi);
-    return nt ? vec_kernel_ptr<DT, DIR, MODE, U, false, true>(multi)
-              : vec_kernel_ptr<DT, DIR, MODE, U, false, false>(multi);
+        return nt ? vec_kernel_ptr<DT, TT, DIR, MODE, U, true, true>(multi)
+                  : vec_kernel_ptr<DT, TT, DIR, MODE, U, true, false>(multi);
+    return nt ? vec_kernel_ptr<DT, TT, DIR, MODE, U, false, true>(multi)
+              : vec_kernel_ptr<DT, TT, DIR, MODE, U, false, false>(multi);
 }
 
-template <int DT, int DIR, int MODE>
-const void* vec_kernel_m(int U, bool share, bool nt, bool multi)
+template <int DT, int TT>
+const void* vec_kernel_t(int dir, int mode, int U, bool share, bool nt, bool multi)
 {
-    switch (U) {
-    case 1: return vec_kernel_u<DT, DIR, MODE, 1>(share, nt, multi);
-    case 2: return vec_kernel_u<DT, DIR, MODE, 2>(share, nt, multi);
-    default: return vec_kernel_u<DT, DIR, MODE, 4>(share, nt, multi);
+    // heads per thread: 1 (the chosen shape) or 2 (kept for launch-shape studies)
+    if (dir == kFwd) {
+        if (mode == kModeIL)
+            return U == 1 ? vec_kernel_u<DT, TT, kFwd, kModeIL, 1>(share, nt, multi)
+                          : vec_kernel_u<DT, TT, kFwd, kModeIL, 2>(share, nt, multi);
+        return U == 1 ? vec_kernel_u<DT, TT, kFwd, kModeRH, 1>(share, nt, multi)
+                      : vec_kernel_u<DT, TT, kFwd, kModeRH, 2>(share, nt, multi);
     }
-}
-
-template <int DT>
-const void* vec_kernel_dt(int dir, int mode, int U, bool share, bool nt, bool multi)
-{
-    if (dir == kFwd)
-        return mode == kModeIL ? vec_kernel_m<DT, kFwd, kModeIL>(U, share, nt, multi)
-                               : vec_kernel_m<DT, kFwd, kModeRH>(U, share, nt, multi);
-    return mode == kModeIL ? vec_kernel_m<DT, kBwd, kModeIL>(U, share, nt, multi)
-                           : vec_kernel_m<DT, kBwd, kModeRH>(U, share, nt, multi);
+    if (mode == kModeIL)
+        return U == 1 ? vec_kernel_u<DT, TT, kBwd, kModeIL, 1>(share, nt, multi)
+                      : vec_kernel_u<DT, TT, kBwd, kModeIL, 2>(share, nt, multi);
+    return U == 1 ? vec_kernel_u<DT, TT, kBwd, kModeRH, 1>(share, nt, multi)
+                  : vec_kernel_u<DT, TT, kBwd, kModeRH, 2>(share, nt, multi);
 }
 
 const void* vec_kernel(const Plan& p, const VecConfig& cfg, bool multi)
 {
     const bool share = p.t1[2] == 0 && p.t2[2] == 0;
+    const bool f32_tables = p.tdtype == ROPE_DTYPE_F32;
     switch (p.dtype) {
-    case ROPE_DTYPE_F32: return vec_kernel_dt<ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
-    case ROPE_DTYPE_F16: return vec_kernel_dt<ROPE_DTYPE_F16>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
-    default: return vec_kernel_dt<ROPE_DTYPE_BF16>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
+    case ROPE_DTYPE_F32:
+        return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
+    case ROPE_DTYPE_F16:
+        return f32_tables ? vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt, multi)
+                          : vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F16>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
+    default:
+        return f32_tables ? vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt, multi)
+                          : vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_BF16>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
     }
 }
 
@@ -619,22 +690,24 @@ hipError_t launch_vec(const Plan& p, const VecArgs& a, const VecConfig& cfg, hip
     return hipLaunchKernel(vec_kernel(p, cfg, false), dim3(vec_grid(a, cfg)), dim3(threads), args, 0, stream);
 }
 
-template <int DT, int DIR, int MODE>
-hipError_t launch_scalar_t(const ScalarArgs& a, dim3 grid, dim3 block, hipStream_t stream)
+template <int DT, int TT>
+const void* scalar_kernel_t(int dir, int mode)
 {
-    void* args[] = {const_cast<ScalarArgs*>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&rope_scalar_kernel<DT, DIR, MODE>), grid, block,
-                           args, 0, stream);
+    if (dir == kFwd)
+        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kFwd, kModeIL>)
+                               : reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kFwd, kModeRH>);
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kBwd, kModeIL>)
+                           : reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kBwd, kModeRH>);
 }
 
 template <int DT>
-hipError_t launch_scalar_dt(const Plan& p, const ScalarArgs& a, dim3 grid, dim3 block, hipStream_t stream)
+const void* scalar_kernel_dt(int tt, int dir, int mode)
 {
-    if (p.dir == kFwd)
-        return p.mode == kModeIL ? launch_scalar_t<DT, kFwd, kModeIL>(a, grid, block, stream)
-                                 : launch_scalar_t<DT, kFwd, kModeRH>(a, grid, block, stream);
-    return p.mode == kModeIL ? launch_scalar_t<DT, kBwd, kModeIL>(a, grid, block, stream)
-                             : launch_scalar_t<DT, kBwd, kModeRH>(a, grid, block, stream);
+    switch (tt) {
+    case ROPE_DTYPE_F32: return scalar_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode);
+    case ROPE_DTYPE_F16: return scalar_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode);
+    default: return scalar_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode);
+    }
 }
 
 hipError_t launch_scalar(const Plan& p, int cus, hipStream_t stream)
@@ -649,12 +722,14 @@ hipError_t launch_scalar(const Plan& p, int cus, hipStream_t stream)
     const uint32_t threads = 256;
     uint64_t grid = (uint64_t)cus * 8;
     grid = std::max<uint64_t>(1, std::min<uint64_t>(grid, (a.items + threads - 1) / threads));
-    const dim3 g((uint32_t)grid), b(threads);
+    const void* fn;
     switch (p.dtype) {
-    case ROPE_DTYPE_F32: return launch_scalar_dt<ROPE_DTYPE_F32>(p, a, g, b, stream);
-    case ROPE_DTYPE_F16: return launch_scalar_dt<ROPE_DTYPE_F16>(p, a, g, b, stream);
-    default: return launch_scalar_dt<ROPE_DTYPE_BF16>(p, a, g, b, stream);
+    case ROPE_DTYPE_F32: fn = scalar_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode); break;
+    case ROPE_DTYPE_F16: fn = scalar_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode); break;
+    default: fn = scalar_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode); break;
     }
+    void* args[] = {&a};
+    return hipLaunchKernel(fn, dim3((uint32_t)grid), dim3(threads), args, 0, stream);
 }
 
 // One tensor's launch, decided on the host.
@@ -812,6 +887,19 @@ rope_status_t rope_partial_bwd_inplace_multi(int32_t count, void* const xs[], co
 {
     return rope::run_multi(count, xs, x_shapes, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides,
                            table_dtype, mode, partial_slice, stream, rope::kBwd);
+}
+
+rope_status_t rope_partial_check(const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                 const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                                 const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                                 rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2])
+{
+    rope::Plan p;
+    std::string why;
+    rope_status_t st = rope::make_plan(const_cast<void*>(x), x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape,
+                                       r2_strides, table_dtype, mode, partial_slice, rope::kFwd, &p, &why);
+    if (st != ROPE_OK) return rope::set_error(st, why);
+    return ROPE_OK;
 }
 
 const char* rope_status_string(rope_status_t status)

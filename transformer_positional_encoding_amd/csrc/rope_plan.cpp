@@ -1,5 +1,6 @@
 // Argument checking for the C ABI (see rope_plan.hpp). Order of checks:
-// scalars -> no-op -> pointers -> table geometry -> dtype support.
+// scalars -> no-op -> pointers -> table geometry. Every combination of
+// x and table dtypes is accepted (r1 and r2 share one).
 #include "rope_plan.hpp"
 
 #include <limits>
@@ -114,8 +115,9 @@ rope_status_t make_plan(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
     Plan p;
     p.B = x_shape[0]; p.S = x_shape[1]; p.N = x_shape[2]; p.D = D;
     p.start = start; p.L = L;
-    p.dtype = dtype; p.mode = (int)mode; p.dir = dir;
+    p.dtype = dtype; p.tdtype = table_dtype; p.mode = (int)mode; p.dir = dir;
     p.esize = element_size(dtype);
+    p.tesize = element_size(table_dtype);
 
     // 2. no-op: nothing to rotate; pointers and tables are not looked at
     if (numel == 0 || L == 0) {
@@ -138,10 +140,6 @@ rope_status_t make_plan(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
     if (st != ROPE_OK) return st;
     st = check_table("r2", r2_shape, r2_strides, x_shape, L, p.t2, why);
     if (st != ROPE_OK) return st;
-
-    // 5. dtype support
-    if (table_dtype != dtype)
-        return fail(ROPE_ERR_UNSUPPORTED, why, "r1/r2 must have the dtype of x");
 
     p.x = x; p.r1 = r1; p.r2 = r2;
     *plan = p;

@@ -18,10 +18,12 @@ enum Direction : int { kFwd = 0, kBwd = 1 };
 struct Plan {
     int64_t B = 0, S = 0, N = 0, D = 0;
     int64_t start = 0, L = 0;
-    int dtype = 0;           // rope_dtype_t
+    int dtype = 0;           // rope_dtype_t of x
+    int tdtype = 0;          // rope_dtype_t of r1 and r2
     int mode = 0;            // ROPE_MODE_*
     int dir = kFwd;
-    int esize = 0;           // bytes per element
+    int esize = 0;           // bytes per element of x
+    int tesize = 0;          // bytes per element of the tables
     bool noop = false;       // empty tensor or empty slice: launch nothing
     void* x = nullptr;
     const void* r1 = nullptr;

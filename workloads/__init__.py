@@ -113,6 +113,9 @@ WORKLOADS: dict[str, Workload] = {
 }
 WORKLOADS["c4_f32"] = replace(WORKLOADS["c4"], name="c4_f32", dtype="f32",
                               note="long-context shard, fp32 rerun")
+# The page's mixed-precision case at the long-context shape: bf16 dx, fp32 tables.
+WORKLOADS["c4_t32"] = replace(WORKLOADS["c4"], name="c4_t32", table_dtype="f32",
+                              note="long-context shard, bf16 dx with fp32 tables")
 
 
 def generator(seed: int) -> torch.Generator:
