@@ -304,3 +304,31 @@ def test_c4_bf16_with_fp32_tables_full_size(direction):
     info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c4 fp32 tables {direction}",
                          sample=4000, seed=41)
     assert info["exact"] == info["n"]
+
+
+# ---------------------------------------------------------------- the largest head dimension
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mode,sl", [("interleave", (0, 1024)), ("rotate_half", (0, 1024)),
+                                     ("interleave", (8, 1016)), ("interleave", (1000, 1024))])
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_head_dim_limit(dtype, mode, sl, direction):
+    """D = 1024, the constraint's limit: a full-width fp32 interleave slice
+    needs 256 threads per row (the kernel's block limit)."""
+    shape = (2, 3, 5, 1024)
+    L = sl[1] - sl[0]
+    seed = zlib.crc32(repr((dtype, mode, sl, direction)).encode()) % 10000
+    x = _rand(shape, dtype, seed)
+    r1 = _rand((1, 3, 1, L), dtype, seed + 1)
+    r2 = _rand((1, 3, 1, L), dtype, seed + 2)
+    info = run_and_check(x, r1, r2, mode, sl, direction, f"D=1024 {dtype} {mode} {sl}")
+    if dtype != "f32":
+        assert info["exact"] == info["n"]
+
+
+def test_d_over_limit_is_rejected():
+    x = torch.zeros((1, 1, 1, 1026), dtype=torch.bfloat16, device=DEV)
+    r = torch.zeros((1, 1, 1, 2), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(rp.RopeError) as e:
+        rp.rope_partial_fwd_inplace(x, r, r, "interleave", (0, 2))
+    assert e.value.status == rp.ROPE_ERR_INVALID
