@@ -269,21 +269,29 @@ struct VecArgs {
     uint32_t nchunk;        // head chunks per (b,s)
     uint32_t tiles;         // B*S*nchunk
     uint32_t btiles;        // ceil(tiles / GL)
-    uint32_t xcd_remap;     // 1: give each XCD a contiguous range of tile groups
+    uint32_t xcd_group;     // P: runs of P consecutive blocks stay on one XCD
+    uint32_t xcd_full;      // blocks [0, xcd_full) are renumbered (a multiple of 8P)
     FastDiv span_div, hl_div, nchunk_div, s_div;  // divisions by span, HL, nchunk, S
+    FastDiv xcd_div;        // division by 8P
 };
 
 // Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
-// XCD i % 8), and each XCD has its own L2. Neighbouring tiles share table
-// rows (the head chunks of one (b,s) position, or one s across batches), so
-// renumber the blocks so that XCD x processes a contiguous range of tile
-// groups: the table rows of a range are then fetched into one L2 only.
-// The map is a bijection of [0, G).
-__device__ __forceinline__ uint32_t xcd_contiguous_block(uint32_t bid, uint32_t G)
+// XCD i % 8), and each XCD has its own L2. The head chunks of one (b,s)
+// position are consecutive tiles that read the same table row. Renumber the
+// blocks in windows of 8P: within a window, XCD x takes the P consecutive
+// tile groups [xP, xP + P). With P a whole number of positions, a table row
+// is fetched into one L2 only (dispatch order, P = 1, fetches it into every
+// L2), and the 8 XCDs stream through one window of x together. Measured on
+// MI355X for a bare whole-line read-modify-write of 1 GiB of 256-byte rows:
+// one contiguous eighth of the grid per XCD (P = G/8) was 12% slower than
+// dispatch order. The map is a bijection of [0, G); blocks past the last
+// whole window keep their number.
+__device__ __forceinline__ uint32_t xcd_grouped_block(uint32_t bid, const VecArgs& a)
 {
-    constexpr uint32_t kXcds = 8;
-    const uint32_t q = G / kXcds, r = G % kXcds, x = bid % kXcds;
-    return x * q + min(x, r) + bid / kXcds;
+    if (bid >= a.xcd_full) return bid;
+    const uint32_t w = fast_div(bid, a.xcd_div);     // window
+    const uint32_t l = bid - w * a.xcd_div.d;        // place in the window
+    return w * a.xcd_div.d + (l & 7u) * a.xcd_group + (l >> 3);
 }
 
 // The kernel body for one tensor: `bid` is the block's number among the G
@@ -304,7 +312,7 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
     const uint32_t v = in_slice ? c - a.start_vec : 0;  // table vector (unused outside)
     if (gl >= a.GL) return;  // no barriers below, so idle threads may leave
 
-    const uint32_t first = a.xcd_remap ? xcd_contiguous_block(bid, G) : bid;
+    const uint32_t first = xcd_grouped_block(bid, a);
     for (uint32_t bt = first; bt < a.btiles; bt += G) {
         const uint32_t tile = bt * a.GL + gl;
         if (tile >= a.tiles) continue;
@@ -500,7 +508,7 @@ struct VecConfig {
     uint32_t HL = 1;    // head lanes per tile
     uint32_t GL = 1;    // tiles per block iteration
     uint32_t grid = 0;  // blocks; 0 = one block per tile group
-    bool xcd_remap = true;
+    uint32_t xcd_group = 1;  // P of the XCD renumbering (1: dispatch order)
     bool nt = false;    // nontemporal loads/stores of x
 };
 
@@ -582,20 +590,45 @@ VecConfig shape_for(const VecArgs& a, int U, uint32_t threads)
 }
 
 // The launch shape. Measured on MI355X with every launch reading data that
-// no cache holds (the slices of several shapes: 1/3 and 1/2 of the row,
-// whole and half 128-byte lines, bf16 and fp32, tables shared or per batch),
-// sweeping heads per thread (1-8), block size (64-256), nontemporal x and
-// XCD renumbering: one head per thread, 64-thread blocks, nontemporal x and
-// XCD-contiguous blocks was within 3% of the best shape on every one.
-// Streaming x past the caches leaves the L2 to the tables, and small blocks
-// let the dispatcher keep every CU's load queues full.
+// no cache holds (the slices of several shapes: 1/4, 1/3, 1/2 and all of the
+// row, whole and half 128-byte lines, bf16 and fp32, tables shared or per
+// batch), sweeping heads per thread (1-8), block size (64-256) and
+// nontemporal x: one head per thread, 64-thread blocks and nontemporal x was
+// within 3% of the best shape on every one. Streaming x past the caches
+// leaves the L2 to the tables, and small blocks let the dispatcher keep
+// every CU's load queues full.
+//
+// XCD runs (see xcd_grouped_block): each XCD takes about kXcdRunBytes of
+// consecutive rows of x per window, in whole (b,s) positions. Swept from one
+// block to an eighth of the grid on twelve shapes: the time depends on the
+// run length in a way that follows the HBM address interleave rather than
+// the shape (runs of 16-64 KiB were 10-25% slower than the best), and runs
+// of 384 KiB were within 4% of the best run length on all but the fp32
+// shapes whose slice is a third of the row (there an eighth of the grid per
+// XCD was 4% faster), and 7% faster than an eighth per XCD for the bf16
+// long-context shard (16,8192,32,128) with lanes [32,96).
+constexpr uint64_t kXcdRunBytes = 384u << 10;
+
 VecConfig choose_vec_config(const Plan& p, const VecArgs& a)
 {
-    (void)p;
     VecConfig c = shape_for(a, 1, 64);
     c.nt = true;
-    c.xcd_remap = true;
+    const uint64_t heads_per_tile = (uint64_t)c.HL * c.U;
+    const uint64_t blocks_per_position = c.GL == 1 ? (a.N + heads_per_tile - 1) / heads_per_tile : 1;
+    const uint64_t block_bytes = heads_per_tile * c.GL * (uint64_t)p.D * (uint64_t)p.esize;
+    const uint64_t position_bytes = block_bytes * blocks_per_position;
+    const uint64_t positions = std::max<uint64_t>(1, (kXcdRunBytes + position_bytes / 2) / position_bytes);
+    c.xcd_group = (uint32_t)std::min<uint64_t>(positions * blocks_per_position, 1u << 24);
     return c;
+}
+
+uint32_t vec_grid(const VecArgs& a, const VecConfig& cfg)
+{
+    // One block per tile group by default: measured faster on MI355X than a
+    // persistent grid for these streaming shapes (the dispatcher keeps every
+    // CU full and no loop-carried dependence serialises the loads).
+    uint64_t grid = cfg.grid ? cfg.grid : a.btiles;
+    return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(grid, a.btiles));
 }
 
 // Complete `a` for a launch shape: head chunks and tile counts. False if a
@@ -618,7 +651,15 @@ bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
     a->span_div = make_fastdiv(a->span);
     a->hl_div = make_fastdiv(a->HL);
     a->nchunk_div = make_fastdiv(a->nchunk);
-    a->xcd_remap = cfg.xcd_remap ? 1u : 0u;
+    const uint64_t G = vec_grid(*a, cfg);
+    const uint64_t P = std::max<uint32_t>(1, cfg.xcd_group);
+    a->xcd_group = (uint32_t)P;
+    a->xcd_full = 0;
+    a->xcd_div = make_fastdiv(8);
+    if (P > 1 && 8 * P <= G) {
+        a->xcd_full = (uint32_t)(G / (8 * P) * (8 * P));
+        a->xcd_div = make_fastdiv((uint32_t)(8 * P));
+    }
     return true;
 }
 
@@ -671,15 +712,6 @@ const void* vec_kernel(const Plan& p, const VecConfig& cfg, bool multi)
         return f32_tables ? vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt, multi)
                           : vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_BF16>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
     }
-}
-
-uint32_t vec_grid(const VecArgs& a, const VecConfig& cfg)
-{
-    // One block per tile group by default: measured faster on MI355X than a
-    // persistent grid for these streaming shapes (the dispatcher keeps every
-    // CU full and no loop-carried dependence serialises the loads).
-    uint64_t grid = cfg.grid ? cfg.grid : a.btiles;
-    return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(grid, a.btiles));
 }
 
 // Launch the vector kernel; `a` is complete (vec_geometry + finish_vec_args).
