@@ -131,6 +131,35 @@ ROPE_API rope_status_t rope_partial_check(
     const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
     rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2]);
 
+/* Kernels of the launch plan (rope_partial_launch_info). */
+#define ROPE_KERNEL_NONE 0   /* no-op call: nothing is launched */
+#define ROPE_KERNEL_VECTOR 1 /* 16-byte vector kernel */
+#define ROPE_KERNEL_SCALAR 2 /* one thread per pair, any alignment */
+#define ROPE_LAUNCH_INFO_LEN 8
+
+/*
+ * rope_partial_launch_info -- the launch plan a call with these arguments
+ * would use (either direction: they plan alike), for tests and profiling.
+ * Runs the checks of rope_partial_check first and returns their status; on
+ * ROPE_OK, info (caller-owned, ROPE_LAUNCH_INFO_LEN elements) receives:
+ *   [0] ROPE_KERNEL_NONE, _VECTOR or _SCALAR;
+ *   [1] blocks of the launch (vector kernel; 0 for the scalar kernel, whose
+ *       grid follows the device's compute-unit count at launch);
+ *   [2] threads per block;
+ *   [3] heads per thread, [4] head lanes per tile, [5] tiles per block;
+ *   [6] XCD run length: consecutive blocks kept on one XCD;
+ *   [7] 16-byte vectors each row's threads cover.
+ * Entries that do not apply are 0. Launches nothing and touches no memory;
+ * pointers are only compared with NULL and checked for alignment.
+ * NULL info is ROPE_ERR_NULLPTR.
+ */
+ROPE_API rope_status_t rope_partial_launch_info(
+    const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    int64_t info[ROPE_LAUNCH_INFO_LEN]);
+
 /* largest tensor count of the _multi entry points */
 #define ROPE_MULTI_MAX 4
 

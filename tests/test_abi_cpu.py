@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string",
-                 "rope_last_error", "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi"):
+                 "rope_last_error", "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi",
+                 "rope_partial_check", "rope_partial_launch_info"):
         assert want in names
 
 

@@ -1,0 +1,128 @@
+"""The launch plan on a machine without a GPU (rope_partial_launch_info):
+which kernel a call takes and with what shape. Nothing is launched; the
+pointers are fake, 128-byte aligned addresses that are never dereferenced."""
+import pytest
+
+import transformer_positional_encoding_amd as rp
+
+OK, NULLPTR, INVALID = rp.ROPE_OK, rp.ROPE_ERR_NULLPTR, rp.ROPE_ERR_INVALID
+F32, F16, BF16 = 0, 1, 2
+IL, RH = 1, 0
+FAKE = 0x10000
+ESIZE = {F32: 4, F16: 2, BF16: 2}
+MAX_GRID_ITEMS = 2 ** 32 - 1
+
+
+def table_geometry(B, S, L, per_batch):
+    shape = (B if per_batch else 1, S, 1, L)
+    strides = (S * L, L, L, 1)
+    return shape, strides
+
+
+def plan(x_shape, dtype, sl, mode=IL, per_batch=False, table_dtype=None, x=FAKE, r=FAKE):
+    B, S, N, D = x_shape
+    L = sl[1] - sl[0]
+    tshape, tstrides = table_geometry(B, S, L, per_batch)
+    return rp.raw_launch_info(x, x_shape, dtype, r, tshape, tstrides, r, tshape, tstrides,
+                              dtype if table_dtype is None else table_dtype, mode, sl)
+
+
+def test_null_info_and_invalid_arguments():
+    st, _ = rp.raw_launch_info(FAKE, (2, 4, 3, 64), BF16, FAKE, (1, 4, 1, 32), (128, 32, 32, 1),
+                               FAKE, (1, 4, 1, 32), (128, 32, 32, 1), BF16, IL, (0, 32), info_out=False)
+    assert st == NULLPTR
+    st, info = plan((2, 4, 3, 64), BF16, (1, 33))          # odd start for interleave pairs is fine...
+    assert st == OK
+    st, info = plan((2, 4, 3, 64), BF16, (0, 31))          # ...an odd slice length is not
+    assert st == INVALID and info is None
+
+
+def test_noop_calls_launch_nothing():
+    st, info = plan((0, 4, 3, 64), BF16, (0, 32))
+    assert st == OK and info["kernel"] == "none" and info["blocks"] == 0
+    st, info = plan((2, 4, 3, 64), BF16, (16, 16))
+    assert st == OK and info["kernel"] == "none"
+
+
+def test_long_context_shard_plan():
+    """(16,8192,32,128) bf16, lanes [32,96), per-batch tables: the slice is
+    half of each of two 128-byte lines, so each row's threads cover both
+    lines (16 vectors); 4 heads per 64-thread block; runs of 384 KiB of x
+    (48 positions of 8 blocks) per XCD."""
+    st, info = plan((16, 8192, 32, 128), BF16, (32, 96), per_batch=True)
+    assert st == OK
+    assert info["kernel"] == "vector"
+    assert info["row_vectors"] == 16 and info["threads"] == 64 and info["head_lanes"] == 4
+    assert info["heads_per_thread"] == 1 and info["tiles_per_block"] == 1
+    assert info["blocks"] == 16 * 8192 * 8
+    assert info["xcd_run"] == 48 * 8
+
+
+@pytest.mark.parametrize("x_shape,dtype,sl,mode,span", [
+    ((4, 4096, 128, 192), BF16, (0, 64), IL, 8),       # whole line [0,128) bytes
+    ((16, 8192, 32, 128), F32, (32, 96), IL, 16),      # bytes [128,384): two whole lines
+    ((32, 256, 16, 128), BF16, (0, 128), RH, 8),       # rotate_half: one vector per half-pair unit
+    ((8, 256, 12, 64), F16, (0, 64), IL, 8),
+])
+def test_vector_plans(x_shape, dtype, sl, mode, span):
+    st, info = plan(x_shape, dtype, sl, mode)
+    assert st == OK and info["kernel"] == "vector"
+    assert info["row_vectors"] == span
+    assert info["threads"] == span * info["head_lanes"] * info["tiles_per_block"] <= 64
+    B, S, N, D = x_shape
+    heads = info["head_lanes"] * info["heads_per_thread"]
+    tiles = B * S * -(-N // heads)
+    assert info["blocks"] == -(-tiles // info["tiles_per_block"])
+    # XCD runs hold whole positions, so a table row is read by one XCD
+    blocks_per_position = -(-N // heads) if info["tiles_per_block"] == 1 else 1
+    assert info["xcd_run"] % blocks_per_position == 0
+
+
+@pytest.mark.parametrize("case", ["misaligned_x", "misaligned_tables", "odd_start", "unaligned_length",
+                                  "fp32_x_bf16_tables", "f16_x_bf16_tables"])
+def test_scalar_plans(case):
+    """Inputs the 16-byte vector kernel cannot take fall to the scalar kernel."""
+    kw = {}
+    x_shape, dtype, sl = (2, 4, 3, 64), BF16, (0, 32)
+    if case == "misaligned_x":
+        kw["x"] = FAKE + 2
+    elif case == "misaligned_tables":
+        kw["r"] = FAKE + 4
+    elif case == "odd_start":
+        sl = (1, 33)
+    elif case == "unaligned_length":
+        sl = (0, 12)                                    # 24 bytes: not a whole number of vectors
+    elif case == "fp32_x_bf16_tables":
+        dtype, kw["table_dtype"] = F32, BF16
+    else:
+        dtype, kw["table_dtype"] = F16, BF16
+    st, info = plan(x_shape, dtype, sl, **kw)
+    assert st == OK and info["kernel"] == "scalar" and info["threads"] == 256
+
+
+def test_mixed_precision_vector_plan():
+    """16-bit x with fp32 tables stays on the vector kernel."""
+    st, info = plan((16, 8192, 32, 128), BF16, (32, 96), per_batch=True, table_dtype=F32)
+    assert st == OK and info["kernel"] == "vector"
+
+
+def test_grid_fits_the_dispatch_packet():
+    """A ragged head count (5 heads in chunks of 4) pads the work-items past
+    2^32 for a 6 GB tensor: the grid is cut so blocks x threads fits the
+    32-bit grid size, and the blocks stride over the remaining tile groups."""
+    x_shape = (1, 40_000_000, 5, 128)
+    st, info = plan(x_shape, BF16, (32, 96))
+    assert st == OK and info["kernel"] == "vector"
+    assert info["head_lanes"] == 4 and info["threads"] == 64
+    tiles = 40_000_000 * 2
+    assert tiles * info["threads"] > MAX_GRID_ITEMS          # one block per tile group would not fit
+    assert info["blocks"] * info["threads"] <= MAX_GRID_ITEMS
+    assert info["blocks"] == MAX_GRID_ITEMS // info["threads"]
+
+
+def test_plan_matches_direction_free_checks():
+    """launch_info returns the status rope_partial_check returns."""
+    for sl in [(0, 32), (0, 31), (-2, 30), (0, 66)]:
+        args = (FAKE, (2, 4, 3, 64), BF16, FAKE, (1, 4, 1, sl[1] - sl[0]), (128, 32, 32, 1),
+                FAKE, (1, 4, 1, sl[1] - sl[0]), (128, 32, 32, 1), BF16, IL, sl)
+        assert rp.raw_launch_info(*args)[0] == rp.raw_check(*args)

@@ -332,3 +332,55 @@ def test_d_over_limit_is_rejected():
     with pytest.raises(rp.RopeError) as e:
         rp.rope_partial_fwd_inplace(x, r, r, "interleave", (0, 2))
     assert e.value.status == rp.ROPE_ERR_INVALID
+
+
+# ---------------------------------------------------------------- a grid at the dispatch limit
+
+def _lane_checksums(xv, lo, hi, rows_per_chunk=1 << 24):
+    """(sum, sum of squares) of the 16-bit patterns of lanes [lo, hi) of
+    every row, computed on the device chunk by chunk."""
+    s = s2 = 0
+    for r0 in range(0, xv.shape[0], rows_per_chunk):
+        part = xv[r0:r0 + rows_per_chunk, lo:hi].contiguous().view(torch.int16).to(torch.int64)
+        s += int(part.sum())
+        s2 += int((part * part).sum())
+        del part
+    return s, s2
+
+
+def test_grid_capped_at_the_dispatch_limit():
+    """(1, 40e6, 5, 128) bf16, lanes [32,96): 5 heads in chunks of 4 make
+    80e6 tile groups of 64 threads, past the 32-bit grid size of a dispatch.
+    The grid is cut to fit and its blocks stride over the remaining groups;
+    sampled rows against the oracle (the first and last among them), the
+    lanes outside the slice checked on the device for every row."""
+    shape, sl, mode = (1, 40_000_000, 5, 128), (32, 96), "interleave"
+    B, S, N, D = shape
+    total = B * S * N
+    announce(f"grid cap shape={shape} bf16 {mode} bwd slice={sl}")
+    x = W.make_x_device(shape, "bf16", seed=77, std=1e-2)
+    r1 = _rand((1, 1, 1, 64), "bf16", 78)
+    r2 = _rand((1, 1, 1, 64), "bf16", 79)
+    r1d, r2d = r1.to(DEV), r2.to(DEV)
+    plan = rp.rope_partial_launch_info(x, r1d, r2d, mode, sl)
+    assert plan["kernel"] == "vector"
+    assert plan["blocks"] * plan["threads"] <= 2 ** 32 - 1
+    assert plan["blocks"] < B * S * 2          # the blocks stride over the tile groups
+    xv = x.view(total, D)
+    rows = W.sample_rows(total, 4000, seed=77)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    x_rows = W.to_numpy_storage(xv.index_select(0, rows_t).cpu())
+    head0, tail0 = _lane_checksums(xv, 0, sl[0]), _lane_checksums(xv, sl[1], D)
+    rp.rope_partial_bwd_inplace(x, r1d, r2d, mode, sl)
+    torch.cuda.synchronize()
+    got = W.to_numpy_storage(xv.index_select(0, rows_t).cpu())
+    want = oracle_rows(x_rows, shape, "bf16", r1, r2, mode, sl, "bwd", rows)
+    L = sl[1] - sl[0]
+    c = np.broadcast_to(r1.double().numpy().reshape(1, L), (len(rows), L))
+    s = np.broadcast_to(r2.double().numpy().reshape(1, L), (len(rows), L))
+    info = compare(got, want, x_rows, c, s, "bf16", mode, "bwd", sl, "grid cap")
+    assert info["exact"] == info["n"]
+    assert _lane_checksums(xv, 0, sl[0]) == head0
+    assert _lane_checksums(xv, sl[1], D) == tail0
+    del x, xv
+    torch.cuda.empty_cache()

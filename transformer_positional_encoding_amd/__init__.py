@@ -20,6 +20,7 @@ import os
 __all__ = [
     "rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string", "inplace_partial_rotary_mul",
     "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi", "MULTI_MAX", "rope_partial_check",
+    "rope_partial_launch_info",
     "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
     "ROPE_ERR_UNSUPPORTED", "ROPE_ERR_RUNTIME", "MODES", "DTYPE_CODES",
 ]
@@ -73,6 +74,8 @@ def library() -> ctypes.CDLL:
             f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p] + _ENTRY_ARGTYPES[2:]
         L.rope_partial_check.restype = ctypes.c_int
         L.rope_partial_check.argtypes = _ENTRY_ARGTYPES[:-1]
+        L.rope_partial_launch_info.restype = ctypes.c_int
+        L.rope_partial_launch_info.argtypes = _ENTRY_ARGTYPES[:-1] + [ctypes.POINTER(ctypes.c_int64)]
         L.rope_status_string.restype = ctypes.c_char_p
         L.rope_status_string.argtypes = [ctypes.c_int]
         L.rope_last_error.restype = ctypes.c_char_p
@@ -108,6 +111,27 @@ def raw_check(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2_ptr, 
     return library().rope_partial_check(x_ptr, _arr4(x_shape), int(dtype), r1_ptr, _arr4(r1_shape),
                                         _arr4(r1_strides), r2_ptr, _arr4(r2_shape), _arr4(r2_strides),
                                         int(table_dtype), int(mode), sl)
+
+
+LAUNCH_INFO_LEN = 8
+KERNELS = {0: "none", 1: "vector", 2: "scalar"}
+
+
+def raw_launch_info(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2_ptr, r2_shape, r2_strides,
+                    table_dtype: int, mode: int, partial_slice, info_out: bool = True):
+    """rope_partial_launch_info with plain integers and sequences (None =
+    NULL): (status, plan dict or None). The plan names the kernel and the
+    launch shape; nothing is launched. info_out=False passes a NULL info."""
+    sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
+    info = (ctypes.c_int64 * LAUNCH_INFO_LEN)() if info_out else None
+    st = library().rope_partial_launch_info(x_ptr, _arr4(x_shape), int(dtype), r1_ptr, _arr4(r1_shape),
+                                            _arr4(r1_strides), r2_ptr, _arr4(r2_shape), _arr4(r2_strides),
+                                            int(table_dtype), int(mode), sl, info)
+    if st != ROPE_OK or info is None:
+        return st, None
+    v = list(info)
+    return st, {"kernel": KERNELS.get(v[0], v[0]), "blocks": v[1], "threads": v[2], "heads_per_thread": v[3],
+                "head_lanes": v[4], "tiles_per_block": v[5], "xcd_run": v[6], "row_vectors": v[7]}
 
 
 def raw_multi_call(direction: str, x_ptrs, x_shapes, dtype: int, r1_ptr, r1_shape, r1_strides,
@@ -232,6 +256,22 @@ def rope_partial_check(x, r1, r2, rotary_mode="interleave", partial_slice=None) 
                    _dtype_code(r1) if r1.dtype == r2.dtype else -1, rotary_mode, partial_slice)
     if st != ROPE_OK:
         raise RopeError(st, last_error())
+
+
+def rope_partial_launch_info(x, r1, r2, rotary_mode="interleave", partial_slice=None) -> dict:
+    """The kernel and launch shape a call with these tensors would use
+    (nothing is launched or read); raises RopeError like the entry points."""
+    if isinstance(rotary_mode, str):
+        if rotary_mode not in MODES:
+            raise ValueError(f"rotary_mode must be one of {sorted(MODES)}")
+        rotary_mode = MODES[rotary_mode]
+    st, plan = raw_launch_info(x.data_ptr() or None, tuple(x.shape), _dtype_code(x), r1.data_ptr() or None,
+                               tuple(r1.shape), tuple(r1.stride()), r2.data_ptr() or None, tuple(r2.shape),
+                               tuple(r2.stride()), _dtype_code(r1) if r1.dtype == r2.dtype else -1,
+                               rotary_mode, partial_slice)
+    if st != ROPE_OK:
+        raise RopeError(st, last_error())
+    return plan
 
 
 def rope_partial_fwd_inplace(x, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:

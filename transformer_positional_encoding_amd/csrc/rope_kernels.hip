@@ -622,12 +622,19 @@ VecConfig choose_vec_config(const Plan& p, const VecArgs& a)
     return c;
 }
 
+// The dispatch packet holds the grid size in work-items as a 32-bit number.
+constexpr uint64_t kMaxGridItems = 0xFFFFFFFFull;
+
 uint32_t vec_grid(const VecArgs& a, const VecConfig& cfg)
 {
     // One block per tile group by default: measured faster on MI355X than a
     // persistent grid for these streaming shapes (the dispatcher keeps every
-    // CU full and no loop-carried dependence serialises the loads).
+    // CU full and no loop-carried dependence serialises the loads). A grid
+    // that would exceed kMaxGridItems work-items is cut to fit, and the
+    // blocks stride over the remaining tile groups.
+    const uint64_t threads = (uint64_t)a.span * a.HL * a.GL;
     uint64_t grid = cfg.grid ? cfg.grid : a.btiles;
+    grid = std::min<uint64_t>(grid, kMaxGridItems / threads);
     return (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(grid, a.btiles));
 }
 
@@ -863,7 +870,7 @@ rope_status_t run_multi(int32_t count, void* const xs[], const int64_t (*x_shape
             blocks += vec_grid(L[i].a, L[i].cfg);
         }
         for (int i = live; i <= kMultiMax; ++i) m.first_block[i] = (uint32_t)blocks;
-        if (blocks >= (1ull << 31)) together = false;
+        if (blocks * threads > kMaxGridItems) together = false;
         if (together) {
             void* args[] = {&m};
             err = hipLaunchKernel(fn, dim3((uint32_t)blocks), dim3(threads), args, 0, s);
@@ -931,6 +938,37 @@ rope_status_t rope_partial_check(const void* x, const int64_t x_shape[4], rope_d
     rope_status_t st = rope::make_plan(const_cast<void*>(x), x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape,
                                        r2_strides, table_dtype, mode, partial_slice, rope::kFwd, &p, &why);
     if (st != ROPE_OK) return rope::set_error(st, why);
+    return ROPE_OK;
+}
+
+rope_status_t rope_partial_launch_info(const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                       const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                                       const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                                       rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                       int64_t info[ROPE_LAUNCH_INFO_LEN])
+{
+    if (info == nullptr) return rope::set_error(ROPE_ERR_NULLPTR, "info is NULL");
+    for (int i = 0; i < ROPE_LAUNCH_INFO_LEN; ++i) info[i] = 0;
+    rope::Launch L;
+    std::string why;
+    rope_status_t st = rope::make_plan(const_cast<void*>(x), x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape,
+                                       r2_strides, table_dtype, mode, partial_slice, rope::kFwd, &L.p, &why);
+    if (st != ROPE_OK) return rope::set_error(st, why);
+    if (L.p.noop) return ROPE_OK;
+    rope::prepare(&L);
+    if (L.vec) {
+        info[0] = ROPE_KERNEL_VECTOR;
+        info[1] = rope::vec_grid(L.a, L.cfg);
+        info[2] = (int64_t)L.a.span * L.a.HL * L.a.GL;
+        info[3] = L.cfg.U;
+        info[4] = L.a.HL;
+        info[5] = L.a.GL;
+        info[6] = L.a.xcd_group;
+        info[7] = L.a.span;
+    } else {
+        info[0] = ROPE_KERNEL_SCALAR;
+        info[2] = 256;
+    }
     return ROPE_OK;
 }
 

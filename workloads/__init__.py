@@ -136,6 +136,26 @@ def make_x(w: Workload, k: int = 0, shape=None, seed=None) -> torch.Tensor:
     return x.to(TORCH_DTYPES[w.dtype])
 
 
+def make_x_device(shape, dtype: str, seed: int, std: float = 1.0, device="cuda",
+                  chunk: int = 1 << 28) -> torch.Tensor:
+    """A large x ~ N(0, std^2) drawn on the device, chunk by chunk, from a
+    seeded device generator (for tensors too large to draw on the host); the
+    values are rounded (RNE) to the storage type like make_x's. Both sides of
+    a comparison read their inputs back from this tensor."""
+    x = torch.empty(tuple(shape), dtype=TORCH_DTYPES[dtype], device=device)
+    flat = x.view(-1)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    for i in range(0, flat.numel(), chunk):
+        n = min(chunk, flat.numel() - i)
+        v = torch.randn(n, generator=g, device=device, dtype=torch.float32)
+        if std != 1.0:
+            v.mul_(std)
+        flat[i:i + n].copy_(v)
+        del v
+    return x
+
+
 def positions(w: Workload) -> np.ndarray:
     """Positions p for every (table-batch, s): shape (Bt, S) int64.
     With position_offsets, batch b uses p = offset_b + s, offset_b ~ U{0..65535}."""
