@@ -12,7 +12,8 @@ Prints one JSON line: whole-job algorithmic GB/s (slice read + slice written +
 cos/sin read once, per launch) and Gelem/s, the roofline of the dominant
 kernel (average launch duration from HIP events on the launch stream), HBM
 traffic from the committed rocprofv3 counter summary when it matches the
-current kernel source, and the CPU oracle timed on a bounded sample.
+current kernel source (and, per kernel, the measured HBM bytes per second
+as a fraction of peak), and the CPU oracle timed on a bounded sample.
 
 `--profile-target` runs only launches of the chosen kernel plus a copy of
 known size (for rocprofv3 counter passes), and prints nothing else.
@@ -187,6 +188,15 @@ def bench_workload(name: str, steps: int, warmup: int, reps: int, stream, want_c
                         "same_buffer_avg_launch_us": round(warm[d] * 1e6, 3)}
                     for d, t in per_launch.items()},
     }
+    # The same launches in measured HBM bytes (rocprofv3 counters of this
+    # kernel source), when they are committed.
+    for d, t in per_launch.items():
+        tr = committed_traffic(name, d)
+        if tr is not None:
+            k = out["kernels"][d]
+            k["hbm_bytes_per_launch"] = tr["hbm_bytes_per_launch"]
+            k["hbm_GBps"] = round(tr["hbm_bytes_per_launch"] / t / 1e9, 1)
+            k["hbm_frac_of_peak"] = round(tr["hbm_bytes_per_launch"] / t / 1e9 / PEAK_GBPS, 4)
     if want_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x_cpu, r1, r2, dirs[0], cpu_s)
     del xs, x_cpu
