@@ -134,7 +134,8 @@ ROPE_API rope_status_t rope_partial_check(
 /* Kernels of the launch plan (rope_partial_launch_info). */
 #define ROPE_KERNEL_NONE 0   /* no-op call: nothing is launched */
 #define ROPE_KERNEL_VECTOR 1 /* 16-byte vector kernel */
-#define ROPE_KERNEL_SCALAR 2 /* one thread per pair, any alignment */
+#define ROPE_KERNEL_SCALAR 2 /* one thread per pair, 64-bit indexing (2^31 rows or more) */
+#define ROPE_KERNEL_ROWS 3   /* one thread per pair, rows of threads, any alignment */
 #define ROPE_LAUNCH_INFO_LEN 8
 
 /*
@@ -142,13 +143,14 @@ ROPE_API rope_status_t rope_partial_check(
  * would use (either direction: they plan alike), for tests and profiling.
  * Runs the checks of rope_partial_check first and returns their status; on
  * ROPE_OK, info (caller-owned, ROPE_LAUNCH_INFO_LEN elements) receives:
- *   [0] ROPE_KERNEL_NONE, _VECTOR or _SCALAR;
- *   [1] blocks of the launch (vector kernel; 0 for the scalar kernel, whose
- *       grid follows the device's compute-unit count at launch);
+ *   [0] ROPE_KERNEL_NONE, _VECTOR, _ROWS or _SCALAR;
+ *   [1] blocks of the launch (0 for the scalar kernel, whose grid follows
+ *       the device's compute-unit count at launch);
  *   [2] threads per block;
- *   [3] heads per thread, [4] head lanes per tile, [5] tiles per block;
- *   [6] XCD run length: consecutive blocks kept on one XCD;
- *   [7] 16-byte vectors each row's threads cover.
+ *   vector kernel: [3] heads per thread, [4] head lanes per tile, [5] tiles
+ *       per block, [6] XCD run length (consecutive blocks kept on one XCD),
+ *       [7] 16-byte vectors each row's threads cover;
+ *   row kernel: [4] rows per block, [7] threads per row.
  * Entries that do not apply are 0. Launches nothing and touches no memory;
  * pointers are only compared with NULL and checked for alignment.
  * NULL info is ROPE_ERR_NULLPTR.

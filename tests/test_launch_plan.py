@@ -81,7 +81,7 @@ def test_vector_plans(x_shape, dtype, sl, mode, span):
 @pytest.mark.parametrize("case", ["misaligned_x", "misaligned_tables", "odd_start", "unaligned_length",
                                   "fp32_x_bf16_tables", "f16_x_bf16_tables"])
 def test_scalar_plans(case):
-    """Inputs the 16-byte vector kernel cannot take fall to the scalar kernel."""
+    """Inputs the 16-byte vector kernel cannot take fall to the row kernel."""
     kw = {}
     x_shape, dtype, sl = (2, 4, 3, 64), BF16, (0, 32)
     if case == "misaligned_x":
@@ -97,7 +97,12 @@ def test_scalar_plans(case):
     else:
         dtype, kw["table_dtype"] = F16, BF16
     st, info = plan(x_shape, dtype, sl, **kw)
-    assert st == OK and info["kernel"] == "scalar" and info["threads"] == 256
+    assert st == OK and info["kernel"] == "rows"
+    pairs = (sl[1] - sl[0]) // 2
+    assert info["threads_per_row"] == min(pairs, 256)
+    assert info["rows_per_block"] == 256 // info["threads_per_row"]
+    assert info["threads"] == info["rows_per_block"] * info["threads_per_row"]
+    assert info["blocks"] == -(-(2 * 4 * 3) // info["rows_per_block"])
 
 
 def test_mixed_precision_vector_plan():
@@ -126,3 +131,26 @@ def test_plan_matches_direction_free_checks():
         args = (FAKE, (2, 4, 3, 64), BF16, FAKE, (1, 4, 1, sl[1] - sl[0]), (128, 32, 32, 1),
                 FAKE, (1, 4, 1, sl[1] - sl[0]), (128, 32, 32, 1), BF16, IL, sl)
         assert rp.raw_launch_info(*args)[0] == rp.raw_check(*args)
+
+
+def test_row_kernel_long_rows_loop():
+    """A slice of more than 512 lanes: 256 threads per row, each taking
+    several pairs."""
+    st, info = plan((2, 3, 5, 1024), BF16, (1, 1023))
+    assert st == OK and info["kernel"] == "rows"
+    assert info["threads_per_row"] == 256 and info["rows_per_block"] == 1 and info["blocks"] == 30
+
+
+def test_row_kernel_grid_fits_the_dispatch_packet():
+    st, info = plan((1, 2 ** 30, 1, 4), BF16, (1, 3))       # 2^30 rows of one pair, odd start
+    assert st == OK and info["kernel"] == "rows"
+    assert info["blocks"] * info["threads"] <= MAX_GRID_ITEMS
+
+
+def test_scalar_kernel_from_two_to_the_31_rows():
+    """The row kernel's divisions hold below 2^31 rows; from there the
+    64-bit scalar kernel runs."""
+    st, info = plan((1, 2 ** 31, 1, 2), BF16, (0, 2))
+    assert st == OK and info["kernel"] == "scalar"
+    st, info = plan((1, 2 ** 31 - 1, 1, 2), BF16, (0, 2))
+    assert st == OK and info["kernel"] == "rows"

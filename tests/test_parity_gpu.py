@@ -310,11 +310,14 @@ def test_c4_bf16_with_fp32_tables_full_size(direction):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode,sl", [("interleave", (0, 1024)), ("rotate_half", (0, 1024)),
-                                     ("interleave", (8, 1016)), ("interleave", (1000, 1024))])
+                                     ("interleave", (8, 1016)), ("interleave", (1000, 1024)),
+                                     ("interleave", (1, 1023)), ("rotate_half", (2, 1022))])
 @pytest.mark.parametrize("direction", ["fwd", "bwd"])
 def test_head_dim_limit(dtype, mode, sl, direction):
     """D = 1024, the constraint's limit: a full-width fp32 interleave slice
-    needs 256 threads per row (the kernel's block limit)."""
+    needs 256 threads per row (the kernel's block limit); the misaligned
+    slices of more than 512 lanes take the row kernel, whose 256 threads per
+    row then loop over the pairs."""
     shape = (2, 3, 5, 1024)
     L = sl[1] - sl[0]
     seed = zlib.crc32(repr((dtype, mode, sl, direction)).encode()) % 10000
@@ -382,5 +385,33 @@ def test_grid_capped_at_the_dispatch_limit():
     assert info["exact"] == info["n"]
     assert _lane_checksums(xv, 0, sl[0]) == head0
     assert _lane_checksums(xv, sl[1], D) == tail0
+    del x, xv
+    torch.cuda.empty_cache()
+
+
+def test_scalar_kernel_past_two_to_the_31_rows():
+    """(1, 2^31 + 96, 1, 2) bf16, the whole two-lane row as the slice: from
+    2^31 rows the 64-bit scalar kernel runs. Sampled rows (the first and last
+    among them) against the oracle."""
+    shape, sl, mode = (1, 2 ** 31 + 96, 1, 2), (0, 2), "interleave"
+    total = shape[1]
+    announce(f"64-bit scalar kernel shape={shape} bf16 fwd slice={sl}")
+    x = W.make_x_device(shape, "bf16", seed=91)
+    r1 = _rand((1, 1, 1, 2), "bf16", 92)
+    r2 = _rand((1, 1, 1, 2), "bf16", 93)
+    r1d, r2d = r1.to(DEV), r2.to(DEV)
+    assert rp.rope_partial_launch_info(x, r1d, r2d, mode, sl)["kernel"] == "scalar"
+    xv = x.view(total, 2)
+    rows = W.sample_rows(total, 4000, seed=91)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    x_rows = W.to_numpy_storage(xv.index_select(0, rows_t).cpu())
+    rp.rope_partial_fwd_inplace(x, r1d, r2d, mode, sl)
+    torch.cuda.synchronize()
+    got = W.to_numpy_storage(xv.index_select(0, rows_t).cpu())
+    want = oracle_rows(x_rows, shape, "bf16", r1, r2, mode, sl, "fwd", rows)
+    c = np.broadcast_to(r1.double().numpy().reshape(1, 2), (len(rows), 2))
+    s = np.broadcast_to(r2.double().numpy().reshape(1, 2), (len(rows), 2))
+    info = compare(got, want, x_rows, c, s, "bf16", mode, "fwd", sl, "64-bit scalar kernel")
+    assert info["exact"] == info["n"]
     del x, xv
     torch.cuda.empty_cache()

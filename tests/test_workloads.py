@@ -49,3 +49,16 @@ def test_sample_rows():
     r = W.sample_rows(1000, 50, 3)
     assert r[0] == 0 and r[-1] == 999 and len(np.unique(r)) == len(r) <= 50
     assert np.array_equal(W.sample_rows(10, 50, 3), np.arange(10))
+
+
+def test_sample_rows_of_billions_of_rows():
+    """Above 2^24 rows the sample comes from seeded uniform draws (no host
+    permutation): distinct, sorted, the first and last rows included, the
+    same on every call, and spread over the whole range."""
+    total = 2 ** 31 + 96
+    r = W.sample_rows(total, 4000, 91)
+    assert len(r) == 4000 and r[0] == 0 and r[-1] == total - 1
+    assert np.all(np.diff(r) > 0)
+    assert np.array_equal(r, W.sample_rows(total, 4000, 91))
+    counts, _ = np.histogram(r, bins=8, range=(0, total))
+    assert counts.min() > 350                     # about 500 per eighth

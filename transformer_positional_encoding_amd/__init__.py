@@ -114,7 +114,7 @@ def raw_check(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2_ptr, 
 
 
 LAUNCH_INFO_LEN = 8
-KERNELS = {0: "none", 1: "vector", 2: "scalar"}
+KERNELS = {0: "none", 1: "vector", 2: "scalar", 3: "rows"}
 
 
 def raw_launch_info(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2_ptr, r2_shape, r2_strides,
@@ -130,6 +130,9 @@ def raw_launch_info(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2
     if st != ROPE_OK or info is None:
         return st, None
     v = list(info)
+    if v[0] == 3:
+        return st, {"kernel": "rows", "blocks": v[1], "threads": v[2], "rows_per_block": v[4],
+                    "threads_per_row": v[7]}
     return st, {"kernel": KERNELS.get(v[0], v[0]), "blocks": v[1], "threads": v[2], "heads_per_thread": v[3],
                 "head_lanes": v[4], "tiles_per_block": v[5], "xcd_run": v[6], "row_vectors": v[7]}
 

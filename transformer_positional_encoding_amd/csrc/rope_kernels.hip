@@ -474,6 +474,56 @@ __global__ void __launch_bounds__(256) rope_scalar_kernel(ScalarArgs a)
     }
 }
 
+// Row kernel: the general kernel for fewer than 2^31 rows. A block holds
+// rpb rows of tpr threads; thread (lr, q0) of the block takes pairs q0,
+// q0 + tpr, ... of row g*rpb + lr for each row group g it visits. The row,
+// head and position come from launch-constant divisions (multiply-high and
+// shift); element offsets stay 64-bit.
+struct RowArgs {
+    void* x;
+    const void* r1;
+    const void* r2;
+    int64_t D, start;       // row length and slice start, elements
+    int64_t t1b, t1s, t1n;  // cos strides in elements (0 = broadcast)
+    int64_t t2b, t2s, t2n;
+    uint32_t L, pairs;      // slice length and rotation pairs per row
+    uint32_t rows, N;
+    uint32_t rpb, tpr;      // rows per block, threads per row
+    uint32_t groups;        // ceil(rows / rpb)
+    FastDiv tpr_div, n_div, s_div;
+};
+
+template <int DT, int TT, int DIR, int MODE>
+__global__ void __launch_bounds__(256) rope_rows_kernel(RowArgs a)
+{
+    const uint32_t t = threadIdx.x;
+    const uint32_t lr = fast_div(t, a.tpr_div);
+    const uint32_t q0 = t - lr * a.tpr;
+    if (lr >= a.rpb) return;
+    for (uint32_t g = blockIdx.x; g < a.groups; g += gridDim.x) {
+        const uint32_t row = g * a.rpb + lr;
+        if (row >= a.rows) return;  // later groups hold larger rows
+        const uint32_t bs = fast_div(row, a.n_div);
+        const uint32_t n = row - bs * a.N;
+        const uint32_t b = fast_div(bs, a.s_div);
+        const uint32_t s = bs - b * a.s_div.d;
+        const int64_t xo = (int64_t)row * a.D + a.start;
+        const int64_t co = b * a.t1b + s * a.t1s + n * a.t1n;
+        const int64_t so = b * a.t2b + s * a.t2s + n * a.t2n;
+        for (uint32_t q = q0; q < a.pairs; q += a.tpr) {
+            const uint32_t j = MODE == kModeIL ? 2 * q : q;               // negated-partner lane
+            const uint32_t pj = MODE == kModeIL ? 2 * q + 1 : q + a.L / 2;
+            float xa = Store<DT>::load1(a.x, xo + j);
+            float xb = Store<DT>::load1(a.x, xo + pj);
+            const float ca = Store<TT>::load1(a.r1, co + j), cb = Store<TT>::load1(a.r1, co + pj);
+            const float sa = Store<TT>::load1(a.r2, so + j), sb = Store<TT>::load1(a.r2, so + pj);
+            rotate_pair<DIR, DT != ROPE_DTYPE_F32>(xa, xb, ca, sa, cb, sb);
+            Store<DT>::store1(a.x, xo + j, xa);
+            Store<DT>::store1(a.x, xo + pj, xb);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -771,12 +821,81 @@ hipError_t launch_scalar(const Plan& p, int cus, hipStream_t stream)
     return hipLaunchKernel(fn, dim3((uint32_t)grid), dim3(threads), args, 0, stream);
 }
 
+template <int DT, int TT>
+const void* rows_kernel_t(int dir, int mode)
+{
+    if (dir == kFwd)
+        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kFwd, kModeIL>)
+                               : reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kFwd, kModeRH>);
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kBwd, kModeIL>)
+                           : reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kBwd, kModeRH>);
+}
+
+template <int DT>
+const void* rows_kernel_dt(int tt, int dir, int mode)
+{
+    switch (tt) {
+    case ROPE_DTYPE_F32: return rows_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode);
+    case ROPE_DTYPE_F16: return rows_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode);
+    default: return rows_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode);
+    }
+}
+
+// Launch shape of the row kernel: up to 256 threads per row (longer rows
+// loop), as many whole rows per block as fit in 256 threads, one block per
+// row group while the grid fits the dispatch packet.
+struct RowShape {
+    uint32_t tpr = 1, rpb = 1, threads = 1, groups = 0, grid = 0;
+};
+
+bool rows_shape(const Plan& p, RowShape* r)
+{
+    const uint64_t rows = (uint64_t)p.B * p.S * p.N;
+    if (rows >= (1ull << 31)) return false;
+    const uint32_t pairs = (uint32_t)(p.L / 2);
+    r->tpr = std::min<uint32_t>(pairs, 256);
+    r->rpb = 256 / r->tpr;
+    r->threads = r->tpr * r->rpb;
+    r->groups = (uint32_t)((rows + r->rpb - 1) / r->rpb);
+    r->grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(r->groups, kMaxGridItems / r->threads));
+    return true;
+}
+
+hipError_t launch_rows(const Plan& p, const RowShape& r, hipStream_t stream)
+{
+    RowArgs a;
+    a.x = p.x; a.r1 = p.r1; a.r2 = p.r2;
+    a.D = p.D; a.start = p.start;
+    a.t1b = p.t1[0]; a.t1s = p.t1[1]; a.t1n = p.t1[2];
+    a.t2b = p.t2[0]; a.t2s = p.t2[1]; a.t2n = p.t2[2];
+    a.L = (uint32_t)p.L;
+    a.pairs = (uint32_t)(p.L / 2);
+    a.rows = (uint32_t)(p.B * p.S * p.N);
+    a.N = (uint32_t)p.N;
+    a.rpb = r.rpb;
+    a.tpr = r.tpr;
+    a.groups = r.groups;
+    a.tpr_div = make_fastdiv(r.tpr);
+    a.n_div = make_fastdiv((uint32_t)p.N);
+    a.s_div = make_fastdiv((uint32_t)p.S);
+    const void* fn;
+    switch (p.dtype) {
+    case ROPE_DTYPE_F32: fn = rows_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode); break;
+    case ROPE_DTYPE_F16: fn = rows_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode); break;
+    default: fn = rows_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode); break;
+    }
+    void* args[] = {&a};
+    return hipLaunchKernel(fn, dim3(r.grid), dim3(r.threads), args, 0, stream);
+}
+
 // One tensor's launch, decided on the host.
 struct Launch {
     Plan p;
     bool vec = false;
     VecArgs a{};
     VecConfig cfg;
+    bool rows = false;  // row kernel (else the 64-bit scalar kernel) when not vec
+    RowShape rs;
 };
 
 void prepare(Launch* L)
@@ -787,11 +906,13 @@ void prepare(Launch* L)
         L->cfg = choose_vec_config(L->p, L->a);
         L->vec = finish_vec_args(L->p, L->cfg, &L->a);
     }
+    if (!L->vec) L->rows = rows_shape(L->p, &L->rs);
 }
 
 hipError_t launch_one(const Launch& L, int cus, hipStream_t s)
 {
-    return L.vec ? launch_vec(L.p, L.a, L.cfg, s) : launch_scalar(L.p, cus, s);
+    if (L.vec) return launch_vec(L.p, L.a, L.cfg, s);
+    return L.rows ? launch_rows(L.p, L.rs, s) : launch_scalar(L.p, cus, s);
 }
 
 rope_status_t device_cus(int* cus)
@@ -965,6 +1086,12 @@ rope_status_t rope_partial_launch_info(const void* x, const int64_t x_shape[4], 
         info[5] = L.a.GL;
         info[6] = L.a.xcd_group;
         info[7] = L.a.span;
+    } else if (L.rows) {
+        info[0] = ROPE_KERNEL_ROWS;
+        info[1] = L.rs.grid;
+        info[2] = L.rs.threads;
+        info[4] = L.rs.rpb;
+        info[7] = L.rs.tpr;
     } else {
         info[0] = ROPE_KERNEL_SCALAR;
         info[2] = 256;

@@ -218,9 +218,19 @@ def from_numpy_storage(a: np.ndarray, dtype: str) -> torch.Tensor:
 
 
 def sample_rows(total_rows: int, n: int, seed: int) -> np.ndarray:
-    """n sorted distinct flat row indices including the first and last rows."""
+    """n sorted distinct flat row indices including the first and last rows
+    (fewer only if 3n random draws repeat too often), drawn uniformly
+    without replacement. Up to 2^24 rows from a seeded permutation; above,
+    the first distinct values of seeded uniform draws, so that no
+    permutation of billions of rows is built on the host."""
     if total_rows <= n:
         return np.arange(total_rows, dtype=np.int64)
     g = generator(seed + 99)
-    pick = torch.randperm(total_rows, generator=g)[: max(n - 2, 0)].numpy().astype(np.int64)
+    k = max(n - 2, 0)
+    if total_rows <= 1 << 24:
+        pick = torch.randperm(total_rows, generator=g)[:k].numpy().astype(np.int64)
+    else:
+        draws = torch.randint(0, total_rows, (3 * max(k, 1),), generator=g, dtype=torch.int64).numpy()
+        uniq, first = np.unique(draws, return_index=True)
+        pick = uniq[np.argsort(first)][:k]
     return np.unique(np.concatenate([pick, [0, total_rows - 1]]).astype(np.int64))
