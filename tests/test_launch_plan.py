@@ -79,7 +79,7 @@ def test_vector_plans(x_shape, dtype, sl, mode, span):
 
 
 @pytest.mark.parametrize("case", ["misaligned_x", "misaligned_tables", "odd_start", "unaligned_length",
-                                  "fp32_x_bf16_tables", "f16_x_bf16_tables"])
+                                  "f16_x_bf16_tables", "bf16_x_f16_tables", "fp32_x_misaligned_16bit_tables"])
 def test_scalar_plans(case):
     """Inputs the 16-byte vector kernel cannot take fall to the row kernel."""
     kw = {}
@@ -92,10 +92,12 @@ def test_scalar_plans(case):
         sl = (1, 33)
     elif case == "unaligned_length":
         sl = (0, 12)                                    # 24 bytes: not a whole number of vectors
-    elif case == "fp32_x_bf16_tables":
-        dtype, kw["table_dtype"] = F32, BF16
-    else:
+    elif case == "f16_x_bf16_tables":
         dtype, kw["table_dtype"] = F16, BF16
+    elif case == "bf16_x_f16_tables":
+        dtype, kw["table_dtype"] = BF16, F16
+    else:                                               # 8-byte table units need 8-byte alignment
+        dtype, kw["table_dtype"], kw["r"] = F32, BF16, FAKE + 4
     st, info = plan(x_shape, dtype, sl, **kw)
     assert st == OK and info["kernel"] == "rows"
     pairs = (sl[1] - sl[0]) // 2
@@ -105,9 +107,16 @@ def test_scalar_plans(case):
     assert info["blocks"] == -(-(2 * 4 * 3) // info["rows_per_block"])
 
 
-def test_mixed_precision_vector_plan():
-    """16-bit x with fp32 tables stays on the vector kernel."""
-    st, info = plan((16, 8192, 32, 128), BF16, (32, 96), per_batch=True, table_dtype=F32)
+@pytest.mark.parametrize("dtype,table_dtype", [(BF16, F32), (F16, F32), (F32, BF16), (F32, F16)])
+@pytest.mark.parametrize("x_shape,sl,mode,per_batch", [
+    ((16, 8192, 32, 128), (32, 96), IL, True),
+    ((2, 8, 4, 128), (32, 96), IL, True),
+    ((2, 8, 4, 128), (0, 128), RH, False),
+])
+def test_mixed_precision_vector_plans(dtype, table_dtype, x_shape, sl, mode, per_batch):
+    """16-bit x with fp32 tables (two 16-byte table units per x vector) and
+    fp32 x with 16-bit tables (one 8-byte unit) stay on the vector kernel."""
+    st, info = plan(x_shape, dtype, sl, mode=mode, per_batch=per_batch, table_dtype=table_dtype)
     assert st == OK and info["kernel"] == "vector"
 
 

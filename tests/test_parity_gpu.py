@@ -306,6 +306,21 @@ def test_c4_bf16_with_fp32_tables_full_size(direction):
     assert info["exact"] == info["n"]
 
 
+@pytest.mark.parametrize("tdtype", ["bf16", "f16"])
+@pytest.mark.parametrize("direction", ["bwd", "fwd"])
+def test_c4_fp32_with_16bit_tables_full_size(tdtype, direction):
+    """fp32 dx with 16-bit tables at the long-context shape: 8-byte table
+    units in the vector kernel; within the fp32 bound of the oracle."""
+    from dataclasses import replace
+    w = replace(W.WORKLOADS["c4_f32"], table_dtype=tdtype)
+    x = W.make_x(w)
+    r1, r2 = W.make_tables(w)
+    assert r1.dtype == W.TORCH_DTYPES[tdtype]
+    assert rp.rope_partial_launch_info(x, r1, r2, w.mode, w.partial_slice)["kernel"] == "vector"
+    run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c4 fp32 {tdtype} tables {direction}",
+                  sample=3000, seed=43)
+
+
 # ---------------------------------------------------------------- the largest head dimension
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -38,6 +38,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // one 16-byte vector
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));  // half of one
 
 constexpr int kModeRH = ROPE_MODE_ROTATE_HALF;
 constexpr int kModeIL = ROPE_MODE_INTERLEAVE;
@@ -186,14 +187,21 @@ __device__ __forceinline__ void rotate_pair(float& a, float& b, float ca, float 
 }
 
 // The cos or sin values for the K lanes of one x vector, from a table of
-// type TT: one 16-byte vector when the table is as wide as x, two when 16-bit
-// x meets an fp32 table (the page's mixed bf16-x / fp32-table case).
+// type TT. They take K * sizeof(TT) bytes, loaded as kVecs table units of
+// type Vec: 8 bytes (half a vector) when fp32 x meets a 16-bit table, one
+// 16-byte vector when the table is as wide as x, two when 16-bit x meets an
+// fp32 table (the page's mixed bf16-x / fp32-table case).
+template <int Bytes> struct TableUnit { using type = v4u; };
+template <> struct TableUnit<8> { using type = v2u; };
+
 template <int TT, int K>
 struct TableLanes {
-    static constexpr int kVecs = K * (TT == ROPE_DTYPE_F32 ? 4 : 2) / 16;
-    static_assert(kVecs == 1 || kVecs == 2, "table vector shape");
+    static constexpr int kBytes = K * (TT == ROPE_DTYPE_F32 ? 4 : 2);
+    static_assert(kBytes == 8 || kBytes == 16 || kBytes == 32, "table unit shape");
+    using Vec = typename TableUnit<kBytes>::type;
+    static constexpr int kVecs = kBytes == 32 ? 2 : 1;
     float v[K];
-    __device__ void unpack(const v4u* q)
+    __device__ void unpack(const Vec* q)
     {
         if constexpr (TT == ROPE_DTYPE_F32) {
 #pragma unroll
@@ -202,7 +210,7 @@ struct TableLanes {
                 for (int w = 0; w < 4; ++w) v[4 * t + w] = __uint_as_float(q[t][w]);
         } else {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
+            for (int w = 0; w < kBytes / 4; ++w) {
                 f32x2 f = Store<TT>::widen(q[0][w]);
                 v[2 * w] = f.x;
                 v[2 * w + 1] = f.y;
@@ -252,15 +260,15 @@ __device__ __forceinline__ void store_x(v4u* p, v4u v)
 // when x and each table span fewer than 2^32 vectors (64 GiB).
 struct VecArgs {
     v4u* x;                 // x as 16-byte vectors
-    const v4u* r1;          // cos table as 16-byte vectors
-    const v4u* r2;          // sin table
+    const void* r1;         // cos table, addressed in table units (TableLanes)
+    const void* r2;         // sin table
     uint32_t row_vecs;      // vectors per row of x (D*esize/16)
     uint32_t start_vec;     // first slice vector within a row
     uint32_t lo_vec;        // first vector the threads of a row cover
     uint32_t half_vecs;     // rotate_half: x vectors per half of the slice
-    uint32_t thalf;         // rotate_half: table vectors per half of the slice
-    uint32_t t1b, t1s, t1n; // cos strides in table vectors (0 = broadcast)
-    uint32_t t2b, t2s, t2n; // sin strides in table vectors
+    uint32_t thalf;         // rotate_half: table units per half of the slice
+    uint32_t t1b, t1s, t1n; // cos strides in table units (0 = broadcast)
+    uint32_t t2b, t2s, t2n; // sin strides in table units
     uint32_t N;
     uint32_t nvec;          // work units per row (in the slice)
     uint32_t span;          // vectors per row the threads cover (>= nvec)
@@ -300,7 +308,10 @@ template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, boo
 __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_t G)
 {
     constexpr int K = Store<DT>::kLanes;
-    constexpr int TV = TableLanes<TT, K>::kVecs;      // table vectors per x vector
+    using TVec = typename TableLanes<TT, K>::Vec;
+    constexpr int TV = TableLanes<TT, K>::kVecs;      // table units per x vector
+    const TVec* r1 = static_cast<const TVec*>(a.r1);
+    const TVec* r2 = static_cast<const TVec*>(a.r2);
     constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
     const uint32_t t = threadIdx.x;
     const uint32_t q = fast_div(t, a.span_div);
@@ -309,7 +320,7 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
     const uint32_t hl = q - gl * a.HL;
     const uint32_t c = a.lo_vec + vs;                 // vector within the row
     const bool in_slice = c >= a.start_vec && c - a.start_vec < a.nvec;
-    const uint32_t v = in_slice ? c - a.start_vec : 0;  // table vector (unused outside)
+    const uint32_t v = in_slice ? c - a.start_vec : 0;  // x vector in the slice (table index)
     if (gl >= a.GL) return;  // no barriers below, so idle threads may leave
 
     const uint32_t first = xcd_grouped_block(bid, a);
@@ -329,17 +340,17 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
         // head past N (ragged last chunk) re-reads row N-1 and skips its
         // store. The tables come first, then the x vectors.
         v4u xa[U], xb[U];
-        v4u ca[U][TV], sa[U][TV], cb[U][TV], sb[U][TV];
+        TVec ca[U][TV], sa[U][TV], cb[U][TV], sb[U][TV];
         uint32_t off[U];
         bool live[U];
         if constexpr (HEADS_SHARE_TABLES) {
 #pragma unroll
             for (int t = 0; t < TV; ++t) {
-                ca[0][t] = a.r1[c_base + t];
-                sa[0][t] = a.r2[s_base + t];
+                ca[0][t] = r1[c_base + t];
+                sa[0][t] = r2[s_base + t];
                 if constexpr (MODE == kModeRH) {
-                    cb[0][t] = a.r1[c_base + a.thalf + t];
-                    sb[0][t] = a.r2[s_base + a.thalf + t];
+                    cb[0][t] = r1[c_base + a.thalf + t];
+                    sb[0][t] = r2[s_base + a.thalf + t];
                 }
             }
         }
@@ -352,11 +363,11 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
             if constexpr (!HEADS_SHARE_TABLES) {
 #pragma unroll
                 for (int t = 0; t < TV; ++t) {
-                    ca[k][t] = a.r1[c_base + nl * a.t1n + t];
-                    sa[k][t] = a.r2[s_base + nl * a.t2n + t];
+                    ca[k][t] = r1[c_base + nl * a.t1n + t];
+                    sa[k][t] = r2[s_base + nl * a.t2n + t];
                     if constexpr (MODE == kModeRH) {
-                        cb[k][t] = a.r1[c_base + nl * a.t1n + a.thalf + t];
-                        sb[k][t] = a.r2[s_base + nl * a.t2n + a.thalf + t];
+                        cb[k][t] = r1[c_base + nl * a.t1n + a.thalf + t];
+                        sb[k][t] = r2[s_base + nl * a.t2n + a.thalf + t];
                     }
                 }
             }
@@ -554,52 +565,55 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Launch shape of the vector kernel.
 struct VecConfig {
-    int U = 1;          // heads per thread per tile (loads in flight per thread)
+    int U = 1;          // heads per thread per tile (the library instantiates 1)
     uint32_t HL = 1;    // head lanes per tile
     uint32_t GL = 1;    // tiles per block iteration
     uint32_t grid = 0;  // blocks; 0 = one block per tile group
     uint32_t xcd_group = 1;  // P of the XCD renumbering (1: dispatch order)
-    bool nt = false;    // nontemporal loads/stores of x
+    bool nt = true;     // nontemporal loads/stores of x (the library instantiates true)
 };
 
 // Can the 16-byte vector kernel run this plan? Fills the geometry of `a`.
-// Table types: the same as x, or fp32 with 16-bit x; other mixes take the
-// scalar kernel.
+// Table types: the same as x, fp32 with 16-bit x, or 16-bit with fp32 x;
+// fp16 with bf16 (either way round) takes the general kernel.
 bool vec_geometry(const Plan& p, VecArgs* a)
 {
     const int64_t es = p.esize, ts = p.tesize;
-    if (!(p.tdtype == p.dtype || (p.tdtype == ROPE_DTYPE_F32 && p.dtype != ROPE_DTYPE_F32))) return false;
-    const int64_t tv = ts / es;   // table vectors per x vector: 1 or 2
-    if (!aligned16(p.x) || !aligned16(p.r1) || !aligned16(p.r2)) return false;
+    if (p.tdtype != p.dtype && p.tdtype != ROPE_DTYPE_F32 && p.dtype != ROPE_DTYPE_F32) return false;
+    const int64_t tbytes = 16 * ts / es;                   // table bytes per x vector: 8, 16 or 32
+    const int64_t unit = std::min<int64_t>(16, tbytes);    // table unit (TableLanes::Vec)
+    const int64_t tv = tbytes / unit;                      // table units per x vector: 1 or 2
+    const auto aligned = [](const void* q, int64_t n) { return (reinterpret_cast<uintptr_t>(q) % n) == 0; };
+    if (!aligned16(p.x) || !aligned(p.r1, unit) || !aligned(p.r2, unit)) return false;
     if ((p.D * es) % 16 || (p.start * es) % 16) return false;
     const int64_t unit_bytes = p.mode == kModeIL ? p.L * es : (p.L / 2) * es;
     if (unit_bytes % 16) return false;
     for (int k = 0; k < 3; ++k)
-        if ((p.t1[k] * ts) % 16 || (p.t2[k] * ts) % 16) return false;
+        if ((p.t1[k] * ts) % unit || (p.t2[k] * ts) % unit) return false;
     // 32-bit vector offsets: x and each table must span fewer than 2^32
     // vectors; tile indices stay below 2^31 (checked in finish_vec_args).
     const int64_t kMax = (1ll << 32) - 1;
     const int64_t x_vecs = p.B * p.S * p.N * (p.D * es / 16);
     if (x_vecs > kMax || p.N >= (1ll << 31) || p.S >= (1ll << 31) || p.B * p.S >= (1ll << 31)) return false;
     const int64_t dims[3] = {p.B, p.S, p.N};
-    int64_t t1_span = p.L * ts / 16, t2_span = p.L * ts / 16;
+    int64_t t1_span = p.L * ts / unit, t2_span = p.L * ts / unit;
     for (int k = 0; k < 3; ++k) {
-        t1_span += (dims[k] - 1) * (p.t1[k] * ts / 16);
-        t2_span += (dims[k] - 1) * (p.t2[k] * ts / 16);
+        t1_span += (dims[k] - 1) * (p.t1[k] * ts / unit);
+        t2_span += (dims[k] - 1) * (p.t2[k] * ts / unit);
     }
     if (t1_span > kMax || t2_span > kMax) return false;
     a->x = static_cast<v4u*>(p.x);
-    a->r1 = static_cast<const v4u*>(p.r1);
-    a->r2 = static_cast<const v4u*>(p.r2);
+    a->r1 = p.r1;
+    a->r2 = p.r2;
     a->row_vecs = (uint32_t)(p.D * es / 16);
     a->start_vec = (uint32_t)(p.start * es / 16);
     a->lo_vec = a->start_vec;
     a->half_vecs = p.mode == kModeRH ? (uint32_t)((p.L / 2) * es / 16) : 0;
     a->thalf = (uint32_t)(a->half_vecs * tv);
-    a->t1b = (uint32_t)(p.t1[0] * ts / 16); a->t1s = (uint32_t)(p.t1[1] * ts / 16);
-    a->t1n = (uint32_t)(p.t1[2] * ts / 16);
-    a->t2b = (uint32_t)(p.t2[0] * ts / 16); a->t2s = (uint32_t)(p.t2[1] * ts / 16);
-    a->t2n = (uint32_t)(p.t2[2] * ts / 16);
+    a->t1b = (uint32_t)(p.t1[0] * ts / unit); a->t1s = (uint32_t)(p.t1[1] * ts / unit);
+    a->t1n = (uint32_t)(p.t1[2] * ts / unit);
+    a->t2b = (uint32_t)(p.t2[0] * ts / unit); a->t2s = (uint32_t)(p.t2[1] * ts / unit);
+    a->t2n = (uint32_t)(p.t2[2] * ts / unit);
     a->N = (uint32_t)p.N;
     a->s_div = make_fastdiv((uint32_t)p.S);
     a->nvec = (uint32_t)(unit_bytes / 16);
@@ -693,8 +707,9 @@ uint32_t vec_grid(const VecArgs& a, const VecConfig& cfg)
 // gridDim.x to it), in which case the scalar kernel runs instead.
 bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
 {
-    if (cfg.U < 1 || cfg.U > 2 || cfg.HL < 1 || cfg.GL < 1 ||
-        (uint64_t)cfg.HL * cfg.GL * a->span > 256)
+    // The library instantiates the chosen shape only: one head per thread,
+    // nontemporal x.
+    if (cfg.U != 1 || !cfg.nt || cfg.HL < 1 || cfg.GL < 1 || (uint64_t)cfg.HL * cfg.GL * a->span > 256)
         return false;
     a->HL = cfg.HL;
     a->GL = cfg.GL;
@@ -727,47 +742,40 @@ const void* vec_kernel_ptr(bool multi)
                  : reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, U, SHARE, NT>);
 }
 
-template <int DT, int TT, int DIR, int MODE, int U>
-const void* vec_kernel_u(bool share, bool nt, bool multi)
+template <int DT, int TT, int DIR, int MODE>
+const void* vec_kernel_s(bool share, bool multi)
 {
-    if (share)
-        return nt ? vec_kernel_ptr<DT, TT, DIR, MODE, U, true, true>(multi)
-                  : vec_kernel_ptr<DT, TT, DIR, MODE, U, true, false>(multi);
-    return nt ? vec_kernel_ptr<DT, TT, DIR, MODE, U, false, true>(multi)
-              : vec_kernel_ptr<DT, TT, DIR, MODE, U, false, false>(multi);
+    return share ? vec_kernel_ptr<DT, TT, DIR, MODE, 1, true, true>(multi)
+                 : vec_kernel_ptr<DT, TT, DIR, MODE, 1, false, true>(multi);
 }
 
 template <int DT, int TT>
-const void* vec_kernel_t(int dir, int mode, int U, bool share, bool nt, bool multi)
+const void* vec_kernel_t(int dir, int mode, bool share, bool multi)
 {
-    // heads per thread: 1 (the chosen shape) or 2 (kept for launch-shape studies)
-    if (dir == kFwd) {
-        if (mode == kModeIL)
-            return U == 1 ? vec_kernel_u<DT, TT, kFwd, kModeIL, 1>(share, nt, multi)
-                          : vec_kernel_u<DT, TT, kFwd, kModeIL, 2>(share, nt, multi);
-        return U == 1 ? vec_kernel_u<DT, TT, kFwd, kModeRH, 1>(share, nt, multi)
-                      : vec_kernel_u<DT, TT, kFwd, kModeRH, 2>(share, nt, multi);
-    }
-    if (mode == kModeIL)
-        return U == 1 ? vec_kernel_u<DT, TT, kBwd, kModeIL, 1>(share, nt, multi)
-                      : vec_kernel_u<DT, TT, kBwd, kModeIL, 2>(share, nt, multi);
-    return U == 1 ? vec_kernel_u<DT, TT, kBwd, kModeRH, 1>(share, nt, multi)
-                  : vec_kernel_u<DT, TT, kBwd, kModeRH, 2>(share, nt, multi);
+    if (dir == kFwd)
+        return mode == kModeIL ? vec_kernel_s<DT, TT, kFwd, kModeIL>(share, multi)
+                               : vec_kernel_s<DT, TT, kFwd, kModeRH>(share, multi);
+    return mode == kModeIL ? vec_kernel_s<DT, TT, kBwd, kModeIL>(share, multi)
+                           : vec_kernel_s<DT, TT, kBwd, kModeRH>(share, multi);
 }
 
+// The vector kernel instance for a plan that vec_geometry accepted.
 const void* vec_kernel(const Plan& p, const VecConfig& cfg, bool multi)
 {
+    (void)cfg;
     const bool share = p.t1[2] == 0 && p.t2[2] == 0;
-    const bool f32_tables = p.tdtype == ROPE_DTYPE_F32;
+    const int tt = p.tdtype;
     switch (p.dtype) {
     case ROPE_DTYPE_F32:
-        return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
+        if (tt == ROPE_DTYPE_F16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F16>(p.dir, p.mode, share, multi);
+        if (tt == ROPE_DTYPE_BF16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_BF16>(p.dir, p.mode, share, multi);
+        return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F32>(p.dir, p.mode, share, multi);
     case ROPE_DTYPE_F16:
-        return f32_tables ? vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt, multi)
-                          : vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F16>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
+        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F32>(p.dir, p.mode, share, multi)
+                                    : vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F16>(p.dir, p.mode, share, multi);
     default:
-        return f32_tables ? vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_F32>(p.dir, p.mode, cfg.U, share, cfg.nt, multi)
-                          : vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_BF16>(p.dir, p.mode, cfg.U, share, cfg.nt, multi);
+        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_F32>(p.dir, p.mode, share, multi)
+                                    : vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_BF16>(p.dir, p.mode, share, multi);
     }
 }
 
