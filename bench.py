@@ -100,15 +100,18 @@ def rotating_copies(w) -> int:
     return max(1, min(8, -(-(3 * MALL_BYTES) // slice_line_bytes(w))))
 
 
-def cpu_baseline(w, x_cpu, r1, r2, direction: str, budget_s: float) -> dict:
-    """The CPU oracle, single-threaded as written, on the first rows of the
-    same workload: calibrated on a small slice, then run for ~budget_s."""
+def cpu_baseline(w, x_cpu, r1, r2, directions, budget_s: float) -> dict:
+    """The CPU oracle, single-threaded as written, running the GPU's step
+    (every direction of the workload, in order) on the same data: calibrated
+    on a small slice, then whole-tensor steps repeated to fill ~budget_s, or
+    the first rows of the tensor when one step would take longer."""
     import numpy as np
 
     import oracle
     import workloads as W
 
     B, S, N, D = (int(v) for v in x_cpu.shape)
+    total = B * S * N
     flat = W.to_numpy_storage(x_cpu).reshape(-1, D)
     t1, t2 = W.to_numpy_storage(r1), W.to_numpy_storage(r2)
     per_row = 2 * w.L * W.ESIZE[w.dtype]
@@ -117,19 +120,23 @@ def cpu_baseline(w, x_cpu, r1, r2, direction: str, budget_s: float) -> dict:
         rows = np.arange(nrows, dtype=np.int64)
         buf = np.ascontiguousarray(flat[:nrows])
         t0 = time.perf_counter()
-        oracle.rope_rows(buf, x_cpu.shape, w.dtype, t1, t2, w.mode, w.partial_slice, direction, rows=rows)
+        for d in directions:
+            oracle.rope_rows(buf, x_cpu.shape, w.dtype, t1, t2, w.mode, w.partial_slice, d, rows=rows)
         return time.perf_counter() - t0
 
-    n_cal = min(flat.shape[0], 20000)
-    dt = run(n_cal)
-    rate = n_cal / max(dt, 1e-9)
-    nrows = int(min(flat.shape[0], max(n_cal, rate * budget_s)))
-    dt = run(nrows)
+    n_cal = min(total, 20000)
+    rate = n_cal / max(run(n_cal), 1e-9)               # rows per second, one step
+    if total / rate <= budget_s:
+        nrows, reps = total, max(1, int(budget_s * rate / total))
+    else:
+        nrows, reps = max(n_cal, int(rate * budget_s)), 1
+    dt = sum(run(nrows) for _ in range(reps))
     groups = -(-nrows // N)
     table_bytes = 2 * groups * w.L * W.ESIZE[w.tdtype]
-    gbps = (nrows * per_row + table_bytes) / dt / 1e9
-    return {"value": round(gbps, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {nrows} of {B * S * N} rows of the workload, one {direction} pass, "
+    moved = reps * len(directions) * (nrows * per_row + table_bytes)
+    what = "all" if nrows == total else f"the first {nrows} of {total}"
+    return {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} step(s) of {'+'.join(directions)} over {what} rows of the workload, "
                       f"{dt:.1f} s single-threaded C oracle; bytes counted as on the GPU"}
 
 
@@ -198,7 +205,7 @@ def bench_workload(name: str, steps: int, warmup: int, reps: int, stream, want_c
             k["hbm_GBps"] = round(tr["hbm_bytes_per_launch"] / t / 1e9, 1)
             k["hbm_frac_of_peak"] = round(tr["hbm_bytes_per_launch"] / t / 1e9 / PEAK_GBPS, 4)
     if want_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, x_cpu, r1, r2, dirs[0], cpu_s)
+        out["cpu_baseline"] = cpu_baseline(w, x_cpu, r1, r2, dirs, cpu_s)
     del xs, x_cpu
     torch.cuda.empty_cache()
     return out
@@ -268,7 +275,8 @@ def main() -> int:
     ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32",
                     help="other workloads measured in the same run (reported under 'other_workloads')")
     ap.add_argument("--reps", type=int, default=50, help="launches per per-kernel timing")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU oracle budget: whole steps repeated to fill about this many seconds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-target", action="store_true")
     args = ap.parse_args()
