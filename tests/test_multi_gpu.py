@@ -71,7 +71,7 @@ def test_four_tensors_match_single_calls(dtype, mode, sl):
 
 
 def test_mixed_kernels_fall_back_to_separate_launches():
-    """One tensor 16-byte aligned, one not (scalar kernel): still one call."""
+    """One tensor 16-byte aligned, one not (general kernel): still one call."""
     announce("multi mixed kernels")
     g = torch.Generator().manual_seed(6)
     a = torch.randn((2, 8, 4, 64), generator=g).to(torch.bfloat16)

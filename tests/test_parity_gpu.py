@@ -124,11 +124,11 @@ CASES = [
     ((3, 5, 13, 96), (16, 80), "interleave", (1, 5, 1, 64)),      # ragged head count
     ((1, 4, 37, 128), (8, 104), "interleave", (1, 4, 1, 96)),     # 12 vectors per row (bf16)
     ((1, 3, 300, 64), (0, 64), "interleave", (1, 3, 1, 64)),      # many heads per block
-    ((2, 6, 5, 64), (3, 35), "interleave", (1, 6, 1, 32)),        # odd start: scalar path
+    ((2, 6, 5, 64), (3, 35), "interleave", (1, 6, 1, 32)),        # odd start: general (row) kernel
     ((2, 6, 5, 40), (2, 14), "interleave", (1, 6, 1, 12)),        # L not a vector multiple
     ((2, 8, 4, 128), (0, 128), "rotate_half", (1, 8, 1, 128)),    # vector path
     ((2, 8, 4, 256), (64, 192), "rotate_half", (2, 8, 1, 128)),
-    ((2, 5, 3, 48), (4, 44), "rotate_half", (1, 5, 1, 40)),       # half of 20 lanes: scalar path
+    ((2, 5, 3, 48), (4, 44), "rotate_half", (1, 5, 1, 40)),       # half of 20 lanes: general (row) kernel
     ((2, 8, 4, 64), (0, 64), "interleave", (2, 8, 4, 64)),        # BSND tables (per head)
     ((2, 8, 4, 64), (0, 64), "interleave", (2, 1, 4, 64)),        # B1ND
     ((2, 8, 4, 64), (0, 64), "interleave", (2, 1, 1, 64)),        # B11D
@@ -275,7 +275,7 @@ MIXED_CASES = [
     ((2, 8, 4, 128), (32, 96), "interleave", (2, 8, 1, 64)),     # vector path (whole lines for f32 tables)
     ((2, 8, 4, 128), (0, 128), "rotate_half", (1, 8, 1, 128)),   # vector path, rotate_half
     ((2, 8, 4, 64), (0, 64), "interleave", (2, 8, 4, 64)),       # per-head tables
-    ((2, 6, 5, 64), (3, 35), "interleave", (1, 6, 1, 32)),       # odd start: scalar path
+    ((2, 6, 5, 64), (3, 35), "interleave", (1, 6, 1, 32)),       # odd start: general (row) kernel
 ]
 
 

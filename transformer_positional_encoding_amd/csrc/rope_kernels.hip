@@ -16,10 +16,10 @@
 // the swap and sign in registers, computes in fp32 (one fp32 rounding, exact
 // products for 16-bit data) and stores only the slice's 16-byte vectors, so
 // lanes outside [start,end) are never written. The path is HBM-bound
-// (0.375-0.75 flop per byte), so there is no MFMA and no LDS: a block owns
-// all heads of one (b,s) position, and when the tables broadcast over heads
-// each thread loads its cos/sin vectors once and reuses them for every head
-// it handles.
+// (0.375-0.75 flop per byte), so there is no MFMA and no LDS: a block takes
+// a chunk of heads of one (b,s) position, the blocks of a position run on
+// one XCD, and when the tables broadcast over heads its cos/sin rows are
+// fetched from HBM once and served by that XCD's L2 to every head.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -233,9 +233,9 @@ struct TableLanes {
 // row cover every vector of those lines instead: each line is then requested
 // whole by one wave instruction, which the L2 serves much faster than two
 // half-line requests (it fetches the whole line either way); vectors outside
-// the slice are loaded and dropped, never stored. The cos/sin vectors of a thread are
-// loaded once per tile and, when the tables broadcast over heads, reused for
-// all its heads. All loads of a tile are issued before any arithmetic. The
+// the slice are loaded and dropped, never stored. The cos/sin units of a
+// thread are loaded once per tile and, when the tables broadcast over heads,
+// reused for all its heads. All loads of a tile are issued before any arithmetic. The
 // grid normally has one block per group of GL tiles; a smaller grid makes
 // the blocks stride over the groups.
 // ---------------------------------------------------------------------------
@@ -256,8 +256,9 @@ __device__ __forceinline__ void store_x(v4u* p, v4u v)
     else *p = v;
 }
 
-// Offsets are in 16-byte vectors and 32-bit: the host runs this kernel only
-// when x and each table span fewer than 2^32 vectors (64 GiB).
+// Offsets are 32-bit, in 16-byte vectors for x and in table units for the
+// tables: the host runs this kernel only when x spans fewer than 2^32
+// vectors (64 GiB) and each table fewer than 2^32 units.
 struct VecArgs {
     v4u* x;                 // x as 16-byte vectors
     const void* r1;         // cos table, addressed in table units (TableLanes)
@@ -345,12 +346,12 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
         bool live[U];
         if constexpr (HEADS_SHARE_TABLES) {
 #pragma unroll
-            for (int t = 0; t < TV; ++t) {
-                ca[0][t] = r1[c_base + t];
-                sa[0][t] = r2[s_base + t];
+            for (int u = 0; u < TV; ++u) {
+                ca[0][u] = r1[c_base + u];
+                sa[0][u] = r2[s_base + u];
                 if constexpr (MODE == kModeRH) {
-                    cb[0][t] = r1[c_base + a.thalf + t];
-                    sb[0][t] = r2[s_base + a.thalf + t];
+                    cb[0][u] = r1[c_base + a.thalf + u];
+                    sb[0][u] = r2[s_base + a.thalf + u];
                 }
             }
         }
@@ -362,12 +363,12 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
             off[k] = (row0 + nl) * a.row_vecs + c;
             if constexpr (!HEADS_SHARE_TABLES) {
 #pragma unroll
-                for (int t = 0; t < TV; ++t) {
-                    ca[k][t] = r1[c_base + nl * a.t1n + t];
-                    sa[k][t] = r2[s_base + nl * a.t2n + t];
+                for (int u = 0; u < TV; ++u) {
+                    ca[k][u] = r1[c_base + nl * a.t1n + u];
+                    sa[k][u] = r2[s_base + nl * a.t2n + u];
                     if constexpr (MODE == kModeRH) {
-                        cb[k][t] = r1[c_base + nl * a.t1n + a.thalf + t];
-                        sb[k][t] = r2[s_base + nl * a.t2n + a.thalf + t];
+                        cb[k][u] = r1[c_base + nl * a.t1n + a.thalf + u];
+                        sb[k][u] = r2[s_base + nl * a.t2n + a.thalf + u];
                     }
                 }
             }
@@ -445,7 +446,8 @@ __global__ void __launch_bounds__(256) rope_vec_multi_kernel(MultiVecArgs m)
 }
 
 // ---------------------------------------------------------------------------
-// Scalar kernel: any alignment, any start parity, any slice length. One
+// Scalar kernel: the general kernel from 2^31 rows on (the row kernel below
+// takes fewer). Any alignment, any start parity, any slice length; one
 // thread per rotation pair; 64-bit indexing throughout.
 // ---------------------------------------------------------------------------
 struct ScalarArgs {
@@ -590,8 +592,8 @@ bool vec_geometry(const Plan& p, VecArgs* a)
     if (unit_bytes % 16) return false;
     for (int k = 0; k < 3; ++k)
         if ((p.t1[k] * ts) % unit || (p.t2[k] * ts) % unit) return false;
-    // 32-bit vector offsets: x and each table must span fewer than 2^32
-    // vectors; tile indices stay below 2^31 (checked in finish_vec_args).
+    // 32-bit offsets: x must span fewer than 2^32 vectors and each table
+    // fewer than 2^32 units; tile indices stay below 2^31 (finish_vec_args).
     const int64_t kMax = (1ll << 32) - 1;
     const int64_t x_vecs = p.B * p.S * p.N * (p.D * es / 16);
     if (x_vecs > kMax || p.N >= (1ll << 31) || p.S >= (1ll << 31) || p.B * p.S >= (1ll << 31)) return false;
@@ -704,7 +706,7 @@ uint32_t vec_grid(const VecArgs& a, const VecConfig& cfg)
 
 // Complete `a` for a launch shape: head chunks and tile counts. False if a
 // tile index could come near 32-bit wrap-around (the grid-stride loop adds
-// gridDim.x to it), in which case the scalar kernel runs instead.
+// gridDim.x to it), in which case a general kernel runs instead.
 bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
 {
     // The library instantiates the chosen shape only: one head per thread,
