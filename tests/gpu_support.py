@@ -5,7 +5,8 @@ The bars: 16-bit data within 1 ulp of the oracle (the kernels are designed to
 match it bit for bit, and the tests report any difference); fp32 data within
 1e-6 of the size of the two terms, |x_j c| + |x_p s| (normwise, so that
 cancellation between the terms does not make the bound meaningless), plus
-2^-126; lanes outside the slice bit-identical.
+2^-126; NaN on the same lanes and infinities equal; lanes outside the slice
+bit-identical.
 """
 from __future__ import annotations
 
@@ -75,12 +76,15 @@ def compare(got: np.ndarray, want: np.ndarray, x_in: np.ndarray, c: np.ndarray, 
     gv, wv = widen(g, dtype), widen(w, dtype)
     nan = np.isnan(wv)
     assert np.array_equal(np.isnan(gv), nan), f"{what}: NaN pattern differs"
+    inf = np.isinf(wv)   # an infinite result must match exactly (1 ulp from the largest finite is not inf)
+    assert np.array_equal(gv[inf], wv[inf]), f"{what}: infinite lanes differ"
     info = {"n": int(g.size), "exact": int(np.sum(g.view(np.uint32 if dtype == 'f32' else np.uint16)
                                                  == w.view(np.uint32 if dtype == 'f32' else np.uint16)))}
     if dtype == "f32":
         xv = widen(x_in[..., start:end], dtype)
-        bound = 1e-6 * term_scale(xv, c, s, mode, direction) + 2.0 ** -126
-        err = np.abs(gv - wv)
+        with np.errstate(invalid="ignore", over="ignore"):   # NaN/inf lanes are excluded below
+            bound = 1e-6 * term_scale(xv, c, s, mode, direction) + 2.0 ** -126
+            err = np.abs(gv - wv)
         fin = ~nan & np.isfinite(wv)
         bad = np.nonzero(fin & (err > bound))
         info["max_ulp"] = int(ulp_distance(g[fin], w[fin], dtype).max(initial=0))
