@@ -100,11 +100,27 @@ def rotating_copies(w) -> int:
     return max(1, min(8, -(-(3 * MALL_BYTES) // slice_line_bytes(w))))
 
 
-def cpu_baseline(w, x_cpu, r1, r2, directions, budget_s: float) -> dict:
-    """The CPU oracle, single-threaded as written, running the GPU's step
-    (every direction of the workload, in order) on the same data: calibrated
-    on a small slice, then whole-tensor steps repeated to fill ~budget_s, or
-    the first rows of the tensor when one step would take longer."""
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, x_cpu, r1, r2, directions, budget_s: float, max_threads: int = 16) -> dict:
+    """The CPU oracle as written, running the GPU's step (every direction of
+    the workload, in order) on the same data. Timed single-threaded, then
+    with the rows split into contiguous blocks over the host cores (one
+    thread per block, each calling the oracle on its rows; the oracle
+    releases the interpreter while it runs). Whole-tensor steps are repeated
+    to fill ~budget_s per timing, or the first rows are taken when one step
+    would take longer."""
+    import threading
+
     import numpy as np
 
     import oracle
@@ -116,28 +132,47 @@ def cpu_baseline(w, x_cpu, r1, r2, directions, budget_s: float) -> dict:
     t1, t2 = W.to_numpy_storage(r1), W.to_numpy_storage(r2)
     per_row = 2 * w.L * W.ESIZE[w.dtype]
 
-    def run(nrows):
-        rows = np.arange(nrows, dtype=np.int64)
-        buf = np.ascontiguousarray(flat[:nrows])
-        t0 = time.perf_counter()
+    def step(buf, rows):
         for d in directions:
             oracle.rope_rows(buf, x_cpu.shape, w.dtype, t1, t2, w.mode, w.partial_slice, d, rows=rows)
+
+    def run(nrows, threads):
+        bounds = np.linspace(0, nrows, threads + 1).astype(np.int64)
+        parts = [(np.ascontiguousarray(flat[a:b]), np.arange(a, b, dtype=np.int64))
+                 for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+        workers = [threading.Thread(target=step, args=part) for part in parts]
+        t0 = time.perf_counter()
+        for th in workers:
+            th.start()
+        for th in workers:
+            th.join()
         return time.perf_counter() - t0
 
-    n_cal = min(total, 20000)
-    rate = n_cal / max(run(n_cal), 1e-9)               # rows per second, one step
-    if total / rate <= budget_s:
-        nrows, reps = total, max(1, int(budget_s * rate / total))
-    else:
-        nrows, reps = max(n_cal, int(rate * budget_s)), 1
-    dt = sum(run(nrows) for _ in range(reps))
-    groups = -(-nrows // N)
-    table_bytes = 2 * groups * w.L * W.ESIZE[w.tdtype]
-    moved = reps * len(directions) * (nrows * per_row + table_bytes)
+    def timed(threads):
+        n_cal = min(total, 20000 * threads)
+        rate = n_cal / max(run(n_cal, threads), 1e-9)          # rows per second, one step
+        if total / rate <= budget_s:
+            nrows, reps = total, max(1, int(budget_s * rate / total))
+        else:
+            nrows, reps = max(n_cal, int(rate * budget_s)), 1
+        dt = sum(run(nrows, threads) for _ in range(reps))
+        groups = -(-nrows // N)
+        table_bytes = 2 * groups * w.L * W.ESIZE[w.tdtype]
+        moved = reps * len(directions) * (nrows * per_row + table_bytes)
+        return moved / dt / 1e9, nrows, reps, dt
+
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_threads))
+    one = timed(1)
+    many = timed(cores) if cores > 1 else one
+    gbps, nrows, reps, dt = many
     what = "all" if nrows == total else f"the first {nrows} of {total}"
-    return {"value": round(moved / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} step(s) of {'+'.join(directions)} over {what} rows of the workload, "
-                      f"{dt:.1f} s single-threaded C oracle; bytes counted as on the GPU"}
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} step(s) of {'+'.join(directions)} over {what} rows of the workload, rows split "
+                      f"over {cores} threads, {dt:.1f} s; bytes counted as on the GPU",
+            "single_core_value": round(one[0], 4),
+            "single_core_sample": f"{one[2]} step(s) over {'all' if one[1] == total else one[1]} rows, "
+                                  f"{one[3]:.1f} s on one thread",
+            "cpu_model": host_cpu_model(), "host_cores_available": len(os.sched_getaffinity(0))}
 
 
 def bench_workload(name: str, steps: int, warmup: int, reps: int, stream, want_cpu: bool, cpu_s: float):
