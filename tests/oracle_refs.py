@@ -104,11 +104,12 @@ def backward_by_autograd(g: np.ndarray, c: np.ndarray, s: np.ndarray, start: int
 def round_to(v: np.ndarray, dtype: str) -> np.ndarray:
     """fp64 values -> storage form: fp32 result (RNE), then RNE to the 16-bit
     type for fp16/bf16. Returns float32 for f32, raw uint16 bits otherwise."""
-    f = np.asarray(v, np.float64).astype(np.float32)
-    if dtype == "f32":
-        return f
-    if dtype == "f16":
-        return f.astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):   # overflow to +-inf is the RNE result the pins expect
+        f = np.asarray(v, np.float64).astype(np.float32)
+        if dtype == "f32":
+            return f
+        if dtype == "f16":
+            return f.astype(np.float16).view(np.uint16)
     return torch.from_numpy(f).to(torch.bfloat16).view(torch.uint16).numpy()
 
 
