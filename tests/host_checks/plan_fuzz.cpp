@@ -1,0 +1,128 @@
+// Randomised check of the C ABI's argument validation (rope_plan.cpp), built
+// with g++ under AddressSanitizer and UndefinedBehaviorSanitizer by the CPU
+// test suite. Arguments mix small, boundary and extreme 64-bit values; every
+// accepted call must describe a launch whose offsets fit in 64 bits.
+#include <stdint.h>
+#include <stdio.h>
+
+#include <limits>
+#include <string>
+
+#include "rope_plan.hpp"
+
+namespace {
+
+uint64_t g_state = 0x9E3779B97F4A7C15ull;
+
+uint64_t next()  // splitmix64
+{
+    uint64_t z = (g_state += 0x9E3779B97F4A7C15ull);
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+int64_t pick()
+{
+    static const int64_t edge[] = {0, 1, 2, 3, 7, 8, 63, 64, 1024, 1025, (1ll << 31) - 1, 1ll << 31, 1ll << 32,
+                                   (1ll << 62), std::numeric_limits<int64_t>::max(), -1, -2,
+                                   std::numeric_limits<int64_t>::min()};
+    switch (next() % 4) {
+    case 0: return edge[next() % (sizeof(edge) / sizeof(edge[0]))];
+    case 1: return (int64_t)(next() % 16);
+    case 2: return (int64_t)(next() % 4096);
+    default: return (int64_t)next();
+    }
+}
+
+typedef __int128 i128;
+
+}  // namespace
+
+int main()
+{
+    const long iters = 3000000;
+    long ok = 0, noop = 0, bad = 0;
+    void* const fake = reinterpret_cast<void*>(0x10000);
+    for (long it = 0; it < iters; ++it) {
+        int64_t xs[4], s1[4], st1[4], s2[4], st2[4], sl[2];
+        for (int k = 0; k < 4; ++k) xs[k] = (next() % 3) ? (int64_t)(next() % 9) : pick();
+        if (next() % 2) xs[3] = 2 * (int64_t)(next() % 520);
+        sl[0] = (next() % 3) ? (int64_t)(next() % (xs[3] > 0 ? (uint64_t)xs[3] + 1 : 2)) : pick();
+        // the driver's own arithmetic wraps (unsigned) so that extreme values stay defined
+        sl[1] = (next() % 3) ? (int64_t)((uint64_t)sl[0] + 2 * (next() % 40)) : pick();
+        const int64_t L = (int64_t)((uint64_t)sl[1] - (uint64_t)sl[0]);
+        for (int k = 0; k < 4; ++k) {
+            s1[k] = (next() % 4) ? ((next() % 2) ? 1 : xs[k]) : pick();
+            s2[k] = (next() % 4) ? ((next() % 2) ? 1 : xs[k]) : pick();
+            st1[k] = (next() % 4) ? (int64_t)(next() % 100000) : pick();
+            st2[k] = (next() % 4) ? (int64_t)(next() % 100000) : pick();
+        }
+        if (next() % 2) { s1[3] = L; s2[3] = L; st1[3] = 1; st2[3] = 1; }
+        if (next() % 2) {
+            // a valid call with at most one field disturbed below
+            for (int k = 0; k < 4; ++k) xs[k] = 1 + (int64_t)(next() % 9);
+            xs[3] = 2 * (1 + (int64_t)(next() % 512));
+            sl[0] = (int64_t)(next() % (uint64_t)(xs[3] + 1));
+            sl[1] = sl[0] + 2 * (int64_t)(next() % ((uint64_t)(xs[3] - sl[0]) / 2 + 1));
+            const int64_t l = sl[1] - sl[0];
+            for (int k = 0; k < 3; ++k) {
+                s1[k] = (next() % 2) ? 1 : xs[k];
+                s2[k] = (next() % 2) ? 1 : xs[k];
+            }
+            s1[3] = s2[3] = l;
+            st1[3] = st2[3] = 1;
+            st1[2] = st2[2] = l;
+            st1[1] = st1[2] * s1[2]; st2[1] = st2[2] * s2[2];
+            st1[0] = st1[1] * s1[1]; st2[0] = st2[1] * s2[1];
+            switch (next() % 12) {   // one disturbance, or none
+            case 0: xs[next() % 4] = pick(); break;
+            case 1: st1[next() % 4] = pick(); break;
+            case 2: s2[next() % 4] = pick(); break;
+            case 3: sl[next() % 2] = pick(); break;
+            case 4: for (int k = 0; k < 3; ++k) st1[k] = (int64_t)(next() >> 2); break;   // huge strides
+            default: break;
+            }
+        }
+        const int dtype = (int)(next() % 4) - (next() % 8 == 0);       // mostly valid, sometimes -1 or 3
+        const int tdtype = (int)(next() % 4) - (next() % 8 == 0);
+        const int64_t mode = (next() % 8) ? (int64_t)(next() % 2) : pick();
+        const bool null_x = next() % 16 == 0, null_shape = next() % 64 == 0, null_slice = next() % 32 == 0;
+        rope::Plan p;
+        std::string why;
+        const rope_status_t st = rope::make_plan(null_x ? nullptr : fake, null_shape ? nullptr : xs,
+                                                 (rope_dtype_t)dtype, fake, s1, st1, fake, s2, st2,
+                                                 (rope_dtype_t)tdtype, mode, null_slice ? nullptr : sl,
+                                                 rope::kFwd, &p, &why);
+        if (st != ROPE_OK && st != ROPE_ERR_NULLPTR && st != ROPE_ERR_INVALID) { ++bad; continue; }
+        if (st != ROPE_OK) {
+            if (why.empty()) ++bad;
+            continue;
+        }
+        if (p.noop) {
+            ++noop;
+            // a no-op is exactly an empty tensor or an empty slice
+            if (!(p.L == 0 || p.B == 0 || p.S == 0 || p.N == 0 || p.D == 0)) ++bad;
+            continue;
+        }
+        if (p.L == 0 || p.B == 0 || p.S == 0 || p.N == 0 || p.D == 0) ++bad;   // should have been a no-op
+        ++ok;
+        // an accepted launch: bounds, parity and 64-bit offsets
+        bool good = p.start >= 0 && p.L > 0 && p.L % 2 == 0 && p.start + p.L <= p.D && p.D <= 1024 &&
+                    p.D % 2 == 0 && p.x == fake && p.B > 0 && p.S > 0 && p.N > 0;
+        i128 numel = (i128)p.B * p.S * p.N * p.D;
+        good = good && numel * p.esize <= (i128)std::numeric_limits<int64_t>::max();
+        const int64_t dims[3] = {p.B, p.S, p.N};
+        for (const int64_t* t : {p.t1, p.t2}) {
+            i128 span = p.L - 1;
+            for (int k = 0; k < 3; ++k) {
+                good = good && t[k] >= 0;
+                span += (i128)t[k] * (dims[k] - 1);
+            }
+            good = good && span <= (i128)std::numeric_limits<int64_t>::max();
+        }
+        if (!good) ++bad;
+    }
+    printf("iters %ld accepted %ld noop %ld bad %ld\n", iters, ok, noop, bad);
+    return bad == 0 && ok > 1000 && noop > 1000 ? 0 : 1;
+}

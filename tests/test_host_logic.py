@@ -1,6 +1,6 @@
 """Host-side logic of the HIP path that runs without a GPU: the launch-time
-fast division behind the kernels' index math, and the bench's buffer
-rotation and traffic bookkeeping."""
+fast division behind the kernels' index math, the argument checks under
+sanitizers, and the bench's buffer rotation and traffic bookkeeping."""
 import os
 import subprocess
 import sys
@@ -16,6 +16,21 @@ def test_fast_division_exact(tmp_path):
     subprocess.run(["g++", "-O2", "-std=c++17", "-I", CSRC,
                     os.path.join(ROOT, "tests", "host_checks", "fastdiv_check.cpp"), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "bad 0" in out.stdout
+
+
+def test_argument_checks_under_sanitizers(tmp_path):
+    """The C ABI's argument validation, built with g++ under AddressSanitizer
+    and UndefinedBehaviorSanitizer (host code only), on three million random
+    and extreme argument sets: no sanitizer report, and every accepted call
+    describes a launch whose offsets fit in 64 bits."""
+    exe = tmp_path / "plan_fuzz"
+    subprocess.run(["g++", "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                    "-I", CSRC, "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "host_checks", "plan_fuzz.cpp"), os.path.join(CSRC, "rope_plan.cpp"),
+                    "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     assert out.returncode == 0, out.stdout + out.stderr
     assert "bad 0" in out.stdout
 
