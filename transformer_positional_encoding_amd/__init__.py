@@ -89,7 +89,14 @@ def rope_status_string(status: int) -> str:
 
 
 def _arr4(v):
-    return None if v is None else _I64x4(*[int(t) for t in v])
+    if v is None:
+        return None
+    if len(v) != 4:
+        raise ValueError(f"expected 4 values, got {len(v)}")
+    try:
+        return _I64x4(*v)                       # tuples of ints (torch sizes and strides)
+    except TypeError:
+        return _I64x4(*[int(t) for t in v])     # other integer types
 
 
 def raw_call(direction: str, x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides,
@@ -99,8 +106,12 @@ def raw_call(direction: str, x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_st
     returns the status code without raising."""
     fn = library().rope_partial_fwd_inplace if direction == "fwd" else library().rope_partial_bwd_inplace
     sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
-    return fn(x_ptr, _arr4(x_shape), int(dtype), r1_ptr, _arr4(r1_shape), _arr4(r1_strides),
-              r2_ptr, _arr4(r2_shape), _arr4(r2_strides), int(table_dtype), int(mode), sl, stream)
+    a1, s1 = _arr4(r1_shape), _arr4(r1_strides)
+    # r2 usually has r1's geometry: the same arrays then serve both
+    a2 = a1 if r2_shape == r1_shape else _arr4(r2_shape)
+    s2 = s1 if r2_strides == r1_strides else _arr4(r2_strides)
+    return fn(x_ptr, _arr4(x_shape), int(dtype), r1_ptr, a1, s1, r2_ptr, a2, s2, int(table_dtype), int(mode), sl,
+              stream)
 
 
 def raw_check(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2_ptr, r2_shape, r2_strides,
@@ -158,12 +169,17 @@ def last_error() -> str:
     return library().rope_last_error().decode()
 
 
+_DTYPE_OF_TORCH = {}
+
+
 def _dtype_code(t) -> int:
-    import torch
-    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-    if t.dtype not in codes:
+    if not _DTYPE_OF_TORCH:
+        import torch
+        _DTYPE_OF_TORCH.update({torch.float32: 0, torch.float16: 1, torch.bfloat16: 2})
+    code = _DTYPE_OF_TORCH.get(t.dtype)
+    if code is None:
         raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
-    return codes[t.dtype]
+    return code
 
 
 def _call(direction: str, x, r1, r2, mode, partial_slice, stream) -> None:
@@ -189,7 +205,9 @@ def _call(direction: str, x, r1, r2, mode, partial_slice, stream) -> None:
         handle = torch.cuda.current_stream(dev).cuda_stream if x.is_cuda else None
     else:
         handle = getattr(stream, "cuda_stream", stream)
-    with torch.cuda.device(dev) if x.is_cuda else _nullcontext():
+    # the launch goes to the current device: switch only when x lives elsewhere
+    switch = x.is_cuda and dev.index != torch.cuda.current_device()
+    with torch.cuda.device(dev) if switch else _nullcontext():
         st = raw_call(direction, x.data_ptr() or None, tuple(x.shape), _dtype_code(x),
                       r1.data_ptr() or None, tuple(r1.shape), tuple(r1.stride()),
                       r2.data_ptr() or None, tuple(r2.shape), tuple(r2.stride()),
