@@ -275,6 +275,52 @@ def bench_multi(name: str, reps: int, stream) -> dict:
             "separate_launches_GBps": round(nbytes / t_each / 1e9, 1)}
 
 
+def bench_out_of_place(name: str, reps: int, stream) -> dict:
+    """The out-of-place entry points on a workload (what the autograd ops
+    run: the backward writes the gradient with respect to x into a new
+    buffer and leaves the incoming gradient alone). Launch time of one
+    out-of-place call against the two-step alternative it replaces, a
+    device copy of x followed by the in-place call. Bytes per call: x read
+    whole, the result written whole, the tables read once."""
+    import torch
+
+    import transformer_positional_encoding_amd as rp
+    import workloads as W
+    w = W.WORKLOADS[name]
+    x = W.make_x(w).to("cuda")
+    r1, r2 = (t.to("cuda") for t in W.make_tables(w))
+    B, S, N, D = w.x_shapes[0]
+    es = W.ESIZE[w.dtype]
+    whole = B * S * N * D * es
+    ncopy = max(1, min(4, -(-(3 * MALL_BYTES) // whole)))
+    xs = [x] + [x.clone() for _ in range(ncopy - 1)]
+    ys = [torch.empty_like(x) for _ in range(ncopy)]
+    nbytes = 2 * whole + (w.algorithmic_bytes() - 2 * B * S * N * w.L * es)
+    res = {"workload": name, "note": w.note + ", out of place", "dtype": w.dtype, "rotating_copies": ncopy,
+           "bytes_per_call": nbytes, "kernels": {}}
+    for d in ("bwd", "fwd"):
+        out_fn = rp.rope_partial_bwd_out if d == "bwd" else rp.rope_partial_fwd_out
+        in_fn = launch_fn(d)
+        one = [(out_fn, (ys[i], xs[i], r1, r2, w.mode, w.partial_slice)) for i in range(ncopy)]
+
+        def copy_then_in_place(y, src):
+            y.copy_(src)
+            in_fn(y, r1, r2, w.mode, w.partial_slice)
+
+        two = [(copy_then_in_place, (ys[i], xs[i])) for i in range(ncopy)]
+        time_launches(one, max(4, reps // 4), stream)
+        t_one = time_launches(one, reps, stream)
+        time_launches(two, max(4, reps // 4), stream)
+        t_two = time_launches(two, reps, stream)
+        res["kernels"][d] = {"out_of_place_us": round(t_one * 1e6, 3),
+                             "GBps": round(nbytes / t_one / 1e9, 1),
+                             "frac_of_peak": round(nbytes / t_one / 1e9 / PEAK_GBPS, 4),
+                             "copy_then_in_place_us": round(t_two * 1e6, 3)}
+    del xs, ys, x
+    torch.cuda.empty_cache()
+    return res
+
+
 def profile_target(name: str, reps: int) -> None:
     """Launches for rocprofv3 counter passes: each direction of the workload
     `reps` times (rotating copies as in the timed run), then a plain device
@@ -307,8 +353,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
-    ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32",
-                    help="other workloads measured in the same run (reported under 'other_workloads')")
+    ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out",
+                    help="other workloads measured in the same run (reported under 'other_workloads'); "
+                         "NAME:out measures the out-of-place entry points on NAME")
     ap.add_argument("--reps", type=int, default=50, help="launches per per-kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle budget: whole steps repeated to fill about this many seconds")
@@ -338,6 +385,9 @@ def main() -> int:
     others = []
     for name in [n for n in args.also.split(",") if n and n != args.workload]:
         import workloads as W
+        if name.endswith(":out"):
+            others.append(bench_out_of_place(name[:-4], max(10, args.reps // 2), stream))
+            continue
         if len(W.WORKLOADS[name].x_shapes) > 1:
             others.append(bench_multi(name, max(10, args.reps // 2), stream))
             continue

@@ -118,6 +118,44 @@ ROPE_API rope_status_t rope_partial_bwd_inplace(
     void* stream);
 
 /*
+ * rope_partial_fwd_out / rope_partial_bwd_out -- the same operation out of
+ * place: y (dx) receives x (dy) with the lanes [start,end) rotated, forward
+ * or backward as above, and every other lane copied bit for bit; x is not
+ * modified. The page's autograd backward (section 自动微分说明) needs this
+ * form: the incoming gradient may be shared with other consumers, so it
+ * cannot be rotated in place, and one pass that reads it and writes the
+ * result moves less memory than a copy followed by the in-place call.
+ *
+ *   y            device buffer for the result: B*S*N*D elements of `dtype`,
+ *                contiguous BSND, owned by the caller. y == x is the
+ *                in-place call; any other overlap of y and x is an error.
+ *   x            device buffer of the input, same shape and type.
+ *   Other arguments are those of rope_partial_fwd_inplace.
+ *
+ * Checks, in this order: the scalar arguments (as above); an empty tensor
+ * returns ROPE_OK without reading any pointer; NULL y or x
+ * (ROPE_ERR_NULLPTR); y and x overlapping without being equal
+ * (ROPE_ERR_INVALID); an empty slice (L == 0) then copies x to y without
+ * looking at the tables, which may be NULL; otherwise the table pointers
+ * and geometry are checked as above. When both buffers are 16-byte aligned
+ * (and the vector kernel's size limits hold) one kernel reads x and writes
+ * y; otherwise x is copied to y on `stream` and y is rotated in place.
+ */
+ROPE_API rope_status_t rope_partial_fwd_out(
+    void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+ROPE_API rope_status_t rope_partial_bwd_out(
+    void* dx, const void* dy, const int64_t x_shape[4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+/*
  * rope_partial_check -- run every argument check of the entry points above
  * (either direction: they are the same) and return the status they would
  * return, without launching anything or touching device memory. For callers

@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for want in ("rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string",
                  "rope_last_error", "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi",
-                 "rope_partial_check", "rope_partial_launch_info"):
+                 "rope_partial_check", "rope_partial_launch_info", "rope_partial_fwd_out",
+                 "rope_partial_bwd_out"):
         assert want in names
 
 
@@ -204,3 +205,65 @@ def test_multi_count_rules():
     assert mcall(count=2, ptrs=None) == NULLPTR
     # every tensor a no-op: nothing launched, no pointer read
     assert mcall(ptrs=(None, None), sl=(8, 8), r1=None, r2=None) == OK
+
+
+FAKE_Y = FAKE + 0x100000  # far from FAKE: no overlap with a small x
+
+
+def ocall(direction="fwd", y=FAKE_Y, x=FAKE, x_shape=(2, 4, 3, 64), dtype=BF16, r1=FAKE, r1_shape=(1, 4, 1, 32),
+          r1_strides=(128, 32, 32, 1), r2=FAKE, mode=IL, sl=(0, 32), table_dtype=None):
+    """The out-of-place entry points, only with arguments that fail
+    validation or are no-ops (nothing may be launched here)."""
+    return rp.raw_out_call(direction, y, x, x_shape, dtype, r1, r1_shape, r1_strides, r2, r1_shape, r1_strides,
+                           dtype if table_dtype is None else table_dtype, mode, sl, None)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("kwargs,code,text", [
+    (dict(mode=2), INVALID, "mode"),
+    (dict(x_shape=(2, 4, 3, 63)), INVALID, "even"),
+    (dict(sl=(40, 72)), INVALID, "<= D"),
+    (dict(x_shape=None), NULLPTR, "x_shape"),
+    (dict(y=None), NULLPTR, "y is NULL"),
+    (dict(x=None), NULLPTR, "x is NULL"),
+    (dict(y=None, sl=(8, 8)), NULLPTR, "y is NULL"),      # an empty slice still copies x to y
+    (dict(y=FAKE + 2), INVALID, "overlap"),               # 2 bytes past x: the buffers overlap
+    (dict(x=FAKE_Y + 3070, y=FAKE_Y), INVALID, "overlap"),  # x starts 2 bytes before y's end
+    (dict(r1=None), NULLPTR, "r1"),
+    (dict(r1_shape=(1, 4, 1, 16)), INVALID, "last dimension"),
+    (dict(r1_strides=(128, 32, 32, 2)), INVALID, "stride 1"),
+])
+def test_out_of_place_argument_errors(direction, kwargs, code, text):
+    assert ocall(direction, **kwargs) == code
+    assert text in rp.last_error()
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_out_of_place_noops(direction):
+    # empty tensor: no pointer is read
+    assert ocall(direction, y=None, x=None, r1=None, r2=None, r1_shape=None, r1_strides=None,
+                 x_shape=(0, 4, 3, 64)) == OK
+    # empty slice on one buffer (y == x): nothing to do, tables not looked at
+    assert ocall(direction, y=FAKE, x=FAKE, r1=None, r2=None, r1_shape=None, r1_strides=None, sl=(8, 8)) == OK
+    # adjacent buffers do not overlap: the checks pass (then the launch would run)
+    assert rp.raw_check(FAKE, (2, 4, 3, 64), BF16, FAKE, (1, 4, 1, 32), (128, 32, 32, 1), FAKE, (1, 4, 1, 32),
+                        (128, 32, 32, 1), BF16, IL, (0, 32)) == OK
+
+
+def test_out_of_place_binding_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(2, 4, 3, 64)
+    r = torch.zeros(1, 4, 1, 32)
+    with pytest.raises(ValueError, match="shape and dtype"):
+        rp.rope_partial_fwd_out(torch.zeros(2, 4, 3, 32), x, r, r, "interleave", (0, 32))
+    with pytest.raises(ValueError, match="shape and dtype"):
+        rp.rope_partial_fwd_out(x.half(), x, r, r, "interleave", (0, 32))
+    with pytest.raises(ValueError, match="GPU"):
+        rp.rope_partial_bwd_out(torch.zeros_like(x), x, r, r, "interleave", (0, 32))
+    with pytest.raises(ValueError, match="contiguous"):
+        rp.rope_partial_fwd_out(torch.zeros(2, 4, 64, 3).transpose(2, 3), torch.zeros(2, 4, 64, 3).transpose(2, 3),
+                                r, r, "interleave", (0, 2))
+    # an empty CPU tensor is a no-op that touches nothing
+    e = torch.zeros(0, 4, 3, 64)
+    rp.rope_partial_fwd_out(torch.zeros_like(e), e, r, r, "interleave", (0, 32))
+    assert rp.partial_rotary_mul(e, r, r, "interleave", (0, 32)).shape == e.shape

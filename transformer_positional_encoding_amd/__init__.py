@@ -20,7 +20,7 @@ import os
 __all__ = [
     "rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string", "inplace_partial_rotary_mul",
     "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi", "MULTI_MAX", "rope_partial_check",
-    "rope_partial_launch_info",
+    "rope_partial_launch_info", "rope_partial_fwd_out", "rope_partial_bwd_out", "partial_rotary_mul",
     "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
     "ROPE_ERR_UNSUPPORTED", "ROPE_ERR_RUNTIME", "MODES", "DTYPE_CODES",
 ]
@@ -68,6 +68,10 @@ def library() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = _ENTRY_ARGTYPES
+        for name in ("rope_partial_fwd_out", "rope_partial_bwd_out"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_void_p] + _ENTRY_ARGTYPES
         for name in ("rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi"):
             f = getattr(L, name)
             f.restype = ctypes.c_int
@@ -112,6 +116,20 @@ def raw_call(direction: str, x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_st
     s2 = s1 if r2_strides == r1_strides else _arr4(r2_strides)
     return fn(x_ptr, _arr4(x_shape), int(dtype), r1_ptr, a1, s1, r2_ptr, a2, s2, int(table_dtype), int(mode), sl,
               stream)
+
+
+def raw_out_call(direction: str, y_ptr, x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides,
+                 r2_ptr, r2_shape, r2_strides, table_dtype: int, mode: int, partial_slice,
+                 stream=None) -> int:
+    """Call rope_partial_{fwd,bwd}_out with plain integers and sequences
+    (None = NULL); returns the status code without raising."""
+    fn = library().rope_partial_fwd_out if direction == "fwd" else library().rope_partial_bwd_out
+    sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
+    a1, s1 = _arr4(r1_shape), _arr4(r1_strides)
+    a2 = a1 if r2_shape == r1_shape else _arr4(r2_shape)
+    s2 = s1 if r2_strides == r1_strides else _arr4(r2_strides)
+    return fn(y_ptr, x_ptr, _arr4(x_shape), int(dtype), r1_ptr, a1, s1, r2_ptr, a2, s2, int(table_dtype), int(mode),
+              sl, stream)
 
 
 def raw_check(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2_ptr, r2_shape, r2_strides,
@@ -216,6 +234,42 @@ def _call(direction: str, x, r1, r2, mode, partial_slice, stream) -> None:
         raise RopeError(st, last_error())
 
 
+def _call_out(direction: str, y, x, r1, r2, mode, partial_slice, stream) -> None:
+    import torch
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"rotary_mode must be one of {sorted(MODES)}")
+        mode = MODES[mode]
+    for name, t in (("out", y), ("x", x), ("r1", r1), ("r2", r2)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D (B,S,N,D layout), got {t.dim()}-D")
+    if y.shape != x.shape or y.dtype != x.dtype:
+        raise ValueError(f"out must match x in shape and dtype: {tuple(y.shape)} {y.dtype} vs "
+                         f"{tuple(x.shape)} {x.dtype}")
+    if not (x.is_contiguous() and y.is_contiguous()):
+        raise ValueError("x and out must be contiguous (BSND)")
+    if x.numel() and not (x.is_cuda and y.is_cuda and y.device == x.device):
+        raise ValueError("x and out must be GPU tensors on one device")
+    dev = x.device
+    for name, t in (("r1", r1), ("r2", r2)):
+        if t.numel() and x.numel() and t.device != dev:
+            raise ValueError(f"{name} must be on {dev}")
+    if stream is None:
+        handle = torch.cuda.current_stream(dev).cuda_stream if x.is_cuda else None
+    else:
+        handle = getattr(stream, "cuda_stream", stream)
+    switch = x.is_cuda and dev.index != torch.cuda.current_device()
+    with torch.cuda.device(dev) if switch else _nullcontext():
+        st = raw_out_call(direction, y.data_ptr() or None, x.data_ptr() or None, tuple(x.shape), _dtype_code(x),
+                          r1.data_ptr() or None, tuple(r1.shape), tuple(r1.stride()),
+                          r2.data_ptr() or None, tuple(r2.shape), tuple(r2.stride()),
+                          _dtype_code(r1) if r1.dtype == r2.dtype else -1, mode, partial_slice, handle)
+    if st != ROPE_OK:
+        raise RopeError(st, last_error())
+
+
 def _call_multi(direction: str, xs, r1, r2, mode, partial_slice, stream) -> None:
     import torch
     xs = list(xs)
@@ -315,6 +369,21 @@ def rope_partial_bwd_inplace(dx, r1, r2, rotary_mode="interleave", partial_slice
     _call("bwd", dx, r1, r2, rotary_mode, partial_slice, stream)
 
 
+def rope_partial_fwd_out(out, x, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:
+    """Out-of-place forward: ``out`` receives ``x`` with ``x[..., start:end)``
+    rotated and every other lane copied; ``x`` is left unchanged. ``out``
+    must be a contiguous tensor of x's shape and dtype that does not overlap
+    x (``out is x`` is the in-place call). Arguments as in
+    :func:`rope_partial_fwd_inplace`."""
+    _call_out("fwd", out, x, r1, r2, rotary_mode, partial_slice, stream)
+
+
+def rope_partial_bwd_out(dx, dy, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:
+    """Out-of-place backward: ``dx`` receives the gradient with respect to x
+    for the incoming gradient ``dy``, which is left unchanged."""
+    _call_out("bwd", dx, dy, r1, r2, rotary_mode, partial_slice, stream)
+
+
 def rope_partial_fwd_inplace_multi(xs, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:
     """Forward on up to MULTI_MAX tensors that share r1/r2 (e.g. Q and K), in
     one kernel launch when they take the same kernel; same result as calling
@@ -351,19 +420,52 @@ def _autograd_function():
         @staticmethod
         def backward(ctx, grad):
             r1, r2 = ctx.saved_tensors
-            # The gradient buffer autograd hands over may be shared or
-            # expanded (stride 0), so the in-place backward runs on a private
-            # contiguous copy of it.
-            dx = grad.contiguous()
-            if dx.data_ptr() == grad.data_ptr():
-                dx = dx.clone()
-            rope_partial_bwd_inplace(dx, r1, r2, ctx.rotary_mode, ctx.partial_slice)
-            return dx, None, None, None, None
+            return _grad_x(grad, r1, r2, ctx.rotary_mode, ctx.partial_slice), None, None, None, None
 
     return InplacePartialRotaryMulFn
 
 
+def _grad_x(grad, r1, r2, rotary_mode, partial_slice):
+    """The gradient with respect to x for the incoming gradient ``grad``,
+    in a new tensor. Autograd may hand the same gradient buffer to other
+    consumers, so it is never modified: a contiguous gradient is read by
+    the out-of-place backward (one pass), any other layout (e.g. the stride-0
+    gradient of an expand) is first made into a private contiguous copy,
+    which is then rotated in place."""
+    import torch
+    if grad.is_contiguous():
+        dx = torch.empty_like(grad, memory_format=torch.contiguous_format)
+        rope_partial_bwd_out(dx, grad, r1, r2, rotary_mode, partial_slice)
+        return dx
+    dx = grad.contiguous()
+    rope_partial_bwd_inplace(dx, r1, r2, rotary_mode, partial_slice)
+    return dx
+
+
+def _out_of_place_function():
+    import torch
+
+    class PartialRotaryMulFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, r1, r2, rotary_mode, partial_slice):
+            xc = x.contiguous()
+            y = torch.empty_like(xc, memory_format=torch.contiguous_format)
+            rope_partial_fwd_out(y, xc, r1, r2, rotary_mode, partial_slice)
+            ctx.save_for_backward(r1, r2)
+            ctx.rotary_mode = rotary_mode
+            ctx.partial_slice = None if partial_slice is None else tuple(int(v) for v in partial_slice)
+            return y
+
+        @staticmethod
+        def backward(ctx, grad):
+            r1, r2 = ctx.saved_tensors
+            return _grad_x(grad, r1, r2, ctx.rotary_mode, ctx.partial_slice), None, None, None, None
+
+    return PartialRotaryMulFn
+
+
 _FN = None
+_FN_OUT = None
 
 
 def inplace_partial_rotary_mul(x, r1, r2, rotary_mode="interleave", partial_slice=None) -> None:
@@ -386,3 +488,21 @@ def inplace_partial_rotary_mul(x, r1, r2, rotary_mode="interleave", partial_slic
         return None
     rope_partial_fwd_inplace(x, r1, r2, rotary_mode, partial_slice)
     return None
+
+
+def partial_rotary_mul(x, r1, r2, rotary_mode="interleave", partial_slice=None):
+    """Out-of-place partial RoPE: returns a new contiguous tensor holding x
+    with ``x[..., start:end)`` rotated; x is not modified. Records itself for
+    autograd (the backward is the out-of-place backward entry point) and
+    works on leaf tensors too, so a training step needs no ``x * 1.0`` copy
+    before the in-place op. r1 and r2 never get gradients."""
+    import torch
+    global _FN_OUT
+    if torch.is_grad_enabled() and x.requires_grad:
+        if _FN_OUT is None:
+            _FN_OUT = _out_of_place_function()
+        return _FN_OUT.apply(x, r1, r2, rotary_mode, partial_slice)
+    xc = x.contiguous()
+    y = torch.empty_like(xc, memory_format=torch.contiguous_format)
+    rope_partial_fwd_out(y, xc, r1, r2, rotary_mode, partial_slice)
+    return y

@@ -233,7 +233,10 @@ struct TableLanes {
 // row cover every vector of those lines instead: each line is then requested
 // whole by one wave instruction, which the L2 serves much faster than two
 // half-line requests (it fetches the whole line either way); vectors outside
-// the slice are loaded and dropped, never stored. The cos/sin units of a
+// the slice are loaded and dropped, never stored. Out of place (src is
+// another tensor) the threads cover whole rows: vectors outside the slice
+// are copied from src to x, and for rotate_half the threads of the slice's
+// first half write both halves. The cos/sin units of a
 // thread are loaded once per tile and, when the tables broadcast over heads,
 // reused for all its heads. All loads of a tile are issued before any arithmetic. The
 // grid normally has one block per group of GL tiles; a smaller grid makes
@@ -260,7 +263,8 @@ __device__ __forceinline__ void store_x(v4u* p, v4u v)
 // tables: the host runs this kernel only when x spans fewer than 2^32
 // vectors (64 GiB) and each table fewer than 2^32 units.
 struct VecArgs {
-    v4u* x;                 // x as 16-byte vectors
+    v4u* x;                 // the tensor written, as 16-byte vectors
+    const v4u* src;         // out of place: the tensor read (in place: unused)
     const void* r1;         // cos table, addressed in table units (TableLanes)
     const void* r2;         // sin table
     uint32_t row_vecs;      // vectors per row of x (D*esize/16)
@@ -304,10 +308,12 @@ __device__ __forceinline__ uint32_t xcd_grouped_block(uint32_t bid, const VecArg
 }
 
 // The kernel body for one tensor: `bid` is the block's number among the G
-// blocks that work on this tensor.
-template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
+// blocks that work on this tensor. OUT: read a.src and write a.x (out of
+// place, whole rows); otherwise read and write a.x.
+template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT, bool OUT>
 __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_t G)
 {
+    const v4u* src = OUT ? a.src : a.x;
     constexpr int K = Store<DT>::kLanes;
     using TVec = typename TableLanes<TT, K>::Vec;
     constexpr int TV = TableLanes<TT, K>::kVecs;      // table units per x vector
@@ -322,7 +328,13 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
     const uint32_t c = a.lo_vec + vs;                 // vector within the row
     const bool in_slice = c >= a.start_vec && c - a.start_vec < a.nvec;
     const uint32_t v = in_slice ? c - a.start_vec : 0;  // x vector in the slice (table index)
-    if (gl >= a.GL) return;  // no barriers below, so idle threads may leave
+    // Out of place, rotate_half: vectors of the slice's second half are
+    // written by the threads of the first half, and threads outside the
+    // slice load their own vector in place of a partner.
+    const bool partner_half =
+        OUT && MODE == kModeRH && c >= a.start_vec + a.nvec && c - a.start_vec - a.nvec < a.nvec;
+    const uint32_t hoff = !OUT || in_slice ? a.half_vecs : 0;
+    if (gl >= a.GL || partner_half) return;  // no barriers below, so idle threads may leave
 
     const uint32_t first = xcd_grouped_block(bid, a);
     for (uint32_t bt = first; bt < a.btiles; bt += G) {
@@ -372,8 +384,8 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
                     }
                 }
             }
-            xa[k] = load_x<NT>(a.x + off[k]);
-            if constexpr (MODE == kModeRH) xb[k] = load_x<NT>(a.x + off[k] + a.half_vecs);
+            xa[k] = load_x<NT>(src + off[k]);
+            if constexpr (MODE == kModeRH) xb[k] = load_x<NT>(src + off[k] + hoff);
         }
         // Keep every load above in flight together: without this barrier the
         // machine scheduler starts the arithmetic on the first vectors and
@@ -382,7 +394,11 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
 
 #pragma unroll
         for (int k = 0; k < U; ++k) {
-            if (!live[k] || !in_slice) continue;
+            if (!live[k]) continue;
+            if (!in_slice) {
+                if constexpr (OUT) store_x<NT>(a.x + off[k], xa[k]);  // copied unchanged
+                continue;
+            }
             const int kt = HEADS_SHARE_TABLES ? 0 : k;
             Lanes<DT> X;
             TableLanes<TT, K> C, S;
@@ -413,7 +429,14 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
 template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
 __global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
 {
-    vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(a, blockIdx.x, gridDim.x);
+    vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(a, blockIdx.x, gridDim.x);
+}
+
+// Out of place: x (the output) receives src with the slice rotated.
+template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
+__global__ void __launch_bounds__(256) rope_vec_out_kernel(VecArgs a)
+{
+    vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, true>(a, blockIdx.x, gridDim.x);
 }
 
 // Several tensors that share the tables (the Q and K of one layer) in one
@@ -438,10 +461,10 @@ __global__ void __launch_bounds__(256) rope_vec_multi_kernel(MultiVecArgs m)
         i += (k < (int)m.count && b >= m.first_block[k]) ? 1u : 0u;
     const uint32_t lo = m.first_block[i], G = m.first_block[i + 1] - lo;
     switch (i) {
-    case 0: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[0], b - lo, G); break;
-    case 1: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[1], b - lo, G); break;
-    case 2: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[2], b - lo, G); break;
-    default: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT>(m.a[3], b - lo, G); break;
+    case 0: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(m.a[0], b - lo, G); break;
+    case 1: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(m.a[1], b - lo, G); break;
+    case 2: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(m.a[2], b - lo, G); break;
+    default: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(m.a[3], b - lo, G); break;
     }
 }
 
@@ -605,6 +628,7 @@ bool vec_geometry(const Plan& p, VecArgs* a)
     }
     if (t1_span > kMax || t2_span > kMax) return false;
     a->x = static_cast<v4u*>(p.x);
+    a->src = nullptr;
     a->r1 = p.r1;
     a->r2 = p.r2;
     a->row_vecs = (uint32_t)(p.D * es / 16);
@@ -737,56 +761,64 @@ bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
     return true;
 }
 
+// Which vector kernel: in place on one tensor, in place on several, or out
+// of place.
+enum VecKind { kVecOne = 0, kVecMulti = 1, kVecOut = 2 };
+
 template <int DT, int TT, int DIR, int MODE, int U, bool SHARE, bool NT>
-const void* vec_kernel_ptr(bool multi)
+const void* vec_kernel_ptr(VecKind kind)
 {
-    return multi ? reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, TT, DIR, MODE, U, SHARE, NT>)
-                 : reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, U, SHARE, NT>);
+    switch (kind) {
+    case kVecMulti: return reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, TT, DIR, MODE, U, SHARE, NT>);
+    case kVecOut: return reinterpret_cast<const void*>(&rope_vec_out_kernel<DT, TT, DIR, MODE, U, SHARE, NT>);
+    default: return reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, U, SHARE, NT>);
+    }
 }
 
 template <int DT, int TT, int DIR, int MODE>
-const void* vec_kernel_s(bool share, bool multi)
+const void* vec_kernel_s(bool share, VecKind kind)
 {
-    return share ? vec_kernel_ptr<DT, TT, DIR, MODE, 1, true, true>(multi)
-                 : vec_kernel_ptr<DT, TT, DIR, MODE, 1, false, true>(multi);
+    return share ? vec_kernel_ptr<DT, TT, DIR, MODE, 1, true, true>(kind)
+                 : vec_kernel_ptr<DT, TT, DIR, MODE, 1, false, true>(kind);
 }
 
 template <int DT, int TT>
-const void* vec_kernel_t(int dir, int mode, bool share, bool multi)
+const void* vec_kernel_t(int dir, int mode, bool share, VecKind kind)
 {
     if (dir == kFwd)
-        return mode == kModeIL ? vec_kernel_s<DT, TT, kFwd, kModeIL>(share, multi)
-                               : vec_kernel_s<DT, TT, kFwd, kModeRH>(share, multi);
-    return mode == kModeIL ? vec_kernel_s<DT, TT, kBwd, kModeIL>(share, multi)
-                           : vec_kernel_s<DT, TT, kBwd, kModeRH>(share, multi);
+        return mode == kModeIL ? vec_kernel_s<DT, TT, kFwd, kModeIL>(share, kind)
+                               : vec_kernel_s<DT, TT, kFwd, kModeRH>(share, kind);
+    return mode == kModeIL ? vec_kernel_s<DT, TT, kBwd, kModeIL>(share, kind)
+                           : vec_kernel_s<DT, TT, kBwd, kModeRH>(share, kind);
 }
 
 // The vector kernel instance for a plan that vec_geometry accepted.
-const void* vec_kernel(const Plan& p, const VecConfig& cfg, bool multi)
+const void* vec_kernel(const Plan& p, VecKind kind)
 {
-    (void)cfg;
     const bool share = p.t1[2] == 0 && p.t2[2] == 0;
     const int tt = p.tdtype;
     switch (p.dtype) {
     case ROPE_DTYPE_F32:
-        if (tt == ROPE_DTYPE_F16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F16>(p.dir, p.mode, share, multi);
-        if (tt == ROPE_DTYPE_BF16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_BF16>(p.dir, p.mode, share, multi);
-        return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F32>(p.dir, p.mode, share, multi);
+        if (tt == ROPE_DTYPE_F16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F16>(p.dir, p.mode, share, kind);
+        if (tt == ROPE_DTYPE_BF16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_BF16>(p.dir, p.mode, share, kind);
+        return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F32>(p.dir, p.mode, share, kind);
     case ROPE_DTYPE_F16:
-        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F32>(p.dir, p.mode, share, multi)
-                                    : vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F16>(p.dir, p.mode, share, multi);
+        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F32>(p.dir, p.mode, share, kind)
+                                    : vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F16>(p.dir, p.mode, share, kind);
     default:
-        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_F32>(p.dir, p.mode, share, multi)
-                                    : vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_BF16>(p.dir, p.mode, share, multi);
+        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_F32>(p.dir, p.mode, share, kind)
+                                    : vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_BF16>(p.dir, p.mode, share, kind);
     }
 }
 
 // Launch the vector kernel; `a` is complete (vec_geometry + finish_vec_args).
+// a.src set means out of place.
 hipError_t launch_vec(const Plan& p, const VecArgs& a, const VecConfig& cfg, hipStream_t stream)
 {
     const uint32_t threads = a.span * a.HL * a.GL;
     void* args[] = {const_cast<VecArgs*>(&a)};
-    return hipLaunchKernel(vec_kernel(p, cfg, false), dim3(vec_grid(a, cfg)), dim3(threads), args, 0, stream);
+    return hipLaunchKernel(vec_kernel(p, a.src ? kVecOut : kVecOne), dim3(vec_grid(a, cfg)), dim3(threads), args,
+                           0, stream);
 }
 
 template <int DT, int TT>
@@ -925,6 +957,31 @@ hipError_t launch_one(const Launch& L, int cus, hipStream_t s)
     return L.rows ? launch_rows(L.p, L.rs, s) : launch_scalar(L.p, cus, s);
 }
 
+// Out of place (p.src is the input, p.x the output; distinct buffers). The
+// vector kernel reads src and writes x in one pass over whole rows: the
+// slice rotated, the other vectors copied. Inputs it cannot take (alignment,
+// sizes) get a device copy of src into x and then the in-place plan on x.
+void prepare_out(Launch* L)
+{
+    L->vec = vec_geometry(L->p, &L->a) && aligned16(L->p.src);
+    if (L->vec) {
+        L->a.src = static_cast<const v4u*>(L->p.src);
+        L->a.lo_vec = 0;
+        L->a.span = L->a.row_vecs;
+        L->cfg = choose_vec_config(L->p, L->a);
+        L->vec = finish_vec_args(L->p, L->cfg, &L->a);
+    }
+    if (!L->vec) L->rows = rows_shape(L->p, &L->rs);
+}
+
+hipError_t launch_out(const Launch& L, int cus, hipStream_t s)
+{
+    if (L.vec) return launch_vec(L.p, L.a, L.cfg, s);
+    hipError_t err = hipMemcpyAsync(L.p.x, L.p.src, (size_t)L.p.bytes, hipMemcpyDeviceToDevice, s);
+    if (err != hipSuccess) return err;
+    return L.rows ? launch_rows(L.p, L.rs, s) : launch_scalar(L.p, cus, s);
+}
+
 rope_status_t device_cus(int* cus)
 {
     int dev = 0;
@@ -951,6 +1008,38 @@ rope_status_t run(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
     prepare(&L);
     hipError_t err = launch_one(L, cus, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
+    return ROPE_OK;
+}
+
+// Out of place: y = x with the slice rotated (y == x is the in-place call).
+rope_status_t run_out(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                      const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                      const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                      rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                      void* stream, Direction dir)
+{
+    Launch L;
+    std::string why;
+    rope_status_t st = make_plan_out(y, x, x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides,
+                                     table_dtype, mode, partial_slice, dir, &L.p, &why);
+    if (st != ROPE_OK) return set_error(st, why);
+    if (L.p.noop) return ROPE_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (L.p.copy_only) {
+        err = hipMemcpyAsync(L.p.x, L.p.src, (size_t)L.p.bytes, hipMemcpyDeviceToDevice, s);
+    } else {
+        int cus = 0;
+        if ((st = device_cus(&cus)) != ROPE_OK) return st;
+        if (L.p.src == nullptr) {
+            prepare(&L);
+            err = launch_one(L, cus, s);
+        } else {
+            prepare_out(&L);
+            err = launch_out(L, cus, s);
+        }
+    }
+    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("launch: ") + hipGetErrorString(err));
     return ROPE_OK;
 }
 
@@ -985,10 +1074,10 @@ rope_status_t run_multi(int32_t count, void* const xs[], const int64_t (*x_shape
 
     bool together = live > 1;
     const uint32_t threads = L[0].a.span * L[0].a.HL * L[0].a.GL;
-    const void* fn = together && L[0].vec ? vec_kernel(L[0].p, L[0].cfg, true) : nullptr;
+    const void* fn = together && L[0].vec ? vec_kernel(L[0].p, kVecMulti) : nullptr;
     for (int i = 0; i < live && together; ++i) {
         together = L[i].vec && L[i].a.span * L[i].a.HL * L[i].a.GL == threads &&
-                   vec_kernel(L[i].p, L[i].cfg, true) == fn && L[i].cfg.grid == 0;
+                   vec_kernel(L[i].p, kVecMulti) == fn && L[i].cfg.grid == 0;
     }
     hipError_t err = hipSuccess;
     if (together) {
@@ -1037,6 +1126,26 @@ rope_status_t rope_partial_bwd_inplace(void* x, const int64_t x_shape[4], rope_d
 {
     return rope::run(x, x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides, table_dtype, mode,
                      partial_slice, stream, rope::kBwd);
+}
+
+rope_status_t rope_partial_fwd_out(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                   const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                                   const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                                   rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                   void* stream)
+{
+    return rope::run_out(y, x, x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides, table_dtype,
+                         mode, partial_slice, stream, rope::kFwd);
+}
+
+rope_status_t rope_partial_bwd_out(void* dx, const void* dy, const int64_t x_shape[4], rope_dtype_t dtype,
+                                   const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                                   const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                                   rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                   void* stream)
+{
+    return rope::run_out(dx, dy, x_shape, dtype, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides, table_dtype,
+                         mode, partial_slice, stream, rope::kBwd);
 }
 
 rope_status_t rope_partial_fwd_inplace_multi(int32_t count, void* const xs[], const int64_t x_shapes[][4],

@@ -66,15 +66,11 @@ rope_status_t check_table(const char* name, const int64_t shape[4], const int64_
     return ROPE_OK;
 }
 
-}  // namespace
-
-rope_status_t make_plan(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
-                        const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
-                        const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
-                        rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
-                        Direction dir, Plan* plan, std::string* why)
+// Check 1: the scalar arguments. Fills every field of p but the pointers.
+rope_status_t check_scalars(const int64_t x_shape[4], rope_dtype_t dtype, rope_dtype_t table_dtype, int64_t mode,
+                            const int64_t partial_slice[2], Direction dir, Plan* p, int64_t* numel_out,
+                            std::string* why)
 {
-    // 1. scalar arguments
     if (x_shape == nullptr)
         return fail(ROPE_ERR_NULLPTR, why, "x_shape is NULL");
     if (mode != ROPE_MODE_INTERLEAVE && mode != ROPE_MODE_ROTATE_HALF)
@@ -112,36 +108,101 @@ rope_status_t make_plan(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
     if (!mul_ok(numel, element_size(dtype), &bytes))
         return fail(ROPE_ERR_INVALID, why, "x byte size overflows 64 bits");
 
-    Plan p;
-    p.B = x_shape[0]; p.S = x_shape[1]; p.N = x_shape[2]; p.D = D;
-    p.start = start; p.L = L;
-    p.dtype = dtype; p.tdtype = table_dtype; p.mode = (int)mode; p.dir = dir;
-    p.esize = element_size(dtype);
-    p.tesize = element_size(table_dtype);
+    p->B = x_shape[0]; p->S = x_shape[1]; p->N = x_shape[2]; p->D = D;
+    p->start = start; p->L = L;
+    p->dtype = dtype; p->tdtype = table_dtype; p->mode = (int)mode; p->dir = dir;
+    p->esize = element_size(dtype);
+    p->tesize = element_size(table_dtype);
+    p->bytes = bytes;
+    *numel_out = numel;
+    return ROPE_OK;
+}
 
-    // 2. no-op: nothing to rotate; pointers and tables are not looked at
-    if (numel == 0 || L == 0) {
-        p.noop = true;
-        *plan = p;
-        return ROPE_OK;
-    }
-
-    // 3. pointers
-    if (x == nullptr) return fail(ROPE_ERR_NULLPTR, why, "x is NULL");
+// Checks 3 (table pointers) and 4 (table geometry).
+rope_status_t check_tables(const int64_t x_shape[4],
+                           const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                           const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                           Plan* p, std::string* why)
+{
     if (r1 == nullptr) return fail(ROPE_ERR_NULLPTR, why, "r1 is NULL");
     if (r2 == nullptr) return fail(ROPE_ERR_NULLPTR, why, "r2 is NULL");
     if (r1_shape == nullptr || r1_strides == nullptr)
         return fail(ROPE_ERR_NULLPTR, why, "r1 shape or strides is NULL");
     if (r2_shape == nullptr || r2_strides == nullptr)
         return fail(ROPE_ERR_NULLPTR, why, "r2 shape or strides is NULL");
-
-    // 4. table geometry
-    rope_status_t st = check_table("r1", r1_shape, r1_strides, x_shape, L, p.t1, why);
+    rope_status_t st = check_table("r1", r1_shape, r1_strides, x_shape, p->L, p->t1, why);
     if (st != ROPE_OK) return st;
-    st = check_table("r2", r2_shape, r2_strides, x_shape, L, p.t2, why);
+    st = check_table("r2", r2_shape, r2_strides, x_shape, p->L, p->t2, why);
+    if (st != ROPE_OK) return st;
+    p->r1 = r1;
+    p->r2 = r2;
+    return ROPE_OK;
+}
+
+}  // namespace
+
+rope_status_t make_plan(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                        const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                        const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                        rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                        Direction dir, Plan* plan, std::string* why)
+{
+    // 1. scalar arguments
+    Plan p;
+    int64_t numel = 0;
+    rope_status_t st = check_scalars(x_shape, dtype, table_dtype, mode, partial_slice, dir, &p, &numel, why);
     if (st != ROPE_OK) return st;
 
-    p.x = x; p.r1 = r1; p.r2 = r2;
+    // 2. no-op: nothing to rotate; pointers and tables are not looked at
+    if (numel == 0 || p.L == 0) {
+        p.noop = true;
+        *plan = p;
+        return ROPE_OK;
+    }
+
+    // 3./4. pointers and table geometry
+    if (x == nullptr) return fail(ROPE_ERR_NULLPTR, why, "x is NULL");
+    st = check_tables(x_shape, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides, &p, why);
+    if (st != ROPE_OK) return st;
+    p.x = x;
+    *plan = p;
+    return ROPE_OK;
+}
+
+rope_status_t make_plan_out(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                            const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                            const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                            rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                            Direction dir, Plan* plan, std::string* why)
+{
+    Plan p;
+    int64_t numel = 0;
+    rope_status_t st = check_scalars(x_shape, dtype, table_dtype, mode, partial_slice, dir, &p, &numel, why);
+    if (st != ROPE_OK) return st;
+    if (numel == 0) {
+        p.noop = true;
+        *plan = p;
+        return ROPE_OK;
+    }
+    if (y == nullptr) return fail(ROPE_ERR_NULLPTR, why, "y is NULL");
+    if (x == nullptr) return fail(ROPE_ERR_NULLPTR, why, "x is NULL");
+    // [y, y+bytes) and [x, x+bytes) overlap iff either start lies less than
+    // `bytes` past the other (unsigned differences; no pointer arithmetic)
+    const uintptr_t yu = reinterpret_cast<uintptr_t>(y), xu = reinterpret_cast<uintptr_t>(x);
+    const uint64_t nb = (uint64_t)p.bytes;
+    const bool same = yu == xu;
+    if (!same && ((uint64_t)(yu - xu) < nb || (uint64_t)(xu - yu) < nb))
+        return fail(ROPE_ERR_INVALID, why, "y and x overlap without being the same buffer");
+    if (p.L == 0) {
+        // y = x: a copy, or nothing at all when they are one buffer
+        p.noop = same;
+        p.copy_only = !same;
+    } else {
+        st = check_tables(x_shape, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides, &p, why);
+        if (st != ROPE_OK) return st;
+    }
+    p.x = y;
+    p.src = same ? nullptr : x;
     *plan = p;
     return ROPE_OK;
 }

@@ -24,8 +24,11 @@ struct Plan {
     int dir = kFwd;
     int esize = 0;           // bytes per element of x
     int tesize = 0;          // bytes per element of the tables
-    bool noop = false;       // empty tensor or empty slice: launch nothing
-    void* x = nullptr;
+    bool noop = false;       // nothing to launch (empty tensor; in place: or empty slice)
+    bool copy_only = false;  // out of place with an empty slice: y = x, no rotation
+    int64_t bytes = 0;       // size of x in bytes
+    void* x = nullptr;       // the tensor written (in place: also read)
+    const void* src = nullptr;  // out of place: the tensor read (distinct from x); else NULL
     const void* r1 = nullptr;
     const void* r2 = nullptr;
     // Table strides in elements for the b, s and n dimensions; 0 where the
@@ -41,6 +44,18 @@ rope_status_t make_plan(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
                         const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
                         rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
                         Direction dir, Plan* plan, std::string* why);
+
+// Out-of-place form: y receives x with its slice rotated and x is left
+// as it is. Checks, in order: the scalar arguments of make_plan; an empty
+// tensor is a no-op; NULL y or x; y and x overlapping without being the
+// same buffer (y == x is the in-place operation); an empty slice is a plain
+// copy (the tables are not looked at); then the tables as in make_plan.
+// On success plan->x is y, and plan->src is x unless y == x.
+rope_status_t make_plan_out(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                            const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                            const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                            rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                            Direction dir, Plan* plan, std::string* why);
 
 int element_size(int dtype);
 
