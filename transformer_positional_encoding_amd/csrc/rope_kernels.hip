@@ -326,15 +326,19 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
     const uint32_t gl = fast_div(q, a.hl_div);
     const uint32_t hl = q - gl * a.HL;
     const uint32_t c = a.lo_vec + vs;                 // vector within the row
-    const bool in_slice = c >= a.start_vec && c - a.start_vec < a.nvec;
-    const uint32_t v = in_slice ? c - a.start_vec : 0;  // x vector in the slice (table index)
-    // Out of place, rotate_half: vectors of the slice's second half are
-    // written by the threads of the first half, and threads outside the
-    // slice load their own vector in place of a partner.
-    const bool partner_half =
+    const bool in_unit = c >= a.start_vec && c - a.start_vec < a.nvec;
+    // Out of place, every thread stores exactly the vector it covers, in one
+    // instruction. For rotate_half the threads of the slice's second half
+    // therefore rotate too: each loads the matching vector of the other half
+    // as its partner (xa = first-half vector, xb = second-half vector) and
+    // keeps its own component. In place, the first-half threads store both.
+    const bool second_half =
         OUT && MODE == kModeRH && c >= a.start_vec + a.nvec && c - a.start_vec - a.nvec < a.nvec;
-    const uint32_t hoff = !OUT || in_slice ? a.half_vecs : 0;
-    if (gl >= a.GL || partner_half) return;  // no barriers below, so idle threads may leave
+    const bool in_slice = in_unit || second_half;
+    const uint32_t v = in_unit ? c - a.start_vec : second_half ? c - a.start_vec - a.nvec : 0;  // unit (table index)
+    const uint32_t back = second_half ? a.half_vecs : 0;             // xa = own vector - back
+    const uint32_t ahead = !OUT || in_unit ? a.half_vecs : 0;        // xb = own vector + ahead
+    if (gl >= a.GL) return;  // no barriers below, so idle threads may leave
 
     const uint32_t first = xcd_grouped_block(bid, a);
     for (uint32_t bt = first; bt < a.btiles; bt += G) {
@@ -384,8 +388,12 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
                     }
                 }
             }
-            xa[k] = load_x<NT>(src + off[k]);
-            if constexpr (MODE == kModeRH) xb[k] = load_x<NT>(src + off[k] + hoff);
+            if constexpr (MODE == kModeRH) {
+                xa[k] = load_x<NT>(src + off[k] - back);
+                xb[k] = load_x<NT>(src + off[k] + ahead);
+            } else {
+                xa[k] = load_x<NT>(src + off[k]);
+            }
         }
         // Keep every load above in flight together: without this barrier the
         // machine scheduler starts the arithmetic on the first vectors and
@@ -395,32 +403,41 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             if (!live[k]) continue;
-            if (!in_slice) {
-                if constexpr (OUT) store_x<NT>(a.x + off[k], xa[k]);  // copied unchanged
-                continue;
+            if (!OUT && !in_slice) continue;
+            // Out of place, a vector outside the slice is copied unchanged.
+            // Each vector is stored by one instruction either way, so a
+            // 128-byte line that the slice splits is written by one wave
+            // instruction rather than two partial ones.
+            v4u ya = xa[k], yb = xa[k];
+            if (in_slice) {
+                const int kt = HEADS_SHARE_TABLES ? 0 : k;
+                Lanes<DT> X;
+                TableLanes<TT, K> C, S;
+                X.unpack(xa[k]);
+                C.unpack(ca[kt]);
+                S.unpack(sa[kt]);
+                if constexpr (MODE == kModeIL) {
+#pragma unroll
+                    for (int i = 0; i < K; i += 2)
+                        rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C.v[i], S.v[i], C.v[i + 1], S.v[i + 1]);
+                } else {
+                    Lanes<DT> X2;
+                    TableLanes<TT, K> C2, S2;
+                    X2.unpack(xb[k]);
+                    C2.unpack(cb[kt]);
+                    S2.unpack(sb[kt]);
+#pragma unroll
+                    for (int i = 0; i < K; ++i)
+                        rotate_pair<DIR, kUnfused>(X.v[i], X2.v[i], C.v[i], S.v[i], C2.v[i], S2.v[i]);
+                    yb = X2.pack();
+                }
+                ya = X.pack();
             }
-            const int kt = HEADS_SHARE_TABLES ? 0 : k;
-            Lanes<DT> X;
-            TableLanes<TT, K> C, S;
-            X.unpack(xa[k]);
-            C.unpack(ca[kt]);
-            S.unpack(sa[kt]);
-            if constexpr (MODE == kModeIL) {
-#pragma unroll
-                for (int i = 0; i < K; i += 2)
-                    rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C.v[i], S.v[i], C.v[i + 1], S.v[i + 1]);
-                store_x<NT>(a.x + off[k], X.pack());
+            if constexpr (OUT) {
+                store_x<NT>(a.x + off[k], second_half ? yb : ya);
             } else {
-                Lanes<DT> X2;
-                TableLanes<TT, K> C2, S2;
-                X2.unpack(xb[k]);
-                C2.unpack(cb[kt]);
-                S2.unpack(sb[kt]);
-#pragma unroll
-                for (int i = 0; i < K; ++i)
-                    rotate_pair<DIR, kUnfused>(X.v[i], X2.v[i], C.v[i], S.v[i], C2.v[i], S2.v[i]);
-                store_x<NT>(a.x + off[k], X.pack());
-                store_x<NT>(a.x + off[k] + a.half_vecs, X2.pack());
+                store_x<NT>(a.x + off[k], ya);
+                if constexpr (MODE == kModeRH) store_x<NT>(a.x + off[k] + a.half_vecs, yb);
             }
         }
     }
@@ -588,9 +605,14 @@ int cu_count(int dev)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Heads per thread of the instantiated vector kernels: in place, and out of
+// place (see prepare_out).
+constexpr int kUInPlace = 1;
+constexpr int kUOut = 2;
+
 // Launch shape of the vector kernel.
 struct VecConfig {
-    int U = 1;          // heads per thread per tile (the library instantiates 1)
+    int U = 1;          // heads per thread per tile (kUInPlace or kUOut)
     uint32_t HL = 1;    // head lanes per tile
     uint32_t GL = 1;    // tiles per block iteration
     uint32_t grid = 0;  // blocks; 0 = one block per tile group
@@ -699,9 +721,9 @@ VecConfig shape_for(const VecArgs& a, int U, uint32_t threads)
 // long-context shard (16,8192,32,128) with lanes [32,96).
 constexpr uint64_t kXcdRunBytes = 384u << 10;
 
-VecConfig choose_vec_config(const Plan& p, const VecArgs& a)
+VecConfig choose_vec_config(const Plan& p, const VecArgs& a, int U)
 {
-    VecConfig c = shape_for(a, 1, 64);
+    VecConfig c = shape_for(a, U, 64);
     c.nt = true;
     const uint64_t heads_per_tile = (uint64_t)c.HL * c.U;
     const uint64_t blocks_per_position = c.GL == 1 ? (a.N + heads_per_tile - 1) / heads_per_tile : 1;
@@ -733,9 +755,10 @@ uint32_t vec_grid(const VecArgs& a, const VecConfig& cfg)
 // gridDim.x to it), in which case a general kernel runs instead.
 bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
 {
-    // The library instantiates the chosen shape only: one head per thread,
-    // nontemporal x.
-    if (cfg.U != 1 || !cfg.nt || cfg.HL < 1 || cfg.GL < 1 || (uint64_t)cfg.HL * cfg.GL * a->span > 256)
+    // The library instantiates the chosen shapes only: kUInPlace or kUOut
+    // heads per thread, nontemporal x.
+    if (cfg.U != (a->src ? kUOut : kUInPlace) || !cfg.nt || cfg.HL < 1 || cfg.GL < 1 ||
+        (uint64_t)cfg.HL * cfg.GL * a->span > 256)
         return false;
     a->HL = cfg.HL;
     a->GL = cfg.GL;
@@ -765,21 +788,21 @@ bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
 // of place.
 enum VecKind { kVecOne = 0, kVecMulti = 1, kVecOut = 2 };
 
-template <int DT, int TT, int DIR, int MODE, int U, bool SHARE, bool NT>
+template <int DT, int TT, int DIR, int MODE, bool SHARE>
 const void* vec_kernel_ptr(VecKind kind)
 {
     switch (kind) {
-    case kVecMulti: return reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, TT, DIR, MODE, U, SHARE, NT>);
-    case kVecOut: return reinterpret_cast<const void*>(&rope_vec_out_kernel<DT, TT, DIR, MODE, U, SHARE, NT>);
-    default: return reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, U, SHARE, NT>);
+    case kVecMulti:
+        return reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, TT, DIR, MODE, kUInPlace, SHARE, true>);
+    case kVecOut: return reinterpret_cast<const void*>(&rope_vec_out_kernel<DT, TT, DIR, MODE, kUOut, SHARE, true>);
+    default: return reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, kUInPlace, SHARE, true>);
     }
 }
 
 template <int DT, int TT, int DIR, int MODE>
 const void* vec_kernel_s(bool share, VecKind kind)
 {
-    return share ? vec_kernel_ptr<DT, TT, DIR, MODE, 1, true, true>(kind)
-                 : vec_kernel_ptr<DT, TT, DIR, MODE, 1, false, true>(kind);
+    return share ? vec_kernel_ptr<DT, TT, DIR, MODE, true>(kind) : vec_kernel_ptr<DT, TT, DIR, MODE, false>(kind);
 }
 
 template <int DT, int TT>
@@ -945,7 +968,7 @@ void prepare(Launch* L)
     L->vec = vec_geometry(L->p, &L->a);
     if (L->vec) {
         cover_whole_lines(L->p, &L->a);
-        L->cfg = choose_vec_config(L->p, L->a);
+        L->cfg = choose_vec_config(L->p, L->a, kUInPlace);
         L->vec = finish_vec_args(L->p, L->cfg, &L->a);
     }
     if (!L->vec) L->rows = rows_shape(L->p, &L->rs);
@@ -961,6 +984,18 @@ hipError_t launch_one(const Launch& L, int cus, hipStream_t s)
 // vector kernel reads src and writes x in one pass over whole rows: the
 // slice rotated, the other vectors copied. Inputs it cannot take (alignment,
 // sizes) get a device copy of src into x and then the in-place plan on x.
+//
+// Launch shape, measured on MI355X over six shapes (bf16 and fp32; slices
+// of 1/3, 1/2 and all of the row; interleave and rotate_half; slices on and
+// off 128-byte line boundaries), heads per thread 1-2, blocks of 64-256
+// threads, and plain or nontemporal loads and stores chosen separately: two
+// heads per thread, 64-thread blocks and nontemporal loads and stores was
+// within 2% of the best on five shapes and 8% on the sixth (a rotate_half
+// slice off line boundaries). One head per thread was 10-15% slower on the
+// rotate_half shapes and the 192-lane rows. With every vector stored by one
+// instruction (see the vector kernel) the long-context shard (16,8192,32,128)
+// bf16 takes 322 us, 6.8 TB/s of read plus write, against 420 us for a
+// plain device copy of the same tensor.
 void prepare_out(Launch* L)
 {
     L->vec = vec_geometry(L->p, &L->a) && aligned16(L->p.src);
@@ -968,7 +1003,7 @@ void prepare_out(Launch* L)
         L->a.src = static_cast<const v4u*>(L->p.src);
         L->a.lo_vec = 0;
         L->a.span = L->a.row_vecs;
-        L->cfg = choose_vec_config(L->p, L->a);
+        L->cfg = choose_vec_config(L->p, L->a, kUOut);
         L->vec = finish_vec_args(L->p, L->cfg, &L->a);
     }
     if (!L->vec) L->rows = rows_shape(L->p, &L->rs);
