@@ -316,35 +316,47 @@ def bench_out_of_place(name: str, reps: int, stream) -> dict:
                              "GBps": round(nbytes / t_one / 1e9, 1),
                              "frac_of_peak": round(nbytes / t_one / 1e9 / PEAK_GBPS, 4),
                              "copy_then_in_place_us": round(t_two * 1e6, 3)}
+        tr = committed_traffic(name + ":out", d)
+        if tr is not None:
+            res["kernels"][d]["hbm_bytes_per_launch"] = tr["hbm_bytes_per_launch"]
+            res["kernels"][d]["hbm_GBps"] = round(tr["hbm_bytes_per_launch"] / t_one / 1e9, 1)
+            res["kernels"][d]["hbm_frac_of_peak"] = round(tr["hbm_bytes_per_launch"] / t_one / 1e9 / PEAK_GBPS, 4)
     del xs, ys, x
     torch.cuda.empty_cache()
     return res
 
 
-def profile_target(name: str, reps: int) -> None:
+def profile_target(name: str, reps: int, out_of_place: bool = False) -> None:
     """Launches for rocprofv3 counter passes: each direction of the workload
-    `reps` times (rotating copies as in the timed run), then a plain device
-    copy of known size for calibrating the byte counters."""
+    `reps` times (rotating copies as in the timed run; out of place, from x
+    into a second buffer), then a plain device copy of known size for
+    calibrating the byte counters."""
     import torch
 
+    import transformer_positional_encoding_amd as rp
     import workloads as W
     w = W.WORKLOADS[name]
-    ncopy = rotating_copies(w)
+    ncopy = 1 if out_of_place else rotating_copies(w)
     xs = [W.make_x(w).to("cuda")]
     xs += [xs[0].clone() for _ in range(ncopy - 1)]
     r1, r2 = (t.to("cuda") for t in W.make_tables(w))
     dirs = list(w.directions) + [d for d in ("fwd", "bwd") if d not in w.directions]
+    y = torch.empty_like(xs[0]) if out_of_place else None
     for d in dirs:
         for i in range(reps):
-            launch_fn(d)(xs[i % ncopy], r1, r2, w.mode, w.partial_slice)
+            if out_of_place:
+                (rp.rope_partial_fwd_out if d == "fwd" else rp.rope_partial_bwd_out)(
+                    y, xs[0], r1, r2, w.mode, w.partial_slice)
+            else:
+                launch_fn(d)(xs[i % ncopy], r1, r2, w.mode, w.partial_slice)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")  # 256 MiB
     src.fill_(1)
     dst = torch.empty_like(src)
     for _ in range(reps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_target": name, "reps": reps, "copy_bytes": src.numel(),
-                      "rotating_copies": ncopy}), flush=True)
+    print(json.dumps({"profile_target": name, "out_of_place": out_of_place, "reps": reps,
+                      "copy_bytes": src.numel(), "rotating_copies": ncopy}), flush=True)
 
 
 def main() -> int:
@@ -361,6 +373,8 @@ def main() -> int:
                     help="CPU oracle budget: whole steps repeated to fill about this many seconds")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-target", action="store_true")
+    ap.add_argument("--out-of-place", action="store_true",
+                    help="with --profile-target: launch the out-of-place entry points")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -376,7 +390,7 @@ def main() -> int:
     rp.library()  # fail loudly if the HIP library is missing
 
     if args.profile_target:
-        profile_target(args.workload, args.reps)
+        profile_target(args.workload, args.reps, args.out_of_place)
         return 0
 
     stream = torch.cuda.current_stream()

@@ -123,6 +123,78 @@ int main()
         }
         if (!good) ++bad;
     }
-    printf("iters %ld accepted %ld noop %ld bad %ld\n", iters, ok, noop, bad);
-    return bad == 0 && ok > 1000 && noop > 1000 ? 0 : 1;
+    // The out-of-place form: the same arguments with an input pointer that is
+    // the output, overlaps it, lies elsewhere or is NULL. Pointers stay below
+    // 2^47, as device addresses do, so that [p, p + bytes) never wraps.
+    long out_ok = 0, out_copy = 0, out_overlap = 0;
+    for (long it = 0; it < iters / 3; ++it) {
+        int64_t xs[4], t[4] = {0, 0, 0, 1}, ts[4], sl[2];
+        for (int k = 0; k < 3; ++k) xs[k] = (next() % 4) ? (int64_t)(next() % 9) : pick();
+        xs[3] = (next() % 8) ? 2 * (int64_t)(next() % 520) : pick();
+        sl[0] = (int64_t)(next() % 64);
+        sl[1] = (next() % 4) ? sl[0] : sl[0] + 2 * (int64_t)(next() % 32);
+        if (next() % 8 == 0) sl[1] = pick();
+        const int64_t L = (int64_t)((uint64_t)sl[1] - (uint64_t)sl[0]);
+        for (int k = 0; k < 3; ++k) { t[k] = 1; ts[k] = 0; }
+        t[3] = L; ts[3] = 1;
+        const int dtype = (int)(next() % 3);
+        const uint64_t y = 0x10000 + (next() % (1ull << 40)) * 16;
+        uint64_t x;
+        switch (next() % 6) {
+        case 0: x = y; break;
+        case 1: x = 0; break;
+        case 2: x = y + (next() % 8192); break;                                  // often inside y
+        case 3: x = y > (next() % 8192) ? y - (next() % 8192) : y; break;        // often overlapping from below
+        default: x = 0x10000 + (next() % (1ull << 46)); break;
+        }
+        const bool null_y = next() % 16 == 0;
+        void* yp = null_y ? nullptr : reinterpret_cast<void*>(y);
+        const void* xp = reinterpret_cast<const void*>(x);
+        rope::Plan p;
+        std::string why;
+        const rope_status_t st = rope::make_plan_out(yp, xp, xs, (rope_dtype_t)dtype, fake, t, ts, fake, t, ts,
+                                                     (rope_dtype_t)dtype, 1, sl, rope::kBwd, &p, &why);
+        if (st != ROPE_OK && st != ROPE_ERR_NULLPTR && st != ROPE_ERR_INVALID) { ++bad; continue; }
+        // the reference: every dimension and the slice valid, element count and bytes in 128 bits
+        bool scalars = sl[0] >= 0 && sl[1] >= sl[0] && sl[1] <= xs[3] && L % 2 == 0 && xs[3] % 2 == 0 &&
+                       xs[3] <= 1024;
+        i128 numel = 1;
+        for (int k = 0; k < 4; ++k) {
+            scalars = scalars && xs[k] >= 0;
+            if (xs[k] >= 0) numel *= xs[k];
+            // saturate just past the 64-bit range (the exact size no longer matters)
+            if (numel > (i128)std::numeric_limits<int64_t>::max()) numel = (i128)std::numeric_limits<int64_t>::max() + 1;
+        }
+        const i128 nbytes = numel * (dtype == 0 ? 4 : 2);
+        scalars = scalars && nbytes <= (i128)std::numeric_limits<int64_t>::max();
+        const bool empty = numel == 0;
+        const bool overlap = !empty && !null_y && x != 0 && x != y && (i128)x < (i128)y + nbytes &&
+                             (i128)y < (i128)x + nbytes;
+        if (st != ROPE_OK) {
+            if (why.empty()) ++bad;
+            if (why.find("overlap") != std::string::npos) {
+                ++out_overlap;
+                if (!overlap) ++bad;
+            }
+            if (scalars && !empty && !null_y && x != 0 && !overlap) ++bad;   // nothing wrong with these arguments
+            continue;
+        }
+        if (!scalars || overlap) { ++bad; continue; }
+        if (empty) {
+            if (!p.noop) ++bad;
+            continue;
+        }
+        if (null_y || x == 0) { ++bad; continue; }
+        if (p.bytes != (int64_t)nbytes || p.x != yp) ++bad;
+        if (L == 0) {
+            if (x == y ? !(p.noop && !p.copy_only) : !(p.copy_only && !p.noop && p.src == xp)) ++bad;
+            out_copy += x != y;
+            continue;
+        }
+        if (p.noop || p.copy_only || p.src != (x == y ? nullptr : xp)) ++bad;
+        ++out_ok;
+    }
+    printf("iters %ld accepted %ld noop %ld out-of-place accepted %ld copies %ld overlaps %ld bad %ld\n", iters, ok,
+           noop, out_ok, out_copy, out_overlap, bad);
+    return bad == 0 && ok > 1000 && noop > 1000 && out_ok > 1000 && out_copy > 1000 && out_overlap > 1000 ? 0 : 1;
 }
