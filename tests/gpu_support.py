@@ -155,3 +155,35 @@ def run_and_check(x_cpu: torch.Tensor, r1: torch.Tensor, r2: torch.Tensor, mode:
 def _bits(t: torch.Tensor) -> torch.Tensor:
     t = t.contiguous()
     return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+def run_out_and_check(x_cpu, r1, r2, mode, sl, direction, what, sample=None, seed=0, y_dev=None, x_dev=None,
+                      device="cuda", r1_dev=None, r2_dev=None):
+    """Run the out-of-place entry point from a fresh device copy of x into
+    y_dev (default: a new tensor) and compare with the oracle on every row or
+    on `sample` rows; x must be unchanged."""
+    dtype = TDT[x_cpu.dtype]
+    announce(f"{what} out-of-place shape={tuple(x_cpu.shape)} {dtype} {mode} {direction} slice={sl}")
+    x_dev = x_cpu.to(device) if x_dev is None else x_dev
+    y_dev = torch.full_like(x_dev, float("nan")) if y_dev is None else y_dev
+    fn = rp.rope_partial_fwd_out if direction == "fwd" else rp.rope_partial_bwd_out
+    fn(y_dev, x_dev, r1.to(device) if r1_dev is None else r1_dev, r2.to(device) if r2_dev is None else r2_dev,
+       mode, sl)
+    torch.cuda.synchronize()
+    B, S, N, D = x_cpu.shape
+    total = B * S * N
+    assert torch.equal(_bits(x_dev), _bits(x_cpu.to(device))), f"{what}: the input changed"
+    rows = np.arange(total, dtype=np.int64) if sample is None else W.sample_rows(total, sample, seed)
+    rows_t = torch.from_numpy(rows).to(device)
+    got = W.to_numpy_storage(y_dev.view(total, D).index_select(0, rows_t).cpu())
+    x_rows = np.ascontiguousarray(W.to_numpy_storage(x_cpu).reshape(total, D)[rows])
+    want = oracle_rows(x_rows, x_cpu.shape, dtype, r1, r2, mode, sl, direction, rows)
+    L = sl[1] - sl[0]
+    c = expanded_tables(r1, x_cpu.shape, rows, L)
+    s = expanded_tables(r2, x_cpu.shape, rows, L)
+    info = compare(got, want, x_rows, c, s, dtype, mode, direction, sl, what)
+    if sample is not None:
+        # every row's lanes outside the slice: x's bytes
+        assert torch.equal(_bits(y_dev[..., : sl[0]]), _bits(x_dev[..., : sl[0]])), f"{what}: head lanes"
+        assert torch.equal(_bits(y_dev[..., sl[1]:]), _bits(x_dev[..., sl[1]:])), f"{what}: tail lanes"
+    return info
