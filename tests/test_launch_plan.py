@@ -163,3 +163,30 @@ def test_scalar_kernel_from_two_to_the_31_rows():
     assert st == OK and info["kernel"] == "scalar"
     st, info = plan((1, 2 ** 31 - 1, 1, 2), BF16, (0, 2))
     assert st == OK and info["kernel"] == "rows"
+
+
+@pytest.mark.parametrize("dtype,sl,span", [
+    (BF16, (0, 128), 8),      # whole bf16 head: each half is one 128-byte line -> pair owner, first half only
+    (F32, (0, 128), 16),      # fp32: halves of 256 bytes, on lines -> pair owner
+    (BF16, (64, 128), 8),     # 64-byte halves -> own vector, the whole slice (one line)
+    (BF16, (32, 96), 16),     # 64-byte halves off line boundaries -> own vector over both lines
+    (BF16, (0, 32), 8),       # NeoX-style rotary_dim 32 of 128: own vector over the slice's whole line
+    (F16, (0, 64), 8),        # 64-byte halves in one line -> own vector
+])
+def test_rotate_half_schemes(dtype, sl, span):
+    """rotate_half in place: the pair-owner scheme (threads cover the first
+    half) when each half is whole 128-byte lines, else the own-vector scheme
+    (threads cover the slice's whole lines)."""
+    st, info = plan((16, 4096, 32, 128), dtype, sl, mode=RH)
+    assert st == OK and info["kernel"] == "vector"
+    assert info["row_vectors"] == span
+    assert info["threads"] <= 64
+
+
+def test_rotate_half_own_vector_needs_single_wave_rows():
+    """(1,3,5,1024) lanes [8,1000): the halves are off line boundaries, but a
+    row of the own-vector scheme would need 124 threads (bf16) or 248 (fp32),
+    more than one wave, so the pair owner runs (62 or 124 threads per row)."""
+    for dtype, span in ((BF16, 62), (F32, 124)):
+        st, info = plan((1, 3, 5, 1024), dtype, (8, 1000), mode=RH)
+        assert st == OK and info["kernel"] == "vector" and info["row_vectors"] == span

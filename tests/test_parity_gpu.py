@@ -134,6 +134,10 @@ CASES = [
     ((2, 8, 4, 64), (0, 64), "interleave", (2, 1, 1, 64)),        # B11D
     ((2, 8, 4, 64), (0, 64), "interleave", (1, 1, 1, 64)),        # 111D
     ((2, 8, 4, 128), (0, 128), "rotate_half", (2, 8, 4, 128)),    # per-head tables, rotate_half
+    ((2, 8, 4, 128), (64, 128), "rotate_half", (1, 8, 1, 64)),    # 16-bit: own-vector rotate_half, one line
+    ((2, 8, 4, 128), (32, 96), "rotate_half", (2, 8, 4, 64)),     # own vector over two lines, per-head tables
+    ((3, 5, 13, 128), (0, 32), "rotate_half", (1, 5, 1, 32)),     # NeoX-style rotary_dim 32: own vector, whole line
+    ((1, 3, 5, 1024), (8, 1000), "rotate_half", (1, 3, 1, 992)),  # rows wider than a wave: pair owner
 ]
 
 

@@ -42,6 +42,12 @@ typedef uint32_t v2u __attribute__((ext_vector_type(2)));  // half of one
 
 constexpr int kModeRH = ROPE_MODE_ROTATE_HALF;
 constexpr int kModeIL = ROPE_MODE_INTERLEAVE;
+// rotate_half schemes of the vector kernel (see there): each thread writes
+// its own vector and takes its partner's from the lane that holds it (a
+// row's threads in one wave), or loads the partner from memory (out of
+// place, rows wider than a wave)
+constexpr int kModeRHOwn = 2;
+constexpr int kModeRHOwnLoad = 3;
 
 // ---------------------------------------------------------------------------
 // fp32 <-> storage conversions. A 32-bit word holds two adjacent 16-bit lanes
@@ -186,6 +192,29 @@ __device__ __forceinline__ void rotate_pair(float& a, float& b, float ca, float 
     }
 }
 
+// One lane of rotate_half in the own-vector scheme: the lane's value x, its
+// partner's value p, and y = x*c - p*s (neg) or x*c + p*s, with c the lane's
+// cos and s the sine the direction takes (the lane's forward, the partner's
+// backward). These are the same products and sum as rotate_pair forms for
+// that lane, with the same roundings.
+__device__ __forceinline__ float rotate_own_unfused(float x, float p, float c, float s, bool neg)
+{
+#pragma clang fp contract(off)
+    const float t = p * s;
+    return x * c + (neg ? -t : t);
+}
+
+template <bool UNFUSED>
+__device__ __forceinline__ float rotate_own(float x, float p, float c, float s, bool neg)
+{
+    if constexpr (UNFUSED) {
+        return rotate_own_unfused(x, p, c, s, neg);
+    } else {
+        const float t = p * s;
+        return x * c + (neg ? -t : t);
+    }
+}
+
 // The cos or sin values for the K lanes of one x vector, from a table of
 // type TT. They take K * sizeof(TT) bytes, loaded as kVecs table units of
 // type Vec: 8 bytes (half a vector) when fp32 x meets a 16-bit table, one
@@ -220,27 +249,43 @@ struct TableLanes {
 };
 
 // ---------------------------------------------------------------------------
-// Vector kernel. Work unit = one 16-byte vector of the slice (interleave:
-// whole pairs inside it) or, for rotate_half, vector k of the first half plus
-// vector k of the second half (lanes i and i+L/2 in matching positions).
+// Vector kernel. A thread works on 16-byte vectors of x: whole interleave
+// pairs inside one vector, or rotate_half pairs across two vectors (lanes i
+// and i+L/2 in matching positions of vector k of each half).
 //
 // Tile = one (b,s) position and a chunk of HL*U heads. A block works on GL
 // tiles at a time; thread t takes row vector c = lo_vec + t % span, head
 // lane hl = (t / span) % HL and tile lane gl = t / (span*HL), and handles
-// heads n = chunk*HL*U + hl + k*HL for k < U. Normally the threads cover
-// exactly the slice (lo_vec = start_vec, span = nvec). When the slice covers
-// only part of its first or last 128-byte line, the threads of an interleave
-// row cover every vector of those lines instead: each line is then requested
-// whole by one wave instruction, which the L2 serves much faster than two
-// half-line requests (it fetches the whole line either way); vectors outside
-// the slice are loaded and dropped, never stored. Out of place (src is
-// another tensor) the threads cover whole rows: vectors outside the slice
-// are copied from src to x, and for rotate_half the threads of the slice's
-// first half write both halves. The cos/sin units of a
-// thread are loaded once per tile and, when the tables broadcast over heads,
-// reused for all its heads. All loads of a tile are issued before any arithmetic. The
-// grid normally has one block per group of GL tiles; a smaller grid makes
-// the blocks stride over the groups.
+// heads n = chunk*HL*U + hl + k*HL for k < U.
+//
+// Which vectors a row's threads cover, and who writes what:
+// * Interleave: the slice's vectors (lo_vec = start_vec, span = nvec). When
+//   the slice covers only part of its first or last 128-byte line, every
+//   vector of those lines instead: each line is then requested whole by one
+//   wave instruction, which the L2 serves much faster than two half-line
+//   requests (it fetches the whole line either way); the vectors outside the
+//   slice are loaded and dropped, never stored.
+// * rotate_half, pair owner (kModeRH): the threads cover the first half;
+//   each loads vector k of both halves and stores both. In place only, for
+//   rows whose threads do not fit one wave.
+// * rotate_half, own vector (kModeRHOwn): the threads cover the whole slice
+//   (or its whole lines, as for interleave); each loads its own vector,
+//   takes its partner's (vector k of the other half) from the lane that
+//   holds it with ds_bpermute, and stores only its own vector, so each line
+//   is requested once by one load instruction and written by one store. The
+//   host runs it with single-wave blocks, so a row's threads share a wave:
+//   the partner is in reach, and in place the wave's loads have all returned
+//   before any of its stores issue, so no thread overwrites a partner's
+//   vector before it is read. kModeRHOwnLoad, out of place for rows wider
+//   than a wave, loads the partner vector from memory instead.
+// * Out of place (src another tensor), the threads cover whole rows:
+//   vectors outside the slice are copied from src to x, and every thread
+//   stores exactly the vector it covers, with one instruction.
+//
+// The cos/sin units of a thread are loaded once per tile and, when the
+// tables broadcast over heads, reused for all its heads. All loads of a tile
+// are issued before any arithmetic. The grid normally has one block per
+// group of GL tiles; a smaller grid makes the blocks stride over the groups.
 // ---------------------------------------------------------------------------
 // x is streamed (each slice byte is read once and written once); the tables
 // are re-read by every head and stay in the caches. NT selects nontemporal
@@ -307,16 +352,31 @@ __device__ __forceinline__ uint32_t xcd_grouped_block(uint32_t bid, const VecArg
     return w * a.xcd_div.d + (l & 7u) * a.xcd_group + (l >> 3);
 }
 
+// The 16-byte vector that the lane at byte address `lane4` (lane * 4) of the
+// wave holds, through the LDS crossbar (ds_bpermute; no LDS is allocated).
+__device__ __forceinline__ v4u lane_exchange(const v4u& v, int lane4)
+{
+    v4u r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(lane4, (int)v[i]);
+    return r;
+}
+
 // The kernel body for one tensor: `bid` is the block's number among the G
 // blocks that work on this tensor. OUT: read a.src and write a.x (out of
-// place, whole rows); otherwise read and write a.x.
+// place); otherwise read and write a.x.
 template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT, bool OUT>
 __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_t G)
 {
-    const v4u* src = OUT ? a.src : a.x;
+    static_assert(!OUT || MODE != kModeRH, "out of place, rotate_half takes the own-vector scheme");
     constexpr int K = Store<DT>::kLanes;
     using TVec = typename TableLanes<TT, K>::Vec;
     constexpr int TV = TableLanes<TT, K>::kVecs;      // table units per x vector
+    static_assert(OUT || MODE != kModeRHOwnLoad, "in place, the own-vector scheme exchanges within the wave");
+    constexpr bool kPair = MODE == kModeRH;           // rotate_half, pair owner
+    constexpr bool kOwn = MODE == kModeRHOwn || MODE == kModeRHOwnLoad;   // rotate_half, own vector
+    constexpr bool kXchg = MODE == kModeRHOwn;        // the partner vector from its lane
+    const v4u* src = OUT ? a.src : a.x;
     const TVec* r1 = static_cast<const TVec*>(a.r1);
     const TVec* r2 = static_cast<const TVec*>(a.r2);
     constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
@@ -326,22 +386,28 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
     const uint32_t gl = fast_div(q, a.hl_div);
     const uint32_t hl = q - gl * a.HL;
     const uint32_t c = a.lo_vec + vs;                 // vector within the row
-    const bool in_unit = c >= a.start_vec && c - a.start_vec < a.nvec;
-    // Out of place, every thread stores exactly the vector it covers, in one
-    // instruction. For rotate_half the threads of the slice's second half
-    // therefore rotate too: each loads the matching vector of the other half
-    // as its partner (xa = first-half vector, xb = second-half vector) and
-    // keeps its own component. In place, the first-half threads store both.
-    const bool second_half =
-        OUT && MODE == kModeRH && c >= a.start_vec + a.nvec && c - a.start_vec - a.nvec < a.nvec;
-    const bool in_slice = in_unit || second_half;
-    const uint32_t v = in_unit ? c - a.start_vec : second_half ? c - a.start_vec - a.nvec : 0;  // unit (table index)
-    const uint32_t back = second_half ? a.half_vecs : 0;             // xa = own vector - back
-    const uint32_t ahead = !OUT || in_unit ? a.half_vecs : 0;        // xb = own vector + ahead
+    // nvec is the slice's vectors (interleave) or one half's (rotate_half)
+    const bool first = c >= a.start_vec && c - a.start_vec < a.nvec;
+    const bool second = kOwn && c >= a.start_vec + a.nvec && c - a.start_vec - a.nvec < a.nvec;
+    const bool in_slice = first || second;
+    const uint32_t v = first ? c - a.start_vec : second ? c - a.start_vec - a.nvec : 0;  // unit (table index)
+    // Own vector: the partner vector in the other half (outside the slice,
+    // the thread's own again), and the table units of the thread's lanes
+    // (cos; sin forward) and of the partner's lanes (sin backward).
+    const uint32_t partner = first ? c + a.half_vecs : second ? c - a.half_vecs : c;
+    const uint32_t t_own = second ? a.thalf : 0;
+    const uint32_t t_sin = DIR == kBwd ? (first ? a.thalf : 0) : t_own;
+    // Own vector: the partner term is subtracted on the first half forward
+    // and on the second half backward.
+    const bool neg = DIR == kFwd ? first : second;
+    // Own vector, exchange: the byte address of the partner's lane for
+    // ds_bpermute (the block is one wave, so the lane is t; the partner is
+    // +-half_vecs lanes away in the same row, or the lane itself).
+    const int xlane = kXchg ? (int)(t + (partner - c)) * 4 : 0;
     if (gl >= a.GL) return;  // no barriers below, so idle threads may leave
 
-    const uint32_t first = xcd_grouped_block(bid, a);
-    for (uint32_t bt = first; bt < a.btiles; bt += G) {
+    const uint32_t first_bt = xcd_grouped_block(bid, a);
+    for (uint32_t bt = first_bt; bt < a.btiles; bt += G) {
         const uint32_t tile = bt * a.GL + gl;
         if (tile >= a.tiles) continue;
         const uint32_t g = fast_div(tile, a.nchunk_div);  // (b,s) position
@@ -349,8 +415,8 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
         const uint32_t b = fast_div(g, a.s_div);
         const uint32_t s = g - b * a.s_div.d;
         const uint32_t n0 = chunk * (a.HL * U) + hl;
-        const uint32_t c_base = b * a.t1b + s * a.t1s + v * TV;
-        const uint32_t s_base = b * a.t2b + s * a.t2s + v * TV;
+        const uint32_t c_base = b * a.t1b + s * a.t1s + v * TV + (kOwn ? t_own : 0);
+        const uint32_t s_base = b * a.t2b + s * a.t2s + v * TV + (kOwn ? t_sin : 0);
         const uint32_t row0 = g * a.N;
 
         // All loads are issued back to back with no branch between them: a
@@ -365,7 +431,7 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
             for (int u = 0; u < TV; ++u) {
                 ca[0][u] = r1[c_base + u];
                 sa[0][u] = r2[s_base + u];
-                if constexpr (MODE == kModeRH) {
+                if constexpr (kPair) {
                     cb[0][u] = r1[c_base + a.thalf + u];
                     sb[0][u] = r2[s_base + a.thalf + u];
                 }
@@ -376,29 +442,33 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
             const uint32_t n = n0 + (uint32_t)k * a.HL;
             live[k] = n < a.N;
             const uint32_t nl = live[k] ? n : a.N - 1;
-            off[k] = (row0 + nl) * a.row_vecs + c;
+            const uint32_t row = (row0 + nl) * a.row_vecs;   // the row's first vector
+            off[k] = row + c;
             if constexpr (!HEADS_SHARE_TABLES) {
 #pragma unroll
                 for (int u = 0; u < TV; ++u) {
                     ca[k][u] = r1[c_base + nl * a.t1n + u];
                     sa[k][u] = r2[s_base + nl * a.t2n + u];
-                    if constexpr (MODE == kModeRH) {
+                    if constexpr (kPair) {
                         cb[k][u] = r1[c_base + nl * a.t1n + a.thalf + u];
                         sb[k][u] = r2[s_base + nl * a.t2n + a.thalf + u];
                     }
                 }
             }
-            if constexpr (MODE == kModeRH) {
-                xa[k] = load_x<NT>(src + off[k] - back);
-                xb[k] = load_x<NT>(src + off[k] + ahead);
-            } else {
-                xa[k] = load_x<NT>(src + off[k]);
-            }
+            xa[k] = load_x<NT>(src + off[k]);
+            if constexpr (kPair) xb[k] = load_x<NT>(src + off[k] + a.half_vecs);
+            if constexpr (kOwn && !kXchg) xb[k] = load_x<NT>(src + row + partner);
         }
         // Keep every load above in flight together: without this barrier the
         // machine scheduler starts the arithmetic on the first vectors and
         // issues the remaining loads only after waiting for them.
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kXchg) {
+            // every lane of the row takes part (no branch has been taken on
+            // the lane's own position yet)
+#pragma unroll
+            for (int k = 0; k < U; ++k) xb[k] = lane_exchange(xa[k], xlane);
+        }
 
 #pragma unroll
         for (int k = 0; k < U; ++k) {
@@ -420,7 +490,7 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
 #pragma unroll
                     for (int i = 0; i < K; i += 2)
                         rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C.v[i], S.v[i], C.v[i + 1], S.v[i + 1]);
-                } else {
+                } else if constexpr (kPair) {
                     Lanes<DT> X2;
                     TableLanes<TT, K> C2, S2;
                     X2.unpack(xb[k]);
@@ -430,15 +500,16 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
                     for (int i = 0; i < K; ++i)
                         rotate_pair<DIR, kUnfused>(X.v[i], X2.v[i], C.v[i], S.v[i], C2.v[i], S2.v[i]);
                     yb = X2.pack();
+                } else {
+                    Lanes<DT> P;
+                    P.unpack(xb[k]);
+#pragma unroll
+                    for (int i = 0; i < K; ++i) X.v[i] = rotate_own<kUnfused>(X.v[i], P.v[i], C.v[i], S.v[i], neg);
                 }
                 ya = X.pack();
             }
-            if constexpr (OUT) {
-                store_x<NT>(a.x + off[k], second_half ? yb : ya);
-            } else {
-                store_x<NT>(a.x + off[k], ya);
-                if constexpr (MODE == kModeRH) store_x<NT>(a.x + off[k] + a.half_vecs, yb);
-            }
+            store_x<NT>(a.x + off[k], ya);
+            if constexpr (kPair) store_x<NT>(a.x + off[k] + a.half_vecs, yb);
         }
     }
 }
@@ -612,6 +683,7 @@ constexpr int kUOut = 2;
 
 // Launch shape of the vector kernel.
 struct VecConfig {
+    int kmode = kModeIL;  // kernel scheme: kModeIL, kModeRH (pair owner) or kModeRHOwn
     int U = 1;          // heads per thread per tile (kUInPlace or kUOut)
     uint32_t HL = 1;    // head lanes per tile
     uint32_t GL = 1;    // tiles per block iteration
@@ -669,10 +741,10 @@ bool vec_geometry(const Plan& p, VecArgs* a)
     return a->nvec >= 1 && a->nvec <= 256;
 }
 
-// Interleave slices that cover only part of their first or last 128-byte
-// line: let the threads of a row cover the whole lines around the slice
-// (see the vector kernel). Needs rows that start on line boundaries so the
-// lines stay inside the row. Measured on MI355X for bf16 lanes [32,96) of
+// Slices that cover only part of their first or last 128-byte line
+// (interleave, and rotate_half in the own-vector scheme): let the threads of
+// a row cover the whole lines around the slice (see the vector kernel).
+// Needs rows that start on line boundaries so the lines stay inside the row. Measured on MI355X for bf16 lanes [32,96) of
 // 128 (same HBM bytes either way): 3-4% faster in this kernel, and 15% in a
 // bare read-modify-write of the same bytes.
 void cover_whole_lines(const Plan& p, VecArgs* a)
@@ -680,7 +752,6 @@ void cover_whole_lines(const Plan& p, VecArgs* a)
     const int64_t es = p.esize;
     const int64_t lo = (p.start * es) / 128 * 128;
     const int64_t hi = ((p.start + p.L) * es + 127) / 128 * 128;
-    if (p.mode != kModeIL) return;
     if (lo == p.start * es && hi == (p.start + p.L) * es) return;   // whole lines already
     if ((p.D * es) % 128 || (reinterpret_cast<uintptr_t>(p.x) & 127u)) return;
     if ((hi - lo) / 16 > 256) return;
@@ -721,9 +792,10 @@ VecConfig shape_for(const VecArgs& a, int U, uint32_t threads)
 // long-context shard (16,8192,32,128) with lanes [32,96).
 constexpr uint64_t kXcdRunBytes = 384u << 10;
 
-VecConfig choose_vec_config(const Plan& p, const VecArgs& a, int U)
+VecConfig choose_vec_config(const Plan& p, const VecArgs& a, int U, int kmode)
 {
     VecConfig c = shape_for(a, U, 64);
+    c.kmode = kmode;
     c.nt = true;
     const uint64_t heads_per_tile = (uint64_t)c.HL * c.U;
     const uint64_t blocks_per_position = c.GL == 1 ? (a.N + heads_per_tile - 1) / heads_per_tile : 1;
@@ -793,9 +865,16 @@ const void* vec_kernel_ptr(VecKind kind)
 {
     switch (kind) {
     case kVecMulti:
-        return reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, TT, DIR, MODE, kUInPlace, SHARE, true>);
-    case kVecOut: return reinterpret_cast<const void*>(&rope_vec_out_kernel<DT, TT, DIR, MODE, kUOut, SHARE, true>);
-    default: return reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, kUInPlace, SHARE, true>);
+        // in place: no memory partner loads
+        if constexpr (MODE == kModeRHOwnLoad) return nullptr;
+        else return reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, TT, DIR, MODE, kUInPlace, SHARE, true>);
+    case kVecOut:
+        // out of place, rotate_half always takes an own-vector scheme
+        if constexpr (MODE == kModeRH) return nullptr;
+        else return reinterpret_cast<const void*>(&rope_vec_out_kernel<DT, TT, DIR, MODE, kUOut, SHARE, true>);
+    default:
+        if constexpr (MODE == kModeRHOwnLoad) return nullptr;
+        else return reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, kUInPlace, SHARE, true>);
     }
 }
 
@@ -805,32 +884,40 @@ const void* vec_kernel_s(bool share, VecKind kind)
     return share ? vec_kernel_ptr<DT, TT, DIR, MODE, true>(kind) : vec_kernel_ptr<DT, TT, DIR, MODE, false>(kind);
 }
 
-template <int DT, int TT>
-const void* vec_kernel_t(int dir, int mode, bool share, VecKind kind)
+template <int DT, int TT, int DIR>
+const void* vec_kernel_m(int kmode, bool share, VecKind kind)
 {
-    if (dir == kFwd)
-        return mode == kModeIL ? vec_kernel_s<DT, TT, kFwd, kModeIL>(share, kind)
-                               : vec_kernel_s<DT, TT, kFwd, kModeRH>(share, kind);
-    return mode == kModeIL ? vec_kernel_s<DT, TT, kBwd, kModeIL>(share, kind)
-                           : vec_kernel_s<DT, TT, kBwd, kModeRH>(share, kind);
+    switch (kmode) {
+    case kModeIL: return vec_kernel_s<DT, TT, DIR, kModeIL>(share, kind);
+    case kModeRH: return vec_kernel_s<DT, TT, DIR, kModeRH>(share, kind);
+    case kModeRHOwn: return vec_kernel_s<DT, TT, DIR, kModeRHOwn>(share, kind);
+    default: return vec_kernel_s<DT, TT, DIR, kModeRHOwnLoad>(share, kind);
+    }
 }
 
-// The vector kernel instance for a plan that vec_geometry accepted.
-const void* vec_kernel(const Plan& p, VecKind kind)
+template <int DT, int TT>
+const void* vec_kernel_t(int dir, int kmode, bool share, VecKind kind)
+{
+    return dir == kFwd ? vec_kernel_m<DT, TT, kFwd>(kmode, share, kind) : vec_kernel_m<DT, TT, kBwd>(kmode, share, kind);
+}
+
+// The vector kernel instance for a plan that vec_geometry accepted, in the
+// scheme `kmode` (VecConfig::kmode).
+const void* vec_kernel(const Plan& p, int kmode, VecKind kind)
 {
     const bool share = p.t1[2] == 0 && p.t2[2] == 0;
     const int tt = p.tdtype;
     switch (p.dtype) {
     case ROPE_DTYPE_F32:
-        if (tt == ROPE_DTYPE_F16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F16>(p.dir, p.mode, share, kind);
-        if (tt == ROPE_DTYPE_BF16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_BF16>(p.dir, p.mode, share, kind);
-        return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F32>(p.dir, p.mode, share, kind);
+        if (tt == ROPE_DTYPE_F16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F16>(p.dir, kmode, share, kind);
+        if (tt == ROPE_DTYPE_BF16) return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_BF16>(p.dir, kmode, share, kind);
+        return vec_kernel_t<ROPE_DTYPE_F32, ROPE_DTYPE_F32>(p.dir, kmode, share, kind);
     case ROPE_DTYPE_F16:
-        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F32>(p.dir, p.mode, share, kind)
-                                    : vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F16>(p.dir, p.mode, share, kind);
+        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F32>(p.dir, kmode, share, kind)
+                                    : vec_kernel_t<ROPE_DTYPE_F16, ROPE_DTYPE_F16>(p.dir, kmode, share, kind);
     default:
-        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_F32>(p.dir, p.mode, share, kind)
-                                    : vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_BF16>(p.dir, p.mode, share, kind);
+        return tt == ROPE_DTYPE_F32 ? vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_F32>(p.dir, kmode, share, kind)
+                                    : vec_kernel_t<ROPE_DTYPE_BF16, ROPE_DTYPE_BF16>(p.dir, kmode, share, kind);
     }
 }
 
@@ -839,9 +926,10 @@ const void* vec_kernel(const Plan& p, VecKind kind)
 hipError_t launch_vec(const Plan& p, const VecArgs& a, const VecConfig& cfg, hipStream_t stream)
 {
     const uint32_t threads = a.span * a.HL * a.GL;
+    const void* fn = vec_kernel(p, cfg.kmode, a.src ? kVecOut : kVecOne);
+    if (fn == nullptr) return hipErrorInvalidDeviceFunction;
     void* args[] = {const_cast<VecArgs*>(&a)};
-    return hipLaunchKernel(vec_kernel(p, a.src ? kVecOut : kVecOne), dim3(vec_grid(a, cfg)), dim3(threads), args,
-                           0, stream);
+    return hipLaunchKernel(fn, dim3(vec_grid(a, cfg)), dim3(threads), args, 0, stream);
 }
 
 template <int DT, int TT>
@@ -963,13 +1051,42 @@ struct Launch {
     RowShape rs;
 };
 
+// In place, rotate_half: the pair-owner scheme requests each half with its
+// own wave instruction, which covers whole 128-byte lines only when the
+// halves start and end on line boundaries (e.g. a whole bf16 head of 128
+// lanes). Otherwise take the own-vector scheme, whose threads cover the
+// slice's whole lines -- when a row's threads fit one wave, as that scheme
+// needs. Measured on MI355X, (16,4096,32,128) bf16 forward: lanes [64,128)
+// 113 -> 86 us (the interleave slice of the same bytes takes 85 us), lanes
+// [0,32) 95 -> 74 us. With the partner loaded from memory instead of taken
+// from its lane, each line was requested twice: 100 and 76 us.
+bool use_rh_own(const Plan& p, VecArgs* a)
+{
+    const int64_t es = p.esize;
+    const int64_t half_bytes = (p.L / 2) * es;
+    if ((p.start * es) % 128 == 0 && half_bytes % 128 == 0) return false;   // halves on whole lines
+    VecArgs own = *a;
+    own.span = 2 * own.nvec;   // the whole slice
+    cover_whole_lines(p, &own);
+    if (own.span > 64) return false;   // a row's threads would span waves
+    *a = own;
+    return true;
+}
+
 void prepare(Launch* L)
 {
     L->vec = vec_geometry(L->p, &L->a);
     if (L->vec) {
-        cover_whole_lines(L->p, &L->a);
-        L->cfg = choose_vec_config(L->p, L->a, kUInPlace);
+        int kmode = L->p.mode;
+        if (L->p.mode == kModeRH) {
+            if (use_rh_own(L->p, &L->a)) kmode = kModeRHOwn;
+        } else {
+            cover_whole_lines(L->p, &L->a);
+        }
+        L->cfg = choose_vec_config(L->p, L->a, kUInPlace, kmode);
         L->vec = finish_vec_args(L->p, L->cfg, &L->a);
+        // the own-vector scheme in place needs single-wave blocks
+        if (L->vec && kmode == kModeRHOwn && L->a.span * L->a.HL * L->a.GL > 64) L->vec = false;
     }
     if (!L->vec) L->rows = rows_shape(L->p, &L->rs);
 }
@@ -1003,8 +1120,12 @@ void prepare_out(Launch* L)
         L->a.src = static_cast<const v4u*>(L->p.src);
         L->a.lo_vec = 0;
         L->a.span = L->a.row_vecs;
-        L->cfg = choose_vec_config(L->p, L->a, kUOut);
+        // rotate_half: the partner vector from its lane when a row fits a wave
+        const int kmode = L->p.mode == kModeIL ? kModeIL : L->a.span <= 64 ? kModeRHOwn : kModeRHOwnLoad;
+        L->cfg = choose_vec_config(L->p, L->a, kUOut, kmode);
         L->vec = finish_vec_args(L->p, L->cfg, &L->a);
+        // the lane exchange needs single-wave blocks
+        if (L->vec && kmode == kModeRHOwn && L->a.span * L->a.HL * L->a.GL > 64) L->vec = false;
     }
     if (!L->vec) L->rows = rows_shape(L->p, &L->rs);
 }
@@ -1109,10 +1230,10 @@ rope_status_t run_multi(int32_t count, void* const xs[], const int64_t (*x_shape
 
     bool together = live > 1;
     const uint32_t threads = L[0].a.span * L[0].a.HL * L[0].a.GL;
-    const void* fn = together && L[0].vec ? vec_kernel(L[0].p, kVecMulti) : nullptr;
+    const void* fn = together && L[0].vec ? vec_kernel(L[0].p, L[0].cfg.kmode, kVecMulti) : nullptr;
     for (int i = 0; i < live && together; ++i) {
         together = L[i].vec && L[i].a.span * L[i].a.HL * L[i].a.GL == threads &&
-                   vec_kernel(L[i].p, kVecMulti) == fn && L[i].cfg.grid == 0;
+                   vec_kernel(L[i].p, L[i].cfg.kmode, kVecMulti) == fn && L[i].cfg.grid == 0;
     }
     hipError_t err = hipSuccess;
     if (together) {
