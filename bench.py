@@ -40,8 +40,15 @@ TRAFFIC_MD = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] of the kernel source with its comments and spacing
+    removed: editing a comment keeps the committed counters valid, changing
+    code makes them stale."""
+    with open(KERNEL_SRC, encoding="utf-8") as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def committed_traffic(workload: str, direction: str):

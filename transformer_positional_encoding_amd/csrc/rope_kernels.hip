@@ -1,4 +1,5 @@
-// In-place partial rotary position embedding for MI355X (gfx950, CDNA4).
+// Partial rotary position embedding for MI355X (gfx950, CDNA4), in place
+// and out of place.
 //
 // Operation: "CANN ops-transformer 算子详解：inplace_partial_rotary_mul
 // 原地部分旋转位置编码", section 功能与计算公式 (interleave pairs (2i,2i+1),
@@ -15,11 +16,13 @@
 // of 16-bit lanes is one 32-bit word; a pair of fp32 lanes is 8 bytes), does
 // the swap and sign in registers, computes in fp32 (one fp32 rounding, exact
 // products for 16-bit data) and stores only the slice's 16-byte vectors, so
-// lanes outside [start,end) are never written. The path is HBM-bound
-// (0.375-0.75 flop per byte), so there is no MFMA and no LDS: a block takes
-// a chunk of heads of one (b,s) position, the blocks of a position run on
-// one XCD, and when the tables broadcast over heads its cos/sin rows are
-// fetched from HBM once and served by that XCD's L2 to every head.
+// lanes outside [start,end) are never written (in place). The path is
+// HBM-bound (0.375-0.75 flop per byte), so there is no MFMA and nothing is
+// staged in LDS (rotate_half partners may move between lanes through the LDS
+// crossbar, ds_bpermute): a block takes a chunk of heads of one (b,s)
+// position, the blocks of a position run on one XCD, and when the tables
+// broadcast over heads its cos/sin rows are fetched from HBM once and served
+// by that XCD's L2 to every head.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
