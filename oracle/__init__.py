@@ -31,20 +31,23 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rope_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "librope_oracle.so")
+_DEFAULT_LIB_PATH = os.path.join(_HERE, "librope_oracle.so")
+# ROPE_ORACLE_LIB points the pins at another build of the oracle (the
+# planted-mistake test runs them against deliberately broken copies).
+_LIB_PATH = os.environ.get("ROPE_ORACLE_LIB") or _DEFAULT_LIB_PATH
 
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 MODES = {"rotate_half": 0, "interleave": 1}
 DIRECTIONS = {"fwd": 0, "bwd": 1}
 
-GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99",
-           "-fPIC", "-shared", _SRC, "-o", _LIB_PATH, "-lm"]
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99", "-fPIC", "-shared"]
+GCC_CMD = ["gcc"] + GCC_FLAGS + [_SRC, "-o", _DEFAULT_LIB_PATH, "-lm"]
 
 
 def build() -> str:
     """Compile the oracle library with gcc; returns its path."""
     subprocess.run(GCC_CMD, check=True)
-    return _LIB_PATH
+    return _DEFAULT_LIB_PATH
 
 
 _lib = None
@@ -54,6 +57,8 @@ def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
+            if _LIB_PATH != _DEFAULT_LIB_PATH:
+                raise FileNotFoundError(_LIB_PATH)
             build()
         L = ctypes.CDLL(_LIB_PATH)
         i64p = ctypes.POINTER(ctypes.c_int64)
