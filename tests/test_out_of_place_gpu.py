@@ -276,3 +276,24 @@ def test_backward_leaves_a_shared_gradient_alone():
     torch.cuda.synchronize()
     assert torch.equal(_bits(other.grad), _bits(w.to(DEV)))
     assert torch.equal(_bits(xd.grad.cpu()), _bits(_oracle(w, r1, r2, mode, sl, "bwd")))
+
+
+def test_out_of_place_op_on_a_non_contiguous_input():
+    """A transposed view: the op rotates a private contiguous copy, x is left
+    alone, and the gradient reaches the view's base."""
+    announce("partial_rotary_mul on a non-contiguous view")
+    shape, sl, mode = (2, 8, 4, 64), (0, 64), "interleave"
+    base = _rand((2, 4, 8, 64), "bf16", 141)
+    r1, r2 = _rand((1, 8, 1, 64), "bf16", 142), _rand((1, 8, 1, 64), "bf16", 143)
+    w = _rand(shape, "bf16", 144)
+    bd = base.to(DEV).requires_grad_(True)
+    xv = bd.transpose(1, 2)                     # (2, 8, 4, 64), not contiguous
+    assert not xv.is_contiguous()
+    y = rp.partial_rotary_mul(xv, r1.to(DEV), r2.to(DEV), mode, sl)
+    y.backward(w.to(DEV))
+    torch.cuda.synchronize()
+    x = base.transpose(1, 2).contiguous()
+    assert torch.equal(_bits(y.detach().cpu()), _bits(_oracle(x, r1, r2, mode, sl, "fwd")))
+    assert torch.equal(_bits(bd.detach().cpu()), _bits(base))
+    want_g = _oracle(w, r1, r2, mode, sl, "bwd").transpose(1, 2)
+    assert torch.equal(_bits(bd.grad.cpu()), _bits(want_g))

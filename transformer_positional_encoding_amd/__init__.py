@@ -442,15 +442,27 @@ def _grad_x(grad, r1, r2, rotary_mode, partial_slice):
     return dx
 
 
+def _rotated_copy(x, r1, r2, rotary_mode, partial_slice):
+    """A new contiguous tensor holding x with its slice rotated. A
+    non-contiguous x is first made into a private contiguous copy, which is
+    then rotated in place (one pass less than copying it again)."""
+    import torch
+    xc = x.contiguous()
+    if xc.numel() and xc.data_ptr() != x.data_ptr():
+        rope_partial_fwd_inplace(xc, r1, r2, rotary_mode, partial_slice)
+        return xc
+    y = torch.empty_like(xc, memory_format=torch.contiguous_format)
+    rope_partial_fwd_out(y, xc, r1, r2, rotary_mode, partial_slice)
+    return y
+
+
 def _out_of_place_function():
     import torch
 
     class PartialRotaryMulFn(torch.autograd.Function):
         @staticmethod
         def forward(ctx, x, r1, r2, rotary_mode, partial_slice):
-            xc = x.contiguous()
-            y = torch.empty_like(xc, memory_format=torch.contiguous_format)
-            rope_partial_fwd_out(y, xc, r1, r2, rotary_mode, partial_slice)
+            y = _rotated_copy(x, r1, r2, rotary_mode, partial_slice)
             ctx.save_for_backward(r1, r2)
             ctx.rotary_mode = rotary_mode
             ctx.partial_slice = None if partial_slice is None else tuple(int(v) for v in partial_slice)
@@ -502,7 +514,4 @@ def partial_rotary_mul(x, r1, r2, rotary_mode="interleave", partial_slice=None):
         if _FN_OUT is None:
             _FN_OUT = _out_of_place_function()
         return _FN_OUT.apply(x, r1, r2, rotary_mode, partial_slice)
-    xc = x.contiguous()
-    y = torch.empty_like(xc, memory_format=torch.contiguous_format)
-    rope_partial_fwd_out(y, xc, r1, r2, rotary_mode, partial_slice)
-    return y
+    return _rotated_copy(x, r1, r2, rotary_mode, partial_slice)
