@@ -99,6 +99,17 @@ def test_c4_long_context_full_size(name, direction):
         assert info["exact"] == info["n"]
 
 
+@pytest.mark.parametrize("name", ["c2_s4096", "rh_64of128", "rh_32of128"])
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_rotate_half_layouts_full_size(name, direction):
+    """rotate_half from HBM: a whole head (pair-owner scheme) and two partial
+    slices with 64- and 32-byte halves (own-vector scheme, lane exchange)."""
+    w, x, r1, r2 = _workload_inputs(name)
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"{name} {direction}",
+                         sample=3000, seed=12)
+    assert info["exact"] == info["n"]
+
+
 # ---------------------------------------------------------------- more shapes and layouts
 
 @pytest.mark.parametrize("direction", ["fwd", "bwd"])

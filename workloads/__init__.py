@@ -116,6 +116,18 @@ WORKLOADS["c4_f32"] = replace(WORKLOADS["c4"], name="c4_f32", dtype="f32",
 # The page's mixed-precision case at the long-context shape: bf16 dx, fp32 tables.
 WORKLOADS["c4_t32"] = replace(WORKLOADS["c4"], name="c4_t32", table_dtype="f32",
                               note="long-context shard, bf16 dx with fp32 tables")
+# rotate_half layouts measured from HBM (c2 itself fits the 256 MB cache):
+# the GQA Q layout of c2 at 4096 positions (whole head, halves of whole
+# 128-byte lines), and partial slices whose halves are 64 and 32 bytes.
+WORKLOADS["c2_s4096"] = W("c2_s4096", ((32, 4096, 16, 128),), "bf16", (0, 128), "rotate_half",
+                          (1, 4096, 1, 128), seed=12, directions=("fwd", "bwd"),
+                          note="GQA Q layout (16 heads, HD 128) at 4096 positions, rotate_half, bf16")
+WORKLOADS["rh_64of128"] = W("rh_64of128", ((16, 4096, 32, 128),), "bf16", (64, 128), "rotate_half",
+                            (1, 4096, 1, 64), seed=13, directions=("fwd", "bwd"),
+                            note="rotate_half on lanes [64,128) of 128, bf16")
+WORKLOADS["rh_32of128"] = W("rh_32of128", ((16, 4096, 40, 128),), "bf16", (0, 32), "rotate_half",
+                            (1, 4096, 1, 32), seed=14, directions=("fwd", "bwd"),
+                            note="rotate_half on lanes [0,32) of 128, 40 heads, bf16")
 
 
 def generator(seed: int) -> torch.Generator:
