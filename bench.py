@@ -216,13 +216,17 @@ def bench_workload(name: str, steps: int, warmup: int, reps: int, stream, want_c
     step_s = ev0.elapsed_time(ev1) / 1e3 / steps
     # per-kernel average launch durations: rotating copies (data from HBM),
     # and back to back on one buffer (what caches keep of it is reused)
+    # Two rounds over the directions, the second kept: the first launches
+    # after a workload's data is generated read a few percent slow, and the
+    # first direction timed would otherwise take all of that.
     per_launch, warm = {}, {}
-    for d in dirs:
-        fn = launch_fn(d)
-        cold = [(fn, (xs[i], r1d, r2d, w.mode, w.partial_slice)) for i in range(ncopy)]
-        time_launches(cold, max(4, reps // 4), stream)  # untimed: settle clocks after the host gap
-        per_launch[d] = time_launches(cold, reps, stream)
-        warm[d] = time_launches(cold[:1], reps, stream)
+    for _ in range(2):
+        for d in dirs:
+            fn = launch_fn(d)
+            cold = [(fn, (xs[i], r1d, r2d, w.mode, w.partial_slice)) for i in range(ncopy)]
+            time_launches(cold, max(10, reps // 2), stream)  # untimed: settle clocks after the host gap
+            per_launch[d] = time_launches(cold, reps, stream)
+            warm[d] = time_launches(cold[:1], reps, stream)
     bytes_launch = w.algorithmic_bytes()
     elems_launch = w.rotated_elements()
     out = {
@@ -412,7 +416,7 @@ def main() -> int:
         if len(W.WORKLOADS[name].x_shapes) > 1:
             others.append(bench_multi(name, max(10, args.reps // 2), stream))
             continue
-        r = bench_workload(name, max(5, args.steps // 5), 2, max(10, args.reps // 2), stream, False, 0)
+        r = bench_workload(name, max(5, args.steps // 5), 10, max(10, args.reps // 2), stream, False, 0)
         others.append({k: r[k] for k in ("workload", "note", "dtype", "directions", "rotating_copies",
                                          "bytes_per_launch", "elements_per_launch", "kernels")})
 

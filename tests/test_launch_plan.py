@@ -190,3 +190,7 @@ def test_rotate_half_own_vector_needs_single_wave_rows():
     for dtype, span in ((BF16, 62), (F32, 124)):
         st, info = plan((1, 3, 5, 1024), dtype, (8, 1000), mode=RH)
         assert st == OK and info["kernel"] == "vector" and info["row_vectors"] == span
+    # lanes [8,520) bf16: the slice's whole lines would take 72 threads, the
+    # slice itself 64, so the own-vector scheme runs over the slice alone
+    st, info = plan((1, 3, 5, 1024), BF16, (8, 520), mode=RH)
+    assert st == OK and info["row_vectors"] == 64 and info["threads"] == 64

@@ -149,6 +149,7 @@ CASES = [
     ((2, 8, 4, 128), (32, 96), "rotate_half", (2, 8, 4, 64)),     # own vector over two lines, per-head tables
     ((3, 5, 13, 128), (0, 32), "rotate_half", (1, 5, 1, 32)),     # NeoX-style rotary_dim 32: own vector, whole line
     ((1, 3, 5, 1024), (8, 1000), "rotate_half", (1, 3, 1, 992)),  # rows wider than a wave: pair owner
+    ((1, 3, 5, 1024), (8, 520), "rotate_half", (1, 3, 1, 512)),   # bf16: own vector over the slice, not its lines
 ]
 
 

@@ -1071,6 +1071,10 @@ bool use_rh_own(const Plan& p, VecArgs* a)
     VecArgs own = *a;
     own.span = 2 * own.nvec;   // the whole slice
     cover_whole_lines(p, &own);
+    if (own.span > 64) {       // the whole lines would not fit one wave: the slice alone may
+        own.lo_vec = own.start_vec;
+        own.span = 2 * own.nvec;
+    }
     if (own.span > 64) return false;   // a row's threads would span waves
     *a = own;
     return true;
