@@ -1,0 +1,101 @@
+"""Concurrent use of the library on one GPU: host threads, each with its own
+stream, launch in-place, out-of-place and multi-tensor calls on their own
+tensors at the same time, and every result matches the oracle. The library's
+only shared state (the per-device compute-unit count) and its per-thread
+error text must hold up under this; the calls themselves share nothing."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import transformer_positional_encoding_amd as rp
+import workloads as W
+from gpu_support import announce, oracle_rows
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _rand(shape, dtype, g):
+    return torch.randn(shape, generator=g).to(DT[dtype])
+
+
+def _want(x, r1, r2, mode, sl, direction):
+    D = x.shape[-1]
+    dt = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}[x.dtype]
+    return oracle_rows(W.to_numpy_storage(x).reshape(-1, D).copy(), x.shape, dt, r1, r2, mode, sl, direction,
+                       None).reshape(tuple(x.shape))
+
+
+JOBS = [
+    # (dtype, shape, slice, mode, table shape, form)
+    ("bf16", (4, 64, 8, 128), (32, 96), "interleave", (4, 64, 1, 64), "inplace"),
+    ("f16", (2, 64, 12, 64), (0, 64), "interleave", (1, 64, 1, 64), "out"),
+    ("bf16", (4, 64, 8, 128), (64, 128), "rotate_half", (1, 64, 1, 64), "inplace"),
+    ("f32", (2, 32, 6, 128), (0, 128), "rotate_half", (1, 32, 1, 128), "out"),
+    ("bf16", (2, 64, 16, 128), (0, 128), "rotate_half", (1, 64, 1, 128), "multi"),
+    ("f16", (2, 48, 5, 96), (3, 35), "interleave", (1, 48, 1, 32), "inplace"),   # general (row) kernel
+]
+
+
+def test_threads_on_their_own_streams():
+    announce("concurrent calls from 6 threads on 6 streams")
+    reps = 20
+    failures = []
+    start = threading.Barrier(len(JOBS))
+
+    def worker(k, job):
+        dtype, shape, sl, mode, tshape, form = job
+        try:
+            g = torch.Generator().manual_seed(500 + k)
+            x = _rand(shape, dtype, g)
+            r1, r2 = _rand(tshape, dtype, g), _rand(tshape, dtype, g)
+            x2 = _rand((shape[0], shape[1], max(1, shape[2] // 4), shape[3]), dtype, g)
+            stream = torch.cuda.Stream()   # default priority
+            with torch.cuda.stream(stream):
+                r1d, r2d = r1.to(DEV), r2.to(DEV)
+                start.wait()
+                for rep in range(reps):
+                    direction = "fwd" if rep % 2 == 0 else "bwd"
+                    if form == "inplace":
+                        xd = x.to(DEV)
+                        (rp.rope_partial_fwd_inplace if direction == "fwd" else rp.rope_partial_bwd_inplace)(
+                            xd, r1d, r2d, mode, sl)
+                        outs = [(xd, x)]
+                    elif form == "out":
+                        xd = x.to(DEV)
+                        y = torch.empty_like(xd)
+                        (rp.rope_partial_fwd_out if direction == "fwd" else rp.rope_partial_bwd_out)(
+                            y, xd, r1d, r2d, mode, sl)
+                        outs = [(y, x)]
+                    else:
+                        xs = [x.to(DEV), x2.to(DEV)]
+                        (rp.rope_partial_fwd_inplace_multi if direction == "fwd"
+                         else rp.rope_partial_bwd_inplace_multi)(xs, r1d, r2d, mode, sl)
+                        outs = [(xs[0], x), (xs[1], x2)]
+                    # a failing call on this thread in between: its own error text
+                    with pytest.raises(rp.RopeError, match="partial_slice end must be <= D"):
+                        rp.rope_partial_fwd_inplace(outs[0][0], r1d, r2d, mode, (0, shape[3] + 2))
+                    stream.synchronize()
+                    if rep < 2:   # check the results of both directions once
+                        for got, src in outs:
+                            want = _want(src, r1, r2, mode, sl, direction)
+                            g_bits = W.to_numpy_storage(got.cpu())
+                            if dtype == "f32":
+                                ok = np.allclose(g_bits, want, rtol=0, atol=1e-5)
+                            else:
+                                ok = g_bits.tobytes() == want.tobytes()
+                            if not ok:
+                                failures.append((k, rep, form))
+        except Exception as e:   # reported below, with the job that raised it
+            failures.append((k, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(k, job)) for k, job in enumerate(JOBS)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=240)
+    assert not any(t.is_alive() for t in threads), "a worker did not finish"
+    assert not failures, failures
