@@ -78,6 +78,13 @@ def lib() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = None
             f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        L.rope_oracle_pos_tables.restype = ctypes.c_int
+        L.rope_oracle_pos_tables.argtypes = [
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+        ]
+        L.oracle_round_double_n.restype = None
+        L.oracle_round_double_n.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -167,4 +174,40 @@ def f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:
     v = np.ascontiguousarray(v, dtype=np.float32)
     out = np.empty(v.shape, np.uint16)
     lib().oracle_f32_to_bf16_n(v.ctypes.data, out.ctypes.data, v.size)
+    return out
+
+
+def pos_tables(positions: np.ndarray, inv_freq: np.ndarray, L: int, mode: str, table_dtype: str):
+    """The (cos, sin) tables of shape (Bp, S, 1, L) in storage form that the
+    position entry points compute in the kernel (see rope_oracle_pos_tables):
+    θ = p * inv_freq[i] in double precision, cos and sin in double precision,
+    rounded once to ``table_dtype``; pair i's values in lanes 2i and 2i+1
+    (interleave) or i and i + L/2 (rotate_half).
+
+    ``positions`` is a 2-D int64 array (Bp, S), any strides; ``inv_freq``
+    holds L/2 doubles."""
+    pos = np.asarray(positions)
+    if pos.dtype != np.int64 or pos.ndim != 2:
+        raise TypeError("positions must be a 2-D int64 array")
+    f = np.ascontiguousarray(inv_freq, dtype=np.float64)
+    if f.size != L // 2:
+        raise ValueError("inv_freq must hold L/2 values")
+    Bp, S = pos.shape
+    sb, ss = (st // pos.itemsize for st in pos.strides)
+    want = np.float32 if table_dtype == "f32" else np.uint16
+    c = np.empty((Bp, S, 1, L), want)
+    s_ = np.empty((Bp, S, 1, L), want)
+    rc = lib().rope_oracle_pos_tables(pos.ctypes.data, Bp, S, sb, ss, f.ctypes.data, int(L), MODES[mode],
+                                      DTYPES[table_dtype], c.ctypes.data, s_.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return c, s_
+
+
+def round_double(values: np.ndarray, dtype: str) -> np.ndarray:
+    """Doubles rounded once, to nearest even, to the values of ``dtype``
+    (returned as float32, which holds every value of the three types)."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, np.float32)
+    lib().oracle_round_double_n(v.ctypes.data, out.ctypes.data, v.size, DTYPES[dtype])
     return out

@@ -259,3 +259,81 @@ int rope_oracle_rows(void* x, const int64_t x_shape[4], int dtype,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Cos/sin tables from positions                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Round a double to the nearest value of a storage type, ties to even, in
+ * one step (rounding to binary32 first and then to 16 bits would round
+ * twice). For binary16 and bfloat16 the value is a whole number of units in
+ * the last place of its binade: ulp = 2^(e - p) for a value in
+ * [2^(e-1), 2^e) with p significand bits, and never below the least
+ * subnormal, 2^(emin - p + 1). rint() rounds the scaled value to an integer,
+ * ties to even, in the default rounding mode; scaling by powers of two is
+ * exact. Returns the rounded value as a float (exact for every value of the
+ * three types); +-inf past the largest finite value, NaN for NaN.
+ */
+static float round_to_type(double v, int dtype)
+{
+    if (dtype == ORACLE_F32) return (float)v;                 /* C's conversion rounds to nearest even */
+    if (v != v) return (float)v;                               /* NaN */
+    const int p = dtype == ORACLE_F16 ? 11 : 8;                 /* significand bits */
+    const int emin = dtype == ORACLE_F16 ? -14 : -126;          /* least normal exponent */
+    const double maxf = dtype == ORACLE_F16 ? 65504.0 : ldexp(2.0 - ldexp(1.0, -7), 127);
+    if (v == 0.0 || isinf(v)) return (float)v;
+    int e;
+    (void)frexp(v, &e);                                         /* |v| in [2^(e-1), 2^e) */
+    int q = e - p;
+    if (q < emin - p + 1) q = emin - p + 1;                     /* subnormal spacing */
+    const double r = ldexp(rint(ldexp(v, -q)), q);
+    if (fabs(r) > maxf) return v > 0 ? INFINITY : -INFINITY;
+    return (float)r;                                            /* exact: r is a value of the type */
+}
+
+/*
+ * The cos/sin tables that "ANE实战RoPE位置编码在MIL中的纯ANE实现", section
+ * 第一步, precomputes on the host, from positions and per-pair frequencies:
+ * θ = p * inv_freq[i] (the page's p / base^(2i/h), with inv_freq[i] =
+ * base^(-2i/L) supplied by the caller), evaluated as the double product of
+ * the position and the frequency; cos θ and sin θ in double precision,
+ * rounded once to the table type. Interleave writes pair i's values to lanes
+ * 2i and 2i+1, rotate_half to lanes i and i + L/2.
+ *
+ * positions  int64; the position of (b, s) is positions[b*stride_b + s*stride_s]
+ * inv_freq   L/2 doubles
+ * cos_out, sin_out   contiguous (Bp, S, 1, L) tables of table_dtype
+ * Returns 0, or -1 on an argument this oracle does not define.
+ */
+int rope_oracle_pos_tables(const int64_t* positions, int64_t Bp, int64_t S, int64_t stride_b, int64_t stride_s,
+                           const double* inv_freq, int64_t L, int mode, int table_dtype,
+                           void* cos_out, void* sin_out)
+{
+    if (L <= 0 || (L % 2) != 0 || Bp < 0 || S < 0) return -1;
+    if (mode != ORACLE_INTERLEAVE && mode != ORACLE_ROTATE_HALF) return -1;
+    if (table_dtype != ORACLE_F32 && table_dtype != ORACLE_F16 && table_dtype != ORACLE_BF16) return -1;
+    const int64_t half = L / 2;
+    for (int64_t b = 0; b < Bp; ++b) {
+        for (int64_t s = 0; s < S; ++s) {
+            const double p = (double)positions[b * stride_b + s * stride_s];
+            const int64_t row = (b * S + s) * L;
+            for (int64_t i = 0; i < half; ++i) {
+                const double theta = p * inv_freq[i];
+                const float c = round_to_type(cos(theta), table_dtype);
+                const float sn = round_to_type(sin(theta), table_dtype);
+                const int64_t j0 = mode == ORACLE_INTERLEAVE ? 2 * i : i;
+                const int64_t j1 = mode == ORACLE_INTERLEAVE ? 2 * i + 1 : i + half;
+                store_f(cos_out, row + j0, table_dtype, c);    /* exact: c is a value of the type */
+                store_f(cos_out, row + j1, table_dtype, c);
+                store_f(sin_out, row + j0, table_dtype, sn);
+                store_f(sin_out, row + j1, table_dtype, sn);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Bulk form of the one-step rounding, used by its tests. */
+void oracle_round_double_n(const double* in, float* out, int64_t n, int dtype)
+{ for (int64_t i = 0; i < n; ++i) out[i] = round_to_type(in[i], dtype); }

@@ -10,8 +10,9 @@ Table recipe (the cos/sin tables are inputs of the operation, not part of it):
 is precomputed on the host, θ = p / base^(2i/h) for position p and pair i,
 and each value is written to both lanes of its pair). For rotate_half the
 value of pair i goes to lanes i and i + L/2 instead. Angles, cos and sin are
-evaluated in fp64 and rounded to the table's storage type with
-round-to-nearest-even.
+evaluated in fp64 and converted to the table's storage type by torch, which
+rounds to nearest even through fp32 (so a 16-bit table value is rounded
+twice).
 
 Random tables with no structure (the single-op example of "CANN ops-transformer
 算子详解：inplace_partial_rotary_mul 原地部分旋转位置编码", section 调用说明,
