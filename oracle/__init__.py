@@ -189,6 +189,8 @@ def pos_tables(positions: np.ndarray, inv_freq: np.ndarray, L: int, mode: str, t
     pos = np.asarray(positions)
     if pos.dtype != np.int64 or pos.ndim != 2:
         raise TypeError("positions must be a 2-D int64 array")
+    if mode not in MODES or table_dtype not in DTYPES:
+        raise ValueError("unknown mode or table type")
     f = np.ascontiguousarray(inv_freq, dtype=np.float64)
     if f.size != L // 2:
         raise ValueError("inv_freq must hold L/2 values")

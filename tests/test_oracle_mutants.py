@@ -1,10 +1,11 @@
 """Planted mistakes in the oracle, on the CPU. Each mutant is rope_oracle.c
 with one plausible slip: a sign, a partner index, the lane of a table read,
 the backward's sign, the broadcast index, the slice start, the row order, a
-rounding rule, the fp16 range, the precision of the products. Every mutant
-must fail at least one pin of the oracle's own test files (closed forms,
-brute force, library conversions, the golden cases); a mutant that passed
-them all would be a mistake the pins cannot see.
+rounding rule, the fp16 range, the precision of the products, and in the
+tables built from positions the angle's precision, the rounding and the
+layout. Every mutant must fail at least one pin of the oracle's own test
+files (closed forms, brute force, library conversions, the golden cases); a
+mutant that passed them all would be a mistake the pins cannot see.
 
 The pins run in a subprocess against the mutant's library (ROPE_ORACLE_LIB);
 a mutant that crashes its process counts as caught."""
@@ -19,7 +20,7 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = [os.path.join(ROOT, "tests", f) for f in
-             ("test_oracle_golden.py", "test_oracle_pins.py", "test_oracle_converters.py")]
+             ("test_oracle_golden.py", "test_oracle_pins.py", "test_oracle_pos.py", "test_oracle_converters.py")]
 
 # (name, text in rope_oracle.c, replacement)
 MUTANTS = [
@@ -47,6 +48,13 @@ MUTANTS = [
     ("fp32 data computed in fp32", "double a = (double)xs[j] * (double)c;\n                double t = (double)sign * (double)xs[pj] * (double)sn;",
      "float a = xs[j] * c;\n                float t = (float)sign * xs[pj] * sn;"),
     ("bf16 NaN not kept quiet", "return (uint16_t)((u >> 16) | 0x40u);", "return (uint16_t)(u >> 16);"),
+    ("position tables rounded through fp32", "if (dtype == ORACLE_F32) return (float)v;", "if (1) return (float)v;"),
+    ("position angle in single precision", "const double theta = p * inv_freq[i];",
+     "const double theta = (double)((float)p * (float)inv_freq[i]);"),
+    ("rotate_half position table laid out as interleave", "const int64_t j0 = mode == ORACLE_INTERLEAVE ? 2 * i : i;",
+     "const int64_t j0 = 2 * i;"),
+    ("one-step rounding ties away from zero", "const double r = ldexp(rint(ldexp(v, -q)), q);",
+     "const double r = ldexp(round(ldexp(v, -q)), q);"),
 ]
 
 
