@@ -337,11 +337,58 @@ def bench_out_of_place(name: str, reps: int, stream) -> dict:
     return res
 
 
-def profile_target(name: str, reps: int, out_of_place: bool = False) -> None:
+def bench_positions(name: str, reps: int, stream) -> dict:
+    """The position entry points on a workload: cos and sin computed in the
+    kernel from the workload's positions (one int64 per (b,s)) and its L/2
+    double frequencies, against the table call on the same x. Bytes per
+    launch: the slice read and written once, the positions and frequencies
+    read once (no tables). Rotating copies as for the table call."""
+    import torch
+
+    import transformer_positional_encoding_amd as rp
+    import workloads as W
+    w = W.WORKLOADS[name]
+    ncopy = rotating_copies(w)
+    xs = [W.make_x(w).to("cuda")]
+    xs += [xs[0].clone() for _ in range(ncopy - 1)]
+    pos = torch.from_numpy(W.positions(w)).to("cuda")
+    f = rp.rope_inv_freq(w.L, w.base, "cuda")
+    r1, r2 = (t.to("cuda") for t in W.make_tables(w))
+    B, S, N, _ = w.x_shapes[0]
+    es = W.ESIZE[w.dtype]
+    nbytes = 2 * B * S * N * w.L * es + pos.numel() * 8 + f.numel() * 8
+    tdt = W.TORCH_DTYPES[w.tdtype]
+    res = {"workload": name, "note": w.note + ", tables computed from positions", "dtype": w.dtype,
+           "table_dtype": w.tdtype, "rotating_copies": ncopy, "bytes_per_launch": nbytes,
+           "table_call_bytes_per_launch": w.algorithmic_bytes(), "kernels": {}}
+    for _ in range(2):   # two rounds, the second kept (as for the table call)
+        for d in ("bwd", "fwd"):
+            pos_fn = rp.rope_partial_bwd_inplace_pos if d == "bwd" else rp.rope_partial_fwd_inplace_pos
+            with_pos = [(pos_fn, (xs[i], pos, f, w.mode, w.partial_slice, tdt)) for i in range(ncopy)]
+            with_tables = [(launch_fn(d), (xs[i], r1, r2, w.mode, w.partial_slice)) for i in range(ncopy)]
+            time_launches(with_pos, max(10, reps // 2), stream)
+            t_pos = time_launches(with_pos, reps, stream)
+            time_launches(with_tables, max(10, reps // 2), stream)
+            t_tab = time_launches(with_tables, reps, stream)
+            res["kernels"][d] = {"positions_us": round(t_pos * 1e6, 3), "GBps": round(nbytes / t_pos / 1e9, 1),
+                                 "frac_of_peak": round(nbytes / t_pos / 1e9 / PEAK_GBPS, 4),
+                                 "table_call_us": round(t_tab * 1e6, 3)}
+            tr = committed_traffic(name + ":pos", d)
+            if tr is not None:
+                res["kernels"][d]["hbm_bytes_per_launch"] = tr["hbm_bytes_per_launch"]
+                res["kernels"][d]["hbm_GBps"] = round(tr["hbm_bytes_per_launch"] / t_pos / 1e9, 1)
+                res["kernels"][d]["hbm_frac_of_peak"] = round(
+                    tr["hbm_bytes_per_launch"] / t_pos / 1e9 / PEAK_GBPS, 4)
+    del xs
+    torch.cuda.empty_cache()
+    return res
+
+
+def profile_target(name: str, reps: int, out_of_place: bool = False, positions: bool = False) -> None:
     """Launches for rocprofv3 counter passes: each direction of the workload
     `reps` times (rotating copies as in the timed run; out of place, from x
-    into a second buffer), then a plain device copy of known size for
-    calibrating the byte counters."""
+    into a second buffer; with positions, the position entry points), then a
+    plain device copy of known size for calibrating the byte counters."""
     import torch
 
     import transformer_positional_encoding_amd as rp
@@ -353,9 +400,14 @@ def profile_target(name: str, reps: int, out_of_place: bool = False) -> None:
     r1, r2 = (t.to("cuda") for t in W.make_tables(w))
     dirs = list(w.directions) + [d for d in ("fwd", "bwd") if d not in w.directions]
     y = torch.empty_like(xs[0]) if out_of_place else None
+    pos = torch.from_numpy(W.positions(w)).to("cuda") if positions else None
+    f = rp.rope_inv_freq(w.L, w.base, "cuda") if positions else None
     for d in dirs:
         for i in range(reps):
-            if out_of_place:
+            if positions:
+                (rp.rope_partial_fwd_inplace_pos if d == "fwd" else rp.rope_partial_bwd_inplace_pos)(
+                    xs[i % ncopy], pos, f, w.mode, w.partial_slice, W.TORCH_DTYPES[w.tdtype])
+            elif out_of_place:
                 (rp.rope_partial_fwd_out if d == "fwd" else rp.rope_partial_bwd_out)(
                     y, xs[0], r1, r2, w.mode, w.partial_slice)
             else:
@@ -366,7 +418,7 @@ def profile_target(name: str, reps: int, out_of_place: bool = False) -> None:
     for _ in range(reps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_target": name, "out_of_place": out_of_place, "reps": reps,
+    print(json.dumps({"profile_target": name, "out_of_place": out_of_place, "positions": positions, "reps": reps,
                       "copy_bytes": src.numel(), "rotating_copies": ncopy}), flush=True)
 
 
@@ -376,9 +428,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
-    ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out,c2_s4096,rh_64of128,rh_32of128",
+    ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out,c4:pos,c2_s4096:pos,c2_s4096,"
+                                      "rh_64of128,rh_32of128",
                     help="other workloads measured in the same run (reported under 'other_workloads'); "
-                         "NAME:out measures the out-of-place entry points on NAME")
+                         "NAME:out measures the out-of-place entry points on NAME, NAME:pos the position "
+                         "entry points")
     ap.add_argument("--reps", type=int, default=50, help="launches per per-kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle budget: whole steps repeated to fill about this many seconds")
@@ -386,6 +440,8 @@ def main() -> int:
     ap.add_argument("--profile-target", action="store_true")
     ap.add_argument("--out-of-place", action="store_true",
                     help="with --profile-target: launch the out-of-place entry points")
+    ap.add_argument("--positions", action="store_true",
+                    help="with --profile-target: launch the position entry points")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -401,7 +457,7 @@ def main() -> int:
     rp.library()  # fail loudly if the HIP library is missing
 
     if args.profile_target:
-        profile_target(args.workload, args.reps, args.out_of_place)
+        profile_target(args.workload, args.reps, args.out_of_place, args.positions)
         return 0
 
     stream = torch.cuda.current_stream()
@@ -412,6 +468,9 @@ def main() -> int:
         import workloads as W
         if name.endswith(":out"):
             others.append(bench_out_of_place(name[:-4], max(10, args.reps // 2), stream))
+            continue
+        if name.endswith(":pos"):
+            others.append(bench_positions(name[:-4], max(10, args.reps // 2), stream))
             continue
         if len(W.WORKLOADS[name].x_shapes) > 1:
             others.append(bench_multi(name, max(10, args.reps // 2), stream))

@@ -156,6 +156,54 @@ ROPE_API rope_status_t rope_partial_bwd_out(
     void* stream);
 
 /*
+ * rope_partial_fwd_inplace_pos / rope_partial_bwd_inplace_pos -- the same
+ * in-place operation with cos and sin computed from positions instead of
+ * read from tables. "ANE实战RoPE位置编码在MIL中的纯ANE实现", section 第一步,
+ * builds the tables from θ = p / base^(2i/h) for position p and pair i;
+ * here, for the row (b,s,n) and the slice's pair i:
+ *   θ = (double)positions[b, s] * inv_freq[i]      (one double product)
+ *   c = RN_T(cos θ),  s = RN_T(sin θ)             (double precision, then
+ *                                                   one rounding to nearest
+ *                                                   even to table_dtype T)
+ * placed as a table would hold them (interleave: lanes 2i and 2i+1;
+ * rotate_half: lanes i and i + L/2). The result is that of the table entry
+ * points given tables (Bp, S, 1, L) of type T with these values, up to the
+ * last-bit differences of two double-precision cos/sin implementations,
+ * which change a rounding to T only for values within about 2^-52 of a
+ * midpoint of T.
+ *
+ *   positions          device int64 array; the position of (b,s) is
+ *                      positions[b*positions_strides[0] + s*positions_strides[1]].
+ *   positions_shape    host {Bp, S}: Bp is 1 (one row of positions for every
+ *                      batch) or B, and S is x's S.
+ *   positions_strides  host, in elements, each >= 0; a size-1 dimension's
+ *                      stride is ignored.
+ *   inv_freq           device array of L/2 doubles, pair i's frequency
+ *                      (base^(-2i/L) for the page's recipe; any values, e.g.
+ *                      scaled frequencies, are taken as given).
+ *   table_dtype        T, the type cos and sin are rounded to (any of the
+ *                      three, independent of dtype).
+ *   Other arguments are those of rope_partial_fwd_inplace.
+ *
+ * Checks, in this order: the scalar arguments; an empty tensor or slice
+ * returns ROPE_OK at once; NULL x, positions, inv_freq, positions_shape or
+ * positions_strides (ROPE_ERR_NULLPTR); positions_shape not {1 or B, S}, a
+ * negative stride, or offsets beyond 64 bits (ROPE_ERR_INVALID). Memory as
+ * for the table entry points: asynchronous on `stream`, nothing allocated.
+ */
+ROPE_API rope_status_t rope_partial_fwd_inplace_pos(
+    void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+ROPE_API rope_status_t rope_partial_bwd_inplace_pos(
+    void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+/*
  * rope_partial_check -- run every argument check of the entry points above
  * (either direction: they are the same) and return the status they would
  * return, without launching anything or touching device memory. For callers
@@ -198,6 +246,29 @@ ROPE_API rope_status_t rope_partial_launch_info(
     const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
     const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
     rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    int64_t info[ROPE_LAUNCH_INFO_LEN]);
+
+/*
+ * rope_partial_launch_info_pos -- the launch plan of a position call
+ * (rope_partial_fwd_inplace_pos / _bwd_inplace_pos) with these arguments,
+ * for tests and profiling. Runs that call's checks first and returns their
+ * status; on ROPE_OK, info (caller-owned, ROPE_LAUNCH_INFO_LEN elements)
+ * receives:
+ *   [0] ROPE_KERNEL_NONE, _VECTOR, _ROWS or _SCALAR;
+ *   [1] blocks of the launch (0 for the scalar kernel);
+ *   [2] threads per block;
+ *   vector kernel: [3] heads per thread, [4] head lanes per position,
+ *       [5] positions per block, [6] head chunks per position, [7] 16-byte
+ *       vectors each row's threads cover;
+ *   row kernel: [4] rows per block, [7] threads per row.
+ * Entries that do not apply are 0. Launches nothing and touches no memory;
+ * pointers are only compared with NULL and checked for alignment. NULL
+ * info is ROPE_ERR_NULLPTR.
+ */
+ROPE_API rope_status_t rope_partial_launch_info_pos(
+    const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
     int64_t info[ROPE_LAUNCH_INFO_LEN]);
 
 /* largest tensor count of the _multi entry points */

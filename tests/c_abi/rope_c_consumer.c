@@ -2,9 +2,9 @@
  * A plain C client of librope_partial.so: it uses the library through the C
  * ABI declared in include/rope_partial.h and nothing else (no PyTorch, no
  * Python). Device memory and streams come from the HIP runtime API. It runs
- * the in-place, out-of-place and multi-tensor entry points and compares every
- * element with the CPU oracle (oracle/librope_oracle.so, test
- * infrastructure), and it checks the documented status codes.
+ * the in-place, out-of-place, multi-tensor and position entry points and
+ * compares every element with the CPU oracle (oracle/librope_oracle.so,
+ * test infrastructure), and it checks the documented status codes.
  *
  * The operation: "CANN ops-transformer 算子详解：inplace_partial_rotary_mul
  * 原地部分旋转位置编码", sections 功能与计算公式 and 约束说明; rotate_half
@@ -33,6 +33,10 @@ int rope_oracle_rows(void* x, const int64_t x_shape[4], int dtype,
                      const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
                      int table_dtype, int mode, int64_t start, int64_t end, int direction,
                      const int64_t* rows, int64_t nrows);
+/* The oracle's cos/sin tables of positions: (Bp, S, 1, L) each. */
+int rope_oracle_pos_tables(const int64_t* positions, int64_t Bp, int64_t S, int64_t stride_b, int64_t stride_s,
+                           const double* inv_freq, int64_t L, int mode, int table_dtype,
+                           void* cos_out, void* sin_out);
 
 #define FAIL(...) do { fprintf(stderr, "FAIL: " __VA_ARGS__); fprintf(stderr, "\n"); exit(1); } while (0)
 #define HIP_OK(call) do { hipError_t e_ = (call); if (e_ != hipSuccess) FAIL("%s: %s", #call, hipGetErrorString(e_)); } while (0)
@@ -192,6 +196,56 @@ static void run_case(const Case* c)
     free(x); free(r1); free(r2); free(out); free(want);
 }
 
+/* The position entry point: per-batch positions offset_b + s (offsets
+ * below 2^16), frequencies base^(-2i/L) computed here in double, tables
+ * computed in the kernel; the oracle builds the same tables and rotates. */
+static void run_pos_case(const char* name, const int64_t xs[4], int dtype, int tdtype, int mode, int dir,
+                         const int64_t sl[2], double base)
+{
+    const int64_t n = numel4(xs), B = xs[0], S = xs[1], L = sl[1] - sl[0];
+    const size_t xb = (size_t)n * esize(dtype);
+    void* x = malloc(xb);
+    fill(x, dtype, n, 4.0f);
+    int64_t* pos = (int64_t*)malloc((size_t)(B * S) * sizeof(int64_t));
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t off = (int64_t)(next_u64() % 65536u);
+        for (int64_t t = 0; t < S; ++t) pos[b * S + t] = off + t;
+    }
+    double* f = (double*)malloc((size_t)(L / 2) * sizeof(double));
+    for (int64_t i = 0; i < L / 2; ++i) f[i] = pow(base, -2.0 * (double)i / (double)L);
+    const int64_t ts[4] = {B, S, 1, L};
+    int64_t tst[4];
+    contiguous_strides(ts, tst);
+    tst[2] = 0;
+    const size_t tb = (size_t)numel4(ts) * esize(tdtype);
+    void* c = malloc(tb);
+    void* sn = malloc(tb);
+    if (rope_oracle_pos_tables(pos, B, S, S, 1, f, L, mode, tdtype, c, sn) != 0)
+        FAIL("%s: the oracle rejected the positions", name);
+    void* want = malloc(xb);
+    memcpy(want, x, xb);
+    if (rope_oracle_rows(want, xs, dtype, c, ts, tst, sn, ts, tst, tdtype, mode, sl[0], sl[1], dir, NULL,
+                         B * S * xs[2]) != 0)
+        FAIL("%s: the oracle rejected the case", name);
+    void* dx = dev_copy(x, xb);
+    void* dpos = dev_copy(pos, (size_t)(B * S) * sizeof(int64_t));
+    void* df = dev_copy(f, (size_t)(L / 2) * sizeof(double));
+    const int64_t pshape[2] = {B, S}, pstrides[2] = {S, 1};
+    int64_t info[ROPE_LAUNCH_INFO_LEN];
+    rope_status_t st = rope_partial_launch_info_pos(dx, xs, dtype, (const int64_t*)dpos, pshape, pstrides,
+                                                    (const double*)df, tdtype, mode, sl, info);
+    if (st != ROPE_OK || info[0] == ROPE_KERNEL_NONE) FAIL("%s: launch plan status %d", name, st);
+    st = (dir == 0 ? rope_partial_fwd_inplace_pos : rope_partial_bwd_inplace_pos)(
+        dx, xs, dtype, (const int64_t*)dpos, pshape, pstrides, (const double*)df, tdtype, mode, sl, NULL);
+    if (st != ROPE_OK) FAIL("%s: status %d (%s)", name, st, rope_last_error());
+    HIP_OK(hipStreamSynchronize(NULL));
+    void* out = malloc(xb);
+    HIP_OK(hipMemcpy(out, dx, xb, hipMemcpyDeviceToHost));
+    compare(name, out, want, dtype, n, 4.0);
+    HIP_OK(hipFree(dx)); HIP_OK(hipFree(dpos)); HIP_OK(hipFree(df));
+    free(x); free(pos); free(f); free(c); free(sn); free(want); free(out);
+}
+
 /* Calls that must return before any HIP call: errors and no-ops. */
 static void expect(const char* what, rope_status_t got, rope_status_t want, const char* text)
 {
@@ -245,6 +299,25 @@ static void check_errors(void)
                                                    ROPE_DTYPE_BF16, ROPE_MODE_INTERLEAVE, sl, info),
            ROPE_OK, NULL);
     if (info[0] != ROPE_KERNEL_VECTOR || info[2] <= 0) FAIL("launch plan: kernel %lld", (long long)info[0]);
+    const int64_t* fake_pos = (const int64_t*)fake;
+    const double* fake_f = (const double*)fake;
+    int64_t ps[2] = {1, 4}, pst[2] = {4, 1}, ps_bad[2] = {3, 4};
+    expect("positions NULL", rope_partial_fwd_inplace_pos(fake, xs, ROPE_DTYPE_BF16, NULL, ps, pst, fake_f,
+                                                          ROPE_DTYPE_BF16, ROPE_MODE_INTERLEAVE, sl, NULL),
+           ROPE_ERR_NULLPTR, "positions is NULL");
+    expect("positions of 3 batches for 2", rope_partial_bwd_inplace_pos(fake, xs, ROPE_DTYPE_BF16, fake_pos, ps_bad,
+                                                                        pst, fake_f, ROPE_DTYPE_BF16,
+                                                                        ROPE_MODE_INTERLEAVE, sl, NULL),
+           ROPE_ERR_INVALID, "dimension B");
+    expect("positions, empty slice, NULL everything", rope_partial_fwd_inplace_pos(
+               NULL, xs, ROPE_DTYPE_F16, NULL, NULL, NULL, NULL, ROPE_DTYPE_F16, ROPE_MODE_ROTATE_HALF, empty_sl,
+               NULL),
+           ROPE_OK, NULL);
+    expect("position launch plan", rope_partial_launch_info_pos(fake, xs, ROPE_DTYPE_BF16, fake_pos, ps, pst,
+                                                                fake_f, ROPE_DTYPE_BF16, ROPE_MODE_INTERLEAVE, sl,
+                                                                info),
+           ROPE_OK, NULL);
+    if (info[0] != ROPE_KERNEL_VECTOR || info[2] <= 0) FAIL("position launch plan: kernel %lld", (long long)info[0]);
 }
 
 int main(int argc, char** argv)
@@ -275,6 +348,11 @@ int main(int argc, char** argv)
          {2, 8, 4, 128}, ROPE_DTYPE_BF16, ROPE_DTYPE_BF16, ROPE_MODE_ROTATE_HALF, 0, {32, 96}, {2, 8, 4, 64}, 0, 0, 0},
     };
     for (size_t i = 0; i < sizeof(cases) / sizeof(cases[0]); ++i) run_case(&cases[i]);
+    const int64_t pxs[4] = {2, 64, 8, 128}, psl[2] = {32, 96}, pxs2[4] = {3, 16, 5, 64}, psl2[2] = {0, 64};
+    run_pos_case("bf16 positions, lanes [32,96), bwd in place", pxs, ROPE_DTYPE_BF16, ROPE_DTYPE_BF16,
+                 ROPE_MODE_INTERLEAVE, 1, psl, 500000.0);
+    run_pos_case("fp32 positions, rotate_half, fwd in place", pxs2, ROPE_DTYPE_F32, ROPE_DTYPE_F32,
+                 ROPE_MODE_ROTATE_HALF, 0, psl2, 10000.0);
     HIP_OK(hipGetLastError());
     printf("all ok\n");
     return 0;

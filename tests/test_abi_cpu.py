@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     for want in ("rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string",
                  "rope_last_error", "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi",
                  "rope_partial_check", "rope_partial_launch_info", "rope_partial_fwd_out",
-                 "rope_partial_bwd_out"):
+                 "rope_partial_bwd_out", "rope_partial_fwd_inplace_pos", "rope_partial_bwd_inplace_pos",
+                 "rope_partial_launch_info_pos"):
         assert want in names
 
 
@@ -267,3 +268,52 @@ def test_out_of_place_binding_rejects_bad_tensors():
     e = torch.zeros(0, 4, 3, 64)
     rp.rope_partial_fwd_out(torch.zeros_like(e), e, r, r, "interleave", (0, 32))
     assert rp.partial_rotary_mul(e, r, r, "interleave", (0, 32)).shape == e.shape
+
+
+def pcall(direction="fwd", x=FAKE, x_shape=(2, 4, 3, 64), dtype=BF16, pos=FAKE, pos_shape=(1, 4), pos_strides=(4, 1),
+          inv_freq=FAKE, table_dtype=BF16, mode=IL, sl=(0, 32)):
+    """The position entry points, only with arguments that fail validation
+    or are no-ops."""
+    return rp.raw_pos_call(direction, x, x_shape, dtype, pos, pos_shape, pos_strides, inv_freq, table_dtype, mode,
+                           sl, None)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("kwargs,code,text", [
+    (dict(mode=3), INVALID, "mode"),
+    (dict(table_dtype=9), INVALID, "table dtype"),
+    (dict(sl=(0, 31)), INVALID, "even"),
+    (dict(x=None), NULLPTR, "x is NULL"),
+    (dict(pos=None), NULLPTR, "positions is NULL"),
+    (dict(inv_freq=None), NULLPTR, "inv_freq is NULL"),
+    (dict(pos_shape=None), NULLPTR, "positions shape"),
+    (dict(pos_strides=None), NULLPTR, "positions shape"),
+    (dict(pos_shape=(3, 4)), INVALID, "dimension B"),
+    (dict(pos_shape=(2, 5)), INVALID, "dimension S"),
+    (dict(pos_shape=(2, 4), pos_strides=(-4, 1)), INVALID, "negative"),
+    (dict(pos_shape=(2, 4), pos_strides=(2 ** 62, 2 ** 62)), INVALID, "overflow"),
+])
+def test_pos_argument_errors(direction, kwargs, code, text):
+    assert pcall(direction, **kwargs) == code
+    assert text in rp.last_error()
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_pos_noops_need_no_pointers(direction):
+    assert pcall(direction, x=None, pos=None, inv_freq=None, pos_shape=None, pos_strides=None, sl=(8, 8)) == OK
+    assert pcall(direction, x=None, pos=None, inv_freq=None, x_shape=(0, 4, 3, 64)) == OK
+    # a size-1 batch dimension's stride is ignored, however large
+    assert pcall(direction, pos_shape=(1, 4), pos_strides=(2 ** 62, 1), x=None) == NULLPTR   # fails only on x
+
+
+def test_pos_binding_checks():
+    import torch
+    x = torch.zeros(2, 4, 3, 64)
+    f = rp.rope_inv_freq(32)
+    with pytest.raises(ValueError, match="int64"):
+        rp.rope_partial_fwd_inplace_pos(x, torch.zeros(1, 4), f, "interleave", (0, 32))
+    with pytest.raises(ValueError, match="float64"):
+        rp.rope_partial_fwd_inplace_pos(x, torch.zeros(1, 4, dtype=torch.int64), f.float(), "interleave", (0, 32))
+    with pytest.raises(ValueError, match="frequencies"):
+        rp.rope_partial_fwd_inplace_pos(x, torch.zeros(1, 4, dtype=torch.int64), rp.rope_inv_freq(16),
+                                        "interleave", (0, 32))

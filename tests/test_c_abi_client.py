@@ -1,8 +1,8 @@
 """A plain C program (tests/c_abi/rope_c_consumer.c, built by
 __graft_entry__.build()) that uses the library through the C ABI alone: HIP
 runtime memory and streams, no PyTorch and no Python in the process. It
-compares the in-place, out-of-place and multi-tensor entry points with the C
-oracle element by element and checks the documented status codes."""
+compares the in-place, out-of-place, multi-tensor and position entry points
+with the C oracle element by element and checks the documented status codes."""
 import os
 import subprocess
 
@@ -25,12 +25,12 @@ def test_c_client_argument_checks_without_a_gpu():
     """Errors, no-ops and the launch plan return before any HIP call."""
     out = _run("--no-gpu", timeout=60)
     assert "ROPE_ERR_NULLPTR" in out and "ROPE_ERR_INVALID" in out
-    assert sum(line.startswith("ok   ") for line in out.splitlines()) == 10
+    assert sum(line.startswith("ok   ") for line in out.splitlines()) == 14
 
 
 @pytest.mark.gpu
 def test_c_client_on_the_gpu():
     out = _run(timeout=120)
     for case in ("per-batch tables", "MLA-like", "rotate_half, bwd out of place", "fp32 tables", "Q and K",
-                 "odd start", "per-head tables"):
+                 "odd start", "per-head tables", "bf16 positions", "fp32 positions"):
         assert case in out, case

@@ -194,3 +194,98 @@ def test_rotate_half_own_vector_needs_single_wave_rows():
     # slice itself 64, so the own-vector scheme runs over the slice alone
     st, info = plan((1, 3, 5, 1024), BF16, (8, 520), mode=RH)
     assert st == OK and info["row_vectors"] == 64 and info["threads"] == 64
+
+
+# ---------------------------------------------------------------- position calls
+
+POS_ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def pos_plan(x_shape, dtype, sl, mode=IL, per_batch=False, x=FAKE, table_dtype=None):
+    B, S = x_shape[0], x_shape[1]
+    pshape = (B if per_batch else 1, S)
+    td = rp.DTYPE_CODES[table_dtype or dtype]
+    return rp.raw_launch_info_pos(x, x_shape, rp.DTYPE_CODES[dtype], FAKE, pshape, (S, 1), FAKE, td,
+                                  mode, sl)
+
+
+def test_pos_plan_null_info_and_noops():
+    assert rp.raw_launch_info_pos(FAKE, (2, 4, 3, 64), 2, FAKE, (1, 4), (4, 1), FAKE, 2, IL, (0, 32),
+                                  info_out=False)[0] == rp.ROPE_ERR_NULLPTR
+    assert pos_plan((2, 4, 3, 64), "bf16", (8, 8)) == (rp.ROPE_OK, {"kernel": "none", "blocks": 0, "threads": 0,
+                                                                  "heads_per_thread": 0, "head_lanes": 0,
+                                                                  "positions_per_block": 0, "head_chunks": 0,
+                                                                  "row_vectors": 0})
+    assert pos_plan((2, 4, 3, 64), "bf16", (0, 31))[0] == rp.ROPE_ERR_INVALID
+
+
+def test_pos_plan_of_the_long_context_shard():
+    st, p = pos_plan((16, 8192, 32, 128), "bf16", (32, 96), IL, per_batch=True)
+    assert st == rp.ROPE_OK
+    # whole 256-byte rows (the slice's lines), 8 head lanes x 2 heads, two chunks of 16 heads
+    assert p == {"kernel": "vector", "blocks": 16 * 8192 * 2, "threads": 128, "heads_per_thread": 2,
+                 "head_lanes": 8, "positions_per_block": 1, "head_chunks": 2, "row_vectors": 16}
+
+
+@pytest.mark.parametrize("x_shape,dtype,sl,mode,kernel,P", [
+    ((2, 7, 1, 128), "bf16", (0, 128), RH, "vector", 8),     # one head: 8 rows of 8 threads per block
+    ((3, 5, 2, 64), "bf16", (0, 64), IL, "vector", 8),
+    ((2, 5, 3, 1024), "f32", (0, 1024), RH, "vector", 1),    # 512 pairs: the whole LDS table
+    ((2, 6, 5, 64), "bf16", (3, 35), IL, "rows", None),      # odd start
+    ((2, 5, 3, 48), "bf16", (4, 44), RH, "rows", None),      # halves of 40 bytes
+])
+def test_pos_plan_kernels(x_shape, dtype, sl, mode, kernel, P):
+    st, p = pos_plan(x_shape, dtype, sl, mode)
+    assert st == rp.ROPE_OK and p["kernel"] == kernel
+    if P is not None:
+        assert p["positions_per_block"] == P
+
+
+def test_pos_plan_unaligned_x_takes_the_row_kernel():
+    assert pos_plan((2, 4, 3, 64), "bf16", (0, 64), x=FAKE + 2)[1]["kernel"] == "rows"
+
+
+def test_pos_plan_invariants_over_random_shapes():
+    """Every vector plan: at most 256 threads, a multiple of the row's
+    threads; the LDS table (positions per block x L/2 pairs) within 512
+    entries; the head chunks cover N exactly; the rows' threads cover the
+    slice; several positions per block only when a position's heads fill
+    fewer than 128 threads; one block per chunk of positions."""
+    import random
+    rng = random.Random(5)
+    seen = {"vector": 0, "rows": 0}
+    for _ in range(3000):
+        dtype = rng.choice(["f32", "f16", "bf16"])
+        es = POS_ESIZE[dtype]
+        D = rng.choice([8, 16, 24, 32, 48, 64, 96, 128, 192, 256, 512, 1024])
+        start = rng.choice([0, 0, 0, 8, 16, 32, 3, 64]) % D
+        start -= start % 2
+        L = rng.randrange(0, D - start + 1, 2)
+        if L == 0:
+            continue
+        mode = rng.choice([IL, RH])
+        B, S, N = rng.randint(1, 4), rng.randint(1, 300), rng.choice([1, 2, 3, 5, 8, 13, 16, 32, 64, 128])
+        st, p = pos_plan((B, S, N, D), dtype, (start, start + L), mode, per_batch=rng.random() < 0.5)
+        assert st == rp.ROPE_OK, (B, S, N, D, dtype, start, L, mode)
+        seen[p["kernel"]] = seen.get(p["kernel"], 0) + 1
+        aligned = (D * es) % 16 == 0 and (start * es) % 16 == 0
+        unit = L * es if mode == IL else (L // 2) * es
+        if not aligned or unit % 16:
+            assert p["kernel"] != "vector"
+            continue
+        if p["kernel"] != "vector":
+            continue
+        span, HL, U, P, chunks = (p["row_vectors"], p["head_lanes"], p["heads_per_thread"],
+                                  p["positions_per_block"], p["head_chunks"])
+        assert p["threads"] == P * span * HL <= 256
+        assert P * (L // 2) <= 512
+        assert (chunks - 1) * HL * U < N <= chunks * HL * U
+        assert HL <= N
+        if mode == IL:
+            assert span * 16 >= L * es and span * 16 <= D * es
+        else:
+            assert span * 16 == (L // 2) * es
+        if P > 1:
+            assert span * HL < 128
+        assert p["blocks"] == -(-(B * S) // P) * chunks
+    assert seen["vector"] > 500 and seen["rows"] > 100, seen

@@ -153,7 +153,8 @@ def test_pos_tables_at_scale_against_numpy(dtype):
     """A long-context-like table (offsets up to 65535 + 4096 positions)
     against numpy's cos/sin and one-step rounding: 16-bit values agree bit
     for bit (an ulp of difference between two double cos/sin implementations
-    changes a 16-bit rounding only within 2^-45 of a midpoint)."""
+    changes a 16-bit rounding only for a value within a double ulp of a
+    midpoint, a chance of about 2^-40 per value)."""
     rng = np.random.default_rng(3)
     L = 64
     pos = (rng.integers(0, 65536, size=(4, 1)) + np.arange(4096)[None, :]).astype(np.int64)

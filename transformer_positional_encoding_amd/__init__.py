@@ -21,6 +21,7 @@ __all__ = [
     "rope_partial_fwd_inplace", "rope_partial_bwd_inplace", "rope_status_string", "inplace_partial_rotary_mul",
     "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi", "MULTI_MAX", "rope_partial_check",
     "rope_partial_launch_info", "rope_partial_fwd_out", "rope_partial_bwd_out", "partial_rotary_mul",
+    "rope_partial_fwd_inplace_pos", "rope_partial_bwd_inplace_pos", "rope_inv_freq",
     "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
     "ROPE_ERR_UNSUPPORTED", "ROPE_ERR_RUNTIME", "MODES", "DTYPE_CODES",
 ]
@@ -72,6 +73,15 @@ def library() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_void_p] + _ENTRY_ARGTYPES
+        pos_args = [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64), ctypes.c_int, ctypes.c_void_p,
+                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p,
+                    ctypes.c_int, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)]
+        for name in ("rope_partial_fwd_inplace_pos", "rope_partial_bwd_inplace_pos"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = pos_args + [ctypes.c_void_p]
+        L.rope_partial_launch_info_pos.restype = ctypes.c_int
+        L.rope_partial_launch_info_pos.argtypes = pos_args + [ctypes.POINTER(ctypes.c_int64)]
         for name in ("rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi"):
             f = getattr(L, name)
             f.restype = ctypes.c_int
@@ -132,6 +142,19 @@ def raw_out_call(direction: str, y_ptr, x_ptr, x_shape, dtype: int, r1_ptr, r1_s
               sl, stream)
 
 
+def raw_pos_call(direction: str, x_ptr, x_shape, dtype: int, pos_ptr, pos_shape, pos_strides, inv_freq_ptr,
+                 table_dtype: int, mode: int, partial_slice, stream=None) -> int:
+    """Call rope_partial_{fwd,bwd}_inplace_pos with plain integers and
+    sequences (None = NULL); returns the status code without raising."""
+    L = library()
+    fn = L.rope_partial_fwd_inplace_pos if direction == "fwd" else L.rope_partial_bwd_inplace_pos
+    sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
+    ps = None if pos_shape is None else _I64x2(int(pos_shape[0]), int(pos_shape[1]))
+    pt = None if pos_strides is None else _I64x2(int(pos_strides[0]), int(pos_strides[1]))
+    return fn(x_ptr, _arr4(x_shape), int(dtype), pos_ptr, ps, pt, inv_freq_ptr, int(table_dtype), int(mode), sl,
+              stream)
+
+
 def raw_check(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2_ptr, r2_shape, r2_strides,
               table_dtype: int, mode: int, partial_slice) -> int:
     """rope_partial_check with plain integers and sequences (None = NULL):
@@ -164,6 +187,26 @@ def raw_launch_info(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2
                     "threads_per_row": v[7]}
     return st, {"kernel": KERNELS.get(v[0], v[0]), "blocks": v[1], "threads": v[2], "heads_per_thread": v[3],
                 "head_lanes": v[4], "tiles_per_block": v[5], "xcd_run": v[6], "row_vectors": v[7]}
+
+
+def raw_launch_info_pos(x_ptr, x_shape, dtype: int, pos_ptr, pos_shape, pos_strides, inv_freq_ptr,
+                        table_dtype: int, mode: int, partial_slice, info_out: bool = True):
+    """rope_partial_launch_info_pos with plain integers and sequences (None =
+    NULL): (status, plan dict or None); nothing is launched."""
+    sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
+    ps = None if pos_shape is None else _I64x2(int(pos_shape[0]), int(pos_shape[1]))
+    pt = None if pos_strides is None else _I64x2(int(pos_strides[0]), int(pos_strides[1]))
+    info = (ctypes.c_int64 * LAUNCH_INFO_LEN)() if info_out else None
+    st = library().rope_partial_launch_info_pos(x_ptr, _arr4(x_shape), int(dtype), pos_ptr, ps, pt, inv_freq_ptr,
+                                                int(table_dtype), int(mode), sl, info)
+    if st != ROPE_OK or info is None:
+        return st, None
+    v = list(info)
+    if v[0] == 3:
+        return st, {"kernel": "rows", "blocks": v[1], "threads": v[2], "rows_per_block": v[4],
+                    "threads_per_row": v[7]}
+    return st, {"kernel": KERNELS.get(v[0], v[0]), "blocks": v[1], "threads": v[2], "heads_per_thread": v[3],
+                "head_lanes": v[4], "positions_per_block": v[5], "head_chunks": v[6], "row_vectors": v[7]}
 
 
 def raw_multi_call(direction: str, x_ptrs, x_shapes, dtype: int, r1_ptr, r1_shape, r1_strides,
@@ -382,6 +425,83 @@ def rope_partial_bwd_out(dx, dy, r1, r2, rotary_mode="interleave", partial_slice
     """Out-of-place backward: ``dx`` receives the gradient with respect to x
     for the incoming gradient ``dy``, which is left unchanged."""
     _call_out("bwd", dx, dy, r1, r2, rotary_mode, partial_slice, stream)
+
+
+def rope_inv_freq(L: int, base: float = 10000.0, device=None):
+    """The frequencies base^(-2i/L), i < L/2, of the page's recipe, as the
+    float64 tensor the _pos entry points take (computed in double on the
+    host)."""
+    import torch
+    i = torch.arange(L // 2, dtype=torch.float64)
+    return torch.pow(torch.tensor(float(base), dtype=torch.float64), -2.0 * i / L).to(device)
+
+
+def _call_pos(direction, x, positions, inv_freq, mode, partial_slice, table_dtype, stream):
+    import torch
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"rotary_mode must be one of {sorted(MODES)}")
+        mode = MODES[mode]
+    for name, t in (("x", x), ("positions", positions), ("inv_freq", inv_freq)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+    if x.dim() != 4:
+        raise ValueError(f"x must be 4-D (B,S,N,D layout), got {x.dim()}-D")
+    if positions.dim() != 2 or positions.dtype != torch.int64:
+        raise ValueError("positions must be a 2-D int64 tensor (B or 1, S)")
+    if inv_freq.dtype != torch.float64 or inv_freq.dim() != 1 or not inv_freq.is_contiguous():
+        raise ValueError("inv_freq must be a contiguous 1-D float64 tensor")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (BSND); non-contiguous tensors are not supported")
+    sl = (0, 0) if partial_slice is None else (int(partial_slice[0]), int(partial_slice[1]))
+    if x.numel() and sl[1] > sl[0]:
+        if inv_freq.numel() != (sl[1] - sl[0]) // 2:
+            raise ValueError(f"inv_freq must hold (end - start) / 2 = {(sl[1] - sl[0]) // 2} frequencies")
+        if not x.is_cuda:
+            raise ValueError("x must be a GPU tensor")
+        for name, t in (("positions", positions), ("inv_freq", inv_freq)):
+            if t.device != x.device:
+                raise ValueError(f"{name} must be on {x.device}")
+    if table_dtype is None:
+        tdt = _dtype_code(x)
+    else:
+        tdt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}.get(table_dtype, DTYPE_CODES.get(table_dtype))
+        if tdt is None:
+            raise TypeError(f"unsupported table dtype {table_dtype}")
+    dev = x.device
+    if stream is None:
+        handle = torch.cuda.current_stream(dev).cuda_stream if x.is_cuda else None
+    else:
+        handle = getattr(stream, "cuda_stream", stream)
+    switch = x.is_cuda and dev.index != torch.cuda.current_device()
+    with torch.cuda.device(dev) if switch else _nullcontext():
+        st = raw_pos_call(direction, x.data_ptr() or None, tuple(x.shape), _dtype_code(x),
+                          positions.data_ptr() or None, tuple(positions.shape), tuple(positions.stride()),
+                          inv_freq.data_ptr() or None, tdt, mode, partial_slice, handle)
+    if st != ROPE_OK:
+        raise RopeError(st, last_error())
+
+
+def rope_partial_fwd_inplace_pos(x, positions, inv_freq, rotary_mode="interleave", partial_slice=None,
+                                 table_dtype=None, stream=None) -> None:
+    """Rotate ``x[..., start:end)`` in place with cos/sin computed in the
+    kernel from positions: θ = positions[b, s] * inv_freq[i] (double), cos
+    and sin in double precision rounded once to ``table_dtype`` (default:
+    x's dtype) -- the values a table of that type built from the same angles
+    would hold.
+
+    positions: int64 GPU tensor (B or 1, S), any strides.
+    inv_freq: contiguous float64 GPU tensor of (end - start) / 2 frequencies
+    (``rope_inv_freq(L, base)`` gives base^(-2i/L)).
+    """
+    _call_pos("fwd", x, positions, inv_freq, rotary_mode, partial_slice, table_dtype, stream)
+
+
+def rope_partial_bwd_inplace_pos(dx, positions, inv_freq, rotary_mode="interleave", partial_slice=None,
+                                 table_dtype=None, stream=None) -> None:
+    """Backward of :func:`rope_partial_fwd_inplace_pos`, in place on the
+    incoming gradient."""
+    _call_pos("bwd", dx, positions, inv_freq, rotary_mode, partial_slice, table_dtype, stream)
 
 
 def rope_partial_fwd_inplace_multi(xs, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:

@@ -560,6 +560,185 @@ __global__ void __launch_bounds__(256) rope_vec_multi_kernel(MultiVecArgs m)
 }
 
 // ---------------------------------------------------------------------------
+// cos and sin from positions ("ANE实战RoPE位置编码在MIL中的纯ANE实现", section
+// 第一步: the table of θ = p / base^(2i/h), here θ = p * inv_freq[i] with the
+// frequencies given): θ is the double product of the position and the pair's
+// frequency, cos θ and sin θ are evaluated in double precision and rounded
+// once, to nearest even, to the table type TT.
+// ---------------------------------------------------------------------------
+
+// A double rounded once to the nearest value of TT, ties to even, returned
+// as the float that holds it. fp32: the conversion instruction (round to
+// nearest even). bf16/fp16: a value of the type is a whole number of units
+// in the last place of its binade, 2^(e - p) for |v| in [2^(e-1), 2^e) with
+// p significand bits, and never below the least subnormal 2^(emin - p + 1);
+// scaling by powers of two is exact and rint() rounds ties to even.
+template <int TT>
+__device__ __forceinline__ float round_to_type(double v)
+{
+    if constexpr (TT == ROPE_DTYPE_F32) {
+        return static_cast<float>(v);
+    } else {
+        constexpr int p = TT == ROPE_DTYPE_F16 ? 11 : 8;
+        constexpr int emin = TT == ROPE_DTYPE_F16 ? -14 : -126;
+        constexpr double maxf = TT == ROPE_DTYPE_F16 ? 65504.0 : 0x1.fep127;
+        if (!(v != 0.0) || !__builtin_isfinite(v)) return static_cast<float>(v);   // zero, inf, NaN
+        int e;
+        (void)frexp(v, &e);
+        const int q = e - p > emin - p + 1 ? e - p : emin - p + 1;
+        const double r = ldexp(rint(ldexp(v, -q)), q);
+        if (fabs(r) > maxf) return v > 0 ? __builtin_inff() : -__builtin_inff();
+        return static_cast<float>(r);   // exact: r is a value of TT
+    }
+}
+
+// (cos θ, sin θ) rounded to TT for position p and frequency f.
+template <int TT>
+__device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
+{
+    double sn, cn;
+    sincos(static_cast<double>(p) * f, &sn, &cn);
+    return make_float2(round_to_type<TT>(cn), round_to_type<TT>(sn));
+}
+
+// ---------------------------------------------------------------------------
+// Vector kernel with the tables computed from positions. A block takes P
+// consecutive (b,s) positions (P > 1 only when one position's heads fill
+// fewer than kPosLanes threads) and, for each, a chunk of up to HL*kUPos
+// heads (HL head lanes, kUPos heads per thread). Its threads first load the
+// position and frequency of the first (cos, sin) pair each evaluates, then
+// issue their x loads, then evaluate cos and sin while x is in flight: the
+// memory counter drains in issue order, so the wait for the frequency does
+// not wait for x, provided every load is issued on every path (indices are
+// clamped, never branched around). The values go to LDS, each pair of each
+// position once per block, and each thread reads those of its lanes from
+// there. The thread layout is the table kernel's: interleave with
+// whole-line coverage, rotate_half as pair owner (a thread takes vector k
+// of both halves). Measured on MI355X (the (16,8192,32,128) shard's slice
+// [32,96), the GQA Q layout at 4096 positions, the MLA-style slice): two
+// heads per thread in 128-thread blocks was the best of 1, 2, 4 or 8 heads
+// per thread in 64-, 128- or 256-thread blocks on all three, and as fast as
+// the table kernel on the first two.
+// ---------------------------------------------------------------------------
+constexpr int kUPos = 2;
+constexpr int kPosLds = ROPE_D_LIMIT / 2;    // (cos, sin) entries per block
+constexpr uint32_t kPosLanes = 128;          // threads a position's heads fill before a block takes more positions
+
+struct PosArgs {
+    v4u* x;
+    const int64_t* pos;      // position of (b,s) at pos[b*pos_sb + s*pos_ss]
+    const double* inv_freq;  // L/2 frequencies
+    int64_t pos_sb, pos_ss;
+    uint32_t row_vecs;       // vectors per row of x
+    uint32_t start_vec;      // first slice vector within a row
+    uint32_t lo_vec;         // first vector the threads of a row cover
+    uint32_t half_vecs;      // rotate_half: vectors per half of the slice
+    uint32_t nvec;           // work units per row (interleave: slice vectors; rotate_half: one half's)
+    uint32_t span;           // vectors per row the threads cover
+    uint32_t HL;             // head lanes per position
+    uint32_t lanes;          // threads per position: span * HL
+    uint32_t P;              // positions per block
+    uint32_t N;
+    uint32_t pairs;          // L/2
+    uint32_t entries;        // P * pairs
+    uint32_t chunks;         // head chunks per position
+    uint32_t bs;             // B*S
+    uint32_t items;          // ceil(B*S / P) * chunks
+    FastDiv span_div, lanes_div, pairs_div, chunk_div, s_div;
+};
+
+template <int DT, int TT, int DIR, int MODE>
+__global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
+{
+    __shared__ float2 cs[kPosLds];   // (cos, sin) of the block's positions, pair-major per position
+    constexpr int K = Store<DT>::kLanes;
+    constexpr int U = kUPos;
+    constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
+    const uint32_t t = threadIdx.x;
+    const uint32_t pp = fast_div(t, a.lanes_div);   // the thread's position within the block
+    const uint32_t r = t - pp * a.lanes;
+    const uint32_t hl = fast_div(r, a.span_div);
+    const uint32_t vs = r - hl * a.span;
+    const uint32_t c = a.lo_vec + vs;                 // vector within the row
+    const bool in_slice = c >= a.start_vec && c - a.start_vec < a.nvec;
+    const uint32_t v = in_slice ? c - a.start_vec : 0;
+    // the table entry this thread evaluates first: position eq, pair ei
+    const uint32_t eq = fast_div(t, a.pairs_div);
+    const uint32_t ei = t - eq * a.pairs;
+    // every thread runs the same iterations, so the barriers below are uniform
+    for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
+        const uint32_t grp = fast_div(w, a.chunk_div);
+        const uint32_t chunk = w - grp * a.chunks;
+        const uint32_t g0 = grp * a.P;                // first position of the block
+        const bool fill = t < a.entries && g0 + eq < a.bs;
+        const uint32_t gq = min(g0 + eq, a.bs - 1);
+        const uint32_t bq = fast_div(gq, a.s_div);
+        const int64_t p0 = a.pos[(int64_t)bq * a.pos_sb + (int64_t)(gq - bq * a.s_div.d) * a.pos_ss];
+        const double f0 = a.inv_freq[ei];
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t g = g0 + pp;
+        const bool pos_live = g < a.bs;
+        const uint32_t gl = pos_live ? g : a.bs - 1;  // past the last position: re-read it, store nothing
+        const uint32_t n0 = chunk * (a.HL * U) + hl;
+        v4u xa[U], xb[U];
+        uint32_t off[U];
+        bool live[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t n = n0 + (uint32_t)k * a.HL;
+            live[k] = pos_live && n < a.N;            // past N: re-read row N-1, store nothing
+            const uint32_t nl = n < a.N ? n : a.N - 1;
+            off[k] = (gl * a.N + nl) * a.row_vecs + c;
+            xa[k] = load_x<true>(a.x + off[k]);
+            if constexpr (MODE == kModeRH) xb[k] = load_x<true>(a.x + off[k] + a.half_vecs);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
+        for (uint32_t e = t + blockDim.x; e < a.entries; e += blockDim.x) {
+            const uint32_t q = fast_div(e, a.pairs_div);
+            const uint32_t ge = g0 + q;
+            if (ge >= a.bs) break;                    // later entries belong to later positions
+            const uint32_t be = fast_div(ge, a.s_div);
+            const int64_t pe = a.pos[(int64_t)be * a.pos_sb + (int64_t)(ge - be * a.s_div.d) * a.pos_ss];
+            cs[e] = pos_cos_sin<TT>(pe, a.inv_freq[e - q * a.pairs]);
+        }
+        __syncthreads();
+        // cos and sin of the thread's lanes: interleave lane j belongs to
+        // pair j/2; rotate_half lane j of the first half to pair j, and the
+        // matching lane of the second half shares it
+        const uint32_t base = pp * a.pairs;
+        float C[K], S[K];
+#pragma unroll
+        for (int e = 0; e < K; ++e) {
+            const uint32_t i = MODE == kModeIL ? (v * K + e) / 2 : v * K + e;
+            const float2 q = cs[in_slice && pos_live ? base + i : 0];
+            C[e] = q.x;
+            S[e] = q.y;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (!live[k] || !in_slice) continue;
+            Lanes<DT> X;
+            X.unpack(xa[k]);
+            if constexpr (MODE == kModeIL) {
+#pragma unroll
+                for (int i = 0; i < K; i += 2)
+                    rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C[i], S[i], C[i + 1], S[i + 1]);
+                store_x<true>(a.x + off[k], X.pack());
+            } else {
+                Lanes<DT> X2;
+                X2.unpack(xb[k]);
+#pragma unroll
+                for (int i = 0; i < K; ++i) rotate_pair<DIR, kUnfused>(X.v[i], X2.v[i], C[i], S[i], C[i], S[i]);
+                store_x<true>(a.x + off[k], X.pack());
+                store_x<true>(a.x + off[k] + a.half_vecs, X2.pack());
+            }
+        }
+        __syncthreads();   // the next item rewrites cs
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Scalar kernel: the general kernel from 2^31 rows on (the row kernel below
 // takes fewer). Any alignment, any start parity, any slice length; one
 // thread per rotation pair; 64-bit indexing throughout.
@@ -568,6 +747,9 @@ struct ScalarArgs {
     void* x;
     const void* r1;
     const void* r2;
+    const int64_t* pos;     // POS: positions (position of (b,s) at pos[b*pos_sb + s*pos_ss])
+    const double* inv_freq; // POS: L/2 frequencies
+    int64_t pos_sb, pos_ss;
     int64_t S, N, D, start, L;
     int64_t pairs;          // pairs per row = L/2
     int64_t items;          // rows * pairs
@@ -575,7 +757,7 @@ struct ScalarArgs {
     int64_t t2b, t2s, t2n;
 };
 
-template <int DT, int TT, int DIR, int MODE>
+template <int DT, int TT, int DIR, int MODE, bool POS>
 __global__ void __launch_bounds__(256) rope_scalar_kernel(ScalarArgs a)
 {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -589,12 +771,22 @@ __global__ void __launch_bounds__(256) rope_scalar_kernel(ScalarArgs a)
         const int64_t s = bs % a.S;
         const int64_t b = bs / a.S;
         const int64_t xo = row * a.D + a.start;
-        const int64_t co = b * a.t1b + s * a.t1s + n * a.t1n;
-        const int64_t so = b * a.t2b + s * a.t2s + n * a.t2n;
         float xa = Store<DT>::load1(a.x, xo + j);
         float xb = Store<DT>::load1(a.x, xo + pj);
-        const float ca = Store<TT>::load1(a.r1, co + j), cb = Store<TT>::load1(a.r1, co + pj);
-        const float sa = Store<TT>::load1(a.r2, so + j), sb = Store<TT>::load1(a.r2, so + pj);
+        float ca, cb, sa, sb;
+        if constexpr (POS) {
+            // both lanes of pair q share its angle
+            const float2 t = pos_cos_sin<TT>(a.pos[b * a.pos_sb + s * a.pos_ss], a.inv_freq[q]);
+            ca = cb = t.x;
+            sa = sb = t.y;
+        } else {
+            const int64_t co = b * a.t1b + s * a.t1s + n * a.t1n;
+            const int64_t so = b * a.t2b + s * a.t2s + n * a.t2n;
+            ca = Store<TT>::load1(a.r1, co + j);
+            cb = Store<TT>::load1(a.r1, co + pj);
+            sa = Store<TT>::load1(a.r2, so + j);
+            sb = Store<TT>::load1(a.r2, so + pj);
+        }
         rotate_pair<DIR, DT != ROPE_DTYPE_F32>(xa, xb, ca, sa, cb, sb);
         Store<DT>::store1(a.x, xo + j, xa);
         Store<DT>::store1(a.x, xo + pj, xb);
@@ -610,6 +802,9 @@ struct RowArgs {
     void* x;
     const void* r1;
     const void* r2;
+    const int64_t* pos;     // POS: positions (position of (b,s) at pos[b*pos_sb + s*pos_ss])
+    const double* inv_freq; // POS: L/2 frequencies
+    int64_t pos_sb, pos_ss;
     int64_t D, start;       // row length and slice start, elements
     int64_t t1b, t1s, t1n;  // cos strides in elements (0 = broadcast)
     int64_t t2b, t2s, t2n;
@@ -620,7 +815,7 @@ struct RowArgs {
     FastDiv tpr_div, n_div, s_div;
 };
 
-template <int DT, int TT, int DIR, int MODE>
+template <int DT, int TT, int DIR, int MODE, bool POS>
 __global__ void __launch_bounds__(256) rope_rows_kernel(RowArgs a)
 {
     const uint32_t t = threadIdx.x;
@@ -637,13 +832,24 @@ __global__ void __launch_bounds__(256) rope_rows_kernel(RowArgs a)
         const int64_t xo = (int64_t)row * a.D + a.start;
         const int64_t co = b * a.t1b + s * a.t1s + n * a.t1n;
         const int64_t so = b * a.t2b + s * a.t2s + n * a.t2n;
+        const int64_t p = POS ? a.pos[b * a.pos_sb + s * a.pos_ss] : 0;
         for (uint32_t q = q0; q < a.pairs; q += a.tpr) {
             const uint32_t j = MODE == kModeIL ? 2 * q : q;               // negated-partner lane
             const uint32_t pj = MODE == kModeIL ? 2 * q + 1 : q + a.L / 2;
             float xa = Store<DT>::load1(a.x, xo + j);
             float xb = Store<DT>::load1(a.x, xo + pj);
-            const float ca = Store<TT>::load1(a.r1, co + j), cb = Store<TT>::load1(a.r1, co + pj);
-            const float sa = Store<TT>::load1(a.r2, so + j), sb = Store<TT>::load1(a.r2, so + pj);
+            float ca, cb, sa, sb;
+            if constexpr (POS) {
+                // both lanes of pair q share its angle
+                const float2 t = pos_cos_sin<TT>(p, a.inv_freq[q]);
+                ca = cb = t.x;
+                sa = sb = t.y;
+            } else {
+                ca = Store<TT>::load1(a.r1, co + j);
+                cb = Store<TT>::load1(a.r1, co + pj);
+                sa = Store<TT>::load1(a.r2, so + j);
+                sb = Store<TT>::load1(a.r2, so + pj);
+            }
             rotate_pair<DIR, DT != ROPE_DTYPE_F32>(xa, xb, ca, sa, cb, sb);
             Store<DT>::store1(a.x, xo + j, xa);
             Store<DT>::store1(a.x, xo + pj, xb);
@@ -935,23 +1141,29 @@ hipError_t launch_vec(const Plan& p, const VecArgs& a, const VecConfig& cfg, hip
     return hipLaunchKernel(fn, dim3(vec_grid(a, cfg)), dim3(threads), args, 0, stream);
 }
 
-template <int DT, int TT>
+template <int DT, int TT, bool POS>
 const void* scalar_kernel_t(int dir, int mode)
 {
     if (dir == kFwd)
-        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kFwd, kModeIL>)
-                               : reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kFwd, kModeRH>);
-    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kBwd, kModeIL>)
-                           : reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kBwd, kModeRH>);
+        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kFwd, kModeIL, POS>)
+                               : reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kFwd, kModeRH, POS>);
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kBwd, kModeIL, POS>)
+                           : reinterpret_cast<const void*>(&rope_scalar_kernel<DT, TT, kBwd, kModeRH, POS>);
+}
+
+template <int DT, int TT>
+const void* scalar_kernel_p(bool pos, int dir, int mode)
+{
+    return pos ? scalar_kernel_t<DT, TT, true>(dir, mode) : scalar_kernel_t<DT, TT, false>(dir, mode);
 }
 
 template <int DT>
-const void* scalar_kernel_dt(int tt, int dir, int mode)
+const void* scalar_kernel_dt(int tt, bool pos, int dir, int mode)
 {
     switch (tt) {
-    case ROPE_DTYPE_F32: return scalar_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode);
-    case ROPE_DTYPE_F16: return scalar_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode);
-    default: return scalar_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode);
+    case ROPE_DTYPE_F32: return scalar_kernel_p<DT, ROPE_DTYPE_F32>(pos, dir, mode);
+    case ROPE_DTYPE_F16: return scalar_kernel_p<DT, ROPE_DTYPE_F16>(pos, dir, mode);
+    default: return scalar_kernel_p<DT, ROPE_DTYPE_BF16>(pos, dir, mode);
     }
 }
 
@@ -959,6 +1171,7 @@ hipError_t launch_scalar(const Plan& p, int cus, hipStream_t stream)
 {
     ScalarArgs a;
     a.x = p.x; a.r1 = p.r1; a.r2 = p.r2;
+    a.pos = p.pos; a.inv_freq = p.inv_freq; a.pos_sb = p.pos_sb; a.pos_ss = p.pos_ss;
     a.S = p.S; a.N = p.N; a.D = p.D; a.start = p.start; a.L = p.L;
     a.pairs = p.L / 2;
     a.items = p.B * p.S * p.N * a.pairs;
@@ -969,31 +1182,37 @@ hipError_t launch_scalar(const Plan& p, int cus, hipStream_t stream)
     grid = std::max<uint64_t>(1, std::min<uint64_t>(grid, (a.items + threads - 1) / threads));
     const void* fn;
     switch (p.dtype) {
-    case ROPE_DTYPE_F32: fn = scalar_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode); break;
-    case ROPE_DTYPE_F16: fn = scalar_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode); break;
-    default: fn = scalar_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode); break;
+    case ROPE_DTYPE_F32: fn = scalar_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.pos != nullptr, p.dir, p.mode); break;
+    case ROPE_DTYPE_F16: fn = scalar_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.pos != nullptr, p.dir, p.mode); break;
+    default: fn = scalar_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.pos != nullptr, p.dir, p.mode); break;
     }
     void* args[] = {&a};
     return hipLaunchKernel(fn, dim3((uint32_t)grid), dim3(threads), args, 0, stream);
 }
 
-template <int DT, int TT>
+template <int DT, int TT, bool POS>
 const void* rows_kernel_t(int dir, int mode)
 {
     if (dir == kFwd)
-        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kFwd, kModeIL>)
-                               : reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kFwd, kModeRH>);
-    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kBwd, kModeIL>)
-                           : reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kBwd, kModeRH>);
+        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kFwd, kModeIL, POS>)
+                               : reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kFwd, kModeRH, POS>);
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kBwd, kModeIL, POS>)
+                           : reinterpret_cast<const void*>(&rope_rows_kernel<DT, TT, kBwd, kModeRH, POS>);
+}
+
+template <int DT, int TT>
+const void* rows_kernel_p(bool pos, int dir, int mode)
+{
+    return pos ? rows_kernel_t<DT, TT, true>(dir, mode) : rows_kernel_t<DT, TT, false>(dir, mode);
 }
 
 template <int DT>
-const void* rows_kernel_dt(int tt, int dir, int mode)
+const void* rows_kernel_dt(int tt, bool pos, int dir, int mode)
 {
     switch (tt) {
-    case ROPE_DTYPE_F32: return rows_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode);
-    case ROPE_DTYPE_F16: return rows_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode);
-    default: return rows_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode);
+    case ROPE_DTYPE_F32: return rows_kernel_p<DT, ROPE_DTYPE_F32>(pos, dir, mode);
+    case ROPE_DTYPE_F16: return rows_kernel_p<DT, ROPE_DTYPE_F16>(pos, dir, mode);
+    default: return rows_kernel_p<DT, ROPE_DTYPE_BF16>(pos, dir, mode);
     }
 }
 
@@ -1021,6 +1240,7 @@ hipError_t launch_rows(const Plan& p, const RowShape& r, hipStream_t stream)
 {
     RowArgs a;
     a.x = p.x; a.r1 = p.r1; a.r2 = p.r2;
+    a.pos = p.pos; a.inv_freq = p.inv_freq; a.pos_sb = p.pos_sb; a.pos_ss = p.pos_ss;
     a.D = p.D; a.start = p.start;
     a.t1b = p.t1[0]; a.t1s = p.t1[1]; a.t1n = p.t1[2];
     a.t2b = p.t2[0]; a.t2s = p.t2[1]; a.t2n = p.t2[2];
@@ -1036,9 +1256,9 @@ hipError_t launch_rows(const Plan& p, const RowShape& r, hipStream_t stream)
     a.s_div = make_fastdiv((uint32_t)p.S);
     const void* fn;
     switch (p.dtype) {
-    case ROPE_DTYPE_F32: fn = rows_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode); break;
-    case ROPE_DTYPE_F16: fn = rows_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode); break;
-    default: fn = rows_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode); break;
+    case ROPE_DTYPE_F32: fn = rows_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.pos != nullptr, p.dir, p.mode); break;
+    case ROPE_DTYPE_F16: fn = rows_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.pos != nullptr, p.dir, p.mode); break;
+    default: fn = rows_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.pos != nullptr, p.dir, p.mode); break;
     }
     void* args[] = {&a};
     return hipLaunchKernel(fn, dim3(r.grid), dim3(r.threads), args, 0, stream);
@@ -1170,6 +1390,118 @@ rope_status_t run(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
     if ((st = device_cus(&cus)) != ROPE_OK) return st;
     prepare(&L);
     hipError_t err = launch_one(L, cus, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
+    return ROPE_OK;
+}
+
+// Launch plan of the position vector kernel; false if the plan needs a
+// general kernel (alignment, sizes), as for the table vector kernel. A
+// position's heads take up to kPosLanes threads (HL head lanes of span
+// threads, kUPos heads each, in chunks past kUPos*HL heads); when they fill
+// fewer threads, a block takes kPosLanes/lanes positions, as many as its
+// LDS table holds.
+bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
+{
+    const int64_t es = p.esize;
+    if (!aligned16(p.x) || (p.D * es) % 16 || (p.start * es) % 16) return false;
+    const int64_t unit_bytes = p.mode == kModeIL ? p.L * es : (p.L / 2) * es;
+    if (unit_bytes % 16 || p.L / 2 > kPosLds) return false;
+    const int64_t kMax = (1ll << 32) - 1;
+    if (p.B * p.S * p.N * (p.D * es / 16) > kMax || p.N >= (1ll << 31) || p.B * p.S >= (1ll << 31)) return false;
+    a->x = static_cast<v4u*>(p.x);
+    a->pos = p.pos;
+    a->inv_freq = p.inv_freq;
+    a->pos_sb = p.pos_sb;
+    a->pos_ss = p.pos_ss;
+    a->row_vecs = (uint32_t)(p.D * es / 16);
+    a->start_vec = (uint32_t)(p.start * es / 16);
+    a->half_vecs = p.mode == kModeRH ? (uint32_t)((p.L / 2) * es / 16) : 0;
+    a->nvec = (uint32_t)(unit_bytes / 16);
+    a->lo_vec = a->start_vec;
+    a->span = a->nvec;
+    if (p.mode == kModeIL) {
+        VecArgs lines{};
+        lines.lo_vec = a->lo_vec;
+        lines.span = a->span;
+        cover_whole_lines(p, &lines);
+        a->lo_vec = lines.lo_vec;
+        a->span = lines.span;
+    }
+    if (a->span < 1 || a->span > 256) return false;
+    a->N = (uint32_t)p.N;
+    a->pairs = (uint32_t)(p.L / 2);
+    a->HL = (uint32_t)std::min<uint64_t>(std::max<uint32_t>(1, kPosLanes / a->span), (uint64_t)p.N);
+    a->chunks = (uint32_t)((p.N + (uint64_t)a->HL * kUPos - 1) / ((uint64_t)a->HL * kUPos));
+    a->lanes = a->span * a->HL;
+    a->P = a->lanes < kPosLanes ? std::min<uint32_t>(kPosLanes / a->lanes, kPosLds / a->pairs) : 1;
+    a->entries = a->P * a->pairs;
+    if (a->entries > (uint32_t)kPosLds) return false;
+    a->bs = (uint32_t)(p.B * p.S);
+    const uint64_t items = (((uint64_t)a->bs + a->P - 1) / a->P) * a->chunks;
+    if (items >= (1ull << 31)) return false;
+    a->items = (uint32_t)items;
+    *threads = a->P * a->lanes;
+    *grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, kMaxGridItems / *threads));
+    a->span_div = make_fastdiv(a->span);
+    a->lanes_div = make_fastdiv(a->lanes);
+    a->pairs_div = make_fastdiv(a->pairs);
+    a->chunk_div = make_fastdiv(a->chunks);
+    a->s_div = make_fastdiv((uint32_t)p.S);
+    return true;
+}
+
+template <int DT, int TT>
+const void* pos_kernel_t(int dir, int mode)
+{
+    if (dir == kFwd)
+        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, kFwd, kModeIL>)
+                               : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, kFwd, kModeRH>);
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, kBwd, kModeIL>)
+                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, kBwd, kModeRH>);
+}
+
+template <int DT>
+const void* pos_kernel_dt(int tt, int dir, int mode)
+{
+    switch (tt) {
+    case ROPE_DTYPE_F32: return pos_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode);
+    case ROPE_DTYPE_F16: return pos_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode);
+    default: return pos_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode);
+    }
+}
+
+// Tables from positions: the position vector kernel, else the row or
+// scalar kernel with their POS form.
+rope_status_t run_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype, const int64_t* positions,
+                      const int64_t positions_shape[2], const int64_t positions_strides[2], const double* inv_freq,
+                      rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2], void* stream,
+                      Direction dir)
+{
+    Plan p;
+    std::string why;
+    rope_status_t st = make_plan_pos(x, x_shape, dtype, positions, positions_shape, positions_strides, inv_freq,
+                                     table_dtype, mode, partial_slice, dir, &p, &why);
+    if (st != ROPE_OK) return set_error(st, why);
+    if (p.noop) return ROPE_OK;
+    int cus = 0;
+    if ((st = device_cus(&cus)) != ROPE_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    PosArgs a{};
+    uint32_t threads = 0, grid = 0;
+    hipError_t err;
+    if (pos_geometry(p, &a, &threads, &grid)) {
+        const void* fn;
+        switch (p.dtype) {
+        case ROPE_DTYPE_F32: fn = pos_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode); break;
+        case ROPE_DTYPE_F16: fn = pos_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode); break;
+        default: fn = pos_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode); break;
+        }
+        void* args[] = {&a};
+        err = hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, s);
+    } else {
+        RowShape rs;
+        err = rows_shape(p, &rs) ? launch_rows(p, rs, s) : launch_scalar(p, cus, s);
+    }
     if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
     return ROPE_OK;
 }
@@ -1311,6 +1643,26 @@ rope_status_t rope_partial_bwd_out(void* dx, const void* dy, const int64_t x_sha
                          mode, partial_slice, stream, rope::kBwd);
 }
 
+rope_status_t rope_partial_fwd_inplace_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                           const int64_t* positions, const int64_t positions_shape[2],
+                                           const int64_t positions_strides[2], const double* inv_freq,
+                                           rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                           void* stream)
+{
+    return rope::run_pos(x, x_shape, dtype, positions, positions_shape, positions_strides, inv_freq, table_dtype,
+                         mode, partial_slice, stream, rope::kFwd);
+}
+
+rope_status_t rope_partial_bwd_inplace_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                           const int64_t* positions, const int64_t positions_shape[2],
+                                           const int64_t positions_strides[2], const double* inv_freq,
+                                           rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                           void* stream)
+{
+    return rope::run_pos(x, x_shape, dtype, positions, positions_shape, positions_strides, inv_freq, table_dtype,
+                         mode, partial_slice, stream, rope::kBwd);
+}
+
 rope_status_t rope_partial_fwd_inplace_multi(int32_t count, void* const xs[], const int64_t x_shapes[][4],
                                              rope_dtype_t dtype, const void* r1, const int64_t r1_shape[4],
                                              const int64_t r1_strides[4], const void* r2, const int64_t r2_shape[4],
@@ -1374,6 +1726,46 @@ rope_status_t rope_partial_launch_info(const void* x, const int64_t x_shape[4], 
         info[2] = L.rs.threads;
         info[4] = L.rs.rpb;
         info[7] = L.rs.tpr;
+    } else {
+        info[0] = ROPE_KERNEL_SCALAR;
+        info[2] = 256;
+    }
+    return ROPE_OK;
+}
+
+rope_status_t rope_partial_launch_info_pos(const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                           const int64_t* positions, const int64_t positions_shape[2],
+                                           const int64_t positions_strides[2], const double* inv_freq,
+                                           rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                           int64_t info[ROPE_LAUNCH_INFO_LEN])
+{
+    if (info == nullptr) return rope::set_error(ROPE_ERR_NULLPTR, "info is NULL");
+    for (int i = 0; i < ROPE_LAUNCH_INFO_LEN; ++i) info[i] = 0;
+    rope::Plan p;
+    std::string why;
+    rope_status_t st = rope::make_plan_pos(const_cast<void*>(x), x_shape, dtype, positions, positions_shape,
+                                           positions_strides, inv_freq, table_dtype, mode, partial_slice, rope::kFwd,
+                                           &p, &why);
+    if (st != ROPE_OK) return rope::set_error(st, why);
+    if (p.noop) return ROPE_OK;
+    rope::PosArgs a{};
+    uint32_t threads = 0, grid = 0;
+    rope::RowShape rs;
+    if (rope::pos_geometry(p, &a, &threads, &grid)) {
+        info[0] = ROPE_KERNEL_VECTOR;
+        info[1] = grid;
+        info[2] = threads;
+        info[3] = rope::kUPos;
+        info[4] = a.HL;
+        info[5] = a.P;
+        info[6] = a.chunks;
+        info[7] = a.span;
+    } else if (rope::rows_shape(p, &rs)) {
+        info[0] = ROPE_KERNEL_ROWS;
+        info[1] = rs.grid;
+        info[2] = rs.threads;
+        info[4] = rs.rpb;
+        info[7] = rs.tpr;
     } else {
         info[0] = ROPE_KERNEL_SCALAR;
         info[2] = 256;

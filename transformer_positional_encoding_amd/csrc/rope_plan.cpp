@@ -207,4 +207,46 @@ rope_status_t make_plan_out(void* y, const void* x, const int64_t x_shape[4], ro
     return ROPE_OK;
 }
 
+rope_status_t make_plan_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype, const int64_t* positions,
+                            const int64_t positions_shape[2], const int64_t positions_strides[2],
+                            const double* inv_freq, rope_dtype_t table_dtype, int64_t mode,
+                            const int64_t partial_slice[2], Direction dir, Plan* plan, std::string* why)
+{
+    Plan p;
+    int64_t numel = 0;
+    rope_status_t st = check_scalars(x_shape, dtype, table_dtype, mode, partial_slice, dir, &p, &numel, why);
+    if (st != ROPE_OK) return st;
+    if (numel == 0 || p.L == 0) {
+        p.noop = true;
+        *plan = p;
+        return ROPE_OK;
+    }
+    if (x == nullptr) return fail(ROPE_ERR_NULLPTR, why, "x is NULL");
+    if (positions == nullptr) return fail(ROPE_ERR_NULLPTR, why, "positions is NULL");
+    if (inv_freq == nullptr) return fail(ROPE_ERR_NULLPTR, why, "inv_freq is NULL");
+    if (positions_shape == nullptr || positions_strides == nullptr)
+        return fail(ROPE_ERR_NULLPTR, why, "positions shape or strides is NULL");
+    if (positions_shape[0] != 1 && positions_shape[0] != x_shape[0])
+        return fail(ROPE_ERR_INVALID, why, "positions: dimension B is " + std::to_string(positions_shape[0])
+                                               + ", must be 1 or " + std::to_string(x_shape[0]));
+    if (positions_shape[1] != x_shape[1])
+        return fail(ROPE_ERR_INVALID, why, "positions: dimension S is " + std::to_string(positions_shape[1])
+                                               + ", must be " + std::to_string(x_shape[1]));
+    if (positions_strides[0] < 0 || positions_strides[1] < 0)
+        return fail(ROPE_ERR_INVALID, why, "positions: negative stride");
+    const int64_t sb = positions_shape[0] == 1 ? 0 : positions_strides[0];
+    const int64_t ss = positions_shape[1] == 1 ? 0 : positions_strides[1];
+    int64_t part_b, part_s;
+    if (!mul_ok(sb, positions_shape[0] - 1, &part_b) || !mul_ok(ss, positions_shape[1] - 1, &part_s) ||
+        part_b > std::numeric_limits<int64_t>::max() - part_s)
+        return fail(ROPE_ERR_INVALID, why, "positions: strides overflow 64-bit offsets");
+    p.x = x;
+    p.pos = positions;
+    p.inv_freq = inv_freq;
+    p.pos_sb = sb;
+    p.pos_ss = ss;
+    *plan = p;
+    return ROPE_OK;
+}
+
 }  // namespace rope

@@ -35,6 +35,13 @@ struct Plan {
     // table broadcasts (size-1 dimension). The lane stride is 1.
     int64_t t1[3] = {0, 0, 0};
     int64_t t2[3] = {0, 0, 0};
+    // Tables computed from positions (the _pos entry points) instead of
+    // read: the position of (b,s) is pos[b*pos_sb + s*pos_ss] (pos_sb is 0
+    // when one row of positions serves every batch); inv_freq holds L/2
+    // frequencies. r1 and r2 are then NULL.
+    const int64_t* pos = nullptr;
+    const double* inv_freq = nullptr;
+    int64_t pos_sb = 0, pos_ss = 0;
 };
 
 // Validate the C-ABI arguments in the documented order and fill `plan`.
@@ -56,6 +63,17 @@ rope_status_t make_plan_out(void* y, const void* x, const int64_t x_shape[4], ro
                             const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
                             rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
                             Direction dir, Plan* plan, std::string* why);
+
+// The _pos form: cos and sin come from positions and per-pair frequencies
+// (checked in place of the tables). Checks, in order: the scalar arguments
+// of make_plan; an empty tensor or slice is a no-op; NULL x, positions,
+// inv_freq, positions_shape or positions_strides; positions_shape is
+// {1 or B, S} with strides >= 0 (a size-1 dimension's stride is ignored)
+// whose offsets fit in 64 bits.
+rope_status_t make_plan_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype, const int64_t* positions,
+                            const int64_t positions_shape[2], const int64_t positions_strides[2],
+                            const double* inv_freq, rope_dtype_t table_dtype, int64_t mode,
+                            const int64_t partial_slice[2], Direction dir, Plan* plan, std::string* why);
 
 int element_size(int dtype);
 
