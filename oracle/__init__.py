@@ -38,6 +38,17 @@ _LIB_PATH = os.environ.get("ROPE_ORACLE_LIB") or _DEFAULT_LIB_PATH
 
 DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
 MODES = {"rotate_half": 0, "interleave": 1}
+
+
+def mode_code(mode) -> int:
+    """A mode name, or an int: 0 / 1 (rotate_half / interleave) or a rotary
+    coefficient c >= 2 (the slice in c parts of L/c lanes; part 2k pairs
+    with part 2k+1 lane by lane)."""
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"unknown mode {mode!r}")
+        return MODES[mode]
+    return int(mode)
 DIRECTIONS = {"fwd": 0, "bwd": 1}
 
 GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99", "-fPIC", "-shared"]
@@ -141,7 +152,7 @@ def rope_rows(x: np.ndarray, x_shape, dtype: str, r1: np.ndarray, r2: np.ndarray
         x.ctypes.data, _i64(x_shape), DTYPES[dtype],
         r1.ctypes.data, _i64(r1.shape), _i64(_table_strides(r1)),
         r2.ctypes.data, _i64(r2.shape), _i64(_table_strides(r2)),
-        DTYPES[table_dtype], MODES[mode], start, end, DIRECTIONS[direction],
+        DTYPES[table_dtype], mode_code(mode), start, end, DIRECTIONS[direction],
         rows_p, nrows)
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
@@ -182,15 +193,17 @@ def pos_tables(positions: np.ndarray, inv_freq: np.ndarray, L: int, mode: str, t
     position entry points compute in the kernel (see rope_oracle_pos_tables):
     θ = p * inv_freq[i] in double precision, cos and sin in double precision,
     rounded once to ``table_dtype``; pair i's values in lanes 2i and 2i+1
-    (interleave) or i and i + L/2 (rotate_half).
+    (interleave), i and i + L/2 (rotate_half), or, for a rotary coefficient
+    c with parts of H = L/c lanes, g*2H + k and g*2H + k + H (i = g*H + k).
 
     ``positions`` is a 2-D int64 array (Bp, S), any strides; ``inv_freq``
     holds L/2 doubles."""
     pos = np.asarray(positions)
     if pos.dtype != np.int64 or pos.ndim != 2:
         raise TypeError("positions must be a 2-D int64 array")
-    if mode not in MODES or table_dtype not in DTYPES:
-        raise ValueError("unknown mode or table type")
+    if table_dtype not in DTYPES:
+        raise ValueError("unknown table type")
+    mode = mode_code(mode)
     f = np.ascontiguousarray(inv_freq, dtype=np.float64)
     if f.size != L // 2:
         raise ValueError("inv_freq must hold L/2 values")
@@ -199,7 +212,7 @@ def pos_tables(positions: np.ndarray, inv_freq: np.ndarray, L: int, mode: str, t
     want = np.float32 if table_dtype == "f32" else np.uint16
     c = np.empty((Bp, S, 1, L), want)
     s_ = np.empty((Bp, S, 1, L), want)
-    rc = lib().rope_oracle_pos_tables(pos.ctypes.data, Bp, S, sb, ss, f.ctypes.data, int(L), MODES[mode],
+    rc = lib().rope_oracle_pos_tables(pos.ctypes.data, Bp, S, sb, ss, f.ctypes.data, int(L), mode,
                                       DTYPES[table_dtype], c.ctypes.data, s_.ctypes.data)
     if rc != 0:
         raise ValueError("oracle rejected its arguments")

@@ -17,6 +17,13 @@
  * partner and sigma(j) is the sign of the partner term:
  *   interleave  : p(j) = j xor 1,      sigma(j) = -1 for even j, +1 for odd j
  *   rotate_half : p(j) = j +- L/2,     sigma(j) = -1 for j < L/2, +1 otherwise
+ *   coefficient c (mode value c >= 2, even, dividing L): the slice splits
+ *   into c parts of H = L/c lanes, and lane i of part 2k pairs with lane i
+ *   of part 2k+1 ("ascend-transformer-boost 的 MlaPreprocessOperation",
+ *   section 2, the rotation coefficients qRotaryCoeff / kRotaryCoeff: 2 is
+ *   the half rotation; 4 and headDim are also allowed):
+ *                 p(j) = j +- H,       sigma(j) = -1 in an even part, +1 in an odd one
+ *   so c = 2 is rotate_half and c = L is interleave.
  * Forward  (P1, section 计算公式; P3, section 先搞懂RoPE):
  *   y_j  = x_j * c_j + sigma(j) * x_p(j) * s_j
  * Backward (P1, section 自动微分说明: the gradient of the forward, which is
@@ -178,14 +185,30 @@ static int64_t table_index(const int64_t shape[4], const int64_t strides[4],
     return off;
 }
 
+/* A mode value of 2 or more is a rotary coefficient: defined when it is even
+   and divides L (L = 0: nothing is rotated). */
+static int mode_defined(int mode, int64_t L)
+{
+    if (mode == ORACLE_INTERLEAVE || mode == ORACLE_ROTATE_HALF) return 1;
+    return mode >= 2 && mode % 2 == 0 && (L == 0 || L % mode == 0);
+}
+
 static int64_t partner(int mode, int64_t j, int64_t L)
 {
+    if (mode >= 2) {                                        /* parts of H lanes: 2k pairs with 2k+1 */
+        const int64_t H = L / mode;
+        return (j / H) % 2 == 0 ? j + H : j - H;
+    }
     if (mode == ORACLE_INTERLEAVE) return j ^ 1;          /* pairs (2i, 2i+1) */
     return j < L / 2 ? j + L / 2 : j - L / 2;               /* pairs (i, i+L/2) */
 }
 
 static int sigma(int mode, int64_t j, int64_t L)
 {
+    if (mode >= 2) {
+        const int64_t H = L / mode;
+        return (j / H) % 2 == 0 ? -1 : 1;                  /* the even part takes the negated partner */
+    }
     if (mode == ORACLE_INTERLEAVE) return (j % 2 == 0) ? -1 : 1;
     return j < L / 2 ? -1 : 1;
 }
@@ -213,7 +236,7 @@ int rope_oracle_rows(void* x, const int64_t x_shape[4], int dtype,
 {
     const int64_t B = x_shape[0], S = x_shape[1], N = x_shape[2], D = x_shape[3];
     const int64_t L = end - start;
-    if (mode != ORACLE_INTERLEAVE && mode != ORACLE_ROTATE_HALF) return -1;
+    if (!mode_defined(mode, L)) return -1;
     if (direction != ORACLE_FWD && direction != ORACLE_BWD) return -1;
     if (start < 0 || end < start || end > D || (L % 2) != 0) return -1;
     if (rows == NULL && nrows != B * S * N) return -1;
@@ -299,7 +322,9 @@ static float round_to_type(double v, int dtype)
  * base^(-2i/L) supplied by the caller), evaluated as the double product of
  * the position and the frequency; cos θ and sin θ in double precision,
  * rounded once to the table type. Interleave writes pair i's values to lanes
- * 2i and 2i+1, rotate_half to lanes i and i + L/2.
+ * 2i and 2i+1, rotate_half to lanes i and i + L/2, and a rotary coefficient
+ * c (parts of H = L/c lanes, numbered in lane order) to lane k of part 2g and
+ * lane k of part 2g+1 for i = g*H + k.
  *
  * positions  int64; the position of (b, s) is positions[b*stride_b + s*stride_s]
  * inv_freq   L/2 doubles
@@ -311,7 +336,7 @@ int rope_oracle_pos_tables(const int64_t* positions, int64_t Bp, int64_t S, int6
                            void* cos_out, void* sin_out)
 {
     if (L <= 0 || (L % 2) != 0 || Bp < 0 || S < 0) return -1;
-    if (mode != ORACLE_INTERLEAVE && mode != ORACLE_ROTATE_HALF) return -1;
+    if (!mode_defined(mode, L)) return -1;
     if (table_dtype != ORACLE_F32 && table_dtype != ORACLE_F16 && table_dtype != ORACLE_BF16) return -1;
     const int64_t half = L / 2;
     for (int64_t b = 0; b < Bp; ++b) {
@@ -322,8 +347,13 @@ int rope_oracle_pos_tables(const int64_t* positions, int64_t Bp, int64_t S, int6
                 const double theta = p * inv_freq[i];
                 const float c = round_to_type(cos(theta), table_dtype);
                 const float sn = round_to_type(sin(theta), table_dtype);
-                const int64_t j0 = mode == ORACLE_INTERLEAVE ? 2 * i : i;
-                const int64_t j1 = mode == ORACLE_INTERLEAVE ? 2 * i + 1 : i + half;
+                int64_t j0 = mode == ORACLE_INTERLEAVE ? 2 * i : i;
+                int64_t j1 = mode == ORACLE_INTERLEAVE ? 2 * i + 1 : i + half;
+                if (mode >= 2) {                            /* pair i = g*H + k of parts 2g, 2g+1 */
+                    const int64_t H = L / mode;
+                    j0 = (i / H) * 2 * H + i % H;
+                    j1 = j0 + H;
+                }
                 store_f(cos_out, row + j0, table_dtype, c);    /* exact: c is a value of the type */
                 store_f(cos_out, row + j1, table_dtype, c);
                 store_f(sin_out, row + j0, table_dtype, sn);

@@ -1,9 +1,10 @@
 """Planted mistakes in the oracle, on the CPU. Each mutant is rope_oracle.c
 with one plausible slip: a sign, a partner index, the lane of a table read,
 the backward's sign, the broadcast index, the slice start, the row order, a
-rounding rule, the fp16 range, the precision of the products, and in the
-tables built from positions the angle's precision, the rounding and the
-layout. Every mutant must fail at least one pin of the oracle's own test
+rounding rule, the fp16 range, the precision of the products, in the tables
+built from positions the angle's precision, the rounding and the layout,
+and in the rotary coefficient the part width, the sign, the table layout and
+the check of the coefficient. Every mutant must fail at least one pin of the oracle's own test
 files (closed forms, brute force, library conversions, the golden cases); a
 mutant that passed them all would be a mistake the pins cannot see.
 
@@ -20,7 +21,8 @@ import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PIN_FILES = [os.path.join(ROOT, "tests", f) for f in
-             ("test_oracle_golden.py", "test_oracle_pins.py", "test_oracle_pos.py", "test_oracle_converters.py")]
+             ("test_oracle_golden.py", "test_oracle_pins.py", "test_oracle_pos.py", "test_oracle_coeff.py",
+              "test_oracle_converters.py")]
 
 # (name, text in rope_oracle.c, replacement)
 MUTANTS = [
@@ -51,10 +53,16 @@ MUTANTS = [
     ("position tables rounded through fp32", "if (dtype == ORACLE_F32) return (float)v;", "if (1) return (float)v;"),
     ("position angle in single precision", "const double theta = p * inv_freq[i];",
      "const double theta = (double)((float)p * (float)inv_freq[i]);"),
-    ("rotate_half position table laid out as interleave", "const int64_t j0 = mode == ORACLE_INTERLEAVE ? 2 * i : i;",
-     "const int64_t j0 = 2 * i;"),
+    ("rotate_half position table laid out as interleave", "int64_t j0 = mode == ORACLE_INTERLEAVE ? 2 * i : i;",
+     "int64_t j0 = 2 * i;"),
     ("one-step rounding ties away from zero", "const double r = ldexp(rint(ldexp(v, -q)), q);",
      "const double r = ldexp(round(ldexp(v, -q)), q);"),
+    ("coefficient parts half as wide in the partner", "const int64_t H = L / mode;\n        return (j / H) % 2 == 0 ? j + H : j - H;",
+     "const int64_t H = L / (2 * mode);\n        return (j / H) % 2 == 0 ? j + H : j - H;"),
+    ("coefficient sign on the odd part", "return (j / H) % 2 == 0 ? -1 : 1;", "return (j / H) % 2 == 0 ? 1 : -1;"),
+    ("coefficient pair as rotate_half in the position table", "j0 = (i / H) * 2 * H + i % H;", "j0 = i;"),
+    ("odd coefficient accepted", "return mode >= 2 && mode % 2 == 0 && (L == 0 || L % mode == 0);",
+     "return mode >= 2 && (L == 0 || L % mode == 0);"),
 ]
 
 
