@@ -11,6 +11,12 @@
  *   keeps its bytes. With L = end - start and slice lane j in [0,L):
  *     interleave  (mode 1): partner p(j) = j xor 1,   sign s(j) = -1 if j even
  *     rotate_half (mode 0): partner p(j) = j +- L/2,  sign s(j) = -1 if j < L/2
+ *     rotary coefficient (mode c >= 2, even, dividing L; "ascend-transformer-
+ *     boost 的 MlaPreprocessOperation", section 2, qRotaryCoeff/kRotaryCoeff:
+ *     2 is the half rotation, 4 or headDim also allowed): the slice in c
+ *     parts of H = L/c lanes, lane k of part 2g paired with lane k of part
+ *     2g+1: p(j) = j +- H, s(j) = -1 in an even part. c = 2 is rotate_half,
+ *     c = L interleave.
  *   forward : y_j  = x_j * r1_j + s(j) * x_p(j) * r2_j
  *   backward: dx_j = g_j * r1_j - s(j) * g_p(j) * r2_p(j)
  *   (the backward is the transposed Jacobian of the forward -- the gradient
@@ -56,7 +62,8 @@ typedef enum rope_dtype {
     ROPE_DTYPE_BF16 = 2
 } rope_dtype_t;
 
-/* rotary modes; interleave keeps the integer the CANN interface gives it */
+/* rotary modes; interleave keeps the integer the CANN interface gives it.
+ * A mode value c >= 2 is a rotary coefficient (above). */
 #define ROPE_MODE_ROTATE_HALF 0
 #define ROPE_MODE_INTERLEAVE 1
 
@@ -81,7 +88,8 @@ typedef enum rope_dtype {
  *   table_dtype  storage type of r1 and r2 (any of the three, independent
  *                of dtype; the page's mixed case is 16-bit x with fp32
  *                tables).
- *   mode         ROPE_MODE_INTERLEAVE or ROPE_MODE_ROTATE_HALF.
+ *   mode         ROPE_MODE_INTERLEAVE, ROPE_MODE_ROTATE_HALF, or a rotary
+ *                coefficient c: even, >= 2, dividing L (when L > 0).
  *   partial_slice host array {start, end} or NULL, which means {0, 0}:
  *                0 <= start <= end <= D and L = end - start even.
  *   stream       hipStream_t to launch on, or NULL.

@@ -55,8 +55,12 @@ def term_scale(x: np.ndarray, c: np.ndarray, s: np.ndarray, mode: str, direction
     L = x.shape[-1]
     if mode == "interleave":
         perm = np.arange(L) ^ 1
-    else:
+    elif mode == "rotate_half":
         perm = np.concatenate([np.arange(L // 2) + L // 2, np.arange(L // 2)])
+    else:   # rotary coefficient c: parts of H = L/c lanes, part 2k paired with 2k+1
+        H = L // int(mode)
+        j = np.arange(L)
+        perm = np.where((j // H) % 2 == 0, j + H, j - H)
     sk = s if direction == "fwd" else s[..., perm]
     return np.abs(x * c) + np.abs(x[..., perm] * sk)
 

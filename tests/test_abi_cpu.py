@@ -85,8 +85,10 @@ def test_valid_arguments_pass_the_checks(dtype, table_dtype):
 
 @pytest.mark.parametrize("direction", ["check", "fwd", "bwd"])
 @pytest.mark.parametrize("kwargs,code,text", [
-    (dict(mode=2), INVALID, "mode"),
+    (dict(mode=3), INVALID, "mode"),                  # odd: neither a named mode nor a coefficient
     (dict(mode=-1), INVALID, "mode"),
+    (dict(mode=6), INVALID, "divide"),                # a coefficient must divide L = 32
+    (dict(mode=64), INVALID, "divide"),
     (dict(dtype=7), INVALID, "dtype"),
     (dict(x_shape=(2, -4, 3, 64)), INVALID, "negative"),
     (dict(x_shape=(2, 4, 3, 63), sl=(0, 32)), INVALID, "even"),
@@ -221,7 +223,8 @@ def ocall(direction="fwd", y=FAKE_Y, x=FAKE, x_shape=(2, 4, 3, 64), dtype=BF16, 
 
 @pytest.mark.parametrize("direction", ["fwd", "bwd"])
 @pytest.mark.parametrize("kwargs,code,text", [
-    (dict(mode=2), INVALID, "mode"),
+    (dict(mode=5), INVALID, "mode"),
+    (dict(mode=12), INVALID, "divide"),
     (dict(x_shape=(2, 4, 3, 63)), INVALID, "even"),
     (dict(sl=(40, 72)), INVALID, "<= D"),
     (dict(x_shape=None), NULLPTR, "x_shape"),
@@ -317,3 +320,15 @@ def test_pos_binding_checks():
     with pytest.raises(ValueError, match="frequencies"):
         rp.rope_partial_fwd_inplace_pos(x, torch.zeros(1, 4, dtype=torch.int64), rp.rope_inv_freq(16),
                                         "interleave", (0, 32))
+
+
+@pytest.mark.parametrize("mode", [2, 4, 8, 16, 32])
+def test_rotary_coefficients_that_divide_the_slice_pass_the_checks(mode):
+    """A mode value c >= 2 is a rotary coefficient: the slice (L = 32) in c
+    parts, part 2k paired with part 2k+1; any even c dividing L is valid."""
+    assert call(mode=mode) == OK
+    assert pcall("fwd", mode=mode, x=None) == NULLPTR          # past the mode checks, stops at x
+
+
+def test_rotary_coefficient_with_an_empty_slice_is_a_noop():
+    assert call("fwd", x=None, r1=None, r2=None, sl=(8, 8), mode=4) == OK

@@ -289,3 +289,33 @@ def test_pos_plan_invariants_over_random_shapes():
             assert span * HL < 128
         assert p["blocks"] == -(-(B * S) // P) * chunks
     assert seen["vector"] > 500 and seen["rows"] > 100, seen
+
+
+# ---------------------------------------------------------------- rotary coefficients
+
+@pytest.mark.parametrize("x_shape,dtype,sl,coeff,kernel,span", [
+    ((4, 4096, 128, 192), BF16, (0, 64), 4, "vector", 8),    # parts of 32 bytes: own vector, lane exchange
+    ((4, 4096, 128, 192), BF16, (0, 64), 8, "vector", 8),    # parts of one vector
+    ((4, 4096, 128, 192), BF16, (0, 64), 16, "rows", None),  # parts of 8 bytes: not whole vectors
+    ((4, 4096, 128, 192), BF16, (0, 64), 64, "vector", 8),   # c = L: interleave
+    ((2, 64, 4, 1024), F32, (0, 1024), 4, "vector", 128),    # rows wider than a wave: pair owner
+])
+def test_rotary_coefficient_plans(x_shape, dtype, sl, coeff, kernel, span):
+    st, p = plan(x_shape, dtype, sl, mode=coeff)
+    assert st == OK and p["kernel"] == kernel, p
+    if span is not None:
+        assert p["row_vectors"] == span
+
+
+def test_rotary_coefficient_two_plans_as_rotate_half():
+    for x_shape, dtype, sl in [((4, 4096, 16, 128), BF16, (0, 128)), ((16, 4096, 32, 128), BF16, (64, 128)),
+                               ((2, 64, 4, 1024), F32, (0, 1024))]:
+        assert plan(x_shape, dtype, sl, mode=2) == plan(x_shape, dtype, sl, mode=RH)
+        L = sl[1] - sl[0]
+        assert plan(x_shape, dtype, sl, mode=L) == plan(x_shape, dtype, sl, mode=IL)
+
+
+@pytest.mark.parametrize("coeff,kernel", [(4, "vector"), (8, "vector"), (16, "rows")])
+def test_rotary_coefficient_position_plans(coeff, kernel):
+    st, p = pos_plan((4, 4096, 128, 192), "bf16", (0, 64), coeff)
+    assert st == OK and p["kernel"] == kernel, p

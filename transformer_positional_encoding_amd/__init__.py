@@ -399,7 +399,10 @@ def rope_partial_fwd_inplace(x, r1, r2, rotary_mode="interleave", partial_slice=
     r1, r2: cos and sin tables, 4-D, last dim ``end-start``, other dims 1 or
     equal to x's (any strides, e.g. from ``expand``); one dtype for both,
     which may differ from x's (e.g. bf16 x with fp32 tables).
-    rotary_mode: "interleave" (pairs 2i, 2i+1) or "rotate_half" (i, i+L/2).
+    rotary_mode: "interleave" (pairs 2i, 2i+1), "rotate_half" (i, i+L/2), or
+    an int rotary coefficient c (even, dividing L): the slice in c parts,
+    lane k of part 2g paired with lane k of part 2g+1 (2: rotate_half; L:
+    interleave).
     partial_slice: (start, end) or None for the empty slice [0, 0).
     stream: a torch stream or raw hipStream_t; default torch's current stream.
     """

@@ -318,8 +318,10 @@ struct VecArgs {
     uint32_t row_vecs;      // vectors per row of x (D*esize/16)
     uint32_t start_vec;     // first slice vector within a row
     uint32_t lo_vec;        // first vector the threads of a row cover
-    uint32_t half_vecs;     // rotate_half: x vectors per half of the slice
-    uint32_t thalf;         // rotate_half: table units per half of the slice
+    uint32_t half_vecs;     // rotate_half: x vectors per half of a group (pair distance)
+    uint32_t gvec;          // rotate_half: x vectors per group (2*half_vecs; the slice unless a
+                            // rotary coefficient splits it into several groups)
+    uint32_t thalf;         // rotate_half: table units per half of a group
     uint32_t t1b, t1s, t1n; // cos strides in table units (0 = broadcast)
     uint32_t t2b, t2s, t2n; // sin strides in table units
     uint32_t N;
@@ -388,14 +390,25 @@ __device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_
     const uint32_t vs = t - q * a.span;
     const uint32_t gl = fast_div(q, a.hl_div);
     const uint32_t hl = q - gl * a.HL;
-    const uint32_t c = a.lo_vec + vs;                 // vector within the row
-    // nvec is the slice's vectors (interleave) or one half's (rotate_half)
-    const bool first = c >= a.start_vec && c - a.start_vec < a.nvec;
-    const bool second = kOwn && c >= a.start_vec + a.nvec && c - a.start_vec - a.nvec < a.nvec;
+    // nvec is the slice's vectors (interleave) or half of them (rotate_half).
+    // rotate_half pairs vector k of the first half of a group of gvec
+    // vectors with vector k of its second half; the slice is one group
+    // unless a rotary coefficient splits it.
+    const uint32_t rel = a.lo_vec + vs - a.start_vec;  // slice-relative (wraps below the slice)
+    const bool in_span = a.lo_vec + vs >= a.start_vec && rel < (kOwn ? 2 * a.nvec : a.nvec);
+    // Pair owner: the thread's unit rel is vector k = rel % half_vecs of the
+    // first half of group rel / half_vecs.
+    const uint32_t c = kPair && a.gvec != 2 * a.nvec
+                           ? a.start_vec + (rel / a.half_vecs) * a.gvec + rel % a.half_vecs
+                           : a.lo_vec + vs;           // vector within the row
+    const uint32_t grel = kOwn && a.gvec != 2 * a.nvec ? rel % a.gvec : rel;   // place in the group
+    const bool first = in_span && (!kOwn || grel < a.half_vecs);
+    const bool second = kOwn && in_span && grel >= a.half_vecs;
     const bool in_slice = first || second;
-    const uint32_t v = first ? c - a.start_vec : second ? c - a.start_vec - a.nvec : 0;  // unit (table index)
-    // Own vector: the partner vector in the other half (outside the slice,
-    // the thread's own again), and the table units of the thread's lanes
+    // unit (table index): the first-half vector of the thread's pair
+    const uint32_t v = first ? c - a.start_vec : second ? c - a.start_vec - a.half_vecs : 0;
+    // Own vector: the partner vector in the other half of the group (outside
+    // the slice, the thread's own again), and the table units of the thread's lanes
     // (cos; sin forward) and of the partner's lanes (sin backward).
     const uint32_t partner = first ? c + a.half_vecs : second ? c - a.half_vecs : c;
     const uint32_t t_own = second ? a.thalf : 0;
@@ -632,8 +645,9 @@ struct PosArgs {
     uint32_t row_vecs;       // vectors per row of x
     uint32_t start_vec;      // first slice vector within a row
     uint32_t lo_vec;         // first vector the threads of a row cover
-    uint32_t half_vecs;      // rotate_half: vectors per half of the slice
-    uint32_t nvec;           // work units per row (interleave: slice vectors; rotate_half: one half's)
+    uint32_t half_vecs;      // rotate_half: vectors per half of a group (pair distance)
+    uint32_t gvec;           // rotate_half: vectors per group (2*half_vecs)
+    uint32_t nvec;           // work units per row (interleave: slice vectors; rotate_half: half of them)
     uint32_t span;           // vectors per row the threads cover
     uint32_t HL;             // head lanes per position
     uint32_t lanes;          // threads per position: span * HL
@@ -662,6 +676,12 @@ __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
     const uint32_t c = a.lo_vec + vs;                 // vector within the row
     const bool in_slice = c >= a.start_vec && c - a.start_vec < a.nvec;
     const uint32_t v = in_slice ? c - a.start_vec : 0;
+    // rotate_half: unit v is vector v % half_vecs of the first half of group
+    // v / half_vecs (one group unless a rotary coefficient splits the slice);
+    // its lanes are pairs v*K + e either way
+    const uint32_t cx = MODE == kModeRH && a.gvec != 2 * a.nvec
+                            ? a.start_vec + (v / a.half_vecs) * a.gvec + v % a.half_vecs
+                            : c;
     // the table entry this thread evaluates first: position eq, pair ei
     const uint32_t eq = fast_div(t, a.pairs_div);
     const uint32_t ei = t - eq * a.pairs;
@@ -688,7 +708,7 @@ __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
             const uint32_t n = n0 + (uint32_t)k * a.HL;
             live[k] = pos_live && n < a.N;            // past N: re-read row N-1, store nothing
             const uint32_t nl = n < a.N ? n : a.N - 1;
-            off[k] = (gl * a.N + nl) * a.row_vecs + c;
+            off[k] = (gl * a.N + nl) * a.row_vecs + cx;
             xa[k] = load_x<true>(a.x + off[k]);
             if constexpr (MODE == kModeRH) xb[k] = load_x<true>(a.x + off[k] + a.half_vecs);
         }
@@ -751,6 +771,7 @@ struct ScalarArgs {
     const double* inv_freq; // POS: L/2 frequencies
     int64_t pos_sb, pos_ss;
     int64_t S, N, D, start, L;
+    int64_t half;           // rotate_half: lanes between a pair's lanes (L/2, or L/c for a coefficient c)
     int64_t pairs;          // pairs per row = L/2
     int64_t items;          // rows * pairs
     int64_t t1b, t1s, t1n;  // cos strides in elements (0 = broadcast)
@@ -764,8 +785,10 @@ __global__ void __launch_bounds__(256) rope_scalar_kernel(ScalarArgs a)
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.items; i += stride) {
         const int64_t row = i / a.pairs;
         const int64_t q = i - row * a.pairs;
-        const int64_t j = MODE == kModeIL ? 2 * q : q;              // negated-partner lane
-        const int64_t pj = MODE == kModeIL ? 2 * q + 1 : q + a.L / 2;
+        // negated-partner lane: interleave 2q; rotate_half lane q % half of
+        // the first half of group q / half (q itself when the slice is one group)
+        const int64_t j = MODE == kModeIL ? 2 * q : (q / a.half) * 2 * a.half + q % a.half;
+        const int64_t pj = MODE == kModeIL ? 2 * q + 1 : j + a.half;
         const int64_t n = row % a.N;
         const int64_t bs = row / a.N;
         const int64_t s = bs % a.S;
@@ -809,6 +832,8 @@ struct RowArgs {
     int64_t t1b, t1s, t1n;  // cos strides in elements (0 = broadcast)
     int64_t t2b, t2s, t2n;
     uint32_t L, pairs;      // slice length and rotation pairs per row
+    uint32_t half;          // rotate_half: lanes between a pair's lanes (L/2, or L/c for a coefficient c)
+    FastDiv half_div;
     uint32_t rows, N;
     uint32_t rpb, tpr;      // rows per block, threads per row
     uint32_t groups;        // ceil(rows / rpb)
@@ -834,8 +859,10 @@ __global__ void __launch_bounds__(256) rope_rows_kernel(RowArgs a)
         const int64_t so = b * a.t2b + s * a.t2s + n * a.t2n;
         const int64_t p = POS ? a.pos[b * a.pos_sb + s * a.pos_ss] : 0;
         for (uint32_t q = q0; q < a.pairs; q += a.tpr) {
-            const uint32_t j = MODE == kModeIL ? 2 * q : q;               // negated-partner lane
-            const uint32_t pj = MODE == kModeIL ? 2 * q + 1 : q + a.L / 2;
+            // negated-partner lane (see the scalar kernel)
+            const uint32_t g = MODE == kModeIL ? 0 : fast_div(q, a.half_div);
+            const uint32_t j = MODE == kModeIL ? 2 * q : g * 2 * a.half + (q - g * a.half);
+            const uint32_t pj = MODE == kModeIL ? 2 * q + 1 : j + a.half;
             float xa = Store<DT>::load1(a.x, xo + j);
             float xb = Store<DT>::load1(a.x, xo + pj);
             float ca, cb, sa, sb;
@@ -916,6 +943,7 @@ bool vec_geometry(const Plan& p, VecArgs* a)
     if ((p.D * es) % 16 || (p.start * es) % 16) return false;
     const int64_t unit_bytes = p.mode == kModeIL ? p.L * es : (p.L / 2) * es;
     if (unit_bytes % 16) return false;
+    if (p.mode == kModeRH && (p.half * es) % 16) return false;   // half-groups of whole vectors
     for (int k = 0; k < 3; ++k)
         if ((p.t1[k] * ts) % unit || (p.t2[k] * ts) % unit) return false;
     // 32-bit offsets: x must span fewer than 2^32 vectors and each table
@@ -937,7 +965,8 @@ bool vec_geometry(const Plan& p, VecArgs* a)
     a->row_vecs = (uint32_t)(p.D * es / 16);
     a->start_vec = (uint32_t)(p.start * es / 16);
     a->lo_vec = a->start_vec;
-    a->half_vecs = p.mode == kModeRH ? (uint32_t)((p.L / 2) * es / 16) : 0;
+    a->half_vecs = p.mode == kModeRH ? (uint32_t)(p.half * es / 16) : 0;
+    a->gvec = 2 * a->half_vecs;
     a->thalf = (uint32_t)(a->half_vecs * tv);
     a->t1b = (uint32_t)(p.t1[0] * ts / unit); a->t1s = (uint32_t)(p.t1[1] * ts / unit);
     a->t1n = (uint32_t)(p.t1[2] * ts / unit);
@@ -1173,6 +1202,7 @@ hipError_t launch_scalar(const Plan& p, int cus, hipStream_t stream)
     a.x = p.x; a.r1 = p.r1; a.r2 = p.r2;
     a.pos = p.pos; a.inv_freq = p.inv_freq; a.pos_sb = p.pos_sb; a.pos_ss = p.pos_ss;
     a.S = p.S; a.N = p.N; a.D = p.D; a.start = p.start; a.L = p.L;
+    a.half = p.half;
     a.pairs = p.L / 2;
     a.items = p.B * p.S * p.N * a.pairs;
     a.t1b = p.t1[0]; a.t1s = p.t1[1]; a.t1n = p.t1[2];
@@ -1246,6 +1276,8 @@ hipError_t launch_rows(const Plan& p, const RowShape& r, hipStream_t stream)
     a.t2b = p.t2[0]; a.t2s = p.t2[1]; a.t2n = p.t2[2];
     a.L = (uint32_t)p.L;
     a.pairs = (uint32_t)(p.L / 2);
+    a.half = (uint32_t)std::max<int64_t>(1, p.half);
+    a.half_div = make_fastdiv(a.half);
     a.rows = (uint32_t)(p.B * p.S * p.N);
     a.N = (uint32_t)p.N;
     a.rpb = r.rpb;
@@ -1286,7 +1318,7 @@ struct Launch {
 bool use_rh_own(const Plan& p, VecArgs* a)
 {
     const int64_t es = p.esize;
-    const int64_t half_bytes = (p.L / 2) * es;
+    const int64_t half_bytes = p.half * es;
     if ((p.start * es) % 128 == 0 && half_bytes % 128 == 0) return false;   // halves on whole lines
     VecArgs own = *a;
     own.span = 2 * own.nvec;   // the whole slice
@@ -1415,7 +1447,9 @@ bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
     a->pos_ss = p.pos_ss;
     a->row_vecs = (uint32_t)(p.D * es / 16);
     a->start_vec = (uint32_t)(p.start * es / 16);
-    a->half_vecs = p.mode == kModeRH ? (uint32_t)((p.L / 2) * es / 16) : 0;
+    if (p.mode == kModeRH && (p.half * es) % 16) return false;   // half-groups of whole vectors
+    a->half_vecs = p.mode == kModeRH ? (uint32_t)(p.half * es / 16) : 0;
+    a->gvec = 2 * a->half_vecs;
     a->nvec = (uint32_t)(unit_bytes / 16);
     a->lo_vec = a->start_vec;
     a->span = a->nvec;

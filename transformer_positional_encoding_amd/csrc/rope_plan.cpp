@@ -73,8 +73,9 @@ rope_status_t check_scalars(const int64_t x_shape[4], rope_dtype_t dtype, rope_d
 {
     if (x_shape == nullptr)
         return fail(ROPE_ERR_NULLPTR, why, "x_shape is NULL");
-    if (mode != ROPE_MODE_INTERLEAVE && mode != ROPE_MODE_ROTATE_HALF)
-        return fail(ROPE_ERR_INVALID, why, "mode must be 0 (rotate_half) or 1 (interleave)");
+    if (mode != ROPE_MODE_INTERLEAVE && mode != ROPE_MODE_ROTATE_HALF && !(mode >= 2 && mode % 2 == 0))
+        return fail(ROPE_ERR_INVALID, why,
+                    "mode must be 0 (rotate_half), 1 (interleave) or an even rotary coefficient >= 2");
     if (element_size(dtype) == 0)
         return fail(ROPE_ERR_INVALID, why, "unknown dtype");
     if (element_size(table_dtype) == 0)
@@ -99,6 +100,8 @@ rope_status_t check_scalars(const int64_t x_shape[4], rope_dtype_t dtype, rope_d
     const int64_t L = end - start;
     if (L % 2 != 0)
         return fail(ROPE_ERR_INVALID, why, "slice length end-start must be even");
+    if (mode >= 2 && L % mode != 0)
+        return fail(ROPE_ERR_INVALID, why, "the rotary coefficient must divide the slice length end-start");
     int64_t numel = 1;
     for (int k = 0; k < 4; ++k) {
         if (!mul_ok(numel, x_shape[k], &numel))
@@ -110,7 +113,18 @@ rope_status_t check_scalars(const int64_t x_shape[4], rope_dtype_t dtype, rope_d
 
     p->B = x_shape[0]; p->S = x_shape[1]; p->N = x_shape[2]; p->D = D;
     p->start = start; p->L = L;
-    p->dtype = dtype; p->tdtype = table_dtype; p->mode = (int)mode; p->dir = dir;
+    p->dtype = dtype; p->tdtype = table_dtype; p->dir = dir;
+    // A rotary coefficient c pairs lanes H = L/c apart within groups of 2H
+    // lanes: H = 1 is interleave and H = L/2 rotate_half. The plan keeps the
+    // two schemes, with `half` the pair distance.
+    if (mode == ROPE_MODE_INTERLEAVE) {
+        p->mode = ROPE_MODE_INTERLEAVE; p->half = 1;
+    } else if (mode == ROPE_MODE_ROTATE_HALF) {
+        p->mode = ROPE_MODE_ROTATE_HALF; p->half = L / 2;
+    } else {
+        p->half = L / mode;
+        p->mode = p->half == 1 ? ROPE_MODE_INTERLEAVE : ROPE_MODE_ROTATE_HALF;
+    }
     p->esize = element_size(dtype);
     p->tesize = element_size(table_dtype);
     p->bytes = bytes;

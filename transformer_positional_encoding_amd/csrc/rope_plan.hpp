@@ -20,7 +20,9 @@ struct Plan {
     int64_t start = 0, L = 0;
     int dtype = 0;           // rope_dtype_t of x
     int tdtype = 0;          // rope_dtype_t of r1 and r2
-    int mode = 0;            // ROPE_MODE_*
+    int mode = 0;            // ROPE_MODE_INTERLEAVE or ROPE_MODE_ROTATE_HALF (a coefficient maps to one)
+    int64_t half = 0;        // lanes between a pair's two lanes: 1 (interleave), L/2 (rotate_half) or L/c;
+                             // rotate_half pairs are (g*2*half + k, g*2*half + k + half)
     int dir = kFwd;
     int esize = 0;           // bytes per element of x
     int tesize = 0;          // bytes per element of the tables

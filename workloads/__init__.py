@@ -41,7 +41,7 @@ class Workload:
     x_shapes: tuple
     dtype: str
     partial_slice: tuple
-    mode: str
+    mode: object                    # "interleave", "rotate_half" or an int rotary coefficient
     table_shape: tuple
     seed: int
     std: float = 1.0
@@ -112,6 +112,9 @@ WORKLOADS: dict[str, Workload] = {
               seed=11, directions=("fwd", "bwd"), table_kind="random",
               note="single-op example shape, random BS1D tables"),
 }
+# MLA's rope part with the page's coefficient 4 (two groups of two 16-lane parts).
+WORKLOADS["c3_coeff4"] = replace(WORKLOADS["c3"], name="c3_coeff4", mode=4, seed=15,
+                                 note="MLA-style rope on lanes [0,64) of 192, rotary coefficient 4, bf16")
 WORKLOADS["c4_f32"] = replace(WORKLOADS["c4"], name="c4_f32", dtype="f32",
                               note="long-context shard, fp32 rerun")
 # The page's mixed-precision case at the long-context shape: bf16 dx, fp32 tables.
@@ -192,7 +195,15 @@ def rope_angles(w: Workload) -> np.ndarray:
     theta = positions(w).astype(np.float64)[:, :, None] * inv_freq[None, None, :]
     if w.mode == "interleave":
         return np.repeat(theta, 2, axis=-1)        # lanes 2i and 2i+1 share θ_i
-    return np.concatenate([theta, theta], axis=-1)  # lanes i and i+L/2 share θ_i
+    if w.mode == "rotate_half":
+        return np.concatenate([theta, theta], axis=-1)  # lanes i and i+L/2 share θ_i
+    # rotary coefficient c: pair i = g*H + k (H = L/c) at lanes g*2H + k and g*2H + k + H
+    H = L // int(w.mode)
+    out = np.empty(theta.shape[:2] + (L,))
+    for i in range(half):
+        g, k = divmod(i, H)
+        out[..., g * 2 * H + k] = out[..., g * 2 * H + k + H] = theta[..., i]
+    return out
 
 
 def make_tables(w: Workload) -> tuple[torch.Tensor, torch.Tensor]:
