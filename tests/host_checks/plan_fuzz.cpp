@@ -86,7 +86,9 @@ int main()
         }
         const int dtype = (int)(next() % 4) - (next() % 8 == 0);       // mostly valid, sometimes -1 or 3
         const int tdtype = (int)(next() % 4) - (next() % 8 == 0);
-        const int64_t mode = (next() % 8) ? (int64_t)(next() % 2) : pick();
+        // mostly the named modes, sometimes a small even coefficient, sometimes anything
+        const uint64_t mk = next() % 16;
+        const int64_t mode = mk < 12 ? (int64_t)(next() % 2) : mk < 15 ? 2 * (int64_t)(1 + next() % 40) : pick();
         const bool null_x = next() % 16 == 0, null_shape = next() % 64 == 0, null_slice = next() % 32 == 0;
         rope::Plan p;
         std::string why;
@@ -121,6 +123,12 @@ int main()
             }
             good = good && span <= (i128)std::numeric_limits<int64_t>::max();
         }
+        // the mode: a named mode, or an even coefficient dividing L, kept as
+        // the pair distance of the interleave or rotate_half scheme
+        if (mode == ROPE_MODE_INTERLEAVE) good = good && p.mode == ROPE_MODE_INTERLEAVE && p.half == 1;
+        else if (mode == ROPE_MODE_ROTATE_HALF) good = good && p.mode == ROPE_MODE_ROTATE_HALF && p.half == p.L / 2;
+        else good = good && mode >= 2 && mode % 2 == 0 && p.L % mode == 0 && p.half == p.L / mode &&
+                    p.mode == (p.half == 1 ? ROPE_MODE_INTERLEAVE : ROPE_MODE_ROTATE_HALF);
         if (!good) ++bad;
     }
     // The out-of-place form: the same arguments with an input pointer that is
