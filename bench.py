@@ -445,8 +445,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the operation shards over B, S or heads with no exchange; see DESIGN.md)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(rows are independent, so the operation shards over B, S or heads with no exchange "
+              "between GPUs)", file=sys.stderr)
         return 2
 
     import torch

@@ -52,7 +52,7 @@ typedef enum rope_status {
     ROPE_OK = 0,
     ROPE_ERR_NULLPTR = 1,      /* a required pointer is NULL                   */
     ROPE_ERR_INVALID = 2,      /* an argument breaks the constraints below     */
-    ROPE_ERR_UNSUPPORTED = 3,  /* a valid combination this build does not run  */
+    ROPE_ERR_UNSUPPORTED = 3,  /* a valid combination the library does not run */
     ROPE_ERR_RUNTIME = 4       /* the HIP runtime reported an error            */
 } rope_status_t;
 
