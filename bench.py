@@ -337,35 +337,46 @@ def bench_out_of_place(name: str, reps: int, stream) -> dict:
     return res
 
 
-def bench_positions(name: str, reps: int, stream) -> dict:
+def bench_positions(name: str, reps: int, stream, out: bool = False) -> dict:
     """The position entry points on a workload: cos and sin computed in the
     kernel from the workload's positions (one int64 per (b,s)) and its L/2
     double frequencies, against the table call on the same x. Bytes per
-    launch: the slice read and written once, the positions and frequencies
-    read once (no tables). Rotating copies as for the table call."""
+    launch: the slice read and written once (out of place: x read whole and
+    the result written whole), the positions and frequencies read once (no
+    tables). Rotating copies as for the table call."""
     import torch
 
     import transformer_positional_encoding_amd as rp
     import workloads as W
     w = W.WORKLOADS[name]
-    ncopy = rotating_copies(w)
+    B, S, N, D = w.x_shapes[0]
+    es = W.ESIZE[w.dtype]
+    whole = B * S * N * D * es
+    ncopy = max(1, min(4, -(-(3 * MALL_BYTES) // whole))) if out else rotating_copies(w)
     xs = [W.make_x(w).to("cuda")]
     xs += [xs[0].clone() for _ in range(ncopy - 1)]
+    ys = [torch.empty_like(xs[0]) for _ in range(ncopy)] if out else xs
     pos = torch.from_numpy(W.positions(w)).to("cuda")
     f = rp.rope_inv_freq(w.L, w.base, "cuda")
     r1, r2 = (t.to("cuda") for t in W.make_tables(w))
-    B, S, N, _ = w.x_shapes[0]
-    es = W.ESIZE[w.dtype]
-    nbytes = 2 * B * S * N * w.L * es + pos.numel() * 8 + f.numel() * 8
+    moved = 2 * whole if out else 2 * B * S * N * w.L * es
+    nbytes = moved + pos.numel() * 8 + f.numel() * 8
+    table_bytes = moved + (w.algorithmic_bytes() - 2 * B * S * N * w.L * es)
     tdt = W.TORCH_DTYPES[w.tdtype]
-    res = {"workload": name, "note": w.note + ", tables computed from positions", "dtype": w.dtype,
-           "table_dtype": w.tdtype, "rotating_copies": ncopy, "bytes_per_launch": nbytes,
-           "table_call_bytes_per_launch": w.algorithmic_bytes(), "kernels": {}}
+    res = {"workload": name, "note": w.note + (", out of place" if out else "") + ", tables computed from positions",
+           "dtype": w.dtype, "table_dtype": w.tdtype, "rotating_copies": ncopy, "bytes_per_launch": nbytes,
+           "table_call_bytes_per_launch": table_bytes, "kernels": {}}
     for _ in range(2):   # two rounds, the second kept (as for the table call)
         for d in ("bwd", "fwd"):
-            pos_fn = rp.rope_partial_bwd_inplace_pos if d == "bwd" else rp.rope_partial_fwd_inplace_pos
-            with_pos = [(pos_fn, (xs[i], pos, f, w.mode, w.partial_slice, tdt)) for i in range(ncopy)]
-            with_tables = [(launch_fn(d), (xs[i], r1, r2, w.mode, w.partial_slice)) for i in range(ncopy)]
+            if out:
+                pos_fn = rp.rope_partial_bwd_out_pos if d == "bwd" else rp.rope_partial_fwd_out_pos
+                tab_fn = rp.rope_partial_bwd_out if d == "bwd" else rp.rope_partial_fwd_out
+                with_pos = [(pos_fn, (ys[i], xs[i], pos, f, w.mode, w.partial_slice, tdt)) for i in range(ncopy)]
+                with_tables = [(tab_fn, (ys[i], xs[i], r1, r2, w.mode, w.partial_slice)) for i in range(ncopy)]
+            else:
+                pos_fn = rp.rope_partial_bwd_inplace_pos if d == "bwd" else rp.rope_partial_fwd_inplace_pos
+                with_pos = [(pos_fn, (xs[i], pos, f, w.mode, w.partial_slice, tdt)) for i in range(ncopy)]
+                with_tables = [(launch_fn(d), (xs[i], r1, r2, w.mode, w.partial_slice)) for i in range(ncopy)]
             time_launches(with_pos, max(10, reps // 2), stream)
             t_pos = time_launches(with_pos, reps, stream)
             time_launches(with_tables, max(10, reps // 2), stream)
@@ -373,13 +384,13 @@ def bench_positions(name: str, reps: int, stream) -> dict:
             res["kernels"][d] = {"positions_us": round(t_pos * 1e6, 3), "GBps": round(nbytes / t_pos / 1e9, 1),
                                  "frac_of_peak": round(nbytes / t_pos / 1e9 / PEAK_GBPS, 4),
                                  "table_call_us": round(t_tab * 1e6, 3)}
-            tr = committed_traffic(name + ":pos", d)
+            tr = committed_traffic(name + (":outpos" if out else ":pos"), d)
             if tr is not None:
                 res["kernels"][d]["hbm_bytes_per_launch"] = tr["hbm_bytes_per_launch"]
                 res["kernels"][d]["hbm_GBps"] = round(tr["hbm_bytes_per_launch"] / t_pos / 1e9, 1)
                 res["kernels"][d]["hbm_frac_of_peak"] = round(
                     tr["hbm_bytes_per_launch"] / t_pos / 1e9 / PEAK_GBPS, 4)
-    del xs
+    del xs, ys
     torch.cuda.empty_cache()
     return res
 
@@ -404,7 +415,10 @@ def profile_target(name: str, reps: int, out_of_place: bool = False, positions: 
     f = rp.rope_inv_freq(w.L, w.base, "cuda") if positions else None
     for d in dirs:
         for i in range(reps):
-            if positions:
+            if positions and out_of_place:
+                (rp.rope_partial_fwd_out_pos if d == "fwd" else rp.rope_partial_bwd_out_pos)(
+                    y, xs[0], pos, f, w.mode, w.partial_slice, W.TORCH_DTYPES[w.tdtype])
+            elif positions:
                 (rp.rope_partial_fwd_inplace_pos if d == "fwd" else rp.rope_partial_bwd_inplace_pos)(
                     xs[i % ncopy], pos, f, w.mode, w.partial_slice, W.TORCH_DTYPES[w.tdtype])
             elif out_of_place:
@@ -428,11 +442,11 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
-    ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out,c4:pos,c2_s4096:pos,c2_s4096,"
-                                      "rh_64of128,rh_32of128,c3_coeff4",
+    ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out,c4:pos,c2_s4096:pos,c4:outpos,"
+                                      "c2_s4096,rh_64of128,rh_32of128,c3_coeff4",
                     help="other workloads measured in the same run (reported under 'other_workloads'); "
                          "NAME:out measures the out-of-place entry points on NAME, NAME:pos the position "
-                         "entry points")
+                         "entry points, NAME:outpos the out-of-place position entry points")
     ap.add_argument("--reps", type=int, default=50, help="launches per per-kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle budget: whole steps repeated to fill about this many seconds")
@@ -472,6 +486,9 @@ def main() -> int:
             continue
         if name.endswith(":pos"):
             others.append(bench_positions(name[:-4], max(10, args.reps // 2), stream))
+            continue
+        if name.endswith(":outpos"):
+            others.append(bench_positions(name[:-7], max(10, args.reps // 2), stream, out=True))
             continue
         if len(W.WORKLOADS[name].x_shapes) > 1:
             others.append(bench_multi(name, max(10, args.reps // 2), stream))

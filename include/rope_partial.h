@@ -257,8 +257,39 @@ ROPE_API rope_status_t rope_partial_launch_info(
     int64_t info[ROPE_LAUNCH_INFO_LEN]);
 
 /*
- * rope_partial_launch_info_pos -- the launch plan of a position call
- * (rope_partial_fwd_inplace_pos / _bwd_inplace_pos) with these arguments,
+ * rope_partial_fwd_out_pos / rope_partial_bwd_out_pos -- the position forms
+ * out of place: y receives x with its slice rotated, cos and sin computed
+ * from positions exactly as rope_partial_fwd_inplace_pos does, and x is left
+ * unchanged. y == x is the in-place call. An empty slice copies x to y.
+ *
+ *   y, x         device buffers of B*S*N*D elements of `dtype`, contiguous
+ *                BSND; y is written, x is read. With both 16-byte aligned
+ *                one kernel reads x and writes y in one pass; otherwise x is
+ *                copied to y and y is rotated in place.
+ *   Other arguments are those of rope_partial_fwd_inplace_pos.
+ *
+ * Checks, in this order: the scalar arguments; an empty tensor returns
+ * ROPE_OK at once; NULL y or x (ROPE_ERR_NULLPTR); y and x overlapping
+ * without being the same buffer (ROPE_ERR_INVALID); an empty slice copies;
+ * then the checks of positions, positions_shape, positions_strides and
+ * inv_freq of the in-place form. Asynchronous on `stream`; nothing is
+ * allocated.
+ */
+ROPE_API rope_status_t rope_partial_fwd_out_pos(
+    void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+ROPE_API rope_status_t rope_partial_bwd_out_pos(
+    void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+/*
+ * rope_partial_launch_info_pos -- the launch plan of an in-place position
+ * call (rope_partial_fwd_inplace_pos / _bwd_inplace_pos) with these arguments,
  * for tests and profiling. Runs that call's checks first and returns their
  * status; on ROPE_OK, info (caller-owned, ROPE_LAUNCH_INFO_LEN elements)
  * receives:

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
                  "rope_last_error", "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi",
                  "rope_partial_check", "rope_partial_launch_info", "rope_partial_fwd_out",
                  "rope_partial_bwd_out", "rope_partial_fwd_inplace_pos", "rope_partial_bwd_inplace_pos",
-                 "rope_partial_launch_info_pos"):
+                 "rope_partial_launch_info_pos", "rope_partial_fwd_out_pos", "rope_partial_bwd_out_pos"):
         assert want in names
 
 
@@ -332,3 +332,35 @@ def test_rotary_coefficients_that_divide_the_slice_pass_the_checks(mode):
 
 def test_rotary_coefficient_with_an_empty_slice_is_a_noop():
     assert call("fwd", x=None, r1=None, r2=None, sl=(8, 8), mode=4) == OK
+
+
+def opcall(direction="fwd", y=FAKE_Y, x=FAKE, x_shape=(2, 4, 3, 64), dtype=BF16, pos=FAKE, pos_shape=(1, 4),
+           pos_strides=(4, 1), inv_freq=FAKE, mode=IL, sl=(0, 32)):
+    """The out-of-place position entry points, only with arguments that
+    fail validation or are no-ops."""
+    return rp.raw_out_pos_call(direction, y, x, x_shape, dtype, pos, pos_shape, pos_strides, inv_freq, dtype,
+                               mode, sl, None)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("kwargs,code,text", [
+    (dict(mode=3), INVALID, "mode"),
+    (dict(y=None), NULLPTR, "y is NULL"),
+    (dict(x=None), NULLPTR, "x is NULL"),
+    (dict(x=FAKE_Y + 2), INVALID, "overlap"),
+    (dict(pos=None), NULLPTR, "positions is NULL"),
+    (dict(inv_freq=None), NULLPTR, "inv_freq is NULL"),
+    (dict(pos_shape=(2, 5)), INVALID, "dimension S"),
+    (dict(y=None, sl=(8, 8)), NULLPTR, "y is NULL"),      # an empty slice still copies x to y
+])
+def test_out_of_place_position_argument_errors(direction, kwargs, code, text):
+    assert opcall(direction, **kwargs) == code
+    assert text in rp.last_error()
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_out_of_place_position_noops(direction):
+    # an empty tensor: nothing is read, not even y or x
+    assert opcall(direction, y=None, x=None, pos=None, inv_freq=None, x_shape=(0, 4, 3, 64)) == OK
+    # y == x with an empty slice: nothing to do
+    assert opcall(direction, y=FAKE, x=FAKE, pos=None, inv_freq=None, sl=(8, 8)) == OK

@@ -93,3 +93,40 @@ def test_multi_tensor_call_replays_like_eager():
         rp.rope_partial_fwd_inplace(ke, r1d, r2d, w.mode, w.partial_slice)
         torch.cuda.synchronize()
         assert torch.equal(_bits(qg), _bits(qe)) and torch.equal(_bits(kg), _bits(ke)), f"replay {rep}"
+
+
+@pytest.mark.parametrize("mode,sl,shape", [("interleave", (32, 96), (4, 64, 8, 128)), (4, (0, 64), (2, 64, 16, 192)),
+                                           ("rotate_half", (4, 44), (2, 16, 3, 48))],
+                         ids=["interleave-vector", "coeff4-vector", "rotate_half-rows"])
+def test_position_calls_replay_like_eager(mode, sl, shape):
+    """The position entry points (cos and sin computed in the kernel) and a
+    rotary coefficient, captured and replayed: the vector kernel and the row
+    kernel's position form."""
+    B, S = shape[0], shape[1]
+    g0 = torch.Generator().manual_seed(41)
+    x0 = torch.randn(shape, generator=g0).to(torch.bfloat16)
+    pos = (torch.randint(0, 60000, (B, 1), generator=g0) + torch.arange(S)[None, :]).to(DEV)
+    f = rp.rope_inv_freq(sl[1] - sl[0], 500000.0, DEV)
+    announce(f"graph positions {mode} {shape} {sl}")
+
+    def calls(x):
+        rp.rope_partial_bwd_inplace_pos(x, pos, f, mode, sl)
+        rp.rope_partial_fwd_inplace_pos(x, pos, f, mode, sl, table_dtype=torch.float32)
+
+    warm = x0.to(DEV)
+    calls(warm)
+    torch.cuda.synchronize()
+    xg, xe = x0.to(DEV), x0.to(DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls(xg)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(xg), _bits(x0.to(DEV))), "capture must not run the kernels"
+    other = torch.randn(1 << 20, device=DEV)
+    for rep in range(4):
+        g.replay()
+        calls(xe)
+        other.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(xg), _bits(xe)), f"replay {rep} differs from the eager calls"
+        assert not torch.equal(_bits(xg), _bits(x0.to(DEV))), "the calls must change x"

@@ -198,3 +198,19 @@ def test_pos_scalar_kernel_past_two_to_the_31_rows():
     assert info["exact"] == info["n"]
     del x, xv, pos
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("tdtype", ["bf16", "f32"])
+def test_pos_large_and_negative_positions(tdtype):
+    """Positions far beyond any context length and negative ones (the angle
+    reaches 10^12 rad, so both sides reduce it over many periods), against
+    the oracle's tables of the same positions."""
+    shape, sl, mode = (2, 64, 4, 128), (0, 128), "rotate_half"
+    x = _rand(shape, "bf16", 81)
+    g = torch.Generator().manual_seed(82)
+    mag = torch.randint(0, 2 ** 40, (2, 64), generator=g, dtype=torch.int64)
+    sign = torch.where(torch.rand((2, 64), generator=g) < 0.5, -1, 1)
+    pos = mag * sign
+    pos[0, :4] = torch.tensor([0, -1, 2 ** 40, -(2 ** 40)])
+    f = rp.rope_inv_freq(128, 10000.0)
+    run_pos_and_check(x, pos, f, mode, sl, "fwd", tdtype, "large and negative positions")

@@ -22,6 +22,8 @@ __all__ = [
     "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi", "MULTI_MAX", "rope_partial_check",
     "rope_partial_launch_info", "rope_partial_fwd_out", "rope_partial_bwd_out", "partial_rotary_mul",
     "rope_partial_fwd_inplace_pos", "rope_partial_bwd_inplace_pos", "rope_inv_freq",
+    "rope_partial_fwd_out_pos", "rope_partial_bwd_out_pos", "partial_rotary_mul_pos",
+    "inplace_partial_rotary_mul_pos",
     "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
     "ROPE_ERR_UNSUPPORTED", "ROPE_ERR_RUNTIME", "MODES", "DTYPE_CODES",
 ]
@@ -80,6 +82,10 @@ def library() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = pos_args + [ctypes.c_void_p]
+        for name in ("rope_partial_fwd_out_pos", "rope_partial_bwd_out_pos"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_void_p] + pos_args + [ctypes.c_void_p]
         L.rope_partial_launch_info_pos.restype = ctypes.c_int
         L.rope_partial_launch_info_pos.argtypes = pos_args + [ctypes.POINTER(ctypes.c_int64)]
         for name in ("rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi"):
@@ -153,6 +159,19 @@ def raw_pos_call(direction: str, x_ptr, x_shape, dtype: int, pos_ptr, pos_shape,
     pt = None if pos_strides is None else _I64x2(int(pos_strides[0]), int(pos_strides[1]))
     return fn(x_ptr, _arr4(x_shape), int(dtype), pos_ptr, ps, pt, inv_freq_ptr, int(table_dtype), int(mode), sl,
               stream)
+
+
+def raw_out_pos_call(direction: str, y_ptr, x_ptr, x_shape, dtype: int, pos_ptr, pos_shape, pos_strides,
+                     inv_freq_ptr, table_dtype: int, mode: int, partial_slice, stream=None) -> int:
+    """Call rope_partial_{fwd,bwd}_out_pos with plain integers and sequences
+    (None = NULL); returns the status code without raising."""
+    L = library()
+    fn = L.rope_partial_fwd_out_pos if direction == "fwd" else L.rope_partial_bwd_out_pos
+    sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
+    ps = None if pos_shape is None else _I64x2(int(pos_shape[0]), int(pos_shape[1]))
+    pt = None if pos_strides is None else _I64x2(int(pos_strides[0]), int(pos_strides[1]))
+    return fn(y_ptr, x_ptr, _arr4(x_shape), int(dtype), pos_ptr, ps, pt, inv_freq_ptr, int(table_dtype),
+              int(mode), sl, stream)
 
 
 def raw_check(x_ptr, x_shape, dtype: int, r1_ptr, r1_shape, r1_strides, r2_ptr, r2_shape, r2_strides,
@@ -439,13 +458,16 @@ def rope_inv_freq(L: int, base: float = 10000.0, device=None):
     return torch.pow(torch.tensor(float(base), dtype=torch.float64), -2.0 * i / L).to(device)
 
 
-def _call_pos(direction, x, positions, inv_freq, mode, partial_slice, table_dtype, stream):
+def _call_pos(direction, x, positions, inv_freq, mode, partial_slice, table_dtype, stream, y=None):
+    """The position entry points: in place on x, or (y given) out of place
+    from x into y."""
     import torch
     if isinstance(mode, str):
         if mode not in MODES:
             raise ValueError(f"rotary_mode must be one of {sorted(MODES)}")
         mode = MODES[mode]
-    for name, t in (("x", x), ("positions", positions), ("inv_freq", inv_freq)):
+    for name, t in (("x", x), ("positions", positions), ("inv_freq", inv_freq)) + ((("out", y),) if y is not None
+                                                                                   else ()):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
     if x.dim() != 4:
@@ -456,6 +478,14 @@ def _call_pos(direction, x, positions, inv_freq, mode, partial_slice, table_dtyp
         raise ValueError("inv_freq must be a contiguous 1-D float64 tensor")
     if not x.is_contiguous():
         raise ValueError("x must be contiguous (BSND); non-contiguous tensors are not supported")
+    if y is not None:
+        if y.shape != x.shape or y.dtype != x.dtype:
+            raise ValueError(f"out must match x in shape and dtype: {tuple(y.shape)} {y.dtype} vs "
+                             f"{tuple(x.shape)} {x.dtype}")
+        if not y.is_contiguous():
+            raise ValueError("out must be contiguous (BSND)")
+        if x.numel() and not (x.is_cuda and y.is_cuda and y.device == x.device):
+            raise ValueError("x and out must be GPU tensors on one device")
     sl = (0, 0) if partial_slice is None else (int(partial_slice[0]), int(partial_slice[1]))
     if x.numel() and sl[1] > sl[0]:
         if inv_freq.numel() != (sl[1] - sl[0]) // 2:
@@ -478,9 +508,15 @@ def _call_pos(direction, x, positions, inv_freq, mode, partial_slice, table_dtyp
         handle = getattr(stream, "cuda_stream", stream)
     switch = x.is_cuda and dev.index != torch.cuda.current_device()
     with torch.cuda.device(dev) if switch else _nullcontext():
-        st = raw_pos_call(direction, x.data_ptr() or None, tuple(x.shape), _dtype_code(x),
-                          positions.data_ptr() or None, tuple(positions.shape), tuple(positions.stride()),
-                          inv_freq.data_ptr() or None, tdt, mode, partial_slice, handle)
+        if y is None:
+            st = raw_pos_call(direction, x.data_ptr() or None, tuple(x.shape), _dtype_code(x),
+                              positions.data_ptr() or None, tuple(positions.shape), tuple(positions.stride()),
+                              inv_freq.data_ptr() or None, tdt, mode, partial_slice, handle)
+        else:
+            st = raw_out_pos_call(direction, y.data_ptr() or None, x.data_ptr() or None, tuple(x.shape),
+                                  _dtype_code(x), positions.data_ptr() or None, tuple(positions.shape),
+                                  tuple(positions.stride()), inv_freq.data_ptr() or None, tdt, mode,
+                                  partial_slice, handle)
     if st != ROPE_OK:
         raise RopeError(st, last_error())
 
@@ -505,6 +541,21 @@ def rope_partial_bwd_inplace_pos(dx, positions, inv_freq, rotary_mode="interleav
     """Backward of :func:`rope_partial_fwd_inplace_pos`, in place on the
     incoming gradient."""
     _call_pos("bwd", dx, positions, inv_freq, rotary_mode, partial_slice, table_dtype, stream)
+
+
+def rope_partial_fwd_out_pos(out, x, positions, inv_freq, rotary_mode="interleave", partial_slice=None,
+                             table_dtype=None, stream=None) -> None:
+    """Out-of-place :func:`rope_partial_fwd_inplace_pos`: ``out`` receives x
+    with its slice rotated; x is left unchanged."""
+    _call_pos("fwd", x, positions, inv_freq, rotary_mode, partial_slice, table_dtype, stream, y=out)
+
+
+def rope_partial_bwd_out_pos(dx, dy, positions, inv_freq, rotary_mode="interleave", partial_slice=None,
+                             table_dtype=None, stream=None) -> None:
+    """Out-of-place backward of the position form: ``dx`` receives the
+    gradient with respect to x for the incoming gradient ``dy``, which is
+    left unchanged."""
+    _call_pos("bwd", dy, positions, inv_freq, rotary_mode, partial_slice, table_dtype, stream, y=dx)
 
 
 def rope_partial_fwd_inplace_multi(xs, r1, r2, rotary_mode="interleave", partial_slice=None, stream=None) -> None:
@@ -638,3 +689,103 @@ def partial_rotary_mul(x, r1, r2, rotary_mode="interleave", partial_slice=None):
             _FN_OUT = _out_of_place_function()
         return _FN_OUT.apply(x, r1, r2, rotary_mode, partial_slice)
     return _rotated_copy(x, r1, r2, rotary_mode, partial_slice)
+
+
+# ---------------------------------------------------------------- autograd, cos/sin from positions
+
+def _grad_x_pos(grad, positions, inv_freq, rotary_mode, partial_slice, table_dtype):
+    """The gradient with respect to x for ``grad`` in a new tensor, cos and
+    sin computed from the positions (see _grad_x: grad is never modified)."""
+    import torch
+    if grad.is_contiguous():
+        dx = torch.empty_like(grad, memory_format=torch.contiguous_format)
+        rope_partial_bwd_out_pos(dx, grad, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+        return dx
+    dx = grad.contiguous()
+    rope_partial_bwd_inplace_pos(dx, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+    return dx
+
+
+def _pos_functions():
+    import torch
+
+    def _save(ctx, positions, inv_freq, rotary_mode, partial_slice, table_dtype):
+        ctx.save_for_backward(positions, inv_freq)
+        ctx.rotary_mode = rotary_mode
+        ctx.partial_slice = None if partial_slice is None else tuple(int(v) for v in partial_slice)
+        ctx.table_dtype = table_dtype
+
+    def _backward(ctx, grad):
+        positions, inv_freq = ctx.saved_tensors
+        dx = _grad_x_pos(grad, positions, inv_freq, ctx.rotary_mode, ctx.partial_slice, ctx.table_dtype)
+        return dx, None, None, None, None, None
+
+    class InplacePartialRotaryMulPosFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, positions, inv_freq, rotary_mode, partial_slice, table_dtype):
+            rope_partial_fwd_inplace_pos(x, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+            ctx.mark_dirty(x)
+            _save(ctx, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+            return x
+
+        backward = staticmethod(_backward)
+
+    class PartialRotaryMulPosFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, positions, inv_freq, rotary_mode, partial_slice, table_dtype):
+            y = _rotated_copy_pos(x, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+            _save(ctx, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+            return y
+
+        backward = staticmethod(_backward)
+
+    return InplacePartialRotaryMulPosFn, PartialRotaryMulPosFn
+
+
+def _rotated_copy_pos(x, positions, inv_freq, rotary_mode, partial_slice, table_dtype):
+    import torch
+    xc = x.contiguous()
+    if xc.numel() and xc.data_ptr() != x.data_ptr():
+        rope_partial_fwd_inplace_pos(xc, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+        return xc
+    y = torch.empty_like(xc, memory_format=torch.contiguous_format)
+    rope_partial_fwd_out_pos(y, xc, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+    return y
+
+
+_POS_FNS = None
+
+
+def inplace_partial_rotary_mul_pos(x, positions, inv_freq, rotary_mode="interleave", partial_slice=None,
+                                   table_dtype=None) -> None:
+    """:func:`inplace_partial_rotary_mul` with cos and sin computed in the
+    kernel from positions (see :func:`rope_partial_fwd_inplace_pos`).
+    positions and inv_freq never get gradients; x must not be a leaf tensor
+    that requires grad."""
+    import torch
+    global _POS_FNS
+    if torch.is_grad_enabled() and x.requires_grad:
+        if x.is_leaf:
+            raise RuntimeError("inplace_partial_rotary_mul_pos: x is a leaf tensor that requires grad; "
+                               "rotate a non-leaf copy of it (e.g. y = x * 1.0)")
+        if _POS_FNS is None:
+            _POS_FNS = _pos_functions()
+        _POS_FNS[0].apply(x, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+        return None
+    rope_partial_fwd_inplace_pos(x, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+    return None
+
+
+def partial_rotary_mul_pos(x, positions, inv_freq, rotary_mode="interleave", partial_slice=None,
+                           table_dtype=None):
+    """:func:`partial_rotary_mul` with cos and sin computed in the kernel from
+    positions: returns a new tensor, x is not modified, and the backward is
+    the out-of-place position backward. positions and inv_freq never get
+    gradients."""
+    import torch
+    global _POS_FNS
+    if torch.is_grad_enabled() and x.requires_grad:
+        if _POS_FNS is None:
+            _POS_FNS = _pos_functions()
+        return _POS_FNS[1].apply(x, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+    return _rotated_copy_pos(x, positions, inv_freq, rotary_mode, partial_slice, table_dtype)

@@ -638,7 +638,8 @@ constexpr int kPosLds = ROPE_D_LIMIT / 2;    // (cos, sin) entries per block
 constexpr uint32_t kPosLanes = 128;          // threads a position's heads fill before a block takes more positions
 
 struct PosArgs {
-    v4u* x;
+    v4u* x;                  // the tensor written (in place: also read)
+    const v4u* src;          // out of place: the tensor read
     const int64_t* pos;      // position of (b,s) at pos[b*pos_sb + s*pos_ss]
     const double* inv_freq;  // L/2 frequencies
     int64_t pos_sb, pos_ss;
@@ -755,6 +756,112 @@ __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
             }
         }
         __syncthreads();   // the next item rewrites cs
+    }
+}
+
+// Out of place with the tables computed from positions: x (the output)
+// receives src with the slice rotated, in one pass over whole rows. A thread
+// covers one vector of a row: outside the slice it copies it, inside it
+// rotates it (interleave: the pairs within the vector; rotate_half: with the
+// partner vector, the matching one in the other half of its group, loaded
+// from src as well) and stores exactly that vector, with one instruction.
+// Blocks, positions, loads and the LDS entries are those of the in-place
+// kernel above.
+template <int DT, int TT, int DIR, int MODE>
+__global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
+{
+    __shared__ float2 cs[kPosLds];
+    constexpr int K = Store<DT>::kLanes;
+    constexpr int U = kUPos;
+    constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
+    const uint32_t t = threadIdx.x;
+    const uint32_t pp = fast_div(t, a.lanes_div);
+    const uint32_t r = t - pp * a.lanes;
+    const uint32_t hl = fast_div(r, a.span_div);
+    const uint32_t c = r - hl * a.span;               // vector within the row (the threads cover the row)
+    const uint32_t rel = c - a.start_vec;             // slice-relative (wraps below the slice)
+    const bool in_slice = c >= a.start_vec && rel < (MODE == kModeIL ? a.nvec : 2 * a.nvec);
+    // rotate_half: the group of the thread's vector, its place in the group,
+    // whether it lies in the first half, its partner, and the first-half
+    // unit whose lanes are pairs unit*K + e
+    const uint32_t grp = MODE == kModeRH && in_slice ? rel / a.gvec : 0;
+    const uint32_t grel = rel - grp * a.gvec;
+    const bool first = MODE == kModeIL || grel < a.half_vecs;
+    const uint32_t partner = MODE == kModeRH && in_slice ? (first ? c + a.half_vecs : c - a.half_vecs) : c;
+    const uint32_t unit = grp * a.half_vecs + (first ? grel : grel - a.half_vecs);
+    // the partner term is subtracted on the first half forward, on the second backward
+    const bool neg = DIR == kFwd ? first : !first;
+    const uint32_t eq = fast_div(t, a.pairs_div);
+    const uint32_t ei = t - eq * a.pairs;
+    for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
+        const uint32_t grpb = fast_div(w, a.chunk_div);
+        const uint32_t chunk = w - grpb * a.chunks;
+        const uint32_t g0 = grpb * a.P;
+        const bool fill = t < a.entries && g0 + eq < a.bs;
+        const uint32_t gq = min(g0 + eq, a.bs - 1);
+        const uint32_t bq = fast_div(gq, a.s_div);
+        const int64_t p0 = a.pos[(int64_t)bq * a.pos_sb + (int64_t)(gq - bq * a.s_div.d) * a.pos_ss];
+        const double f0 = a.inv_freq[ei];
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t g = g0 + pp;
+        const bool pos_live = g < a.bs;
+        const uint32_t gl = pos_live ? g : a.bs - 1;
+        const uint32_t n0 = chunk * (a.HL * U) + hl;
+        v4u xa[U], xb[U];
+        uint32_t off[U];
+        bool live[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t n = n0 + (uint32_t)k * a.HL;
+            live[k] = pos_live && n < a.N;
+            const uint32_t nl = n < a.N ? n : a.N - 1;
+            const uint32_t row = (gl * a.N + nl) * a.row_vecs;
+            off[k] = row + c;
+            xa[k] = load_x<true>(a.src + off[k]);
+            if constexpr (MODE == kModeRH) xb[k] = load_x<true>(a.src + row + partner);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
+        for (uint32_t e = t + blockDim.x; e < a.entries; e += blockDim.x) {
+            const uint32_t q = fast_div(e, a.pairs_div);
+            const uint32_t ge = g0 + q;
+            if (ge >= a.bs) break;
+            const uint32_t be = fast_div(ge, a.s_div);
+            const int64_t pe = a.pos[(int64_t)be * a.pos_sb + (int64_t)(ge - be * a.s_div.d) * a.pos_ss];
+            cs[e] = pos_cos_sin<TT>(pe, a.inv_freq[e - q * a.pairs]);
+        }
+        __syncthreads();
+        const uint32_t base = pp * a.pairs;
+        float C[K], S[K];
+#pragma unroll
+        for (int e = 0; e < K; ++e) {
+            const uint32_t i = MODE == kModeIL ? (rel * K + e) / 2 : unit * K + e;
+            const float2 q = cs[in_slice && pos_live ? base + i : 0];
+            C[e] = q.x;
+            S[e] = q.y;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (!live[k]) continue;
+            v4u y = xa[k];
+            if (in_slice) {
+                Lanes<DT> X;
+                X.unpack(xa[k]);
+                if constexpr (MODE == kModeIL) {
+#pragma unroll
+                    for (int i = 0; i < K; i += 2)
+                        rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C[i], S[i], C[i + 1], S[i + 1]);
+                } else {
+                    Lanes<DT> Pv;
+                    Pv.unpack(xb[k]);
+#pragma unroll
+                    for (int i = 0; i < K; ++i) X.v[i] = rotate_own<kUnfused>(X.v[i], Pv.v[i], C[i], S[i], neg);
+                }
+                y = X.pack();
+            }
+            store_x<true>(a.x + off[k], y);
+        }
+        __syncthreads();
     }
 }
 
@@ -1432,35 +1539,35 @@ rope_status_t run(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
 // threads, kUPos heads each, in chunks past kUPos*HL heads); when they fill
 // fewer threads, a block takes kPosLanes/lanes positions, as many as its
 // LDS table holds.
-bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
+// The vector geometry both position kernels share: alignment, sizes, the
+// slice in vectors and the rotate_half groups. out: also src aligned.
+static bool pos_vectors(const Plan& p, PosArgs* a, bool out)
 {
     const int64_t es = p.esize;
-    if (!aligned16(p.x) || (p.D * es) % 16 || (p.start * es) % 16) return false;
+    if (!aligned16(p.x) || (out && !aligned16(p.src)) || (p.D * es) % 16 || (p.start * es) % 16) return false;
     const int64_t unit_bytes = p.mode == kModeIL ? p.L * es : (p.L / 2) * es;
     if (unit_bytes % 16 || p.L / 2 > kPosLds) return false;
+    if (p.mode == kModeRH && (p.half * es) % 16) return false;   // half-groups of whole vectors
     const int64_t kMax = (1ll << 32) - 1;
     if (p.B * p.S * p.N * (p.D * es / 16) > kMax || p.N >= (1ll << 31) || p.B * p.S >= (1ll << 31)) return false;
     a->x = static_cast<v4u*>(p.x);
+    a->src = static_cast<const v4u*>(p.src);
     a->pos = p.pos;
     a->inv_freq = p.inv_freq;
     a->pos_sb = p.pos_sb;
     a->pos_ss = p.pos_ss;
     a->row_vecs = (uint32_t)(p.D * es / 16);
     a->start_vec = (uint32_t)(p.start * es / 16);
-    if (p.mode == kModeRH && (p.half * es) % 16) return false;   // half-groups of whole vectors
     a->half_vecs = p.mode == kModeRH ? (uint32_t)(p.half * es / 16) : 0;
     a->gvec = 2 * a->half_vecs;
     a->nvec = (uint32_t)(unit_bytes / 16);
-    a->lo_vec = a->start_vec;
-    a->span = a->nvec;
-    if (p.mode == kModeIL) {
-        VecArgs lines{};
-        lines.lo_vec = a->lo_vec;
-        lines.span = a->span;
-        cover_whole_lines(p, &lines);
-        a->lo_vec = lines.lo_vec;
-        a->span = lines.span;
-    }
+    return true;
+}
+
+// Heads, positions per block and the grid, once the vectors a row's
+// threads cover (lo_vec, span) are set.
+static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
+{
     if (a->span < 1 || a->span > 256) return false;
     a->N = (uint32_t)p.N;
     a->pairs = (uint32_t)(p.L / 2);
@@ -1484,23 +1591,63 @@ bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
     return true;
 }
 
-template <int DT, int TT>
-const void* pos_kernel_t(int dir, int mode)
+bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
 {
-    if (dir == kFwd)
-        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, kFwd, kModeIL>)
-                               : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, kFwd, kModeRH>);
-    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, kBwd, kModeIL>)
-                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, kBwd, kModeRH>);
+    if (!pos_vectors(p, a, false)) return false;
+    a->lo_vec = a->start_vec;
+    a->span = a->nvec;
+    if (p.mode == kModeIL) {
+        VecArgs lines{};
+        lines.lo_vec = a->lo_vec;
+        lines.span = a->span;
+        cover_whole_lines(p, &lines);
+        a->lo_vec = lines.lo_vec;
+        a->span = lines.span;
+    }
+    return pos_launch_shape(p, a, threads, grid);
+}
+
+// Out of place: the threads of a row cover all of its vectors.
+bool pos_geometry_out(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
+{
+    if (!pos_vectors(p, a, true)) return false;
+    a->lo_vec = 0;
+    a->span = a->row_vecs;
+    return pos_launch_shape(p, a, threads, grid);
+}
+
+template <int DT, int TT, int DIR>
+const void* pos_kernel_d(int mode, bool out)
+{
+    if (out)
+        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeIL>)
+                               : reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeRH>);
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL>)
+                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH>);
+}
+
+template <int DT, int TT>
+const void* pos_kernel_t(int dir, int mode, bool out)
+{
+    return dir == kFwd ? pos_kernel_d<DT, TT, kFwd>(mode, out) : pos_kernel_d<DT, TT, kBwd>(mode, out);
 }
 
 template <int DT>
-const void* pos_kernel_dt(int tt, int dir, int mode)
+const void* pos_kernel_dt(int tt, int dir, int mode, bool out)
 {
     switch (tt) {
-    case ROPE_DTYPE_F32: return pos_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode);
-    case ROPE_DTYPE_F16: return pos_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode);
-    default: return pos_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode);
+    case ROPE_DTYPE_F32: return pos_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode, out);
+    case ROPE_DTYPE_F16: return pos_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode, out);
+    default: return pos_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode, out);
+    }
+}
+
+const void* pos_kernel(const Plan& p, bool out)
+{
+    switch (p.dtype) {
+    case ROPE_DTYPE_F32: return pos_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode, out);
+    case ROPE_DTYPE_F16: return pos_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode, out);
+    default: return pos_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode, out);
     }
 }
 
@@ -1524,17 +1671,58 @@ rope_status_t run_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype, con
     uint32_t threads = 0, grid = 0;
     hipError_t err;
     if (pos_geometry(p, &a, &threads, &grid)) {
-        const void* fn;
-        switch (p.dtype) {
-        case ROPE_DTYPE_F32: fn = pos_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode); break;
-        case ROPE_DTYPE_F16: fn = pos_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode); break;
-        default: fn = pos_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode); break;
-        }
         void* args[] = {&a};
-        err = hipLaunchKernel(fn, dim3(grid), dim3(threads), args, 0, s);
+        err = hipLaunchKernel(pos_kernel(p, false), dim3(grid), dim3(threads), args, 0, s);
     } else {
         RowShape rs;
         err = rows_shape(p, &rs) ? launch_rows(p, rs, s) : launch_scalar(p, cus, s);
+    }
+    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
+    return ROPE_OK;
+}
+
+// Out of place from positions: the position out-of-place kernel, else a
+// device copy of x into y and the in-place position plan on y.
+rope_status_t run_out_pos(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                          const int64_t* positions, const int64_t positions_shape[2],
+                          const int64_t positions_strides[2], const double* inv_freq, rope_dtype_t table_dtype,
+                          int64_t mode, const int64_t partial_slice[2], void* stream, Direction dir)
+{
+    Plan p;
+    std::string why;
+    rope_status_t st = make_plan_out_pos(y, x, x_shape, dtype, positions, positions_shape, positions_strides,
+                                         inv_freq, table_dtype, mode, partial_slice, dir, &p, &why);
+    if (st != ROPE_OK) return set_error(st, why);
+    if (p.noop) return ROPE_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (p.copy_only) {
+        err = hipMemcpyAsync(p.x, p.src, (size_t)p.bytes, hipMemcpyDeviceToDevice, s);
+        if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("copy: ") + hipGetErrorString(err));
+        return ROPE_OK;
+    }
+    if (p.src == nullptr)   // y == x: the in-place call
+        return run_pos(p.x, x_shape, dtype, positions, positions_shape, positions_strides, inv_freq, table_dtype,
+                       mode, partial_slice, stream, dir);
+    int cus = 0;
+    if ((st = device_cus(&cus)) != ROPE_OK) return st;
+    PosArgs a{};
+    uint32_t threads = 0, grid = 0;
+    if (pos_geometry_out(p, &a, &threads, &grid)) {
+        void* args[] = {&a};
+        err = hipLaunchKernel(pos_kernel(p, true), dim3(grid), dim3(threads), args, 0, s);
+    } else {
+        err = hipMemcpyAsync(p.x, p.src, (size_t)p.bytes, hipMemcpyDeviceToDevice, s);
+        if (err == hipSuccess) {
+            PosArgs b{};
+            if (pos_geometry(p, &b, &threads, &grid)) {
+                void* args[] = {&b};
+                err = hipLaunchKernel(pos_kernel(p, false), dim3(grid), dim3(threads), args, 0, s);
+            } else {
+                RowShape rs;
+                err = rows_shape(p, &rs) ? launch_rows(p, rs, s) : launch_scalar(p, cus, s);
+            }
+        }
     }
     if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
     return ROPE_OK;
@@ -1695,6 +1883,26 @@ rope_status_t rope_partial_bwd_inplace_pos(void* x, const int64_t x_shape[4], ro
 {
     return rope::run_pos(x, x_shape, dtype, positions, positions_shape, positions_strides, inv_freq, table_dtype,
                          mode, partial_slice, stream, rope::kBwd);
+}
+
+rope_status_t rope_partial_fwd_out_pos(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                       const int64_t* positions, const int64_t positions_shape[2],
+                                       const int64_t positions_strides[2], const double* inv_freq,
+                                       rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                       void* stream)
+{
+    return rope::run_out_pos(y, x, x_shape, dtype, positions, positions_shape, positions_strides, inv_freq,
+                             table_dtype, mode, partial_slice, stream, rope::kFwd);
+}
+
+rope_status_t rope_partial_bwd_out_pos(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                       const int64_t* positions, const int64_t positions_shape[2],
+                                       const int64_t positions_strides[2], const double* inv_freq,
+                                       rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                       void* stream)
+{
+    return rope::run_out_pos(y, x, x_shape, dtype, positions, positions_shape, positions_strides, inv_freq,
+                             table_dtype, mode, partial_slice, stream, rope::kBwd);
 }
 
 rope_status_t rope_partial_fwd_inplace_multi(int32_t count, void* const xs[], const int64_t x_shapes[][4],

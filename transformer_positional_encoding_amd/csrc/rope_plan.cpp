@@ -221,21 +221,13 @@ rope_status_t make_plan_out(void* y, const void* x, const int64_t x_shape[4], ro
     return ROPE_OK;
 }
 
-rope_status_t make_plan_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype, const int64_t* positions,
-                            const int64_t positions_shape[2], const int64_t positions_strides[2],
-                            const double* inv_freq, rope_dtype_t table_dtype, int64_t mode,
-                            const int64_t partial_slice[2], Direction dir, Plan* plan, std::string* why)
+// The positions and frequencies of the _pos entry points (after the no-op
+// test): pointers, the {1 or B, S} shape, non-negative strides and 64-bit
+// offsets. Fills p's position fields.
+static rope_status_t check_positions(const int64_t x_shape[4], const int64_t* positions,
+                                     const int64_t positions_shape[2], const int64_t positions_strides[2],
+                                     const double* inv_freq, Plan* p, std::string* why)
 {
-    Plan p;
-    int64_t numel = 0;
-    rope_status_t st = check_scalars(x_shape, dtype, table_dtype, mode, partial_slice, dir, &p, &numel, why);
-    if (st != ROPE_OK) return st;
-    if (numel == 0 || p.L == 0) {
-        p.noop = true;
-        *plan = p;
-        return ROPE_OK;
-    }
-    if (x == nullptr) return fail(ROPE_ERR_NULLPTR, why, "x is NULL");
     if (positions == nullptr) return fail(ROPE_ERR_NULLPTR, why, "positions is NULL");
     if (inv_freq == nullptr) return fail(ROPE_ERR_NULLPTR, why, "inv_freq is NULL");
     if (positions_shape == nullptr || positions_strides == nullptr)
@@ -254,11 +246,66 @@ rope_status_t make_plan_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtyp
     if (!mul_ok(sb, positions_shape[0] - 1, &part_b) || !mul_ok(ss, positions_shape[1] - 1, &part_s) ||
         part_b > std::numeric_limits<int64_t>::max() - part_s)
         return fail(ROPE_ERR_INVALID, why, "positions: strides overflow 64-bit offsets");
+    p->pos = positions;
+    p->inv_freq = inv_freq;
+    p->pos_sb = sb;
+    p->pos_ss = ss;
+    return ROPE_OK;
+}
+
+rope_status_t make_plan_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype, const int64_t* positions,
+                            const int64_t positions_shape[2], const int64_t positions_strides[2],
+                            const double* inv_freq, rope_dtype_t table_dtype, int64_t mode,
+                            const int64_t partial_slice[2], Direction dir, Plan* plan, std::string* why)
+{
+    Plan p;
+    int64_t numel = 0;
+    rope_status_t st = check_scalars(x_shape, dtype, table_dtype, mode, partial_slice, dir, &p, &numel, why);
+    if (st != ROPE_OK) return st;
+    if (numel == 0 || p.L == 0) {
+        p.noop = true;
+        *plan = p;
+        return ROPE_OK;
+    }
+    if (x == nullptr) return fail(ROPE_ERR_NULLPTR, why, "x is NULL");
+    st = check_positions(x_shape, positions, positions_shape, positions_strides, inv_freq, &p, why);
+    if (st != ROPE_OK) return st;
     p.x = x;
-    p.pos = positions;
-    p.inv_freq = inv_freq;
-    p.pos_sb = sb;
-    p.pos_ss = ss;
+    *plan = p;
+    return ROPE_OK;
+}
+
+rope_status_t make_plan_out_pos(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                const int64_t* positions, const int64_t positions_shape[2],
+                                const int64_t positions_strides[2], const double* inv_freq,
+                                rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                Direction dir, Plan* plan, std::string* why)
+{
+    Plan p;
+    int64_t numel = 0;
+    rope_status_t st = check_scalars(x_shape, dtype, table_dtype, mode, partial_slice, dir, &p, &numel, why);
+    if (st != ROPE_OK) return st;
+    if (numel == 0) {
+        p.noop = true;
+        *plan = p;
+        return ROPE_OK;
+    }
+    if (y == nullptr) return fail(ROPE_ERR_NULLPTR, why, "y is NULL");
+    if (x == nullptr) return fail(ROPE_ERR_NULLPTR, why, "x is NULL");
+    const uintptr_t yu = reinterpret_cast<uintptr_t>(y), xu = reinterpret_cast<uintptr_t>(x);
+    const uint64_t nb = (uint64_t)p.bytes;
+    const bool same = yu == xu;
+    if (!same && ((uint64_t)(yu - xu) < nb || (uint64_t)(xu - yu) < nb))
+        return fail(ROPE_ERR_INVALID, why, "y and x overlap without being the same buffer");
+    if (p.L == 0) {
+        p.noop = same;
+        p.copy_only = !same;
+    } else {
+        st = check_positions(x_shape, positions, positions_shape, positions_strides, inv_freq, &p, why);
+        if (st != ROPE_OK) return st;
+    }
+    p.x = y;
+    p.src = same ? nullptr : x;
     *plan = p;
     return ROPE_OK;
 }

@@ -77,6 +77,15 @@ rope_status_t make_plan_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtyp
                             const double* inv_freq, rope_dtype_t table_dtype, int64_t mode,
                             const int64_t partial_slice[2], Direction dir, Plan* plan, std::string* why);
 
+// Out of place from positions: the checks of make_plan_out with those of
+// make_plan_pos in place of the table checks (positions, frequencies,
+// shape and strides), in that order.
+rope_status_t make_plan_out_pos(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+                                const int64_t* positions, const int64_t positions_shape[2],
+                                const int64_t positions_strides[2], const double* inv_freq,
+                                rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                Direction dir, Plan* plan, std::string* why);
+
 int element_size(int dtype);
 
 }  // namespace rope
