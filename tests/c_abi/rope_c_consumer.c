@@ -235,13 +235,25 @@ static void run_pos_case(const char* name, const int64_t xs[4], int dtype, int t
     rope_status_t st = rope_partial_launch_info_pos(dx, xs, dtype, (const int64_t*)dpos, pshape, pstrides,
                                                     (const double*)df, tdtype, mode, sl, info);
     if (st != ROPE_OK || info[0] == ROPE_KERNEL_NONE) FAIL("%s: launch plan status %d", name, st);
+    /* out of place first (x must stay unchanged), then in place */
+    void* dy = NULL;
+    HIP_OK(hipMalloc(&dy, xb));
+    st = (dir == 0 ? rope_partial_fwd_out_pos : rope_partial_bwd_out_pos)(
+        dy, dx, xs, dtype, (const int64_t*)dpos, pshape, pstrides, (const double*)df, tdtype, mode, sl, NULL);
+    if (st != ROPE_OK) FAIL("%s, out of place: status %d (%s)", name, st, rope_last_error());
+    HIP_OK(hipStreamSynchronize(NULL));
+    void* out = malloc(xb);
+    HIP_OK(hipMemcpy(out, dy, xb, hipMemcpyDeviceToHost));
+    compare("  out of place", out, want, dtype, n, 4.0);
+    HIP_OK(hipMemcpy(out, dx, xb, hipMemcpyDeviceToHost));
+    if (memcmp(out, x, xb) != 0) FAIL("%s, out of place: the input changed", name);
     st = (dir == 0 ? rope_partial_fwd_inplace_pos : rope_partial_bwd_inplace_pos)(
         dx, xs, dtype, (const int64_t*)dpos, pshape, pstrides, (const double*)df, tdtype, mode, sl, NULL);
     if (st != ROPE_OK) FAIL("%s: status %d (%s)", name, st, rope_last_error());
     HIP_OK(hipStreamSynchronize(NULL));
-    void* out = malloc(xb);
     HIP_OK(hipMemcpy(out, dx, xb, hipMemcpyDeviceToHost));
     compare(name, out, want, dtype, n, 4.0);
+    HIP_OK(hipFree(dy));
     HIP_OK(hipFree(dx)); HIP_OK(hipFree(dpos)); HIP_OK(hipFree(df));
     free(x); free(pos); free(f); free(c); free(sn); free(want); free(out);
 }
@@ -313,6 +325,10 @@ static void check_errors(void)
                NULL, xs, ROPE_DTYPE_F16, NULL, NULL, NULL, NULL, ROPE_DTYPE_F16, ROPE_MODE_ROTATE_HALF, empty_sl,
                NULL),
            ROPE_OK, NULL);
+    expect("out of place positions, overlapping", rope_partial_fwd_out_pos(
+               (char*)fake + 2, fake, xs, ROPE_DTYPE_BF16, fake_pos, ps, pst, fake_f, ROPE_DTYPE_BF16,
+               ROPE_MODE_INTERLEAVE, sl, NULL),
+           ROPE_ERR_INVALID, "overlap");
     expect("position launch plan", rope_partial_launch_info_pos(fake, xs, ROPE_DTYPE_BF16, fake_pos, ps, pst,
                                                                 fake_f, ROPE_DTYPE_BF16, ROPE_MODE_INTERLEAVE, sl,
                                                                 info),

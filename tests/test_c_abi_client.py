@@ -25,7 +25,7 @@ def test_c_client_argument_checks_without_a_gpu():
     """Errors, no-ops and the launch plan return before any HIP call."""
     out = _run("--no-gpu", timeout=60)
     assert "ROPE_ERR_NULLPTR" in out and "ROPE_ERR_INVALID" in out
-    assert sum(line.startswith("ok   ") for line in out.splitlines()) == 14
+    assert sum(line.startswith("ok   ") for line in out.splitlines()) == 15
 
 
 @pytest.mark.gpu

@@ -636,6 +636,15 @@ __device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
 constexpr int kUPos = 2;
 constexpr int kPosLds = ROPE_D_LIMIT / 2;    // (cos, sin) entries per block
 constexpr uint32_t kPosLanes = 128;          // threads a position's heads fill before a block takes more positions
+// The out-of-place position kernel's heads per thread and threads per
+// position, by mode. Measured on MI355X (cold data; the (16,8192,32,128)
+// shard's lanes [32,96), the MLA-style slice, a whole rotate_half head and
+// its second half), over 1, 2 or 4 heads per thread in blocks of 64, 128 or
+// 256 threads: interleave was fastest with 2 heads in 128 threads (326 and
+// 257 us), rotate_half with 4 heads in 64 threads (165 and 164 us, the table
+// path's times; 172 and 167 us with the interleave shape).
+constexpr int pos_out_heads(int mode) { return mode == kModeIL ? 2 : 4; }
+constexpr uint32_t pos_out_lanes(int mode) { return mode == kModeIL ? 128 : 64; }
 
 struct PosArgs {
     v4u* x;                  // the tensor written (in place: also read)
@@ -763,16 +772,18 @@ __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
 // receives src with the slice rotated, in one pass over whole rows. A thread
 // covers one vector of a row: outside the slice it copies it, inside it
 // rotates it (interleave: the pairs within the vector; rotate_half: with the
-// partner vector, the matching one in the other half of its group, loaded
-// from src as well) and stores exactly that vector, with one instruction.
-// Blocks, positions, loads and the LDS entries are those of the in-place
-// kernel above.
-template <int DT, int TT, int DIR, int MODE>
+// partner vector, the matching one in the other half of its group) and
+// stores exactly that vector, with one instruction. XCHG: the partner vector
+// comes from the lane that holds it (ds_bpermute; rows of 64/k vectors, so a
+// row's threads never straddle a wave); otherwise it is loaded from src as
+// well. Blocks, positions, loads and the LDS entries are those of the
+// in-place kernel above.
+template <int DT, int TT, int DIR, int MODE, bool XCHG>
 __global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
 {
     __shared__ float2 cs[kPosLds];
     constexpr int K = Store<DT>::kLanes;
-    constexpr int U = kUPos;
+    constexpr int U = pos_out_heads(MODE);
     constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
     const uint32_t t = threadIdx.x;
     const uint32_t pp = fast_div(t, a.lanes_div);
@@ -791,6 +802,9 @@ __global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
     const uint32_t unit = grp * a.half_vecs + (first ? grel : grel - a.half_vecs);
     // the partner term is subtracted on the first half forward, on the second backward
     const bool neg = DIR == kFwd ? first : !first;
+    // XCHG: byte address of the partner's lane for ds_bpermute (the lane
+    // itself outside the slice)
+    const int xlane = XCHG ? (int)((t & 63u) + (partner - c)) * 4 : 0;
     const uint32_t eq = fast_div(t, a.pairs_div);
     const uint32_t ei = t - eq * a.pairs;
     for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
@@ -818,9 +832,14 @@ __global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
             const uint32_t row = (gl * a.N + nl) * a.row_vecs;
             off[k] = row + c;
             xa[k] = load_x<true>(a.src + off[k]);
-            if constexpr (MODE == kModeRH) xb[k] = load_x<true>(a.src + row + partner);
+            if constexpr (MODE == kModeRH && !XCHG) xb[k] = load_x<true>(a.src + row + partner);
         }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MODE == kModeRH && XCHG) {
+            // every lane takes part (no branch on the lane's own position yet)
+#pragma unroll
+            for (int k = 0; k < U; ++k) xb[k] = lane_exchange(xa[k], xlane);
+        }
         if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
         for (uint32_t e = t + blockDim.x; e < a.entries; e += blockDim.x) {
             const uint32_t q = fast_div(e, a.pairs_div);
@@ -1565,16 +1584,18 @@ static bool pos_vectors(const Plan& p, PosArgs* a, bool out)
 }
 
 // Heads, positions per block and the grid, once the vectors a row's
-// threads cover (lo_vec, span) are set.
-static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
+// threads cover (lo_vec, span) are set: U heads per thread, a position's
+// heads over up to `lanes_target` threads.
+static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid, int U,
+                             uint32_t lanes_target)
 {
     if (a->span < 1 || a->span > 256) return false;
     a->N = (uint32_t)p.N;
     a->pairs = (uint32_t)(p.L / 2);
-    a->HL = (uint32_t)std::min<uint64_t>(std::max<uint32_t>(1, kPosLanes / a->span), (uint64_t)p.N);
-    a->chunks = (uint32_t)((p.N + (uint64_t)a->HL * kUPos - 1) / ((uint64_t)a->HL * kUPos));
+    a->HL = (uint32_t)std::min<uint64_t>(std::max<uint32_t>(1, lanes_target / a->span), (uint64_t)p.N);
+    a->chunks = (uint32_t)((p.N + (uint64_t)a->HL * U - 1) / ((uint64_t)a->HL * U));
     a->lanes = a->span * a->HL;
-    a->P = a->lanes < kPosLanes ? std::min<uint32_t>(kPosLanes / a->lanes, kPosLds / a->pairs) : 1;
+    a->P = a->lanes < lanes_target ? std::min<uint32_t>(lanes_target / a->lanes, kPosLds / a->pairs) : 1;
     a->entries = a->P * a->pairs;
     if (a->entries > (uint32_t)kPosLds) return false;
     a->bs = (uint32_t)(p.B * p.S);
@@ -1604,7 +1625,7 @@ bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
         a->lo_vec = lines.lo_vec;
         a->span = lines.span;
     }
-    return pos_launch_shape(p, a, threads, grid);
+    return pos_launch_shape(p, a, threads, grid, kUPos, kPosLanes);
 }
 
 // Out of place: the threads of a row cover all of its vectors.
@@ -1613,41 +1634,44 @@ bool pos_geometry_out(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* gr
     if (!pos_vectors(p, a, true)) return false;
     a->lo_vec = 0;
     a->span = a->row_vecs;
-    return pos_launch_shape(p, a, threads, grid);
+    return pos_launch_shape(p, a, threads, grid, pos_out_heads(p.mode), pos_out_lanes(p.mode));
 }
 
 template <int DT, int TT, int DIR>
-const void* pos_kernel_d(int mode, bool out)
+const void* pos_kernel_d(int mode, bool out, bool xchg)
 {
     if (out)
-        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeIL>)
-                               : reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeRH>);
+        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeIL, false>)
+               : xchg          ? reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeRH, true>)
+                               : reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeRH, false>);
     return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL>)
                            : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH>);
 }
 
 template <int DT, int TT>
-const void* pos_kernel_t(int dir, int mode, bool out)
+const void* pos_kernel_t(int dir, int mode, bool out, bool xchg)
 {
-    return dir == kFwd ? pos_kernel_d<DT, TT, kFwd>(mode, out) : pos_kernel_d<DT, TT, kBwd>(mode, out);
+    return dir == kFwd ? pos_kernel_d<DT, TT, kFwd>(mode, out, xchg) : pos_kernel_d<DT, TT, kBwd>(mode, out, xchg);
 }
 
 template <int DT>
-const void* pos_kernel_dt(int tt, int dir, int mode, bool out)
+const void* pos_kernel_dt(int tt, int dir, int mode, bool out, bool xchg)
 {
     switch (tt) {
-    case ROPE_DTYPE_F32: return pos_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode, out);
-    case ROPE_DTYPE_F16: return pos_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode, out);
-    default: return pos_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode, out);
+    case ROPE_DTYPE_F32: return pos_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode, out, xchg);
+    case ROPE_DTYPE_F16: return pos_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode, out, xchg);
+    default: return pos_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode, out, xchg);
     }
 }
 
-const void* pos_kernel(const Plan& p, bool out)
+// out: the out-of-place kernel; xchg: its lane exchange (a row's threads
+// within one wave: rows of 64/k vectors)
+const void* pos_kernel(const Plan& p, bool out, bool xchg = false)
 {
     switch (p.dtype) {
-    case ROPE_DTYPE_F32: return pos_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode, out);
-    case ROPE_DTYPE_F16: return pos_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode, out);
-    default: return pos_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode, out);
+    case ROPE_DTYPE_F32: return pos_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode, out, xchg);
+    case ROPE_DTYPE_F16: return pos_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode, out, xchg);
+    default: return pos_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode, out, xchg);
     }
 }
 
@@ -1710,7 +1734,8 @@ rope_status_t run_out_pos(void* y, const void* x, const int64_t x_shape[4], rope
     uint32_t threads = 0, grid = 0;
     if (pos_geometry_out(p, &a, &threads, &grid)) {
         void* args[] = {&a};
-        err = hipLaunchKernel(pos_kernel(p, true), dim3(grid), dim3(threads), args, 0, s);
+        const bool xchg = a.span <= 64 && 64 % a.span == 0;
+        err = hipLaunchKernel(pos_kernel(p, true, xchg), dim3(grid), dim3(threads), args, 0, s);
     } else {
         err = hipMemcpyAsync(p.x, p.src, (size_t)p.bytes, hipMemcpyDeviceToDevice, s);
         if (err == hipSuccess) {
