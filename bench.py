@@ -286,6 +286,38 @@ def bench_multi(name: str, reps: int, stream) -> dict:
             "separate_launches_GBps": round(nbytes / t_each / 1e9, 1)}
 
 
+def bench_pos_multi(name: str, reps: int, stream) -> dict:
+    """A workload with several tensors (the GQA Q and K) through the
+    position entry points: forward launch time of one _pos_multi call (cos
+    and sin evaluated once per position for both tensors) against one
+    position call per tensor, rotating copies as bench_multi does."""
+    import torch
+
+    import transformer_positional_encoding_amd as rp
+    import workloads as W
+    w = W.WORKLOADS[name]
+    pos = torch.from_numpy(W.positions(w)).to("cuda")
+    f = rp.rope_inv_freq(w.L, w.base, "cuda")
+    per_set = sum(slice_line_bytes(dataclasses.replace(w, x_shapes=(shp,))) for shp in w.x_shapes)
+    ncopy = max(1, min(8, -(-(3 * MALL_BYTES) // per_set)))
+    base = [W.make_x(w, k).to("cuda") for k in range(len(w.x_shapes))]
+    sets = [[t.clone() for t in base] for _ in range(ncopy)]
+    one = [(rp.rope_partial_fwd_inplace_pos_multi, (sets[i], pos, f, w.mode, w.partial_slice)) for i in range(ncopy)]
+    each = [(lambda xs: [rp.rope_partial_fwd_inplace_pos(x, pos, f, w.mode, w.partial_slice) for x in xs], (sets[i],))
+            for i in range(ncopy)]
+    time_launches(one, max(4, reps // 4), stream)
+    t_one = time_launches(one, reps, stream)
+    time_launches(each, max(4, reps // 4), stream)
+    t_each = time_launches(each, reps, stream)
+    nbytes = sum(2 * B * S * N * w.L * W.ESIZE[w.dtype] for (B, S, N, _) in w.x_shapes) + pos.numel() * 8 + f.numel() * 8
+    return {"workload": name, "note": w.note + ", tables computed from positions", "dtype": w.dtype,
+            "directions": ["fwd"], "rotating_copies": ncopy, "bytes_per_call": nbytes,
+            "elements_per_call": w.rotated_elements(),
+            "one_launch_us": round(t_one * 1e6, 3), "one_launch_GBps": round(nbytes / t_one / 1e9, 1),
+            "separate_launches_us": round(t_each * 1e6, 3),
+            "separate_launches_GBps": round(nbytes / t_each / 1e9, 1)}
+
+
 def bench_out_of_place(name: str, reps: int, stream) -> dict:
     """The out-of-place entry points on a workload (what the autograd ops
     run: the backward writes the gradient with respect to x into a new
@@ -443,10 +475,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out,c4:pos,c2_s4096:pos,c4:outpos,"
-                                      "c2_s4096:outpos,c2_s4096,rh_64of128,rh_32of128,c3_coeff4",
+                                      "c2_s4096:outpos,c2:posmulti,c2_s4096,rh_64of128,rh_32of128,c3_coeff4",
                     help="other workloads measured in the same run (reported under 'other_workloads'); "
                          "NAME:out measures the out-of-place entry points on NAME, NAME:pos the position "
-                         "entry points, NAME:outpos the out-of-place position entry points")
+                         "entry points, NAME:outpos the out-of-place position entry points, NAME:posmulti "
+                         "the multi-tensor position entry points")
     ap.add_argument("--reps", type=int, default=50, help="launches per per-kernel timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU oracle budget: whole steps repeated to fill about this many seconds")
@@ -489,6 +522,9 @@ def main() -> int:
             continue
         if name.endswith(":outpos"):
             others.append(bench_positions(name[:-7], max(10, args.reps // 2), stream, out=True))
+            continue
+        if name.endswith(":posmulti"):
+            others.append(bench_pos_multi(name[:-9], max(10, args.reps // 2), stream))
             continue
         if len(W.WORKLOADS[name].x_shapes) > 1:
             others.append(bench_multi(name, max(10, args.reps // 2), stream))

@@ -257,6 +257,39 @@ ROPE_API rope_status_t rope_partial_launch_info(
     int64_t info[ROPE_LAUNCH_INFO_LEN]);
 
 /*
+ * rope_partial_fwd_inplace_pos_multi / rope_partial_bwd_inplace_pos_multi
+ * -- the position forms for `count` tensors that share one set of positions
+ * (the Q and K of one attention layer, whose head counts may differ); the
+ * result is that of calling rope_partial_fwd_inplace_pos on xs[0], xs[1],
+ * ... in order on `stream`. When the tensors share B, S and D and take the
+ * vector kernel, all of them run in a single launch that evaluates each
+ * pair's cos and sin once per position for every tensor. "ANE实战RoPE位置编码
+ * 在MIL中的纯ANE实现", section 第二步, applies the same rotation to Q and K.
+ *
+ *   count      0..ROPE_MULTI_MAX; 0 is a no-op.
+ *   xs         host array of `count` device pointers.
+ *   x_shapes   host array of `count` shapes {B, S, N, D}.
+ *   Other arguments are those of rope_partial_fwd_inplace_pos and apply to
+ *   every tensor: positions_shape must fit each tensor's B and S.
+ *
+ * Every tensor is checked before anything is launched: on an error no
+ * memory has been touched, and rope_last_error() names the tensor. count
+ * outside [0, ROPE_MULTI_MAX] is ROPE_ERR_INVALID; NULL xs or x_shapes with
+ * count > 0 is ROPE_ERR_NULLPTR. The tensors must not overlap.
+ */
+ROPE_API rope_status_t rope_partial_fwd_inplace_pos_multi(
+    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+ROPE_API rope_status_t rope_partial_bwd_inplace_pos_multi(
+    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+/*
  * rope_partial_fwd_out_pos / rope_partial_bwd_out_pos -- the position forms
  * out of place: y receives x with its slice rotated, cos and sin computed
  * from positions exactly as rope_partial_fwd_inplace_pos does, and x is left

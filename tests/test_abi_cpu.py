@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
                  "rope_last_error", "rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi",
                  "rope_partial_check", "rope_partial_launch_info", "rope_partial_fwd_out",
                  "rope_partial_bwd_out", "rope_partial_fwd_inplace_pos", "rope_partial_bwd_inplace_pos",
-                 "rope_partial_launch_info_pos", "rope_partial_fwd_out_pos", "rope_partial_bwd_out_pos"):
+                 "rope_partial_launch_info_pos", "rope_partial_fwd_out_pos", "rope_partial_bwd_out_pos",
+                 "rope_partial_fwd_inplace_pos_multi", "rope_partial_bwd_inplace_pos_multi"):
         assert want in names
 
 
@@ -364,3 +365,29 @@ def test_out_of_place_position_noops(direction):
     assert opcall(direction, y=None, x=None, pos=None, inv_freq=None, x_shape=(0, 4, 3, 64)) == OK
     # y == x with an empty slice: nothing to do
     assert opcall(direction, y=FAKE, x=FAKE, pos=None, inv_freq=None, sl=(8, 8)) == OK
+
+
+def pmcall(direction="fwd", ptrs=(FAKE, FAKE_Y), shapes=((2, 4, 3, 64), (2, 4, 1, 64)), pos=FAKE, pos_shape=(1, 4),
+           pos_strides=(4, 1), inv_freq=FAKE, mode=IL, sl=(0, 32), count=None):
+    """The multi-tensor position entry points, only with arguments that fail
+    validation or are no-ops."""
+    return rp.raw_pos_multi_call(direction, ptrs, shapes, BF16, pos, pos_shape, pos_strides, inv_freq, BF16, mode,
+                                 sl, None, count=count)
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_position_multi_argument_errors(direction):
+    assert pmcall(direction, count=5) == INVALID and "count" in rp.last_error()
+    assert pmcall(direction, count=-1) == INVALID
+    assert pmcall(direction, ptrs=None, shapes=None, count=2) == NULLPTR
+    assert pmcall(direction, shapes=((2, 4, 3, 64), (2, 5, 1, 64))) == INVALID
+    assert "tensor 1" in rp.last_error() and "dimension S" in rp.last_error()
+    assert pmcall(direction, ptrs=(FAKE, None)) == NULLPTR and "tensor 1" in rp.last_error()
+    assert pmcall(direction, pos=None) == NULLPTR and "tensor 0" in rp.last_error()
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_position_multi_noops(direction):
+    assert pmcall(direction, ptrs=None, shapes=None, count=0) == OK
+    assert pmcall(direction, ptrs=(None, None), pos=None, inv_freq=None, sl=(8, 8)) == OK
+    assert pmcall(direction, ptrs=(None, None), shapes=((0, 4, 3, 64), (2, 0, 1, 64)), pos=None, inv_freq=None) == OK

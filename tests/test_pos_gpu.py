@@ -214,3 +214,54 @@ def test_pos_large_and_negative_positions(tdtype):
     pos[0, :4] = torch.tensor([0, -1, 2 ** 40, -(2 ** 40)])
     f = rp.rope_inv_freq(128, 10000.0)
     run_pos_and_check(x, pos, f, mode, sl, "fwd", tdtype, "large and negative positions")
+
+
+# ---------------------------------------------------------------- several tensors
+
+MULTI_CASES = [
+    # (shapes, slice, mode): one launch when B, S and D agree
+    (((2, 32, 16, 128), (2, 32, 2, 128)), (0, 128), "rotate_half"),       # GQA Q and K
+    (((2, 32, 16, 128), (2, 32, 4, 128)), (32, 96), "interleave"),        # half-line slice
+    (((1, 24, 8, 192), (1, 24, 1, 192), (1, 24, 3, 192), (1, 24, 5, 192)), (0, 64), 4),   # four, coefficient 4
+    (((2, 16, 6, 192), (2, 16, 2, 64)), (0, 64), "interleave"),           # D differs: one launch each
+    (((2, 12, 5, 64), (2, 12, 3, 64)), (3, 35), "interleave"),            # odd start: the row kernel each
+]
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("case", MULTI_CASES, ids=[f"{len(c[0])}x-{c[1]}-{c[2]}" for c in MULTI_CASES])
+def test_pos_multi_equals_single_calls_and_the_oracle(case, direction):
+    shapes, sl, mode = case
+    L = sl[1] - sl[0]
+    B, S = shapes[0][0], shapes[0][1]
+    xs = [_rand(sh, "bf16", 300 + i) for i, sh in enumerate(shapes)]
+    pos = _positions(B, S, True, 310)
+    f = rp.rope_inv_freq(L, 500000.0)
+    announce(f"positions multi {[tuple(s) for s in shapes]} {sl} {mode} {direction}")
+    multi = [x.to(DEV) for x in xs]
+    single = [x.to(DEV) for x in xs]
+    (rp.rope_partial_fwd_inplace_pos_multi if direction == "fwd" else rp.rope_partial_bwd_inplace_pos_multi)(
+        multi, pos.to(DEV), f.to(DEV), mode, sl)
+    fn = rp.rope_partial_fwd_inplace_pos if direction == "fwd" else rp.rope_partial_bwd_inplace_pos
+    for t in single:
+        fn(t, pos.to(DEV), f.to(DEV), mode, sl)
+    torch.cuda.synchronize()
+    c, s = oracle.pos_tables(pos.numpy(), f.numpy(), L, mode, "bf16")
+    for x, m, one in zip(xs, multi, single):
+        assert torch.equal(m.view(torch.int16), one.view(torch.int16))
+        want = W.to_numpy_storage(x).copy()
+        oracle.rope_rows(want, x.shape, "bf16", c, s, mode, sl, direction, table_dtype="bf16")
+        assert np.array_equal(W.to_numpy_storage(m.cpu()), want)
+
+
+def test_pos_multi_error_touches_nothing():
+    q = _rand((1, 8, 4, 64), "bf16", 320).to(DEV)
+    k = _rand((1, 9, 2, 64), "bf16", 321).to(DEV)          # S differs from the positions'
+    q0 = q.clone()
+    pos = torch.arange(8, dtype=torch.int64, device=DEV).view(1, 8)
+    f = rp.rope_inv_freq(64).to(DEV)
+    announce("positions multi: an error touches nothing")
+    with pytest.raises(rp.RopeError, match="tensor 1"):
+        rp.rope_partial_fwd_inplace_pos_multi([q, k], pos, f, "interleave", (0, 64))
+    torch.cuda.synchronize()
+    assert torch.equal(q.view(torch.int16), q0.view(torch.int16))

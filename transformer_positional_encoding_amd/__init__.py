@@ -23,7 +23,7 @@ __all__ = [
     "rope_partial_launch_info", "rope_partial_fwd_out", "rope_partial_bwd_out", "partial_rotary_mul",
     "rope_partial_fwd_inplace_pos", "rope_partial_bwd_inplace_pos", "rope_inv_freq",
     "rope_partial_fwd_out_pos", "rope_partial_bwd_out_pos", "partial_rotary_mul_pos",
-    "inplace_partial_rotary_mul_pos",
+    "inplace_partial_rotary_mul_pos", "rope_partial_fwd_inplace_pos_multi", "rope_partial_bwd_inplace_pos_multi",
     "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
     "ROPE_ERR_UNSUPPORTED", "ROPE_ERR_RUNTIME", "MODES", "DTYPE_CODES",
 ]
@@ -86,6 +86,10 @@ def library() -> ctypes.CDLL:
             f = getattr(L, name)
             f.restype = ctypes.c_int
             f.argtypes = [ctypes.c_void_p] + pos_args + [ctypes.c_void_p]
+        for name in ("rope_partial_fwd_inplace_pos_multi", "rope_partial_bwd_inplace_pos_multi"):
+            f = getattr(L, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p] + pos_args[2:] + [ctypes.c_void_p]
         L.rope_partial_launch_info_pos.restype = ctypes.c_int
         L.rope_partial_launch_info_pos.argtypes = pos_args + [ctypes.POINTER(ctypes.c_int64)]
         for name in ("rope_partial_fwd_inplace_multi", "rope_partial_bwd_inplace_multi"):
@@ -243,6 +247,24 @@ def raw_multi_call(direction: str, x_ptrs, x_shapes, dtype: int, r1_ptr, r1_shap
     sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
     return fn(int(count), ptrs, shapes, int(dtype), r1_ptr, _arr4(r1_shape), _arr4(r1_strides),
               r2_ptr, _arr4(r2_shape), _arr4(r2_strides), int(table_dtype), int(mode), sl, stream)
+
+
+def raw_pos_multi_call(direction: str, x_ptrs, x_shapes, dtype: int, pos_ptr, pos_shape, pos_strides,
+                       inv_freq_ptr, table_dtype: int, mode: int, partial_slice, stream=None, count=None) -> int:
+    """Call a _pos_multi entry point with plain integers and sequences
+    (None = NULL); returns the status code without raising."""
+    L = library()
+    fn = L.rope_partial_fwd_inplace_pos_multi if direction == "fwd" else L.rope_partial_bwd_inplace_pos_multi
+    n = len(x_ptrs) if x_ptrs is not None else 0
+    count = n if count is None else count
+    ptrs = None if x_ptrs is None else (ctypes.c_void_p * max(n, 1))(*x_ptrs)
+    flat = [] if x_shapes is None else [int(v) for sh in x_shapes for v in sh]
+    shapes = None if x_shapes is None else (ctypes.c_int64 * max(len(flat), 4))(*flat)
+    sl = None if partial_slice is None else _I64x2(int(partial_slice[0]), int(partial_slice[1]))
+    ps = None if pos_shape is None else _I64x2(int(pos_shape[0]), int(pos_shape[1]))
+    pt = None if pos_strides is None else _I64x2(int(pos_strides[0]), int(pos_strides[1]))
+    return fn(int(count), ptrs, shapes, int(dtype), pos_ptr, ps, pt, inv_freq_ptr, int(table_dtype), int(mode), sl,
+              stream)
 
 
 def last_error() -> str:
@@ -789,3 +811,71 @@ def partial_rotary_mul_pos(x, positions, inv_freq, rotary_mode="interleave", par
             _POS_FNS = _pos_functions()
         return _POS_FNS[1].apply(x, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
     return _rotated_copy_pos(x, positions, inv_freq, rotary_mode, partial_slice, table_dtype)
+
+
+def _call_pos_multi(direction, xs, positions, inv_freq, mode, partial_slice, table_dtype, stream):
+    import torch
+    xs = list(xs)
+    if len(xs) > MULTI_MAX:
+        raise ValueError(f"at most {MULTI_MAX} tensors per call")
+    if not xs:
+        return
+    if isinstance(mode, str):
+        if mode not in MODES:
+            raise ValueError(f"rotary_mode must be one of {sorted(MODES)}")
+        mode = MODES[mode]
+    for i, x in enumerate(xs):
+        if not isinstance(x, torch.Tensor) or x.dim() != 4:
+            raise ValueError(f"xs[{i}] must be a 4-D torch.Tensor (B,S,N,D layout)")
+        if not x.is_contiguous():
+            raise ValueError(f"xs[{i}] must be contiguous (BSND)")
+        if x.numel() and not x.is_cuda:
+            raise ValueError(f"xs[{i}] must be a GPU tensor")
+    if len({x.dtype for x in xs}) != 1:
+        raise TypeError("all tensors of one call must share a dtype")
+    devs = {x.device for x in xs if x.numel()}
+    if len(devs) > 1:
+        raise ValueError("all tensors of one call must be on one device")
+    if positions.dim() != 2 or positions.dtype != torch.int64:
+        raise ValueError("positions must be a 2-D int64 tensor (B or 1, S)")
+    if inv_freq.dtype != torch.float64 or inv_freq.dim() != 1 or not inv_freq.is_contiguous():
+        raise ValueError("inv_freq must be a contiguous 1-D float64 tensor")
+    dev = next(iter(devs)) if devs else None
+    sl = (0, 0) if partial_slice is None else (int(partial_slice[0]), int(partial_slice[1]))
+    if dev is not None and sl[1] > sl[0]:
+        if inv_freq.numel() != (sl[1] - sl[0]) // 2:
+            raise ValueError(f"inv_freq must hold (end - start) / 2 = {(sl[1] - sl[0]) // 2} frequencies")
+        for name, t in (("positions", positions), ("inv_freq", inv_freq)):
+            if t.device != dev:
+                raise ValueError(f"{name} must be on {dev}")
+    if table_dtype is None:
+        tdt = _dtype_code(xs[0])
+    else:
+        tdt = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}.get(table_dtype, DTYPE_CODES.get(table_dtype))
+        if tdt is None:
+            raise TypeError(f"unsupported table dtype {table_dtype}")
+    if stream is None:
+        handle = torch.cuda.current_stream(dev).cuda_stream if dev is not None else None
+    else:
+        handle = getattr(stream, "cuda_stream", stream)
+    with torch.cuda.device(dev) if dev is not None else _nullcontext():
+        st = raw_pos_multi_call(direction, [x.data_ptr() or None for x in xs], [tuple(x.shape) for x in xs],
+                                _dtype_code(xs[0]), positions.data_ptr() or None, tuple(positions.shape),
+                                tuple(positions.stride()), inv_freq.data_ptr() or None, tdt, mode, partial_slice,
+                                handle)
+    if st != ROPE_OK:
+        raise RopeError(st, last_error())
+
+
+def rope_partial_fwd_inplace_pos_multi(xs, positions, inv_freq, rotary_mode="interleave", partial_slice=None,
+                                       table_dtype=None, stream=None) -> None:
+    """:func:`rope_partial_fwd_inplace_pos` on up to 4 tensors sharing the
+    positions (e.g. Q and K of one layer), in one launch when they share B,
+    S and D: each pair's cos and sin is then evaluated once per position."""
+    _call_pos_multi("fwd", xs, positions, inv_freq, rotary_mode, partial_slice, table_dtype, stream)
+
+
+def rope_partial_bwd_inplace_pos_multi(xs, positions, inv_freq, rotary_mode="interleave", partial_slice=None,
+                                       table_dtype=None, stream=None) -> None:
+    """Backward of :func:`rope_partial_fwd_inplace_pos_multi`."""
+    _call_pos_multi("bwd", xs, positions, inv_freq, rotary_mode, partial_slice, table_dtype, stream)

@@ -669,9 +669,37 @@ struct PosArgs {
     uint32_t bs;             // B*S
     uint32_t items;          // ceil(B*S / P) * chunks
     FastDiv span_div, lanes_div, pairs_div, chunk_div, s_div;
+    // Several tensors in one launch (MULTI): N counts the heads of all of
+    // them; head n of a position belongs to the last tensor q with
+    // hoff[q] <= n (hoff past the last tensor is UINT32_MAX), which holds
+    // nt[q] heads per position and starts at xs[q].
+    v4u* xs[kMultiMax];
+    uint32_t nt[kMultiMax];
+    uint32_t hoff[kMultiMax];
 };
 
-template <int DT, int TT, int DIR, int MODE>
+// The row of head nl of position g in one tensor, or, MULTI, in the tensor
+// the head belongs to; as a vector pointer with the thread's vector c.
+template <bool MULTI>
+__device__ __forceinline__ v4u* pos_row_vec(const PosArgs& a, uint32_t g, uint32_t nl, uint32_t c)
+{
+    if constexpr (!MULTI) {
+        return a.x + ((g * a.N + nl) * a.row_vecs + c);
+    } else {
+        v4u* base = a.xs[0];
+        uint32_t nt = a.nt[0], ho = 0;
+#pragma unroll
+        for (int q = 1; q < kMultiMax; ++q) {
+            const bool in = nl >= a.hoff[q];
+            base = in ? a.xs[q] : base;
+            nt = in ? a.nt[q] : nt;
+            ho = in ? a.hoff[q] : ho;
+        }
+        return base + ((g * nt + (nl - ho)) * a.row_vecs + c);
+    }
+}
+
+template <int DT, int TT, int DIR, int MODE, bool MULTI>
 __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
 {
     __shared__ float2 cs[kPosLds];   // (cos, sin) of the block's positions, pair-major per position
@@ -711,16 +739,16 @@ __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
         const uint32_t gl = pos_live ? g : a.bs - 1;  // past the last position: re-read it, store nothing
         const uint32_t n0 = chunk * (a.HL * U) + hl;
         v4u xa[U], xb[U];
-        uint32_t off[U];
+        v4u* px[U];
         bool live[U];
 #pragma unroll
         for (int k = 0; k < U; ++k) {
             const uint32_t n = n0 + (uint32_t)k * a.HL;
             live[k] = pos_live && n < a.N;            // past N: re-read row N-1, store nothing
             const uint32_t nl = n < a.N ? n : a.N - 1;
-            off[k] = (gl * a.N + nl) * a.row_vecs + cx;
-            xa[k] = load_x<true>(a.x + off[k]);
-            if constexpr (MODE == kModeRH) xb[k] = load_x<true>(a.x + off[k] + a.half_vecs);
+            px[k] = pos_row_vec<MULTI>(a, gl, nl, cx);
+            xa[k] = load_x<true>(px[k]);
+            if constexpr (MODE == kModeRH) xb[k] = load_x<true>(px[k] + a.half_vecs);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
@@ -754,14 +782,14 @@ __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
 #pragma unroll
                 for (int i = 0; i < K; i += 2)
                     rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C[i], S[i], C[i + 1], S[i + 1]);
-                store_x<true>(a.x + off[k], X.pack());
+                store_x<true>(px[k], X.pack());
             } else {
                 Lanes<DT> X2;
                 X2.unpack(xb[k]);
 #pragma unroll
                 for (int i = 0; i < K; ++i) rotate_pair<DIR, kUnfused>(X.v[i], X2.v[i], C[i], S[i], C[i], S[i]);
-                store_x<true>(a.x + off[k], X.pack());
-                store_x<true>(a.x + off[k] + a.half_vecs, X2.pack());
+                store_x<true>(px[k], X.pack());
+                store_x<true>(px[k] + a.half_vecs, X2.pack());
             }
         }
         __syncthreads();   // the next item rewrites cs
@@ -1644,8 +1672,41 @@ const void* pos_kernel_d(int mode, bool out, bool xchg)
         return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeIL, false>)
                : xchg          ? reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeRH, true>)
                                : reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeRH, false>);
-    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL>)
-                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH>);
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL, false>)
+                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH, false>);
+}
+
+template <int DT, int TT, int DIR>
+const void* pos_multi_kernel_d(int mode)
+{
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL, true>)
+                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH, true>);
+}
+
+template <int DT, int TT>
+const void* pos_multi_kernel_t(int dir, int mode)
+{
+    return dir == kFwd ? pos_multi_kernel_d<DT, TT, kFwd>(mode) : pos_multi_kernel_d<DT, TT, kBwd>(mode);
+}
+
+template <int DT>
+const void* pos_multi_kernel_dt(int tt, int dir, int mode)
+{
+    switch (tt) {
+    case ROPE_DTYPE_F32: return pos_multi_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode);
+    case ROPE_DTYPE_F16: return pos_multi_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode);
+    default: return pos_multi_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode);
+    }
+}
+
+// the position kernel over several tensors at once
+const void* pos_multi_kernel(const Plan& p)
+{
+    switch (p.dtype) {
+    case ROPE_DTYPE_F32: return pos_multi_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode);
+    case ROPE_DTYPE_F16: return pos_multi_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode);
+    default: return pos_multi_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode);
+    }
 }
 
 template <int DT, int TT>
@@ -1675,8 +1736,20 @@ const void* pos_kernel(const Plan& p, bool out, bool xchg = false)
     }
 }
 
-// Tables from positions: the position vector kernel, else the row or
-// scalar kernel with their POS form.
+// Tables from positions, one planned tensor: the position vector kernel,
+// else the row or scalar kernel with their POS form.
+hipError_t launch_pos_plan(const Plan& p, int cus, hipStream_t s)
+{
+    PosArgs a{};
+    uint32_t threads = 0, grid = 0;
+    if (pos_geometry(p, &a, &threads, &grid)) {
+        void* args[] = {&a};
+        return hipLaunchKernel(pos_kernel(p, false), dim3(grid), dim3(threads), args, 0, s);
+    }
+    RowShape rs;
+    return rows_shape(p, &rs) ? launch_rows(p, rs, s) : launch_scalar(p, cus, s);
+}
+
 rope_status_t run_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype, const int64_t* positions,
                       const int64_t positions_shape[2], const int64_t positions_strides[2], const double* inv_freq,
                       rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2], void* stream,
@@ -1690,16 +1763,72 @@ rope_status_t run_pos(void* x, const int64_t x_shape[4], rope_dtype_t dtype, con
     if (p.noop) return ROPE_OK;
     int cus = 0;
     if ((st = device_cus(&cus)) != ROPE_OK) return st;
+    const hipError_t err = launch_pos_plan(p, cus, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
+    return ROPE_OK;
+}
+
+// Several tensors with one set of positions (the Q and K of a layer): every
+// tensor is checked first; when they share B, S, D and the vector geometry,
+// one launch of the position kernel takes the heads of all of them, each
+// pair's cos and sin evaluated once per position for every tensor;
+// otherwise one launch per tensor.
+rope_status_t run_pos_multi(int32_t count, void* const xs[], const int64_t (*x_shapes)[4], rope_dtype_t dtype,
+                            const int64_t* positions, const int64_t positions_shape[2],
+                            const int64_t positions_strides[2], const double* inv_freq, rope_dtype_t table_dtype,
+                            int64_t mode, const int64_t partial_slice[2], void* stream, Direction dir)
+{
+    if (count < 0 || count > kMultiMax)
+        return set_error(ROPE_ERR_INVALID, "count must be in [0, " + std::to_string(kMultiMax) + "]");
+    if (count == 0) return ROPE_OK;
+    if (xs == nullptr || x_shapes == nullptr) return set_error(ROPE_ERR_NULLPTR, "xs or x_shapes is NULL");
+    Plan P[kMultiMax];
+    int live = 0;
+    for (int i = 0; i < count; ++i) {
+        std::string why;
+        rope_status_t st = make_plan_pos(xs[i], x_shapes[i], dtype, positions, positions_shape, positions_strides,
+                                         inv_freq, table_dtype, mode, partial_slice, dir, &P[live], &why);
+        if (st != ROPE_OK) return set_error(st, "tensor " + std::to_string(i) + ": " + why);
+        if (!P[live].noop) ++live;
+    }
+    if (live == 0) return ROPE_OK;
+    int cus = 0;
+    rope_status_t st = device_cus(&cus);
+    if (st != ROPE_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    PosArgs a{};
+    bool together = live > 1;
+    PosArgs each[kMultiMax];
+    uint64_t heads = 0;
+    for (int i = 0; i < live && together; ++i) {
+        uint32_t t = 0, g = 0;
+        together = P[i].B == P[0].B && P[i].S == P[0].S && P[i].D == P[0].D &&
+                   pos_geometry(P[i], &each[i], &t, &g) && each[i].lo_vec == each[0].lo_vec &&
+                   each[i].span == each[0].span;
+        heads += (uint64_t)P[i].N;
+    }
+    hipError_t err = hipSuccess;
+    PosArgs m{};
     uint32_t threads = 0, grid = 0;
-    hipError_t err;
-    if (pos_geometry(p, &a, &threads, &grid)) {
-        void* args[] = {&a};
-        err = hipLaunchKernel(pos_kernel(p, false), dim3(grid), dim3(threads), args, 0, s);
+    if (together && heads < (1ull << 31)) {
+        Plan q = P[0];
+        q.N = (int64_t)heads;
+        m = each[0];
+        together = pos_launch_shape(q, &m, &threads, &grid, kUPos, kPosLanes);
+        uint32_t first = 0;
+        for (int i = 0; i < kMultiMax; ++i) {
+            m.xs[i] = i < live ? each[i].x : nullptr;
+            m.nt[i] = i < live ? (uint32_t)P[i].N : 0;
+            m.hoff[i] = i < live ? first : 0xFFFFFFFFu;
+            if (i < live) first += (uint32_t)P[i].N;
+        }
     } else {
-        RowShape rs;
-        err = rows_shape(p, &rs) ? launch_rows(p, rs, s) : launch_scalar(p, cus, s);
+        together = false;
+    }
+    if (together) {
+        void* args[] = {&m};
+        err = hipLaunchKernel(pos_multi_kernel(P[0]), dim3(grid), dim3(threads), args, 0, s);
+    } else {
+        for (int i = 0; i < live && err == hipSuccess; ++i) err = launch_pos_plan(P[i], cus, s);
     }
     if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
     return ROPE_OK;
@@ -1738,16 +1867,7 @@ rope_status_t run_out_pos(void* y, const void* x, const int64_t x_shape[4], rope
         err = hipLaunchKernel(pos_kernel(p, true, xchg), dim3(grid), dim3(threads), args, 0, s);
     } else {
         err = hipMemcpyAsync(p.x, p.src, (size_t)p.bytes, hipMemcpyDeviceToDevice, s);
-        if (err == hipSuccess) {
-            PosArgs b{};
-            if (pos_geometry(p, &b, &threads, &grid)) {
-                void* args[] = {&b};
-                err = hipLaunchKernel(pos_kernel(p, false), dim3(grid), dim3(threads), args, 0, s);
-            } else {
-                RowShape rs;
-                err = rows_shape(p, &rs) ? launch_rows(p, rs, s) : launch_scalar(p, cus, s);
-            }
-        }
+        if (err == hipSuccess) err = launch_pos_plan(p, cus, s);
     }
     if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
     return ROPE_OK;
@@ -1908,6 +2028,26 @@ rope_status_t rope_partial_bwd_inplace_pos(void* x, const int64_t x_shape[4], ro
 {
     return rope::run_pos(x, x_shape, dtype, positions, positions_shape, positions_strides, inv_freq, table_dtype,
                          mode, partial_slice, stream, rope::kBwd);
+}
+
+rope_status_t rope_partial_fwd_inplace_pos_multi(int32_t count, void* const xs[], const int64_t x_shapes[][4],
+                                                 rope_dtype_t dtype, const int64_t* positions,
+                                                 const int64_t positions_shape[2], const int64_t positions_strides[2],
+                                                 const double* inv_freq, rope_dtype_t table_dtype, int64_t mode,
+                                                 const int64_t partial_slice[2], void* stream)
+{
+    return rope::run_pos_multi(count, xs, x_shapes, dtype, positions, positions_shape, positions_strides, inv_freq,
+                               table_dtype, mode, partial_slice, stream, rope::kFwd);
+}
+
+rope_status_t rope_partial_bwd_inplace_pos_multi(int32_t count, void* const xs[], const int64_t x_shapes[][4],
+                                                 rope_dtype_t dtype, const int64_t* positions,
+                                                 const int64_t positions_shape[2], const int64_t positions_strides[2],
+                                                 const double* inv_freq, rope_dtype_t table_dtype, int64_t mode,
+                                                 const int64_t partial_slice[2], void* stream)
+{
+    return rope::run_pos_multi(count, xs, x_shapes, dtype, positions, positions_shape, positions_strides, inv_freq,
+                               table_dtype, mode, partial_slice, stream, rope::kBwd);
 }
 
 rope_status_t rope_partial_fwd_out_pos(void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
