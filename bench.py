@@ -35,16 +35,19 @@ if ROOT not in sys.path:
 
 METRIC = "achieved HBM GB/s (% of MI355X peak) + Gelem/s, partial-RoPE fwd/bwd in place"
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD public spec
-KERNEL_SRC = os.path.join(ROOT, "transformer_positional_encoding_amd", "csrc", "rope_kernels.hip")
+KERNEL_DIR = os.path.join(ROOT, "transformer_positional_encoding_amd", "csrc")
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def kernel_source_hash() -> str:
-    """sha256[:16] of the kernel source with its comments and spacing
-    removed: editing a comment keeps the committed counters valid, changing
-    code makes them stale."""
-    with open(KERNEL_SRC, encoding="utf-8") as f:
-        text = f.read()
+    """sha256[:16] of the library's sources (every file of csrc/, in name
+    order) with comments and spacing removed: editing a comment keeps the
+    committed counters valid, changing code makes them stale."""
+    text = ""
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            with open(os.path.join(KERNEL_DIR, name), encoding="utf-8") as f:
+                text += f"\n// {name}\n" + f.read()
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = re.sub(r"\s+", " ", text).strip()

@@ -30,1013 +30,15 @@
 #include <atomic>
 #include <string>
 
-#include "rope_fastdiv.hpp"
+#include "rope_device.hpp"
+#include "rope_general_kernels.hpp"
 #include "rope_partial.h"
 #include "rope_plan.hpp"
+#include "rope_pos_kernels.hpp"
+#include "rope_vec_kernels.hpp"
 
 namespace rope {
 namespace {
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));  // one 16-byte vector
-typedef uint32_t v2u __attribute__((ext_vector_type(2)));  // half of one
-
-constexpr int kModeRH = ROPE_MODE_ROTATE_HALF;
-constexpr int kModeIL = ROPE_MODE_INTERLEAVE;
-// rotate_half schemes of the vector kernel (see there): each thread writes
-// its own vector and takes its partner's from the lane that holds it (a
-// row's threads in one wave), or loads the partner from memory (out of
-// place, rows wider than a wave)
-constexpr int kModeRHOwn = 2;
-constexpr int kModeRHOwnLoad = 3;
-
-// ---------------------------------------------------------------------------
-// fp32 <-> storage conversions. A 32-bit word holds two adjacent 16-bit lanes
-// (lower lane in the low half). Widening is exact; narrowing rounds to nearest
-// even (v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32), keeps fp16 subnormals and
-// NaNs, and overflows to infinity.
-// ---------------------------------------------------------------------------
-template <int DT> struct Store;
-
-template <> struct Store<ROPE_DTYPE_BF16> {
-    static constexpr int kLanes = 8;  // per 16-byte vector
-    __device__ static f32x2 widen(uint32_t w)
-    {
-        f32x2 r;
-        r.x = __uint_as_float(w << 16);
-        r.y = __uint_as_float(w & 0xffff0000u);
-        return r;
-    }
-    __device__ static uint32_t narrow(f32x2 v)
-    {
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-    }
-    __device__ static float load1(const void* p, int64_t i)
-    {
-        return __uint_as_float((uint32_t)static_cast<const uint16_t*>(p)[i] << 16);
-    }
-    __device__ static void store1(void* p, int64_t i, float v)
-    {
-        static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
-    }
-};
-
-template <> struct Store<ROPE_DTYPE_F16> {
-    static constexpr int kLanes = 8;
-    __device__ static f32x2 widen(uint32_t w)
-    {
-        return __builtin_convertvector(__builtin_bit_cast(f16x2, w), f32x2);
-    }
-    __device__ static uint32_t narrow(f32x2 v)
-    {
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-    }
-    __device__ static float load1(const void* p, int64_t i)
-    {
-        return static_cast<float>(static_cast<const _Float16*>(p)[i]);
-    }
-    __device__ static void store1(void* p, int64_t i, float v)
-    {
-        static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
-    }
-};
-
-template <> struct Store<ROPE_DTYPE_F32> {
-    static constexpr int kLanes = 4;
-    __device__ static float load1(const void* p, int64_t i) { return static_cast<const float*>(p)[i]; }
-    __device__ static void store1(void* p, int64_t i, float v) { static_cast<float*>(p)[i] = v; }
-};
-
-// A 16-byte vector of lanes as fp32 values.
-template <int DT>
-struct Lanes {
-    float v[Store<DT>::kLanes];
-    __device__ void unpack(const v4u& q)
-    {
-        if constexpr (DT == ROPE_DTYPE_F32) {
-            v[0] = __uint_as_float(q[0]); v[1] = __uint_as_float(q[1]);
-            v[2] = __uint_as_float(q[2]); v[3] = __uint_as_float(q[3]);
-        } else {
-            const uint32_t w[4] = {q[0], q[1], q[2], q[3]};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                f32x2 f = Store<DT>::widen(w[k]);
-                v[2 * k] = f.x;
-                v[2 * k + 1] = f.y;
-            }
-        }
-    }
-    __device__ v4u pack() const
-    {
-        if constexpr (DT == ROPE_DTYPE_F32) {
-            return v4u{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                       __float_as_uint(v[3])};
-        } else {
-            uint32_t w[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                f32x2 f;
-                f.x = v[2 * k];
-                f.y = v[2 * k + 1];
-                w[k] = Store<DT>::narrow(f);
-            }
-            return v4u{w[0], w[1], w[2], w[3]};
-        }
-    }
-};
-
-// ---------------------------------------------------------------------------
-// The rotation of one pair (a, b) = (x_j, x_p(j)) where j is the lane whose
-// partner term is negated in the forward (even lane / first half):
-//   forward : a' = a*c_a - b*s_a        b' = b*c_b + a*s_b
-//   backward: a' = a*c_a + b*s_b        b' = b*c_b - a*s_a   (transpose)
-// 16-bit x (UNFUSED): each product is rounded to fp32 and the sum is rounded
-// once more, as the page's "cast to fp32, multiply-add in fp32" reads. With
-// 16-bit tables both products are exact, so this is also the single
-// rounding of the exact sum; with fp32 tables the product roundings are part
-// of the definition. fp32 x: the compiler may fuse (the result is held to a
-// tolerance, not to bits).
-// ---------------------------------------------------------------------------
-template <int DIR>
-__device__ __forceinline__ void rotate_pair_unfused(float& a, float& b, float ca, float sa, float cb, float sb)
-{
-#pragma clang fp contract(off)
-    // no fused multiply-add in this function: every product and sum rounds
-    float na, nb;
-    if constexpr (DIR == kFwd) {
-        na = a * ca - b * sa;
-        nb = b * cb + a * sb;
-    } else {
-        na = a * ca + b * sb;
-        nb = b * cb - a * sa;
-    }
-    a = na;
-    b = nb;
-}
-
-template <int DIR, bool UNFUSED>
-__device__ __forceinline__ void rotate_pair(float& a, float& b, float ca, float sa, float cb, float sb)
-{
-    if constexpr (UNFUSED) {
-        rotate_pair_unfused<DIR>(a, b, ca, sa, cb, sb);
-    } else {
-        float na, nb;
-        if constexpr (DIR == kFwd) {
-            na = a * ca - b * sa;
-            nb = b * cb + a * sb;
-        } else {
-            na = a * ca + b * sb;
-            nb = b * cb - a * sa;
-        }
-        a = na;
-        b = nb;
-    }
-}
-
-// One lane of rotate_half in the own-vector scheme: the lane's value x, its
-// partner's value p, and y = x*c - p*s (neg) or x*c + p*s, with c the lane's
-// cos and s the sine the direction takes (the lane's forward, the partner's
-// backward). These are the same products and sum as rotate_pair forms for
-// that lane, with the same roundings.
-__device__ __forceinline__ float rotate_own_unfused(float x, float p, float c, float s, bool neg)
-{
-#pragma clang fp contract(off)
-    const float t = p * s;
-    return x * c + (neg ? -t : t);
-}
-
-template <bool UNFUSED>
-__device__ __forceinline__ float rotate_own(float x, float p, float c, float s, bool neg)
-{
-    if constexpr (UNFUSED) {
-        return rotate_own_unfused(x, p, c, s, neg);
-    } else {
-        const float t = p * s;
-        return x * c + (neg ? -t : t);
-    }
-}
-
-// The cos or sin values for the K lanes of one x vector, from a table of
-// type TT. They take K * sizeof(TT) bytes, loaded as kVecs table units of
-// type Vec: 8 bytes (half a vector) when fp32 x meets a 16-bit table, one
-// 16-byte vector when the table is as wide as x, two when 16-bit x meets an
-// fp32 table (the page's mixed bf16-x / fp32-table case).
-template <int Bytes> struct TableUnit { using type = v4u; };
-template <> struct TableUnit<8> { using type = v2u; };
-
-template <int TT, int K>
-struct TableLanes {
-    static constexpr int kBytes = K * (TT == ROPE_DTYPE_F32 ? 4 : 2);
-    static_assert(kBytes == 8 || kBytes == 16 || kBytes == 32, "table unit shape");
-    using Vec = typename TableUnit<kBytes>::type;
-    static constexpr int kVecs = kBytes == 32 ? 2 : 1;
-    float v[K];
-    __device__ void unpack(const Vec* q)
-    {
-        if constexpr (TT == ROPE_DTYPE_F32) {
-#pragma unroll
-            for (int t = 0; t < kVecs; ++t)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) v[4 * t + w] = __uint_as_float(q[t][w]);
-        } else {
-#pragma unroll
-            for (int w = 0; w < kBytes / 4; ++w) {
-                f32x2 f = Store<TT>::widen(q[0][w]);
-                v[2 * w] = f.x;
-                v[2 * w + 1] = f.y;
-            }
-        }
-    }
-};
-
-// ---------------------------------------------------------------------------
-// Vector kernel. A thread works on 16-byte vectors of x: whole interleave
-// pairs inside one vector, or rotate_half pairs across two vectors (lanes i
-// and i+L/2 in matching positions of vector k of each half).
-//
-// Tile = one (b,s) position and a chunk of HL*U heads. A block works on GL
-// tiles at a time; thread t takes row vector c = lo_vec + t % span, head
-// lane hl = (t / span) % HL and tile lane gl = t / (span*HL), and handles
-// heads n = chunk*HL*U + hl + k*HL for k < U.
-//
-// Which vectors a row's threads cover, and who writes what:
-// * Interleave: the slice's vectors (lo_vec = start_vec, span = nvec). When
-//   the slice covers only part of its first or last 128-byte line, every
-//   vector of those lines instead: each line is then requested whole by one
-//   wave instruction, which the L2 serves much faster than two half-line
-//   requests (it fetches the whole line either way); the vectors outside the
-//   slice are loaded and dropped, never stored.
-// * rotate_half, pair owner (kModeRH): the threads cover the first half;
-//   each loads vector k of both halves and stores both. In place only, for
-//   rows whose threads do not fit one wave.
-// * rotate_half, own vector (kModeRHOwn): the threads cover the whole slice
-//   (or its whole lines, as for interleave); each loads its own vector,
-//   takes its partner's (vector k of the other half) from the lane that
-//   holds it with ds_bpermute, and stores only its own vector, so each line
-//   is requested once by one load instruction and written by one store. The
-//   host runs it with single-wave blocks, so a row's threads share a wave:
-//   the partner is in reach, and in place the wave's loads have all returned
-//   before any of its stores issue, so no thread overwrites a partner's
-//   vector before it is read. kModeRHOwnLoad, out of place for rows wider
-//   than a wave, loads the partner vector from memory instead.
-// * Out of place (src another tensor), the threads cover whole rows:
-//   vectors outside the slice are copied from src to x, and every thread
-//   stores exactly the vector it covers, with one instruction.
-//
-// The cos/sin units of a thread are loaded once per tile and, when the
-// tables broadcast over heads, reused for all its heads. All loads of a tile
-// are issued before any arithmetic. The grid normally has one block per
-// group of GL tiles; a smaller grid makes the blocks stride over the groups.
-// ---------------------------------------------------------------------------
-// x is streamed (each slice byte is read once and written once); the tables
-// are re-read by every head and stay in the caches. NT selects nontemporal
-// (streaming) loads and stores for x.
-template <bool NT>
-__device__ __forceinline__ v4u load_x(const v4u* p)
-{
-    if constexpr (NT) return __builtin_nontemporal_load(p);
-    else return *p;
-}
-
-template <bool NT>
-__device__ __forceinline__ void store_x(v4u* p, v4u v)
-{
-    if constexpr (NT) __builtin_nontemporal_store(v, p);
-    else *p = v;
-}
-
-// Offsets are 32-bit, in 16-byte vectors for x and in table units for the
-// tables: the host runs this kernel only when x spans fewer than 2^32
-// vectors (64 GiB) and each table fewer than 2^32 units.
-struct VecArgs {
-    v4u* x;                 // the tensor written, as 16-byte vectors
-    const v4u* src;         // out of place: the tensor read (in place: unused)
-    const void* r1;         // cos table, addressed in table units (TableLanes)
-    const void* r2;         // sin table
-    uint32_t row_vecs;      // vectors per row of x (D*esize/16)
-    uint32_t start_vec;     // first slice vector within a row
-    uint32_t lo_vec;        // first vector the threads of a row cover
-    uint32_t half_vecs;     // rotate_half: x vectors per half of a group (pair distance)
-    uint32_t gvec;          // rotate_half: x vectors per group (2*half_vecs; the slice unless a
-                            // rotary coefficient splits it into several groups)
-    uint32_t thalf;         // rotate_half: table units per half of a group
-    uint32_t t1b, t1s, t1n; // cos strides in table units (0 = broadcast)
-    uint32_t t2b, t2s, t2n; // sin strides in table units
-    uint32_t N;
-    uint32_t nvec;          // work units per row (in the slice)
-    uint32_t span;          // vectors per row the threads cover (>= nvec)
-    uint32_t HL;            // head lanes per tile
-    uint32_t GL;            // tiles per block iteration
-    uint32_t nchunk;        // head chunks per (b,s)
-    uint32_t tiles;         // B*S*nchunk
-    uint32_t btiles;        // ceil(tiles / GL)
-    uint32_t xcd_group;     // P: runs of P consecutive blocks stay on one XCD
-    uint32_t xcd_full;      // blocks [0, xcd_full) are renumbered (a multiple of 8P)
-    FastDiv span_div, hl_div, nchunk_div, s_div;  // divisions by span, HL, nchunk, S
-    FastDiv xcd_div;        // division by 8P
-};
-
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup i runs on
-// XCD i % 8), and each XCD has its own L2. The head chunks of one (b,s)
-// position are consecutive tiles that read the same table row. Renumber the
-// blocks in windows of 8P: within a window, XCD x takes the P consecutive
-// tile groups [xP, xP + P). With P a whole number of positions, a table row
-// is fetched into one L2 only (dispatch order, P = 1, fetches it into every
-// L2), and the 8 XCDs stream through one window of x together. Measured on
-// MI355X for a bare whole-line read-modify-write of 1 GiB of 256-byte rows:
-// one contiguous eighth of the grid per XCD (P = G/8) was 12% slower than
-// dispatch order. The map is a bijection of [0, G); blocks past the last
-// whole window keep their number.
-__device__ __forceinline__ uint32_t xcd_grouped_block(uint32_t bid, const VecArgs& a)
-{
-    if (bid >= a.xcd_full) return bid;
-    const uint32_t w = fast_div(bid, a.xcd_div);     // window
-    const uint32_t l = bid - w * a.xcd_div.d;        // place in the window
-    return w * a.xcd_div.d + (l & 7u) * a.xcd_group + (l >> 3);
-}
-
-// The 16-byte vector that the lane at byte address `lane4` (lane * 4) of the
-// wave holds, through the LDS crossbar (ds_bpermute; no LDS is allocated).
-__device__ __forceinline__ v4u lane_exchange(const v4u& v, int lane4)
-{
-    v4u r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(lane4, (int)v[i]);
-    return r;
-}
-
-// The kernel body for one tensor: `bid` is the block's number among the G
-// blocks that work on this tensor. OUT: read a.src and write a.x (out of
-// place); otherwise read and write a.x.
-template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT, bool OUT>
-__device__ __forceinline__ void vec_body(const VecArgs& a, uint32_t bid, uint32_t G)
-{
-    static_assert(!OUT || MODE != kModeRH, "out of place, rotate_half takes the own-vector scheme");
-    constexpr int K = Store<DT>::kLanes;
-    using TVec = typename TableLanes<TT, K>::Vec;
-    constexpr int TV = TableLanes<TT, K>::kVecs;      // table units per x vector
-    static_assert(OUT || MODE != kModeRHOwnLoad, "in place, the own-vector scheme exchanges within the wave");
-    constexpr bool kPair = MODE == kModeRH;           // rotate_half, pair owner
-    constexpr bool kOwn = MODE == kModeRHOwn || MODE == kModeRHOwnLoad;   // rotate_half, own vector
-    constexpr bool kXchg = MODE == kModeRHOwn;        // the partner vector from its lane
-    const v4u* src = OUT ? a.src : a.x;
-    const TVec* r1 = static_cast<const TVec*>(a.r1);
-    const TVec* r2 = static_cast<const TVec*>(a.r2);
-    constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
-    const uint32_t t = threadIdx.x;
-    const uint32_t q = fast_div(t, a.span_div);
-    const uint32_t vs = t - q * a.span;
-    const uint32_t gl = fast_div(q, a.hl_div);
-    const uint32_t hl = q - gl * a.HL;
-    // nvec is the slice's vectors (interleave) or half of them (rotate_half).
-    // rotate_half pairs vector k of the first half of a group of gvec
-    // vectors with vector k of its second half; the slice is one group
-    // unless a rotary coefficient splits it.
-    const uint32_t rel = a.lo_vec + vs - a.start_vec;  // slice-relative (wraps below the slice)
-    const bool in_span = a.lo_vec + vs >= a.start_vec && rel < (kOwn ? 2 * a.nvec : a.nvec);
-    // Pair owner: the thread's unit rel is vector k = rel % half_vecs of the
-    // first half of group rel / half_vecs.
-    const uint32_t c = kPair && a.gvec != 2 * a.nvec
-                           ? a.start_vec + (rel / a.half_vecs) * a.gvec + rel % a.half_vecs
-                           : a.lo_vec + vs;           // vector within the row
-    const uint32_t grel = kOwn && a.gvec != 2 * a.nvec ? rel % a.gvec : rel;   // place in the group
-    const bool first = in_span && (!kOwn || grel < a.half_vecs);
-    const bool second = kOwn && in_span && grel >= a.half_vecs;
-    const bool in_slice = first || second;
-    // unit (table index): the first-half vector of the thread's pair
-    const uint32_t v = first ? c - a.start_vec : second ? c - a.start_vec - a.half_vecs : 0;
-    // Own vector: the partner vector in the other half of the group (outside
-    // the slice, the thread's own again), and the table units of the thread's lanes
-    // (cos; sin forward) and of the partner's lanes (sin backward).
-    const uint32_t partner = first ? c + a.half_vecs : second ? c - a.half_vecs : c;
-    const uint32_t t_own = second ? a.thalf : 0;
-    const uint32_t t_sin = DIR == kBwd ? (first ? a.thalf : 0) : t_own;
-    // Own vector: the partner term is subtracted on the first half forward
-    // and on the second half backward.
-    const bool neg = DIR == kFwd ? first : second;
-    // Own vector, exchange: the byte address of the partner's lane for
-    // ds_bpermute (the block is one wave, so the lane is t; the partner is
-    // +-half_vecs lanes away in the same row, or the lane itself).
-    const int xlane = kXchg ? (int)(t + (partner - c)) * 4 : 0;
-    if (gl >= a.GL) return;  // no barriers below, so idle threads may leave
-
-    const uint32_t first_bt = xcd_grouped_block(bid, a);
-    for (uint32_t bt = first_bt; bt < a.btiles; bt += G) {
-        const uint32_t tile = bt * a.GL + gl;
-        if (tile >= a.tiles) continue;
-        const uint32_t g = fast_div(tile, a.nchunk_div);  // (b,s) position
-        const uint32_t chunk = tile - g * a.nchunk;
-        const uint32_t b = fast_div(g, a.s_div);
-        const uint32_t s = g - b * a.s_div.d;
-        const uint32_t n0 = chunk * (a.HL * U) + hl;
-        const uint32_t c_base = b * a.t1b + s * a.t1s + v * TV + (kOwn ? t_own : 0);
-        const uint32_t s_base = b * a.t2b + s * a.t2s + v * TV + (kOwn ? t_sin : 0);
-        const uint32_t row0 = g * a.N;
-
-        // All loads are issued back to back with no branch between them: a
-        // head past N (ragged last chunk) re-reads row N-1 and skips its
-        // store. The tables come first, then the x vectors.
-        v4u xa[U], xb[U];
-        TVec ca[U][TV], sa[U][TV], cb[U][TV], sb[U][TV];
-        uint32_t off[U];
-        bool live[U];
-        if constexpr (HEADS_SHARE_TABLES) {
-#pragma unroll
-            for (int u = 0; u < TV; ++u) {
-                ca[0][u] = r1[c_base + u];
-                sa[0][u] = r2[s_base + u];
-                if constexpr (kPair) {
-                    cb[0][u] = r1[c_base + a.thalf + u];
-                    sb[0][u] = r2[s_base + a.thalf + u];
-                }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const uint32_t n = n0 + (uint32_t)k * a.HL;
-            live[k] = n < a.N;
-            const uint32_t nl = live[k] ? n : a.N - 1;
-            const uint32_t row = (row0 + nl) * a.row_vecs;   // the row's first vector
-            off[k] = row + c;
-            if constexpr (!HEADS_SHARE_TABLES) {
-#pragma unroll
-                for (int u = 0; u < TV; ++u) {
-                    ca[k][u] = r1[c_base + nl * a.t1n + u];
-                    sa[k][u] = r2[s_base + nl * a.t2n + u];
-                    if constexpr (kPair) {
-                        cb[k][u] = r1[c_base + nl * a.t1n + a.thalf + u];
-                        sb[k][u] = r2[s_base + nl * a.t2n + a.thalf + u];
-                    }
-                }
-            }
-            xa[k] = load_x<NT>(src + off[k]);
-            if constexpr (kPair) xb[k] = load_x<NT>(src + off[k] + a.half_vecs);
-            if constexpr (kOwn && !kXchg) xb[k] = load_x<NT>(src + row + partner);
-        }
-        // Keep every load above in flight together: without this barrier the
-        // machine scheduler starts the arithmetic on the first vectors and
-        // issues the remaining loads only after waiting for them.
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (kXchg) {
-            // every lane of the row takes part (no branch has been taken on
-            // the lane's own position yet)
-#pragma unroll
-            for (int k = 0; k < U; ++k) xb[k] = lane_exchange(xa[k], xlane);
-        }
-
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            if (!live[k]) continue;
-            if (!OUT && !in_slice) continue;
-            // Out of place, a vector outside the slice is copied unchanged.
-            // Each vector is stored by one instruction either way, so a
-            // 128-byte line that the slice splits is written by one wave
-            // instruction rather than two partial ones.
-            v4u ya = xa[k], yb = xa[k];
-            if (in_slice) {
-                const int kt = HEADS_SHARE_TABLES ? 0 : k;
-                Lanes<DT> X;
-                TableLanes<TT, K> C, S;
-                X.unpack(xa[k]);
-                C.unpack(ca[kt]);
-                S.unpack(sa[kt]);
-                if constexpr (MODE == kModeIL) {
-#pragma unroll
-                    for (int i = 0; i < K; i += 2)
-                        rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C.v[i], S.v[i], C.v[i + 1], S.v[i + 1]);
-                } else if constexpr (kPair) {
-                    Lanes<DT> X2;
-                    TableLanes<TT, K> C2, S2;
-                    X2.unpack(xb[k]);
-                    C2.unpack(cb[kt]);
-                    S2.unpack(sb[kt]);
-#pragma unroll
-                    for (int i = 0; i < K; ++i)
-                        rotate_pair<DIR, kUnfused>(X.v[i], X2.v[i], C.v[i], S.v[i], C2.v[i], S2.v[i]);
-                    yb = X2.pack();
-                } else {
-                    Lanes<DT> P;
-                    P.unpack(xb[k]);
-#pragma unroll
-                    for (int i = 0; i < K; ++i) X.v[i] = rotate_own<kUnfused>(X.v[i], P.v[i], C.v[i], S.v[i], neg);
-                }
-                ya = X.pack();
-            }
-            store_x<NT>(a.x + off[k], ya);
-            if constexpr (kPair) store_x<NT>(a.x + off[k] + a.half_vecs, yb);
-        }
-    }
-}
-
-template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
-__global__ void __launch_bounds__(256) rope_vec_kernel(VecArgs a)
-{
-    vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(a, blockIdx.x, gridDim.x);
-}
-
-// Out of place: x (the output) receives src with the slice rotated.
-template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
-__global__ void __launch_bounds__(256) rope_vec_out_kernel(VecArgs a)
-{
-    vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, true>(a, blockIdx.x, gridDim.x);
-}
-
-// Several tensors that share the tables (the Q and K of one layer) in one
-// launch: blocks [first_block[i], first_block[i+1]) work on tensor i. The
-// switch keeps every field access a constant offset into the kernel
-// arguments.
-constexpr int kMultiMax = ROPE_MULTI_MAX;
-
-struct MultiVecArgs {
-    uint32_t count;
-    uint32_t first_block[kMultiMax + 1];
-    VecArgs a[kMultiMax];
-};
-
-template <int DT, int TT, int DIR, int MODE, int U, bool HEADS_SHARE_TABLES, bool NT>
-__global__ void __launch_bounds__(256) rope_vec_multi_kernel(MultiVecArgs m)
-{
-    const uint32_t b = blockIdx.x;
-    uint32_t i = 0;
-#pragma unroll
-    for (int k = 1; k < kMultiMax; ++k)
-        i += (k < (int)m.count && b >= m.first_block[k]) ? 1u : 0u;
-    const uint32_t lo = m.first_block[i], G = m.first_block[i + 1] - lo;
-    switch (i) {
-    case 0: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(m.a[0], b - lo, G); break;
-    case 1: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(m.a[1], b - lo, G); break;
-    case 2: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(m.a[2], b - lo, G); break;
-    default: vec_body<DT, TT, DIR, MODE, U, HEADS_SHARE_TABLES, NT, false>(m.a[3], b - lo, G); break;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// cos and sin from positions ("ANE实战RoPE位置编码在MIL中的纯ANE实现", section
-// 第一步: the table of θ = p / base^(2i/h), here θ = p * inv_freq[i] with the
-// frequencies given): θ is the double product of the position and the pair's
-// frequency, cos θ and sin θ are evaluated in double precision and rounded
-// once, to nearest even, to the table type TT.
-// ---------------------------------------------------------------------------
-
-// A double rounded once to the nearest value of TT, ties to even, returned
-// as the float that holds it. fp32: the conversion instruction (round to
-// nearest even). bf16/fp16: a value of the type is a whole number of units
-// in the last place of its binade, 2^(e - p) for |v| in [2^(e-1), 2^e) with
-// p significand bits, and never below the least subnormal 2^(emin - p + 1);
-// scaling by powers of two is exact and rint() rounds ties to even.
-template <int TT>
-__device__ __forceinline__ float round_to_type(double v)
-{
-    if constexpr (TT == ROPE_DTYPE_F32) {
-        return static_cast<float>(v);
-    } else {
-        constexpr int p = TT == ROPE_DTYPE_F16 ? 11 : 8;
-        constexpr int emin = TT == ROPE_DTYPE_F16 ? -14 : -126;
-        constexpr double maxf = TT == ROPE_DTYPE_F16 ? 65504.0 : 0x1.fep127;
-        if (!(v != 0.0) || !__builtin_isfinite(v)) return static_cast<float>(v);   // zero, inf, NaN
-        int e;
-        (void)frexp(v, &e);
-        const int q = e - p > emin - p + 1 ? e - p : emin - p + 1;
-        const double r = ldexp(rint(ldexp(v, -q)), q);
-        if (fabs(r) > maxf) return v > 0 ? __builtin_inff() : -__builtin_inff();
-        return static_cast<float>(r);   // exact: r is a value of TT
-    }
-}
-
-// (cos θ, sin θ) rounded to TT for position p and frequency f.
-template <int TT>
-__device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
-{
-    double sn, cn;
-    sincos(static_cast<double>(p) * f, &sn, &cn);
-    return make_float2(round_to_type<TT>(cn), round_to_type<TT>(sn));
-}
-
-// ---------------------------------------------------------------------------
-// Vector kernel with the tables computed from positions. A block takes P
-// consecutive (b,s) positions (P > 1 only when one position's heads fill
-// fewer than kPosLanes threads) and, for each, a chunk of up to HL*kUPos
-// heads (HL head lanes, kUPos heads per thread). Its threads first load the
-// position and frequency of the first (cos, sin) pair each evaluates, then
-// issue their x loads, then evaluate cos and sin while x is in flight: the
-// memory counter drains in issue order, so the wait for the frequency does
-// not wait for x, provided every load is issued on every path (indices are
-// clamped, never branched around). The values go to LDS, each pair of each
-// position once per block, and each thread reads those of its lanes from
-// there. The thread layout is the table kernel's: interleave with
-// whole-line coverage, rotate_half as pair owner (a thread takes vector k
-// of both halves). Measured on MI355X (the (16,8192,32,128) shard's slice
-// [32,96), the GQA Q layout at 4096 positions, the MLA-style slice): two
-// heads per thread in 128-thread blocks was the best of 1, 2, 4 or 8 heads
-// per thread in 64-, 128- or 256-thread blocks on all three, and as fast as
-// the table kernel on the first two.
-// ---------------------------------------------------------------------------
-constexpr int kUPos = 2;
-constexpr int kPosLds = ROPE_D_LIMIT / 2;    // (cos, sin) entries per block
-constexpr uint32_t kPosLanes = 128;          // threads a position's heads fill before a block takes more positions
-// The out-of-place position kernel's heads per thread and threads per
-// position, by mode. Measured on MI355X (cold data; the (16,8192,32,128)
-// shard's lanes [32,96), the MLA-style slice, a whole rotate_half head and
-// its second half), over 1, 2 or 4 heads per thread in blocks of 64, 128 or
-// 256 threads: interleave was fastest with 2 heads in 128 threads (326 and
-// 257 us), rotate_half with 4 heads in 64 threads (165 and 164 us, the table
-// path's times; 172 and 167 us with the interleave shape).
-constexpr int pos_out_heads(int mode) { return mode == kModeIL ? 2 : 4; }
-constexpr uint32_t pos_out_lanes(int mode) { return mode == kModeIL ? 128 : 64; }
-
-struct PosArgs {
-    v4u* x;                  // the tensor written (in place: also read)
-    const v4u* src;          // out of place: the tensor read
-    const int64_t* pos;      // position of (b,s) at pos[b*pos_sb + s*pos_ss]
-    const double* inv_freq;  // L/2 frequencies
-    int64_t pos_sb, pos_ss;
-    uint32_t row_vecs;       // vectors per row of x
-    uint32_t start_vec;      // first slice vector within a row
-    uint32_t lo_vec;         // first vector the threads of a row cover
-    uint32_t half_vecs;      // rotate_half: vectors per half of a group (pair distance)
-    uint32_t gvec;           // rotate_half: vectors per group (2*half_vecs)
-    uint32_t nvec;           // work units per row (interleave: slice vectors; rotate_half: half of them)
-    uint32_t span;           // vectors per row the threads cover
-    uint32_t HL;             // head lanes per position
-    uint32_t lanes;          // threads per position: span * HL
-    uint32_t P;              // positions per block
-    uint32_t N;
-    uint32_t pairs;          // L/2
-    uint32_t entries;        // P * pairs
-    uint32_t chunks;         // head chunks per position
-    uint32_t bs;             // B*S
-    uint32_t items;          // ceil(B*S / P) * chunks
-    FastDiv span_div, lanes_div, pairs_div, chunk_div, s_div;
-    // Several tensors in one launch (MULTI): N counts the heads of all of
-    // them; head n of a position belongs to the last tensor q with
-    // hoff[q] <= n (hoff past the last tensor is UINT32_MAX), which holds
-    // nt[q] heads per position and starts at xs[q].
-    v4u* xs[kMultiMax];
-    uint32_t nt[kMultiMax];
-    uint32_t hoff[kMultiMax];
-};
-
-// The row of head nl of position g in one tensor, or, MULTI, in the tensor
-// the head belongs to; as a vector pointer with the thread's vector c.
-template <bool MULTI>
-__device__ __forceinline__ v4u* pos_row_vec(const PosArgs& a, uint32_t g, uint32_t nl, uint32_t c)
-{
-    if constexpr (!MULTI) {
-        return a.x + ((g * a.N + nl) * a.row_vecs + c);
-    } else {
-        v4u* base = a.xs[0];
-        uint32_t nt = a.nt[0], ho = 0;
-#pragma unroll
-        for (int q = 1; q < kMultiMax; ++q) {
-            const bool in = nl >= a.hoff[q];
-            base = in ? a.xs[q] : base;
-            nt = in ? a.nt[q] : nt;
-            ho = in ? a.hoff[q] : ho;
-        }
-        return base + ((g * nt + (nl - ho)) * a.row_vecs + c);
-    }
-}
-
-template <int DT, int TT, int DIR, int MODE, bool MULTI>
-__global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
-{
-    __shared__ float2 cs[kPosLds];   // (cos, sin) of the block's positions, pair-major per position
-    constexpr int K = Store<DT>::kLanes;
-    constexpr int U = kUPos;
-    constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
-    const uint32_t t = threadIdx.x;
-    const uint32_t pp = fast_div(t, a.lanes_div);   // the thread's position within the block
-    const uint32_t r = t - pp * a.lanes;
-    const uint32_t hl = fast_div(r, a.span_div);
-    const uint32_t vs = r - hl * a.span;
-    const uint32_t c = a.lo_vec + vs;                 // vector within the row
-    const bool in_slice = c >= a.start_vec && c - a.start_vec < a.nvec;
-    const uint32_t v = in_slice ? c - a.start_vec : 0;
-    // rotate_half: unit v is vector v % half_vecs of the first half of group
-    // v / half_vecs (one group unless a rotary coefficient splits the slice);
-    // its lanes are pairs v*K + e either way
-    const uint32_t cx = MODE == kModeRH && a.gvec != 2 * a.nvec
-                            ? a.start_vec + (v / a.half_vecs) * a.gvec + v % a.half_vecs
-                            : c;
-    // the table entry this thread evaluates first: position eq, pair ei
-    const uint32_t eq = fast_div(t, a.pairs_div);
-    const uint32_t ei = t - eq * a.pairs;
-    // every thread runs the same iterations, so the barriers below are uniform
-    for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
-        const uint32_t grp = fast_div(w, a.chunk_div);
-        const uint32_t chunk = w - grp * a.chunks;
-        const uint32_t g0 = grp * a.P;                // first position of the block
-        const bool fill = t < a.entries && g0 + eq < a.bs;
-        const uint32_t gq = min(g0 + eq, a.bs - 1);
-        const uint32_t bq = fast_div(gq, a.s_div);
-        const int64_t p0 = a.pos[(int64_t)bq * a.pos_sb + (int64_t)(gq - bq * a.s_div.d) * a.pos_ss];
-        const double f0 = a.inv_freq[ei];
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t g = g0 + pp;
-        const bool pos_live = g < a.bs;
-        const uint32_t gl = pos_live ? g : a.bs - 1;  // past the last position: re-read it, store nothing
-        const uint32_t n0 = chunk * (a.HL * U) + hl;
-        v4u xa[U], xb[U];
-        v4u* px[U];
-        bool live[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const uint32_t n = n0 + (uint32_t)k * a.HL;
-            live[k] = pos_live && n < a.N;            // past N: re-read row N-1, store nothing
-            const uint32_t nl = n < a.N ? n : a.N - 1;
-            px[k] = pos_row_vec<MULTI>(a, gl, nl, cx);
-            xa[k] = load_x<true>(px[k]);
-            if constexpr (MODE == kModeRH) xb[k] = load_x<true>(px[k] + a.half_vecs);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
-        for (uint32_t e = t + blockDim.x; e < a.entries; e += blockDim.x) {
-            const uint32_t q = fast_div(e, a.pairs_div);
-            const uint32_t ge = g0 + q;
-            if (ge >= a.bs) break;                    // later entries belong to later positions
-            const uint32_t be = fast_div(ge, a.s_div);
-            const int64_t pe = a.pos[(int64_t)be * a.pos_sb + (int64_t)(ge - be * a.s_div.d) * a.pos_ss];
-            cs[e] = pos_cos_sin<TT>(pe, a.inv_freq[e - q * a.pairs]);
-        }
-        __syncthreads();
-        // cos and sin of the thread's lanes: interleave lane j belongs to
-        // pair j/2; rotate_half lane j of the first half to pair j, and the
-        // matching lane of the second half shares it
-        const uint32_t base = pp * a.pairs;
-        float C[K], S[K];
-#pragma unroll
-        for (int e = 0; e < K; ++e) {
-            const uint32_t i = MODE == kModeIL ? (v * K + e) / 2 : v * K + e;
-            const float2 q = cs[in_slice && pos_live ? base + i : 0];
-            C[e] = q.x;
-            S[e] = q.y;
-        }
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            if (!live[k] || !in_slice) continue;
-            Lanes<DT> X;
-            X.unpack(xa[k]);
-            if constexpr (MODE == kModeIL) {
-#pragma unroll
-                for (int i = 0; i < K; i += 2)
-                    rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C[i], S[i], C[i + 1], S[i + 1]);
-                store_x<true>(px[k], X.pack());
-            } else {
-                Lanes<DT> X2;
-                X2.unpack(xb[k]);
-#pragma unroll
-                for (int i = 0; i < K; ++i) rotate_pair<DIR, kUnfused>(X.v[i], X2.v[i], C[i], S[i], C[i], S[i]);
-                store_x<true>(px[k], X.pack());
-                store_x<true>(px[k] + a.half_vecs, X2.pack());
-            }
-        }
-        __syncthreads();   // the next item rewrites cs
-    }
-}
-
-// Out of place with the tables computed from positions: x (the output)
-// receives src with the slice rotated, in one pass over whole rows. A thread
-// covers one vector of a row: outside the slice it copies it, inside it
-// rotates it (interleave: the pairs within the vector; rotate_half: with the
-// partner vector, the matching one in the other half of its group) and
-// stores exactly that vector, with one instruction. XCHG: the partner vector
-// comes from the lane that holds it (ds_bpermute; rows of 64/k vectors, so a
-// row's threads never straddle a wave); otherwise it is loaded from src as
-// well. Blocks, positions, loads and the LDS entries are those of the
-// in-place kernel above.
-template <int DT, int TT, int DIR, int MODE, bool XCHG>
-__global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
-{
-    __shared__ float2 cs[kPosLds];
-    constexpr int K = Store<DT>::kLanes;
-    constexpr int U = pos_out_heads(MODE);
-    constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
-    const uint32_t t = threadIdx.x;
-    const uint32_t pp = fast_div(t, a.lanes_div);
-    const uint32_t r = t - pp * a.lanes;
-    const uint32_t hl = fast_div(r, a.span_div);
-    const uint32_t c = r - hl * a.span;               // vector within the row (the threads cover the row)
-    const uint32_t rel = c - a.start_vec;             // slice-relative (wraps below the slice)
-    const bool in_slice = c >= a.start_vec && rel < (MODE == kModeIL ? a.nvec : 2 * a.nvec);
-    // rotate_half: the group of the thread's vector, its place in the group,
-    // whether it lies in the first half, its partner, and the first-half
-    // unit whose lanes are pairs unit*K + e
-    const uint32_t grp = MODE == kModeRH && in_slice ? rel / a.gvec : 0;
-    const uint32_t grel = rel - grp * a.gvec;
-    const bool first = MODE == kModeIL || grel < a.half_vecs;
-    const uint32_t partner = MODE == kModeRH && in_slice ? (first ? c + a.half_vecs : c - a.half_vecs) : c;
-    const uint32_t unit = grp * a.half_vecs + (first ? grel : grel - a.half_vecs);
-    // the partner term is subtracted on the first half forward, on the second backward
-    const bool neg = DIR == kFwd ? first : !first;
-    // XCHG: byte address of the partner's lane for ds_bpermute (the lane
-    // itself outside the slice)
-    const int xlane = XCHG ? (int)((t & 63u) + (partner - c)) * 4 : 0;
-    const uint32_t eq = fast_div(t, a.pairs_div);
-    const uint32_t ei = t - eq * a.pairs;
-    for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
-        const uint32_t grpb = fast_div(w, a.chunk_div);
-        const uint32_t chunk = w - grpb * a.chunks;
-        const uint32_t g0 = grpb * a.P;
-        const bool fill = t < a.entries && g0 + eq < a.bs;
-        const uint32_t gq = min(g0 + eq, a.bs - 1);
-        const uint32_t bq = fast_div(gq, a.s_div);
-        const int64_t p0 = a.pos[(int64_t)bq * a.pos_sb + (int64_t)(gq - bq * a.s_div.d) * a.pos_ss];
-        const double f0 = a.inv_freq[ei];
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t g = g0 + pp;
-        const bool pos_live = g < a.bs;
-        const uint32_t gl = pos_live ? g : a.bs - 1;
-        const uint32_t n0 = chunk * (a.HL * U) + hl;
-        v4u xa[U], xb[U];
-        uint32_t off[U];
-        bool live[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            const uint32_t n = n0 + (uint32_t)k * a.HL;
-            live[k] = pos_live && n < a.N;
-            const uint32_t nl = n < a.N ? n : a.N - 1;
-            const uint32_t row = (gl * a.N + nl) * a.row_vecs;
-            off[k] = row + c;
-            xa[k] = load_x<true>(a.src + off[k]);
-            if constexpr (MODE == kModeRH && !XCHG) xb[k] = load_x<true>(a.src + row + partner);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (MODE == kModeRH && XCHG) {
-            // every lane takes part (no branch on the lane's own position yet)
-#pragma unroll
-            for (int k = 0; k < U; ++k) xb[k] = lane_exchange(xa[k], xlane);
-        }
-        if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
-        for (uint32_t e = t + blockDim.x; e < a.entries; e += blockDim.x) {
-            const uint32_t q = fast_div(e, a.pairs_div);
-            const uint32_t ge = g0 + q;
-            if (ge >= a.bs) break;
-            const uint32_t be = fast_div(ge, a.s_div);
-            const int64_t pe = a.pos[(int64_t)be * a.pos_sb + (int64_t)(ge - be * a.s_div.d) * a.pos_ss];
-            cs[e] = pos_cos_sin<TT>(pe, a.inv_freq[e - q * a.pairs]);
-        }
-        __syncthreads();
-        const uint32_t base = pp * a.pairs;
-        float C[K], S[K];
-#pragma unroll
-        for (int e = 0; e < K; ++e) {
-            const uint32_t i = MODE == kModeIL ? (rel * K + e) / 2 : unit * K + e;
-            const float2 q = cs[in_slice && pos_live ? base + i : 0];
-            C[e] = q.x;
-            S[e] = q.y;
-        }
-#pragma unroll
-        for (int k = 0; k < U; ++k) {
-            if (!live[k]) continue;
-            v4u y = xa[k];
-            if (in_slice) {
-                Lanes<DT> X;
-                X.unpack(xa[k]);
-                if constexpr (MODE == kModeIL) {
-#pragma unroll
-                    for (int i = 0; i < K; i += 2)
-                        rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C[i], S[i], C[i + 1], S[i + 1]);
-                } else {
-                    Lanes<DT> Pv;
-                    Pv.unpack(xb[k]);
-#pragma unroll
-                    for (int i = 0; i < K; ++i) X.v[i] = rotate_own<kUnfused>(X.v[i], Pv.v[i], C[i], S[i], neg);
-                }
-                y = X.pack();
-            }
-            store_x<true>(a.x + off[k], y);
-        }
-        __syncthreads();
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Scalar kernel: the general kernel from 2^31 rows on (the row kernel below
-// takes fewer). Any alignment, any start parity, any slice length; one
-// thread per rotation pair; 64-bit indexing throughout.
-// ---------------------------------------------------------------------------
-struct ScalarArgs {
-    void* x;
-    const void* r1;
-    const void* r2;
-    const int64_t* pos;     // POS: positions (position of (b,s) at pos[b*pos_sb + s*pos_ss])
-    const double* inv_freq; // POS: L/2 frequencies
-    int64_t pos_sb, pos_ss;
-    int64_t S, N, D, start, L;
-    int64_t half;           // rotate_half: lanes between a pair's lanes (L/2, or L/c for a coefficient c)
-    int64_t pairs;          // pairs per row = L/2
-    int64_t items;          // rows * pairs
-    int64_t t1b, t1s, t1n;  // cos strides in elements (0 = broadcast)
-    int64_t t2b, t2s, t2n;
-};
-
-template <int DT, int TT, int DIR, int MODE, bool POS>
-__global__ void __launch_bounds__(256) rope_scalar_kernel(ScalarArgs a)
-{
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < a.items; i += stride) {
-        const int64_t row = i / a.pairs;
-        const int64_t q = i - row * a.pairs;
-        // negated-partner lane: interleave 2q; rotate_half lane q % half of
-        // the first half of group q / half (q itself when the slice is one group)
-        const int64_t j = MODE == kModeIL ? 2 * q : (q / a.half) * 2 * a.half + q % a.half;
-        const int64_t pj = MODE == kModeIL ? 2 * q + 1 : j + a.half;
-        const int64_t n = row % a.N;
-        const int64_t bs = row / a.N;
-        const int64_t s = bs % a.S;
-        const int64_t b = bs / a.S;
-        const int64_t xo = row * a.D + a.start;
-        float xa = Store<DT>::load1(a.x, xo + j);
-        float xb = Store<DT>::load1(a.x, xo + pj);
-        float ca, cb, sa, sb;
-        if constexpr (POS) {
-            // both lanes of pair q share its angle
-            const float2 t = pos_cos_sin<TT>(a.pos[b * a.pos_sb + s * a.pos_ss], a.inv_freq[q]);
-            ca = cb = t.x;
-            sa = sb = t.y;
-        } else {
-            const int64_t co = b * a.t1b + s * a.t1s + n * a.t1n;
-            const int64_t so = b * a.t2b + s * a.t2s + n * a.t2n;
-            ca = Store<TT>::load1(a.r1, co + j);
-            cb = Store<TT>::load1(a.r1, co + pj);
-            sa = Store<TT>::load1(a.r2, so + j);
-            sb = Store<TT>::load1(a.r2, so + pj);
-        }
-        rotate_pair<DIR, DT != ROPE_DTYPE_F32>(xa, xb, ca, sa, cb, sb);
-        Store<DT>::store1(a.x, xo + j, xa);
-        Store<DT>::store1(a.x, xo + pj, xb);
-    }
-}
-
-// Row kernel: the general kernel for fewer than 2^31 rows. A block holds
-// rpb rows of tpr threads; thread (lr, q0) of the block takes pairs q0,
-// q0 + tpr, ... of row g*rpb + lr for each row group g it visits. The row,
-// head and position come from launch-constant divisions (multiply-high and
-// shift); element offsets stay 64-bit.
-struct RowArgs {
-    void* x;
-    const void* r1;
-    const void* r2;
-    const int64_t* pos;     // POS: positions (position of (b,s) at pos[b*pos_sb + s*pos_ss])
-    const double* inv_freq; // POS: L/2 frequencies
-    int64_t pos_sb, pos_ss;
-    int64_t D, start;       // row length and slice start, elements
-    int64_t t1b, t1s, t1n;  // cos strides in elements (0 = broadcast)
-    int64_t t2b, t2s, t2n;
-    uint32_t L, pairs;      // slice length and rotation pairs per row
-    uint32_t half;          // rotate_half: lanes between a pair's lanes (L/2, or L/c for a coefficient c)
-    FastDiv half_div;
-    uint32_t rows, N;
-    uint32_t rpb, tpr;      // rows per block, threads per row
-    uint32_t groups;        // ceil(rows / rpb)
-    FastDiv tpr_div, n_div, s_div;
-};
-
-template <int DT, int TT, int DIR, int MODE, bool POS>
-__global__ void __launch_bounds__(256) rope_rows_kernel(RowArgs a)
-{
-    const uint32_t t = threadIdx.x;
-    const uint32_t lr = fast_div(t, a.tpr_div);
-    const uint32_t q0 = t - lr * a.tpr;
-    if (lr >= a.rpb) return;
-    for (uint32_t g = blockIdx.x; g < a.groups; g += gridDim.x) {
-        const uint32_t row = g * a.rpb + lr;
-        if (row >= a.rows) return;  // later groups hold larger rows
-        const uint32_t bs = fast_div(row, a.n_div);
-        const uint32_t n = row - bs * a.N;
-        const uint32_t b = fast_div(bs, a.s_div);
-        const uint32_t s = bs - b * a.s_div.d;
-        const int64_t xo = (int64_t)row * a.D + a.start;
-        const int64_t co = b * a.t1b + s * a.t1s + n * a.t1n;
-        const int64_t so = b * a.t2b + s * a.t2s + n * a.t2n;
-        const int64_t p = POS ? a.pos[b * a.pos_sb + s * a.pos_ss] : 0;
-        for (uint32_t q = q0; q < a.pairs; q += a.tpr) {
-            // negated-partner lane (see the scalar kernel)
-            const uint32_t g = MODE == kModeIL ? 0 : fast_div(q, a.half_div);
-            const uint32_t j = MODE == kModeIL ? 2 * q : g * 2 * a.half + (q - g * a.half);
-            const uint32_t pj = MODE == kModeIL ? 2 * q + 1 : j + a.half;
-            float xa = Store<DT>::load1(a.x, xo + j);
-            float xb = Store<DT>::load1(a.x, xo + pj);
-            float ca, cb, sa, sb;
-            if constexpr (POS) {
-                // both lanes of pair q share its angle
-                const float2 t = pos_cos_sin<TT>(p, a.inv_freq[q]);
-                ca = cb = t.x;
-                sa = sb = t.y;
-            } else {
-                ca = Store<TT>::load1(a.r1, co + j);
-                cb = Store<TT>::load1(a.r1, co + pj);
-                sa = Store<TT>::load1(a.r2, so + j);
-                sb = Store<TT>::load1(a.r2, so + pj);
-            }
-            rotate_pair<DIR, DT != ROPE_DTYPE_F32>(xa, xb, ca, sa, cb, sb);
-            Store<DT>::store1(a.x, xo + j, xa);
-            Store<DT>::store1(a.x, xo + pj, xb);
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Host side

@@ -1,0 +1,354 @@
+// rope_pos_kernels.hpp -- the vector kernels that compute cos/sin from positions
+// (in place, out of place, several tensors).
+// Included once, by rope_kernels.hip (the one translation unit of the
+// library): its kernels are instantiated there, next to the host code
+// that selects and launches them.
+#pragma once
+
+#include "rope_vec_kernels.hpp"
+
+namespace rope {
+namespace {
+
+// ---------------------------------------------------------------------------
+// cos and sin from positions ("ANE实战RoPE位置编码在MIL中的纯ANE实现", section
+// 第一步: the table of θ = p / base^(2i/h), here θ = p * inv_freq[i] with the
+// frequencies given): θ is the double product of the position and the pair's
+// frequency, cos θ and sin θ are evaluated in double precision and rounded
+// once, to nearest even, to the table type TT.
+// ---------------------------------------------------------------------------
+
+// A double rounded once to the nearest value of TT, ties to even, returned
+// as the float that holds it. fp32: the conversion instruction (round to
+// nearest even). bf16/fp16: a value of the type is a whole number of units
+// in the last place of its binade, 2^(e - p) for |v| in [2^(e-1), 2^e) with
+// p significand bits, and never below the least subnormal 2^(emin - p + 1);
+// scaling by powers of two is exact and rint() rounds ties to even.
+template <int TT>
+__device__ __forceinline__ float round_to_type(double v)
+{
+    if constexpr (TT == ROPE_DTYPE_F32) {
+        return static_cast<float>(v);
+    } else {
+        constexpr int p = TT == ROPE_DTYPE_F16 ? 11 : 8;
+        constexpr int emin = TT == ROPE_DTYPE_F16 ? -14 : -126;
+        constexpr double maxf = TT == ROPE_DTYPE_F16 ? 65504.0 : 0x1.fep127;
+        if (!(v != 0.0) || !__builtin_isfinite(v)) return static_cast<float>(v);   // zero, inf, NaN
+        int e;
+        (void)frexp(v, &e);
+        const int q = e - p > emin - p + 1 ? e - p : emin - p + 1;
+        const double r = ldexp(rint(ldexp(v, -q)), q);
+        if (fabs(r) > maxf) return v > 0 ? __builtin_inff() : -__builtin_inff();
+        return static_cast<float>(r);   // exact: r is a value of TT
+    }
+}
+
+// (cos θ, sin θ) rounded to TT for position p and frequency f.
+template <int TT>
+__device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
+{
+    double sn, cn;
+    sincos(static_cast<double>(p) * f, &sn, &cn);
+    return make_float2(round_to_type<TT>(cn), round_to_type<TT>(sn));
+}
+
+// ---------------------------------------------------------------------------
+// Vector kernel with the tables computed from positions. A block takes P
+// consecutive (b,s) positions (P > 1 only when one position's heads fill
+// fewer than kPosLanes threads) and, for each, a chunk of up to HL*kUPos
+// heads (HL head lanes, kUPos heads per thread). Its threads first load the
+// position and frequency of the first (cos, sin) pair each evaluates, then
+// issue their x loads, then evaluate cos and sin while x is in flight: the
+// memory counter drains in issue order, so the wait for the frequency does
+// not wait for x, provided every load is issued on every path (indices are
+// clamped, never branched around). The values go to LDS, each pair of each
+// position once per block, and each thread reads those of its lanes from
+// there. The thread layout is the table kernel's: interleave with
+// whole-line coverage, rotate_half as pair owner (a thread takes vector k
+// of both halves). Measured on MI355X (the (16,8192,32,128) shard's slice
+// [32,96), the GQA Q layout at 4096 positions, the MLA-style slice): two
+// heads per thread in 128-thread blocks was the best of 1, 2, 4 or 8 heads
+// per thread in 64-, 128- or 256-thread blocks on all three, and as fast as
+// the table kernel on the first two.
+// ---------------------------------------------------------------------------
+constexpr int kUPos = 2;
+constexpr int kPosLds = ROPE_D_LIMIT / 2;    // (cos, sin) entries per block
+constexpr uint32_t kPosLanes = 128;          // threads a position's heads fill before a block takes more positions
+// The out-of-place position kernel's heads per thread and threads per
+// position, by mode. Measured on MI355X (cold data; the (16,8192,32,128)
+// shard's lanes [32,96), the MLA-style slice, a whole rotate_half head and
+// its second half), over 1, 2 or 4 heads per thread in blocks of 64, 128 or
+// 256 threads: interleave was fastest with 2 heads in 128 threads (326 and
+// 257 us), rotate_half with 4 heads in 64 threads (165 and 164 us, the table
+// path's times; 172 and 167 us with the interleave shape).
+constexpr int pos_out_heads(int mode) { return mode == kModeIL ? 2 : 4; }
+constexpr uint32_t pos_out_lanes(int mode) { return mode == kModeIL ? 128 : 64; }
+
+struct PosArgs {
+    v4u* x;                  // the tensor written (in place: also read)
+    const v4u* src;          // out of place: the tensor read
+    const int64_t* pos;      // position of (b,s) at pos[b*pos_sb + s*pos_ss]
+    const double* inv_freq;  // L/2 frequencies
+    int64_t pos_sb, pos_ss;
+    uint32_t row_vecs;       // vectors per row of x
+    uint32_t start_vec;      // first slice vector within a row
+    uint32_t lo_vec;         // first vector the threads of a row cover
+    uint32_t half_vecs;      // rotate_half: vectors per half of a group (pair distance)
+    uint32_t gvec;           // rotate_half: vectors per group (2*half_vecs)
+    uint32_t nvec;           // work units per row (interleave: slice vectors; rotate_half: half of them)
+    uint32_t span;           // vectors per row the threads cover
+    uint32_t HL;             // head lanes per position
+    uint32_t lanes;          // threads per position: span * HL
+    uint32_t P;              // positions per block
+    uint32_t N;
+    uint32_t pairs;          // L/2
+    uint32_t entries;        // P * pairs
+    uint32_t chunks;         // head chunks per position
+    uint32_t bs;             // B*S
+    uint32_t items;          // ceil(B*S / P) * chunks
+    FastDiv span_div, lanes_div, pairs_div, chunk_div, s_div;
+    // Several tensors in one launch (MULTI): N counts the heads of all of
+    // them; head n of a position belongs to the last tensor q with
+    // hoff[q] <= n (hoff past the last tensor is UINT32_MAX), which holds
+    // nt[q] heads per position and starts at xs[q].
+    v4u* xs[kMultiMax];
+    uint32_t nt[kMultiMax];
+    uint32_t hoff[kMultiMax];
+};
+
+// The row of head nl of position g in one tensor, or, MULTI, in the tensor
+// the head belongs to; as a vector pointer with the thread's vector c.
+template <bool MULTI>
+__device__ __forceinline__ v4u* pos_row_vec(const PosArgs& a, uint32_t g, uint32_t nl, uint32_t c)
+{
+    if constexpr (!MULTI) {
+        return a.x + ((g * a.N + nl) * a.row_vecs + c);
+    } else {
+        v4u* base = a.xs[0];
+        uint32_t nt = a.nt[0], ho = 0;
+#pragma unroll
+        for (int q = 1; q < kMultiMax; ++q) {
+            const bool in = nl >= a.hoff[q];
+            base = in ? a.xs[q] : base;
+            nt = in ? a.nt[q] : nt;
+            ho = in ? a.hoff[q] : ho;
+        }
+        return base + ((g * nt + (nl - ho)) * a.row_vecs + c);
+    }
+}
+
+template <int DT, int TT, int DIR, int MODE, bool MULTI>
+__global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
+{
+    __shared__ float2 cs[kPosLds];   // (cos, sin) of the block's positions, pair-major per position
+    constexpr int K = Store<DT>::kLanes;
+    constexpr int U = kUPos;
+    constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
+    const uint32_t t = threadIdx.x;
+    const uint32_t pp = fast_div(t, a.lanes_div);   // the thread's position within the block
+    const uint32_t r = t - pp * a.lanes;
+    const uint32_t hl = fast_div(r, a.span_div);
+    const uint32_t vs = r - hl * a.span;
+    const uint32_t c = a.lo_vec + vs;                 // vector within the row
+    const bool in_slice = c >= a.start_vec && c - a.start_vec < a.nvec;
+    const uint32_t v = in_slice ? c - a.start_vec : 0;
+    // rotate_half: unit v is vector v % half_vecs of the first half of group
+    // v / half_vecs (one group unless a rotary coefficient splits the slice);
+    // its lanes are pairs v*K + e either way
+    const uint32_t cx = MODE == kModeRH && a.gvec != 2 * a.nvec
+                            ? a.start_vec + (v / a.half_vecs) * a.gvec + v % a.half_vecs
+                            : c;
+    // the table entry this thread evaluates first: position eq, pair ei
+    const uint32_t eq = fast_div(t, a.pairs_div);
+    const uint32_t ei = t - eq * a.pairs;
+    // every thread runs the same iterations, so the barriers below are uniform
+    for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
+        const uint32_t grp = fast_div(w, a.chunk_div);
+        const uint32_t chunk = w - grp * a.chunks;
+        const uint32_t g0 = grp * a.P;                // first position of the block
+        const bool fill = t < a.entries && g0 + eq < a.bs;
+        const uint32_t gq = min(g0 + eq, a.bs - 1);
+        const uint32_t bq = fast_div(gq, a.s_div);
+        const int64_t p0 = a.pos[(int64_t)bq * a.pos_sb + (int64_t)(gq - bq * a.s_div.d) * a.pos_ss];
+        const double f0 = a.inv_freq[ei];
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t g = g0 + pp;
+        const bool pos_live = g < a.bs;
+        const uint32_t gl = pos_live ? g : a.bs - 1;  // past the last position: re-read it, store nothing
+        const uint32_t n0 = chunk * (a.HL * U) + hl;
+        v4u xa[U], xb[U];
+        v4u* px[U];
+        bool live[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t n = n0 + (uint32_t)k * a.HL;
+            live[k] = pos_live && n < a.N;            // past N: re-read row N-1, store nothing
+            const uint32_t nl = n < a.N ? n : a.N - 1;
+            px[k] = pos_row_vec<MULTI>(a, gl, nl, cx);
+            xa[k] = load_x<true>(px[k]);
+            if constexpr (MODE == kModeRH) xb[k] = load_x<true>(px[k] + a.half_vecs);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
+        for (uint32_t e = t + blockDim.x; e < a.entries; e += blockDim.x) {
+            const uint32_t q = fast_div(e, a.pairs_div);
+            const uint32_t ge = g0 + q;
+            if (ge >= a.bs) break;                    // later entries belong to later positions
+            const uint32_t be = fast_div(ge, a.s_div);
+            const int64_t pe = a.pos[(int64_t)be * a.pos_sb + (int64_t)(ge - be * a.s_div.d) * a.pos_ss];
+            cs[e] = pos_cos_sin<TT>(pe, a.inv_freq[e - q * a.pairs]);
+        }
+        __syncthreads();
+        // cos and sin of the thread's lanes: interleave lane j belongs to
+        // pair j/2; rotate_half lane j of the first half to pair j, and the
+        // matching lane of the second half shares it
+        const uint32_t base = pp * a.pairs;
+        float C[K], S[K];
+#pragma unroll
+        for (int e = 0; e < K; ++e) {
+            const uint32_t i = MODE == kModeIL ? (v * K + e) / 2 : v * K + e;
+            const float2 q = cs[in_slice && pos_live ? base + i : 0];
+            C[e] = q.x;
+            S[e] = q.y;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (!live[k] || !in_slice) continue;
+            Lanes<DT> X;
+            X.unpack(xa[k]);
+            if constexpr (MODE == kModeIL) {
+#pragma unroll
+                for (int i = 0; i < K; i += 2)
+                    rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C[i], S[i], C[i + 1], S[i + 1]);
+                store_x<true>(px[k], X.pack());
+            } else {
+                Lanes<DT> X2;
+                X2.unpack(xb[k]);
+#pragma unroll
+                for (int i = 0; i < K; ++i) rotate_pair<DIR, kUnfused>(X.v[i], X2.v[i], C[i], S[i], C[i], S[i]);
+                store_x<true>(px[k], X.pack());
+                store_x<true>(px[k] + a.half_vecs, X2.pack());
+            }
+        }
+        __syncthreads();   // the next item rewrites cs
+    }
+}
+
+// Out of place with the tables computed from positions: x (the output)
+// receives src with the slice rotated, in one pass over whole rows. A thread
+// covers one vector of a row: outside the slice it copies it, inside it
+// rotates it (interleave: the pairs within the vector; rotate_half: with the
+// partner vector, the matching one in the other half of its group) and
+// stores exactly that vector, with one instruction. XCHG: the partner vector
+// comes from the lane that holds it (ds_bpermute; rows of 64/k vectors, so a
+// row's threads never straddle a wave); otherwise it is loaded from src as
+// well. Blocks, positions, loads and the LDS entries are those of the
+// in-place kernel above.
+template <int DT, int TT, int DIR, int MODE, bool XCHG>
+__global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
+{
+    __shared__ float2 cs[kPosLds];
+    constexpr int K = Store<DT>::kLanes;
+    constexpr int U = pos_out_heads(MODE);
+    constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
+    const uint32_t t = threadIdx.x;
+    const uint32_t pp = fast_div(t, a.lanes_div);
+    const uint32_t r = t - pp * a.lanes;
+    const uint32_t hl = fast_div(r, a.span_div);
+    const uint32_t c = r - hl * a.span;               // vector within the row (the threads cover the row)
+    const uint32_t rel = c - a.start_vec;             // slice-relative (wraps below the slice)
+    const bool in_slice = c >= a.start_vec && rel < (MODE == kModeIL ? a.nvec : 2 * a.nvec);
+    // rotate_half: the group of the thread's vector, its place in the group,
+    // whether it lies in the first half, its partner, and the first-half
+    // unit whose lanes are pairs unit*K + e
+    const uint32_t grp = MODE == kModeRH && in_slice ? rel / a.gvec : 0;
+    const uint32_t grel = rel - grp * a.gvec;
+    const bool first = MODE == kModeIL || grel < a.half_vecs;
+    const uint32_t partner = MODE == kModeRH && in_slice ? (first ? c + a.half_vecs : c - a.half_vecs) : c;
+    const uint32_t unit = grp * a.half_vecs + (first ? grel : grel - a.half_vecs);
+    // the partner term is subtracted on the first half forward, on the second backward
+    const bool neg = DIR == kFwd ? first : !first;
+    // XCHG: byte address of the partner's lane for ds_bpermute (the lane
+    // itself outside the slice)
+    const int xlane = XCHG ? (int)((t & 63u) + (partner - c)) * 4 : 0;
+    const uint32_t eq = fast_div(t, a.pairs_div);
+    const uint32_t ei = t - eq * a.pairs;
+    for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
+        const uint32_t grpb = fast_div(w, a.chunk_div);
+        const uint32_t chunk = w - grpb * a.chunks;
+        const uint32_t g0 = grpb * a.P;
+        const bool fill = t < a.entries && g0 + eq < a.bs;
+        const uint32_t gq = min(g0 + eq, a.bs - 1);
+        const uint32_t bq = fast_div(gq, a.s_div);
+        const int64_t p0 = a.pos[(int64_t)bq * a.pos_sb + (int64_t)(gq - bq * a.s_div.d) * a.pos_ss];
+        const double f0 = a.inv_freq[ei];
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t g = g0 + pp;
+        const bool pos_live = g < a.bs;
+        const uint32_t gl = pos_live ? g : a.bs - 1;
+        const uint32_t n0 = chunk * (a.HL * U) + hl;
+        v4u xa[U], xb[U];
+        uint32_t off[U];
+        bool live[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const uint32_t n = n0 + (uint32_t)k * a.HL;
+            live[k] = pos_live && n < a.N;
+            const uint32_t nl = n < a.N ? n : a.N - 1;
+            const uint32_t row = (gl * a.N + nl) * a.row_vecs;
+            off[k] = row + c;
+            xa[k] = load_x<true>(a.src + off[k]);
+            if constexpr (MODE == kModeRH && !XCHG) xb[k] = load_x<true>(a.src + row + partner);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (MODE == kModeRH && XCHG) {
+            // every lane takes part (no branch on the lane's own position yet)
+#pragma unroll
+            for (int k = 0; k < U; ++k) xb[k] = lane_exchange(xa[k], xlane);
+        }
+        if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
+        for (uint32_t e = t + blockDim.x; e < a.entries; e += blockDim.x) {
+            const uint32_t q = fast_div(e, a.pairs_div);
+            const uint32_t ge = g0 + q;
+            if (ge >= a.bs) break;
+            const uint32_t be = fast_div(ge, a.s_div);
+            const int64_t pe = a.pos[(int64_t)be * a.pos_sb + (int64_t)(ge - be * a.s_div.d) * a.pos_ss];
+            cs[e] = pos_cos_sin<TT>(pe, a.inv_freq[e - q * a.pairs]);
+        }
+        __syncthreads();
+        const uint32_t base = pp * a.pairs;
+        float C[K], S[K];
+#pragma unroll
+        for (int e = 0; e < K; ++e) {
+            const uint32_t i = MODE == kModeIL ? (rel * K + e) / 2 : unit * K + e;
+            const float2 q = cs[in_slice && pos_live ? base + i : 0];
+            C[e] = q.x;
+            S[e] = q.y;
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            if (!live[k]) continue;
+            v4u y = xa[k];
+            if (in_slice) {
+                Lanes<DT> X;
+                X.unpack(xa[k]);
+                if constexpr (MODE == kModeIL) {
+#pragma unroll
+                    for (int i = 0; i < K; i += 2)
+                        rotate_pair<DIR, kUnfused>(X.v[i], X.v[i + 1], C[i], S[i], C[i + 1], S[i + 1]);
+                } else {
+                    Lanes<DT> Pv;
+                    Pv.unpack(xb[k]);
+#pragma unroll
+                    for (int i = 0; i < K; ++i) X.v[i] = rotate_own<kUnfused>(X.v[i], Pv.v[i], C[i], S[i], neg);
+                }
+                y = X.pack();
+            }
+            store_x<true>(a.x + off[k], y);
+        }
+        __syncthreads();
+    }
+}
+
+}  // namespace
+}  // namespace rope
