@@ -36,7 +36,7 @@ if ROOT not in sys.path:
 METRIC = "achieved HBM GB/s (% of MI355X peak) + Gelem/s, partial-RoPE fwd/bwd in place"
 PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD public spec
 KERNEL_DIR = os.path.join(ROOT, "transformer_positional_encoding_amd", "csrc")
-TRAFFIC_MD = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "rope_kernels_hbm_traffic_by_workload.md")
 
 
 def kernel_source_hash() -> str:
@@ -56,7 +56,7 @@ def kernel_source_hash() -> str:
 
 def committed_traffic(workload: str, direction: str):
     """Per-launch HBM bytes (read, write) measured by rocprofv3 for this
-    kernel source, from profiles/hbm_traffic.md; None if absent or stale."""
+    kernel source, from profiles/rope_kernels_hbm_traffic_by_workload.md; None if absent or stale."""
     if not os.path.exists(TRAFFIC_MD):
         return None
     text = open(TRAFFIC_MD, encoding="utf-8").read()
