@@ -518,21 +518,21 @@ def main() -> int:
     for name in [n for n in args.also.split(",") if n and n != args.workload]:
         import workloads as W
         if name.endswith(":out"):
-            others.append(bench_out_of_place(name[:-4], max(10, args.reps // 2), stream))
+            others.append(bench_out_of_place(name[:-4], args.reps, stream))
             continue
         if name.endswith(":pos"):
-            others.append(bench_positions(name[:-4], max(10, args.reps // 2), stream))
+            others.append(bench_positions(name[:-4], args.reps, stream))
             continue
         if name.endswith(":outpos"):
-            others.append(bench_positions(name[:-7], max(10, args.reps // 2), stream, out=True))
+            others.append(bench_positions(name[:-7], args.reps, stream, out=True))
             continue
         if name.endswith(":posmulti"):
-            others.append(bench_pos_multi(name[:-9], max(10, args.reps // 2), stream))
+            others.append(bench_pos_multi(name[:-9], args.reps, stream))
             continue
         if len(W.WORKLOADS[name].x_shapes) > 1:
-            others.append(bench_multi(name, max(10, args.reps // 2), stream))
+            others.append(bench_multi(name, args.reps, stream))
             continue
-        r = bench_workload(name, max(5, args.steps // 5), 10, max(10, args.reps // 2), stream, False, 0)
+        r = bench_workload(name, max(5, args.steps // 5), 10, args.reps, stream, False, 0)
         others.append({k: r[k] for k in ("workload", "note", "dtype", "directions", "rotating_copies",
                                          "bytes_per_launch", "elements_per_launch", "kernels")})
 
