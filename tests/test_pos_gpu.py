@@ -118,16 +118,37 @@ def test_pos_strided_positions_and_unaligned_x():
     run_pos_and_check(x, shared, f, mode, sl, "fwd", "bf16", "expanded positions", pos_dev=shared.to(DEV).expand(2, 12))
 
 
+@pytest.mark.parametrize("tdtype", ["bf16", "f32"])
 @pytest.mark.parametrize("direction", ["bwd", "fwd"])
-def test_pos_long_context_shard(direction):
+def test_pos_long_context_shard(direction, tdtype):
     """The long-context shard's x with its per-batch positions (offset + s)
-    and base 5e5, bf16 tables computed in the kernel; sampled rows."""
+    and base 5e5, bf16 or fp32 cos/sin computed in the kernel (the bench's
+    c4:pos and c4_t32:pos launches); sampled rows."""
     w = W.WORKLOADS["c4"]
     x = W.make_x(w)
     pos = torch.from_numpy(W.positions(w))
     f = rp.rope_inv_freq(w.L, w.base)
-    run_pos_and_check(x, pos, f, w.mode, w.partial_slice, direction, "bf16", f"c4 positions {direction}",
+    run_pos_and_check(x, pos, f, w.mode, w.partial_slice, direction, tdtype, f"c4 positions {direction} {tdtype}",
                       sample=4000, seed=5)
+
+
+def test_pos_multi_gqa_q_and_k_full_size():
+    """c2's Q (32,256,16,128) and K (32,256,8,128), rotate_half, in one
+    position call (the bench's c2:posmulti launch); every row of both
+    against the oracle."""
+    w = W.WORKLOADS["c2"]
+    q, k = W.make_x(w, 0), W.make_x(w, 1)
+    pos = torch.from_numpy(W.positions(w))
+    f = rp.rope_inv_freq(w.L, w.base)
+    announce("positions multi c2 Q+K full size")
+    qd, kd = q.to(DEV), k.to(DEV)
+    rp.rope_partial_fwd_inplace_pos_multi([qd, kd], pos.to(DEV), f.to(DEV), w.mode, w.partial_slice)
+    torch.cuda.synchronize()
+    c, s = oracle.pos_tables(pos.numpy(), f.numpy(), w.L, w.mode, "bf16")
+    for t, td in ((q, qd), (k, kd)):
+        want = W.to_numpy_storage(t).copy()
+        oracle.rope_rows(want, t.shape, "bf16", c, s, w.mode, w.partial_slice, "fwd", table_dtype="bf16")
+        assert np.array_equal(W.to_numpy_storage(td.cpu()), want)
 
 
 def test_pos_equals_the_table_call_with_the_oracle_tables():
