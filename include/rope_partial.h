@@ -70,6 +70,8 @@ typedef enum rope_dtype {
 /* largest supported head dimension D (the page's D limit) */
 #define ROPE_D_LIMIT 1024
 
+/* ======================== cos/sin from tables ======================== */
+
 /*
  * rope_partial_fwd_inplace -- rotate x[..., start:end) in place (forward).
  *
@@ -163,6 +165,46 @@ ROPE_API rope_status_t rope_partial_bwd_out(
     rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
     void* stream);
 
+/* largest tensor count of the _multi entry points */
+#define ROPE_MULTI_MAX 4
+
+/*
+ * rope_partial_fwd_inplace_multi / rope_partial_bwd_inplace_multi -- rotate
+ * `count` tensors that share one pair of tables (for example the Q and K of
+ * one attention layer, whose head counts differ under grouped-query
+ * attention) with one call; the result is that of calling the single-tensor
+ * entry point on xs[0], xs[1], ... in order on `stream`. When every tensor
+ * takes the same vector kernel, all of them run in a single kernel launch
+ * (one launch overhead, tables shared in cache). "ANE实战RoPE位置编码在MIL中的
+ * 纯ANE实现", section 第二步, applies the same rotation to Q and to K.
+ *
+ *   count      0..ROPE_MULTI_MAX; 0 is a no-op.
+ *   xs         host array of `count` device pointers.
+ *   x_shapes   host array of `count` shapes {B, S, N, D}.
+ *   Other arguments are those of rope_partial_fwd_inplace and apply to every
+ *   tensor: the tables must broadcast against each tensor's slice.
+ *
+ * Every tensor is checked before anything is launched: on an error no
+ * memory has been touched, and rope_last_error() names the tensor.
+ * count outside [0, ROPE_MULTI_MAX] is ROPE_ERR_INVALID; NULL xs or x_shapes
+ * with count > 0 is ROPE_ERR_NULLPTR. The tensors must not overlap.
+ */
+ROPE_API rope_status_t rope_partial_fwd_inplace_multi(
+    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+ROPE_API rope_status_t rope_partial_bwd_inplace_multi(
+    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+/* ====================== cos/sin from positions ====================== */
+
 /*
  * rope_partial_fwd_inplace_pos / rope_partial_bwd_inplace_pos -- the same
  * in-place operation with cos and sin computed from positions instead of
@@ -212,8 +254,74 @@ ROPE_API rope_status_t rope_partial_bwd_inplace_pos(
     void* stream);
 
 /*
- * rope_partial_check -- run every argument check of the entry points above
- * (either direction: they are the same) and return the status they would
+ * rope_partial_fwd_out_pos / rope_partial_bwd_out_pos -- the position forms
+ * out of place: y receives x with its slice rotated, cos and sin computed
+ * from positions exactly as rope_partial_fwd_inplace_pos does, and x is left
+ * unchanged. y == x is the in-place call. An empty slice copies x to y.
+ *
+ *   y, x         device buffers of B*S*N*D elements of `dtype`, contiguous
+ *                BSND; y is written, x is read. With both 16-byte aligned
+ *                one kernel reads x and writes y in one pass; otherwise x is
+ *                copied to y and y is rotated in place.
+ *   Other arguments are those of rope_partial_fwd_inplace_pos.
+ *
+ * Checks, in this order: the scalar arguments; an empty tensor returns
+ * ROPE_OK at once; NULL y or x (ROPE_ERR_NULLPTR); y and x overlapping
+ * without being the same buffer (ROPE_ERR_INVALID); an empty slice copies;
+ * then the checks of positions, positions_shape, positions_strides and
+ * inv_freq of the in-place form. Asynchronous on `stream`; nothing is
+ * allocated.
+ */
+ROPE_API rope_status_t rope_partial_fwd_out_pos(
+    void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+ROPE_API rope_status_t rope_partial_bwd_out_pos(
+    void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+/*
+ * rope_partial_fwd_inplace_pos_multi / rope_partial_bwd_inplace_pos_multi
+ * -- the position forms for `count` tensors that share one set of positions
+ * (the Q and K of one attention layer, whose head counts may differ); the
+ * result is that of calling rope_partial_fwd_inplace_pos on xs[0], xs[1],
+ * ... in order on `stream`. When the tensors share B, S and D and take the
+ * vector kernel, all of them run in a single launch that evaluates each
+ * pair's cos and sin once per position for every tensor. "ANE实战RoPE位置编码
+ * 在MIL中的纯ANE实现", section 第二步, applies the same rotation to Q and K.
+ *
+ *   count      0..ROPE_MULTI_MAX; 0 is a no-op.
+ *   xs         host array of `count` device pointers.
+ *   x_shapes   host array of `count` shapes {B, S, N, D}.
+ *   Other arguments are those of rope_partial_fwd_inplace_pos and apply to
+ *   every tensor: positions_shape must fit each tensor's B and S.
+ *
+ * Every tensor is checked before anything is launched: on an error no
+ * memory has been touched, and rope_last_error() names the tensor. count
+ * outside [0, ROPE_MULTI_MAX] is ROPE_ERR_INVALID; NULL xs or x_shapes with
+ * count > 0 is ROPE_ERR_NULLPTR. The tensors must not overlap.
+ */
+ROPE_API rope_status_t rope_partial_fwd_inplace_pos_multi(
+    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+ROPE_API rope_status_t rope_partial_bwd_inplace_pos_multi(
+    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
+    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
+    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
+
+/* ====================== checks and launch plans ====================== */
+
+/*
+ * rope_partial_check -- run every argument check of rope_partial_fwd_inplace
+ * (either direction: they are the same) and return the status it would
  * return, without launching anything or touching device memory. For callers
  * that validate ahead of time, as the page's graph-mode meta implementation
  * does at compile time (section 调用说明, graph mode). Pointers are only
@@ -257,70 +365,6 @@ ROPE_API rope_status_t rope_partial_launch_info(
     int64_t info[ROPE_LAUNCH_INFO_LEN]);
 
 /*
- * rope_partial_fwd_inplace_pos_multi / rope_partial_bwd_inplace_pos_multi
- * -- the position forms for `count` tensors that share one set of positions
- * (the Q and K of one attention layer, whose head counts may differ); the
- * result is that of calling rope_partial_fwd_inplace_pos on xs[0], xs[1],
- * ... in order on `stream`. When the tensors share B, S and D and take the
- * vector kernel, all of them run in a single launch that evaluates each
- * pair's cos and sin once per position for every tensor. "ANE实战RoPE位置编码
- * 在MIL中的纯ANE实现", section 第二步, applies the same rotation to Q and K.
- *
- *   count      0..ROPE_MULTI_MAX; 0 is a no-op.
- *   xs         host array of `count` device pointers.
- *   x_shapes   host array of `count` shapes {B, S, N, D}.
- *   Other arguments are those of rope_partial_fwd_inplace_pos and apply to
- *   every tensor: positions_shape must fit each tensor's B and S.
- *
- * Every tensor is checked before anything is launched: on an error no
- * memory has been touched, and rope_last_error() names the tensor. count
- * outside [0, ROPE_MULTI_MAX] is ROPE_ERR_INVALID; NULL xs or x_shapes with
- * count > 0 is ROPE_ERR_NULLPTR. The tensors must not overlap.
- */
-ROPE_API rope_status_t rope_partial_fwd_inplace_pos_multi(
-    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
-    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
-    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
-    void* stream);
-
-ROPE_API rope_status_t rope_partial_bwd_inplace_pos_multi(
-    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
-    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
-    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
-    void* stream);
-
-/*
- * rope_partial_fwd_out_pos / rope_partial_bwd_out_pos -- the position forms
- * out of place: y receives x with its slice rotated, cos and sin computed
- * from positions exactly as rope_partial_fwd_inplace_pos does, and x is left
- * unchanged. y == x is the in-place call. An empty slice copies x to y.
- *
- *   y, x         device buffers of B*S*N*D elements of `dtype`, contiguous
- *                BSND; y is written, x is read. With both 16-byte aligned
- *                one kernel reads x and writes y in one pass; otherwise x is
- *                copied to y and y is rotated in place.
- *   Other arguments are those of rope_partial_fwd_inplace_pos.
- *
- * Checks, in this order: the scalar arguments; an empty tensor returns
- * ROPE_OK at once; NULL y or x (ROPE_ERR_NULLPTR); y and x overlapping
- * without being the same buffer (ROPE_ERR_INVALID); an empty slice copies;
- * then the checks of positions, positions_shape, positions_strides and
- * inv_freq of the in-place form. Asynchronous on `stream`; nothing is
- * allocated.
- */
-ROPE_API rope_status_t rope_partial_fwd_out_pos(
-    void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
-    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
-    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
-    void* stream);
-
-ROPE_API rope_status_t rope_partial_bwd_out_pos(
-    void* y, const void* x, const int64_t x_shape[4], rope_dtype_t dtype,
-    const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
-    const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
-    void* stream);
-
-/*
  * rope_partial_launch_info_pos -- the launch plan of an in-place position
  * call (rope_partial_fwd_inplace_pos / _bwd_inplace_pos) with these arguments,
  * for tests and profiling. Runs that call's checks first and returns their
@@ -343,43 +387,7 @@ ROPE_API rope_status_t rope_partial_launch_info_pos(
     const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
     int64_t info[ROPE_LAUNCH_INFO_LEN]);
 
-/* largest tensor count of the _multi entry points */
-#define ROPE_MULTI_MAX 4
-
-/*
- * rope_partial_fwd_inplace_multi / rope_partial_bwd_inplace_multi -- rotate
- * `count` tensors that share one pair of tables (for example the Q and K of
- * one attention layer, whose head counts differ under grouped-query
- * attention) with one call; the result is that of calling the single-tensor
- * entry point on xs[0], xs[1], ... in order on `stream`. When every tensor
- * takes the same vector kernel, all of them run in a single kernel launch
- * (one launch overhead, tables shared in cache). "ANE实战RoPE位置编码在MIL中的
- * 纯ANE实现", section 第二步, applies the same rotation to Q and to K.
- *
- *   count      0..ROPE_MULTI_MAX; 0 is a no-op.
- *   xs         host array of `count` device pointers.
- *   x_shapes   host array of `count` shapes {B, S, N, D}.
- *   Other arguments are those of rope_partial_fwd_inplace and apply to every
- *   tensor: the tables must broadcast against each tensor's slice.
- *
- * Every tensor is checked before anything is launched: on an error no
- * memory has been touched, and rope_last_error() names the tensor.
- * count outside [0, ROPE_MULTI_MAX] is ROPE_ERR_INVALID; NULL xs or x_shapes
- * with count > 0 is ROPE_ERR_NULLPTR. The tensors must not overlap.
- */
-ROPE_API rope_status_t rope_partial_fwd_inplace_multi(
-    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
-    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
-    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
-    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
-    void* stream);
-
-ROPE_API rope_status_t rope_partial_bwd_inplace_multi(
-    int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
-    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
-    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
-    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
-    void* stream);
+/* ============================== status ============================== */
 
 /* Static text for a status code; never NULL. */
 ROPE_API const char* rope_status_string(rope_status_t status);
