@@ -227,15 +227,17 @@ def test_pos_plan_of_the_long_context_shard():
                  "head_lanes": 8, "positions_per_block": 1, "head_chunks": 2, "row_vectors": 16}
 
 
-@pytest.mark.parametrize("x_shape,dtype,sl,mode,kernel,P", [
-    ((2, 7, 1, 128), "bf16", (0, 128), RH, "vector", 8),     # one head: 8 rows of 8 threads per block
-    ((3, 5, 2, 64), "bf16", (0, 64), IL, "vector", 8),
-    ((2, 5, 3, 1024), "f32", (0, 1024), RH, "vector", 1),    # 512 pairs: the whole LDS table
-    ((2, 6, 5, 64), "bf16", (3, 35), IL, "rows", None),      # odd start
-    ((2, 5, 3, 48), "bf16", (4, 44), RH, "rows", None),      # halves of 40 bytes
+@pytest.mark.parametrize("x_shape,dtype,sl,mode,per_batch,kernel,P", [
+    ((2, 7, 1, 128), "bf16", (0, 128), RH, True, "vector", 8),   # one head: 8 positions of 8 threads per block
+    ((3, 5, 2, 64), "bf16", (0, 64), IL, True, "vector", 8),
+    ((2, 7, 1, 128), "bf16", (0, 128), RH, False, "vector", 8),  # shared positions: 2 batches x 1 head per s
+    ((3, 5, 2, 64), "bf16", (0, 64), IL, False, "vector", 2),    # 3 batches x 2 heads per s
+    ((2, 5, 3, 1024), "f32", (0, 1024), RH, False, "vector", 1),  # 512 pairs: the whole LDS table
+    ((2, 6, 5, 64), "bf16", (3, 35), IL, False, "rows", None),    # odd start
+    ((2, 5, 3, 48), "bf16", (4, 44), RH, False, "rows", None),    # halves of 40 bytes
 ])
-def test_pos_plan_kernels(x_shape, dtype, sl, mode, kernel, P):
-    st, p = pos_plan(x_shape, dtype, sl, mode)
+def test_pos_plan_kernels(x_shape, dtype, sl, mode, per_batch, kernel, P):
+    st, p = pos_plan(x_shape, dtype, sl, mode, per_batch=per_batch)
     assert st == rp.ROPE_OK and p["kernel"] == kernel
     if P is not None:
         assert p["positions_per_block"] == P
@@ -250,7 +252,9 @@ def test_pos_plan_invariants_over_random_shapes():
     threads; the LDS table (positions per block x L/2 pairs) within 512
     entries; the head chunks cover N exactly; the rows' threads cover the
     slice; several positions per block only when a position's heads fill
-    fewer than 128 threads; one block per chunk of positions."""
+    fewer than 128 threads; one block per chunk of positions. When the
+    positions are shared by the batch, the positions are the S values and
+    the heads the B*N (b, n) pairs."""
     import random
     rng = random.Random(5)
     seen = {"vector": 0, "rows": 0}
@@ -265,7 +269,9 @@ def test_pos_plan_invariants_over_random_shapes():
             continue
         mode = rng.choice([IL, RH])
         B, S, N = rng.randint(1, 4), rng.randint(1, 300), rng.choice([1, 2, 3, 5, 8, 13, 16, 32, 64, 128])
-        st, p = pos_plan((B, S, N, D), dtype, (start, start + L), mode, per_batch=rng.random() < 0.5)
+        per_batch = rng.random() < 0.5
+        shared_positions = not per_batch
+        st, p = pos_plan((B, S, N, D), dtype, (start, start + L), mode, per_batch=per_batch)
         assert st == rp.ROPE_OK, (B, S, N, D, dtype, start, L, mode)
         seen[p["kernel"]] = seen.get(p["kernel"], 0) + 1
         aligned = (D * es) % 16 == 0 and (start * es) % 16 == 0
@@ -277,17 +283,20 @@ def test_pos_plan_invariants_over_random_shapes():
             continue
         span, HL, U, P, chunks = (p["row_vectors"], p["head_lanes"], p["heads_per_thread"],
                                   p["positions_per_block"], p["head_chunks"])
+        # positions shared by the batch: the batches are heads of one position per s
+        vheads = shared_positions and B > 1 and span * N < 128
+        heads, positions = (B * N, S) if vheads else (N, B * S)
         assert p["threads"] == P * span * HL <= 256
-        assert P * (L // 2) <= 512
-        assert (chunks - 1) * HL * U < N <= chunks * HL * U
-        assert HL <= N
+        assert (chunks - 1) * HL * U < heads <= chunks * HL * U
+        assert HL <= heads
         if mode == IL:
             assert span * 16 >= L * es and span * 16 <= D * es
         else:
             assert span * 16 == (L // 2) * es
         if P > 1:
             assert span * HL < 128
-        assert p["blocks"] == -(-(B * S) // P) * chunks
+        assert P * (L // 2) <= 512
+        assert p["blocks"] == -(-positions // P) * chunks
     assert seen["vector"] > 500 and seen["rows"] > 100, seen
 
 
@@ -319,3 +328,16 @@ def test_rotary_coefficient_two_plans_as_rotate_half():
 def test_rotary_coefficient_position_plans(coeff, kernel):
     st, p = pos_plan((4, 4096, 128, 192), "bf16", (0, 64), coeff)
     assert st == OK and p["kernel"] == kernel, p
+
+
+def test_pos_plan_shares_positions_across_the_batch():
+    """Positions the same for every batch (one row, or a batch stride of 0):
+    the batches become heads of one position per s. For a single K head of
+    128 lanes (8 threads per row) and 32 batches: 16 head lanes of 2 heads,
+    one block per s."""
+    st, p = pos_plan((32, 4096, 1, 128), "bf16", (0, 128), RH, per_batch=False)
+    assert st == OK and p["head_lanes"] == 16 and p["head_chunks"] == 1 and p["positions_per_block"] == 1
+    assert p["blocks"] == 4096 and p["threads"] == 128
+    # per-batch positions: 16 consecutive (b, s) positions per block, LDS permitting (512 entries / 64 pairs)
+    st, p = pos_plan((32, 4096, 1, 128), "bf16", (0, 128), RH, per_batch=True)
+    assert st == OK and p["positions_per_block"] == 8 and p["blocks"] == 32 * 4096 // 8

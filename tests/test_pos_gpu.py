@@ -286,3 +286,42 @@ def test_pos_multi_error_touches_nothing():
         rp.rope_partial_fwd_inplace_pos_multi([q, k], pos, f, "interleave", (0, 64))
     torch.cuda.synchronize()
     assert torch.equal(q.view(torch.int16), q0.view(torch.int16))
+
+
+@pytest.mark.parametrize("out", [False, True])
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_pos_mqa_k_positions_shared_by_the_batch(direction, out):
+    """A single K head (32,4096,1,128) bf16, rotate_half, with one row of
+    positions for all 32 batches: the kernels take the batches as heads of
+    one position per s (each s's cos and sin evaluated once). Sampled rows
+    against the oracle; out of place, x unchanged."""
+    w = W.WORKLOADS["mqa_k"]
+    x = W.make_x(w)
+    pos = torch.from_numpy(W.positions(w))
+    assert pos.shape == (1, 4096)
+    f = rp.rope_inv_freq(w.L, w.base)
+    st, plan = rp.raw_launch_info_pos(1 << 20, w.x_shapes[0], rp.DTYPE_CODES["bf16"], 1 << 20, (1, 4096), (4096, 1),
+                                      1 << 20, rp.DTYPE_CODES["bf16"], rp.MODES[w.mode], w.partial_slice)
+    assert st == rp.ROPE_OK and plan["head_lanes"] == 16 and plan["blocks"] == 4096
+    announce(f"positions mqa_k shared {direction} out={out}")
+    xd = x.to(DEV)
+    if out:
+        y = torch.empty_like(xd)
+        (rp.rope_partial_fwd_out_pos if direction == "fwd" else rp.rope_partial_bwd_out_pos)(
+            y, xd, pos.to(DEV), f.to(DEV), w.mode, w.partial_slice)
+    else:
+        y = xd
+        (rp.rope_partial_fwd_inplace_pos if direction == "fwd" else rp.rope_partial_bwd_inplace_pos)(
+            y, pos.to(DEV), f.to(DEV), w.mode, w.partial_slice)
+    torch.cuda.synchronize()
+    if out:
+        assert torch.equal(xd.view(torch.int16), x.to(DEV).view(torch.int16))
+    B, S, N, D = w.x_shapes[0]
+    total = B * S * N
+    rows = W.sample_rows(total, 4000, 23)
+    got = W.to_numpy_storage(y.view(total, D).index_select(0, torch.from_numpy(rows).to(DEV)).cpu())
+    x_rows = np.ascontiguousarray(W.to_numpy_storage(x).reshape(total, D)[rows])
+    c, s = oracle.pos_tables(pos.numpy(), f.numpy(), w.L, w.mode, "bf16")
+    want = x_rows.copy()
+    oracle.rope_rows(want, x.shape, "bf16", c, s, w.mode, w.partial_slice, direction, rows=rows, table_dtype="bf16")
+    assert np.array_equal(got, want)

@@ -617,18 +617,27 @@ static bool pos_vectors(const Plan& p, PosArgs* a, bool out)
 // threads cover (lo_vec, span) are set: U heads per thread, a position's
 // heads over up to `lanes_target` threads.
 static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid, int U,
-                             uint32_t lanes_target)
+                             uint32_t lanes_target, bool allow_vheads)
 {
     if (a->span < 1 || a->span > 256) return false;
-    a->N = (uint32_t)p.N;
+    // positions shared by the batch (batch stride 0), and too few heads to
+    // fill a block: the batches become heads of one position per s (see
+    // PosArgs::vheads). With more heads the (b,s) order is kept, which
+    // streams through x: the GQA Q layout (32,4096,16,128) took 197 us with
+    // the batches as heads, where one (b,s) per block takes 167 us.
+    a->vheads = allow_vheads && p.pos_sb == 0 && p.B > 1 && (uint64_t)a->span * p.N < lanes_target;
+    const uint64_t heads = a->vheads ? (uint64_t)p.B * p.N : (uint64_t)p.N;
+    const uint64_t positions = a->vheads ? (uint64_t)p.S : (uint64_t)p.B * p.S;
+    if (heads >= (1ull << 31) || positions >= (1ull << 31)) return false;
+    a->N = (uint32_t)heads;
     a->pairs = (uint32_t)(p.L / 2);
-    a->HL = (uint32_t)std::min<uint64_t>(std::max<uint32_t>(1, lanes_target / a->span), (uint64_t)p.N);
-    a->chunks = (uint32_t)((p.N + (uint64_t)a->HL * U - 1) / ((uint64_t)a->HL * U));
+    a->HL = (uint32_t)std::min<uint64_t>(std::max<uint32_t>(1, lanes_target / a->span), heads);
+    a->chunks = (uint32_t)((heads + (uint64_t)a->HL * U - 1) / ((uint64_t)a->HL * U));
     a->lanes = a->span * a->HL;
     a->P = a->lanes < lanes_target ? std::min<uint32_t>(lanes_target / a->lanes, kPosLds / a->pairs) : 1;
     a->entries = a->P * a->pairs;
     if (a->entries > (uint32_t)kPosLds) return false;
-    a->bs = (uint32_t)(p.B * p.S);
+    a->bs = (uint32_t)positions;
     const uint64_t items = (((uint64_t)a->bs + a->P - 1) / a->P) * a->chunks;
     if (items >= (1ull << 31)) return false;
     a->items = (uint32_t)items;
@@ -639,6 +648,7 @@ static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint3
     a->pairs_div = make_fastdiv(a->pairs);
     a->chunk_div = make_fastdiv(a->chunks);
     a->s_div = make_fastdiv((uint32_t)p.S);
+    a->nx_div = make_fastdiv((uint32_t)std::max<int64_t>(1, p.N));
     return true;
 }
 
@@ -655,7 +665,7 @@ bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
         a->lo_vec = lines.lo_vec;
         a->span = lines.span;
     }
-    return pos_launch_shape(p, a, threads, grid, kUPos, kPosLanes);
+    return pos_launch_shape(p, a, threads, grid, kUPos, kPosLanes, true);
 }
 
 // Out of place: the threads of a row cover all of its vectors.
@@ -664,7 +674,7 @@ bool pos_geometry_out(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* gr
     if (!pos_vectors(p, a, true)) return false;
     a->lo_vec = 0;
     a->span = a->row_vecs;
-    return pos_launch_shape(p, a, threads, grid, pos_out_heads(p.mode), pos_out_lanes(p.mode));
+    return pos_launch_shape(p, a, threads, grid, pos_out_heads(p.mode), pos_out_lanes(p.mode), true);
 }
 
 template <int DT, int TT, int DIR>
@@ -815,7 +825,7 @@ rope_status_t run_pos_multi(int32_t count, void* const xs[], const int64_t (*x_s
         Plan q = P[0];
         q.N = (int64_t)heads;
         m = each[0];
-        together = pos_launch_shape(q, &m, &threads, &grid, kUPos, kPosLanes);
+        together = pos_launch_shape(q, &m, &threads, &grid, kUPos, kPosLanes, false);
         uint32_t first = 0;
         for (int i = 0; i < kMultiMax; ++i) {
             m.xs[i] = i < live ? each[i].x : nullptr;

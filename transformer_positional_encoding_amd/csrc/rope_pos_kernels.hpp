@@ -105,8 +105,15 @@ struct PosArgs {
     uint32_t entries;        // P * pairs
     uint32_t chunks;         // head chunks per position
     uint32_t bs;             // B*S
-    uint32_t items;          // ceil(B*S / P) * chunks
-    FastDiv span_div, lanes_div, pairs_div, chunk_div, s_div;
+    uint32_t items;          // ceil(bs / P) * chunks
+    // vheads: the positions are the same for every batch (batch stride 0).
+    // The kernel's positions are then the S values of s (bs = S), and its
+    // heads are the B*N pairs (b, n) of each s (N = B*N), head h being
+    // batch h / nx and head h % nx: each s's cos and sin is evaluated once
+    // for every batch, and the head slots of a thread stay full when N is
+    // small. Otherwise positions are (b, s) pairs g = b*S + s.
+    uint32_t vheads;
+    FastDiv span_div, lanes_div, pairs_div, chunk_div, s_div, nx_div;
     // Several tensors in one launch (MULTI): N counts the heads of all of
     // them; head n of a position belongs to the last tensor q with
     // hoff[q] <= n (hoff past the last tensor is UINT32_MAX), which holds
@@ -116,13 +123,41 @@ struct PosArgs {
     uint32_t hoff[kMultiMax];
 };
 
+// The offset in `pos` of position g: g = b*S + s, or, vheads, g = s.
+__device__ __forceinline__ int64_t pos_offset(const PosArgs& a, uint32_t g)
+{
+    const uint32_t b = fast_div(g, a.s_div);
+    return (int64_t)b * a.pos_sb + (int64_t)(g - b * a.s_div.d) * a.pos_ss;
+}
+
+// The row of x (b*S + s)*N + n that head nl of position g stands for.
+__device__ __forceinline__ uint32_t pos_row(const PosArgs& a, uint32_t g, uint32_t nl)
+{
+    if (!a.vheads) return g * a.N + nl;
+    const uint32_t b = fast_div(nl, a.nx_div);
+    return (b * a.s_div.d + g) * a.nx_div.d + (nl - b * a.nx_div.d);
+}
+
+// The (cos, sin) entries past the first blockDim of the block's table:
+// entry e is pair e % pairs of the block's position g0 + e / pairs.
+template <int TT>
+__device__ __forceinline__ void pos_fill_rest(const PosArgs& a, uint32_t g0, float2* cs)
+{
+    for (uint32_t e = threadIdx.x + blockDim.x; e < a.entries; e += blockDim.x) {
+        const uint32_t q = fast_div(e, a.pairs_div);
+        const uint32_t ge = g0 + q;
+        if (ge >= a.bs) break;                    // later entries belong to later positions
+        cs[e] = pos_cos_sin<TT>(a.pos[pos_offset(a, ge)], a.inv_freq[e - q * a.pairs]);
+    }
+}
+
 // The row of head nl of position g in one tensor, or, MULTI, in the tensor
 // the head belongs to; as a vector pointer with the thread's vector c.
 template <bool MULTI>
 __device__ __forceinline__ v4u* pos_row_vec(const PosArgs& a, uint32_t g, uint32_t nl, uint32_t c)
 {
     if constexpr (!MULTI) {
-        return a.x + ((g * a.N + nl) * a.row_vecs + c);
+        return a.x + (pos_row(a, g, nl) * a.row_vecs + c);
     } else {
         v4u* base = a.xs[0];
         uint32_t nt = a.nt[0], ho = 0;
@@ -165,11 +200,10 @@ __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
     for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
         const uint32_t grp = fast_div(w, a.chunk_div);
         const uint32_t chunk = w - grp * a.chunks;
-        const uint32_t g0 = grp * a.P;                // first position of the block
-        const bool fill = t < a.entries && g0 + eq < a.bs;
-        const uint32_t gq = min(g0 + eq, a.bs - 1);
-        const uint32_t bq = fast_div(gq, a.s_div);
-        const int64_t p0 = a.pos[(int64_t)bq * a.pos_sb + (int64_t)(gq - bq * a.s_div.d) * a.pos_ss];
+        const uint32_t g0 = grp * a.P;                        // the block's first position
+        const uint32_t ge = g0 + eq;                          // the position of entry t
+        const bool fill = t < a.entries && ge < a.bs;
+        const int64_t p0 = a.pos[pos_offset(a, min(ge, a.bs - 1))];
         const double f0 = a.inv_freq[ei];
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t g = g0 + pp;
@@ -190,14 +224,7 @@ __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
         }
         __builtin_amdgcn_sched_barrier(0);
         if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
-        for (uint32_t e = t + blockDim.x; e < a.entries; e += blockDim.x) {
-            const uint32_t q = fast_div(e, a.pairs_div);
-            const uint32_t ge = g0 + q;
-            if (ge >= a.bs) break;                    // later entries belong to later positions
-            const uint32_t be = fast_div(ge, a.s_div);
-            const int64_t pe = a.pos[(int64_t)be * a.pos_sb + (int64_t)(ge - be * a.s_div.d) * a.pos_ss];
-            cs[e] = pos_cos_sin<TT>(pe, a.inv_freq[e - q * a.pairs]);
-        }
+        pos_fill_rest<TT>(a, g0, cs);
         __syncthreads();
         // cos and sin of the thread's lanes: interleave lane j belongs to
         // pair j/2; rotate_half lane j of the first half to pair j, and the
@@ -274,18 +301,17 @@ __global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
     const uint32_t eq = fast_div(t, a.pairs_div);
     const uint32_t ei = t - eq * a.pairs;
     for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
-        const uint32_t grpb = fast_div(w, a.chunk_div);
-        const uint32_t chunk = w - grpb * a.chunks;
-        const uint32_t g0 = grpb * a.P;
-        const bool fill = t < a.entries && g0 + eq < a.bs;
-        const uint32_t gq = min(g0 + eq, a.bs - 1);
-        const uint32_t bq = fast_div(gq, a.s_div);
-        const int64_t p0 = a.pos[(int64_t)bq * a.pos_sb + (int64_t)(gq - bq * a.s_div.d) * a.pos_ss];
+        const uint32_t grp = fast_div(w, a.chunk_div);
+        const uint32_t chunk = w - grp * a.chunks;
+        const uint32_t g0 = grp * a.P;                        // the block's first position
+        const uint32_t ge = g0 + eq;                          // the position of entry t
+        const bool fill = t < a.entries && ge < a.bs;
+        const int64_t p0 = a.pos[pos_offset(a, min(ge, a.bs - 1))];
         const double f0 = a.inv_freq[ei];
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t g = g0 + pp;
         const bool pos_live = g < a.bs;
-        const uint32_t gl = pos_live ? g : a.bs - 1;
+        const uint32_t gl = pos_live ? g : a.bs - 1;  // past the last position: re-read it, store nothing
         const uint32_t n0 = chunk * (a.HL * U) + hl;
         v4u xa[U], xb[U];
         uint32_t off[U];
@@ -295,7 +321,7 @@ __global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
             const uint32_t n = n0 + (uint32_t)k * a.HL;
             live[k] = pos_live && n < a.N;
             const uint32_t nl = n < a.N ? n : a.N - 1;
-            const uint32_t row = (gl * a.N + nl) * a.row_vecs;
+            const uint32_t row = pos_row(a, gl, nl) * a.row_vecs;
             off[k] = row + c;
             xa[k] = load_x<true>(a.src + off[k]);
             if constexpr (MODE == kModeRH && !XCHG) xb[k] = load_x<true>(a.src + row + partner);
@@ -307,14 +333,7 @@ __global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
             for (int k = 0; k < U; ++k) xb[k] = lane_exchange(xa[k], xlane);
         }
         if (fill) cs[t] = pos_cos_sin<TT>(p0, f0);
-        for (uint32_t e = t + blockDim.x; e < a.entries; e += blockDim.x) {
-            const uint32_t q = fast_div(e, a.pairs_div);
-            const uint32_t ge = g0 + q;
-            if (ge >= a.bs) break;
-            const uint32_t be = fast_div(ge, a.s_div);
-            const int64_t pe = a.pos[(int64_t)be * a.pos_sb + (int64_t)(ge - be * a.s_div.d) * a.pos_ss];
-            cs[e] = pos_cos_sin<TT>(pe, a.inv_freq[e - q * a.pairs]);
-        }
+        pos_fill_rest<TT>(a, g0, cs);
         __syncthreads();
         const uint32_t base = pp * a.pairs;
         float C[K], S[K];

@@ -112,6 +112,11 @@ WORKLOADS: dict[str, Workload] = {
               seed=11, directions=("fwd", "bwd"), table_kind="random",
               note="single-op example shape, random BS1D tables"),
 }
+# A single K head (multi-query attention) at 4096 positions shared by the
+# batch: each position's 64 pairs of cos/sin serve 512 bytes of x.
+WORKLOADS["mqa_k"] = W("mqa_k", ((32, 4096, 1, 128),), "bf16", (0, 128), "rotate_half", (1, 4096, 1, 128),
+                       seed=16, directions=("fwd", "bwd"),
+                       note="MQA K (one head, HD 128) at 4096 positions, rotate_half, bf16")
 # MLA's rope part with the page's coefficient 4 (two groups of two 16-lane parts).
 WORKLOADS["c3_coeff4"] = replace(WORKLOADS["c3"], name="c3_coeff4", mode=4, seed=15,
                                  note="MLA-style rope on lanes [0,64) of 192, rotary coefficient 4, bf16")
