@@ -58,6 +58,18 @@ def test_long_context_shard_plan():
     assert info["xcd_run"] == 48 * 8
 
 
+@pytest.mark.parametrize("dtype,tdtype,heads", [(BF16, F32, 2), (F16, F32, 2), (BF16, BF16, 1), (F32, F32, 1),
+                                                (F32, BF16, 1)])
+def test_in_place_heads_per_thread_follow_the_table_unit(dtype, tdtype, heads):
+    """In place, a thread takes two heads when each 16-byte x vector needs
+    two vectors each of cos and sin (16-bit x with fp32 tables), one head
+    otherwise: the long-context shard's plan with per-batch tables."""
+    st, info = plan((16, 8192, 32, 128), dtype, (32, 96), per_batch=True, table_dtype=tdtype)
+    assert st == OK and info["kernel"] == "vector"
+    assert info["heads_per_thread"] == heads and info["head_lanes"] == 4 and info["threads"] == 64
+    assert info["blocks"] == 16 * 8192 * (32 // (4 * heads))
+
+
 @pytest.mark.parametrize("x_shape,dtype,sl,mode,span", [
     ((4, 4096, 128, 192), BF16, (0, 64), IL, 8),       # whole line [0,128) bytes
     ((16, 8192, 32, 128), F32, (32, 96), IL, 16),      # bytes [128,384): two whole lines

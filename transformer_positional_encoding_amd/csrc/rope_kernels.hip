@@ -68,15 +68,26 @@ int cu_count(int dev)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Heads per thread of the instantiated vector kernels: in place, and out of
-// place (see prepare_out).
-constexpr int kUInPlace = 1;
+// Heads per thread of the instantiated vector kernels. In place: one, or two
+// for 16-bit x with fp32 tables, where each 16-byte x vector takes two
+// vectors each of cos and sin. A wave lasts as long as its slowest load, so
+// with one head per thread those four table loads come with one x load;
+// with two heads they serve two. Measured on MI355X (cold data), the
+// long-context shard (16,8192,32,128) bf16, lanes [32,96), per-batch fp32
+// tables: 289 us with one head per thread, 260 us with two, 286 us with
+// four. With tables of x's dtype two heads per thread are slower (that
+// shard 255 -> 258 us, the (4,4096,128,192) MLA rope slice 94 -> 100 us).
+// Out of place: two (see prepare_out).
+constexpr int u_in_place(int dtype, int tdtype)
+{
+    return dtype != ROPE_DTYPE_F32 && tdtype == ROPE_DTYPE_F32 ? 2 : 1;
+}
 constexpr int kUOut = 2;
 
 // Launch shape of the vector kernel.
 struct VecConfig {
     int kmode = kModeIL;  // kernel scheme: kModeIL, kModeRH (pair owner) or kModeRHOwn
-    int U = 1;          // heads per thread per tile (kUInPlace or kUOut)
+    int U = 1;          // heads per thread per tile (u_in_place or kUOut)
     uint32_t HL = 1;    // head lanes per tile
     uint32_t GL = 1;    // tiles per block iteration
     uint32_t grid = 0;  // blocks; 0 = one block per tile group
@@ -221,9 +232,9 @@ uint32_t vec_grid(const VecArgs& a, const VecConfig& cfg)
 // gridDim.x to it), in which case a general kernel runs instead.
 bool finish_vec_args(const Plan& p, const VecConfig& cfg, VecArgs* a)
 {
-    // The library instantiates the chosen shapes only: kUInPlace or kUOut
+    // The library instantiates the chosen shapes only: u_in_place or kUOut
     // heads per thread, nontemporal x.
-    if (cfg.U != (a->src ? kUOut : kUInPlace) || !cfg.nt || cfg.HL < 1 || cfg.GL < 1 ||
+    if (cfg.U != (a->src ? kUOut : u_in_place(p.dtype, p.tdtype)) || !cfg.nt || cfg.HL < 1 || cfg.GL < 1 ||
         (uint64_t)cfg.HL * cfg.GL * a->span > 256)
         return false;
     a->HL = cfg.HL;
@@ -261,14 +272,14 @@ const void* vec_kernel_ptr(VecKind kind)
     case kVecMulti:
         // in place: no memory partner loads
         if constexpr (MODE == kModeRHOwnLoad) return nullptr;
-        else return reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, TT, DIR, MODE, kUInPlace, SHARE, true>);
+        else return reinterpret_cast<const void*>(&rope_vec_multi_kernel<DT, TT, DIR, MODE, u_in_place(DT, TT), SHARE, true>);
     case kVecOut:
         // out of place, rotate_half always takes an own-vector scheme
         if constexpr (MODE == kModeRH) return nullptr;
         else return reinterpret_cast<const void*>(&rope_vec_out_kernel<DT, TT, DIR, MODE, kUOut, SHARE, true>);
     default:
         if constexpr (MODE == kModeRHOwnLoad) return nullptr;
-        else return reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, kUInPlace, SHARE, true>);
+        else return reinterpret_cast<const void*>(&rope_vec_kernel<DT, TT, DIR, MODE, u_in_place(DT, TT), SHARE, true>);
     }
 }
 
@@ -498,7 +509,7 @@ void prepare(Launch* L)
         } else {
             cover_whole_lines(L->p, &L->a);
         }
-        L->cfg = choose_vec_config(L->p, L->a, kUInPlace, kmode);
+        L->cfg = choose_vec_config(L->p, L->a, u_in_place(L->p.dtype, L->p.tdtype), kmode);
         L->vec = finish_vec_args(L->p, L->cfg, &L->a);
         // the own-vector scheme in place needs single-wave blocks
         if (L->vec && kmode == kModeRHOwn && L->a.span * L->a.HL * L->a.GL > 64) L->vec = false;
