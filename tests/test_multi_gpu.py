@@ -7,7 +7,7 @@ import torch
 
 import transformer_positional_encoding_amd as rp
 import workloads as W
-from gpu_support import announce, oracle_rows
+from gpu_support import announce, compare, expanded_tables, oracle_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -43,18 +43,19 @@ def test_gqa_q_and_k_one_call(direction):
     assert _same(kd.cpu(), _oracle(k, r1, r2, "rotate_half", (0, 128), direction))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype,tdtype", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32"), ("f16", "f32")])
 @pytest.mark.parametrize("mode,sl", [("interleave", (32, 96)), ("interleave", (0, 64)), ("rotate_half", (0, 128))])
-def test_four_tensors_match_single_calls(dtype, mode, sl):
+def test_four_tensors_match_single_calls(dtype, tdtype, mode, sl):
     """Head counts 16, 8, 3, 1 and two row widths, one call; equal to four
-    single calls and to the oracle."""
-    announce(f"multi 4 tensors {dtype} {mode} {sl}")
+    single calls and to the oracle. 16-bit x with fp32 tables takes two
+    heads per thread in place, in the multi-tensor kernel as well."""
+    announce(f"multi 4 tensors {dtype} tables={tdtype} {mode} {sl}")
     g = torch.Generator().manual_seed(5)
     shapes = [(2, 64, 16, 128), (2, 64, 8, 128), (2, 64, 3, 192), (1, 64, 1, 128)]
     xs = [torch.randn(s, generator=g).to(DT[dtype]) for s in shapes]
     L = sl[1] - sl[0]
-    r1 = torch.randn((1, 64, 1, L), generator=g).to(DT[dtype])
-    r2 = torch.randn((1, 64, 1, L), generator=g).to(DT[dtype])
+    r1 = torch.randn((1, 64, 1, L), generator=g).to(DT[tdtype])
+    r2 = torch.randn((1, 64, 1, L), generator=g).to(DT[tdtype])
     multi = [x.to(DEV) for x in xs]
     single = [x.to(DEV) for x in xs]
     rp.rope_partial_fwd_inplace_multi(multi, r1.to(DEV), r2.to(DEV), mode, sl)
@@ -66,6 +67,12 @@ def test_four_tensors_match_single_calls(dtype, mode, sl):
         want = _oracle(x, r1, r2, mode, sl, "fwd")
         if dtype == "f32":
             torch.testing.assert_close(m.cpu(), want, rtol=0, atol=1e-5)
+        elif tdtype == "f32":
+            D = x.shape[-1]
+            rows = np.arange(x.numel() // D, dtype=np.int64)
+            compare(W.to_numpy_storage(m.cpu()).reshape(-1, D), W.to_numpy_storage(want).reshape(-1, D),
+                    W.to_numpy_storage(x).reshape(-1, D), expanded_tables(r1, x.shape, rows, L),
+                    expanded_tables(r2, x.shape, rows, L), dtype, mode, "fwd", sl, f"multi {dtype}/{tdtype}")
         else:
             assert _same(m.cpu(), want)
 
