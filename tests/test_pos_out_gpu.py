@@ -211,3 +211,58 @@ def test_position_autograd_leaf_rule_and_shared_gradient():
     want, _, _ = _oracle(g.cpu(), pos.cpu(), f.cpu(), "interleave", (0, 64), "bwd", "bf16")
     # x.grad = bwd(g) (through y) + bwd(g) (through z = y * 1.0), each rounded to bf16, summed in bf16
     assert torch.equal(_bits(x.grad.cpu()), _bits(want + want))
+
+
+SHARED = [
+    # (shape, slice, mode, dtype, positions as one row (1,S) or expanded over the batch with stride 0)
+    ((3, 37, 1, 128), (0, 128), "rotate_half", "bf16", "row"),      # one head: several positions per block
+    ((4, 19, 2, 192), (0, 64), 4, "bf16", "expand"),                 # coefficient 4, two heads
+    ((5, 23, 3, 64), (0, 64), "interleave", "f32", "row"),           # fp32, heads in a part-full chunk
+    ((2, 9, 5, 128), (32, 96), "interleave", "f16", "expand"),       # half-line slice inside whole rows
+]
+
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+@pytest.mark.parametrize("case", SHARED, ids=[f"{c[0]}-{c[2]}-{c[3]}-{c[4]}" for c in SHARED])
+def test_out_of_place_positions_shared_by_the_batch(case, direction):
+    """Positions with batch stride 0 and few heads: the kernel takes the
+    batches as heads of one position per s. Every row against the oracle;
+    the input unchanged; 16-bit results equal to the in-place call's."""
+    shape, sl, mode, dtype, layout = case
+    B, S, N, D = shape
+    L = sl[1] - sl[0]
+    seed = _seed("shared", case)
+    x = _rand(shape, dtype, seed)
+    row = _positions(1, S, seed + 1)
+    pos_dev = row.to(DEV) if layout == "row" else row.to(DEV).expand(B, S)
+    assert layout == "row" or pos_dev.stride(0) == 0
+    f = rp.rope_inv_freq(L, 10000.0)
+    st, plan = rp.raw_launch_info_pos(1 << 20, shape, rp.DTYPE_CODES[dtype], 1 << 20, tuple(pos_dev.shape),
+                                      tuple(pos_dev.stride()), 1 << 20, rp.DTYPE_CODES[dtype], rp.MODES.get(mode, mode),
+                                      sl)
+    assert st == rp.ROPE_OK and plan["kernel"] == "vector"
+    # the in-place plan's blocks: ceil(S / positions per block) * head chunks of B*N heads
+    heads = plan["head_lanes"] * plan["heads_per_thread"]
+    assert plan["head_chunks"] == -(-(B * N) // heads)
+    assert plan["blocks"] == -(-S // plan["positions_per_block"]) * plan["head_chunks"]
+    announce(f"out-of-place positions shared by the batch {shape} {mode} {dtype} {layout} {direction}")
+    xd = x.to(DEV)
+    y = torch.full_like(xd, float("nan"))
+    (rp.rope_partial_fwd_out_pos if direction == "fwd" else rp.rope_partial_bwd_out_pos)(
+        y, xd, pos_dev, f.to(DEV), mode, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(xd), _bits(x.to(DEV))), "the input changed"
+    want, c, s = _oracle(x, row.expand(B, S), f, mode, sl, direction, dtype)
+    rows = np.arange(B * S * N, dtype=np.int64)
+    info = compare(W.to_numpy_storage(y.cpu()).reshape(-1, D), W.to_numpy_storage(want).reshape(-1, D),
+                   W.to_numpy_storage(x).reshape(-1, D),
+                   expanded_tables(W.from_numpy_storage(c, dtype), shape, rows, L),
+                   expanded_tables(W.from_numpy_storage(s, dtype), shape, rows, L), dtype, mode, direction, sl,
+                   "out-of-place positions shared by the batch")
+    if dtype != "f32":
+        assert info["exact"] == info["n"]
+        xi = x.to(DEV)
+        (rp.rope_partial_fwd_inplace_pos if direction == "fwd" else rp.rope_partial_bwd_inplace_pos)(
+            xi, pos_dev, f.to(DEV), mode, sl)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(xi), _bits(y))
