@@ -478,7 +478,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out,c4:pos,c2_s4096:pos,c4:outpos,"
-                                      "c2_s4096:outpos,c2:posmulti,c4_t32:pos,mqa_k:pos,c2_s4096,rh_64of128,rh_32of128,"
+                                      "c2_s4096:outpos,c2:posmulti,tp_qk:posmulti,c4_t32:pos,mqa_k:pos,c2_s4096,rh_64of128,"
+                                      "rh_32of128,"
                                       "c3_coeff4",
                     help="other workloads measured in the same run (reported under 'other_workloads'); "
                          "NAME:out measures the out-of-place entry points on NAME, NAME:pos the position "

@@ -151,6 +151,27 @@ def test_pos_multi_gqa_q_and_k_full_size():
         assert np.array_equal(W.to_numpy_storage(td.cpu()), want)
 
 
+def test_pos_multi_tensor_parallel_q_and_k_full_size():
+    """One tensor-parallel rank's Q (32,4096,4,128) and K (32,4096,1,128),
+    rotate_half, positions shared by the batch, in one position call (the
+    bench's tp_qk:posmulti launch: the batches are heads of one position per
+    s); every row of both against the oracle."""
+    w = W.WORKLOADS["tp_qk"]
+    q, k = W.make_x(w, 0), W.make_x(w, 1)
+    pos = torch.from_numpy(W.positions(w))
+    assert pos.shape == (1, 4096)
+    f = rp.rope_inv_freq(w.L, w.base)
+    announce("positions multi tp_qk Q+K full size")
+    qd, kd = q.to(DEV), k.to(DEV)
+    rp.rope_partial_fwd_inplace_pos_multi([qd, kd], pos.to(DEV), f.to(DEV), w.mode, w.partial_slice)
+    torch.cuda.synchronize()
+    c, s = oracle.pos_tables(pos.numpy(), f.numpy(), w.L, w.mode, "bf16")
+    for t, td in ((q, qd), (k, kd)):
+        want = W.to_numpy_storage(t).copy()
+        oracle.rope_rows(want, t.shape, "bf16", c, s, w.mode, w.partial_slice, "fwd", table_dtype="bf16")
+        assert np.array_equal(W.to_numpy_storage(td.cpu()), want)
+
+
 def test_pos_equals_the_table_call_with_the_oracle_tables():
     """The position call and the table call given the oracle's tables of the
     same positions write the same bytes."""
@@ -246,17 +267,20 @@ MULTI_CASES = [
     (((1, 24, 8, 192), (1, 24, 1, 192), (1, 24, 3, 192), (1, 24, 5, 192)), (0, 64), 4),   # four, coefficient 4
     (((2, 16, 6, 192), (2, 16, 2, 64)), (0, 64), "interleave"),           # D differs: one launch each
     (((2, 12, 5, 64), (2, 12, 3, 64)), (3, 35), "interleave"),            # odd start: the row kernel each
+    (((4, 20, 4, 128), (4, 20, 1, 128)), (0, 128), "rotate_half"),        # few heads: with shared positions,
+    (((3, 17, 2, 64), (3, 17, 1, 64), (3, 17, 3, 64)), (0, 64), "interleave"),   # the batches become heads
 ]
 
 
+@pytest.mark.parametrize("per_batch", [True, False], ids=["positions-per-batch", "positions-shared"])
 @pytest.mark.parametrize("direction", ["fwd", "bwd"])
 @pytest.mark.parametrize("case", MULTI_CASES, ids=[f"{len(c[0])}x-{c[1]}-{c[2]}" for c in MULTI_CASES])
-def test_pos_multi_equals_single_calls_and_the_oracle(case, direction):
+def test_pos_multi_equals_single_calls_and_the_oracle(case, direction, per_batch):
     shapes, sl, mode = case
     L = sl[1] - sl[0]
     B, S = shapes[0][0], shapes[0][1]
     xs = [_rand(sh, "bf16", 300 + i) for i, sh in enumerate(shapes)]
-    pos = _positions(B, S, True, 310)
+    pos = _positions(B, S, per_batch, 310)
     f = rp.rope_inv_freq(L, 500000.0)
     announce(f"positions multi {[tuple(s) for s in shapes]} {sl} {mode} {direction}")
     multi = [x.to(DEV) for x in xs]

@@ -628,7 +628,7 @@ static bool pos_vectors(const Plan& p, PosArgs* a, bool out)
 // threads cover (lo_vec, span) are set: U heads per thread, a position's
 // heads over up to `lanes_target` threads.
 static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid, int U,
-                             uint32_t lanes_target, bool allow_vheads)
+                             uint32_t lanes_target)
 {
     if (a->span < 1 || a->span > 256) return false;
     // positions shared by the batch (batch stride 0), and too few heads to
@@ -636,7 +636,7 @@ static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint3
     // PosArgs::vheads). With more heads the (b,s) order is kept, which
     // streams through x: the GQA Q layout (32,4096,16,128) took 197 us with
     // the batches as heads, where one (b,s) per block takes 167 us.
-    a->vheads = allow_vheads && p.pos_sb == 0 && p.B > 1 && (uint64_t)a->span * p.N < lanes_target;
+    a->vheads = p.pos_sb == 0 && p.B > 1 && (uint64_t)a->span * p.N < lanes_target;
     const uint64_t heads = a->vheads ? (uint64_t)p.B * p.N : (uint64_t)p.N;
     const uint64_t positions = a->vheads ? (uint64_t)p.S : (uint64_t)p.B * p.S;
     if (heads >= (1ull << 31) || positions >= (1ull << 31)) return false;
@@ -676,7 +676,7 @@ bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
         a->lo_vec = lines.lo_vec;
         a->span = lines.span;
     }
-    return pos_launch_shape(p, a, threads, grid, kUPos, kPosLanes, true);
+    return pos_launch_shape(p, a, threads, grid, kUPos, kPosLanes);
 }
 
 // Out of place: the threads of a row cover all of its vectors.
@@ -685,7 +685,7 @@ bool pos_geometry_out(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* gr
     if (!pos_vectors(p, a, true)) return false;
     a->lo_vec = 0;
     a->span = a->row_vecs;
-    return pos_launch_shape(p, a, threads, grid, pos_out_heads(p.mode), pos_out_lanes(p.mode), true);
+    return pos_launch_shape(p, a, threads, grid, pos_out_heads(p.mode), pos_out_lanes(p.mode));
 }
 
 template <int DT, int TT, int DIR>
@@ -836,7 +836,7 @@ rope_status_t run_pos_multi(int32_t count, void* const xs[], const int64_t (*x_s
         Plan q = P[0];
         q.N = (int64_t)heads;
         m = each[0];
-        together = pos_launch_shape(q, &m, &threads, &grid, kUPos, kPosLanes, false);
+        together = pos_launch_shape(q, &m, &threads, &grid, kUPos, kPosLanes);
         uint32_t first = 0;
         for (int i = 0; i < kMultiMax; ++i) {
             m.xs[i] = i < live ? each[i].x : nullptr;

@@ -159,16 +159,24 @@ __device__ __forceinline__ v4u* pos_row_vec(const PosArgs& a, uint32_t g, uint32
     if constexpr (!MULTI) {
         return a.x + (pos_row(a, g, nl) * a.row_vecs + c);
     } else {
+        // vheads: head nl is head n of the tensors' joint range in batch b,
+        // at (b, s) = (b, g); otherwise g is the (b, s) pair itself
+        uint32_t n = nl, bs = g;
+        if (a.vheads) {
+            const uint32_t b = fast_div(nl, a.nx_div);
+            n = nl - b * a.nx_div.d;
+            bs = b * a.s_div.d + g;
+        }
         v4u* base = a.xs[0];
         uint32_t nt = a.nt[0], ho = 0;
 #pragma unroll
         for (int q = 1; q < kMultiMax; ++q) {
-            const bool in = nl >= a.hoff[q];
+            const bool in = n >= a.hoff[q];
             base = in ? a.xs[q] : base;
             nt = in ? a.nt[q] : nt;
             ho = in ? a.hoff[q] : ho;
         }
-        return base + ((g * nt + (nl - ho)) * a.row_vecs + c);
+        return base + ((bs * nt + (n - ho)) * a.row_vecs + c);
     }
 }
 

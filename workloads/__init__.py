@@ -117,6 +117,12 @@ WORKLOADS: dict[str, Workload] = {
 WORKLOADS["mqa_k"] = W("mqa_k", ((32, 4096, 1, 128),), "bf16", (0, 128), "rotate_half", (1, 4096, 1, 128),
                        seed=16, directions=("fwd", "bwd"),
                        note="MQA K (one head, HD 128) at 4096 positions, rotate_half, bf16")
+# The GQA Q and K of one tensor-parallel rank (a 32/8-head layer split over
+# 8 GPUs: 4 Q heads and 1 K head) at 4096 positions shared by the batch.
+WORKLOADS["tp_qk"] = W("tp_qk", ((32, 4096, 4, 128), (32, 4096, 1, 128)), "bf16", (0, 128), "rotate_half",
+                       (1, 4096, 1, 128), seed=17, directions=("fwd",),
+                       note="GQA Q/K of one of 8 tensor-parallel ranks (4 + 1 heads, HD 128) at 4096 positions, "
+                            "rotate_half, bf16")
 # MLA's rope part with the page's coefficient 4 (two groups of two 16-lane parts).
 WORKLOADS["c3_coeff4"] = replace(WORKLOADS["c3"], name="c3_coeff4", mode=4, seed=15,
                                  note="MLA-style rope on lanes [0,64) of 192, rotary coefficient 4, bf16")
