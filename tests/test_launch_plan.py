@@ -242,8 +242,9 @@ def test_pos_plan_of_the_long_context_shard():
 @pytest.mark.parametrize("x_shape,dtype,sl,mode,per_batch,kernel,P", [
     ((2, 7, 1, 128), "bf16", (0, 128), RH, True, "vector", 8),   # one head: 8 positions of 8 threads per block
     ((3, 5, 2, 64), "bf16", (0, 64), IL, True, "vector", 8),
-    ((2, 7, 1, 128), "bf16", (0, 128), RH, False, "vector", 8),  # shared positions: 2 batches x 1 head per s
-    ((3, 5, 2, 64), "bf16", (0, 64), IL, False, "vector", 2),    # 3 batches x 2 heads per s
+    ((2, 7, 1, 128), "bf16", (0, 128), RH, False, "vector", 4),  # shared positions: 2 batches x 1 head per s,
+                                                                 # blocks of up to 64 threads
+    ((3, 5, 2, 64), "bf16", (0, 64), IL, False, "vector", 1),    # 3 batches x 2 heads per s: 48 threads
     ((2, 5, 3, 1024), "f32", (0, 1024), RH, False, "vector", 1),  # 512 pairs: the whole LDS table
     ((2, 6, 5, 64), "bf16", (3, 35), IL, False, "rows", None),    # odd start
     ((2, 5, 3, 48), "bf16", (4, 44), RH, False, "rows", None),    # halves of 40 bytes
@@ -299,6 +300,9 @@ def test_pos_plan_invariants_over_random_shapes():
         vheads = shared_positions and B > 1 and span * N < 128
         heads, positions = (B * N, S) if vheads else (N, B * S)
         assert p["threads"] == P * span * HL <= 256
+        # with the batches as heads, blocks of up to 64 threads unless one row is wider
+        if vheads:
+            assert p["threads"] <= max(64, span)
         assert (chunks - 1) * HL * U < heads <= chunks * HL * U
         assert HL <= heads
         if mode == IL:
@@ -306,7 +310,7 @@ def test_pos_plan_invariants_over_random_shapes():
         else:
             assert span * 16 == (L // 2) * es
         if P > 1:
-            assert span * HL < 128
+            assert span * HL < (64 if vheads else 128)
         assert P * (L // 2) <= 512
         assert p["blocks"] == -(-positions // P) * chunks
     assert seen["vector"] > 500 and seen["rows"] > 100, seen
@@ -344,12 +348,12 @@ def test_rotary_coefficient_position_plans(coeff, kernel):
 
 def test_pos_plan_shares_positions_across_the_batch():
     """Positions the same for every batch (one row, or a batch stride of 0):
-    the batches become heads of one position per s. For a single K head of
-    128 lanes (8 threads per row) and 32 batches: 16 head lanes of 2 heads,
-    one block per s."""
+    the batches become heads of one position per s, in blocks of up to 64
+    threads. For a single K head of 128 lanes (8 threads per row) and 32
+    batches: 8 head lanes of 2 heads, two blocks per s."""
     st, p = pos_plan((32, 4096, 1, 128), "bf16", (0, 128), RH, per_batch=False)
-    assert st == OK and p["head_lanes"] == 16 and p["head_chunks"] == 1 and p["positions_per_block"] == 1
-    assert p["blocks"] == 4096 and p["threads"] == 128
+    assert st == OK and p["head_lanes"] == 8 and p["head_chunks"] == 2 and p["positions_per_block"] == 1
+    assert p["blocks"] == 2 * 4096 and p["threads"] == 64
     # per-batch positions: 16 consecutive (b, s) positions per block, LDS permitting (512 entries / 64 pairs)
     st, p = pos_plan((32, 4096, 1, 128), "bf16", (0, 128), RH, per_batch=True)
     assert st == OK and p["positions_per_block"] == 8 and p["blocks"] == 32 * 4096 // 8

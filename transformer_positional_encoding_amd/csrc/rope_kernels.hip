@@ -626,9 +626,10 @@ static bool pos_vectors(const Plan& p, PosArgs* a, bool out)
 
 // Heads, positions per block and the grid, once the vectors a row's
 // threads cover (lo_vec, span) are set: U heads per thread, a position's
-// heads over up to `lanes_target` threads.
+// heads over up to `lanes_target` threads (`vheads_lanes` with the batches
+// as heads).
 static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid, int U,
-                             uint32_t lanes_target)
+                             uint32_t lanes_target, uint32_t vheads_lanes)
 {
     if (a->span < 1 || a->span > 256) return false;
     // positions shared by the batch (batch stride 0), and too few heads to
@@ -642,10 +643,11 @@ static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint3
     if (heads >= (1ull << 31) || positions >= (1ull << 31)) return false;
     a->N = (uint32_t)heads;
     a->pairs = (uint32_t)(p.L / 2);
-    a->HL = (uint32_t)std::min<uint64_t>(std::max<uint32_t>(1, lanes_target / a->span), heads);
+    const uint32_t target = a->vheads ? vheads_lanes : lanes_target;   // threads a position's heads fill
+    a->HL = (uint32_t)std::min<uint64_t>(std::max<uint32_t>(1, target / a->span), heads);
     a->chunks = (uint32_t)((heads + (uint64_t)a->HL * U - 1) / ((uint64_t)a->HL * U));
     a->lanes = a->span * a->HL;
-    a->P = a->lanes < lanes_target ? std::min<uint32_t>(lanes_target / a->lanes, kPosLds / a->pairs) : 1;
+    a->P = a->lanes < target ? std::min<uint32_t>(target / a->lanes, kPosLds / a->pairs) : 1;
     a->entries = a->P * a->pairs;
     if (a->entries > (uint32_t)kPosLds) return false;
     a->bs = (uint32_t)positions;
@@ -676,7 +678,7 @@ bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
         a->lo_vec = lines.lo_vec;
         a->span = lines.span;
     }
-    return pos_launch_shape(p, a, threads, grid, kUPos, kPosLanes);
+    return pos_launch_shape(p, a, threads, grid, kUPos, kPosLanes, kPosVheadsLanes);
 }
 
 // Out of place: the threads of a row cover all of its vectors.
@@ -685,7 +687,8 @@ bool pos_geometry_out(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* gr
     if (!pos_vectors(p, a, true)) return false;
     a->lo_vec = 0;
     a->span = a->row_vecs;
-    return pos_launch_shape(p, a, threads, grid, pos_out_heads(p.mode), pos_out_lanes(p.mode));
+    return pos_launch_shape(p, a, threads, grid, pos_out_heads(p.mode), pos_out_lanes(p.mode),
+                            pos_out_lanes(p.mode));
 }
 
 template <int DT, int TT, int DIR>
@@ -836,7 +839,7 @@ rope_status_t run_pos_multi(int32_t count, void* const xs[], const int64_t (*x_s
         Plan q = P[0];
         q.N = (int64_t)heads;
         m = each[0];
-        together = pos_launch_shape(q, &m, &threads, &grid, kUPos, kPosLanes);
+        together = pos_launch_shape(q, &m, &threads, &grid, kUPos, kPosLanes, kPosVheadsLanes);
         uint32_t first = 0;
         for (int i = 0; i < kMultiMax; ++i) {
             m.xs[i] = i < live ? each[i].x : nullptr;

@@ -74,6 +74,14 @@ __device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
 constexpr int kUPos = 2;
 constexpr int kPosLds = ROPE_D_LIMIT / 2;    // (cos, sin) entries per block
 constexpr uint32_t kPosLanes = 128;          // threads a position's heads fill before a block takes more positions
+// In place, with the batches as heads (positions shared by the batch, few
+// heads): blocks of half that width, so a small grid spreads over more
+// blocks. Measured on MI355X (cold data): the single K head (32,4096,1,128)
+// bf16 rotate_half 15.4 -> 14.7 us, one tensor-parallel rank's Q
+// (32,4096,4,128) and K (32,4096,1,128) in one call 63.6 -> 60.1 us. Out of
+// place the rotate_half rows are already 64 threads wide, and halving them
+// took the single K head from 15.7 to 22.3 us.
+constexpr uint32_t kPosVheadsLanes = 64;
 // The out-of-place position kernel's heads per thread and threads per
 // position, by mode. Measured on MI355X (cold data; the (16,8192,32,128)
 // shard's lanes [32,96), the MLA-style slice, a whole rotate_half head and
