@@ -471,6 +471,172 @@ def profile_target(name: str, reps: int, out_of_place: bool = False, positions: 
                       "copy_bytes": src.numel(), "rotating_copies": ncopy}), flush=True)
 
 
+PROBE_LIB = os.path.join(ROOT, "transformer_positional_encoding_amd", "_lib", "libhbm_probe.so")
+
+
+def probe_fn():
+    """hbm_probe_rmw from the benchmark's access-pattern probe library."""
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is not built (python -m transformer_positional_encoding_amd.build)")
+    f = ctypes.CDLL(PROBE_LIB).hbm_probe_rmw
+    i64 = ctypes.c_int64
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, i64, i64,
+                  ctypes.c_void_p]
+    return f
+
+
+def probe_variants(w) -> dict:
+    """The access patterns of a workload's in-place launch, as (load range,
+    store range) in 16-byte vectors of a row: the slice alone, the whole
+    128-byte lines around it with the slice stored (what the rotation
+    kernel loads), and the whole row (when a row is at most 64 vectors)."""
+    import workloads as W
+    B, S, N, D = w.x_shapes[0]
+    es = W.ESIZE[w.dtype]
+    row_vecs = D * es // 16
+    lo, hi = w.partial_slice[0] * es, w.partial_slice[1] * es
+    assert lo % 16 == 0 and hi % 16 == 0 and (D * es) % 128 == 0
+    sl = (lo // 16, hi // 16)
+    lines = (lo // 128 * 8, -(-hi // 128) * 8)
+    out = {"slice": (sl, sl)}
+    if lines != sl:
+        out["lines"] = (lines, sl)
+    if row_vecs <= 64:
+        out["row"] = ((0, row_vecs), (0, row_vecs))
+    return out
+
+
+def probe_pattern(w, spec: str) -> dict:
+    """One probe launch pattern from `spec` = VARIANT[:ORDER][:polK][:heads]:
+    VARIANT as in probe_variants; ORDER xcd_runs (default: about 384 KiB of
+    rows per XCD run, as in the rotation library), dispatch (no
+    renumbering), pN (runs of N blocks) or eighth (one eighth of the grid per
+    XCD); polK the load cache-policy bits K (0-7: sc0, sc1, nt; default:
+    the compiler's nontemporal loads); heads: a block takes the same head of
+    consecutive positions instead of consecutive heads."""
+    import workloads as W
+    B, S, N, D = w.x_shapes[0]
+    parts = spec.split(":")
+    ld, st = probe_variants(w)[parts[0]]
+    span = ld[1] - ld[0]
+    rpb = 64 // span
+    blocks = -(-(B * S * N) // rpb)
+    order, pol, stride = "xcd_runs", -1, 1
+    for part in parts[1:]:
+        if part.startswith("pol"):
+            pol = int(part[3:])
+        elif part == "heads":
+            stride = N
+        else:
+            order = part
+    if order == "xcd_runs":
+        p = max(1, round((384 << 10) / (rpb * D * W.ESIZE[w.dtype])))
+    elif order == "dispatch":
+        p = 1
+    elif order == "eighth":
+        p = max(1, blocks // 8)
+    else:
+        p = int(order[1:])
+    return {"load": ld, "store": st, "xcd_run_blocks": p, "load_policy": pol, "row_stride": stride}
+
+
+# The patterns --ceiling times per workload: the slice, the kernel's whole
+# lines and the whole row in two block orders; for half-line slices, every
+# load cache policy; for the MLA shape, further block orders.
+CEILING_PATTERNS = {
+    "c4": ["slice", "slice:dispatch", "lines", "lines:dispatch", "row", "row:dispatch"]
+          + [f"slice:pol{k}" for k in range(8)] + ["lines:pol4", "lines:pol0"],
+    "c3": ["slice", "slice:dispatch", "row", "slice:p8", "slice:p32", "slice:p512", "slice:p2048", "slice:eighth",
+           "slice:heads", "slice:heads:dispatch", "slice:pol0", "slice:pol7"],
+    "c4_f32": ["slice", "slice:dispatch", "row"],
+}
+
+
+def bench_ceiling(names, reps: int, stream) -> dict:
+    """Each workload's bare access pattern (hbm_probe_rmw: the same bytes
+    read and written back, no tables, no arithmetic) timed beside the
+    rotation kernel on the same rotating copies, so each kernel can be set
+    against what its access pattern alone achieves."""
+    import torch
+
+    import workloads as W
+    probe = probe_fn()
+    res = {}
+    for name in names:
+        w = W.WORKLOADS[name]
+        B, S, N, D = w.x_shapes[0]
+        es = W.ESIZE[w.dtype]
+        rows, row_vecs = B * S * N, D * es // 16
+        ncopy = rotating_copies(w)
+        xs = [W.make_x(w).to("cuda")]
+        xs += [xs[0].clone() for _ in range(ncopy - 1)]
+        r1, r2 = (t.to("cuda") for t in W.make_tables(w))
+        sptr = stream.cuda_stream
+        alg = w.algorithmic_bytes()
+        entry = {"x_shape": [B, S, N, D], "dtype": w.dtype, "slice": list(w.partial_slice),
+                 "rotating_copies": ncopy, "algorithmic_bytes": alg, "patterns": {}}
+
+        def probe_call(x, pat):
+            rc = probe(x.data_ptr(), rows, row_vecs, pat["load"][0], pat["load"][1], pat["store"][0],
+                       pat["store"][1], 1, pat["load_policy"], pat["xcd_run_blocks"], pat["row_stride"], sptr)
+            if rc != 0:
+                raise RuntimeError(f"hbm_probe_rmw returned {rc}")
+
+        for _ in range(2):    # two rounds, the second kept
+            for spec in CEILING_PATTERNS.get(name, ["slice", "slice:dispatch"]):
+                pat = probe_pattern(w, spec)
+                calls = [(probe_call, (xs[i], pat)) for i in range(ncopy)]
+                time_launches(calls, max(10, reps // 2), stream)
+                t = time_launches(calls, reps, stream)
+                moved = rows * 2 * (pat["store"][1] - pat["store"][0]) * 16
+                entry["patterns"][spec] = dict(
+                    pat, avg_launch_us=round(t * 1e6, 2), slice_GBps=round(moved / t / 1e9, 1),
+                    kernel_bytes_frac_at_this_time=round(alg / t / 1e9 / PEAK_GBPS, 4))
+            for d in ("bwd", "fwd"):
+                calls = [(launch_fn(d), (xs[i], r1, r2, w.mode, w.partial_slice)) for i in range(ncopy)]
+                time_launches(calls, max(10, reps // 2), stream)
+                t = time_launches(calls, reps, stream)
+                entry[f"kernel_{d}_us"] = round(t * 1e6, 2)
+                entry[f"kernel_{d}_frac"] = round(alg / t / 1e9 / PEAK_GBPS, 4)
+        res[name] = entry
+        del xs
+        torch.cuda.empty_cache()
+    return res
+
+
+def ceiling_target(name: str, spec: str, reps: int) -> None:
+    """Launches for rocprofv3 counter passes over one probe pattern (spec as
+    in probe_pattern), then a device copy of known size, as profile_target
+    does."""
+    import torch
+
+    import workloads as W
+    w = W.WORKLOADS[name]
+    B, S, N, D = w.x_shapes[0]
+    rows, row_vecs = B * S * N, D * W.ESIZE[w.dtype] // 16
+    pat = probe_pattern(w, spec)
+    ncopy = rotating_copies(w)
+    xs = [W.make_x(w).to("cuda")]
+    xs += [xs[0].clone() for _ in range(ncopy - 1)]
+    probe = probe_fn()
+    sptr = torch.cuda.current_stream().cuda_stream
+    for i in range(reps):
+        rc = probe(xs[i % ncopy].data_ptr(), rows, row_vecs, pat["load"][0], pat["load"][1], pat["store"][0],
+                   pat["store"][1], 1, pat["load_policy"], pat["xcd_run_blocks"], pat["row_stride"], sptr)
+        if rc != 0:
+            raise RuntimeError(f"hbm_probe_rmw returned {rc}")
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(pat, ceiling_target=name, spec=spec, reps=reps, copy_bytes=src.numel(),
+                          rotating_copies=ncopy)), flush=True)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -494,6 +660,11 @@ def main() -> int:
                     help="with --profile-target: launch the out-of-place entry points")
     ap.add_argument("--positions", action="store_true",
                     help="with --profile-target: launch the position entry points")
+    ap.add_argument("--ceiling", default=None, metavar="WL,WL",
+                    help="time each workload's bare access pattern (libhbm_probe.so) beside its kernel; "
+                         "prints one JSON line and nothing else")
+    ap.add_argument("--ceiling-target", default=None, metavar="WL:PATTERN",
+                    help="launch one access pattern of the probe (for rocprofv3 counter passes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -511,6 +682,14 @@ def main() -> int:
 
     if args.profile_target:
         profile_target(args.workload, args.reps, args.out_of_place, args.positions)
+        return 0
+    if args.ceiling_target:
+        name, _, variant = args.ceiling_target.partition(":")
+        ceiling_target(name, variant, args.reps)
+        return 0
+    if args.ceiling:
+        res = bench_ceiling([n for n in args.ceiling.split(",") if n], args.reps, torch.cuda.current_stream())
+        print(json.dumps({"ceiling": res}), flush=True)
         return 0
 
     stream = torch.cuda.current_stream()

@@ -16,6 +16,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(PKG, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "librope_partial.so")
 SOURCES = [os.path.join(CSRC, "rope_kernels.hip"), os.path.join(CSRC, "rope_plan.cpp")]
+# The bare access-pattern probe the benchmark times beside the kernels (its
+# own library; the rotation library does not use it).
+PROBE_LIB_PATH = os.path.join(LIB_DIR, "libhbm_probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "probe", "hbm_probe.hip")]
 ARCH = "gfx950"
 
 
@@ -36,17 +40,25 @@ def compile_flags() -> list[str]:
     ]
 
 
-def build(verbose: bool = False) -> str:
+def _compile(sources: list[str], out: str, verbose: bool) -> str:
     os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + compile_flags() + SOURCES + ["-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [hipcc()] + compile_flags() + sources + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build librope_partial.so")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"hipcc failed to build {os.path.basename(out)}")
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Build the rotation library and the benchmark's access-pattern probe;
+    returns the rotation library's path."""
+    _compile(SOURCES, LIB_PATH, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 
