@@ -219,6 +219,53 @@ def pos_tables(positions: np.ndarray, inv_freq: np.ndarray, L: int, mode: str, t
     return c, s_
 
 
+def proj_rope(x: np.ndarray, w: np.ndarray, y_shape, dtype: str, r1: np.ndarray, r2: np.ndarray, mode,
+              partial_slice, out_dtype: str, table_dtype: str | None = None) -> np.ndarray:
+    """A head projection followed by the rotation of each head's slice: the
+    Q projection and RoPE stages of "ascend-transformer-boost 的
+    MlaPreprocessOperation：MLA 预处理四阶段融合算子深度解析" (section 3, the
+    four-stage pipeline: the WUQ matmul gives headNum x 192 lanes per token,
+    then Q[..., :qRopeDim] is rotated with cos/sin of shape [tokenNum, 64]
+    given from outside; section 2, qRopeDim and qRotaryCoeff).
+
+    ``x`` holds M = B*S tokens of K inputs, (M, K); ``w`` the weights as a
+    linear layer stores them, (N, K) with N = H*Dh (output lanes by inputs,
+    the page's transposed-weight default). ``y_shape`` = (B, S, H, Dh).
+    Storage as for rope_rows (fp32 as float32, 16-bit as uint16 bits).
+
+    In the page's order, with the projection result in fp32 (a fused
+    epilogue holds it in fp32 registers; nothing in between is rounded to
+    the storage type):
+      1. p = sum_k x[m,k] * w[n,k], in double precision (numpy matmul: the
+         products of 16-bit inputs are exact, and a double sum of them is
+         exact to far below fp32 resolution), rounded once to fp32;
+      2. the slice [start, end) of each head of p rotated as fp32 data by
+         rope_rows (fwd: double-precision evaluation, one rounding to fp32),
+         tables (B or 1, S or 1, 1 or H, L) broadcasting as rope_rows takes
+         them;
+      3. rounded once more, to nearest even, to ``out_dtype`` (no rounding
+         when it is fp32).
+    Returns y, shape (B, S, H, Dh), in ``out_dtype`` storage."""
+    B, S, H, Dh = (int(v) for v in y_shape)
+    M, N = B * S, H * Dh
+    for name, a in (("x", x), ("w", w)):
+        _check_storage(a, dtype)
+    if x.shape != (M, x.shape[-1]) or w.shape != (N, x.shape[-1]):
+        raise ValueError("x must be (B*S, K) and w (H*Dh, K)")
+    widen = {"f32": lambda a: a, "f16": f16_bits_to_f32, "bf16": bf16_bits_to_f32}[dtype]
+    xd = widen(x).astype(np.float64)
+    wd = widen(w).astype(np.float64)
+    p = np.ascontiguousarray((xd @ wd.T).astype(np.float32)).reshape(B, S, H, Dh)
+    start, end = (0, 0) if partial_slice is None else (int(partial_slice[0]), int(partial_slice[1]))
+    if end > start:
+        rope_rows(p, (B, S, H, Dh), "f32", r1, r2, mode, (start, end), "fwd",
+                  table_dtype=table_dtype if table_dtype else dtype)
+    if out_dtype == "f32":
+        return p
+    narrow = {"f16": f32_to_f16_bits, "bf16": f32_to_bf16_bits}[out_dtype]
+    return narrow(p)
+
+
 def round_double(values: np.ndarray, dtype: str) -> np.ndarray:
     """Doubles rounded once, to nearest even, to the values of ``dtype``
     (returned as float32, which holds every value of the three types)."""
