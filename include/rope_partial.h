@@ -48,6 +48,12 @@ extern "C" {
 /* symbols of the C ABI; everything else in the library is hidden */
 #define ROPE_API __attribute__((visibility("default")))
 
+/*
+ * Status codes. The classes follow the aclnn convention described on the
+ * CANN ops-transformer page on aclnnMoeTokenUnpermuteWithEpGrad, section
+ * 六、返回值与错误码 (a NULL required tensor, a parameter outside the supported
+ * range, an inner error); the numbers are this library's own.
+ */
 typedef enum rope_status {
     ROPE_OK = 0,
     ROPE_ERR_NULLPTR = 1,      /* a required pointer is NULL                   */
@@ -102,8 +108,8 @@ typedef enum rope_dtype {
  * pointer (no-op, as the page specifies for forward and backward); then NULL
  * data or table pointers (ROPE_ERR_NULLPTR); then table shapes and strides
  * (ROPE_ERR_INVALID); finally the launch (ROPE_ERR_RUNTIME if HIP reports
- * an error). ROPE_ERR_UNSUPPORTED is reserved: no valid combination returns
- * it at present.
+ * an error). ROPE_ERR_UNSUPPORTED is not returned by this call (only
+ * rope_proj_fwd returns it, for shapes its kernel does not tile).
  * Overlapping x with r1 or r2 is undefined. Results are deterministic: each
  * element is computed by one thread from the same inputs on every call.
  */
@@ -187,7 +193,10 @@ ROPE_API rope_status_t rope_partial_bwd_out(
  * Every tensor is checked before anything is launched: on an error no
  * memory has been touched, and rope_last_error() names the tensor.
  * count outside [0, ROPE_MULTI_MAX] is ROPE_ERR_INVALID; NULL xs or x_shapes
- * with count > 0 is ROPE_ERR_NULLPTR. The tensors must not overlap.
+ * with count > 0 is ROPE_ERR_NULLPTR. Tensors that share any byte (the same
+ * tensor passed twice included) are ROPE_ERR_INVALID, checked after every
+ * tensor's own checks and before any launch: one fused launch would read
+ * and write the shared bytes from two threads at once.
  */
 ROPE_API rope_status_t rope_partial_fwd_inplace_multi(
     int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
@@ -303,7 +312,8 @@ ROPE_API rope_status_t rope_partial_bwd_out_pos(
  * Every tensor is checked before anything is launched: on an error no
  * memory has been touched, and rope_last_error() names the tensor. count
  * outside [0, ROPE_MULTI_MAX] is ROPE_ERR_INVALID; NULL xs or x_shapes with
- * count > 0 is ROPE_ERR_NULLPTR. The tensors must not overlap.
+ * count > 0 is ROPE_ERR_NULLPTR. Tensors that share any byte are
+ * ROPE_ERR_INVALID, as for rope_partial_fwd_inplace_multi.
  */
 ROPE_API rope_status_t rope_partial_fwd_inplace_pos_multi(
     int32_t count, void* const xs[], const int64_t x_shapes[][4], rope_dtype_t dtype,
@@ -386,6 +396,64 @@ ROPE_API rope_status_t rope_partial_launch_info_pos(
     const int64_t* positions, const int64_t positions_shape[2], const int64_t positions_strides[2],
     const double* inv_freq, rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
     int64_t info[ROPE_LAUNCH_INFO_LEN]);
+
+/* ===================== projection with a rotary epilogue ===================== */
+
+/*
+ * rope_proj_fwd -- a head projection whose epilogue rotates each head's
+ * slice before the result is stored: for every token m = b*S + s and output
+ * lane n = h*Dh + j,
+ *     p[m,n] = fl32( sum_k x[m,k] * w[n,k] )            (fp32 accumulation)
+ *     y[b,s,h,j] = p rotated on the lanes [start,end) of each head, forward,
+ *                  as rope_partial_fwd_inplace rotates fp32 data, then
+ *                  rounded once to y's type.
+ * This is the Q projection and RoPE stages of "ascend-transformer-boost 的
+ * MlaPreprocessOperation：MLA 预处理四阶段融合算子深度解析", section 3 (the
+ * WUQ matmul gives headNum x 192 lanes per token; Q[..., :qRopeDim] is then
+ * rotated with cos/sin of shape [tokenNum, 64] given from outside) and
+ * section 2 (qRopeDim, qRotaryCoeff), fused so that the projection result is
+ * rotated in registers: it is never rounded to the storage type, and never
+ * written and read back, before the rotation. The quantisation, RMS norms
+ * and KV-cache stages of that page are not part of this call.
+ *
+ *   y            device buffer of the result, (B, S, H, Dh) contiguous, of
+ *                type y_dtype; owned by the caller; must not overlap x or w.
+ *   y_dtype      the type of x and w, or ROPE_DTYPE_F32 (no final rounding).
+ *   x            device buffer (B*S, K), row-major, of `dtype`.
+ *   w            device buffer (H*Dh, K), row-major, of `dtype`: output lanes
+ *                by inputs, as a linear layer stores its weight (the page's
+ *                transposed-weight default).
+ *   dtype        ROPE_DTYPE_BF16 or ROPE_DTYPE_F16.
+ *   y_shape      host array {B, S, H, Dh}.
+ *   K            inputs per token: a positive multiple of 64.
+ *   r1, r2, shapes and strides, table_dtype, mode, partial_slice
+ *                as for rope_partial_fwd_inplace, against y's shape: tables
+ *                (1 or B, 1 or S, 1 or H, L); the page's case is one row per
+ *                token, (B, S, 1, L) or (1, S, 1, L) broadcast over B.
+ *   stream       hipStream_t to launch on, or NULL.
+ *
+ * Checks, in this order: the scalar arguments of rope_partial_fwd_inplace
+ * on y's shape with y_dtype (ROPE_ERR_NULLPTR for a NULL y_shape,
+ * ROPE_ERR_INVALID otherwise); dtype bf16 or fp16, y_dtype dtype or fp32
+ * and K >= 0 (ROPE_ERR_INVALID); an empty y returns ROPE_OK without reading
+ * any pointer; K not a positive multiple of 64, or Dh not one of 32, 64,
+ * 96, 128 and 192 (ROPE_ERR_UNSUPPORTED: block tiles hold whole heads);
+ * NULL y, x or w (ROPE_ERR_NULLPTR); y, x or w not 16-byte aligned or
+ * sizes beyond 64-bit offsets (ROPE_ERR_INVALID); x or w of 2^31 elements
+ * or more (ROPE_ERR_UNSUPPORTED); y overlapping x or w (ROPE_ERR_INVALID); then,
+ * for a non-empty slice, the tables as for rope_partial_fwd_inplace; a grid
+ * too large for one launch (ROPE_ERR_UNSUPPORTED); finally the launch
+ * (ROPE_ERR_RUNTIME). An empty slice gives the plain projection. The
+ * library allocates nothing; results are deterministic (each output is
+ * accumulated by one wave in a fixed order).
+ */
+ROPE_API rope_status_t rope_proj_fwd(
+    void* y, rope_dtype_t y_dtype, const void* x, const void* w, rope_dtype_t dtype,
+    const int64_t y_shape[4], int64_t K,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    void* stream);
 
 /* ============================== status ============================== */
 

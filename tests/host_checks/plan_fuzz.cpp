@@ -202,7 +202,82 @@ int main()
         if (p.noop || p.copy_only || p.src != (x == y ? nullptr : xp)) ++bad;
         ++out_ok;
     }
+    // The projection with a rotary epilogue: random shapes, K, types and
+    // pointers (y, x, w below 2^47, sometimes overlapping). Accepted calls
+    // must be within what the kernel tiles: K a positive multiple of 64, a
+    // head dimension the kernel takes, x and w under 2^31 elements, 16-byte
+    // aligned, disjoint buffers, and tables whose offsets fit in 64 bits.
+    long proj_ok = 0;
+    for (long it = 0; it < iters / 3; ++it) {
+        int64_t ys[4], sl[2], ts[4], tst[4];
+        static const int64_t dhs[] = {32, 64, 96, 128, 192, 100, 256, 2};
+        for (int k = 0; k < 3; ++k) ys[k] = (next() % 4) ? (int64_t)(next() % 9) : pick();
+        ys[3] = (next() % 4) ? dhs[next() % 8] : pick();
+        const int64_t K = (next() % 4) ? 64 * (int64_t)(next() % 40) : pick();
+        sl[0] = (int64_t)(next() % 64);
+        sl[1] = sl[0] + 2 * (int64_t)(next() % 40);
+        const int64_t L = sl[1] - sl[0];
+        for (int k = 0; k < 4; ++k) {
+            ts[k] = (next() % 4) ? ((next() % 2) ? 1 : ys[k]) : pick();
+            tst[k] = (next() % 4) ? (int64_t)(next() % 100000) : pick();
+        }
+        ts[3] = (next() % 8) ? L : pick();
+        tst[3] = (next() % 8) ? 1 : pick();
+        uintptr_t base[3];
+        for (int k = 0; k < 3; ++k) base[k] = (uintptr_t)((next() % (1ull << 40)) & ~(uintptr_t)((next() % 8) ? 15 : 0));
+        if (next() % 4 == 0) base[0] = base[1] + (uintptr_t)(next() % 4096);   // y near x
+        const int dt = (int)(next() % 3), yt = (next() % 2) ? dt : (int)(next() % 3), tt = (int)(next() % 3);
+        const int64_t mode = (next() % 4) ? (int64_t)(next() % 2) : 2 * (int64_t)(1 + next() % 4);
+        rope::ProjPlan q;
+        std::string why;
+        const rope_status_t st = rope::make_proj_plan(
+            reinterpret_cast<void*>(base[0]), (rope_dtype_t)yt, reinterpret_cast<void*>(base[1]),
+            reinterpret_cast<void*>(base[2]), (rope_dtype_t)dt, ys, K, fake, ts, tst, fake, ts, tst,
+            (rope_dtype_t)tt, mode, sl, &q, &why);
+        if (st != ROPE_OK) {
+            if (why.empty() || (st != ROPE_ERR_NULLPTR && st != ROPE_ERR_INVALID && st != ROPE_ERR_UNSUPPORTED)) ++bad;
+            continue;
+        }
+        if (q.noop) {
+            if (!(ys[0] == 0 || ys[1] == 0 || ys[2] == 0 || ys[3] == 0)) ++bad;
+            continue;
+        }
+        ++proj_ok;
+        const i128 M = (i128)ys[0] * ys[1], N = (i128)ys[2] * ys[3];
+        bool good = K > 0 && K % 64 == 0 && rope::proj_head_dim_supported(ys[3]) && M * K < ((i128)1 << 31) &&
+                    N * K < ((i128)1 << 31) && (dt == ROPE_DTYPE_BF16 || dt == ROPE_DTYPE_F16) &&
+                    (yt == dt || yt == ROPE_DTYPE_F32) && (base[0] & 15) == 0 && (base[1] & 15) == 0 &&
+                    (base[2] & 15) == 0;
+        const i128 yb = M * N * (yt == ROPE_DTYPE_F32 ? 4 : 2), xb = M * K * 2, wb = N * K * 2;
+        const auto apart = [](i128 a, i128 na, i128 b, i128 nb) { return a + na <= b || b + nb <= a; };
+        good = good && apart(base[0], yb, base[1], xb) && apart(base[0], yb, base[2], wb);
+        if (!good) ++bad;
+    }
+    // Multi-tensor calls: tensors that share a byte are rejected, others pass.
+    long disjoint_ok = 0, disjoint_bad = 0;
+    for (long it = 0; it < iters / 30; ++it) {
+        rope::Plan ps[4];
+        const int n = 1 + (int)(next() % 4);
+        for (int i = 0; i < n; ++i) {
+            ps[i].x = reinterpret_cast<void*>((uintptr_t)(next() % (1ull << 16)));
+            ps[i].bytes = (int64_t)(1 + next() % 4096);
+        }
+        std::string why;
+        const bool rejected = rope::check_disjoint(ps, n, &why) != ROPE_OK;
+        bool overlap = false;
+        for (int i = 0; i < n; ++i)
+            for (int j = i + 1; j < n; ++j) {
+                const i128 a = (i128)reinterpret_cast<uintptr_t>(ps[i].x), b = (i128)reinterpret_cast<uintptr_t>(ps[j].x);
+                if (!(a + ps[i].bytes <= b || b + ps[j].bytes <= a)) overlap = true;
+            }
+        if (rejected != overlap) ++bad;
+        (rejected ? disjoint_bad : disjoint_ok)++;
+    }
+    printf("projection accepted %ld, multi disjoint %ld overlapping %ld\n", proj_ok, disjoint_ok, disjoint_bad);
     printf("iters %ld accepted %ld noop %ld out-of-place accepted %ld copies %ld overlaps %ld bad %ld\n", iters, ok,
            noop, out_ok, out_copy, out_overlap, bad);
-    return bad == 0 && ok > 1000 && noop > 1000 && out_ok > 1000 && out_copy > 1000 && out_overlap > 1000 ? 0 : 1;
+    return bad == 0 && ok > 1000 && noop > 1000 && out_ok > 1000 && out_copy > 1000 && out_overlap > 1000 &&
+                   proj_ok > 1000 && disjoint_ok > 1000 && disjoint_bad > 1000
+               ? 0
+               : 1;
 }

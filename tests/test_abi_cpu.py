@@ -391,3 +391,66 @@ def test_position_multi_noops(direction):
     assert pmcall(direction, ptrs=None, shapes=None, count=0) == OK
     assert pmcall(direction, ptrs=(None, None), pos=None, inv_freq=None, sl=(8, 8)) == OK
     assert pmcall(direction, ptrs=(None, None), shapes=((0, 4, 3, 64), (2, 0, 1, 64)), pos=None, inv_freq=None) == OK
+
+
+# ---------------------------------------------------------------- overlapping multi-tensor calls
+
+@pytest.mark.parametrize("direction", ["fwd", "bwd"])
+def test_multi_rejects_overlapping_tensors(direction):
+    """The same tensor twice, or two byte ranges that share bytes, are
+    ROPE_ERR_INVALID before any launch (fake aligned addresses: nothing is
+    dereferenced)."""
+    shp = (2, 4, 3, 64)                      # bf16: 3072 bytes
+    nbytes = 2 * 4 * 3 * 64 * 2
+    tab = 0x200000
+    args = dict(dtype=2, r1_ptr=tab, r1_shape=(1, 4, 1, 64), r1_strides=(0, 64, 0, 1), r2_ptr=tab,
+                r2_shape=(1, 4, 1, 64), r2_strides=(0, 64, 0, 1), table_dtype=2, mode=1, partial_slice=(0, 64))
+    for ptrs in ([0x100000, 0x100000], [0x100000, 0x100000 + nbytes - 16], [0x100000 + 16, 0x100000, 0x140000]):
+        st = rp.raw_multi_call(direction, ptrs, [shp] * len(ptrs), **args)
+        assert st == rp.ROPE_ERR_INVALID, ptrs
+        assert "overlap" in rp.last_error()
+    pos = dict(pos_ptr=0x300000, pos_shape=(1, 4), pos_strides=(4, 1), inv_freq_ptr=0x400000, table_dtype=2,
+               mode=1, partial_slice=(0, 64))
+    st = rp.raw_pos_multi_call(direction, [0x100000, 0x100000], [shp, shp], 2, **pos)
+    assert st == rp.ROPE_ERR_INVALID and "overlap" in rp.last_error()
+
+
+# ---------------------------------------------------------------- projection with a rotary epilogue
+
+def _proj(**kw):
+    base = dict(y_ptr=0x1000000, y_dtype=2, x_ptr=0x2000000, w_ptr=0x3000000, dtype=2, y_shape=(1, 8, 2, 192),
+                K=128, r1_ptr=0x4000000, r1_shape=(1, 8, 1, 64), r1_strides=(0, 64, 0, 1), r2_ptr=0x5000000,
+                r2_shape=(1, 8, 1, 64), r2_strides=(0, 64, 0, 1), table_dtype=2, mode=1, partial_slice=(0, 64))
+    base.update(kw)
+    return rp.raw_proj_call(*base.values())
+
+
+@pytest.mark.parametrize("kwargs,code,text", [
+    (dict(dtype=0, y_dtype=0), rp.ROPE_ERR_INVALID, "bf16 or fp16"),
+    (dict(y_dtype=1), rp.ROPE_ERR_INVALID, "type of x and w"),
+    (dict(K=-64), rp.ROPE_ERR_INVALID, "K is negative"),
+    (dict(K=96), rp.ROPE_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(K=0), rp.ROPE_ERR_UNSUPPORTED, "multiple of 64"),
+    (dict(y_shape=(1, 8, 2, 160), r1_shape=(1, 8, 1, 64), r2_shape=(1, 8, 1, 64)), rp.ROPE_ERR_UNSUPPORTED,
+     "head dimension"),
+    (dict(y_ptr=None), rp.ROPE_ERR_NULLPTR, "y is NULL"),
+    (dict(w_ptr=None), rp.ROPE_ERR_NULLPTR, "w is NULL"),
+    (dict(x_ptr=0x2000008), rp.ROPE_ERR_INVALID, "16-byte aligned"),
+    (dict(y_ptr=0x2000000 + 64), rp.ROPE_ERR_INVALID, "overlaps"),
+    (dict(r1_shape=(1, 8, 1, 32)), rp.ROPE_ERR_INVALID, "last dimension"),
+    (dict(r2_ptr=None), rp.ROPE_ERR_NULLPTR, "r2 is NULL"),
+    (dict(partial_slice=(0, 200)), rp.ROPE_ERR_INVALID, "end must be <= D"),
+    (dict(mode=3), rp.ROPE_ERR_INVALID, "mode"),
+    (dict(y_shape=(1, 1 << 20, 2, 192), r1_shape=(1, 1 << 20, 1, 64), r2_shape=(1, 1 << 20, 1, 64), K=4096),
+     rp.ROPE_ERR_UNSUPPORTED, "2^31"),
+])
+def test_projection_argument_errors(kwargs, code, text):
+    assert _proj(**kwargs) == code
+    assert text in rp.last_error()
+
+
+def test_projection_noops_need_no_pointers():
+    """No tokens (or no heads): ROPE_OK without looking at any pointer."""
+    none = dict(y_ptr=None, x_ptr=None, w_ptr=None, r1_ptr=None, r2_ptr=None)
+    assert _proj(y_shape=(0, 8, 2, 192), **none) == rp.ROPE_OK
+    assert _proj(y_shape=(1, 8, 0, 192), **none) == rp.ROPE_OK

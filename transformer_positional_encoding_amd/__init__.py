@@ -24,7 +24,7 @@ __all__ = [
     "rope_partial_fwd_inplace_pos", "rope_partial_bwd_inplace_pos", "rope_inv_freq",
     "rope_partial_fwd_out_pos", "rope_partial_bwd_out_pos", "partial_rotary_mul_pos",
     "inplace_partial_rotary_mul_pos", "rope_partial_fwd_inplace_pos_multi", "rope_partial_bwd_inplace_pos_multi",
-    "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
+    "rope_proj_fwd", "RopeError", "library", "LIB_PATH", "ROPE_OK", "ROPE_ERR_NULLPTR", "ROPE_ERR_INVALID",
     "ROPE_ERR_UNSUPPORTED", "ROPE_ERR_RUNTIME", "MODES", "DTYPE_CODES",
 ]
 
@@ -100,6 +100,9 @@ def library() -> ctypes.CDLL:
         L.rope_partial_check.argtypes = _ENTRY_ARGTYPES[:-1]
         L.rope_partial_launch_info.restype = ctypes.c_int
         L.rope_partial_launch_info.argtypes = _ENTRY_ARGTYPES[:-1] + [ctypes.POINTER(ctypes.c_int64)]
+        L.rope_proj_fwd.restype = ctypes.c_int
+        L.rope_proj_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.POINTER(ctypes.c_int64), ctypes.c_int64] + _ENTRY_ARGTYPES[3:]
         L.rope_status_string.restype = ctypes.c_char_p
         L.rope_status_string.argtypes = [ctypes.c_int]
         L.rope_last_error.restype = ctypes.c_char_p
@@ -265,6 +268,16 @@ def raw_pos_multi_call(direction: str, x_ptrs, x_shapes, dtype: int, pos_ptr, po
     pt = None if pos_strides is None else _I64x2(int(pos_strides[0]), int(pos_strides[1]))
     return fn(int(count), ptrs, shapes, int(dtype), pos_ptr, ps, pt, inv_freq_ptr, int(table_dtype), int(mode), sl,
               stream)
+
+
+def raw_proj_call(y_ptr, y_dtype: int, x_ptr, w_ptr, dtype: int, y_shape, K: int, r1_ptr, r1_shape, r1_strides,
+                  r2_ptr, r2_shape, r2_strides, table_dtype: int, mode: int, partial_slice, stream=None) -> int:
+    """rope_proj_fwd with plain integers and sequences (None = NULL); returns
+    the status code without raising."""
+    sl = None if partial_slice is None else _I64x2(*partial_slice)
+    return library().rope_proj_fwd(y_ptr, y_dtype, x_ptr, w_ptr, dtype, _arr4(y_shape), int(K),
+                                   r1_ptr, _arr4(r1_shape), _arr4(r1_strides), r2_ptr, _arr4(r2_shape),
+                                   _arr4(r2_strides), table_dtype, mode, sl, stream)
 
 
 def last_error() -> str:
@@ -879,3 +892,57 @@ def rope_partial_bwd_inplace_pos_multi(xs, positions, inv_freq, rotary_mode="int
                                        table_dtype=None, stream=None) -> None:
     """Backward of :func:`rope_partial_fwd_inplace_pos_multi`."""
     _call_pos_multi("bwd", xs, positions, inv_freq, rotary_mode, partial_slice, table_dtype, stream)
+
+
+def rope_proj_fwd(x, w, r1, r2, heads: int, rotary_mode="interleave", partial_slice=None, out=None,
+                  out_dtype=None, stream=None):
+    """Head projection with a rotary epilogue (the C ABI's rope_proj_fwd):
+    ``y[b,s,h,:] = rotate(x[b,s,:] @ w[h*Dh:(h+1)*Dh, :].T)`` with each head's
+    lanes ``[start, end)`` rotated by the tables, the projection accumulated
+    in fp32 and rounded once, after the rotation, to ``out_dtype`` ("ascend-
+    transformer-boost 的 MlaPreprocessOperation：MLA 预处理四阶段融合算子深度解析",
+    section 3: the Q projection and RoPE stages, fused).
+
+    x: (B, S, K) or (M, K) bf16/fp16; w: (H*Dh, K) of x's dtype (a linear
+    layer's weight); r1/r2: 4-D tables broadcasting against (B, S, H, L).
+    Returns ``out`` (allocated when None): (B, S, H, Dh) of ``out_dtype``
+    (x's dtype by default, or torch.float32)."""
+    import torch
+    if isinstance(rotary_mode, str):
+        if rotary_mode not in MODES:
+            raise ValueError(f"rotary_mode must be one of {sorted(MODES)}")
+        rotary_mode = MODES[rotary_mode]
+    for name, t in (("x", x), ("w", w), ("r1", r1), ("r2", r2)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+    if x.dim() not in (2, 3) or w.dim() != 2:
+        raise ValueError("x must be (B, S, K) or (M, K) and w (H*Dh, K)")
+    B, S = (1, x.shape[0]) if x.dim() == 2 else (x.shape[0], x.shape[1])
+    K = x.shape[-1]
+    N = w.shape[0]
+    if w.shape[1] != K or heads <= 0 or N % heads:
+        raise ValueError(f"w must be (heads*Dh, K={K}), got {tuple(w.shape)} for {heads} heads")
+    if w.dtype != x.dtype:
+        raise ValueError("x and w must share a dtype")
+    if not (x.is_contiguous() and w.is_contiguous()):
+        raise ValueError("x and w must be contiguous")
+    y_shape = (B, S, heads, N // heads)
+    if out is None:
+        out = torch.empty(y_shape, dtype=out_dtype or x.dtype, device=x.device)
+    elif tuple(out.shape) != y_shape or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {y_shape} tensor")
+    for name, t in (("x", x), ("w", w), ("out", out)):
+        if t.numel() and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    dev = x.device
+    handle = (torch.cuda.current_stream(dev).cuda_stream if x.is_cuda else None) if stream is None else \
+        getattr(stream, "cuda_stream", stream)
+    switch = x.is_cuda and dev.index != torch.cuda.current_device()
+    with torch.cuda.device(dev) if switch else _nullcontext():
+        st = raw_proj_call(out.data_ptr() or None, _dtype_code(out), x.data_ptr() or None, w.data_ptr() or None,
+                           _dtype_code(x), y_shape, K, r1.data_ptr() or None, tuple(r1.shape), tuple(r1.stride()),
+                           r2.data_ptr() or None, tuple(r2.shape), tuple(r2.stride()),
+                           _dtype_code(r1) if r1.dtype == r2.dtype else -1, rotary_mode, partial_slice, handle)
+    if st != ROPE_OK:
+        raise RopeError(st, last_error())
+    return out

@@ -35,6 +35,7 @@
 #include "rope_partial.h"
 #include "rope_plan.hpp"
 #include "rope_pos_kernels.hpp"
+#include "rope_proj_kernels.hpp"
 #include "rope_vec_kernels.hpp"
 
 namespace rope {
@@ -818,6 +819,11 @@ rope_status_t run_pos_multi(int32_t count, void* const xs[], const int64_t (*x_s
         if (!P[live].noop) ++live;
     }
     if (live == 0) return ROPE_OK;
+    {
+        std::string why;
+        rope_status_t st = check_disjoint(P, live, &why);
+        if (st != ROPE_OK) return set_error(st, why);
+    }
     int cus = 0;
     rope_status_t st = device_cus(&cus);
     if (st != ROPE_OK) return st;
@@ -931,6 +937,101 @@ rope_status_t run_out(void* y, const void* x, const int64_t x_shape[4], rope_dty
     return ROPE_OK;
 }
 
+// Projection with a rotary epilogue: one launch of rope_proj_kernel.
+template <int DT, int BN>
+hipError_t launch_proj(const ProjArgs& a, bool tvec, uint32_t grid, hipStream_t s)
+{
+    if (tvec)
+        hipLaunchKernelGGL((rope_proj_kernel<DT, BN, true>), dim3(grid), dim3(kProjThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((rope_proj_kernel<DT, BN, false>), dim3(grid), dim3(kProjThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void* w, rope_dtype_t dtype,
+                       const int64_t y_shape[4], int64_t K,
+                       const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                       const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                       rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2], void* stream)
+{
+    ProjPlan q;
+    std::string why;
+    rope_status_t st = make_proj_plan(y, y_dtype, x, w, dtype, y_shape, K, r1, r1_shape, r1_strides, r2, r2_shape,
+                                      r2_strides, table_dtype, mode, partial_slice, &q, &why);
+    if (st != ROPE_OK) return set_error(st, why);
+    if (q.noop) return ROPE_OK;
+    const Plan& p = q.rope;
+    ProjArgs a{};
+    a.x = static_cast<const uint16_t*>(q.x);
+    a.w = static_cast<const uint16_t*>(q.w);
+    a.y = q.y;
+    a.ydt = q.out_dtype;
+    a.tdt = p.tdtype;
+    a.r1 = p.r1;
+    a.r2 = p.r2;
+    a.t1b = p.t1[0]; a.t1s = p.t1[1]; a.t1n = p.t1[2];
+    a.t2b = p.t2[0]; a.t2s = p.t2[1]; a.t2n = p.t2[2];
+    a.M = p.B * p.S;
+    a.N = p.N * p.D;
+    a.K = q.K;
+    a.S = p.S;
+    a.Dh = (int32_t)p.D;
+    a.start = (int32_t)p.start;
+    a.L = (int32_t)p.L;
+    a.half = p.L > 0 ? (int32_t)p.half : 1;
+    // block tiles of whole heads: 192 lanes for heads of 96 or 192, else 128
+    const int BN = p.D % 3 == 0 ? 192 : 128;
+    const int64_t MB = (a.M + kProjBM - 1) / kProjBM, NB = (a.N + BN - 1) / BN;
+    // the dispatch packet holds the grid in work-items as a 32-bit number
+    if (MB * NB > (int64_t)(0xFFFFFFFFull / kProjThreads))
+        return set_error(ROPE_ERR_UNSUPPORTED, "the projection's grid exceeds one launch");
+    a.MB = (int32_t)MB;
+    a.NB = (int32_t)NB;
+    // Measured on MI355X on the (4*4096 tokens, 1536) x (24576, 1536) MLA
+    // projection: groups of 2 M-tiles with each XCD taking a contiguous run
+    // of tiles were the fastest of 1, 2, 4, 8, 16 (by up to 8%).
+    a.group_m = 2;
+    a.xcd_chunk = (int32_t)(MB * NB / 8);
+    a.s_div = make_fastdiv((uint32_t)p.S);
+    a.dh_div = make_fastdiv((uint32_t)p.D);
+    a.l_div = make_fastdiv((uint32_t)std::max<int64_t>(p.L, 1));
+    // tables that differ by head are staged per head of the tile
+    a.t1h = p.t1[2] != 0 ? (int32_t)(BN / p.D) : 1;
+    a.t2h = p.t2[2] != 0 ? (int32_t)(BN / p.D) : 1;
+    // the epilogue stages table rows in 16-byte chunks when every row of both
+    // tables starts 16-byte aligned and L fills whole chunks
+    bool tvec = false;
+    {
+        const int64_t per = 16 / p.tesize;
+        bool v = p.L > 0 && p.L % per == 0 && aligned16(p.r1) && aligned16(p.r2);
+        for (int k = 0; k < 3 && v; ++k) v = p.t1[k] % per == 0 && p.t2[k] % per == 0;
+        tvec = v;
+        a.lc_div = make_fastdiv((uint32_t)std::max<int64_t>(p.L / per, 1));
+    }
+    // the 8-lane vectors of a head that meet the slice
+    {
+        const int64_t vph = p.D / 8;
+        a.rv_lo = p.L > 0 ? (int32_t)(p.start / 8) : 0;
+        a.nrv = p.L > 0 ? (int32_t)((p.start + p.L + 7) / 8 - p.start / 8) : 0;
+        const int64_t heads_t = BN / p.D;
+        a.rot_row_div = make_fastdiv((uint32_t)std::max<int64_t>(heads_t * a.nrv, 1));
+        a.rot_head_div = make_fastdiv((uint32_t)std::max<int32_t>(a.nrv, 1));
+        a.cp_row_div = make_fastdiv((uint32_t)std::max<int64_t>(heads_t * (vph - a.nrv), 1));
+        a.cp_head_div = make_fastdiv((uint32_t)std::max<int64_t>(vph - a.nrv, 1));
+    }
+    const uint32_t grid = (uint32_t)(MB * NB);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (q.in_dtype == ROPE_DTYPE_BF16)
+        err = BN == 192 ? launch_proj<ROPE_DTYPE_BF16, 192>(a, tvec, grid, s)
+                        : launch_proj<ROPE_DTYPE_BF16, 128>(a, tvec, grid, s);
+    else
+        err = BN == 192 ? launch_proj<ROPE_DTYPE_F16, 192>(a, tvec, grid, s)
+                        : launch_proj<ROPE_DTYPE_F16, 128>(a, tvec, grid, s);
+    if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
+    return ROPE_OK;
+}
+
 // Several tensors with shared tables: every tensor is checked before any
 // launch; tensors that all take the same vector kernel and block size go in
 // one launch, otherwise each is launched in turn (same result either way).
@@ -954,6 +1055,13 @@ rope_status_t run_multi(int32_t count, void* const xs[], const int64_t (*x_shape
         if (!L[live].p.noop) ++live;
     }
     if (live == 0) return ROPE_OK;
+    {
+        Plan ps[kMultiMax];
+        for (int i = 0; i < live; ++i) ps[i] = L[i].p;
+        std::string why;
+        rope_status_t st = check_disjoint(ps, live, &why);
+        if (st != ROPE_OK) return set_error(st, why);
+    }
     int cus = 0;
     rope_status_t st = device_cus(&cus);
     if (st != ROPE_OK) return st;
@@ -1204,6 +1312,16 @@ rope_status_t rope_partial_launch_info_pos(const void* x, const int64_t x_shape[
         info[2] = 256;
     }
     return ROPE_OK;
+}
+
+rope_status_t rope_proj_fwd(void* y, rope_dtype_t y_dtype, const void* x, const void* w, rope_dtype_t dtype,
+                            const int64_t y_shape[4], int64_t K,
+                            const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                            const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                            rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2], void* stream)
+{
+    return rope::run_proj(y, y_dtype, x, w, dtype, y_shape, K, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides,
+                          table_dtype, mode, partial_slice, stream);
 }
 
 const char* rope_status_string(rope_status_t status)

@@ -310,4 +310,89 @@ rope_status_t make_plan_out_pos(void* y, const void* x, const int64_t x_shape[4]
     return ROPE_OK;
 }
 
+rope_status_t check_disjoint(const Plan plans[], int n, std::string* why)
+{
+    for (int i = 0; i < n; ++i) {
+        const uintptr_t ai = reinterpret_cast<uintptr_t>(plans[i].x);
+        for (int j = i + 1; j < n; ++j) {
+            const uintptr_t aj = reinterpret_cast<uintptr_t>(plans[j].x);
+            // [ai, ai+bi) and [aj, aj+bj) overlap iff either start lies inside the other
+            const bool overlap = (ai >= aj && (uint64_t)(ai - aj) < (uint64_t)plans[j].bytes) ||
+                                 (aj >= ai && (uint64_t)(aj - ai) < (uint64_t)plans[i].bytes);
+            if (overlap)
+                return fail(ROPE_ERR_INVALID, why, "tensors " + std::to_string(i) + " and " + std::to_string(j)
+                                                       + " overlap");
+        }
+    }
+    return ROPE_OK;
+}
+
+bool proj_head_dim_supported(int64_t Dh)
+{
+    return Dh == 32 || Dh == 64 || Dh == 96 || Dh == 128 || Dh == 192;
+}
+
+rope_status_t make_proj_plan(void* y, rope_dtype_t out_dtype, const void* x, const void* w, rope_dtype_t dtype,
+                             const int64_t y_shape[4], int64_t K,
+                             const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                             const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                             rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                             ProjPlan* plan, std::string* why)
+{
+    ProjPlan q;
+    int64_t numel = 0;
+    rope_status_t st = check_scalars(y_shape, out_dtype, table_dtype, mode, partial_slice, kFwd, &q.rope, &numel, why);
+    if (st != ROPE_OK) return st;
+    if (dtype != ROPE_DTYPE_BF16 && dtype != ROPE_DTYPE_F16)
+        return fail(ROPE_ERR_INVALID, why, "the projection takes bf16 or fp16 x and w");
+    if (out_dtype != dtype && out_dtype != ROPE_DTYPE_F32)
+        return fail(ROPE_ERR_INVALID, why, "y must have the type of x and w, or fp32");
+    if (K < 0) return fail(ROPE_ERR_INVALID, why, "K is negative");
+    q.K = K;
+    q.in_dtype = dtype;
+    q.out_dtype = out_dtype;
+    if (numel == 0) {
+        q.noop = true;
+        *plan = q;
+        return ROPE_OK;
+    }
+    const int64_t Dh = y_shape[3];
+    if (K == 0 || K % 64 != 0)
+        return fail(ROPE_ERR_UNSUPPORTED, why, "K must be a positive multiple of 64");
+    if (!proj_head_dim_supported(Dh))
+        return fail(ROPE_ERR_UNSUPPORTED, why, "head dimension must be 32, 64, 96, 128 or 192");
+    if (y == nullptr) return fail(ROPE_ERR_NULLPTR, why, "y is NULL");
+    if (x == nullptr) return fail(ROPE_ERR_NULLPTR, why, "x is NULL");
+    if (w == nullptr) return fail(ROPE_ERR_NULLPTR, why, "w is NULL");
+    const auto misaligned = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
+    if (misaligned(y) || misaligned(x) || misaligned(w))
+        return fail(ROPE_ERR_INVALID, why, "y, x and w must be 16-byte aligned");
+    const int64_t M = y_shape[0] * y_shape[1];   // no overflow: numel fits and the other factors are >= 1
+    const int64_t N = y_shape[2] * Dh;
+    int64_t x_bytes, w_bytes;
+    if (!mul_ok(M, K, &x_bytes) || !mul_ok(x_bytes, 2, &x_bytes) || !mul_ok(N, K, &w_bytes) ||
+        !mul_ok(w_bytes, 2, &w_bytes))
+        return fail(ROPE_ERR_INVALID, why, "x or w byte size overflows 64 bits");
+    // the kernel addresses x and w with 32-bit element offsets
+    if (M * K >= (int64_t(1) << 31) || N * K >= (int64_t(1) << 31))
+        return fail(ROPE_ERR_UNSUPPORTED, why, "x and w must each hold fewer than 2^31 elements");
+    const auto overlap = [](const void* a, uint64_t na, const void* b, uint64_t nb) {
+        const uintptr_t au = reinterpret_cast<uintptr_t>(a), bu = reinterpret_cast<uintptr_t>(b);
+        return (au >= bu && (uint64_t)(au - bu) < nb) || (bu >= au && (uint64_t)(bu - au) < na);
+    };
+    const uint64_t y_bytes = (uint64_t)q.rope.bytes;
+    if (overlap(y, y_bytes, x, (uint64_t)x_bytes) || overlap(y, y_bytes, w, (uint64_t)w_bytes))
+        return fail(ROPE_ERR_INVALID, why, "y overlaps x or w");
+    if (q.rope.L > 0) {
+        st = check_tables(y_shape, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides, &q.rope, why);
+        if (st != ROPE_OK) return st;
+    }
+    q.x = x;
+    q.w = w;
+    q.y = y;
+    q.rope.x = y;
+    *plan = q;
+    return ROPE_OK;
+}
+
 }  // namespace rope

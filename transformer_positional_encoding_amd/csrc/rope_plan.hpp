@@ -86,6 +86,45 @@ rope_status_t make_plan_out_pos(void* y, const void* x, const int64_t x_shape[4]
                                 rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
                                 Direction dir, Plan* plan, std::string* why);
 
+// The projection with a rotary epilogue (rope_proj_fwd): y (B,S,H,Dh) =
+// x (B*S, K) . w (H*Dh, K)^T, each head's slice rotated. `rope` holds y's
+// geometry as a plan of the table call (x_shape = y's shape, the output
+// type as its dtype, the slice, pair distance and tables).
+struct ProjPlan {
+    Plan rope;
+    int64_t K = 0;
+    int in_dtype = 0;          // rope_dtype_t of x and w (bf16 or fp16)
+    int out_dtype = 0;         // rope_dtype_t of y (the inputs' type or fp32)
+    const void* x = nullptr;
+    const void* w = nullptr;
+    void* y = nullptr;
+    bool noop = false;         // y has no elements
+};
+
+// The tensors of one multi-tensor call must not share a byte: one fused
+// launch rotates them all at once, so a shared byte would be read and
+// written by two threads (and two rotations of one tensor would differ from
+// two calls). ROPE_ERR_INVALID names the first overlapping pair.
+rope_status_t check_disjoint(const Plan plans[], int n, std::string* why);
+
+// Lanes per head the fused kernel takes (block tiles of whole heads).
+bool proj_head_dim_supported(int64_t Dh);
+
+// Checks, in order: the scalar arguments of make_plan on y's shape (with the
+// output type); input type bf16 or fp16; output type the inputs' type or
+// fp32; K >= 0; an empty y is a no-op; K a positive multiple of 64 and Dh
+// one the kernel tiles (ROPE_ERR_UNSUPPORTED); NULL y, x or w; 16-byte
+// alignment of y, x and w; sizes within 64-bit offsets; x or w of 2^31
+// elements or more (ROPE_ERR_UNSUPPORTED: 32-bit offsets in the kernel); y
+// overlapping x or w; then, for a non-empty slice, the tables as in
+// make_plan with y's shape.
+rope_status_t make_proj_plan(void* y, rope_dtype_t out_dtype, const void* x, const void* w, rope_dtype_t dtype,
+                             const int64_t y_shape[4], int64_t K,
+                             const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                             const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                             rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                             ProjPlan* plan, std::string* why);
+
 int element_size(int dtype);
 
 }  // namespace rope
