@@ -448,6 +448,62 @@ def bench_positions(name: str, reps: int, stream, out: bool = False) -> dict:
     return res
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA, AMD public spec
+
+
+def bench_proj(name: str, reps: int, stream) -> dict:
+    """The projection with a rotary epilogue (rope_proj_fwd) on a workload,
+    against the ways to get the same result in two steps: this library's
+    projection without the rotation (an empty slice) or torch's matmul
+    (hipBLASLt), each followed by the in-place rotation of the result. The
+    fused call also rotates the fp32 accumulator rather than a rounded
+    result (the two-step results may differ by a unit in the last place)."""
+    import torch
+
+    import transformer_positional_encoding_amd as rp
+    import workloads as W
+    pw = W.PROJ_WORKLOADS[name]
+    wr = W.WORKLOADS[pw.rope]
+    B, S, H, Dh = pw.y_shape
+    x, w = (t.to("cuda") for t in W.make_proj_inputs(pw))
+    r1, r2 = (t.to("cuda") for t in W.make_tables(wr))
+    z = torch.zeros((1, 1, 1, 0), dtype=x.dtype, device="cuda")
+    y = torch.empty((B, S, H, Dh), dtype=x.dtype, device="cuda")
+    y2 = y.view(B * S, H * Dh)
+    x2, wt = x.view(B * S, pw.K), w.t()
+    sl, mode = wr.partial_slice, wr.mode
+
+    def fused():
+        rp.rope_proj_fwd(x, w, r1, r2, H, mode, sl, out=y)
+
+    def plain():
+        rp.rope_proj_fwd(x, w, z, z, H, mode, None, out=y)
+
+    def plain_then_rope():
+        plain()
+        rp.rope_partial_fwd_inplace(y, r1, r2, mode, sl)
+
+    def torch_mm():
+        torch.matmul(x2, wt, out=y2)
+
+    def torch_then_rope():
+        torch_mm()
+        rp.rope_partial_fwd_inplace(y, r1, r2, mode, sl)
+
+    res = {"workload": name, "note": pw.note, "dtype": wr.dtype, "x_shape": [B, S, pw.K], "w_shape": [H * Dh, pw.K],
+           "y_shape": [B, S, H, Dh], "slice": list(sl), "mode": mode, "flops_per_call": pw.flops(), "calls": {}}
+    n = max(10, reps // 5)
+    for label, fn in (("fused", fused), ("projection_only", plain), ("projection_then_rope", plain_then_rope),
+                      ("torch_matmul_only", torch_mm), ("torch_matmul_then_rope", torch_then_rope)):
+        settle(lambda j: fn(), min_launches=10, min_seconds=0.05)
+        t = time_launches([(fn, ())], n, stream)
+        res["calls"][label] = {"us": round(t * 1e6, 2), "TFLOPs": round(pw.flops() / t / 1e12, 1),
+                               "mfma_frac": round(pw.flops() / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    del x, w, y
+    torch.cuda.empty_cache()
+    return res
+
+
 def profile_target(name: str, reps: int, out_of_place: bool = False, positions: bool = False) -> None:
     """Launches for rocprofv3 counter passes: each direction of the workload
     `reps` times (rotating copies as in the timed run; out of place, from x
@@ -699,7 +755,7 @@ def main() -> int:
     ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out,c4:pos,c2_s4096:pos,c4:outpos,"
                                       "c2_s4096:outpos,c2:posmulti,tp_qk:posmulti,c4_t32:pos,mqa_k:pos,c2_s4096,rh_64of128,"
                                       "rh_32of128,"
-                                      "c3_coeff4",
+                                      "c3_coeff4,c3_proj",
                     help="other workloads measured in the same run (reported under 'other_workloads'); "
                          "NAME:out measures the out-of-place entry points on NAME, NAME:pos the position "
                          "entry points, NAME:outpos the out-of-place position entry points, NAME:posmulti "
@@ -762,6 +818,9 @@ def main() -> int:
             continue
         if name.endswith(":posmulti"):
             others.append(bench_pos_multi(name[:-9], args.reps, stream))
+            continue
+        if name in W.PROJ_WORKLOADS:
+            others.append(bench_proj(name, args.reps, stream))
             continue
         if len(W.WORKLOADS[name].x_shapes) > 1:
             others.append(bench_multi(name, args.reps, stream))
@@ -828,6 +887,17 @@ def main() -> int:
                        **targets}
     line["settle"] = dict(main_res["settle"], note="untimed launches before the warm-up: after any idle "
                           "period the first ~80 launches run 5-40% slow while the memory clocks ramp")
+    # the projection with a rotary epilogue (a compact summary; the detail is
+    # on the other-workloads line)
+    for o in others:
+        if o.get("workload") in W.PROJ_WORKLOADS:
+            c = o["calls"]
+            line["fused_projection"] = {
+                "workload": o["workload"], "fused_us": c["fused"]["us"], "TFLOPs": c["fused"]["TFLOPs"],
+                "mfma_frac": c["fused"]["mfma_frac"], "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                "projection_then_rope_us": c["projection_then_rope"]["us"],
+                "torch_matmul_then_rope_us": c["torch_matmul_then_rope"]["us"],
+                "torch_matmul_only_us": c["torch_matmul_only"]["us"]}
     # the other workloads go on a line of their own, before the result line
     print("# other_workloads " + json.dumps(others), flush=True)
     print(json.dumps(line), flush=True)

@@ -252,3 +252,17 @@ def test_projection_errors():
         rp.rope_proj_fwd(x, w, r[..., :32], r[..., :32], 1, "interleave", (0, 64))
     empty = rp.rope_proj_fwd(x[:, :0], w, r, r, 1, "interleave", (0, 64))   # no tokens: a no-op
     assert empty.shape == (1, 0, 1, 128)
+
+
+def test_projection_at_the_bench_shape():
+    """The bench's workload: the MLA Q projection (K 1536 -> 128 heads x 192)
+    over 4 x 4096 tokens with c3's rotation ([0,64), interleave, tables
+    (1,4096,1,64)), every output lane against the oracle."""
+    pw = W.PROJ_WORKLOADS["c3_proj"]
+    wr = W.WORKLOADS[pw.rope]
+    x, w = W.make_proj_inputs(pw)
+    r1, r2 = W.make_tables(wr)
+    B, S, H, Dh = pw.y_shape
+    info = check_proj(x, w, r1, r2, H, wr.mode, wr.partial_slice, "bf16", "c3_proj")
+    announce(f"  exact {info['exact_fraction']:.4f}, max err/bound {info['max_err_over_bound']:.3g}")
+    assert info["n"] == B * S * H * Dh and info["exact_fraction"] > 0.9

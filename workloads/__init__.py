@@ -145,6 +145,46 @@ WORKLOADS["rh_32of128"] = W("rh_32of128", ((16, 4096, 40, 128),), "bf16", (0, 32
                             note="rotate_half on lanes [0,32) of 128, 40 heads, bf16")
 
 
+@dataclass(frozen=True)
+class ProjWorkload:
+    """A head projection whose result is rotated (the Q projection and RoPE
+    stages of "ascend-transformer-boost 的 MlaPreprocessOperation：MLA 预处理
+    四阶段融合算子深度解析", section 3): x (B*S, K) ~ N(0, 1) (the normalised
+    latent the page's projection takes), w (H*Dh, K) ~ N(0, 1/K) (so each
+    output lane is ~N(0, 1)), both rounded to `dtype`; the slice, mode and
+    tables of the rotation workload `rope` (whose x shape is (B, S, H, Dh))."""
+    name: str
+    rope: str
+    K: int
+    seed: int
+    note: str = field(default="", compare=False)
+
+    @property
+    def y_shape(self):
+        return WORKLOADS[self.rope].x_shapes[0]
+
+    def flops(self) -> int:
+        B, S, H, Dh = self.y_shape
+        return 2 * B * S * H * Dh * self.K
+
+
+PROJ_WORKLOADS: dict[str, ProjWorkload] = {
+    "c3_proj": ProjWorkload("c3_proj", "c3", 1536, 18,
+                            note="MLA Q projection, K 1536 -> 128 heads x 192, over c3's 4 x 4096 tokens, "
+                                 "rope lanes [0,64) interleave"),
+}
+
+
+def make_proj_inputs(p: ProjWorkload) -> tuple[torch.Tensor, torch.Tensor]:
+    """x (B, S, K) and w (H*Dh, K) CPU tensors in the rotation workload's dtype."""
+    w0 = WORKLOADS[p.rope]
+    B, S, H, Dh = p.y_shape
+    g = generator(p.seed)
+    x = torch.randn((B, S, p.K), generator=g).to(TORCH_DTYPES[w0.dtype])
+    w = (torch.randn((H * Dh, p.K), generator=g) * (1.0 / np.sqrt(p.K))).to(TORCH_DTYPES[w0.dtype])
+    return x, w
+
+
 def generator(seed: int) -> torch.Generator:
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
