@@ -11,7 +11,7 @@ import torch
 
 import transformer_positional_encoding_amd as rp
 import workloads as W
-from gpu_support import announce, oracle_rows
+from gpu_support import announce, check_tensor, oracle_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -82,12 +82,11 @@ def test_threads_on_their_own_streams():
                     if rep < 2:   # check the results of both directions once
                         for got, src in outs:
                             want = _want(src, r1, r2, mode, sl, direction)
-                            g_bits = W.to_numpy_storage(got.cpu())
                             if dtype == "f32":
-                                ok = np.allclose(g_bits, want, rtol=0, atol=1e-5)
-                            else:
-                                ok = g_bits.tobytes() == want.tobytes()
-                            if not ok:
+                                # the normwise 1e-6 bound (raises on a failure)
+                                check_tensor(got.cpu(), src, W.from_numpy_storage(want, dtype), r1, r2, mode, sl,
+                                             direction, f"concurrent job {k} rep {rep} {form}")
+                            elif W.to_numpy_storage(got.cpu()).tobytes() != want.tobytes():
                                 failures.append((k, rep, form))
         except Exception as e:   # reported below, with the job that raised it
             failures.append((k, repr(e)))

@@ -7,7 +7,7 @@ import torch
 
 import transformer_positional_encoding_amd as rp
 import workloads as W
-from gpu_support import announce, compare, expanded_tables, oracle_rows
+from gpu_support import announce, check_tensor, compare, expanded_tables, oracle_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -66,7 +66,7 @@ def test_four_tensors_match_single_calls(dtype, tdtype, mode, sl):
         assert _same(m, s)
         want = _oracle(x, r1, r2, mode, sl, "fwd")
         if dtype == "f32":
-            torch.testing.assert_close(m.cpu(), want, rtol=0, atol=1e-5)
+            check_tensor(m.cpu(), x, want, r1, r2, mode, sl, "fwd", f"multi {dtype}/{tdtype}")
         elif tdtype == "f32":
             D = x.shape[-1]
             rows = np.arange(x.numel() // D, dtype=np.int64)

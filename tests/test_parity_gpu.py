@@ -84,8 +84,8 @@ def test_c2_bf16_gqa_q_then_k():
 @pytest.mark.parametrize("direction", ["fwd", "bwd"])
 def test_c3_bf16_mla_full_size(direction):
     w, x, r1, r2 = _workload_inputs("c3")
-    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c3 {direction}",
-                         sample=6000, seed=3)
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c3 {direction}")
+    assert info["rows"] == 4 * 4096 * 128
     assert info["exact"] == info["n"]
 
 
@@ -93,8 +93,8 @@ def test_c3_bf16_mla_full_size(direction):
 @pytest.mark.parametrize("direction", ["bwd", "fwd"])
 def test_c4_long_context_full_size(name, direction):
     w, x, r1, r2 = _workload_inputs(name)
-    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"{name} {direction}",
-                         sample=6000, seed=4)
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"{name} {direction}")
+    assert info["rows"] == 16 * 8192 * 32
     if w.dtype != "f32":
         assert info["exact"] == info["n"]
 
@@ -105,8 +105,7 @@ def test_rotate_half_layouts_full_size(name, direction):
     """rotate_half from HBM: a whole head (pair-owner scheme) and two partial
     slices with 64- and 32-byte halves (own-vector scheme, lane exchange)."""
     w, x, r1, r2 = _workload_inputs(name)
-    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"{name} {direction}",
-                         sample=3000, seed=12)
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"{name} {direction}")
     assert info["exact"] == info["n"]
 
 
@@ -317,8 +316,8 @@ def test_c4_bf16_with_fp32_tables_full_size(direction):
     x = W.make_x(w)
     r1, r2 = W.make_tables(w)
     assert r1.dtype == torch.float32
-    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c4 fp32 tables {direction}",
-                         sample=4000, seed=41)
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c4 fp32 tables {direction}")
+    assert info["rows"] == 16 * 8192 * 32
     assert info["exact"] == info["n"]
 
 
@@ -333,8 +332,8 @@ def test_c4_fp32_with_16bit_tables_full_size(tdtype, direction):
     r1, r2 = W.make_tables(w)
     assert r1.dtype == W.TORCH_DTYPES[tdtype]
     assert rp.rope_partial_launch_info(x, r1, r2, w.mode, w.partial_slice)["kernel"] == "vector"
-    run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c4 fp32 {tdtype} tables {direction}",
-                  sample=3000, seed=43)
+    info = run_and_check(x, r1, r2, w.mode, w.partial_slice, direction, f"c4 fp32 {tdtype} tables {direction}")
+    assert info["rows"] == 16 * 8192 * 32
 
 
 # ---------------------------------------------------------------- the largest head dimension

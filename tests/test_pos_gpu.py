@@ -16,7 +16,7 @@ import torch
 import oracle
 import transformer_positional_encoding_amd as rp
 import workloads as W
-from gpu_support import announce, compare, expanded_tables
+from gpu_support import announce, compare, compare_all_rows, expanded_tables, oracle_all_rows
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -55,13 +55,20 @@ def run_pos_and_check(x, positions, inv_freq, mode, sl, direction, tdtype, what,
     torch.cuda.synchronize()
     B, S, N, D = x.shape
     total = B * S * N
-    rows = np.arange(total, dtype=np.int64) if sample is None else W.sample_rows(total, sample, seed)
-    got = W.to_numpy_storage(xd.reshape(total, D)[torch.from_numpy(rows).to(DEV)].cpu())
-    x_rows = np.ascontiguousarray(W.to_numpy_storage(x).reshape(total, D)[rows])
-    want = x_rows.copy()
-    oracle.rope_rows(want, x.shape, dtype, c, s, mode, sl, direction, rows=rows, table_dtype=tdtype)
-    info = compare(got, want, x_rows, expanded_tables(r1, x.shape, rows, L), expanded_tables(r2, x.shape, rows, L),
-                   dtype, mode, direction, sl, what)
+    if sample is None:
+        # every row; the oracle split over the host's cores
+        got = W.to_numpy_storage(xd.cpu()).reshape(total, D)
+        x_flat = W.to_numpy_storage(x).reshape(total, D)
+        want = oracle_all_rows(x_flat, tuple(x.shape), dtype, r1, r2, mode, sl, direction)
+        info = compare_all_rows(got, want, x_flat, r1, r2, tuple(x.shape), dtype, mode, direction, sl, what)
+    else:
+        rows = W.sample_rows(total, sample, seed)
+        got = W.to_numpy_storage(xd.reshape(total, D)[torch.from_numpy(rows).to(DEV)].cpu())
+        x_rows = np.ascontiguousarray(W.to_numpy_storage(x).reshape(total, D)[rows])
+        want = x_rows.copy()
+        oracle.rope_rows(want, x.shape, dtype, c, s, mode, sl, direction, rows=rows, table_dtype=tdtype)
+        info = compare(got, want, x_rows, expanded_tables(r1, x.shape, rows, L),
+                       expanded_tables(r2, x.shape, rows, L), dtype, mode, direction, sl, what)
     if dtype != "f32" and tdtype != "f32":
         assert info["exact"] == info["n"], f"{what}: {info['n'] - info['exact']} lanes differ from the oracle"
     return info, xd
@@ -123,13 +130,14 @@ def test_pos_strided_positions_and_unaligned_x():
 def test_pos_long_context_shard(direction, tdtype):
     """The long-context shard's x with its per-batch positions (offset + s)
     and base 5e5, bf16 or fp32 cos/sin computed in the kernel (the bench's
-    c4:pos and c4_t32:pos launches); sampled rows."""
+    c4:pos and c4_t32:pos launches); every row against the oracle."""
     w = W.WORKLOADS["c4"]
     x = W.make_x(w)
     pos = torch.from_numpy(W.positions(w))
     f = rp.rope_inv_freq(w.L, w.base)
-    run_pos_and_check(x, pos, f, w.mode, w.partial_slice, direction, tdtype, f"c4 positions {direction} {tdtype}",
-                      sample=4000, seed=5)
+    info, _ = run_pos_and_check(x, pos, f, w.mode, w.partial_slice, direction, tdtype,
+                                f"c4 positions {direction} {tdtype}")
+    assert info["rows"] == 16 * 8192 * 32
 
 
 def test_pos_multi_gqa_q_and_k_full_size():
