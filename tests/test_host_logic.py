@@ -62,3 +62,32 @@ def test_traffic_is_dropped_when_the_kernel_changes(tmp_path, monkeypatch):
     assert bench.committed_traffic("c4", "bwd")["hbm_bytes_per_launch"] == 5
     md.write_text('```json\n{"kernel_source_sha256_16": "0000", "launches": {"c4:bwd": {"hbm_bytes_per_launch": 5}}}\n```\n')
     assert bench.committed_traffic("c4", "bwd") is None
+
+
+def test_rope_inv_freq_follows_the_recipe():
+    """rope_inv_freq(L, base) gives the frequencies of "ANE实战RoPE位置编码在MIL中的
+    纯ANE实现", section 第一步 (θ = p / base^(2i/h), i < h/2), as doubles: each is
+    base^(-2i/L) evaluated with 50 significant digits (the decimal module)
+    and compared with the returned double: the two differ by less than one
+    unit in the last place (the double power is faithfully rounded; it need
+    not be the nearest double, 2^-0.5 is not), and the first is 1."""
+    import decimal
+    import math
+
+    import numpy as np
+
+    sys.path.insert(0, ROOT)
+    import transformer_positional_encoding_amd as rp
+    ctx = decimal.Context(prec=50)
+    for L in (2, 32, 64, 128, 1024):
+        for base in (10000.0, 500000.0, 2.0):
+            f = rp.rope_inv_freq(L, base).numpy()
+            assert f.dtype == np.float64 and f.shape == (L // 2,)
+            assert f[0] == 1.0
+            b = decimal.Decimal(base)
+            for i in range(L // 2):
+                exact = ctx.power(b, ctx.divide(decimal.Decimal(-2 * i), decimal.Decimal(L)))
+                ref = float(exact)
+                err = abs(decimal.Decimal(float(f[i])) - exact)
+                assert err < decimal.Decimal(math.ulp(ref)), (L, base, i, f[i], exact)
+            assert np.all(np.diff(f) < 0)
