@@ -939,12 +939,15 @@ rope_status_t run_out(void* y, const void* x, const int64_t x_shape[4], rope_dty
 
 // Projection with a rotary epilogue: one launch of rope_proj_kernel.
 template <int DT, int BN>
-hipError_t launch_proj(const ProjArgs& a, bool tvec, uint32_t grid, hipStream_t s)
+hipError_t launch_proj(const ProjArgs& a, int tdt, uint32_t grid, hipStream_t s)
 {
-    if (tvec)
-        hipLaunchKernelGGL((rope_proj_kernel<DT, BN, true>), dim3(grid), dim3(kProjThreads), 0, s, a);
+    const dim3 block(ProjTile<BN>::THREADS);
+    if (tdt == ROPE_DTYPE_BF16)
+        hipLaunchKernelGGL((rope_proj_kernel<DT, BN, ROPE_DTYPE_BF16>), dim3(grid), block, 0, s, a);
+    else if (tdt == ROPE_DTYPE_F16)
+        hipLaunchKernelGGL((rope_proj_kernel<DT, BN, ROPE_DTYPE_F16>), dim3(grid), block, 0, s, a);
     else
-        hipLaunchKernelGGL((rope_proj_kernel<DT, BN, false>), dim3(grid), dim3(kProjThreads), 0, s, a);
+        hipLaunchKernelGGL((rope_proj_kernel<DT, BN, ROPE_DTYPE_F32>), dim3(grid), block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -966,68 +969,57 @@ rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void*
     a.w = static_cast<const uint16_t*>(q.w);
     a.y = q.y;
     a.ydt = q.out_dtype;
-    a.tdt = p.tdtype;
     a.r1 = p.r1;
     a.r2 = p.r2;
     a.t1b = p.t1[0]; a.t1s = p.t1[1]; a.t1n = p.t1[2];
     a.t2b = p.t2[0]; a.t2s = p.t2[1]; a.t2n = p.t2[2];
-    a.M = p.B * p.S;
-    a.N = p.N * p.D;
-    a.K = q.K;
-    a.S = p.S;
+    // the plan bounds x and w below 2^31 elements, so M, N and K fit in 32 bits
+    a.M = (int32_t)(p.B * p.S);
+    a.N = (int32_t)(p.N * p.D);
+    a.K = (int32_t)q.K;
+    a.S = (int32_t)p.S;
     a.Dh = (int32_t)p.D;
     a.start = (int32_t)p.start;
     a.L = (int32_t)p.L;
     a.half = p.L > 0 ? (int32_t)p.half : 1;
-    // block tiles of whole heads: 192 lanes for heads of 96 or 192, else 128
+    // block tiles of whole heads: 192 lanes (384 tokens) for heads of 96 or
+    // 192 lanes, else 128 lanes (256 tokens)
     const int BN = p.D % 3 == 0 ? 192 : 128;
-    const int64_t MB = (a.M + kProjBM - 1) / kProjBM, NB = (a.N + BN - 1) / BN;
+    const int BM = BN == 192 ? ProjTile<192>::BM : ProjTile<128>::BM;
+    const int threads = BN == 192 ? ProjTile<192>::THREADS : ProjTile<128>::THREADS;
+    const int64_t MB = (a.M + BM - 1) / BM, NB = (a.N + BN - 1) / BN;
     // the dispatch packet holds the grid in work-items as a 32-bit number
-    if (MB * NB > (int64_t)(0xFFFFFFFFull / kProjThreads))
+    if (MB * NB > (int64_t)(0xFFFFFFFFull / threads))
         return set_error(ROPE_ERR_UNSUPPORTED, "the projection's grid exceeds one launch");
     a.MB = (int32_t)MB;
     a.NB = (int32_t)NB;
     // Measured on MI355X on the (4*4096 tokens, 1536) x (24576, 1536) MLA
-    // projection: groups of 2 M-tiles with each XCD taking a contiguous run
-    // of tiles were the fastest of 1, 2, 4, 8, 16 (by up to 8%).
-    a.group_m = 2;
+    // projection: groups of 4 M-tiles with each XCD taking a contiguous run
+    // of tiles.
+    a.group_m = 4;
     a.xcd_chunk = (int32_t)(MB * NB / 8);
     a.s_div = make_fastdiv((uint32_t)p.S);
     a.dh_div = make_fastdiv((uint32_t)p.D);
-    a.l_div = make_fastdiv((uint32_t)std::max<int64_t>(p.L, 1));
-    // tables that differ by head are staged per head of the tile
-    a.t1h = p.t1[2] != 0 ? (int32_t)(BN / p.D) : 1;
-    a.t2h = p.t2[2] != 0 ? (int32_t)(BN / p.D) : 1;
-    // the epilogue stages table rows in 16-byte chunks when every row of both
-    // tables starts 16-byte aligned and L fills whole chunks
-    bool tvec = false;
+    // The vector epilogue: whole 8-lane slice vectors whose partners are in
+    // the vector or a whole vector away, and 16-byte aligned runs of 8 cos
+    // and 8 sin values in every table row.
     {
-        const int64_t per = 16 / p.tesize;
-        bool v = p.L > 0 && p.L % per == 0 && aligned16(p.r1) && aligned16(p.r2);
-        for (int k = 0; k < 3 && v; ++k) v = p.t1[k] % per == 0 && p.t2[k] % per == 0;
-        tvec = v;
-        a.lc_div = make_fastdiv((uint32_t)std::max<int64_t>(p.L / per, 1));
-    }
-    // the 8-lane vectors of a head that meet the slice
-    {
-        const int64_t vph = p.D / 8;
-        a.rv_lo = p.L > 0 ? (int32_t)(p.start / 8) : 0;
-        a.nrv = p.L > 0 ? (int32_t)((p.start + p.L + 7) / 8 - p.start / 8) : 0;
-        const int64_t heads_t = BN / p.D;
-        a.rot_row_div = make_fastdiv((uint32_t)std::max<int64_t>(heads_t * a.nrv, 1));
-        a.rot_head_div = make_fastdiv((uint32_t)std::max<int32_t>(a.nrv, 1));
-        a.cp_row_div = make_fastdiv((uint32_t)std::max<int64_t>(heads_t * (vph - a.nrv), 1));
-        a.cp_head_div = make_fastdiv((uint32_t)std::max<int64_t>(vph - a.nrv, 1));
+        const int64_t per = 16 / p.tesize;                 // table lanes per 16 bytes
+        bool f = p.L > 0 && p.start % 8 == 0 && p.L % 8 == 0 && (p.half == 1 || p.half % 8 == 0);
+        f = f && aligned16(p.r1) && aligned16(p.r2);
+        for (int k = 0; k < 3 && f; ++k) f = p.t1[k] % per == 0 && p.t2[k] % per == 0;
+        a.fast = f ? 1 : 0;
     }
     const uint32_t grid = (uint32_t)(MB * NB);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
+    const int tdt = p.L > 0 ? p.tdtype : (int)ROPE_DTYPE_BF16;
     if (q.in_dtype == ROPE_DTYPE_BF16)
-        err = BN == 192 ? launch_proj<ROPE_DTYPE_BF16, 192>(a, tvec, grid, s)
-                        : launch_proj<ROPE_DTYPE_BF16, 128>(a, tvec, grid, s);
+        err = BN == 192 ? launch_proj<ROPE_DTYPE_BF16, 192>(a, tdt, grid, s)
+                        : launch_proj<ROPE_DTYPE_BF16, 128>(a, tdt, grid, s);
     else
-        err = BN == 192 ? launch_proj<ROPE_DTYPE_F16, 192>(a, tvec, grid, s)
-                        : launch_proj<ROPE_DTYPE_F16, 128>(a, tvec, grid, s);
+        err = BN == 192 ? launch_proj<ROPE_DTYPE_F16, 192>(a, tdt, grid, s)
+                        : launch_proj<ROPE_DTYPE_F16, 128>(a, tdt, grid, s);
     if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
     return ROPE_OK;
 }

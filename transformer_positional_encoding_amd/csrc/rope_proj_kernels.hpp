@@ -18,29 +18,35 @@
 // the MFMA fragments take: a lane of v_mfma_f32_32x32x16 holds 8 consecutive
 // k of one row of A (x) and 8 consecutive k of one column of B (a row of w).
 //
-// Tiling (gfx950, 256 CUs, 160 KiB LDS per CU): a block of 4 waves computes a
-// 256 x BN tile of y (BN = 128 or 192, a whole number of heads); wave (wm,
-// wn) holds a 128 x BN/2 sub-tile as 4 x BN/64 accumulators of 32 x 32 fp32.
-// The K loop runs over stages of 32 k: 256 x 32 of x and BN x 32 of w, 64
-// bytes per row, in a ring of 4 LDS stages filled by the gfx950 direct
-// global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes go to
-// the wave's LDS base + 16 * lane, no registers in between). A stage is
-// loaded three stages ahead of its MFMAs. Within each 64-byte row the four
-// 16-byte k-vectors are stored XOR-swizzled by bits 1-2 of the row, so the
-// MFMA fragment reads (16 bytes of 8 consecutive rows at one k) fall in
-// distinct LDS banks. The loads are issued from inline assembly and waited
-// for with explicit vmcnt counts: the compiler, which does not see them,
-// would otherwise wait for every outstanding load before each LDS read.
+// Tiling (gfx950: 256 CUs, 160 KiB LDS and 512 VGPRs per SIMD lane): a block
+// computes a BM x BN tile of y (BN = 192 or 128 output lanes, a whole number
+// of heads; BM = 384 or 256 tokens) with BM/64 x 2 waves, each holding a
+// 64 x BN/2 sub-tile as 2 x BN/64 accumulators of 32 x 32 fp32 (96 or 64
+// registers), so that 3 (or 2) waves share each SIMD and one wave's LDS
+// reads overlap another's MFMAs. The K loop runs over stages of 64 k: each
+// row of x and w contributes one whole 128-byte line per stage (a stage of
+// 32 k would fetch every line twice). Two stages of (BM + BN) x 128 bytes
+// form the LDS ring, filled by the gfx950 direct global-to-LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes go to the wave's LDS base +
+// 16 * lane, no registers in between) one stage ahead of the MFMAs. Within a
+// 128-byte row the eight 16-byte k-vectors are stored XOR-swizzled by a
+// function of the row modulo 32, chosen so that the 8, 16 or 32 lanes that
+// one LDS cycle serves read distinct banks (the fragment reads take 16 bytes
+// of 32 consecutive rows at one k). The loads are issued from inline
+// assembly and waited for with explicit vmcnt counts: the compiler, which
+// does not see them, would otherwise wait for every outstanding load before
+// each LDS read.
 //
-// Epilogue: the accumulators go to LDS in two halves of 128 rows (the ring
-// is free by then), and each thread then takes 8 consecutive output lanes
-// of a row (consecutive threads, consecutive lanes: the stores coalesce):
-// lanes outside the slice are stored as they are; a slice lane j is rotated
-// with its partner p(j) and the cos/sin of its token and head,
+// Epilogue, in two halves of BM/2 rows (the ring is free by then): every
+// wave writes its accumulators for the half to LDS as fp32, then 8
+// consecutive threads take the 8-lane vectors of one row (one 128-byte line
+// of 16-bit output per 8 threads): lanes outside the slice are stored as
+// they are; a slice lane j is rotated with its partner p(j) and the cos/sin
+// of its token and head,
 //   y_j = p_j c_j + sigma(j) p_p(j) s_j    (fp32, as the table call's fp32 rule),
-// then rounded once to the output type. The next vector's table values are
-// loaded (16 bytes at a time where aligned) while the current one is
-// computed.
+// then rounded once to the output type. Each thread's cos and sin values
+// for the half are loaded from the tables into registers before the half's
+// accumulators are written to LDS, so their latency overlaps that write.
 #pragma once
 
 #include <type_traits>
@@ -54,20 +60,42 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kProjBM = 256;      // tokens per block tile
-constexpr int kProjBK = 32;       // k per LDS stage (64-byte rows)
-constexpr int kProjStages = 4;    // LDS ring depth
-constexpr int kProjThreads = 256;
+constexpr int kProjBK = 64;       // k per LDS stage: one 128-byte line of each row
+constexpr int kProjStages = 2;    // LDS ring depth
 
-__host__ __device__ constexpr int proj_stage_bytes(int BN) { return (kProjBM + BN) * kProjBK * 2; }
-// epilogue: 64 rows of fp32 results, then cos and sin for those rows as fp32
-// (at most 64 rows x BN lanes each: one table row per token and head)
-__host__ __device__ constexpr int proj_epi_bytes(int BN) { return 64 * (BN + 4) * 4 + 2 * 64 * BN * 4; }
-__host__ __device__ constexpr int proj_lds_bytes(int BN)
-{
-    return kProjStages * proj_stage_bytes(BN) > proj_epi_bytes(BN) ? kProjStages * proj_stage_bytes(BN)
-                                                                    : proj_epi_bytes(BN);
-}
+// The block tile for BN output lanes: BM tokens, (BM/64) x 2 waves of
+// 64 x BN/2 each.
+template <int BN>
+struct ProjTile {
+    static_assert(BN == 128 || BN == 192, "block tile width");
+    static constexpr int BM = BN == 192 ? 384 : 256;
+    static constexpr int WM = BM / 64;            // wave rows
+    static constexpr int NW = 2 * WM;             // waves
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int MT = 2;                  // 32-row accumulator tiles per wave
+    static constexpr int NT = BN / 64;            // 32-column accumulator tiles per wave
+    static constexpr int STAGE = (BM + BN) * kProjBK * 2;
+    static constexpr int NLOAD = (BM + BN) / 8;   // 1 KiB wave loads (8 rows x 128 bytes) per stage
+    static constexpr int LW = NLOAD / NW;         // per wave
+    static_assert(NLOAD % NW == 0, "every wave issues the same number of loads");
+    static_assert(BM % 8 == 0, "no wave load straddles x and w");
+    static constexpr int LDC = BN + 4;            // epilogue row pitch in floats
+    static constexpr int RH = BM / 2;             // rows per epilogue half
+    static constexpr int EPI = RH * LDC * 4;
+    static constexpr int LDS = kProjStages * STAGE > EPI ? kProjStages * STAGE : EPI;
+    static_assert(LDS <= 160 * 1024, "LDS per block");
+    static constexpr int RPP = THREADS / 8;       // rows per epilogue pass: 8 threads per row
+    static constexpr int PR = RH / RPP;           // passes per half
+    static_assert(RH % RPP == 0, "whole passes");
+    static constexpr int VI = BN / 64;            // vectors per thread and row: 8 threads x 8 lanes per step
+};
+
+// The k-vector slot of row r: bits 0-2 of the result are r0^r3, r1^r4 and
+// r2. For rows r..r+31 read at one k (one fragment), the lanes that one LDS
+// cycle serves (8 rows of 128 bytes over 32 banks, 16 over 64 banks or 32
+// over 128 banks) then meet distinct 16-byte bank groups; the value depends
+// only on r mod 32, so every 32-row fragment uses the same slots.
+__device__ __forceinline__ int proj_swz(int r) { return ((r ^ (r >> 3)) & 3) | (r & 4); }
 
 // One direct global-to-LDS load of 16 bytes per lane: lane l's bytes go to
 // LDS byte address lds_base + 16*l (lds_base is the same for the whole wave).
@@ -90,31 +118,23 @@ struct ProjArgs {
     const uint16_t* w;     // (N, K) 16-bit
     void* y;               // (M, N), output type ydt
     int32_t ydt;           // rope_dtype_t of y: the inputs' type or fp32
-    int32_t tdt;           // rope_dtype_t of r1 and r2
     const void* r1;        // cos, table type; element (b,s,h,j) at b*t1b + s*t1s + h*t1n + j
     const void* r2;        // sin
     int64_t t1b, t1s, t1n, t2b, t2s, t2n;
-    int64_t M, N, K;
-    int64_t S;             // tokens m = b*S + s
+    int32_t M, N, K;       // x and w hold fewer than 2^31 elements
+    int32_t S;             // tokens m = b*S + s
     int32_t Dh;            // lanes per head (BN is a multiple of Dh)
     int32_t start, L;      // the slice of each head, [start, start + L)
     int32_t half;          // pair distance: 1 (interleave), L/2 (rotate_half) or L/c
+    // every slice vector is whole (start and L multiples of 8), its partner
+    // is in the vector (interleave) or a whole vector away (half a multiple
+    // of 8), and its 8 cos and 8 sin values are 16-byte aligned in the tables
+    int32_t fast;
     int32_t MB, NB;        // block tiles along M and N
     int32_t group_m;       // raster: groups of group_m M-tiles walk all N-tiles
     int32_t xcd_chunk;     // blocks [0, 8*xcd_chunk) are dealt to the XCDs in contiguous chunks
     FastDiv s_div;         // division by S (tokens m < 2^31)
     FastDiv dh_div;        // division by Dh
-    FastDiv l_div;         // division by L (L > 0)
-    int32_t t1h, t2h;      // heads of the tile whose cos (sin) rows differ: BN/Dh, or 1 when broadcast over heads
-    FastDiv lc_div;        // division by the 16-byte chunks of a table row (16-byte staging)
-    // The 8-lane vectors of a head (Dh/8 of them) that meet the slice are
-    // [rv_lo, rv_lo + nrv); the epilogue stores the others in a first pass
-    // and rotates these in a second one.
-    int32_t rv_lo, nrv;
-    FastDiv rot_row_div;   // division by (BN/Dh) * nrv: rotated vectors per row of the tile
-    FastDiv rot_head_div;  // division by nrv
-    FastDiv cp_row_div;    // division by (BN/Dh) * (Dh/8 - nrv): other vectors per row
-    FastDiv cp_head_div;   // division by Dh/8 - nrv
 };
 
 template <int DT>
@@ -146,61 +166,79 @@ __device__ __forceinline__ void proj_tile(const ProjArgs& a, int32_t& mb, int32_
     nb = r / gsize;
 }
 
-// TV: the tables are staged in 16-byte chunks (every row aligned, L whole
-// chunks); otherwise element by element.
-template <int DT, int BN, bool TV>
-__global__ void __launch_bounds__(kProjThreads) rope_proj_kernel(ProjArgs a)
+// 8 table values as fp32 from an aligned 16-byte (16-bit table) or 32-byte
+// (fp32 table) run.
+template <int TT>
+struct ProjTab8 {
+    static constexpr int kVecs = TT == ROPE_DTYPE_F32 ? 2 : 1;
+    v4u q[kVecs];
+    __device__ void load(const void* tab, int64_t i)
+    {
+        const v4u* p = reinterpret_cast<const v4u*>(static_cast<const char*>(tab) + i * (TT == ROPE_DTYPE_F32 ? 4 : 2));
+#pragma unroll
+        for (int k = 0; k < kVecs; ++k) q[k] = p[k];
+    }
+    __device__ void widen(float (&f)[8]) const
+    {
+        if constexpr (TT == ROPE_DTYPE_F32) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                f[k] = __uint_as_float(q[0][k]);
+                f[4 + k] = __uint_as_float(q[1][k]);
+            }
+        } else {
+            Lanes<TT> T;
+            T.unpack(q[0]);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) f[k] = T.v[k];
+        }
+    }
+};
+
+template <int DT, int BN, int TT>
+__global__ void __launch_bounds__(ProjTile<BN>::THREADS)
+    __attribute__((amdgpu_waves_per_eu(ProjTile<BN>::NW / 4, ProjTile<BN>::NW / 4))) rope_proj_kernel(ProjArgs a)
 {
-    static_assert(BN == 128 || BN == 192, "block tile width");
-    constexpr int NT = BN / 64;                        // 32-wide accumulator tiles per wave along N
-    constexpr int MT = 4;                              // 32-high accumulator tiles per wave along M
-    constexpr int LDC = BN + 4;                        // epilogue row pitch in floats
-    static_assert(proj_epi_bytes(BN) <= proj_lds_bytes(BN), "epilogue staging fits the LDS");
-    static_assert(proj_lds_bytes(BN) <= 160 * 1024, "LDS per block");
-    __shared__ __attribute__((aligned(16))) uint16_t smem[proj_lds_bytes(BN) / 2];
+    using T_ = ProjTile<BN>;
+    constexpr int BM = T_::BM, MT = T_::MT, NT = T_::NT, LW = T_::LW, LDC = T_::LDC;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[T_::LDS / 2];
 
     int32_t mb, nb;
     proj_tile(a, mb, nb);
-    const int64_t m0 = (int64_t)mb * kProjBM;
-    const int64_t n0 = (int64_t)nb * BN;
+    const int32_t m0 = mb * BM;
+    const int32_t n0 = nb * BN;
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int wm = wave % T_::WM, wn = wave / T_::WM;
 
-    // A stage: rows 0..255 of x then rows 0..BN-1 of w, 64 bytes each; one
-    // wave load instruction fills 16 consecutive rows (1 KiB). Wave `wave`
-    // fills x rows [64*wave, +64) (4 loads) and w rows [BN/4*wave, +BN/4).
-    // Lane l of a load writes row 16*i + l/4 at 16-byte slot l%4, which
-    // holds k-vector (l%4) ^ ((row/2) % 4) of the stage. Rows past M or N
-    // re-read the last row (always in bounds); their results are never
-    // stored. Element offsets are 32-bit (x and w hold fewer than 2^31
+    // ---------------------------------------------------------------- main loop
+    // A stage: rows 0..BM-1 of x then rows 0..BN-1 of w, 128 bytes each. Wave
+    // load li (of NLOAD) fills stage rows 8*li .. 8*li+7; wave `wave` issues
+    // loads [LW*wave, LW*wave + LW). Lane l of a load writes row 8*li + l/8
+    // at 16-byte slot l%8, which holds k-vector (l%8) ^ proj_swz(row). Rows
+    // past M or N re-read the last row (always in bounds); their results are
+    // never stored. Element offsets are 32-bit (x and w hold fewer than 2^31
     // elements).
-    constexpr int A_LOADS = kProjBM / 16 / 4;          // 4 per wave
-    constexpr int B_LOADS = BN / 16 / 4;               // 2 or 3 per wave
-    constexpr int LOADS = A_LOADS + B_LOADS;           // per wave per stage
-    uint32_t goff[LOADS];
+    uint32_t goff[LW];
+    bool from_x[LW];
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const bool isA = i < A_LOADS;
-        const int row = isA ? (wave * A_LOADS + i) * 16 + (lane >> 2)
-                            : (wave * B_LOADS + (i - A_LOADS)) * 16 + (lane >> 2);
-        const int kv = (lane & 3) ^ ((row >> 1) & 3);
-        const int64_t g = isA ? min(m0 + row, a.M - 1) : min(n0 + row, a.N - 1);
-        goff[i] = (uint32_t)(g * a.K + kv * 8);
+    for (int i = 0; i < LW; ++i) {
+        const int li = wave * LW + i;
+        const int srow = li * 8 + (lane >> 3);
+        from_x[i] = li * 8 < BM;
+        const int row = from_x[i] ? srow : srow - BM;
+        const int kv = (lane & 7) ^ proj_swz(row & 31);
+        const int32_t g = from_x[i] ? min(m0 + row, a.M - 1) : min(n0 + row, a.N - 1);
+        goff[i] = (uint32_t)g * (uint32_t)a.K + (uint32_t)(kv * 8);
     }
     const uint32_t smem_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
-    // LDS byte address of load i of this wave in stage slot 0
-    const uint32_t wave_a = __builtin_amdgcn_readfirstlane(smem_lds + wave * A_LOADS * 1024);
-    const uint32_t wave_b = __builtin_amdgcn_readfirstlane(smem_lds + kProjBM * 64 + wave * B_LOADS * 1024);
-    auto issue_stage = [&](int64_t k, int slot) {
+    const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(smem_lds + wave * LW * 1024);
+    auto issue_stage = [&](int32_t k, int slot) {
         const uint32_t koff = (uint32_t)(k * kProjBK);
-        const uint32_t sbase = (uint32_t)(slot * proj_stage_bytes(BN));
+        const uint32_t sbase = wave_lds + (uint32_t)(slot * T_::STAGE);
 #pragma unroll
-        for (int i = 0; i < A_LOADS; ++i) proj_dma16(a.x + (goff[i] + koff), wave_a + sbase + i * 1024);
-#pragma unroll
-        for (int i = 0; i < B_LOADS; ++i)
-            proj_dma16(a.w + (goff[A_LOADS + i] + koff), wave_b + sbase + i * 1024);
+        for (int i = 0; i < LW; ++i) proj_dma16((from_x[i] ? a.x : a.w) + (goff[i] + koff), sbase + i * 1024);
     };
 
     f32x16 acc[MT][NT];
@@ -209,25 +247,26 @@ __global__ void __launch_bounds__(kProjThreads) rope_proj_kernel(ProjArgs a)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = f32x16{};
 
-    // fragment reads: A row r = wm*128 + mt*32 + lane%32 (B row similarly),
-    // k-vector kv = 2*kk + lane/32 at slot kv ^ ((r/2) % 4); lane%32 runs
-    // over 32 consecutive rows, so (r/2) % 4 = ((lane%32)/2) % 4
+    // fragment reads: A row r = wm*64 + mt*32 + lane%32 (B row similarly),
+    // k-vector kv = 2*kk + lane/32 at slot kv ^ proj_swz(lane%32)
     const int fr = lane & 31;
-    const int sw = (fr >> 1) & 3;
-    const int a_row = (wm * 128 + fr) * 32;            // in 16-bit elements
-    const int b_row = kProjBM * 32 + (wn * (BN / 2) + fr) * 32;
+    const int sw = proj_swz(fr);
+    const int a_row = (wm * 64 + fr) * kProjBK;        // in 16-bit elements
+    const int b_row = BM * kProjBK + (wn * (BN / 2) + fr) * kProjBK;
     auto mma_stage = [&](int slot) {
-        const uint16_t* S0 = smem + slot * (proj_stage_bytes(BN) / 2);
+        const uint16_t* S0 = smem + slot * (T_::STAGE / 2);
+        // interleave the LDS reads with the MFMAs of the stage
+        __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
         for (int kk = 0; kk < kProjBK / 16; ++kk) {
             const int slot16 = ((2 * kk + (lane >> 5)) ^ sw) * 8;
             v4u fa[MT], fb[NT];
 #pragma unroll
             for (int i = 0; i < MT; ++i)
-                fa[i] = *reinterpret_cast<const v4u*>(S0 + a_row + i * 32 * 32 + slot16);
+                fa[i] = *reinterpret_cast<const v4u*>(S0 + a_row + i * 32 * kProjBK + slot16);
 #pragma unroll
             for (int j = 0; j < NT; ++j)
-                fb[j] = *reinterpret_cast<const v4u*>(S0 + b_row + j * 32 * 32 + slot16);
+                fb[j] = *reinterpret_cast<const v4u*>(S0 + b_row + j * 32 * kProjBK + slot16);
 #pragma unroll
             for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -235,279 +274,168 @@ __global__ void __launch_bounds__(kProjThreads) rope_proj_kernel(ProjArgs a)
         }
     };
 
-    // Stage k lives in slot k % 4. Three stages are in flight ahead of the
-    // one being computed; past the last stage the last one is loaded again
-    // (into a free slot) so that every step waits for the same count.
-    const int64_t KT = a.K / kProjBK;
-#pragma unroll
-    for (int k = 0; k < kProjStages - 1; ++k) issue_stage(min<int64_t>(k, KT - 1), k);
-    for (int64_t kt = 0; kt < KT; ++kt) {
-        proj_wait_vm<LOADS * (kProjStages - 2)>();     // this wave's loads of stage kt are in LDS
-        // everyone's are, and everyone has consumed stage kt-1 (whose slot
-        // is refilled next). A bare barrier: a fenced one would wait for
-        // every outstanding load, the three stages in flight included.
+    // Stage k lives in slot k % 2 and is loaded while stage k-1 is computed.
+    const int32_t KT = a.K / kProjBK;
+    issue_stage(0, 0);
+    for (int32_t kt = 0; kt < KT; ++kt) {
+        proj_wait_vm<0>();                             // this wave's loads of stage kt are in LDS
+        // everyone's are, and everyone has consumed stage kt-1, whose slot is
+        // refilled next. A bare barrier (no fence); the empty asm keeps the
+        // compiler from moving this stage's LDS reads above it.
         __builtin_amdgcn_s_barrier();
-        issue_stage(min<int64_t>(kt + kProjStages - 1, KT - 1), (int)((kt + kProjStages - 1) % kProjStages));
-        mma_stage((int)(kt % kProjStages));
+        asm volatile("" ::: "memory");
+        if (kt + 1 < KT) issue_stage(kt + 1, (int)((kt + 1) & 1));
+        mma_stage((int)(kt & 1));
     }
-    proj_wait_vm<0>();
-    __syncthreads();
+    __syncthreads();                                   // every wave is done with the ring
 
     // ---------------------------------------------------------------- epilogue
-    // Four quarters of 64 rows: accumulator row tile mt = qq of both wave
-    // rows. For each quarter the block first stages, as fp32 in LDS, the cos
-    // and sin values of its 64 tokens (and of each head of the tile when the
-    // tables differ by head): independent loads spread over all threads, so
-    // their latency is paid once per quarter. The accumulators follow into
-    // LDS; then step `it` gives 8-lane vector v = 256*it + t of the quarter's
-    // rows to thread t (consecutive threads, consecutive lanes of a row: the
-    // stores coalesce).
-    constexpr int RV = BN / 8;                         // 8-lane vectors per row of the tile
-    float* Cs = reinterpret_cast<float*>(smem);        // [64][LDC]
-    float* Tc = Cs + 64 * LDC;                         // [64][t1h][L]
-    float* Tsn = Tc + 64 * a.t1h * a.L;                // [64][t2h][L]
-    const int64_t N = a.N;
-    const int64_t h0 = n0 / a.Dh;                      // the tile's first head
-    auto token = [&](int qq, int lr) { return m0 + (lr >> 5) * 128 + qq * 32 + (lr & 31); };
-    // Stage the table rows of quarter qq: row r = lr * th + head of the tile,
-    // lanes [0, L). With 16-byte rows (TV), round `rd` gives thread t the
-    // 16-byte chunks rd*R*256 + u*256 + t (u < R) of the quarter's rows;
-    // otherwise single elements, R per round. A round's loads of both tables
-    // go out together and land in registers; committing writes them to LDS.
-    // Round 0 of the next quarter is loaded while this quarter's vectors are
-    // computed, so for tables up to R*256 chunks per quarter (64 tokens x 64
-    // lanes of 16-bit cos and sin, the MLA case) no load latency is exposed
-    // after the first quarter.
-    constexpr int es_chunk = 16;
-    constexpr int R = 4;
-    using TabVal = typename std::conditional<TV, v4u, float>::type;
-    struct TabRound {
-        TabVal c[R], s[R];
-    };
-    auto table_index = [&](int qq, int row, int th, int64_t tb, int64_t ts, int64_t tn) {
-        const int lr = th == 1 ? row : row / th, hl = row - lr * th;
-        const int64_t m = min(token(qq, lr), a.M - 1);
-        const int64_t b = fast_div((uint32_t)m, a.s_div), sp = m - b * a.S;
-        return b * tb + sp * ts + (h0 + hl) * tn;
-    };
-    const int tes = a.tdt == ROPE_DTYPE_F32 ? 4 : 2;
-    const int per = es_chunk / tes;                       // lanes per 16-byte chunk (TV)
-    // units (chunks or elements) per quarter of each table
-    const int units1 = TV ? 64 * a.t1h * a.L / per : 64 * a.t1h * a.L;
-    const int units2 = TV ? 64 * a.t2h * a.L / per : 64 * a.t2h * a.L;
-    auto load_unit = [&](const void* tab, int qq, int th, int64_t tb, int64_t ts, int64_t tn, int units, int u,
-                         TabVal& out) {
-        u = min(u, units - 1);
-        if constexpr (TV) {
-            const int row = (int)fast_div((uint32_t)u, a.lc_div);
-            const int lane0 = (u - row * (int)a.lc_div.d) * per;
-            const int64_t i = table_index(qq, row, th, tb, ts, tn) + lane0;
-            out = *reinterpret_cast<const v4u*>(static_cast<const char*>(tab) + i * tes);
-        } else {
-            const int row = (int)fast_div((uint32_t)u, a.l_div);
-            const int64_t i = table_index(qq, row, th, tb, ts, tn) + (u - row * a.L);
-            if (a.tdt == ROPE_DTYPE_BF16) out = Store<ROPE_DTYPE_BF16>::load1(tab, i);
-            else if (a.tdt == ROPE_DTYPE_F16) out = Store<ROPE_DTYPE_F16>::load1(tab, i);
-            else out = Store<ROPE_DTYPE_F32>::load1(tab, i);
-        }
-    };
-    auto store_unit = [&](float* dst, int units, int u, const TabVal& v) {
-        if (u >= units) return;
-        if constexpr (TV) {
-            float* d = dst + u * per;
-            if (a.tdt == ROPE_DTYPE_F32) {
-                *reinterpret_cast<v4u*>(d) = v;
-            } else {
-                float f[8];
-                if (a.tdt == ROPE_DTYPE_BF16) {
-                    Lanes<ROPE_DTYPE_BF16> T;
-                    T.unpack(v);
+    // Half h holds accumulator row tile mt = h of every wave: tile rows
+    // wm*64 + h*32 + [0, 32), local row lr = wm*32 + [0, 32). Thread t takes
+    // row lr = t/8 + p*RPP of the half (p < PR) and the 8-lane vectors
+    // v = t%8 + 8*i (i < VI) of that row: consecutive threads take
+    // consecutive vectors, so each 8 threads store one 128-byte line.
+    float* Cs = reinterpret_cast<float*>(smem);        // [RH][LDC]
+    const int tv = t & 7, tr = t >> 3;
+    const int32_t h0 = (int32_t)fast_div((uint32_t)n0, a.dh_div);   // the tile's first head
+    const int g2 = 2 * a.half;
+    // per vector i: lanes [c0, c0+8) of the tile, head hl, slice-relative first lane rel0
+    int c0[T_::VI], hl[T_::VI], rel0[T_::VI];
+    bool live_v[T_::VI], rot[T_::VI];
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) f[k] = T.v[k];
-                } else {
-                    Lanes<ROPE_DTYPE_F16> T;
-                    T.unpack(v);
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) f[k] = T.v[k];
-                }
-                reinterpret_cast<float4*>(d)[0] = float4{f[0], f[1], f[2], f[3]};
-                reinterpret_cast<float4*>(d)[1] = float4{f[4], f[5], f[6], f[7]};
-            }
-        } else {
-            dst[u] = v;
-        }
-    };
-    auto load_round = [&](int qq, int rd, TabRound& r) {
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const int u = (rd * R + k) * kProjThreads + t;
-            load_unit(a.r1, qq, a.t1h, a.t1b, a.t1s, a.t1n, units1, u, r.c[k]);
-            load_unit(a.r2, qq, a.t2h, a.t2b, a.t2s, a.t2n, units2, u, r.s[k]);
-        }
-    };
-    auto store_round = [&](int rd, const TabRound& r) {
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const int u = (rd * R + k) * kProjThreads + t;
-            store_unit(Tc, units1, u, r.c[k]);
-            store_unit(Tsn, units2, u, r.s[k]);
-        }
-    };
-    const int rounds = (max(units1, units2) + R * kProjThreads - 1) / (R * kProjThreads);
-    TabRound pre;                                          // round 0 of the next quarter
-    if (a.L > 0) load_round(0, 0, pre);
-    // The quarters run in a loop that is not unrolled (one copy of the
-    // staging and vector code); only the write of the quarter's accumulators,
-    // which must index them by constants to keep them in registers, is
-    // replicated, behind a switch.
+    for (int i = 0; i < T_::VI; ++i) {
+        c0[i] = 8 * (tv + 8 * i);
+        hl[i] = (int)fast_div((uint32_t)c0[i], a.dh_div);
+        rel0[i] = c0[i] - hl[i] * a.Dh - a.start;
+        live_v[i] = n0 + c0[i] < a.N;
+        // rotated: meets the slice, in a head that exists (the last tile
+        // along N may reach past N; its table rows must not be read)
+        rot[i] = live_v[i] && a.L > 0 && rel0[i] < a.L && rel0[i] + 8 > 0;
+    }
     auto write_acc = [&](const f32x16 (&accq)[NT]) {
-        // accumulator (qq, nt), register r holds row 8*(r/4) + 4*(lane/32) + r%4
+        // accumulator (h, nt), register r holds row 8*(r/4) + 4*(lane/32) + r%4
         // and column lane%32 of its 32 x 32 tile
 #pragma unroll
         for (int j = 0; j < NT; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                const int lr = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 const int col = wn * (BN / 2) + j * 32 + (lane & 31);
-                Cs[row * LDC + col] = accq[j][r];
+                Cs[lr * LDC + col] = accq[j][r];
             }
     };
-    static_assert(MT == 4, "four quarters");
-#pragma unroll 1
-    for (int qq = 0; qq < MT; ++qq) {
-        if (a.L > 0) {
-            store_round(0, pre);
-            for (int rd = 1; rd < rounds; ++rd) {
-                TabRound r;
-                load_round(qq, rd, r);
-                store_round(rd, r);
+    // Table values prefetched for the first vector of each pass (lanes
+    // [0, 64) of the tile: a 64-lane slice at the start of each head, as the
+    // MLA rope dimension, is all prefetched); other vectors read theirs when
+    // they come (more would not fit the registers of 3 waves per SIMD).
+    constexpr int VP = 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int64_t m[T_::PR], o1[T_::PR], o2[T_::PR];
+        ProjTab8<TT> pc[T_::PR][VP], ps[T_::PR][VP];
+#pragma unroll
+        for (int p = 0; p < T_::PR; ++p) {
+            const int lr = tr + p * T_::RPP;
+            m[p] = m0 + (lr >> 5) * 64 + h * 32 + (lr & 31);
+            const int32_t mc = (int32_t)min<int64_t>(m[p], a.M - 1);
+            const int32_t b = (int32_t)fast_div((uint32_t)mc, a.s_div), sp = mc - b * a.S;
+            o1[p] = b * a.t1b + sp * a.t1s + (int64_t)h0 * a.t1n;
+            o2[p] = b * a.t2b + sp * a.t2s + (int64_t)h0 * a.t2n;
+            if (a.fast) {
+#pragma unroll
+                for (int i = 0; i < VP; ++i)
+                    if (rot[i]) {
+                        pc[p][i].load(a.r1, o1[p] + hl[i] * a.t1n + rel0[i]);
+                        ps[p][i].load(a.r2, o2[p] + hl[i] * a.t2n + rel0[i]);
+                    }
             }
         }
-        switch (qq) {
-        case 0: write_acc(acc[0]); break;
-        case 1: write_acc(acc[1]); break;
-        case 2: write_acc(acc[2]); break;
-        default: write_acc(acc[3]); break;
-        }
+        if (h == 0) write_acc(acc[0]);
+        else write_acc(acc[1]);
         __syncthreads();
-        if (a.L > 0 && qq + 1 < MT) load_round(qq + 1, 0, pre);
-        // One vector: row lr of the quarter, 8 lanes from column c0 of the
-        // tile; rotated when `rot` (then it meets the slice).
-        auto vector = [&](int lr, int c0, bool rot) {
-            const int64_t m = token(qq, lr);
-            const int64_t n = n0 + c0;
-            if (m >= a.M || n >= N) return;
-            const float* crow = Cs + lr * LDC;
-            float val[8];
-            {
-                const float4 q0 = *reinterpret_cast<const float4*>(crow + c0);
-                const float4 q1 = *reinterpret_cast<const float4*>(crow + c0 + 4);
-                val[0] = q0.x; val[1] = q0.y; val[2] = q0.z; val[3] = q0.w;
-                val[4] = q1.x; val[5] = q1.y; val[6] = q1.z; val[7] = q1.w;
-            }
-            if (rot) {
-                const int hl = (int)fast_div((uint32_t)c0, a.dh_div);
-                const int j0 = c0 - hl * a.Dh;
-                const int rel0 = j0 - a.start;
-                const float* crow_t = Tc + (lr * a.t1h + (a.t1h > 1 ? hl : 0)) * a.L;
-                const float* srow_t = Tsn + (lr * a.t2h + (a.t2h > 1 ? hl : 0)) * a.L;
-                const int g2 = 2 * a.half;
-                // partners and pair roles: in the vector itself for interleave
-                // with an even start (pairs never straddle a vector), a vector
-                // `half` lanes away when the 8 lanes lie in one half-group
-                // (half and the slice-relative start multiples of 8), else
-                // lane by lane
-                float xp[8];
-                bool first[8];
-                if (a.half == 1 && (a.start & 1) == 0) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        xp[e] = val[e ^ 1];
-                        first[e] = (e & 1) == 0;
-                    }
-                } else if ((a.half & 7) == 0 && (rel0 & 7) == 0 && rel0 >= 0 && rel0 + 8 <= a.L) {
-                    const bool f = rel0 % g2 < a.half;
-                    const float* pp = crow + c0 + (f ? a.half : -a.half);
-                    const float4 p0 = *reinterpret_cast<const float4*>(pp);
-                    const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
-                    xp[0] = p0.x; xp[1] = p0.y; xp[2] = p0.z; xp[3] = p0.w;
-                    xp[4] = p1.x; xp[5] = p1.y; xp[6] = p1.z; xp[7] = p1.w;
+        for (int p = 0; p < T_::PR; ++p) {
+            if (m[p] >= a.M) continue;
+            const float* crow = Cs + (tr + p * T_::RPP) * LDC;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) first[e] = f;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int rel = min(max(rel0 + e, 0), a.L - 1);
-                        first[e] = rel % g2 < a.half;
-                        xp[e] = crow[c0 + (rel - rel0) + (first[e] ? a.half : -a.half)];
-                    }
-                }
-                // the 8 lanes' cos and sin from LDS, all read before any is
-                // used (two 16-byte reads each when the lanes lie in the
-                // slice on a 4-lane boundary, else clamped single reads)
-                float cc[8], ss[8];
-                if (rel0 >= 0 && rel0 + 8 <= a.L && (rel0 & 3) == 0 && (a.L & 3) == 0) {
-                    const float4 c0v = *reinterpret_cast<const float4*>(crow_t + rel0);
-                    const float4 c1v = *reinterpret_cast<const float4*>(crow_t + rel0 + 4);
-                    const float4 s0v = *reinterpret_cast<const float4*>(srow_t + rel0);
-                    const float4 s1v = *reinterpret_cast<const float4*>(srow_t + rel0 + 4);
-                    cc[0] = c0v.x; cc[1] = c0v.y; cc[2] = c0v.z; cc[3] = c0v.w;
-                    cc[4] = c1v.x; cc[5] = c1v.y; cc[6] = c1v.z; cc[7] = c1v.w;
-                    ss[0] = s0v.x; ss[1] = s0v.y; ss[2] = s0v.z; ss[3] = s0v.w;
-                    ss[4] = s1v.x; ss[5] = s1v.y; ss[6] = s1v.z; ss[7] = s1v.w;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int rc = min(max(rel0 + e, 0), a.L - 1);
-                        cc[e] = crow_t[rc];
-                        ss[e] = srow_t[rc];
-                    }
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int rel = rel0 + e;
-                    const float yv = rotate_own<false>(val[e], xp[e], cc[e], ss[e], first[e]);
-                    val[e] = rel >= 0 && rel < a.L ? yv : val[e];
-                }
-            }
-            if (a.ydt == ROPE_DTYPE_F32) {
-                float4* yp = reinterpret_cast<float4*>(static_cast<float*>(a.y) + m * N + n);
-                yp[0] = float4{val[0], val[1], val[2], val[3]};
-                yp[1] = float4{val[4], val[5], val[6], val[7]};
-            } else {
-                Lanes<DT> Y;   // the output is the inputs' 16-bit type
-#pragma unroll
-                for (int e = 0; e < 8; ++e) Y.v[e] = val[e];
-                *reinterpret_cast<v4u*>(static_cast<uint16_t*>(a.y) + m * N + n) = Y.pack();
-            }
-        };
-        const int vph = a.Dh / 8;                      // vectors per head
-        const int heads_t = BN / a.Dh;                 // heads per tile
-        // pass 1: the vectors outside the slice (stored as they are)
-        {
-            const int ncp = vph - a.nrv;
-            const int total = 64 * heads_t * ncp;
+            for (int i = 0; i < T_::VI; ++i) {
+                if (!live_v[i]) continue;
+                const int64_t yo = m[p] * a.N + n0 + c0[i];
+                if (rot[i] && !a.fast) {
+                    // any other geometry: lane by lane from the row in LDS
+                    // (partners there too), cos and sin read one by one, one
+                    // store per lane
 #pragma unroll 1
-            for (int k = t; k < total; k += kProjThreads) {
-                const int lr = (int)fast_div((uint32_t)k, a.cp_row_div);
-                const int idx = k - lr * (int)a.cp_row_div.d;
-                const int hl = (int)fast_div((uint32_t)idx, a.cp_head_div);
-                const int jv = idx - hl * ncp;
-                vector(lr, (hl * vph + (jv < a.rv_lo ? jv : jv + a.nrv)) * 8, false);
+                    for (int e = 0; e < 8; ++e) {
+                        const int rel = rel0[i] + e;
+                        float ye = crow[c0[i] + e];
+                        if (rel >= 0 && rel < a.L) {
+                            const bool f = rel % g2 < a.half;
+                            const float xpe = crow[c0[i] + e + (f ? a.half : -a.half)];
+                            const float ce = Store<TT>::load1(a.r1, o1[p] + hl[i] * a.t1n + rel);
+                            const float se = Store<TT>::load1(a.r2, o2[p] + hl[i] * a.t2n + rel);
+                            ye = rotate_own<false>(ye, xpe, ce, se, f);
+                        }
+                        if (a.ydt == ROPE_DTYPE_F32) Store<ROPE_DTYPE_F32>::store1(a.y, yo + e, ye);
+                        else Store<DT>::store1(a.y, yo + e, ye);
+                    }
+                    continue;
+                }
+                float val[8];
+                {
+                    const float4 q0 = *reinterpret_cast<const float4*>(crow + c0[i]);
+                    const float4 q1 = *reinterpret_cast<const float4*>(crow + c0[i] + 4);
+                    val[0] = q0.x; val[1] = q0.y; val[2] = q0.z; val[3] = q0.w;
+                    val[4] = q1.x; val[5] = q1.y; val[6] = q1.z; val[7] = q1.w;
+                }
+                if (rot[i]) {
+                    // whole vector in the slice: partners in the vector
+                    // (interleave) or the vector `half` lanes away
+                    float cc[8], ss[8];
+                    if (i < VP) {
+                        pc[p][i < VP ? i : 0].widen(cc);
+                        ps[p][i < VP ? i : 0].widen(ss);
+                    } else {
+                        ProjTab8<TT> c1, s1;
+                        c1.load(a.r1, o1[p] + hl[i] * a.t1n + rel0[i]);
+                        s1.load(a.r2, o2[p] + hl[i] * a.t2n + rel0[i]);
+                        c1.widen(cc);
+                        s1.widen(ss);
+                    }
+                    float xp[8];
+                    bool first[8];
+                    if (a.half == 1) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            xp[e] = val[e ^ 1];
+                            first[e] = (e & 1) == 0;
+                        }
+                    } else {
+                        const bool f = rel0[i] % g2 < a.half;
+                        const float* pp = crow + c0[i] + (f ? a.half : -a.half);
+                        const float4 p0 = *reinterpret_cast<const float4*>(pp);
+                        const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
+                        xp[0] = p0.x; xp[1] = p0.y; xp[2] = p0.z; xp[3] = p0.w;
+                        xp[4] = p1.x; xp[5] = p1.y; xp[6] = p1.z; xp[7] = p1.w;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) first[e] = f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) val[e] = rotate_own<false>(val[e], xp[e], cc[e], ss[e], first[e]);
+                }
+                if (a.ydt == ROPE_DTYPE_F32) {
+                    float4* yp = reinterpret_cast<float4*>(static_cast<float*>(a.y) + yo);
+                    yp[0] = float4{val[0], val[1], val[2], val[3]};
+                    yp[1] = float4{val[4], val[5], val[6], val[7]};
+                } else {
+                    Lanes<DT> Y;   // the output is the inputs' 16-bit type
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) Y.v[e] = val[e];
+                    *reinterpret_cast<v4u*>(static_cast<uint16_t*>(a.y) + yo) = Y.pack();
+                }
             }
         }
-        // pass 2: the vectors that meet the slice, rotated (every lane busy)
-        if (a.nrv > 0) {
-            const int total = 64 * heads_t * a.nrv;
-#pragma unroll 1
-            for (int k = t; k < total; k += kProjThreads) {
-                const int lr = (int)fast_div((uint32_t)k, a.rot_row_div);
-                const int idx = k - lr * (int)a.rot_row_div.d;
-                const int hl = (int)fast_div((uint32_t)idx, a.rot_head_div);
-                vector(lr, (hl * vph + a.rv_lo + (idx - hl * a.nrv)) * 8, true);
-            }
-        }
-        __syncthreads();
+        __syncthreads();                               // the half's rows are read before the next is written
     }
 }
 
