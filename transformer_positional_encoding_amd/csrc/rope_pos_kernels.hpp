@@ -43,13 +43,102 @@ __device__ __forceinline__ float round_to_type(double v)
     }
 }
 
+// (cos θ, sin θ) rounded to TT, by the double evaluation. Not inlined: the
+// kernels reach it rarely (16-bit tables) and its registers would otherwise
+// count in theirs.
+template <int TT>
+__device__ __attribute__((noinline)) float2 pos_cos_sin_double(double th)
+{
+    double sn, cn;
+    sincos(th, &sn, &cn);
+    return make_float2(round_to_type<TT>(cn), round_to_type<TT>(sn));
+}
+
+// A faster route to the same values for 16-bit tables, with Ziv's rounding
+// test (cheap approximation, then a proof that it rounds as the accurate
+// value would, else the accurate evaluation):
+//  * θ = k π/2 + r, |r| <= π/4 + 2^-30, in double: k = rint(θ 2/π), then r =
+//    θ - k (P1 + P2 + P3) with π/2 split into three doubles (159 bits), one
+//    fused multiply-add per part. For |θ| <= 2^30 (|k| < 2^30) each step
+//    rounds once at |r| < 0.8, so r is within 3e-16 of θ - k π/2;
+//  * cos r and sin r in fp32 from r rounded to fp32, by their Taylor series
+//    to r^10 and r^9 (truncation below 2e-9 at π/4) in Horner form; then the
+//    quadrant k mod 4 swaps and negates them. The absolute error is below
+//    1.1e-7 (r's rounding 2.3e-8, the last two roundings of each series
+//    ~8e-8, the rest below 1e-8), and 6.6e-8 was the largest of 60 000
+//    angles measured against double cos and sin;
+//  * each value v is kept when v - E and v + E (E = 2^-21, over four times
+//    the bound) round to one value of TT: every number in between, the
+//    exact cos or sin and its double evaluation among them (within 2e-7 of
+//    v), rounds to that value too. Values of TT, and the midpoints between
+//    them, are fp32 numbers, so rounding fp32 endpoints decides this. On the
+//    angles above 0.06% of bf16 values and 0.5% of fp16 values fail the
+//    test (they lie within E of a rounding midpoint, or near 0) and take
+//    the double evaluation, as do angles beyond 2^30 and fp32 tables.
+constexpr double kPosPio2P1 = 0x1.921fb54442d18p+0;
+constexpr double kPosPio2P2 = 0x1.1a62633145c07p-54;
+constexpr double kPosPio2P3 = -0x1.f1976b7ed8fbcp-110;
+constexpr double kPosTwoOverPi = 0x1.45f306dc9c883p-1;
+constexpr double kPosFastMaxAngle = 0x1p30;
+constexpr float kPosFastErr = 0x1p-21f;
+
+// v rounded to TT (nearest, ties to even), as TT's bits.
+template <int TT>
+__device__ __forceinline__ uint32_t pos_round_bits(float v)
+{
+    if constexpr (TT == ROPE_DTYPE_BF16) {
+        const uint32_t u = __float_as_uint(v);   // finite here
+        return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    } else {
+        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+    }
+}
+
+template <int TT>
+__device__ __forceinline__ float pos_from_bits(uint32_t b)
+{
+    if constexpr (TT == ROPE_DTYPE_BF16) return __uint_as_float(b << 16);
+    else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(b)));
+}
+
 // (cos θ, sin θ) rounded to TT for position p and frequency f.
 template <int TT>
 __device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
 {
-    double sn, cn;
-    sincos(static_cast<double>(p) * f, &sn, &cn);
-    return make_float2(round_to_type<TT>(cn), round_to_type<TT>(sn));
+    const double th = static_cast<double>(p) * f;
+    if constexpr (TT != ROPE_DTYPE_F32) {
+        bool ok = false;
+        float2 out;
+        if (fabs(th) <= kPosFastMaxAngle) {
+            const double k = rint(th * kPosTwoOverPi);
+            double r = fma(-k, kPosPio2P1, th);
+            r = fma(-k, kPosPio2P2, r);
+            r = fma(-k, kPosPio2P3, r);
+            const float x = static_cast<float>(r);
+            const float z = x * x;
+            float sp = 0x1.71de3ap-19f;                        //  1/9!
+            sp = __builtin_fmaf(sp, z, -0x1.a01a02p-13f);      // -1/7!
+            sp = __builtin_fmaf(sp, z, 0x1.111112p-7f);        //  1/5!
+            sp = __builtin_fmaf(sp, z, -0x1.555556p-3f);       // -1/3!
+            const float sr = __builtin_fmaf(sp * z, x, x);
+            float cp = -0x1.27e4fcp-22f;                       // -1/10!
+            cp = __builtin_fmaf(cp, z, 0x1.a01a02p-16f);       //  1/8!
+            cp = __builtin_fmaf(cp, z, -0x1.6c16c2p-10f);      // -1/6!
+            cp = __builtin_fmaf(cp, z, 0x1.555556p-5f);        //  1/4!
+            cp = __builtin_fmaf(cp, z, -0.5f);
+            const float cr = __builtin_fmaf(cp, z, 1.0f);
+            const int q = static_cast<int>(k) & 3;
+            const float sv = (q & 1) ? cr : sr, cv = (q & 1) ? sr : cr;
+            const float sn = (q & 2) ? -sv : sv;                 // sin: q 0 sr, 1 cr, 2 -sr, 3 -cr
+            const float cn = ((q + 1) & 2) ? -cv : cv;           // cos: q 0 cr, 1 -sr, 2 -cr, 3 sr
+            const uint32_t cb = pos_round_bits<TT>(cn), sb = pos_round_bits<TT>(sn);
+            ok = pos_round_bits<TT>(cn - kPosFastErr) == cb && pos_round_bits<TT>(cn + kPosFastErr) == cb &&
+                 pos_round_bits<TT>(sn - kPosFastErr) == sb && pos_round_bits<TT>(sn + kPosFastErr) == sb;
+            out = make_float2(pos_from_bits<TT>(cb), pos_from_bits<TT>(sb));
+        }
+        if (ok) return out;
+    }
+    return pos_cos_sin_double<TT>(th);
 }
 
 // ---------------------------------------------------------------------------
