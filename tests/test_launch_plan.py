@@ -350,10 +350,12 @@ def test_pos_plan_shares_positions_across_the_batch():
     """Positions the same for every batch (one row, or a batch stride of 0):
     the batches become heads of one position per s, in blocks of up to 64
     threads. For a single K head of 128 lanes (8 threads per row) and 32
-    batches: 8 head lanes of 2 heads, two blocks per s."""
+    batches: 8 head lanes of 1 head (the rows' threads cover only the
+    slice), four blocks per s."""
     st, p = pos_plan((32, 4096, 1, 128), "bf16", (0, 128), RH, per_batch=False)
-    assert st == OK and p["head_lanes"] == 8 and p["head_chunks"] == 2 and p["positions_per_block"] == 1
-    assert p["blocks"] == 2 * 4096 and p["threads"] == 64
+    assert st == OK and p["head_lanes"] == 8 and p["head_chunks"] == 4 and p["positions_per_block"] == 1
+    assert p["heads_per_thread"] == 1
+    assert p["blocks"] == 4 * 4096 and p["threads"] == 64
     # per-batch positions: 16 consecutive (b, s) positions per block, LDS permitting (512 entries / 64 pairs)
     st, p = pos_plan((32, 4096, 1, 128), "bf16", (0, 128), RH, per_batch=True)
     assert st == OK and p["positions_per_block"] == 8 and p["blocks"] == 32 * 4096 // 8

@@ -334,8 +334,8 @@ def test_pos_mqa_k_positions_shared_by_the_batch(direction, out):
     f = rp.rope_inv_freq(w.L, w.base)
     st, plan = rp.raw_launch_info_pos(1 << 20, w.x_shapes[0], rp.DTYPE_CODES["bf16"], 1 << 20, (1, 4096), (4096, 1),
                                       1 << 20, rp.DTYPE_CODES["bf16"], rp.MODES[w.mode], w.partial_slice)
-    # the batches as heads: 32 per s, in two chunks of 8 head lanes x 2 heads (64-thread blocks)
-    assert st == rp.ROPE_OK and plan["head_lanes"] == 8 and plan["threads"] == 64 and plan["blocks"] == 8192
+    # the batches as heads: 32 per s, in four chunks of 8 head lanes x 1 head (64-thread blocks)
+    assert st == rp.ROPE_OK and plan["head_lanes"] == 8 and plan["threads"] == 64 and plan["blocks"] == 16384
     announce(f"positions mqa_k shared {direction} out={out}")
     xd = x.to(DEV)
     if out:

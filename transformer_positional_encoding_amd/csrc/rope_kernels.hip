@@ -597,7 +597,7 @@ rope_status_t run(void* x, const int64_t x_shape[4], rope_dtype_t dtype,
 // Launch plan of the position vector kernel; false if the plan needs a
 // general kernel (alignment, sizes), as for the table vector kernel. A
 // position's heads take up to kPosLanes threads (HL head lanes of span
-// threads, kUPos heads each, in chunks past kUPos*HL heads); when they fill
+// threads, U heads each, in chunks past U*HL heads); when they fill
 // fewer threads, a block takes kPosLanes/lanes positions, as many as its
 // LDS table holds.
 // The vector geometry both position kernels share: alignment, sizes, the
@@ -645,6 +645,7 @@ static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint3
     a->N = (uint32_t)heads;
     a->pairs = (uint32_t)(p.L / 2);
     const uint32_t target = a->vheads ? vheads_lanes : lanes_target;   // threads a position's heads fill
+    a->U = (uint32_t)U;
     a->HL = (uint32_t)std::min<uint64_t>(std::max<uint32_t>(1, target / a->span), heads);
     a->chunks = (uint32_t)((heads + (uint64_t)a->HL * U - 1) / ((uint64_t)a->HL * U));
     a->lanes = a->span * a->HL;
@@ -657,6 +658,20 @@ static bool pos_launch_shape(const Plan& p, PosArgs* a, uint32_t* threads, uint3
     a->items = (uint32_t)items;
     *threads = a->P * a->lanes;
     *grid = (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(items, kMaxGridItems / *threads));
+    // XCD runs of about kXcdRunBytes of x in whole position groups (all the
+    // head chunks of P positions), as for the table kernels
+    {
+        const uint64_t group_bytes = (uint64_t)a->P * heads * (uint64_t)p.D * (uint64_t)p.esize;
+        const uint64_t groups = std::max<uint64_t>(1, (kXcdRunBytes + group_bytes / 2) / group_bytes);
+        const uint64_t P = std::min<uint64_t>(groups * a->chunks, 1u << 24);
+        a->xcd_group = (uint32_t)P;
+        a->xcd_full = 0;
+        a->xcd_div = make_fastdiv(8);
+        if (P > 1 && 8 * P <= *grid) {
+            a->xcd_full = (uint32_t)(*grid / (8 * P) * (8 * P));
+            a->xcd_div = make_fastdiv((uint32_t)(8 * P));
+        }
+    }
     a->span_div = make_fastdiv(a->span);
     a->lanes_div = make_fastdiv(a->lanes);
     a->pairs_div = make_fastdiv(a->pairs);
@@ -679,7 +694,10 @@ bool pos_geometry(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* grid)
         a->lo_vec = lines.lo_vec;
         a->span = lines.span;
     }
-    return pos_launch_shape(p, a, threads, grid, kUPos, kPosLanes, kPosVheadsLanes);
+    // more heads per thread when a row's threads also carry the dropped
+    // vectors of whole-line coverage (see rope_pos_kernel)
+    const int u = a->span > a->nvec ? kUPosLines : 1;
+    return pos_launch_shape(p, a, threads, grid, u, kPosLanes, kPosVheadsLanes);
 }
 
 // Out of place: the threads of a row cover all of its vectors.
@@ -693,73 +711,79 @@ bool pos_geometry_out(const Plan& p, PosArgs* a, uint32_t* threads, uint32_t* gr
 }
 
 template <int DT, int TT, int DIR>
-const void* pos_kernel_d(int mode, bool out, bool xchg)
+const void* pos_kernel_d(int mode, bool out, bool xchg, int u)
 {
     if (out)
         return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeIL, false>)
                : xchg          ? reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeRH, true>)
                                : reinterpret_cast<const void*>(&rope_pos_out_kernel<DT, TT, DIR, kModeRH, false>);
-    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL, false>)
-                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH, false>);
+    if (u == 1)
+        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL, false, 1>)
+                               : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH, false, 1>);
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL, false, kUPosLines>)
+                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH, false, kUPosLines>);
 }
 
 template <int DT, int TT, int DIR>
-const void* pos_multi_kernel_d(int mode)
+const void* pos_multi_kernel_d(int mode, int u)
 {
-    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL, true>)
-                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH, true>);
+    if (u == 1)
+        return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL, true, 1>)
+                               : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH, true, 1>);
+    return mode == kModeIL ? reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeIL, true, kUPosLines>)
+                           : reinterpret_cast<const void*>(&rope_pos_kernel<DT, TT, DIR, kModeRH, true, kUPosLines>);
 }
 
 template <int DT, int TT>
-const void* pos_multi_kernel_t(int dir, int mode)
+const void* pos_multi_kernel_t(int dir, int mode, int u)
 {
-    return dir == kFwd ? pos_multi_kernel_d<DT, TT, kFwd>(mode) : pos_multi_kernel_d<DT, TT, kBwd>(mode);
+    return dir == kFwd ? pos_multi_kernel_d<DT, TT, kFwd>(mode, u) : pos_multi_kernel_d<DT, TT, kBwd>(mode, u);
 }
 
 template <int DT>
-const void* pos_multi_kernel_dt(int tt, int dir, int mode)
+const void* pos_multi_kernel_dt(int tt, int dir, int mode, int u)
 {
     switch (tt) {
-    case ROPE_DTYPE_F32: return pos_multi_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode);
-    case ROPE_DTYPE_F16: return pos_multi_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode);
-    default: return pos_multi_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode);
+    case ROPE_DTYPE_F32: return pos_multi_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode, u);
+    case ROPE_DTYPE_F16: return pos_multi_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode, u);
+    default: return pos_multi_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode, u);
     }
 }
 
 // the position kernel over several tensors at once
-const void* pos_multi_kernel(const Plan& p)
+const void* pos_multi_kernel(const Plan& p, int u)
 {
     switch (p.dtype) {
-    case ROPE_DTYPE_F32: return pos_multi_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode);
-    case ROPE_DTYPE_F16: return pos_multi_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode);
-    default: return pos_multi_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode);
+    case ROPE_DTYPE_F32: return pos_multi_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode, u);
+    case ROPE_DTYPE_F16: return pos_multi_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode, u);
+    default: return pos_multi_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode, u);
     }
 }
 
 template <int DT, int TT>
-const void* pos_kernel_t(int dir, int mode, bool out, bool xchg)
+const void* pos_kernel_t(int dir, int mode, bool out, bool xchg, int u)
 {
-    return dir == kFwd ? pos_kernel_d<DT, TT, kFwd>(mode, out, xchg) : pos_kernel_d<DT, TT, kBwd>(mode, out, xchg);
+    return dir == kFwd ? pos_kernel_d<DT, TT, kFwd>(mode, out, xchg, u) : pos_kernel_d<DT, TT, kBwd>(mode, out, xchg, u);
 }
 
 template <int DT>
-const void* pos_kernel_dt(int tt, int dir, int mode, bool out, bool xchg)
+const void* pos_kernel_dt(int tt, int dir, int mode, bool out, bool xchg, int u)
 {
     switch (tt) {
-    case ROPE_DTYPE_F32: return pos_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode, out, xchg);
-    case ROPE_DTYPE_F16: return pos_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode, out, xchg);
-    default: return pos_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode, out, xchg);
+    case ROPE_DTYPE_F32: return pos_kernel_t<DT, ROPE_DTYPE_F32>(dir, mode, out, xchg, u);
+    case ROPE_DTYPE_F16: return pos_kernel_t<DT, ROPE_DTYPE_F16>(dir, mode, out, xchg, u);
+    default: return pos_kernel_t<DT, ROPE_DTYPE_BF16>(dir, mode, out, xchg, u);
     }
 }
 
 // out: the out-of-place kernel; xchg: its lane exchange (a row's threads
 // within one wave: rows of 64/k vectors)
-const void* pos_kernel(const Plan& p, bool out, bool xchg = false)
+const void* pos_kernel(const Plan& p, bool out, bool xchg = false, int u = kUPosLines)
 {
     switch (p.dtype) {
-    case ROPE_DTYPE_F32: return pos_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode, out, xchg);
-    case ROPE_DTYPE_F16: return pos_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode, out, xchg);
-    default: return pos_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode, out, xchg);
+    case ROPE_DTYPE_F32: return pos_kernel_dt<ROPE_DTYPE_F32>(p.tdtype, p.dir, p.mode, out, xchg, u);
+    case ROPE_DTYPE_F16: return pos_kernel_dt<ROPE_DTYPE_F16>(p.tdtype, p.dir, p.mode, out, xchg, u);
+    default: return pos_kernel_dt<ROPE_DTYPE_BF16>(p.tdtype, p.dir, p.mode, out, xchg, u);
     }
 }
 
@@ -771,7 +795,7 @@ hipError_t launch_pos_plan(const Plan& p, int cus, hipStream_t s)
     uint32_t threads = 0, grid = 0;
     if (pos_geometry(p, &a, &threads, &grid)) {
         void* args[] = {&a};
-        return hipLaunchKernel(pos_kernel(p, false), dim3(grid), dim3(threads), args, 0, s);
+        return hipLaunchKernel(pos_kernel(p, false, false, (int)a.U), dim3(grid), dim3(threads), args, 0, s);
     }
     RowShape rs;
     return rows_shape(p, &rs) ? launch_rows(p, rs, s) : launch_scalar(p, cus, s);
@@ -845,7 +869,7 @@ rope_status_t run_pos_multi(int32_t count, void* const xs[], const int64_t (*x_s
         Plan q = P[0];
         q.N = (int64_t)heads;
         m = each[0];
-        together = pos_launch_shape(q, &m, &threads, &grid, kUPos, kPosLanes, kPosVheadsLanes);
+        together = pos_launch_shape(q, &m, &threads, &grid, (int)m.U, kPosLanes, kPosVheadsLanes);
         uint32_t first = 0;
         for (int i = 0; i < kMultiMax; ++i) {
             m.xs[i] = i < live ? each[i].x : nullptr;
@@ -858,7 +882,7 @@ rope_status_t run_pos_multi(int32_t count, void* const xs[], const int64_t (*x_s
     }
     if (together) {
         void* args[] = {&m};
-        err = hipLaunchKernel(pos_multi_kernel(P[0]), dim3(grid), dim3(threads), args, 0, s);
+        err = hipLaunchKernel(pos_multi_kernel(P[0], (int)m.U), dim3(grid), dim3(threads), args, 0, s);
     } else {
         for (int i = 0; i < live && err == hipSuccess; ++i) err = launch_pos_plan(P[i], cus, s);
     }
@@ -1288,7 +1312,7 @@ rope_status_t rope_partial_launch_info_pos(const void* x, const int64_t x_shape[
         info[0] = ROPE_KERNEL_VECTOR;
         info[1] = grid;
         info[2] = threads;
-        info[3] = rope::kUPos;
+        info[3] = a.U;
         info[4] = a.HL;
         info[5] = a.P;
         info[6] = a.chunks;

@@ -60,27 +60,35 @@ __device__ __attribute__((noinline)) float2 pos_cos_sin_double(double th)
 //  * θ = k π/2 + r, |r| <= π/4 + 2^-30, in double: k = rint(θ 2/π), then r =
 //    θ - k (P1 + P2 + P3) with π/2 split into three doubles (159 bits), one
 //    fused multiply-add per part. For |θ| <= 2^30 (|k| < 2^30) each step
-//    rounds once at |r| < 0.8, so r is within 3e-16 of θ - k π/2;
-//  * cos r and sin r in fp32 from r rounded to fp32, by their Taylor series
-//    to r^10 and r^9 (truncation below 2e-9 at π/4) in Horner form; then the
-//    quadrant k mod 4 swaps and negates them. The absolute error is below
-//    1.1e-7 (r's rounding 2.3e-8, the last two roundings of each series
-//    ~8e-8, the rest below 1e-8), and 6.6e-8 was the largest of 60 000
-//    angles measured against double cos and sin;
-//  * each value v is kept when v - E and v + E (E = 2^-21, over four times
-//    the bound) round to one value of TT: every number in between, the
-//    exact cos or sin and its double evaluation among them (within 2e-7 of
-//    v), rounds to that value too. Values of TT, and the midpoints between
-//    them, are fp32 numbers, so rounding fp32 endpoints decides this. On the
-//    angles above 0.06% of bf16 values and 0.5% of fp16 values fail the
-//    test (they lie within E of a rounding midpoint, or near 0) and take
-//    the double evaluation, as do angles beyond 2^30 and fp32 tables.
+//    rounds once at |r| < 0.8, so r is within 3e-16 of θ - k π/2 (1.1e-16
+//    measured);
+//  * sin r and cos r in fp32 from r rounded to fp32, by their Taylor series
+//    to r^9 and r^10 (truncation below 2e-9 at π/4) in Horner form, the
+//    sine as r + r z p(z) so that its error is relative to its value; then
+//    the quadrant k mod 4 swaps and negates them. Error bounds: the sine
+//    within 2.4 units of 2^-24 of |sin r| (r's rounding, the last two
+//    roundings, the rest; 1.93 measured over angles from 1e-12 to 1e5), the
+//    cosine within 1.1e-7 absolute (1.08 units of 2^-24 measured);
+//  * each value v is kept when the ends of an interval around it that holds
+//    the exact value round to one value of TT: half-width |v| 2^-21 + 2^-50
+//    for a value from the sine (the 2^-50 covers the reduction) and 2^-21
+//    for one from the cosine, over three times the bounds above, each end
+//    moved out by a further |v| 2^-23 so that its own fp32 rounding cannot
+//    pull it inside. Values of TT and the midpoints between them are fp32
+//    numbers, so if both ends round to one value every number in between
+//    does too, the exact cos or sin and its double evaluation (within a
+//    unit in its last place) among them. About 0.05% of bf16 values and
+//    0.5% of fp16 values fail the test (they lie within the half-width of
+//    a rounding midpoint) and take the double evaluation, as do angles
+//    beyond 2^30 and fp32 tables.
 constexpr double kPosPio2P1 = 0x1.921fb54442d18p+0;
 constexpr double kPosPio2P2 = 0x1.1a62633145c07p-54;
 constexpr double kPosPio2P3 = -0x1.f1976b7ed8fbcp-110;
 constexpr double kPosTwoOverPi = 0x1.45f306dc9c883p-1;
 constexpr double kPosFastMaxAngle = 0x1p30;
-constexpr float kPosFastErr = 0x1p-21f;
+constexpr float kPosFastRel = 0x1p-21f;     // the half-widths' relative part
+constexpr float kPosFastAbsSin = 0x1p-50f;  // absolute part for a value from the sine
+constexpr float kPosFastAbsCos = 0x1p-21f;  // absolute part for a value from the cosine
 
 // v rounded to TT (nearest, ties to even), as TT's bits.
 template <int TT>
@@ -131,9 +139,13 @@ __device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
             const float sv = (q & 1) ? cr : sr, cv = (q & 1) ? sr : cr;
             const float sn = (q & 2) ? -sv : sv;                 // sin: q 0 sr, 1 cr, 2 -sr, 3 -cr
             const float cn = ((q + 1) & 2) ? -cv : cv;           // cos: q 0 cr, 1 -sr, 2 -cr, 3 sr
+            // half-widths, ends moved out by |v| 2^-23 more
+            const float es = fabsf(sr) * (kPosFastRel + 0x1p-23f) + kPosFastAbsSin;
+            const float ec = fabsf(cr) * 0x1p-23f + kPosFastAbsCos;
+            const float e_sn = (q & 1) ? ec : es, e_cn = (q & 1) ? es : ec;
             const uint32_t cb = pos_round_bits<TT>(cn), sb = pos_round_bits<TT>(sn);
-            ok = pos_round_bits<TT>(cn - kPosFastErr) == cb && pos_round_bits<TT>(cn + kPosFastErr) == cb &&
-                 pos_round_bits<TT>(sn - kPosFastErr) == sb && pos_round_bits<TT>(sn + kPosFastErr) == sb;
+            ok = pos_round_bits<TT>(cn - e_cn) == cb && pos_round_bits<TT>(cn + e_cn) == cb &&
+                 pos_round_bits<TT>(sn - e_sn) == sb && pos_round_bits<TT>(sn + e_sn) == sb;
             out = make_float2(pos_from_bits<TT>(cb), pos_from_bits<TT>(sb));
         }
         if (ok) return out;
@@ -144,23 +156,28 @@ __device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
 // ---------------------------------------------------------------------------
 // Vector kernel with the tables computed from positions. A block takes P
 // consecutive (b,s) positions (P > 1 only when one position's heads fill
-// fewer than kPosLanes threads) and, for each, a chunk of up to HL*kUPos
-// heads (HL head lanes, kUPos heads per thread). Its threads first load the
-// position and frequency of the first (cos, sin) pair each evaluates, then
-// issue their x loads, then evaluate cos and sin while x is in flight: the
-// memory counter drains in issue order, so the wait for the frequency does
-// not wait for x, provided every load is issued on every path (indices are
+// fewer than kPosLanes threads) and, for each, a chunk of up to HL*U heads
+// (HL head lanes, U heads per thread). Its threads first load the position
+// and frequency of the first (cos, sin) pair each evaluates, then issue
+// their x loads, then evaluate cos and sin while x is in flight: the memory
+// counter drains in issue order, so the wait for the frequency does not
+// wait for x, provided every load is issued on every path (indices are
 // clamped, never branched around). The values go to LDS, each pair of each
 // position once per block, and each thread reads those of its lanes from
 // there. The thread layout is the table kernel's: interleave with
 // whole-line coverage, rotate_half as pair owner (a thread takes vector k
-// of both halves). Measured on MI355X (the (16,8192,32,128) shard's slice
-// [32,96), the GQA Q layout at 4096 positions, the MLA-style slice): two
-// heads per thread in 128-thread blocks was the best of 1, 2, 4 or 8 heads
-// per thread in 64-, 128- or 256-thread blocks on all three, and as fast as
-// the table kernel on the first two.
+// of both halves); the blocks walk x in XCD runs as the table kernel's do.
+// Heads per thread (kUPosLines when the rows' threads also cover vectors
+// outside the slice, to fill whole lines; else 1), measured on MI355X with
+// the fp32 cos/sin below, in 128-thread blocks (µs per launch, cold data,
+// table call beside):
+//   (16,8192,32,128) shard, slice [32,96): 1 head 302-304, 2 heads 260-261 (256-257)
+//   (32,4096,16,128) GQA Q, rotate_half:   1 head 160.6-160.9, 2 heads 161.8-162.7 (163.2-163.5)
+//   MLA-style slice [0,64) of 192 lanes:   1 head 95.3-96.0, 2 heads 100.6-103.3 (94.5-95.9)
+//   one K head, positions shared:          1 head 13.8-13.9, 2 heads 14.2-14.4 (14.3-14.4)
+// 4 or 8 heads per thread, and 64- or 256-thread blocks, were slower on all.
 // ---------------------------------------------------------------------------
-constexpr int kUPos = 2;
+constexpr int kUPosLines = 2;
 constexpr int kPosLds = ROPE_D_LIMIT / 2;    // (cos, sin) entries per block
 constexpr uint32_t kPosLanes = 128;          // threads a position's heads fill before a block takes more positions
 // In place, with the batches as heads (positions shared by the batch, few
@@ -195,6 +212,7 @@ struct PosArgs {
     uint32_t nvec;           // work units per row (interleave: slice vectors; rotate_half: half of them)
     uint32_t span;           // vectors per row the threads cover
     uint32_t HL;             // head lanes per position
+    uint32_t U;              // heads per thread (the kernel's template argument)
     uint32_t lanes;          // threads per position: span * HL
     uint32_t P;              // positions per block
     uint32_t N;
@@ -218,7 +236,22 @@ struct PosArgs {
     v4u* xs[kMultiMax];
     uint32_t nt[kMultiMax];
     uint32_t hoff[kMultiMax];
+    // XCD runs, as for the table kernels (xcd_grouped_block): blocks
+    // [0, xcd_full) are renumbered so that XCD x takes blocks [xP, xP + P)
+    // of each window of 8P (P = xcd_group)
+    uint32_t xcd_group, xcd_full;
+    FastDiv xcd_div;
 };
+
+// The block's first item under the XCD runs (a bijection of [0, gridDim.x)).
+__device__ __forceinline__ uint32_t pos_first_item(const PosArgs& a)
+{
+    const uint32_t bid = blockIdx.x;
+    if (bid >= a.xcd_full) return bid;
+    const uint32_t w = fast_div(bid, a.xcd_div);
+    const uint32_t l = bid - w * a.xcd_div.d;
+    return w * a.xcd_div.d + (l & 7u) * a.xcd_group + (l >> 3);
+}
 
 // The offset in `pos` of position g: g = b*S + s, or, vheads, g = s.
 __device__ __forceinline__ int64_t pos_offset(const PosArgs& a, uint32_t g)
@@ -277,12 +310,12 @@ __device__ __forceinline__ v4u* pos_row_vec(const PosArgs& a, uint32_t g, uint32
     }
 }
 
-template <int DT, int TT, int DIR, int MODE, bool MULTI>
+template <int DT, int TT, int DIR, int MODE, bool MULTI, int U>
 __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
 {
     __shared__ float2 cs[kPosLds];   // (cos, sin) of the block's positions, pair-major per position
     constexpr int K = Store<DT>::kLanes;
-    constexpr int U = kUPos;
+    static_assert(U == 1 || U == kUPosLines, "instantiated head counts");
     constexpr bool kUnfused = DT != ROPE_DTYPE_F32;
     const uint32_t t = threadIdx.x;
     const uint32_t pp = fast_div(t, a.lanes_div);   // the thread's position within the block
@@ -302,7 +335,7 @@ __global__ void __launch_bounds__(256) rope_pos_kernel(PosArgs a)
     const uint32_t eq = fast_div(t, a.pairs_div);
     const uint32_t ei = t - eq * a.pairs;
     // every thread runs the same iterations, so the barriers below are uniform
-    for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
+    for (uint32_t w = pos_first_item(a); w < a.items; w += gridDim.x) {
         const uint32_t grp = fast_div(w, a.chunk_div);
         const uint32_t chunk = w - grp * a.chunks;
         const uint32_t g0 = grp * a.P;                        // the block's first position
@@ -405,7 +438,7 @@ __global__ void __launch_bounds__(256) rope_pos_out_kernel(PosArgs a)
     const int xlane = XCHG ? (int)((t & 63u) + (partner - c)) * 4 : 0;
     const uint32_t eq = fast_div(t, a.pairs_div);
     const uint32_t ei = t - eq * a.pairs;
-    for (uint32_t w = blockIdx.x; w < a.items; w += gridDim.x) {
+    for (uint32_t w = pos_first_item(a); w < a.items; w += gridDim.x) {
         const uint32_t grp = fast_div(w, a.chunk_div);
         const uint32_t chunk = w - grp * a.chunks;
         const uint32_t g0 = grp * a.P;                        // the block's first position
