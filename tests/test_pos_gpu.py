@@ -266,6 +266,33 @@ def test_pos_large_and_negative_positions(tdtype):
     run_pos_and_check(x, pos, f, mode, sl, "fwd", tdtype, "large and negative positions")
 
 
+@pytest.mark.parametrize("tdtype", ["bf16", "f16"])
+@pytest.mark.parametrize("mode", ["interleave", "rotate_half"])
+def test_pos_fast_evaluation_edges(mode, tdtype):
+    """For 16-bit tables the kernels evaluate cos and sin in fp32 and keep a
+    value only when its rounding to the table type is proven (Ziv's test),
+    else they take the double evaluation. The frequencies and positions here
+    reach every branch: a zero frequency (angle 0: the sine's interval
+    straddles zero), tiny angles where the sine's relative bound decides
+    (frequencies down to 1e-12), angles near multiples of pi/2 (small
+    reduced arguments in every quadrant), negative positions (angle -0 with
+    the zero frequency), angles past 2^30 (batch 1 starts at position
+    2^31), and a dense spread of frequencies that puts many
+    values near rounding midpoints. Every lane must equal the rotation with
+    the oracle's tables bit for bit."""
+    shape, sl = (2, 256, 4, 128), (0, 128)
+    x = _rand(shape, "bf16", 91)
+    g = torch.Generator().manual_seed(92)
+    f = torch.empty(64, dtype=torch.float64)
+    f[:8] = torch.tensor([0.0, 1e-12, 1e-9, 1e-6, 1e-4, 1e-2, 1.0, 1.5707963267948966], dtype=torch.float64)
+    f[8:16] = torch.tensor([0.5 * np.pi, np.pi, 2 * np.pi, 0.25 * np.pi, 1e-3, 3e-7, 0.1, 0.7], dtype=torch.float64)
+    f[16:] = 10.0 ** (torch.rand(48, generator=g, dtype=torch.float64) * 6 - 5)
+    pos = torch.arange(256, dtype=torch.int64)[None, :].repeat(2, 1)
+    pos[0, 200:216] = -torch.arange(1, 17)          # with the zero frequency: angle -0
+    pos[1] += 2 ** 31
+    run_pos_and_check(x, pos, f, mode, sl, "fwd", tdtype, f"fast evaluation edges {mode} {tdtype}")
+
+
 # ---------------------------------------------------------------- several tensors
 
 MULTI_CASES = [

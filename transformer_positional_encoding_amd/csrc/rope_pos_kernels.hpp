@@ -71,7 +71,8 @@ __device__ __attribute__((noinline)) float2 pos_cos_sin_double(double th)
 //    cosine within 1.1e-7 absolute (1.08 units of 2^-24 measured);
 //  * each value v is kept when the ends of an interval around it that holds
 //    the exact value round to one value of TT: half-width |v| 2^-21 + 2^-50
-//    for a value from the sine (the 2^-50 covers the reduction) and 2^-21
+//    for a value from the sine (the 2^-50 covers the reduction; with k = 0
+//    it is exact, r = θ, and the term is left out) and 2^-21
 //    for one from the cosine, over three times the bounds above, each end
 //    moved out by a further |v| 2^-23 so that its own fp32 rounding cannot
 //    pull it inside. Values of TT and the midpoints between them are fp32
@@ -119,16 +120,19 @@ __device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
         float2 out;
         if (fabs(th) <= kPosFastMaxAngle) {
             const double k = rint(th * kPosTwoOverPi);
-            double r = fma(-k, kPosPio2P1, th);
-            r = fma(-k, kPosPio2P2, r);
-            r = fma(-k, kPosPio2P3, r);
+            double r = th;                                   // k = 0: exact, and -0 keeps its sign
+            if (k != 0.0) {
+                r = fma(-k, kPosPio2P1, th);
+                r = fma(-k, kPosPio2P2, r);
+                r = fma(-k, kPosPio2P3, r);
+            }
             const float x = static_cast<float>(r);
             const float z = x * x;
             float sp = 0x1.71de3ap-19f;                        //  1/9!
             sp = __builtin_fmaf(sp, z, -0x1.a01a02p-13f);      // -1/7!
             sp = __builtin_fmaf(sp, z, 0x1.111112p-7f);        //  1/5!
             sp = __builtin_fmaf(sp, z, -0x1.555556p-3f);       // -1/3!
-            const float sr = __builtin_fmaf(sp * z, x, x);
+            const float sr = x == 0.0f ? x : __builtin_fmaf(sp * z, x, x);   // sin(±0) = ±0 exactly
             float cp = -0x1.27e4fcp-22f;                       // -1/10!
             cp = __builtin_fmaf(cp, z, 0x1.a01a02p-16f);       //  1/8!
             cp = __builtin_fmaf(cp, z, -0x1.6c16c2p-10f);      // -1/6!
@@ -140,7 +144,7 @@ __device__ __forceinline__ float2 pos_cos_sin(int64_t p, double f)
             const float sn = (q & 2) ? -sv : sv;                 // sin: q 0 sr, 1 cr, 2 -sr, 3 -cr
             const float cn = ((q + 1) & 2) ? -cv : cv;           // cos: q 0 cr, 1 -sr, 2 -cr, 3 sr
             // half-widths, ends moved out by |v| 2^-23 more
-            const float es = fabsf(sr) * (kPosFastRel + 0x1p-23f) + kPosFastAbsSin;
+            const float es = fabsf(sr) * (kPosFastRel + 0x1p-23f) + (k != 0.0 ? kPosFastAbsSin : 0.0f);
             const float ec = fabsf(cr) * 0x1p-23f + kPosFastAbsCos;
             const float e_sn = (q & 1) ? ec : es, e_cn = (q & 1) ? es : ec;
             const uint32_t cb = pos_round_bits<TT>(cn), sb = pos_round_bits<TT>(sn);
