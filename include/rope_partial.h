@@ -436,8 +436,12 @@ ROPE_API rope_status_t rope_partial_launch_info_pos(
  * on y's shape with y_dtype (ROPE_ERR_NULLPTR for a NULL y_shape,
  * ROPE_ERR_INVALID otherwise); dtype bf16 or fp16, y_dtype dtype or fp32
  * and K >= 0 (ROPE_ERR_INVALID); an empty y returns ROPE_OK without reading
- * any pointer; K not a positive multiple of 64, or Dh not one of 32, 64,
- * 96, 128 and 192 (ROPE_ERR_UNSUPPORTED: block tiles hold whole heads);
+ * any pointer; K not a positive multiple of 64; Dh not one of 32, 64, 96,
+ * 128 and 192 (block tiles of whole heads) nor a multiple of 192 or 128 up
+ * to 1024 (a head over whole tiles of 192 or 128 lanes, such as MLA's 576-
+ * lane compressed KV with its 64 rope lanes); or, for such a wide head, a
+ * rotate_half or coefficient group of the slice (2 x its pair distance
+ * lanes) that spans two tiles (ROPE_ERR_UNSUPPORTED);
  * NULL y, x or w (ROPE_ERR_NULLPTR); y, x or w not 16-byte aligned or
  * sizes beyond 64-bit offsets (ROPE_ERR_INVALID); x or w of 2^31 elements
  * or more (ROPE_ERR_UNSUPPORTED); y overlapping x or w (ROPE_ERR_INVALID); then,

@@ -433,6 +433,17 @@ def _proj(**kw):
     (dict(K=0), rp.ROPE_ERR_UNSUPPORTED, "multiple of 64"),
     (dict(y_shape=(1, 8, 2, 160), r1_shape=(1, 8, 1, 64), r2_shape=(1, 8, 1, 64)), rp.ROPE_ERR_UNSUPPORTED,
      "head dimension"),
+    # heads wider than a tile: 320 is neither a multiple of 192 nor of 128
+    (dict(y_shape=(1, 8, 1, 320)), rp.ROPE_ERR_UNSUPPORTED, "head dimension"),
+    # a 384-lane head over two 192-lane tiles: rotate_half over lanes [0, 384)
+    # pairs lane j with j + 192, in the other tile; [128, 256) straddles too
+    (dict(y_shape=(1, 8, 1, 384), r1_shape=(1, 8, 1, 384), r2_shape=(1, 8, 1, 384), r1_strides=(0, 384, 0, 1),
+          r2_strides=(0, 384, 0, 1), mode=0, partial_slice=(0, 384)), rp.ROPE_ERR_UNSUPPORTED, "spans two column tiles"),
+    (dict(y_shape=(1, 8, 1, 384), mode=0, partial_slice=(160, 224)), rp.ROPE_ERR_UNSUPPORTED, "spans two column tiles"),
+    # a coefficient's parts likewise: 4 parts of 32 over [160, 288) form groups [160, 224) and
+    # [224, 288), the first across lane 192 (over [128, 256) the groups meet at 192 and are accepted)
+    (dict(y_shape=(1, 8, 1, 384), r1_shape=(1, 8, 1, 128), r2_shape=(1, 8, 1, 128), r1_strides=(0, 128, 0, 1),
+          r2_strides=(0, 128, 0, 1), mode=4, partial_slice=(160, 288)), rp.ROPE_ERR_UNSUPPORTED, "spans two column tiles"),
     (dict(y_ptr=None), rp.ROPE_ERR_NULLPTR, "y is NULL"),
     (dict(w_ptr=None), rp.ROPE_ERR_NULLPTR, "w is NULL"),
     (dict(x_ptr=0x2000008), rp.ROPE_ERR_INVALID, "16-byte aligned"),
@@ -447,6 +458,23 @@ def _proj(**kw):
 def test_projection_argument_errors(kwargs, code, text):
     assert _proj(**kwargs) == code
     assert text in rp.last_error()
+
+
+def test_projection_wide_heads_pass_the_checks():
+    """Heads wider than a tile pass every argument check when each rotation
+    group stays in one tile: MLA's 576-lane compressed KV with rope on its
+    last 64 lanes (interleave or rotate_half), a 256-lane head (two 128-lane
+    tiles), and a coefficient's groups inside a 384-lane head's second tile.
+    Without a GPU the call then fails at the launch, past every check."""
+    for kw in (dict(y_shape=(1, 8, 1, 576), mode=1, partial_slice=(512, 576)),
+               dict(y_shape=(1, 8, 1, 576), mode=0, partial_slice=(512, 576)),
+               dict(y_shape=(1, 8, 3, 256), mode=0, partial_slice=(0, 64)),
+               dict(y_shape=(1, 8, 1, 384), r1_shape=(1, 8, 1, 128), r2_shape=(1, 8, 1, 128),
+                    r1_strides=(0, 128, 0, 1), r2_strides=(0, 128, 0, 1), mode=4, partial_slice=(192, 320)),
+               dict(y_shape=(1, 8, 1, 384), r1_shape=(1, 8, 1, 128), r2_shape=(1, 8, 1, 128),
+                    r1_strides=(0, 128, 0, 1), r2_strides=(0, 128, 0, 1), mode=4, partial_slice=(128, 256))):
+        st = _proj(**kw)
+        assert st == rp.ROPE_ERR_RUNTIME, (kw, st, rp.last_error())
 
 
 def test_projection_noops_need_no_pointers():

@@ -157,6 +157,15 @@ CASES = [
     (1, 70, 128, 4, 96, (32, 96), "rotate_half", "f16", "f16", "f32", "offset"),
     # the plain projection (empty slice)
     (1, 512, 1536, 32, 192, None, "interleave", "bf16", "bf16", "bf16", "token"),
+    # heads wider than a tile: MLA's compressed KV (512 lanes) with its K rope lanes (64) at the
+    # end, one 576-lane head over three 192-lane tiles ([P4] section 3, kRopeDim), both modes
+    (1, 300, 512, 1, 576, (512, 576), "rotate_half", "bf16", "bf16", "bf16", "token"),
+    (2, 100, 256, 1, 576, (512, 576), "interleave", "bf16", "f32", "f32", "batch"),
+    # a 256-lane head over two 128-lane tiles, per-head tables; a coefficient inside a
+    # 384-lane head's second tile; an odd start in a wide head (lane by lane)
+    (1, 130, 128, 3, 256, (0, 64), "rotate_half", "f16", "f16", "f16", "head"),
+    (1, 90, 192, 2, 384, (192, 320), 4, "bf16", "bf16", "bf16", "token"),
+    (2, 33, 64, 1, 512, (3, 35), "interleave", "bf16", "bf16", "bf16", "batch"),
 ]
 
 

@@ -1006,9 +1006,10 @@ rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void*
     a.start = (int32_t)p.start;
     a.L = (int32_t)p.L;
     a.half = p.L > 0 ? (int32_t)p.half : 1;
-    // block tiles of whole heads: 192 lanes (384 tokens) for heads of 96 or
-    // 192 lanes, else 128 lanes (256 tokens)
-    const int BN = p.D % 3 == 0 ? 192 : 128;
+    // block tiles of whole heads, or of part of one wider head: 192 lanes
+    // (384 tokens) for heads of a multiple of 3 lanes, else 128 lanes (256
+    // tokens)
+    const int BN = (int)proj_tile_lanes(p.D);
     const int BM = BN == 192 ? ProjTile<192>::BM : ProjTile<128>::BM;
     const int threads = BN == 192 ? ProjTile<192>::THREADS : ProjTile<128>::THREADS;
     const int64_t MB = (a.M + BM - 1) / BM, NB = (a.N + BN - 1) / BN;

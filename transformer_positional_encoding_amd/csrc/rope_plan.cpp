@@ -329,7 +329,19 @@ rope_status_t check_disjoint(const Plan plans[], int n, std::string* why)
 
 bool proj_head_dim_supported(int64_t Dh)
 {
-    return Dh == 32 || Dh == 64 || Dh == 96 || Dh == 128 || Dh == 192;
+    if (Dh == 32 || Dh == 64 || Dh == 96 || Dh == 128 || Dh == 192) return true;   // whole heads per tile
+    return Dh > 192 && Dh <= ROPE_D_LIMIT && (Dh % 192 == 0 || Dh % 128 == 0);   // a head over whole tiles
+}
+
+int64_t proj_tile_lanes(int64_t Dh) { return Dh % 3 == 0 ? 192 : 128; }
+
+bool proj_groups_in_tiles(int64_t Dh, int64_t start, int64_t L, int64_t half)
+{
+    const int64_t bn = proj_tile_lanes(Dh);
+    if (Dh <= bn || L == 0 || half == 1) return true;   // whole heads per tile, or pairs of adjacent lanes
+    for (int64_t lo = start; lo < start + L; lo += 2 * half)
+        if (lo / bn != (lo + 2 * half - 1) / bn) return false;
+    return true;
 }
 
 rope_status_t make_proj_plan(void* y, rope_dtype_t out_dtype, const void* x, const void* w, rope_dtype_t dtype,
@@ -360,7 +372,11 @@ rope_status_t make_proj_plan(void* y, rope_dtype_t out_dtype, const void* x, con
     if (K == 0 || K % 64 != 0)
         return fail(ROPE_ERR_UNSUPPORTED, why, "K must be a positive multiple of 64");
     if (!proj_head_dim_supported(Dh))
-        return fail(ROPE_ERR_UNSUPPORTED, why, "head dimension must be 32, 64, 96, 128 or 192");
+        return fail(ROPE_ERR_UNSUPPORTED, why,
+                    "head dimension must be 32, 64, 96, 128 or 192, or a multiple of 192 or 128 up to 1024");
+    if (!proj_groups_in_tiles(Dh, q.rope.start, q.rope.L, q.rope.half))
+        return fail(ROPE_ERR_UNSUPPORTED, why,
+                    "a rotation group of the slice spans two column tiles of a head wider than the tile");
     if (y == nullptr) return fail(ROPE_ERR_NULLPTR, why, "y is NULL");
     if (x == nullptr) return fail(ROPE_ERR_NULLPTR, why, "x is NULL");
     if (w == nullptr) return fail(ROPE_ERR_NULLPTR, why, "w is NULL");

@@ -107,13 +107,25 @@ struct ProjPlan {
 // two calls). ROPE_ERR_INVALID names the first overlapping pair.
 rope_status_t check_disjoint(const Plan plans[], int n, std::string* why);
 
-// Lanes per head the fused kernel takes (block tiles of whole heads).
+// Lanes per head the fused kernel takes: 32, 64, 96, 128 or 192 (block
+// tiles of whole heads), or a multiple of 192 or 128 up to 1024 (a head over
+// whole tiles).
 bool proj_head_dim_supported(int64_t Dh);
+
+// Output lanes per block tile for heads of Dh lanes: 192 when Dh is a
+// multiple of 3, else 128.
+int64_t proj_tile_lanes(int64_t Dh);
+
+// With heads wider than a tile, a rotation partner must lie in the same
+// tile: every group of 2*half lanes of the slice (a rotate_half pair's or a
+// coefficient part pair's span) within one tile; interleave (half 1) always.
+bool proj_groups_in_tiles(int64_t Dh, int64_t start, int64_t L, int64_t half);
 
 // Checks, in order: the scalar arguments of make_plan on y's shape (with the
 // output type); input type bf16 or fp16; output type the inputs' type or
-// fp32; K >= 0; an empty y is a no-op; K a positive multiple of 64 and Dh
-// one the kernel tiles (ROPE_ERR_UNSUPPORTED); NULL y, x or w; 16-byte
+// fp32; K >= 0; an empty y is a no-op; K a positive multiple of 64, Dh one
+// the kernel tiles, and the slice's rotation groups within tiles
+// (ROPE_ERR_UNSUPPORTED); NULL y, x or w; 16-byte
 // alignment of y, x and w; sizes within 64-bit offsets; x or w of 2^31
 // elements or more (ROPE_ERR_UNSUPPORTED: 32-bit offsets in the kernel); y
 // overlapping x or w; then, for a non-empty slice, the tables as in

@@ -19,8 +19,9 @@
 // k of one row of A (x) and 8 consecutive k of one column of B (a row of w).
 //
 // Tiling (gfx950: 256 CUs, 160 KiB LDS and 512 VGPRs per SIMD lane): a block
-// computes a BM x BN tile of y (BN = 192 or 128 output lanes, a whole number
-// of heads; BM = 384 or 256 tokens) with BM/64 x 2 waves, each holding a
+// computes a BM x BN tile of y (BN = 192 or 128 output lanes: a whole number
+// of heads, or part of one head that spans whole tiles; BM = 384 or 256
+// tokens) with BM/64 x 2 waves, each holding a
 // 64 x BN/2 sub-tile as 2 x BN/64 accumulators of 32 x 32 fp32 (96 or 64
 // registers), so that 3 (or 2) waves share each SIMD and one wave's LDS
 // reads overlap another's MFMAs. The K loop runs over stages of 64 k: each
@@ -297,16 +298,17 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
     // consecutive vectors, so each 8 threads store one 128-byte line.
     float* Cs = reinterpret_cast<float*>(smem);        // [RH][LDC]
     const int tv = t & 7, tr = t >> 3;
-    const int32_t h0 = (int32_t)fast_div((uint32_t)n0, a.dh_div);   // the tile's first head
     const int g2 = 2 * a.half;
-    // per vector i: lanes [c0, c0+8) of the tile, head hl, slice-relative first lane rel0
+    // per vector i: lanes [c0, c0+8) of the tile, in head hl (of y, from the
+    // vector's column n0 + c0: a tile holds whole heads, or part of one head
+    // wider than the tile), slice-relative first lane rel0
     int c0[T_::VI], hl[T_::VI], rel0[T_::VI];
     bool live_v[T_::VI], rot[T_::VI];
 #pragma unroll
     for (int i = 0; i < T_::VI; ++i) {
         c0[i] = 8 * (tv + 8 * i);
-        hl[i] = (int)fast_div((uint32_t)c0[i], a.dh_div);
-        rel0[i] = c0[i] - hl[i] * a.Dh - a.start;
+        hl[i] = (int)fast_div((uint32_t)(n0 + c0[i]), a.dh_div);
+        rel0[i] = n0 + c0[i] - hl[i] * a.Dh - a.start;
         live_v[i] = n0 + c0[i] < a.N;
         // rotated: meets the slice, in a head that exists (the last tile
         // along N may reach past N; its table rows must not be read)
@@ -339,14 +341,14 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
             m[p] = m0 + (lr >> 5) * 64 + h * 32 + (lr & 31);
             const int32_t mc = (int32_t)min<int64_t>(m[p], a.M - 1);
             const int32_t b = (int32_t)fast_div((uint32_t)mc, a.s_div), sp = mc - b * a.S;
-            o1[p] = b * a.t1b + sp * a.t1s + (int64_t)h0 * a.t1n;
-            o2[p] = b * a.t2b + sp * a.t2s + (int64_t)h0 * a.t2n;
+            o1[p] = b * a.t1b + sp * a.t1s;
+            o2[p] = b * a.t2b + sp * a.t2s;
             if (a.fast) {
 #pragma unroll
                 for (int i = 0; i < VP; ++i)
                     if (rot[i]) {
-                        pc[p][i].load(a.r1, o1[p] + hl[i] * a.t1n + rel0[i]);
-                        ps[p][i].load(a.r2, o2[p] + hl[i] * a.t2n + rel0[i]);
+                        pc[p][i].load(a.r1, o1[p] + (int64_t)hl[i] * a.t1n + rel0[i]);
+                        ps[p][i].load(a.r2, o2[p] + (int64_t)hl[i] * a.t2n + rel0[i]);
                     }
             }
         }
@@ -372,8 +374,8 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
                         if (rel >= 0 && rel < a.L) {
                             const bool f = rel % g2 < a.half;
                             const float xpe = crow[c0[i] + e + (f ? a.half : -a.half)];
-                            const float ce = Store<TT>::load1(a.r1, o1[p] + hl[i] * a.t1n + rel);
-                            const float se = Store<TT>::load1(a.r2, o2[p] + hl[i] * a.t2n + rel);
+                            const float ce = Store<TT>::load1(a.r1, o1[p] + (int64_t)hl[i] * a.t1n + rel);
+                            const float se = Store<TT>::load1(a.r2, o2[p] + (int64_t)hl[i] * a.t2n + rel);
                             ye = rotate_own<false>(ye, xpe, ce, se, f);
                         }
                         if (a.ydt == ROPE_DTYPE_F32) Store<ROPE_DTYPE_F32>::store1(a.y, yo + e, ye);
@@ -397,8 +399,8 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
                         ps[p][i < VP ? i : 0].widen(ss);
                     } else {
                         ProjTab8<TT> c1, s1;
-                        c1.load(a.r1, o1[p] + hl[i] * a.t1n + rel0[i]);
-                        s1.load(a.r2, o2[p] + hl[i] * a.t2n + rel0[i]);
+                        c1.load(a.r1, o1[p] + (int64_t)hl[i] * a.t1n + rel0[i]);
+                        s1.load(a.r2, o2[p] + (int64_t)hl[i] * a.t2n + rel0[i]);
                         c1.widen(cc);
                         s1.widen(ss);
                     }
