@@ -513,28 +513,44 @@ def profile_target(name: str, reps: int, out_of_place: bool = False, positions: 
 
     import transformer_positional_encoding_amd as rp
     import workloads as W
-    w = W.WORKLOADS[name]
-    ncopy = 1 if out_of_place else rotating_copies(w)
-    xs = [W.make_x(w).to("cuda")]
-    xs += [xs[0].clone() for _ in range(ncopy - 1)]
-    r1, r2 = (t.to("cuda") for t in W.make_tables(w))
-    dirs = list(w.directions) + [d for d in ("fwd", "bwd") if d not in w.directions]
-    y = torch.empty_like(xs[0]) if out_of_place else None
-    pos = torch.from_numpy(W.positions(w)).to("cuda") if positions else None
-    f = rp.rope_inv_freq(w.L, w.base, "cuda") if positions else None
-    for d in dirs:
-        for i in range(reps):
-            if positions and out_of_place:
-                (rp.rope_partial_fwd_out_pos if d == "fwd" else rp.rope_partial_bwd_out_pos)(
-                    y, xs[0], pos, f, w.mode, w.partial_slice, W.TORCH_DTYPES[w.tdtype])
-            elif positions:
-                (rp.rope_partial_fwd_inplace_pos if d == "fwd" else rp.rope_partial_bwd_inplace_pos)(
-                    xs[i % ncopy], pos, f, w.mode, w.partial_slice, W.TORCH_DTYPES[w.tdtype])
-            elif out_of_place:
-                (rp.rope_partial_fwd_out if d == "fwd" else rp.rope_partial_bwd_out)(
-                    y, xs[0], r1, r2, w.mode, w.partial_slice)
-            else:
-                launch_fn(d)(xs[i % ncopy], r1, r2, w.mode, w.partial_slice)
+    if name in W.PROJ_WORKLOADS:
+        # the projection with a rotary epilogue, then the same projection with
+        # an empty slice (plain GEMM)
+        pw = W.PROJ_WORKLOADS[name]
+        wr = W.WORKLOADS[pw.rope]
+        B, S, H, Dh = pw.y_shape
+        x, wt = (t.to("cuda") for t in W.make_proj_inputs(pw))
+        r1, r2 = (t.to("cuda") for t in W.make_tables(wr))
+        z = torch.zeros((1, 1, 1, 0), dtype=x.dtype, device="cuda")
+        y = torch.empty((B, S, H, Dh), dtype=x.dtype, device="cuda")
+        for _ in range(reps):
+            rp.rope_proj_fwd(x, wt, r1, r2, H, wr.mode, wr.partial_slice, out=y)
+        for _ in range(reps):
+            rp.rope_proj_fwd(x, wt, z, z, H, wr.mode, None, out=y)
+        ncopy = 1
+    else:
+        w = W.WORKLOADS[name]
+        ncopy = 1 if out_of_place else rotating_copies(w)
+        xs = [W.make_x(w).to("cuda")]
+        xs += [xs[0].clone() for _ in range(ncopy - 1)]
+        r1, r2 = (t.to("cuda") for t in W.make_tables(w))
+        dirs = list(w.directions) + [d for d in ("fwd", "bwd") if d not in w.directions]
+        y = torch.empty_like(xs[0]) if out_of_place else None
+        pos = torch.from_numpy(W.positions(w)).to("cuda") if positions else None
+        f = rp.rope_inv_freq(w.L, w.base, "cuda") if positions else None
+        for d in dirs:
+            for i in range(reps):
+                if positions and out_of_place:
+                    (rp.rope_partial_fwd_out_pos if d == "fwd" else rp.rope_partial_bwd_out_pos)(
+                        y, xs[0], pos, f, w.mode, w.partial_slice, W.TORCH_DTYPES[w.tdtype])
+                elif positions:
+                    (rp.rope_partial_fwd_inplace_pos if d == "fwd" else rp.rope_partial_bwd_inplace_pos)(
+                        xs[i % ncopy], pos, f, w.mode, w.partial_slice, W.TORCH_DTYPES[w.tdtype])
+                elif out_of_place:
+                    (rp.rope_partial_fwd_out if d == "fwd" else rp.rope_partial_bwd_out)(
+                        y, xs[0], r1, r2, w.mode, w.partial_slice)
+                else:
+                    launch_fn(d)(xs[i % ncopy], r1, r2, w.mode, w.partial_slice)
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")  # 256 MiB
     src.fill_(1)
     dst = torch.empty_like(src)
