@@ -768,7 +768,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c4")
-    ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out,c4:pos,c2_s4096:pos,c4:outpos,"
+    ap.add_argument("--also", default="c3,c4_f32,c2,c4_t32,c4:out,c3:out,c4:pos,c2_s4096:pos,c3:pos,c4:outpos,"
                                       "c2_s4096:outpos,c2:posmulti,tp_qk:posmulti,c4_t32:pos,mqa_k:pos,c2_s4096,rh_64of128,"
                                       "rh_32of128,"
                                       "c3_coeff4,c3_proj",
