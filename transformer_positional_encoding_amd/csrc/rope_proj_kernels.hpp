@@ -29,7 +29,11 @@
 // 32 k would fetch every line twice). Two stages of (BM + BN) x 128 bytes
 // form the LDS ring, filled by the gfx950 direct global-to-LDS loads
 // (global_load_lds_dwordx4: each lane's 16 bytes go to the wave's LDS base +
-// 16 * lane, no registers in between) one stage ahead of the MFMAs. Within a
+// 16 * lane, no registers in between) one stage ahead of the MFMAs. They take
+// the SGPR-base form (a uniform base per stage and operand plus a 32-bit byte
+// offset per lane): the CU accepts these about a third faster than loads with
+// a 64-bit address per lane, and a wave whose load cannot issue yet holds back
+// the MFMAs behind it, so a stage's load issue is on the MFMAs' path. Within a
 // 128-byte row the eight 16-byte k-vectors are stored XOR-swizzled by a
 // function of the row modulo 32, chosen so that the 8, 16 or 32 lanes that
 // one LDS cycle serves read distinct banks (the fragment reads take 16 bytes
@@ -98,11 +102,12 @@ struct ProjTile {
 // only on r mod 32, so every 32-row fragment uses the same slots.
 __device__ __forceinline__ int proj_swz(int r) { return ((r ^ (r >> 3)) & 3) | (r & 4); }
 
-// One direct global-to-LDS load of 16 bytes per lane: lane l's bytes go to
-// LDS byte address lds_base + 16*l (lds_base is the same for the whole wave).
-__device__ __forceinline__ void proj_dma16(const void* g, uint32_t lds_base)
+// One direct global-to-LDS load of 16 bytes per lane from base + voff (base
+// the same for the whole wave, voff lane l's byte offset): lane l's bytes go
+// to LDS byte address lds_base + 16*l (lds_base the same for the whole wave).
+__device__ __forceinline__ void proj_dma16(const void* base, uint32_t voff, uint32_t lds_base)
 {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(g) : "memory");
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_base), "v"(voff), "s"(base) : "memory");
 }
 
 // s_waitcnt vmcnt(N) with lgkmcnt and expcnt left free (gfx9 encoding:
@@ -210,7 +215,7 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
     const int32_t n0 = nb * BN;
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int wave = t >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wave % T_::WM, wn = wave / T_::WM;
 
     // ---------------------------------------------------------------- main loop
@@ -219,7 +224,7 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
     // loads [LW*wave, LW*wave + LW). Lane l of a load writes row 8*li + l/8
     // at 16-byte slot l%8, which holds k-vector (l%8) ^ proj_swz(row). Rows
     // past M or N re-read the last row (always in bounds); their results are
-    // never stored. Element offsets are 32-bit (x and w hold fewer than 2^31
+    // never stored. Byte offsets are 32-bit (x and w hold fewer than 2^31
     // elements).
     uint32_t goff[LW];
     bool from_x[LW];
@@ -231,15 +236,16 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
         const int row = from_x[i] ? srow : srow - BM;
         const int kv = (lane & 7) ^ proj_swz(row & 31);
         const int32_t g = from_x[i] ? min(m0 + row, a.M - 1) : min(n0 + row, a.N - 1);
-        goff[i] = (uint32_t)g * (uint32_t)a.K + (uint32_t)(kv * 8);
+        goff[i] = ((uint32_t)g * (uint32_t)a.K + (uint32_t)(kv * 8)) * 2u;
     }
     const uint32_t smem_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
     const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(smem_lds + wave * LW * 1024);
     auto issue_stage = [&](int32_t k, int slot) {
-        const uint32_t koff = (uint32_t)(k * kProjBK);
+        const uint16_t* xk = a.x + k * kProjBK;
+        const uint16_t* wk = a.w + k * kProjBK;
         const uint32_t sbase = wave_lds + (uint32_t)(slot * T_::STAGE);
 #pragma unroll
-        for (int i = 0; i < LW; ++i) proj_dma16((from_x[i] ? a.x : a.w) + (goff[i] + koff), sbase + i * 1024);
+        for (int i = 0; i < LW; ++i) proj_dma16(from_x[i] ? xk : wk, goff[i], sbase + i * 1024);
     };
 
     f32x16 acc[MT][NT];
