@@ -84,18 +84,9 @@ struct ProjTile {
     static constexpr int LW = NLOAD / NW;         // per wave
     static_assert(NLOAD % NW == 0, "every wave issues the same number of loads");
     static_assert(BM % 8 == 0, "no wave load straddles x and w");
-    static constexpr int LDC = BN + 20;           // epilogue row pitch in floats
+    static constexpr int LDC = BN + 4;            // epilogue row pitch in floats
     static constexpr int RH = BM / 2;             // rows per epilogue half
-    // Row r of the epilogue staging starts at float r*LDC, plus 16 in every
-    // second group of 4 rows (LDC >= BN + 16: rows never overlap). An
-    // accumulator write puts lanes 32..63 four rows below lanes 0..31:
-    // 4*LDC + 16 = 32 (mod 64) floats, so the two halves meet distinct banks.
-    // The row reads (16 bytes per lane, 8 lanes per row) serve rows in pairs
-    // 2j, 2j+1 that share a group and are 4*LDC = 80 (mod 256) bytes apart,
-    // 20 banks, so their 16-byte pieces interleave.
-    static_assert(LDC >= BN + 16 && (4 * LDC + 16) % 64 == 32 && LDC % 8 == 4, "staging layout");
-    __device__ static int row_at(int r) { return r * LDC + ((r >> 2) & 1) * 16; }
-    static constexpr int EPI = (RH * LDC + 16) * 4;
+    static constexpr int EPI = RH * LDC * 4;
     static constexpr int LDS = kProjStages * STAGE > EPI ? kProjStages * STAGE : EPI;
     static_assert(LDS <= 160 * 1024, "LDS per block");
     static constexpr int RPP = THREADS / 8;       // rows per epilogue pass: 8 threads per row
@@ -215,7 +206,7 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
     __attribute__((amdgpu_waves_per_eu(ProjTile<BN>::NW / 4, ProjTile<BN>::NW / 4))) rope_proj_kernel(ProjArgs a)
 {
     using T_ = ProjTile<BN>;
-    constexpr int BM = T_::BM, MT = T_::MT, NT = T_::NT, LW = T_::LW;
+    constexpr int BM = T_::BM, MT = T_::MT, NT = T_::NT, LW = T_::LW, LDC = T_::LDC;
     __shared__ __attribute__((aligned(16))) uint16_t smem[T_::LDS / 2];
 
     int32_t mb, nb;
@@ -311,7 +302,7 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
     // row lr = t/8 + p*RPP of the half (p < PR) and the 8-lane vectors
     // v = t%8 + 8*i (i < VI) of that row: consecutive threads take
     // consecutive vectors, so each 8 threads store one 128-byte line.
-    float* Cs = reinterpret_cast<float*>(smem);        // RH rows, row r at row_at(r)
+    float* Cs = reinterpret_cast<float*>(smem);        // [RH][LDC]
     const int tv = t & 7, tr = t >> 3;
     const int g2 = 2 * a.half;
     // per vector i: lanes [c0, c0+8) of the tile, in head hl (of y, from the
@@ -338,7 +329,7 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
             for (int r = 0; r < 16; ++r) {
                 const int lr = wm * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
                 const int col = wn * (BN / 2) + j * 32 + (lane & 31);
-                Cs[T_::row_at(lr) + col] = accq[j][r];
+                Cs[lr * LDC + col] = accq[j][r];
             }
     };
     // Table values prefetched for the first vector of each pass (lanes
@@ -373,7 +364,7 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
 #pragma unroll
         for (int p = 0; p < T_::PR; ++p) {
             if (m[p] >= a.M) continue;
-            const float* crow = Cs + T_::row_at(tr + p * T_::RPP);
+            const float* crow = Cs + (tr + p * T_::RPP) * LDC;
 #pragma unroll
             for (int i = 0; i < T_::VI; ++i) {
                 if (!live_v[i]) continue;
