@@ -224,8 +224,9 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
     // loads [LW*wave, LW*wave + LW). Lane l of a load writes row 8*li + l/8
     // at 16-byte slot l%8, which holds k-vector (l%8) ^ proj_swz(row). Rows
     // past M or N re-read the last row (always in bounds); their results are
-    // never stored. Byte offsets are 32-bit (x and w hold fewer than 2^31
-    // elements).
+    // never stored. The SGPR-base loads take the per-lane byte offset as an
+    // unsigned 32-bit number; x and w hold fewer than 2^31 elements, so every
+    // offset is below 2^32.
     uint32_t goff[LW];
     bool from_x[LW];
 #pragma unroll
