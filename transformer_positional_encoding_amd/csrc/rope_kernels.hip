@@ -975,6 +975,29 @@ hipError_t launch_proj(const ProjArgs& a, int tdt, uint32_t grid, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int DT, int EPI>
+hipError_t launch_proj_sq(const ProjArgs& a, int tdt, uint32_t grid, hipStream_t s)
+{
+    const dim3 block(ProjSq::THREADS);
+    if (tdt == ROPE_DTYPE_BF16)
+        hipLaunchKernelGGL((rope_proj_sq_kernel<DT, ROPE_DTYPE_BF16, EPI>), dim3(grid), block, 0, s, a);
+    else if (tdt == ROPE_DTYPE_F16)
+        hipLaunchKernelGGL((rope_proj_sq_kernel<DT, ROPE_DTYPE_F16, EPI>), dim3(grid), block, 0, s, a);
+    else
+        hipLaunchKernelGGL((rope_proj_sq_kernel<DT, ROPE_DTYPE_F32, EPI>), dim3(grid), block, 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_proj_sq_epi(const ProjArgs& a, int tdt, uint32_t grid, hipStream_t s)
+{
+    switch (a.epi) {
+    case 0: return launch_proj_sq<DT, 0>(a, tdt, grid, s);
+    case 1: return launch_proj_sq<DT, 1>(a, tdt, grid, s);
+    default: return launch_proj_sq<DT, -1>(a, tdt, grid, s);
+    }
+}
+
 rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void* w, rope_dtype_t dtype,
                        const int64_t y_shape[4], int64_t K,
                        const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
@@ -1006,12 +1029,16 @@ rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void*
     a.start = (int32_t)p.start;
     a.L = (int32_t)p.L;
     a.half = p.L > 0 ? (int32_t)p.half : 1;
-    // block tiles of whole heads, or of part of one wider head: 192 lanes
+    // Square 256 x 256 tiles when K is a whole number of stage pairs (128 k)
+    // and every rotation group lies within one 256-lane column tile;
+    // otherwise tiles of whole heads, or of part of one wider head: 192 lanes
     // (384 tokens) for heads of a multiple of 3 lanes, else 128 lanes (256
-    // tokens)
-    const int BN = (int)proj_tile_lanes(p.D);
-    const int BM = BN == 192 ? ProjTile<192>::BM : ProjTile<128>::BM;
-    const int threads = BN == 192 ? ProjTile<192>::THREADS : ProjTile<128>::THREADS;
+    // tokens).
+    const bool sq = a.K % (2 * kProjBK) == 0 &&
+                    proj_groups_in_column_tiles(p.D, (int64_t)a.N, p.start, p.L, a.half, ProjSq::BN);
+    const int BN = sq ? ProjSq::BN : (int)proj_tile_lanes(p.D);
+    const int BM = sq ? ProjSq::BM : BN == 192 ? ProjTile<192>::BM : ProjTile<128>::BM;
+    const int threads = sq ? ProjSq::THREADS : BN == 192 ? ProjTile<192>::THREADS : ProjTile<128>::THREADS;
     const int64_t MB = (a.M + BM - 1) / BM, NB = (a.N + BN - 1) / BN;
     // the dispatch packet holds the grid in work-items as a 32-bit number
     if (MB * NB > (int64_t)(0xFFFFFFFFull / threads))
@@ -1035,11 +1062,39 @@ rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void*
         for (int k = 0; k < 3 && f; ++k) f = p.t1[k] % per == 0 && p.t2[k] % per == 0;
         a.fast = f ? 1 : 0;
     }
+    // The square tiles' epilogue: the vector epilogue when the slice is
+    // whole vectors (fast) whose partners are in the vector (interleave) or
+    // whole vectors away within one wave's 128 lanes, with the tables' rows
+    // staged in LDS when both tables are shared by all heads and a row's L
+    // values take 16, 32, 64 or 128 bytes that 32-bit byte offsets reach;
+    // otherwise the general one.
+    a.epi = -1;
+    a.tab_crl = -1;
+    if (sq) {
+        if (p.L == 0) {
+            a.epi = 0;
+        } else if (a.fast && (a.half == 1 || proj_groups_in_column_tiles(p.D, (int64_t)a.N, p.start, p.L, a.half,
+                                                                          ProjSq::BN / 2))) {
+            a.epi = a.half == 1 ? 0 : 1;
+            if (p.t1[2] == 0 && p.t2[2] == 0) {
+                const int64_t row = p.L * p.tesize;
+                int crl = -1;
+                for (int k = 0; k < 4; ++k)
+                    if (row == (int64_t)16 << k) crl = k;
+                const int64_t reach1 = ((p.B - 1) * p.t1[0] + (p.S - 1) * p.t1[1] + p.L) * p.tesize;
+                const int64_t reach2 = ((p.B - 1) * p.t2[0] + (p.S - 1) * p.t2[1] + p.L) * p.tesize;
+                if (crl >= 0 && reach1 <= (int64_t)UINT32_MAX && reach2 <= (int64_t)UINT32_MAX) a.tab_crl = crl;
+            }
+        }
+    }
     const uint32_t grid = (uint32_t)(MB * NB);
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     const int tdt = p.L > 0 ? p.tdtype : (int)ROPE_DTYPE_BF16;
-    if (q.in_dtype == ROPE_DTYPE_BF16)
+    if (sq)
+        err = q.in_dtype == ROPE_DTYPE_BF16 ? launch_proj_sq_epi<ROPE_DTYPE_BF16>(a, tdt, grid, s)
+                                            : launch_proj_sq_epi<ROPE_DTYPE_F16>(a, tdt, grid, s);
+    else if (q.in_dtype == ROPE_DTYPE_BF16)
         err = BN == 192 ? launch_proj<ROPE_DTYPE_BF16, 192>(a, tdt, grid, s)
                         : launch_proj<ROPE_DTYPE_BF16, 128>(a, tdt, grid, s);
     else

@@ -3,6 +3,7 @@
 // x and table dtypes is accepted (r1 and r2 share one).
 #include "rope_plan.hpp"
 
+#include <algorithm>
 #include <limits>
 
 namespace rope {
@@ -341,6 +342,24 @@ bool proj_groups_in_tiles(int64_t Dh, int64_t start, int64_t L, int64_t half)
     if (Dh <= bn || L == 0 || half == 1) return true;   // whole heads per tile, or pairs of adjacent lanes
     for (int64_t lo = start; lo < start + L; lo += 2 * half)
         if (lo / bn != (lo + 2 * half - 1) / bn) return false;
+    return true;
+}
+
+bool proj_groups_in_column_tiles(int64_t Dh, int64_t N, int64_t start, int64_t L, int64_t half, int64_t kTile)
+{
+    if (L == 0) return true;
+    const int64_t g = 2 * half;                        // lanes per rotation group
+    if (g > kTile) return false;
+    // groups on a grid of g lanes in every head never straddle a tile edge
+    if (kTile % g == 0 && start % g == 0 && Dh % g == 0) return true;
+    // head h's groups start at h*Dh + start + j*g; the offsets mod kTile
+    // repeat after kTile / gcd(Dh, kTile) heads
+    int64_t a = Dh, b = kTile;
+    while (b != 0) { const int64_t r = a % b; a = b; b = r; }
+    const int64_t heads = std::min(N / Dh, kTile / a);
+    for (int64_t h = 0; h < heads; ++h)
+        for (int64_t lo = h * Dh + start; lo < h * Dh + start + L; lo += g)
+            if (lo / kTile != (lo + g - 1) / kTile) return false;
     return true;
 }
 

@@ -120,6 +120,12 @@ int64_t proj_tile_lanes(int64_t Dh);
 // tile: every group of 2*half lanes of the slice (a rotate_half pair's or a
 // coefficient part pair's span) within one tile; interleave (half 1) always.
 bool proj_groups_in_tiles(int64_t Dh, int64_t start, int64_t L, int64_t half);
+// Whether every rotation group of every head's slice lies within one column
+// tile of `tile` lanes (tiles start at multiples of `tile`; N = heads * Dh
+// lanes in all): the square-tile projection kernel needs each group's
+// partners in its own 256-lane tile, and its register epilogue in its own
+// wave's 128 lanes.
+bool proj_groups_in_column_tiles(int64_t Dh, int64_t N, int64_t start, int64_t L, int64_t half, int64_t tile);
 
 // Checks, in order: the scalar arguments of make_plan on y's shape (with the
 // output type); input type bf16 or fp16; output type the inputs' type or

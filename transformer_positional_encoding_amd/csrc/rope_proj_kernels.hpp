@@ -136,6 +136,15 @@ struct ProjArgs {
     // is in the vector (interleave) or a whole vector away (half a multiple
     // of 8), and its 8 cos and 8 sin values are 16-byte aligned in the tables
     int32_t fast;
+    // square tiles' epilogue: -1 the general one (any geometry); 0 the
+    // vector epilogue, partners in the vector (interleave, or no slice); 1
+    // the vector epilogue, partners `half` lanes (whole vectors) away
+    int32_t epi;
+    // vector epilogue: >= 0 when the table rows of the tile's tokens go to
+    // LDS during the last K stage, 2^tab_crl 16-byte chunks per row (the
+    // slice's L lanes; the same row for every head); -1 reads them from the
+    // tables
+    int32_t tab_crl;
     int32_t MB, NB;        // block tiles along M and N
     int32_t group_m;       // raster: groups of group_m M-tiles walk all N-tiles
     int32_t xcd_chunk;     // blocks [0, 8*xcd_chunk) are dealt to the XCDs in contiguous chunks
@@ -450,6 +459,491 @@ __global__ void __launch_bounds__(ProjTile<BN>::THREADS)
             }
         }
         __syncthreads();                               // the half's rows are read before the next is written
+    }
+}
+
+}  // namespace
+}  // namespace rope
+
+namespace rope {
+namespace {
+
+// ---------------------------------------------------------------------------
+// Square tiles: 256 tokens x 256 output lanes per block, 4 waves (one per
+// SIMD) of 128 x 128, each holding 4 x 4 accumulators of 32 x 32 fp32 (256
+// registers, the accumulation registers of the wave). With one wave per SIMD
+// nothing hides a stall, so the K loop is software-pipelined by hand: every
+// MFMA of a 16-k step is paired with at most one LDS fragment read for the
+// next step and one direct global-to-LDS load for the next stage, in a fixed
+// order that the scheduler may not change. A stage's 16 loads per wave are
+// spread over its first 32 MFMAs (one every 64 MFMA cycles per wave, about
+// the rate at which the CU accepts them from its four waves), so no wave
+// waits at the head of a stage for its loads to be accepted; they then have
+// the rest of the stage to land. The accumulators are transposed (MFMA A =
+// w fragment, B = x fragment): lane l holds token l%32 and 4 consecutive
+// output lanes per register group, so each goes to the epilogue staging as
+// one 16-byte LDS write.
+// The tile is not aligned to heads: the epilogue finds each vector's head
+// from its column, and the host takes this kernel only when no rotation
+// group of the slice straddles two 256-lane tiles.
+// ---------------------------------------------------------------------------
+struct ProjSq {
+    static constexpr int BM = 256, BN = 256;
+    static constexpr int THREADS = 256;
+    static constexpr int STAGE = (BM + BN) * kProjBK * 2;   // 64 KiB
+    static constexpr int LW = (BM + BN) / 8 / 4;             // 16 wave loads per stage
+    static constexpr int LDC = BN + 4;                        // staging pitch: rows 16 bytes apart mod 128
+    static constexpr int RH = BM / 2;                         // rows per epilogue half
+    static constexpr int EPI = RH * LDC * 4;
+    static constexpr int LDS = 2 * STAGE > EPI ? 2 * STAGE : EPI;
+    static_assert(LDS <= 160 * 1024, "LDS per block");
+    static constexpr int RPP = THREADS / 8;                   // rows per epilogue pass
+    static constexpr int PR = RH / RPP;                       // passes per half
+    static constexpr int VI = BN / 64;                        // vectors per thread and row
+    // the vector epilogue: table rows in stage slot 0, then each wave's 32 x
+    // 128 fp32 staging rows of LDW floats (rows 16 bytes apart modulo 128)
+    static constexpr int LDW = 132;
+    static_assert(STAGE + 4 * 32 * LDW * 4 <= LDS, "vector epilogue staging");
+    static_assert(2 * 256 * 128 <= STAGE, "table rows of up to 128 bytes in slot 0");
+};
+
+// The square tiles' vector epilogue, for slices of whole 8-lane vectors whose
+// partners are in the vector (interleave, PV = false) or a whole number of
+// vectors away (PV = true, any half that is a multiple of 8; the host keeps
+// every group inside one wave's 128 lanes). Each wave works on its own
+// 128 tokens x 128 output lanes, in four quarters of 32 tokens (token tile
+// q), with no barrier: a wave's LDS operations complete in order, so its
+// reads of a quarter see its writes and precede its next quarter's writes.
+//  1. The wave writes its accumulators for the quarter to its own LDS
+//     region as fp32, straight from the accumulation registers (16-byte
+//     writes; lane l of acc[nt][q] holds 4 consecutive output lanes of token
+//     l%32). Staging row l%32 of 132 floats (rows 16 bytes apart modulo 128,
+//     so the 8 rows one write cycle serves meet distinct banks).
+//  2. Lane l takes column vector 8*(l%8) + 64G of rows l/8 + 8k (k < 4) for
+//     both 64-lane halves G (8 lanes of a row store one 128-byte line of
+//     16-bit output). A vector in the slice is rotated with its partner (in
+//     the vector, or `half` lanes away in the same staging row) and its 8
+//     cos and 8 sin values, then rounded once. Whether a vector is rotated
+//     depends only on its column, so for a slice of whole 64-lane groups
+//     (MLA's rope lanes) it is the same for every lane of an instruction.
+// The tables come from LDS when the host staged them there during the last
+// K stage (tab_crl >= 0: [table][token][L lanes], 16-byte chunks of a row
+// XOR-swizzled by the token's low bits), else from global memory.
+template <int DT, int TT, bool PV>
+__device__ __forceinline__ void proj_sq_epilogue_vec(const ProjArgs& a, const f32x16 (&acc)[4][4], uint16_t* smem,
+                                                     int32_t m0, int32_t n0, int wm, int wn, int wave, int lane)
+{
+    constexpr int LDW = ProjSq::LDW;                    // staging row pitch in floats
+    constexpr int TS = TT == ROPE_DTYPE_F32 ? 4 : 2;   // table element bytes
+    const int fr = lane & 31, hw = lane >> 5;
+    const uint8_t* tabs = reinterpret_cast<const uint8_t*>(smem);
+    float* Cs = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(smem) + ProjSq::STAGE) + wave * 32 * LDW;
+    const bool tab_lds = a.tab_crl >= 0;
+    const int crl = tab_lds ? a.tab_crl : 0, crm = (1 << crl) - 1;
+    // the lane's column vector in each 64-lane half G of the wave's 128
+    // lanes, and its place in the slice
+    const int vl = lane & 7, lr0 = lane >> 3;
+    int32_t colg[2], rel0g[2];
+    int64_t hn1g[2], hn2g[2];
+    bool liveg[2], rotg[2], firstg[2];
+#pragma unroll
+    for (int G = 0; G < 2; ++G) {
+        colg[G] = n0 + wn * 128 + 64 * G + 8 * vl;
+        const int32_t hd = (int32_t)fast_div((uint32_t)colg[G], a.dh_div);
+        rel0g[G] = colg[G] - hd * a.Dh - a.start;
+        hn1g[G] = (int64_t)hd * a.t1n;
+        hn2g[G] = (int64_t)hd * a.t2n;
+        liveg[G] = colg[G] < a.N;
+        rotg[G] = liveg[G] && a.L > 0 && rel0g[G] >= 0 && rel0g[G] < a.L;
+        firstg[G] = !PV || rel0g[G] % (2 * a.half) < a.half;   // first half of its group: partner term negated
+    }
+    // 8 table values of token row tr (tile row) and absolute token m at
+    // slice lane rel0 (head offsets hn1, hn2)
+    auto tab8 = [&](int table, int tr, int32_t m, int32_t rel0, int64_t hn1, int64_t hn2, float (&f)[8]) {
+        if (tab_lds) {
+            const int byte = rel0 * TS;
+            const uint8_t* row = tabs + (table << (12 + crl)) + (tr << (4 + crl));
+            if constexpr (TT == ROPE_DTYPE_F32) {
+                const v4u q0 = *reinterpret_cast<const v4u*>(row + (((byte >> 4) ^ (tr & crm)) << 4));
+                const v4u q1 = *reinterpret_cast<const v4u*>(row + ((((byte >> 4) + 1) ^ (tr & crm)) << 4));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    f[k] = __uint_as_float(q0[k]);
+                    f[4 + k] = __uint_as_float(q1[k]);
+                }
+            } else {
+                const v4u q0 = *reinterpret_cast<const v4u*>(row + (((byte >> 4) ^ (tr & crm)) << 4));
+                Lanes<TT> T;
+                T.unpack(q0);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) f[k] = T.v[k];
+            }
+        } else {
+            const int32_t mc = min(m, a.M - 1);
+            const int32_t b = (int32_t)fast_div((uint32_t)mc, a.s_div), sp = mc - b * a.S;
+            ProjTab8<TT> q;
+            q.load(table ? a.r2 : a.r1,
+                   table ? b * a.t2b + sp * a.t2s + hn2 + rel0 : b * a.t1b + sp * a.t1s + hn1 + rel0);
+            q.widen(f);
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        // 1. the quarter's accumulators to LDS, straight from the
+        //    accumulation registers (q is a constant here: a loop over q
+        //    kept as a loop reads every accumulator into VGPRs each time)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const f32x16& c = acc[nt][q];
+                *reinterpret_cast<float4*>(Cs + fr * LDW + nt * 32 + 8 * g + 4 * hw) =
+                    float4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+            }
+        // 2. the quarter's 32 rows of the wave's 128 lanes
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int G = 0; G < 2; ++G) {
+                const int sr = lr0 + 8 * k;                              // staging row
+                const int tr = wm * 128 + q * 32 + sr;                   // tile row
+                const int32_t m = m0 + tr;
+                const int c8 = 64 * G + 8 * vl;                          // first float of the vector
+                const float* crow = Cs + sr * LDW;
+                float val[8];
+                {
+                    const float4 q0 = *reinterpret_cast<const float4*>(crow + c8);
+                    const float4 q1 = *reinterpret_cast<const float4*>(crow + c8 + 4);
+                    val[0] = q0.x; val[1] = q0.y; val[2] = q0.z; val[3] = q0.w;
+                    val[4] = q1.x; val[5] = q1.y; val[6] = q1.z; val[7] = q1.w;
+                }
+                if (rotg[G]) {
+                    float cc[8], ss[8], xp[8];
+                    tab8(0, tr, m, rel0g[G], hn1g[G], hn2g[G], cc);
+                    tab8(1, tr, m, rel0g[G], hn1g[G], hn2g[G], ss);
+                    if constexpr (PV) {
+                        const int pc = c8 + (firstg[G] ? a.half : -a.half);
+                        const float4 p0 = *reinterpret_cast<const float4*>(crow + pc);
+                        const float4 p1 = *reinterpret_cast<const float4*>(crow + pc + 4);
+                        xp[0] = p0.x; xp[1] = p0.y; xp[2] = p0.z; xp[3] = p0.w;
+                        xp[4] = p1.x; xp[5] = p1.y; xp[6] = p1.z; xp[7] = p1.w;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            val[e] = rotate_own<false>(val[e], xp[e], cc[e], ss[e], firstg[G]);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) xp[e] = val[e ^ 1];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            val[e] = rotate_own<false>(val[e], xp[e], cc[e], ss[e], (e & 1) == 0);
+                    }
+                }
+                if (m < a.M && liveg[G]) {
+                    const int64_t yo = (int64_t)m * a.N + colg[G];
+                    if (a.ydt == ROPE_DTYPE_F32) {
+                        v4u* yp = reinterpret_cast<v4u*>(static_cast<float*>(a.y) + yo);
+                        __builtin_nontemporal_store(v4u{__float_as_uint(val[0]), __float_as_uint(val[1]),
+                                                        __float_as_uint(val[2]), __float_as_uint(val[3])}, yp);
+                        __builtin_nontemporal_store(v4u{__float_as_uint(val[4]), __float_as_uint(val[5]),
+                                                        __float_as_uint(val[6]), __float_as_uint(val[7])}, yp + 1);
+                    } else {
+                        Lanes<DT> Y;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) Y.v[e] = val[e];
+                        __builtin_nontemporal_store(Y.pack(),
+                                                    reinterpret_cast<v4u*>(static_cast<uint16_t*>(a.y) + yo));
+                    }
+                }
+            }
+    }
+}
+
+// EPI: the epilogue (ProjArgs::epi): -1 the general one (any geometry), 0
+// the vector epilogue with partners in the vector, 1 with partners whole
+// vectors away (a kernel of its own each: one kernel holding several
+// epilogues spills the accumulators)
+template <int DT, int TT, int EPI>
+__global__ void __launch_bounds__(ProjSq::THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+    rope_proj_sq_kernel(ProjArgs a)
+{
+    using T_ = ProjSq;
+    constexpr int BM = T_::BM, BN = T_::BN, LW = T_::LW, LDC = T_::LDC;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[T_::LDS / 2];
+
+    int32_t mb, nb;
+    proj_tile(a, mb, nb);
+    const int32_t m0 = mb * BM;
+    const int32_t n0 = nb * BN;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave & 1, wn = wave >> 1;
+
+    // ---------------------------------------------------------------- loads
+    // A stage: rows 0..255 of x then rows 0..255 of w, 128 bytes each; waves
+    // 0 and 1 load x rows [128*wave, +128), waves 2 and 3 w rows [128*(wave-2),
+    // +128). Load i of a wave fills its rows 8i..8i+7; lane l writes row
+    // 8i + l/8 at 16-byte slot l%8, which holds k-vector (l%8) ^ proj_swz(row).
+    // Rows past M or N re-read the last row (in bounds); their results are
+    // never stored. Offsets are unsigned 32-bit bytes (operands below 2^31
+    // elements).
+    const bool wx = wave < 2;
+    const uint16_t* src = wx ? a.x : a.w;
+    uint32_t goff[LW];
+#pragma unroll
+    for (int i = 0; i < LW; ++i) {
+        const int row = (wave & 1) * 128 + 8 * i + (lane >> 3);
+        const int kv = (lane & 7) ^ proj_swz(row & 31);
+        const int32_t g = wx ? min(m0 + row, a.M - 1) : min(n0 + row, a.N - 1);
+        goff[i] = ((uint32_t)g * (uint32_t)a.K + (uint32_t)(kv * 8)) * 2u;
+    }
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint16_t*)smem);
+    const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(smem_lds + wave * LW * 1024);
+    auto load1 = [&](int32_t kt, int slot, int i) {
+        proj_dma16(src + kt * kProjBK, goff[i], wave_lds + (uint32_t)(slot * T_::STAGE) + i * 1024);
+    };
+
+    // ---------------------------------------------------------------- fragments
+    // x row r = wm*128 + mt*32 + lane%32, w row BM + wn*128 + nt*32 + lane%32;
+    // k-vector kv = 2*kk + lane/32 at slot kv ^ proj_swz(lane%32)
+    const int fr = lane & 31;
+    const int sw = proj_swz(fr);
+    const int a_row = (wm * 128 + fr) * kProjBK;
+    const int b_row = (BM + wn * 128 + fr) * kProjBK;
+    v4u fa[2][4], fb[2][4];
+    // fragment read q of step kk (q < 8, in the order the MFMAs use them:
+    // w fragment 0, x fragments 0..3, w fragments 1..3)
+    auto read1 = [&](int slot, int kk, int buf, int q) {
+        const uint16_t* S0 = smem + slot * (T_::STAGE / 2);
+        const int s16 = ((2 * kk + (lane >> 5)) ^ sw) * 8;
+        if (q == 0) fb[buf][0] = *reinterpret_cast<const v4u*>(S0 + b_row + s16);
+        else if (q <= 4) fa[buf][q - 1] = *reinterpret_cast<const v4u*>(S0 + a_row + (q - 1) * 32 * kProjBK + s16);
+        else fb[buf][q - 4] = *reinterpret_cast<const v4u*>(S0 + b_row + (q - 4) * 32 * kProjBK + s16);
+    };
+
+    f32x16 acc[4][4];   // [nt][mt]: rows are output lanes, columns tokens
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+    // One stage: 4 steps of 16 k, 16 MFMAs each (nt-major). Step kk reads the
+    // fragments of step kk+1 (buffer (kk+1)&1); steps 0 and 1 issue the next
+    // stage's loads, one per even MFMA; step 3 waits for those loads and for
+    // its own fragment reads, meets the other waves at the barrier halfway
+    // through, and reads the next stage's first fragments after it.
+    // The vector epilogue's table rows (slice lanes [0, L) of the cos and
+    // sin rows of the tile's 256 tokens, 2^tab_crl chunks each) go to ring
+    // slot 0 during the last stage, whose slot 0 is free: wave load i of
+    // wave w fills chunk positions p = (2^(crl+1)*w + i)*64 + lane of
+    // [table][token][chunk slot]; slot cs of token tr holds chunk
+    // cs ^ (tr % 2^crl). Rows past M re-read the last token's row.
+    const int ntab = EPI >= 0 && a.L > 0 && a.tab_crl >= 0 ? 2 << a.tab_crl : 0;   // loads per wave
+    auto tab_dma = [&](int i) {
+        const int crl = a.tab_crl;
+        const int li = __builtin_amdgcn_readfirstlane(wave * (2 << crl) + i);
+        const int table = li >> (2 + crl);             // 4*2^crl wave loads per table
+        const int pos = ((li << 6) + lane) & ((256 << crl) - 1);
+        const int tr = pos >> crl;
+        const int c = (pos & ((1 << crl) - 1)) ^ (tr & ((1 << crl) - 1));
+        const int32_t mc = min(m0 + tr, a.M - 1);
+        const int32_t b = (int32_t)fast_div((uint32_t)mc, a.s_div), sp = mc - b * a.S;
+        const int64_t o = table ? b * a.t2b + sp * a.t2s : b * a.t1b + sp * a.t1s;
+        constexpr int TS = TT == ROPE_DTYPE_F32 ? 4 : 2;
+        const uint32_t voff = (uint32_t)((o + c * (16 / TS)) * TS);   // the host bounds it below 2^32
+        proj_dma16(table ? a.r2 : a.r1, voff, smem_lds + (uint32_t)(li * 1024));
+    };
+    auto stage = [&](auto slot_c, auto more_c, int32_t kt) {
+        constexpr int slot = decltype(slot_c)::value;
+        constexpr bool more = decltype(more_c)::value;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (kk == 3 && j == 8 && more) {
+                    proj_wait_vm<0>();
+                    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0), vmcnt and expcnt free
+                    __builtin_amdgcn_s_barrier();
+                    asm volatile("" ::: "memory");
+                }
+                const int nt = j >> 2, mt = j & 3;
+                acc[nt][mt] = proj_mfma<DT>(fb[cur][nt], fa[cur][mt], acc[nt][mt]);
+                if (more && kk < 2 && (j & 1) == 0) load1(kt + 1, slot ^ 1, kk * 8 + (j >> 1));
+                if constexpr (!more && EPI >= 0)
+                    if (kk < 2 && (j & 1) == 0 && kk * 8 + (j >> 1) < ntab) tab_dma(kk * 8 + (j >> 1));
+                if (kk < 3 && (j & 1)) read1(slot, kk + 1, nxt, j >> 1);
+                if (kk == 3 && j >= 8 && more) read1(slot ^ 1, 0, nxt, j - 8);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    };
+
+    // K is a whole number of stage pairs (the host checks): the last pair
+    // ends the loop without a branch on the stage count
+    const int32_t KT = a.K / kProjBK;
+#pragma unroll
+    for (int i = 0; i < LW; ++i) load1(0, 0, i);
+    proj_wait_vm<0>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int q = 0; q < 8; ++q) read1(0, 0, 0, q);
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using More = std::true_type;
+    using Last = std::false_type;
+    int32_t kt = 0;
+    for (; kt + 2 < KT; kt += 2) {
+        stage(S0{}, More{}, kt);
+        stage(S1{}, More{}, kt + 1);
+    }
+    stage(S0{}, More{}, kt);
+    stage(S1{}, Last{}, kt + 1);
+    proj_wait_vm<0>();                                 // this wave's table rows are in LDS
+    __syncthreads();                                   // every wave is done with the ring
+
+    if constexpr (EPI >= 0) {
+        proj_sq_epilogue_vec<DT, TT, EPI == 1>(a, acc, smem, m0, n0, wm, wn, wave, lane);
+        return;
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    // Half h stages accumulator columns mt = 2h, 2h+1 of every wave: tile
+    // rows wm*128 + h*64 + [0, 64) at staging row lr = wm*64 + [0, 64).
+    float* Cs = reinterpret_cast<float*>(smem);        // [RH][LDC]
+    const int tv = t & 7, tr = t >> 3;
+    const int g2 = 2 * a.half;
+    int c0[T_::VI], hl[T_::VI], rel0[T_::VI];
+    bool live_v[T_::VI], rot[T_::VI];
+#pragma unroll
+    for (int i = 0; i < T_::VI; ++i) {
+        c0[i] = 8 * (tv + 8 * i);
+        hl[i] = (int)fast_div((uint32_t)(n0 + c0[i]), a.dh_div);
+        rel0[i] = n0 + c0[i] - hl[i] * a.Dh - a.start;
+        live_v[i] = n0 + c0[i] < a.N;
+        rot[i] = live_v[i] && a.L > 0 && rel0[i] < a.L && rel0[i] + 8 > 0;
+    }
+    // table values prefetched, before the half's accumulators go to LDS, for
+    // every vector of a thread's rows (16-bit tables) or the first two (fp32
+    // tables, which would not fit the registers); the rest read on demand
+    constexpr int VP = TT == ROPE_DTYPE_F32 ? 2 : T_::VI;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int64_t m[T_::PR], o1[T_::PR], o2[T_::PR];
+        ProjTab8<TT> pc[T_::PR][VP], ps[T_::PR][VP];
+#pragma unroll
+        for (int p = 0; p < T_::PR; ++p) {
+            const int lr = tr + p * T_::RPP;
+            m[p] = m0 + (lr >> 6) * 128 + h * 64 + (lr & 63);
+            const int32_t mc = (int32_t)min<int64_t>(m[p], a.M - 1);
+            const int32_t b = (int32_t)fast_div((uint32_t)mc, a.s_div), sp = mc - b * a.S;
+            o1[p] = b * a.t1b + sp * a.t1s;
+            o2[p] = b * a.t2b + sp * a.t2s;
+            if (a.fast) {
+#pragma unroll
+                for (int i = 0; i < VP; ++i)
+                    if (rot[i]) {
+                        pc[p][i].load(a.r1, o1[p] + (int64_t)hl[i] * a.t1n + rel0[i]);
+                        ps[p][i].load(a.r2, o2[p] + (int64_t)hl[i] * a.t2n + rel0[i]);
+                    }
+            }
+        }
+        // accumulator (nt, mt), register 4g + e of lane l: output lane
+        // nt*32 + 8g + 4*(l/32) + e, token mt*32 + l%32
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+            for (int ml = 0; ml < 2; ++ml)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x16& c = acc[nt][2 * h + ml];
+                    const int lr = wm * 64 + ml * 32 + fr;
+                    const int col = wn * 128 + nt * 32 + 8 * g + 4 * (lane >> 5);
+                    *reinterpret_cast<float4*>(Cs + lr * LDC + col) =
+                        float4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+                }
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < T_::PR; ++p) {
+            if (m[p] >= a.M) continue;
+            const float* crow = Cs + (tr + p * T_::RPP) * LDC;
+#pragma unroll
+            for (int i = 0; i < T_::VI; ++i) {
+                if (!live_v[i]) continue;
+                const int64_t yo = m[p] * a.N + n0 + c0[i];
+                if (rot[i] && !a.fast) {
+#pragma unroll 1
+                    for (int e = 0; e < 8; ++e) {
+                        const int rel = rel0[i] + e;
+                        float ye = crow[c0[i] + e];
+                        if (rel >= 0 && rel < a.L) {
+                            const bool f = rel % g2 < a.half;
+                            const float xpe = crow[c0[i] + e + (f ? a.half : -a.half)];
+                            const float ce = Store<TT>::load1(a.r1, o1[p] + (int64_t)hl[i] * a.t1n + rel);
+                            const float se = Store<TT>::load1(a.r2, o2[p] + (int64_t)hl[i] * a.t2n + rel);
+                            ye = rotate_own<false>(ye, xpe, ce, se, f);
+                        }
+                        if (a.ydt == ROPE_DTYPE_F32) Store<ROPE_DTYPE_F32>::store1(a.y, yo + e, ye);
+                        else Store<DT>::store1(a.y, yo + e, ye);
+                    }
+                    continue;
+                }
+                float val[8];
+                {
+                    const float4 q0 = *reinterpret_cast<const float4*>(crow + c0[i]);
+                    const float4 q1 = *reinterpret_cast<const float4*>(crow + c0[i] + 4);
+                    val[0] = q0.x; val[1] = q0.y; val[2] = q0.z; val[3] = q0.w;
+                    val[4] = q1.x; val[5] = q1.y; val[6] = q1.z; val[7] = q1.w;
+                }
+                if (rot[i]) {
+                    float cc[8], ss[8];
+                    if (i < VP) {
+                        pc[p][i < VP ? i : 0].widen(cc);
+                        ps[p][i < VP ? i : 0].widen(ss);
+                    } else {
+                        ProjTab8<TT> c1, s1;
+                        c1.load(a.r1, o1[p] + (int64_t)hl[i] * a.t1n + rel0[i]);
+                        s1.load(a.r2, o2[p] + (int64_t)hl[i] * a.t2n + rel0[i]);
+                        c1.widen(cc);
+                        s1.widen(ss);
+                    }
+                    float xp[8];
+                    bool first[8];
+                    if (a.half == 1) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            xp[e] = val[e ^ 1];
+                            first[e] = (e & 1) == 0;
+                        }
+                    } else {
+                        const bool f = rel0[i] % g2 < a.half;
+                        const float* pp = crow + c0[i] + (f ? a.half : -a.half);
+                        const float4 p0 = *reinterpret_cast<const float4*>(pp);
+                        const float4 p1 = *reinterpret_cast<const float4*>(pp + 4);
+                        xp[0] = p0.x; xp[1] = p0.y; xp[2] = p0.z; xp[3] = p0.w;
+                        xp[4] = p1.x; xp[5] = p1.y; xp[6] = p1.z; xp[7] = p1.w;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) first[e] = f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) val[e] = rotate_own<false>(val[e], xp[e], cc[e], ss[e], first[e]);
+                }
+                if (a.ydt == ROPE_DTYPE_F32) {
+                    v4u* yp = reinterpret_cast<v4u*>(static_cast<float*>(a.y) + yo);
+                    __builtin_nontemporal_store(v4u{__float_as_uint(val[0]), __float_as_uint(val[1]),
+                                                    __float_as_uint(val[2]), __float_as_uint(val[3])}, yp);
+                    __builtin_nontemporal_store(v4u{__float_as_uint(val[4]), __float_as_uint(val[5]),
+                                                    __float_as_uint(val[6]), __float_as_uint(val[7])}, yp + 1);
+                } else {
+                    Lanes<DT> Y;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) Y.v[e] = val[e];
+                    __builtin_nontemporal_store(Y.pack(), reinterpret_cast<v4u*>(static_cast<uint16_t*>(a.y) + yo));
+                }
+            }
+        }
+        __syncthreads();
     }
 }
 
