@@ -441,7 +441,8 @@ ROPE_API rope_status_t rope_partial_launch_info_pos(
  * to 1024 (a head over whole tiles of 192 or 128 lanes, such as MLA's 576-
  * lane compressed KV with its 64 rope lanes); or, for such a wide head, a
  * rotate_half or coefficient group of the slice (2 x its pair distance
- * lanes) that spans two tiles (ROPE_ERR_UNSUPPORTED);
+ * lanes) that spans two tiles, unless K is a multiple of 128 and every
+ * group lies in one 256-lane column tile of y (ROPE_ERR_UNSUPPORTED);
  * NULL y, x or w (ROPE_ERR_NULLPTR); y, x or w not 16-byte aligned or
  * sizes beyond 64-bit offsets (ROPE_ERR_INVALID); x or w of 2^31 elements
  * or more (ROPE_ERR_UNSUPPORTED); y overlapping x or w (ROPE_ERR_INVALID); then,
@@ -458,6 +459,39 @@ ROPE_API rope_status_t rope_proj_fwd(
     const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
     rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
     void* stream);
+
+/* Kernels of a projection's launch plan (rope_proj_launch_info). */
+#define ROPE_KERNEL_PROJ_HEADS 4  /* tiles of whole heads: 384 x 192 (12 waves) or 256 x 128 (8 waves) */
+#define ROPE_KERNEL_PROJ_SQUARE 5 /* 256 x 256 tiles, 4 waves of 128 x 128 */
+
+/*
+ * rope_proj_launch_info -- the launch plan rope_proj_fwd would use for
+ * these arguments (y, x and w themselves aside), for tests and profiling.
+ * Runs rope_proj_fwd's checks, with stand-ins for the y, x and w pointers
+ * that pass the NULL, alignment and overlap checks, and returns their
+ * status; on ROPE_OK, info (caller-owned, ROPE_LAUNCH_INFO_LEN elements)
+ * receives:
+ *   [0] ROPE_KERNEL_NONE (an empty y), ROPE_KERNEL_PROJ_HEADS or
+ *       ROPE_KERNEL_PROJ_SQUARE (K a multiple of 128 and every rotation
+ *       group of the slice inside one 256-lane column tile);
+ *   [1] blocks; [2] threads per block; [3] tokens and [4] output lanes per
+ *       block tile;
+ *   square tiles: [5] the epilogue: 0 the general one (any geometry), 1 the
+ *       vector epilogue with rotation partners in the 8-lane vector
+ *       (interleave, or no slice), 2 the vector epilogue with partners whole
+ *       vectors away inside one wave's 128 lanes; [6] 1 when the tables' rows
+ *       are staged in LDS during the K loop (both tables shared by all heads,
+ *       a row of L values 16, 32, 64 or 128 bytes).
+ * Entries that do not apply are 0. Launches nothing and touches no memory;
+ * table pointers are only compared with NULL and checked for alignment.
+ * NULL info is ROPE_ERR_NULLPTR.
+ */
+ROPE_API rope_status_t rope_proj_launch_info(
+    rope_dtype_t y_dtype, rope_dtype_t dtype, const int64_t y_shape[4], int64_t K,
+    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+    int64_t info[ROPE_LAUNCH_INFO_LEN]);
 
 /* ============================== status ============================== */
 

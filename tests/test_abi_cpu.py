@@ -436,10 +436,13 @@ def _proj(**kw):
     # heads wider than a tile: 320 is neither a multiple of 192 nor of 128
     (dict(y_shape=(1, 8, 1, 320)), rp.ROPE_ERR_UNSUPPORTED, "head dimension"),
     # a 384-lane head over two 192-lane tiles: rotate_half over lanes [0, 384)
-    # pairs lane j with j + 192, in the other tile; [128, 256) straddles too
+    # pairs lane j with j + 192, in the other tile (and wider than a 256-lane
+    # square tile); [160, 224) straddles lane 192 too, and with K = 64 (not a
+    # multiple of 128) there is no square tile to take it
     (dict(y_shape=(1, 8, 1, 384), r1_shape=(1, 8, 1, 384), r2_shape=(1, 8, 1, 384), r1_strides=(0, 384, 0, 1),
           r2_strides=(0, 384, 0, 1), mode=0, partial_slice=(0, 384)), rp.ROPE_ERR_UNSUPPORTED, "spans two column tiles"),
-    (dict(y_shape=(1, 8, 1, 384), mode=0, partial_slice=(160, 224)), rp.ROPE_ERR_UNSUPPORTED, "spans two column tiles"),
+    (dict(y_shape=(1, 8, 1, 384), mode=0, partial_slice=(160, 224), K=64), rp.ROPE_ERR_UNSUPPORTED,
+     "spans two column tiles"),
     # a coefficient's parts likewise: 4 parts of 32 over [160, 288) form groups [160, 224) and
     # [224, 288), the first across lane 192 (over [128, 256) the groups meet at 192 and are accepted)
     (dict(y_shape=(1, 8, 1, 384), r1_shape=(1, 8, 1, 128), r2_shape=(1, 8, 1, 128), r1_strides=(0, 128, 0, 1),
@@ -467,6 +470,8 @@ def test_projection_wide_heads_pass_the_checks():
     tiles), and a coefficient's groups inside a 384-lane head's second tile.
     Without a GPU the call then fails at the launch, past every check."""
     for kw in (dict(y_shape=(1, 8, 1, 576), mode=1, partial_slice=(512, 576)),
+               # [160, 224) crosses lane 192 of the head tiles but lies in the square tile [0, 256)
+               dict(y_shape=(1, 8, 1, 384), mode=0, partial_slice=(160, 224)),
                dict(y_shape=(1, 8, 1, 576), mode=0, partial_slice=(512, 576)),
                dict(y_shape=(1, 8, 3, 256), mode=0, partial_slice=(0, 64)),
                dict(y_shape=(1, 8, 1, 384), r1_shape=(1, 8, 1, 128), r2_shape=(1, 8, 1, 128),
@@ -482,3 +487,78 @@ def test_projection_noops_need_no_pointers():
     none = dict(y_ptr=None, x_ptr=None, w_ptr=None, r1_ptr=None, r2_ptr=None)
     assert _proj(y_shape=(0, 8, 2, 192), **none) == rp.ROPE_OK
     assert _proj(y_shape=(1, 8, 0, 192), **none) == rp.ROPE_OK
+
+
+def _proj_plan(**kw):
+    base = dict(y_dtype=2, dtype=2, y_shape=(4, 4096, 128, 192), K=1536, r1_ptr=0x4000000, r1_shape=(1, 4096, 1, 64),
+                r1_strides=(0, 64, 0, 1), r2_ptr=0x5000000, r2_shape=(1, 4096, 1, 64), r2_strides=(0, 64, 0, 1),
+                table_dtype=2, mode=1, partial_slice=(0, 64))
+    base.update(kw)
+    st, plan = rp.raw_proj_launch_info(*base.values())
+    assert st == rp.ROPE_OK, rp.last_error()
+    return plan
+
+
+def test_projection_plan_mla_q():
+    """The MLA Q projection (4 x 4096 tokens, K 1536, 128 heads of 192, rope
+    on lanes [0, 64) with one table row per token): 256 x 256 tiles (64 x 96
+    of them), the vector epilogue with the table rows staged in LDS; with
+    rotate_half the partners are 32 lanes (whole vectors) away."""
+    plan = _proj_plan()
+    assert plan == {"kernel": "square", "blocks": 64 * 96, "threads": 256, "tile_tokens": 256, "tile_lanes": 256,
+                    "epilogue": "vector", "tables_in_lds": True}
+    assert _proj_plan(mode=0)["epilogue"] == "vector_partner"
+    assert _proj_plan(partial_slice=None)["epilogue"] == "vector"          # the plain projection
+
+
+@pytest.mark.parametrize("kw,kernel,epilogue,lds", [
+    # K = 192: three stages, not a whole number of stage pairs -> tiles of whole heads (384 x 192)
+    (dict(K=192), "heads", None, False),
+    # whole 192-lane heads under rotate_half: head 1's group [192, 384) crosses lane 256
+    (dict(r1_shape=(1, 4096, 1, 192), r2_shape=(1, 4096, 1, 192), r1_strides=(0, 192, 0, 1),
+          r2_strides=(0, 192, 0, 1), mode=0, partial_slice=(0, 192)), "heads", None, False),
+    # heads of 128 with a 256-lane rotate_half group: inside the 256-lane tile, not inside a wave's 128
+    (dict(y_shape=(1, 64, 8, 256), r1_shape=(1, 64, 1, 256), r2_shape=(1, 64, 1, 256), r1_strides=(0, 256, 0, 1),
+          r2_strides=(0, 256, 0, 1), mode=0, partial_slice=(0, 256)), "square", "general", False),
+    # an odd start: not whole vectors -> the general epilogue
+    (dict(y_shape=(1, 64, 8, 64), r1_shape=(1, 64, 1, 32), r2_shape=(1, 64, 1, 32), r1_strides=(0, 32, 0, 1),
+          r2_strides=(0, 32, 0, 1), partial_slice=(3, 35)), "square", "general", False),
+    # tables per head (stride over heads): read per vector
+    (dict(r1_shape=(1, 4096, 128, 64), r2_shape=(1, 4096, 128, 64), r1_strides=(0, 8192, 64, 1),
+          r2_strides=(0, 8192, 64, 1)), "square", "vector", False),
+    # fp32 tables: a row of 64 lanes is 256 bytes, too wide to stage
+    (dict(table_dtype=0), "square", "vector", False),
+    # fp32 tables of 32 lanes (128 bytes) are staged
+    (dict(y_shape=(1, 64, 8, 64), r1_shape=(1, 64, 1, 32), r2_shape=(1, 64, 1, 32), r1_strides=(0, 32, 0, 1),
+          r2_strides=(0, 32, 0, 1), partial_slice=(0, 32), table_dtype=0), "square", "vector", True),
+    # per-batch rows (one per token) are staged too
+    (dict(r1_shape=(4, 4096, 1, 64), r2_shape=(4, 4096, 1, 64), r1_strides=(4096 * 64, 64, 0, 1),
+          r2_strides=(4096 * 64, 64, 0, 1)), "square", "vector", True),
+    # MLA's compressed KV: one 576-lane head, rope on its last 64 lanes (tile 2 of 3)
+    (dict(y_shape=(1, 4096, 1, 576), K=512, partial_slice=(512, 576)), "square", "vector", True),
+    # fp32 output takes the vector epilogue as well
+    (dict(y_dtype=0, mode=0), "square", "vector_partner", True),
+])
+def test_projection_plan_choices(kw, kernel, epilogue, lds):
+    plan = _proj_plan(**kw)
+    assert (plan["kernel"], plan["epilogue"], plan["tables_in_lds"]) == (kernel, epilogue, lds), plan
+
+
+def test_projection_plan_shapes_and_errors():
+    """Block counts follow the tile: 256 x 256 rounds both dimensions up;
+    the 384 x 192 tiles of whole heads likewise. Errors are the call's own
+    (same checks, same order); an empty y plans nothing; NULL info is an
+    error."""
+    p = _proj_plan(y_shape=(1, 300, 3, 128), r1_shape=(1, 300, 1, 64), r2_shape=(1, 300, 1, 64))
+    assert (p["kernel"], p["blocks"]) == ("square", 2 * 2)
+    p = _proj_plan(y_shape=(1, 300, 3, 192), r1_shape=(1, 300, 1, 64), r2_shape=(1, 300, 1, 64), K=64)
+    assert (p["kernel"], p["blocks"], p["threads"], p["tile_tokens"], p["tile_lanes"]) == ("heads", 1 * 3, 768,
+                                                                                           384, 192)
+    st, plan = rp.raw_proj_launch_info(2, 2, (1, 8, 2, 192), 96, 0x4000000, (1, 8, 1, 64), (0, 64, 0, 1),
+                                       0x5000000, (1, 8, 1, 64), (0, 64, 0, 1), 2, 1, (0, 64))
+    assert st == rp.ROPE_ERR_UNSUPPORTED and "multiple of 64" in rp.last_error()
+    st, plan = rp.raw_proj_launch_info(2, 2, (0, 8, 2, 192), 128, None, None, None, None, None, None, 2, 1, (0, 64))
+    assert st == rp.ROPE_OK and plan["kernel"] == "none"
+    st, plan = rp.raw_proj_launch_info(2, 2, (1, 8, 2, 192), 128, 0x4000000, (1, 8, 1, 64), (0, 64, 0, 1),
+                                       0x5000000, (1, 8, 1, 64), (0, 64, 0, 1), 2, 1, (0, 64), info_out=False)
+    assert st == rp.ROPE_ERR_NULLPTR

@@ -166,12 +166,57 @@ CASES = [
     (1, 130, 128, 3, 256, (0, 64), "rotate_half", "f16", "f16", "f16", "head"),
     (1, 90, 192, 2, 384, (192, 320), 4, "bf16", "bf16", "bf16", "token"),
     (2, 33, 64, 1, 512, (3, 35), "interleave", "bf16", "bf16", "bf16", "batch"),
+    # square tiles, fp32 tables too wide to stage in LDS (64 lanes x 4 bytes): read per vector
+    (2, 96, 256, 4, 128, (0, 64), "interleave", "bf16", "bf16", "f32", "token"),
+    # square tiles' general epilogue: 256-lane rotate_half groups fit the tile but not a wave's 128 lanes
+    (1, 40, 128, 2, 256, (0, 256), "rotate_half", "f16", "f16", "f16", "token"),
+    # whole 192-lane heads rotated: groups straddle 256-lane tiles, so tiles of whole heads
+    (1, 64, 256, 4, 192, (0, 192), "rotate_half", "bf16", "bf16", "bf16", "token"),
+    # a group across lane 192 of a 384-lane head (no 192-lane tile holds it) inside the 256-lane square tile
+    (1, 50, 128, 1, 384, (160, 224), "rotate_half", "bf16", "bf16", "bf16", "token"),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}xK{c[2]}-h{c[3]}x{c[4]}-{c[5]}-{c[6]}-{c[7]}-{c[8]}-{c[9]}-{c[10]}"
                                             for c in CASES])
 def test_projection_with_rotary_epilogue(case):
+    B, S, K, H, Dh, sl, mode, dt, out, tdt, layout = case
+    x, w, r1, r2, r1_dev, r2_dev = _case_inputs(case)
+    info = check_proj(x, w, r1, r2, H, mode, sl, out, f"proj {case}", r1_dev=r1_dev, r2_dev=r2_dev)
+    announce(f"  exact {info['exact_fraction']:.4f}, max err/bound {info['max_err_over_bound']:.3g}")
+    # the bound is loose (first-order, worst case); most 16-bit lanes match
+    # the oracle exactly (fp32 lanes differ in the last bits with the order)
+    if out != "f32":
+        assert info["exact_fraction"] > 0.9
+
+
+def test_projection_cases_cover_every_kernel_and_epilogue():
+    """The cases above run every projection kernel and epilogue: tiles of
+    whole heads, and square tiles with the general epilogue, the vector
+    epilogue (partners in the vector, or whole vectors away) with the table
+    rows staged in LDS and read from the tables (rope_proj_launch_info)."""
+    seen = set()
+    for case in CASES:
+        B, S, K, H, Dh, sl, mode, dt, out, tdt, layout = case
+        x, w, r1, r2, r1_dev, r2_dev = _case_inputs(case)
+        t1 = r1 if r1_dev is None else r1_dev
+        t2 = r2 if r2_dev is None else r2_dev
+        code = rp.MODES[mode] if isinstance(mode, str) else int(mode)
+        tcode = rp._dtype_code(t1) if t1.numel() else 2
+        st, plan = rp.raw_proj_launch_info(rp._dtype_code(torch.empty(0, dtype=TORCH[out])), rp._dtype_code(x),
+                                           (B, S, H, Dh), K, t1.data_ptr() or None, tuple(t1.shape),
+                                           tuple(t1.stride()), t2.data_ptr() or None, tuple(t2.shape),
+                                           tuple(t2.stride()), tcode, code, sl)
+        assert st == rp.ROPE_OK, (case, rp.last_error())
+        seen.add((plan["kernel"], plan["epilogue"], plan["tables_in_lds"]))
+    want = {("heads", None, False), ("square", "general", False), ("square", "vector", True),
+            ("square", "vector", False), ("square", "vector_partner", True), ("square", "vector_partner", False)}
+    assert want <= seen, sorted(want - seen)
+
+
+def _case_inputs(case):
+    """x, w, the CPU tables and (for the "offset" layout) device views of
+    them, for one entry of CASES."""
     B, S, K, H, Dh, sl, mode, dt, out, tdt, layout = case
     x = _rand((B, S, K), dt, 11, 0.5)
     w = _rand((H * Dh, K), dt, 12, 0.05)
@@ -191,12 +236,7 @@ def test_projection_with_rotary_epilogue(case):
             assert r1_dev.data_ptr() % 16 != 0
     else:
         r1 = r2 = torch.zeros((1, 1, 1, 0), dtype=TORCH[tdt])
-    info = check_proj(x, w, r1, r2, H, mode, sl, out, f"proj {case}", r1_dev=r1_dev, r2_dev=r2_dev)
-    announce(f"  exact {info['exact_fraction']:.4f}, max err/bound {info['max_err_over_bound']:.3g}")
-    # the bound is loose (first-order, worst case); most 16-bit lanes match
-    # the oracle exactly (fp32 lanes differ in the last bits with the order)
-    if out != "f32":
-        assert info["exact_fraction"] > 0.9
+    return x, w, r1, r2, r1_dev, r2_dev
 
 
 def test_plain_projection_matches_torch_matmul_closely():

@@ -103,6 +103,9 @@ def library() -> ctypes.CDLL:
         L.rope_proj_fwd.restype = ctypes.c_int
         L.rope_proj_fwd.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                     ctypes.POINTER(ctypes.c_int64), ctypes.c_int64] + _ENTRY_ARGTYPES[3:]
+        L.rope_proj_launch_info.restype = ctypes.c_int
+        L.rope_proj_launch_info.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                                            ctypes.c_int64] + _ENTRY_ARGTYPES[3:-1] + [ctypes.POINTER(ctypes.c_int64)]
         L.rope_status_string.restype = ctypes.c_char_p
         L.rope_status_string.argtypes = [ctypes.c_int]
         L.rope_last_error.restype = ctypes.c_char_p
@@ -278,6 +281,28 @@ def raw_proj_call(y_ptr, y_dtype: int, x_ptr, w_ptr, dtype: int, y_shape, K: int
     return library().rope_proj_fwd(y_ptr, y_dtype, x_ptr, w_ptr, dtype, _arr4(y_shape), int(K),
                                    r1_ptr, _arr4(r1_shape), _arr4(r1_strides), r2_ptr, _arr4(r2_shape),
                                    _arr4(r2_strides), table_dtype, mode, sl, stream)
+
+
+PROJ_KERNELS = {0: "none", 4: "heads", 5: "square"}
+PROJ_EPILOGUES = {0: "general", 1: "vector", 2: "vector_partner"}
+
+
+def raw_proj_launch_info(y_dtype: int, dtype: int, y_shape, K: int, r1_ptr, r1_shape, r1_strides, r2_ptr, r2_shape,
+                         r2_strides, table_dtype: int, mode: int, partial_slice, info_out: bool = True):
+    """rope_proj_launch_info with plain integers and sequences (None =
+    NULL): (status, plan dict or None). The plan names the projection kernel,
+    its tile and (square tiles) its epilogue; nothing is launched."""
+    sl = None if partial_slice is None else _I64x2(*partial_slice)
+    info = (ctypes.c_int64 * LAUNCH_INFO_LEN)() if info_out else None
+    st = library().rope_proj_launch_info(int(y_dtype), int(dtype), _arr4(y_shape), int(K), r1_ptr, _arr4(r1_shape),
+                                         _arr4(r1_strides), r2_ptr, _arr4(r2_shape), _arr4(r2_strides),
+                                         int(table_dtype), int(mode), sl, info)
+    if st != ROPE_OK or info is None:
+        return st, None
+    v = list(info)
+    return st, {"kernel": PROJ_KERNELS.get(v[0], v[0]), "blocks": v[1], "threads": v[2], "tile_tokens": v[3],
+                "tile_lanes": v[4], "epilogue": PROJ_EPILOGUES.get(v[5], v[5]) if v[0] == 5 else None,
+                "tables_in_lds": bool(v[6])}
 
 
 def last_error() -> str:

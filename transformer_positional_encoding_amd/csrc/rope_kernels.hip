@@ -998,20 +998,29 @@ hipError_t launch_proj_sq_epi(const ProjArgs& a, int tdt, uint32_t grid, hipStre
     }
 }
 
-rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void* w, rope_dtype_t dtype,
-                       const int64_t y_shape[4], int64_t K,
-                       const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
-                       const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
-                       rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2], void* stream)
-{
+// A projection call's checked plan, kernel arguments and kernel choice.
+struct ProjLaunch {
     ProjPlan q;
-    std::string why;
-    rope_status_t st = make_proj_plan(y, y_dtype, x, w, dtype, y_shape, K, r1, r1_shape, r1_strides, r2, r2_shape,
-                                      r2_strides, table_dtype, mode, partial_slice, &q, &why);
-    if (st != ROPE_OK) return set_error(st, why);
-    if (q.noop) return ROPE_OK;
-    const Plan& p = q.rope;
     ProjArgs a{};
+    bool sq = false;            // square 256 x 256 tiles (else tiles of whole heads)
+    int BM = 0, BN = 0, threads = 0;
+    uint32_t grid = 0;
+    int tdt = ROPE_DTYPE_BF16;  // table type the kernel is instantiated for
+};
+
+rope_status_t prepare_proj(void* y, rope_dtype_t y_dtype, const void* x, const void* w, rope_dtype_t dtype,
+                           const int64_t y_shape[4], int64_t K,
+                           const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                           const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                           rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2], ProjLaunch* P,
+                           std::string* why)
+{
+    ProjPlan& q = P->q;
+    rope_status_t st = make_proj_plan(y, y_dtype, x, w, dtype, y_shape, K, r1, r1_shape, r1_strides, r2, r2_shape,
+                                      r2_strides, table_dtype, mode, partial_slice, &q, why);
+    if (st != ROPE_OK || q.noop) return st;
+    const Plan& p = q.rope;
+    ProjArgs& a = P->a;
     a.x = static_cast<const uint16_t*>(q.x);
     a.w = static_cast<const uint16_t*>(q.w);
     a.y = q.y;
@@ -1034,15 +1043,18 @@ rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void*
     // otherwise tiles of whole heads, or of part of one wider head: 192 lanes
     // (384 tokens) for heads of a multiple of 3 lanes, else 128 lanes (256
     // tokens).
-    const bool sq = a.K % (2 * kProjBK) == 0 &&
+    const bool sq = P->sq = a.K % (2 * kProjBK) == 0 &&
                     proj_groups_in_column_tiles(p.D, (int64_t)a.N, p.start, p.L, a.half, ProjSq::BN);
-    const int BN = sq ? ProjSq::BN : (int)proj_tile_lanes(p.D);
-    const int BM = sq ? ProjSq::BM : BN == 192 ? ProjTile<192>::BM : ProjTile<128>::BM;
-    const int threads = sq ? ProjSq::THREADS : BN == 192 ? ProjTile<192>::THREADS : ProjTile<128>::THREADS;
+    const int BN = P->BN = sq ? ProjSq::BN : (int)proj_tile_lanes(p.D);
+    const int BM = P->BM = sq ? ProjSq::BM : BN == 192 ? ProjTile<192>::BM : ProjTile<128>::BM;
+    const int threads = P->threads = sq ? ProjSq::THREADS : BN == 192 ? ProjTile<192>::THREADS : ProjTile<128>::THREADS;
     const int64_t MB = (a.M + BM - 1) / BM, NB = (a.N + BN - 1) / BN;
     // the dispatch packet holds the grid in work-items as a 32-bit number
     if (MB * NB > (int64_t)(0xFFFFFFFFull / threads))
-        return set_error(ROPE_ERR_UNSUPPORTED, "the projection's grid exceeds one launch");
+    {
+        *why = "the projection's grid exceeds one launch";
+        return ROPE_ERR_UNSUPPORTED;
+    }
     a.MB = (int32_t)MB;
     a.NB = (int32_t)NB;
     // Measured on MI355X on the (4*4096 tokens, 1536) x (24576, 1536) MLA
@@ -1087,19 +1099,37 @@ rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void*
             }
         }
     }
-    const uint32_t grid = (uint32_t)(MB * NB);
+    P->grid = (uint32_t)(MB * NB);
+    P->tdt = p.L > 0 ? p.tdtype : (int)ROPE_DTYPE_BF16;
+    return ROPE_OK;
+}
+
+rope_status_t run_proj(void* y, rope_dtype_t y_dtype, const void* x, const void* w, rope_dtype_t dtype,
+                       const int64_t y_shape[4], int64_t K,
+                       const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                       const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                       rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2], void* stream)
+{
+    ProjLaunch P;
+    std::string why;
+    rope_status_t st = prepare_proj(y, y_dtype, x, w, dtype, y_shape, K, r1, r1_shape, r1_strides, r2, r2_shape,
+                                    r2_strides, table_dtype, mode, partial_slice, &P, &why);
+    if (st != ROPE_OK) return set_error(st, why);
+    if (P.q.noop) return ROPE_OK;
+    const ProjArgs& a = P.a;
+    const uint32_t grid = P.grid;
+    const int tdt = P.tdt;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
-    const int tdt = p.L > 0 ? p.tdtype : (int)ROPE_DTYPE_BF16;
-    if (sq)
-        err = q.in_dtype == ROPE_DTYPE_BF16 ? launch_proj_sq_epi<ROPE_DTYPE_BF16>(a, tdt, grid, s)
-                                            : launch_proj_sq_epi<ROPE_DTYPE_F16>(a, tdt, grid, s);
-    else if (q.in_dtype == ROPE_DTYPE_BF16)
-        err = BN == 192 ? launch_proj<ROPE_DTYPE_BF16, 192>(a, tdt, grid, s)
-                        : launch_proj<ROPE_DTYPE_BF16, 128>(a, tdt, grid, s);
+    if (P.sq)
+        err = P.q.in_dtype == ROPE_DTYPE_BF16 ? launch_proj_sq_epi<ROPE_DTYPE_BF16>(a, tdt, grid, s)
+                                              : launch_proj_sq_epi<ROPE_DTYPE_F16>(a, tdt, grid, s);
+    else if (P.q.in_dtype == ROPE_DTYPE_BF16)
+        err = P.BN == 192 ? launch_proj<ROPE_DTYPE_BF16, 192>(a, tdt, grid, s)
+                          : launch_proj<ROPE_DTYPE_BF16, 128>(a, tdt, grid, s);
     else
-        err = BN == 192 ? launch_proj<ROPE_DTYPE_F16, 192>(a, tdt, grid, s)
-                        : launch_proj<ROPE_DTYPE_F16, 128>(a, tdt, grid, s);
+        err = P.BN == 192 ? launch_proj<ROPE_DTYPE_F16, 192>(a, tdt, grid, s)
+                          : launch_proj<ROPE_DTYPE_F16, 128>(a, tdt, grid, s);
     if (err != hipSuccess) return set_error(ROPE_ERR_RUNTIME, std::string("kernel launch: ") + hipGetErrorString(err));
     return ROPE_OK;
 }
@@ -1394,6 +1424,36 @@ rope_status_t rope_proj_fwd(void* y, rope_dtype_t y_dtype, const void* x, const 
 {
     return rope::run_proj(y, y_dtype, x, w, dtype, y_shape, K, r1, r1_shape, r1_strides, r2, r2_shape, r2_strides,
                           table_dtype, mode, partial_slice, stream);
+}
+
+rope_status_t rope_proj_launch_info(rope_dtype_t y_dtype, rope_dtype_t dtype, const int64_t y_shape[4], int64_t K,
+                                    const void* r1, const int64_t r1_shape[4], const int64_t r1_strides[4],
+                                    const void* r2, const int64_t r2_shape[4], const int64_t r2_strides[4],
+                                    rope_dtype_t table_dtype, int64_t mode, const int64_t partial_slice[2],
+                                    int64_t info[ROPE_LAUNCH_INFO_LEN])
+{
+    if (info == nullptr) return rope::set_error(ROPE_ERR_NULLPTR, "info is NULL");
+    for (int i = 0; i < ROPE_LAUNCH_INFO_LEN; ++i) info[i] = 0;
+    // distinct, 16-byte aligned stand-ins for y, x and w, never dereferenced:
+    // the plan only compares them with NULL and checks alignment and overlap
+    static const uint64_t kNowhere = uint64_t(1) << 62;
+    void* y = reinterpret_cast<void*>(kNowhere);
+    const void* x = reinterpret_cast<const void*>(kNowhere * 2);
+    const void* w = reinterpret_cast<const void*>(kNowhere * 3);
+    rope::ProjLaunch P;
+    std::string why;
+    rope_status_t st = rope::prepare_proj(y, y_dtype, x, w, dtype, y_shape, K, r1, r1_shape, r1_strides, r2, r2_shape,
+                                          r2_strides, table_dtype, mode, partial_slice, &P, &why);
+    if (st != ROPE_OK) return rope::set_error(st, why);
+    if (P.q.noop) return ROPE_OK;
+    info[0] = P.sq ? ROPE_KERNEL_PROJ_SQUARE : ROPE_KERNEL_PROJ_HEADS;
+    info[1] = P.grid;
+    info[2] = P.threads;
+    info[3] = P.BM;
+    info[4] = P.BN;
+    info[5] = P.sq && P.a.epi >= 0 ? 1 + P.a.epi : 0;
+    info[6] = P.sq && P.a.epi >= 0 && P.q.rope.L > 0 && P.a.tab_crl >= 0 ? 1 : 0;
+    return ROPE_OK;
 }
 
 const char* rope_status_string(rope_status_t status)

@@ -393,7 +393,11 @@ rope_status_t make_proj_plan(void* y, rope_dtype_t out_dtype, const void* x, con
     if (!proj_head_dim_supported(Dh))
         return fail(ROPE_ERR_UNSUPPORTED, why,
                     "head dimension must be 32, 64, 96, 128 or 192, or a multiple of 192 or 128 up to 1024");
-    if (!proj_groups_in_tiles(Dh, q.rope.start, q.rope.L, q.rope.half))
+    // a rotation group must lie in one column tile of the kernel that takes
+    // the call: a tile of whole heads (or of part of a wider head), or, with
+    // K a multiple of 128, a 256-lane square tile
+    if (!proj_groups_in_tiles(Dh, q.rope.start, q.rope.L, q.rope.half) &&
+        !(K % 128 == 0 && proj_groups_in_column_tiles(Dh, y_shape[2] * Dh, q.rope.start, q.rope.L, q.rope.half, 256)))
         return fail(ROPE_ERR_UNSUPPORTED, why,
                     "a rotation group of the slice spans two column tiles of a head wider than the tile");
     if (y == nullptr) return fail(ROPE_ERR_NULLPTR, why, "y is NULL");
