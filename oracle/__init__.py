@@ -19,7 +19,13 @@ Storage convention: fp32 data is a ``numpy.float32`` array; fp16 and bf16
 data are ``numpy.uint16`` arrays holding the raw 16-bit patterns.
 
 Parity pins: every function here is pinned by ``tests/test_oracle_*.py``
-against closed forms, brute force and library conversions.
+against closed forms, brute force and library conversions. One reading is
+parity unpinned: a rotary coefficient c other than 2 and L (the MLA
+preprocess page, section 2, names qRotaryCoeff / kRotaryCoeff values 2, 4 and
+headDim with no formula). The oracle's rule for it -- the slice in c parts,
+part 2g paired lane by lane with part 2g+1 -- reduces to rotate_half at c = 2
+and to interleave at c = L, which are pinned; for other c the pins check that
+rule against restatements of itself, not against anything the pages fix.
 """
 from __future__ import annotations
 
