@@ -519,8 +519,8 @@ struct ProjSq {
 //     writes; lane l of acc[nt][q] holds 4 consecutive output lanes of token
 //     l%32). Staging row l%32 of 132 floats (rows 16 bytes apart modulo 128,
 //     so the 8 rows one write cycle serves meet distinct banks).
-//  2. Lane l takes column vector 8*(l%8) + 64G of rows l/8 + 8k (k < 4) for
-//     both 64-lane halves G (8 lanes of a row store one 128-byte line of
+//  2. Lane l takes column vector 8*(l%8) + 64G of rows l/8 + 8k (k < 4), one
+//     64-lane half G at a time (8 lanes of a row store one 128-byte line of
 //     16-bit output). A vector in the slice is rotated with its partner (in
 //     the vector, or `half` lanes away in the same staging row) and its 8
 //     cos and 8 sin values, then rounded once. Whether a vector is rotated
@@ -600,61 +600,70 @@ __device__ __forceinline__ void proj_sq_epilogue_vec(const ProjArgs& a, const f3
                 *reinterpret_cast<float4*>(Cs + fr * LDW + nt * 32 + 8 * g + 4 * hw) =
                     float4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
             }
-        // 2. the quarter's 32 rows of the wave's 128 lanes
+        // 2. the quarter's 32 rows of the wave's 128 lanes, one 64-lane half
+        //    G at a time: all four rows' LDS reads (values, partners, cos and
+        //    sin) go out before any arithmetic, inside one branch on
+        //    "rotated" (the same for every lane when the slice is whole
+        //    64-lane groups)
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
+        for (int G = 0; G < 2; ++G) {
+            const int c8 = 64 * G + 8 * vl;                              // first float of the vector
+            float val[4][8];
+            auto read8 = [&](const float* p, float (&v)[8]) {
+                const float4 q0 = *reinterpret_cast<const float4*>(p);
+                const float4 q1 = *reinterpret_cast<const float4*>(p + 4);
+                v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
+                v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+            };
 #pragma unroll
-            for (int G = 0; G < 2; ++G) {
-                const int sr = lr0 + 8 * k;                              // staging row
-                const int tr = wm * 128 + q * 32 + sr;                   // tile row
-                const int32_t m = m0 + tr;
-                const int c8 = 64 * G + 8 * vl;                          // first float of the vector
-                const float* crow = Cs + sr * LDW;
-                float val[8];
-                {
-                    const float4 q0 = *reinterpret_cast<const float4*>(crow + c8);
-                    const float4 q1 = *reinterpret_cast<const float4*>(crow + c8 + 4);
-                    val[0] = q0.x; val[1] = q0.y; val[2] = q0.z; val[3] = q0.w;
-                    val[4] = q1.x; val[5] = q1.y; val[6] = q1.z; val[7] = q1.w;
+            for (int k = 0; k < 4; ++k) read8(Cs + (lr0 + 8 * k) * LDW + c8, val[k]);
+            if (rotg[G]) {
+                float cc[4][8], ss[4][8], xp[4][8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int tr = wm * 128 + q * 32 + lr0 + 8 * k;     // tile row
+                    tab8(0, tr, m0 + tr, rel0g[G], hn1g[G], hn2g[G], cc[k]);
+                    tab8(1, tr, m0 + tr, rel0g[G], hn1g[G], hn2g[G], ss[k]);
+                    if constexpr (PV)
+                        read8(Cs + (lr0 + 8 * k) * LDW + c8 + (firstg[G] ? a.half : -a.half), xp[k]);
                 }
-                if (rotg[G]) {
-                    float cc[8], ss[8], xp[8];
-                    tab8(0, tr, m, rel0g[G], hn1g[G], hn2g[G], cc);
-                    tab8(1, tr, m, rel0g[G], hn1g[G], hn2g[G], ss);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
                     if constexpr (PV) {
-                        const int pc = c8 + (firstg[G] ? a.half : -a.half);
-                        const float4 p0 = *reinterpret_cast<const float4*>(crow + pc);
-                        const float4 p1 = *reinterpret_cast<const float4*>(crow + pc + 4);
-                        xp[0] = p0.x; xp[1] = p0.y; xp[2] = p0.z; xp[3] = p0.w;
-                        xp[4] = p1.x; xp[5] = p1.y; xp[6] = p1.z; xp[7] = p1.w;
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            val[e] = rotate_own<false>(val[e], xp[e], cc[e], ss[e], firstg[G]);
+                            val[k][e] = rotate_own<false>(val[k][e], xp[k][e], cc[k][e], ss[k][e], firstg[G]);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) xp[e] = val[e ^ 1];
+                        for (int e = 0; e < 8; ++e) xp[k][e] = val[k][e ^ 1];
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            val[e] = rotate_own<false>(val[e], xp[e], cc[e], ss[e], (e & 1) == 0);
+                            val[k][e] = rotate_own<false>(val[k][e], xp[k][e], cc[k][e], ss[k][e], (e & 1) == 0);
                     }
                 }
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int32_t m = m0 + wm * 128 + q * 32 + lr0 + 8 * k;
                 if (m < a.M && liveg[G]) {
                     const int64_t yo = (int64_t)m * a.N + colg[G];
                     if (a.ydt == ROPE_DTYPE_F32) {
                         v4u* yp = reinterpret_cast<v4u*>(static_cast<float*>(a.y) + yo);
-                        __builtin_nontemporal_store(v4u{__float_as_uint(val[0]), __float_as_uint(val[1]),
-                                                        __float_as_uint(val[2]), __float_as_uint(val[3])}, yp);
-                        __builtin_nontemporal_store(v4u{__float_as_uint(val[4]), __float_as_uint(val[5]),
-                                                        __float_as_uint(val[6]), __float_as_uint(val[7])}, yp + 1);
+                        __builtin_nontemporal_store(v4u{__float_as_uint(val[k][0]), __float_as_uint(val[k][1]),
+                                                        __float_as_uint(val[k][2]), __float_as_uint(val[k][3])}, yp);
+                        __builtin_nontemporal_store(v4u{__float_as_uint(val[k][4]), __float_as_uint(val[k][5]),
+                                                        __float_as_uint(val[k][6]), __float_as_uint(val[k][7])},
+                                                    yp + 1);
                     } else {
                         Lanes<DT> Y;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) Y.v[e] = val[e];
+                        for (int e = 0; e < 8; ++e) Y.v[e] = val[k][e];
                         __builtin_nontemporal_store(Y.pack(),
                                                     reinterpret_cast<v4u*>(static_cast<uint16_t*>(a.y) + yo));
                     }
                 }
             }
+        }
     }
 }
 
