@@ -730,11 +730,9 @@ __global__ void __launch_bounds__(ProjSq::THREADS) __attribute__((amdgpu_waves_p
         else fb[buf][q - 4] = *reinterpret_cast<const v4u*>(S0 + b_row + (q - 4) * 32 * kProjBK + s16);
     };
 
-    f32x16 acc[4][4];   // [nt][mt]: rows are output lanes, columns tokens
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    // [nt][mt]: rows are output lanes, columns tokens; the first step of the
+    // first stage starts them from an inline zero (no per-tile clearing)
+    f32x16 acc[4][4];
 
     // One stage: 4 steps of 16 k, 16 MFMAs each (nt-major). Step kk reads the
     // fragments of step kk+1 (buffer (kk+1)&1); steps 0 and 1 issue the next
@@ -762,9 +760,10 @@ __global__ void __launch_bounds__(ProjSq::THREADS) __attribute__((amdgpu_waves_p
         const uint32_t voff = (uint32_t)((o + c * (16 / TS)) * TS);   // the host bounds it below 2^32
         proj_dma16(table ? a.r2 : a.r1, voff, smem_lds + (uint32_t)(li * 1024));
     };
-    auto stage = [&](auto slot_c, auto more_c, int32_t kt) {
+    auto stage = [&](auto slot_c, auto more_c, auto first_c, int32_t kt) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr bool more = decltype(more_c)::value;
+        constexpr bool first = decltype(first_c)::value;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int cur = kk & 1, nxt = cur ^ 1;
@@ -777,7 +776,7 @@ __global__ void __launch_bounds__(ProjSq::THREADS) __attribute__((amdgpu_waves_p
                     asm volatile("" ::: "memory");
                 }
                 const int nt = j >> 2, mt = j & 3;
-                acc[nt][mt] = proj_mfma<DT>(fb[cur][nt], fa[cur][mt], acc[nt][mt]);
+                acc[nt][mt] = proj_mfma<DT>(fb[cur][nt], fa[cur][mt], first && kk == 0 ? f32x16{} : acc[nt][mt]);
                 if (more && kk < 2 && (j & 1) == 0) load1(kt + 1, slot ^ 1, kk * 8 + (j >> 1));
                 if constexpr (!more && EPI >= 0)
                     if (kk < 2 && (j & 1) == 0 && kk * 8 + (j >> 1) < ntab) tab_dma(kk * 8 + (j >> 1));
@@ -802,13 +801,17 @@ __global__ void __launch_bounds__(ProjSq::THREADS) __attribute__((amdgpu_waves_p
     using S1 = std::integral_constant<int, 1>;
     using More = std::true_type;
     using Last = std::false_type;
-    int32_t kt = 0;
+    using First = std::true_type;
+    using Later = std::false_type;
+    // stage kt in slot kt % 2: the first stage peeled (zero accumulators),
+    // then pairs, then the last stage (KT even)
+    stage(S0{}, More{}, First{}, 0);
+    int32_t kt = 1;
     for (; kt + 2 < KT; kt += 2) {
-        stage(S0{}, More{}, kt);
-        stage(S1{}, More{}, kt + 1);
+        stage(S1{}, More{}, Later{}, kt);
+        stage(S0{}, More{}, Later{}, kt + 1);
     }
-    stage(S0{}, More{}, kt);
-    stage(S1{}, Last{}, kt + 1);
+    stage(S1{}, Last{}, Later{}, kt);
     proj_wait_vm<0>();                                 // this wave's table rows are in LDS
     __syncthreads();                                   // every wave is done with the ring
 
