@@ -745,21 +745,59 @@ __global__ void __launch_bounds__(ProjSq::THREADS) __attribute__((amdgpu_waves_p
     // wave w fills chunk positions p = (2^(crl+1)*w + i)*64 + lane of
     // [table][token][chunk slot]; slot cs of token tr holds chunk
     // cs ^ (tr % 2^crl). Rows past M re-read the last token's row.
+    // Waves 0 and 1 load the cos rows, 2 and 3 the sin rows (2^(crl+2)
+    // loads per table). The byte offsets are computed while the first
+    // stage loads: between the last stage's MFMAs they would hold back the
+    // MFMA issue (and wait for reloaded kernel arguments, a wait that also
+    // waits out the fragment reads). Load i of a wave covers tokens
+    // tr0 + i * (64 >> crl) at one chunk slot, so the offsets step by whole
+    // rows, carrying into the next batch when s passes S (at most once per
+    // step when S >= 64 >> crl; shorter sequences take one division per
+    // load). 32-bit arithmetic: the host bounds every row's byte offset
+    // below 2^32, so sums modulo 2^32 are exact.
     const int ntab = EPI >= 0 && a.L > 0 && a.tab_crl >= 0 ? 2 << a.tab_crl : 0;   // loads per wave
-    auto tab_dma = [&](int i) {
-        const int crl = a.tab_crl;
-        const int li = __builtin_amdgcn_readfirstlane(wave * (2 << crl) + i);
-        const int table = li >> (2 + crl);             // 4*2^crl wave loads per table
-        const int pos = ((li << 6) + lane) & ((256 << crl) - 1);
-        const int tr = pos >> crl;
-        const int c = (pos & ((1 << crl) - 1)) ^ (tr & ((1 << crl) - 1));
-        const int32_t mc = min(m0 + tr, a.M - 1);
-        const int32_t b = (int32_t)fast_div((uint32_t)mc, a.s_div), sp = mc - b * a.S;
-        const int64_t o = table ? b * a.t2b + sp * a.t2s : b * a.t1b + sp * a.t1s;
-        constexpr int TS = TT == ROPE_DTYPE_F32 ? 4 : 2;
-        const uint32_t voff = (uint32_t)((o + c * (16 / TS)) * TS);   // the host bounds it below 2^32
-        proj_dma16(table ? a.r2 : a.r1, voff, smem_lds + (uint32_t)(li * 1024));
+    const int tcrl = a.tab_crl < 0 ? 0 : a.tab_crl;
+    const void* tab_base = wave >> 1 ? a.r2 : a.r1;
+    const uint32_t tab_lds = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(wave * (2 << tcrl) * 1024));
+    uint32_t toff[LW];
+    auto tab_offsets = [&]() {
+        const uint32_t tb = (uint32_t)(wave >> 1 ? a.t2b : a.t1b), ts = (uint32_t)(wave >> 1 ? a.t2s : a.t1s);
+        constexpr uint32_t TS = TT == ROPE_DTYPE_F32 ? 4 : 2;
+        const int tstep = 64 >> tcrl;
+        const int pos = ((wave * (2 << tcrl)) * 64 + lane) & ((256 << tcrl) - 1);
+        const int tr0 = pos >> tcrl;
+        const uint32_t cb = (uint32_t)(((pos & ((1 << tcrl) - 1)) ^ (tr0 & ((1 << tcrl) - 1))) * 16);
+        auto row = [&](int32_t m) {                    // element offset of token m's row
+            const uint32_t b = fast_div((uint32_t)m, a.s_div);
+            return b * tb + ((uint32_t)m - b * (uint32_t)a.S) * ts;
+        };
+        const uint32_t last = row(a.M - 1);            // rows past M re-read the last token's row
+        int32_t m = m0 + tr0;
+        if (a.S >= tstep) {
+            const int32_t mc = min(m, a.M - 1);
+            const uint32_t b = fast_div((uint32_t)mc, a.s_div);
+            uint32_t sp = (uint32_t)mc - b * (uint32_t)a.S;
+            uint32_t off = b * tb + sp * ts;
+            const uint32_t rstep = (uint32_t)tstep * ts, carry = tb - (uint32_t)a.S * ts;
+#pragma unroll
+            for (int i = 0; i < LW; ++i) {
+                toff[i] = (m < a.M ? off : last) * TS + cb;
+                m += tstep;
+                sp += tstep;
+                off += rstep;
+                if (sp >= (uint32_t)a.S) {
+                    sp -= (uint32_t)a.S;
+                    off += carry;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < LW; ++i) toff[i] = row(min(m + i * tstep, a.M - 1)) * TS + cb;
+        }
+#pragma unroll
+        for (int i = 0; i < LW; ++i) asm volatile("" : "+v"(toff[i]));   // kept here, not sunk to the uses
     };
+    auto tab_dma = [&](int i) { proj_dma16(tab_base, toff[i], tab_lds + (uint32_t)(i * 1024)); };
     auto stage = [&](auto slot_c, auto more_c, auto first_c, int32_t kt) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr bool more = decltype(more_c)::value;
@@ -792,6 +830,8 @@ __global__ void __launch_bounds__(ProjSq::THREADS) __attribute__((amdgpu_waves_p
     const int32_t KT = a.K / kProjBK;
 #pragma unroll
     for (int i = 0; i < LW; ++i) load1(0, 0, i);
+    if constexpr (EPI >= 0)
+        if (ntab) tab_offsets();
     proj_wait_vm<0>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
