@@ -174,6 +174,16 @@ CASES = [
     (1, 64, 256, 4, 192, (0, 192), "rotate_half", "bf16", "bf16", "bf16", "token"),
     # a group across lane 192 of a 384-lane head (no 192-lane tile holds it) inside the 256-lane square tile
     (1, 50, 128, 1, 384, (160, 224), "rotate_half", "bf16", "bf16", "bf16", "token"),
+    # table rows staged in LDS at every row width (16 to 128 bytes) and batch layout: a wave's
+    # loads step 64/2^crl tokens at a time, carrying into the next batch when s passes S
+    # (13, 50, 300 tokens per batch), or one division per load when S is shorter than a step
+    # (5, 6 and 20 tokens per batch); ragged M
+    (40, 5, 128, 2, 128, (0, 64), "interleave", "bf16", "bf16", "bf16", "batch"),
+    (50, 6, 128, 2, 64, (0, 64), "rotate_half", "bf16", "bf16", "bf16", "token"),
+    (23, 13, 256, 3, 128, (64, 128), "rotate_half", "f16", "f16", "f16", "batch"),
+    (3, 50, 128, 4, 64, (0, 32), "interleave", "bf16", "bf16", "f32", "batch"),
+    (2, 300, 128, 2, 128, (0, 16), "interleave", "bf16", "bf16", "bf16", "batch"),
+    (30, 20, 128, 2, 128, (0, 16), "interleave", "bf16", "bf16", "bf16", "batch"),
 ]
 
 
