@@ -642,6 +642,8 @@ CEILING_PATTERNS = {
     "c3": ["slice", "slice:dispatch", "row", "slice:p8", "slice:p32", "slice:p512", "slice:p2048", "slice:eighth",
            "slice:heads", "slice:heads:dispatch", "slice:pol0", "slice:pol7"],
     "c4_f32": ["slice", "slice:dispatch", "row"],
+    "rh_32of128": ["slice", "slice:dispatch", "lines", "lines:dispatch", "row"],
+    "rh_64of128": ["slice", "slice:dispatch", "row"],
 }
 
 
