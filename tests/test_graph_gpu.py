@@ -130,3 +130,39 @@ def test_position_calls_replay_like_eager(mode, sl, shape):
         torch.cuda.synchronize()
         assert torch.equal(_bits(xg), _bits(xe)), f"replay {rep} differs from the eager calls"
         assert not torch.equal(_bits(xg), _bits(x0.to(DEV))), "the calls must change x"
+
+
+@pytest.mark.parametrize("mode,sl", [("interleave", (0, 64)), ("rotate_half", (0, 64)), ("interleave", None)])
+def test_projection_call_replays_like_eager(mode, sl):
+    """The projection with a rotary epilogue into a given output, captured
+    and replayed (square tiles: the vector epilogue with the table rows
+    staged in LDS, or the plain projection). x changes between the replays
+    (eager work), and each replay writes the same bytes as an eager call on
+    the same x."""
+    g0 = torch.Generator().manual_seed(43)
+    M, K, H, Dh = 300, 256, 4, 192
+    x = torch.randn((1, M, K), generator=g0).to(torch.bfloat16).to(DEV)
+    w = (torch.randn((H * Dh, K), generator=g0) / 16).to(torch.bfloat16).to(DEV)
+    th = torch.randn((1, M, 1, 64), generator=g0, dtype=torch.float64)
+    c = torch.cos(th).to(torch.bfloat16).to(DEV)
+    s = torch.sin(th).to(torch.bfloat16).to(DEV)
+    if sl is None:
+        c = s = torch.zeros((1, 1, 1, 0), dtype=torch.bfloat16, device=DEV)
+    announce(f"graph projection {mode} {sl}")
+    yg = torch.empty((1, M, H, Dh), dtype=torch.bfloat16, device=DEV)
+    ye = torch.empty_like(yg)
+    rp.rope_proj_fwd(x, w, c, s, H, mode, sl, out=yg)      # first call outside the capture
+    torch.cuda.synchronize()
+    yg.fill_(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        rp.rope_proj_fwd(x, w, c, s, H, mode, sl, out=yg)
+    torch.cuda.synchronize()
+    assert not bool(yg.view(torch.int16).any()), "capture must not run the kernel"
+    for rep in range(4):
+        x.mul_(-1.0).add_(0.25)                              # eager work: another x for each replay
+        g.replay()
+        rp.rope_proj_fwd(x, w, c, s, H, mode, sl, out=ye)
+        torch.cuda.synchronize()
+        assert torch.equal(yg.view(torch.int16), ye.view(torch.int16)), f"replay {rep} differs from the eager call"
