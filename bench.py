@@ -913,6 +913,7 @@ def main() -> int:
             line["fused_projection"] = {
                 "workload": o["workload"], "fused_us": c["fused"]["us"], "TFLOPs": c["fused"]["TFLOPs"],
                 "mfma_frac": c["fused"]["mfma_frac"], "peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                "projection_only_us": c["projection_only"]["us"],
                 "projection_then_rope_us": c["projection_then_rope"]["us"],
                 "torch_matmul_then_rope_us": c["torch_matmul_then_rope"]["us"],
                 "torch_matmul_only_us": c["torch_matmul_only"]["us"]}
